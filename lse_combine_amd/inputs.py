@@ -1,0 +1,181 @@
+"""Seeded synthetic decode-attention inputs (data generation only, no attention math).
+
+Both the HIP path's tests/benchmark and the CPU oracle consume these tensors,
+so this module holds nothing but random draws and index bookkeeping. Tensors
+are generated on the CPU with ``torch.Generator('cpu')`` so that both sides
+see identical bits; callers copy them to the device themselves.
+
+Draw order for every workload: sequence lengths (when variable), page
+permutation (when paged), q, K, V (V is not drawn when it aliases K).
+Values are ``torch.randn`` in fp32, cast to bf16 (round-to-nearest-even) for
+bf16 workloads.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+
+@dataclass
+class Case:
+    """One decode step's inputs plus the metadata the C ABI needs."""
+
+    name: str
+    q: torch.Tensor                    # [B, Hq, Dqk]
+    k_cache: torch.Tensor              # contiguous [B, Lcap, Hkv, Dqk] or paged [N, ps, Hkv, Dqk]
+    v_cache: torch.Tensor | None       # same layout with Dv; None when V is the prefix of K
+    seq_lens: torch.Tensor             # int32 [B]
+    page_table: torch.Tensor | None    # int32 [B, max_pages] (padding -1) or None
+    page_size: int
+    scale: float
+    num_splits: int                    # 0 = automatic split selection
+    v_is_k_prefix: bool = False
+    ov_depth: int = 0
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def batch(self):
+        return self.q.shape[0]
+
+    @property
+    def num_q_heads(self):
+        return self.q.shape[1]
+
+    @property
+    def num_kv_heads(self):
+        return self.k_cache.shape[2]
+
+    @property
+    def qk_depth(self):
+        return self.q.shape[2]
+
+    @property
+    def dtype_name(self):
+        return {torch.float32: "f32", torch.bfloat16: "bf16"}[self.q.dtype]
+
+    def kv_bytes(self) -> int:
+        """Bytes of K and V that attention must read (attended tokens only)."""
+        tokens = int(self.seq_lens.clamp(min=0).sum())
+        es = self.q.element_size()
+        if self.v_is_k_prefix:
+            per_tok = self.num_kv_heads * self.qk_depth * es
+        else:
+            per_tok = self.num_kv_heads * (self.qk_depth + self.ov_depth) * es
+        return tokens * per_tok
+
+    def flops(self) -> int:
+        tokens = int(self.seq_lens.clamp(min=0).sum())
+        return 2 * self.num_q_heads * tokens * (self.qk_depth + self.ov_depth)
+
+
+def _randn(gen, shape, dtype):
+    x = torch.randn(shape, generator=gen, dtype=torch.float32)
+    return x if dtype == torch.float32 else x.to(dtype)
+
+
+def make_case(name="case", *, batch, num_q_heads, num_kv_heads, qk_depth, ov_depth=None,
+              dtype=torch.bfloat16, page_size=0, seq_lens=None, len_range=None, kv_capacity=None,
+              num_splits=0, seed=0, v_is_k_prefix=False, scale=None, poison=False,
+              spare_pages=0, q_scale=1.0, page_table_width=None) -> Case:
+    """Build a seeded case.
+
+    Exactly one of ``seq_lens`` (a list of lengths) or ``len_range``
+    ((lo, hi) inclusive, drawn with ``torch.randint``) is given.
+    Paged pools hold exactly sum(ceil(L_b / page_size)) pages (+ ``spare_pages``)
+    in a seeded random order; page-table padding is -1. ``poison`` fills every
+    cache slot that no sequence attends (tail of last pages, spare pages,
+    contiguous slots past L_b) with NaN so that a kernel reading them shows up.
+    ``q_scale`` multiplies q after the draw (large-logit tests).
+    """
+    ov_depth = qk_depth if ov_depth is None else ov_depth
+    gen = torch.Generator("cpu")
+    gen.manual_seed(seed)
+    if seq_lens is None:
+        lo, hi = len_range
+        lens = torch.randint(lo, hi + 1, (batch,), generator=gen, dtype=torch.int64)
+    else:
+        lens = torch.as_tensor(seq_lens, dtype=torch.int64)
+        assert lens.numel() == batch
+    lens32 = lens.to(torch.int32)
+    pos_lens = lens.clamp(min=0)
+    if page_size > 0:
+        pages_per_seq = [(-(-int(L) // page_size)) for L in pos_lens]
+        n_pages = sum(pages_per_seq) + spare_pages
+        n_pages = max(n_pages, 1)
+        perm = torch.randperm(n_pages, generator=gen).to(torch.int32)
+        width = page_table_width or max(1, max(pages_per_seq) if pages_per_seq else 1)
+        pt = torch.full((batch, width), -1, dtype=torch.int32)
+        off = 0
+        for b, npg in enumerate(pages_per_seq):
+            pt[b, :npg] = perm[off:off + npg]
+            off += npg
+        kv_shape_k = (n_pages, page_size, num_kv_heads, qk_depth)
+        kv_shape_v = (n_pages, page_size, num_kv_heads, ov_depth)
+    else:
+        pt = None
+        cap = kv_capacity or max(1, int(pos_lens.max()) if batch else 1)
+        kv_shape_k = (batch, cap, num_kv_heads, qk_depth)
+        kv_shape_v = (batch, cap, num_kv_heads, ov_depth)
+    q = _randn(gen, (batch, num_q_heads, qk_depth), dtype)
+    if q_scale != 1.0:
+        q = (q.float() * q_scale).to(dtype)
+    k = _randn(gen, kv_shape_k, dtype)
+    v = None if v_is_k_prefix else _randn(gen, kv_shape_v, dtype)
+    if poison:
+        _poison(k, v, pos_lens, pt, page_size)
+    sc = scale if scale is not None else 1.0 / math.sqrt(qk_depth)
+    return Case(name=name, q=q, k_cache=k, v_cache=v, seq_lens=lens32, page_table=pt,
+                page_size=page_size, scale=sc, num_splits=num_splits,
+                v_is_k_prefix=v_is_k_prefix, ov_depth=ov_depth, meta={"seed": seed})
+
+
+def _poison(k, v, lens, pt, page_size):
+    nan = float("nan")
+    if pt is None:
+        for b, L in enumerate(lens.tolist()):
+            k[b, L:] = nan
+            if v is not None:
+                v[b, L:] = nan
+        return
+    used = torch.zeros(k.shape[0], k.shape[1], dtype=torch.bool)
+    for b, L in enumerate(lens.tolist()):
+        for t0 in range(0, L, page_size):
+            n = min(page_size, L - t0)
+            used[int(pt[b, t0 // page_size]), :n] = True
+    k[~used] = nan
+    if v is not None:
+        v[~used] = nan
+
+
+# ---------------------------------------------------------------------------
+# the five named decode workloads
+# ---------------------------------------------------------------------------
+WORKLOADS = {
+    # batch 1, 1 q head / 1 kv head, D 128, L 1024, fp32, 4 partitions of 256 keys, contiguous
+    "tiny": dict(seed=1, batch=1, num_q_heads=1, num_kv_heads=1, qk_depth=128,
+                 dtype=torch.float32, page_size=0, seq_lens=[1024], num_splits=4),
+    # batch 8, 32/8 heads (group 4), D 128, L 4096, bf16, contiguous, 8 splits
+    "gqa": dict(seed=2, batch=8, num_q_heads=32, num_kv_heads=8, qk_depth=128,
+                dtype=torch.bfloat16, page_size=0, seq_lens=[4096] * 8, num_splits=8),
+    # batch 32, 64/8 heads (group 8), D 128, bf16, page 64, L_b ~ U[512, 32768], automatic splits
+    "paged_gqa": dict(seed=3, batch=32, num_q_heads=64, num_kv_heads=8, qk_depth=128,
+                      dtype=torch.bfloat16, page_size=64, len_range=(512, 32768),
+                      num_splits=0, page_table_width=512),
+    # batch 1, 32/4 heads (group 8), D 128, L 131072, bf16, page 64, 64 splits
+    "long": dict(seed=4, batch=1, num_q_heads=32, num_kv_heads=4, qk_depth=128,
+                 dtype=torch.bfloat16, page_size=64, seq_lens=[131072], num_splits=64),
+    # batch 16, 128 q heads / 1 kv head, qk 576 (512 + 64 rotary), ov 512 = K[..., :512],
+    # L 8192, bf16, page 64, 8 splits
+    "latent": dict(seed=5, batch=16, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512,
+                   dtype=torch.bfloat16, page_size=64, seq_lens=[8192] * 16, num_splits=8,
+                   v_is_k_prefix=True),
+}
+
+
+def workload(name: str, **overrides) -> Case:
+    spec = dict(WORKLOADS[name])
+    spec.update(overrides)
+    return make_case(name, **spec)

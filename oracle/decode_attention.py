@@ -1,0 +1,232 @@
+"""Plain fp64 CPU oracle for split-KV decode attention and its log-sum-exp combine.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or run
+this module: only the tests, the smoke check and the benchmark's CPU-baseline
+leg use it. It shares no code, constant or helper with the HIP library.
+
+What is computed (single query per sequence, i.e. decode):
+
+* ``decode_attention_fp64`` -- the plain definition. For every sequence b and
+  query head h, with kv head k = floor(h / g), g = Hq / Hkv:
+      x_t  = sum_d q[b,h,d] * K[b,t,k,d]            t < L_b
+      m    = max_t x_t
+      Z    = sum_t exp(scale * (x_t - m))
+      O[d] = sum_t exp(scale * (x_t - m)) * V[b,t,k,d] / Z
+      LSE  = scale * m + ln Z
+  The split-K method re-associates exactly this sum, so the definition is the
+  oracle for the whole path (fa4_splitk_combine_write, first paragraph: the
+  per-partition weights sum to one and the partition sums cancel the
+  normalisation of each partial O).
+* ``partition_partials_fp64`` -- pass 1 of split-K as the pages describe it:
+  each key partition yields its row max, row sum and NORMALISED partial O
+  (fa4_splitk_combine_write, second paragraph).
+* ``combine_fp64`` -- pass 2, the combine formula of fa4_splitk_combine_write
+  (first paragraph) written out in the pages' exp2 form:
+      Gmax = max_p max_p,  Gsum = sum_p sum_p * exp2((max_p - Gmax) * c),
+      w_p = sum_p * exp2((max_p - Gmax) * c) / Gsum,  O = sum_p w_p * O_p,
+  with c = scale * log2(e) (the ``scale_log2e`` argument of that function).
+* ``bf16_round_fp64`` -- the final cast to bf16 (same paragraph), read as
+  round-to-nearest-even.
+
+Readings where the pages are silent (each is listed in the design notes):
+the max is kept in raw q.k units; empty partitions contribute weight 0 and an
+empty sequence gives O = 0, LSE = -inf; partitions are contiguous chunks of
+``chunk`` keys; q head h reads kv head h // g (FA4Config, BM_eff: a fused
+GQA tile covers ``group`` heads); in the latent-shared layout V is the first
+``ov_depth`` columns of K (FA4Config, shared_kv_cols / nope_cols_per_cta).
+
+Every function here is pinned by the ``-m "not gpu"`` tests against brute
+force, closed forms, library routines and invariants.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+LOG2E = 1.0 / math.log(2.0)
+
+
+# ---------------------------------------------------------------------------
+# gathering one (sequence, kv-head) slice of the cache
+# ---------------------------------------------------------------------------
+def _key_rows(k_cache, b, kvh, L, page_table, page_size):
+    """Return the L key vectors of sequence b, kv head kvh, as fp64 [L, D].
+
+    Contiguous layout: k_cache is [B, L_cap, Hkv, D] and key t is k_cache[b, t].
+    Paged layout: k_cache is a page pool [N_pages, page_size, Hkv, D] and key t
+    lives in page page_table[b, t // page_size] at slot t % page_size
+    (FA4Config, v_row_major: a block-indirected paged cache addresses a page's
+    rows at block_idx * stride).
+    """
+    t = np.arange(L)
+    if page_table is None:
+        rows = k_cache[b, :L, kvh, :]
+    else:
+        pages = np.asarray(page_table)[b, t // page_size]
+        rows = k_cache[pages, t % page_size, kvh, :]
+    return np.asarray(rows, dtype=np.float64)
+
+
+def _gather(q, k_cache, v_cache, b, kvh, g, L, page_table, page_size, v_is_k_prefix, ov_depth):
+    qg = np.asarray(q[b, kvh * g:(kvh + 1) * g, :], dtype=np.float64)
+    K = _key_rows(k_cache, b, kvh, L, page_table, page_size)
+    if v_is_k_prefix:
+        V = K[:, :ov_depth]
+    else:
+        V = _key_rows(v_cache, b, kvh, L, page_table, page_size)
+    return qg, K, V
+
+
+def _dims(q, k_cache, v_cache, v_is_k_prefix, ov_depth):
+    B, Hq, Dqk = q.shape
+    Hkv = k_cache.shape[2]
+    if Hq % Hkv:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    if v_is_k_prefix:
+        Dv = Dqk if ov_depth is None else int(ov_depth)
+    else:
+        Dv = v_cache.shape[3]
+    return B, Hq, Hkv, Hq // Hkv, Dqk, Dv
+
+
+# ---------------------------------------------------------------------------
+# the definition
+# ---------------------------------------------------------------------------
+def decode_attention_fp64(q, k_cache, v_cache, seq_lens, scale, page_table=None, page_size=0,
+                          v_is_k_prefix=False, ov_depth=None):
+    """Full softmax(scale * q K^T) V per (sequence, head), in fp64.
+
+    q: [B, Hq, Dqk]; caches as described in ``_key_rows``; seq_lens: [B].
+    Returns (O [B, Hq, Dv] fp64, LSE [B, Hq] fp64, natural log).
+    A sequence of length 0 gives O = 0 and LSE = -inf.
+    """
+    B, Hq, Hkv, g, Dqk, Dv = _dims(q, k_cache, v_cache, v_is_k_prefix, ov_depth)
+    O = np.zeros((B, Hq, Dv), dtype=np.float64)
+    LSE = np.full((B, Hq), -np.inf, dtype=np.float64)
+    for b in range(B):
+        L = int(seq_lens[b])
+        if L <= 0:
+            continue
+        for kvh in range(Hkv):
+            qg, K, V = _gather(q, k_cache, v_cache, b, kvh, g, L, page_table, page_size,
+                               v_is_k_prefix, Dv)
+            x = qg @ K.T                                   # [g, L] raw scores
+            m = x.max(axis=1, keepdims=True)
+            e = np.exp(scale * (x - m))
+            Z = e.sum(axis=1, keepdims=True)
+            O[b, kvh * g:(kvh + 1) * g] = (e @ V) / Z
+            LSE[b, kvh * g:(kvh + 1) * g] = scale * m[:, 0] + np.log(Z[:, 0])
+    return O, LSE
+
+
+# ---------------------------------------------------------------------------
+# split-K pass 1: per-partition (max, sum, normalised O)
+# ---------------------------------------------------------------------------
+def partition_partials_fp64(q, k_cache, v_cache, seq_lens, scale, chunk, num_partitions,
+                            page_table=None, page_size=0, v_is_k_prefix=False, ov_depth=None):
+    """Per-partition partials of the split-K method.
+
+    Partition p of sequence b covers keys [p*chunk, min((p+1)*chunk, L_b)).
+    Returns (m [B,Hq,P], l [B,Hq,P], O [B,Hq,P,Dv]) with m the raw-unit row max,
+    l = sum_t exp(scale*(x_t - m)) and O the partition's output already divided
+    by l (fa4_splitk_combine_write, second paragraph: the staged O_cta is
+    normalised). A partition with no keys holds (m, l, O) = (-inf, 0, 0).
+    """
+    B, Hq, Hkv, g, Dqk, Dv = _dims(q, k_cache, v_cache, v_is_k_prefix, ov_depth)
+    P = int(num_partitions)
+    m = np.full((B, Hq, P), -np.inf)
+    l = np.zeros((B, Hq, P))
+    O = np.zeros((B, Hq, P, Dv))
+    for b in range(B):
+        L = int(seq_lens[b])
+        if L <= 0:
+            continue
+        for kvh in range(Hkv):
+            qg, K, V = _gather(q, k_cache, v_cache, b, kvh, g, L, page_table, page_size,
+                               v_is_k_prefix, Dv)
+            x = qg @ K.T
+            hs = slice(kvh * g, (kvh + 1) * g)
+            for p in range(P):
+                lo, hi = p * chunk, min((p + 1) * chunk, L)
+                if lo >= hi:
+                    continue
+                xp = x[:, lo:hi]
+                mp = xp.max(axis=1, keepdims=True)
+                e = np.exp(scale * (xp - mp))
+                lp = e.sum(axis=1, keepdims=True)
+                m[b, hs, p] = mp[:, 0]
+                l[b, hs, p] = lp[:, 0]
+                O[b, hs, p] = (e @ V[lo:hi]) / lp
+    return m, l, O
+
+
+# ---------------------------------------------------------------------------
+# split-K pass 2: the LSE combine
+# ---------------------------------------------------------------------------
+def combine_fp64(m, l, O, scale):
+    """Merge P partitions per row with the log-sum-exp combine.
+
+    m, l: [..., P]; O: [..., P, Dv]. Follows fa4_splitk_combine_write
+    (first paragraph) with c = scale * log2(e). Partitions with l == 0 get
+    weight 0; a row whose partitions are all empty gives O = 0, LSE = -inf.
+    Returns (O [..., Dv], LSE [...]).
+    """
+    m = np.asarray(m, dtype=np.float64)
+    l = np.asarray(l, dtype=np.float64)
+    O = np.asarray(O, dtype=np.float64)
+    c = scale * LOG2E
+    lead = m.shape[:-1]
+    Dv = O.shape[-1]
+    out = np.zeros(lead + (Dv,))
+    lse = np.full(lead, -np.inf)
+    for idx in np.ndindex(*lead):
+        live = l[idx] > 0
+        if not live.any():
+            continue
+        mp, lp, Op = m[idx][live], l[idx][live], O[idx][live]
+        gmax = mp.max()
+        e = np.exp2((mp - gmax) * c)
+        gsum = (lp * e).sum()
+        w = lp * e / gsum
+        out[idx] = (w[:, None] * Op).sum(axis=0)
+        lse[idx] = scale * gmax + math.log(gsum)
+    return out, lse
+
+
+def decode_attention_splitk_fp64(q, k_cache, v_cache, seq_lens, scale, chunk, page_table=None,
+                                 page_size=0, v_is_k_prefix=False, ov_depth=None):
+    """Split-K pass 1 then the LSE combine, the two steps in the pages' order."""
+    max_len = int(np.max(seq_lens)) if len(seq_lens) else 0
+    P = max(1, -(-max_len // chunk))
+    m, l, O = partition_partials_fp64(q, k_cache, v_cache, seq_lens, scale, chunk, P,
+                                      page_table, page_size, v_is_k_prefix, ov_depth)
+    return combine_fp64(m, l, O, scale)
+
+
+# ---------------------------------------------------------------------------
+# the bf16 cast
+# ---------------------------------------------------------------------------
+def bf16_round_fp64(x):
+    """Round fp64 values to the nearest bf16 (ties to even), returned as fp64.
+
+    bf16 keeps 8 significant bits and fp32's exponent range: normal values
+    have the form k * 2^(e-7) with 128 <= |k| < 256; below 2^-126 the spacing
+    is the fixed subnormal step 2^-133; beyond the largest finite bf16 the
+    result is +-inf.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.array(x, copy=True)
+    fin = np.isfinite(x) & (x != 0)
+    xf = x[fin]
+    mant, expo = np.frexp(xf)                      # xf = mant * 2^expo, 0.5 <= |mant| < 1
+    normal = np.abs(xf) >= 2.0 ** -126
+    r = np.empty_like(xf)
+    r[normal] = np.ldexp(np.rint(np.ldexp(mant[normal], 8)), expo[normal] - 8)
+    sub = ~normal
+    r[sub] = np.ldexp(np.rint(np.ldexp(xf[sub], 133)), -133)
+    max_bf16 = (2.0 - 2.0 ** -7) * 2.0 ** 127
+    r[np.abs(r) > max_bf16] = np.copysign(np.inf, r[np.abs(r) > max_bf16])
+    out[fin] = r
+    return out

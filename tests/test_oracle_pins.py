@@ -1,0 +1,322 @@
+"""Pins for the fp64 oracle: each check ties it to something other than itself.
+
+The pages print no worked numeric example, so the oracle is pinned by
+brute force, closed forms, library routines (scipy, torch) and the
+invariants of softmax attention and of the split-K combine
+(fa4_splitk_combine_write, first and second paragraphs).
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+from oracle import (
+    bf16_round_fp64,
+    combine_fp64,
+    decode_attention_fp64,
+    decode_attention_splitk_fp64,
+    partition_partials_fp64,
+)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rng_case(seed, B=2, Hq=4, Hkv=2, D=8, Dv=None, L=(5, 9), paged=0, dtype=np.float64):
+    r = np.random.default_rng(seed)
+    Dv = D if Dv is None else Dv
+    lens = np.array([L[b % len(L)] for b in range(B)])
+    q = r.standard_normal((B, Hq, D))
+    if paged:
+        npg = [-(-int(x) // paged) for x in lens]
+        n = sum(npg) + 2
+        perm = r.permutation(n)
+        pt = -np.ones((B, max(npg)), dtype=np.int64)
+        off = 0
+        for b in range(B):
+            pt[b, :npg[b]] = perm[off:off + npg[b]]
+            off += npg[b]
+        k = r.standard_normal((n, paged, Hkv, D))
+        v = r.standard_normal((n, paged, Hkv, Dv))
+        return q, k, v, lens, pt
+    cap = int(lens.max())
+    k = r.standard_normal((B, cap, Hkv, D))
+    v = r.standard_normal((B, cap, Hkv, Dv))
+    return q, k, v, lens, None
+
+
+# ---------------------------------------------------------------------------
+# brute force: pure-Python loops with math.exp and math.fsum
+# ---------------------------------------------------------------------------
+def brute(q, k, v, lens, scale, pt=None, ps=0):
+    B, Hq, D = q.shape
+    Hkv = k.shape[2]
+    g = Hq // Hkv
+    Dv = v.shape[3]
+    O = [[[0.0] * Dv for _ in range(Hq)] for _ in range(B)]
+    LSE = [[-math.inf] * Hq for _ in range(B)]
+    for b in range(B):
+        L = int(lens[b])
+        for h in range(Hq):
+            kv = h // g
+            keys, vals = [], []
+            for t in range(L):
+                if pt is None:
+                    keys.append(k[b][t][kv]); vals.append(v[b][t][kv])
+                else:
+                    page = int(pt[b][t // ps]); slot = t % ps
+                    keys.append(k[page][slot][kv]); vals.append(v[page][slot][kv])
+            if not keys:
+                continue
+            xs = [math.fsum(float(q[b][h][d]) * float(kk[d]) for d in range(D)) for kk in keys]
+            # exact log-sum-exp of scale*x without a max shift would overflow for big x;
+            # shift by the first score instead of the max to stay independent of the oracle
+            s0 = xs[0]
+            ws = [math.exp(scale * (x - s0)) for x in xs]
+            Z = math.fsum(ws)
+            for d in range(Dv):
+                O[b][h][d] = math.fsum(w * float(vv[d]) for w, vv in zip(ws, vals)) / Z
+            LSE[b][h] = scale * s0 + math.log(Z)
+    return np.array(O), np.array(LSE)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("paged", [0, 4])
+def test_brute_force_tiny(seed, paged):
+    q, k, v, lens, pt = rng_case(seed, B=2, Hq=4, Hkv=2, D=6, Dv=5, L=(7, 13), paged=paged)
+    scale = 0.37
+    O, LSE = decode_attention_fp64(q, k, v, lens, scale, page_table=pt, page_size=paged)
+    Ob, Lb = brute(q, k, v, lens, scale, pt, paged)
+    np.testing.assert_allclose(O, Ob, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(LSE, Lb, rtol=1e-14, atol=1e-13)
+
+
+def test_brute_force_group1_and_group4():
+    for Hq, Hkv in [(3, 3), (8, 2), (4, 1)]:
+        q, k, v, lens, pt = rng_case(10 + Hq, B=2, Hq=Hq, Hkv=Hkv, D=4, L=(3, 11))
+        O, LSE = decode_attention_fp64(q, k, v, lens, 0.9)
+        Ob, Lb = brute(q, k, v, lens, 0.9)
+        np.testing.assert_allclose(O, Ob, atol=1e-13)
+        np.testing.assert_allclose(LSE, Lb, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# library routines: scipy's logsumexp / softmax
+# ---------------------------------------------------------------------------
+def test_matches_scipy_softmax_and_logsumexp():
+    q, k, v, lens, _ = rng_case(5, B=1, Hq=2, Hkv=1, D=16, L=(40,))
+    scale = 0.25
+    O, LSE = decode_attention_fp64(q, k, v, lens, scale)
+    for h in range(2):
+        x = scale * (k[0, :40, 0, :] @ q[0, h])
+        np.testing.assert_allclose(LSE[0, h], scipy.special.logsumexp(x), rtol=1e-14)
+        np.testing.assert_allclose(O[0, h], scipy.special.softmax(x) @ v[0, :40, 0, :], atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# closed forms
+# ---------------------------------------------------------------------------
+def test_constant_v_gives_v():
+    q, k, v, lens, _ = rng_case(7, B=2, Hq=4, Hkv=2, D=8, L=(33, 17))
+    u = np.linspace(-2, 3, 8)
+    v[:] = u
+    O, _ = decode_attention_fp64(q, k, v, lens, 0.5)
+    np.testing.assert_allclose(O, np.broadcast_to(u, O.shape), rtol=0, atol=4e-16 * 3)
+
+
+def test_zero_k_gives_mean_v_and_log_len():
+    q, k, v, lens, _ = rng_case(8, B=2, Hq=2, Hkv=1, D=8, L=(21, 9))
+    k[:] = 0
+    O, LSE = decode_attention_fp64(q, k, v, lens, 0.3)
+    for b in range(2):
+        L = lens[b]
+        np.testing.assert_allclose(O[b], np.broadcast_to(v[b, :L, 0].mean(0), O[b].shape), atol=1e-15)
+        np.testing.assert_allclose(LSE[b], math.log(L), rtol=1e-15)
+
+
+def test_single_key_and_two_keys():
+    q, k, v, lens, _ = rng_case(9, B=1, Hq=1, Hkv=1, D=8, L=(1,))
+    s = 0.7
+    O, LSE = decode_attention_fp64(q, k, v, lens, s)
+    np.testing.assert_allclose(O[0, 0], v[0, 0, 0], atol=0)
+    np.testing.assert_allclose(LSE[0, 0], s * float(q[0, 0] @ k[0, 0, 0]), rtol=1e-15)
+    q, k, v, lens, _ = rng_case(11, B=1, Hq=1, Hkv=1, D=8, L=(2,))
+    O, LSE = decode_attention_fp64(q, k, v, lens, s)
+    x0, x1 = float(q[0, 0] @ k[0, 0, 0]), float(q[0, 0] @ k[0, 1, 0])
+    sig = lambda z: 1.0 / (1.0 + math.exp(-z))  # noqa: E731
+    ref = sig(s * (x0 - x1)) * v[0, 0, 0] + sig(s * (x1 - x0)) * v[0, 1, 0]
+    np.testing.assert_allclose(O[0, 0], ref, atol=1e-15)
+    np.testing.assert_allclose(LSE[0, 0], math.log(math.exp(s * x0) + math.exp(s * x1)), rtol=1e-14)
+
+
+def test_empty_sequence():
+    q, k, v, lens, _ = rng_case(12, B=2, Hq=2, Hkv=1, D=4, L=(0, 5))
+    O, LSE = decode_attention_fp64(q, k, v, lens, 1.0)
+    assert np.all(O[0] == 0) and np.all(np.isneginf(LSE[0]))
+    assert np.all(np.isfinite(LSE[1]))
+
+
+# ---------------------------------------------------------------------------
+# invariants
+# ---------------------------------------------------------------------------
+def test_shift_invariance_and_overflow_safety():
+    q, k, v, lens, _ = rng_case(13, B=1, Hq=2, Hkv=1, D=8, L=(50,))
+    s = 0.5
+    O, LSE = decode_attention_fp64(q, k, v, lens, s)
+    a = np.full(8, 400.0)  # scale*q.a is far beyond exp's range: needs the max shift
+    k2 = k + a
+    O2, LSE2 = decode_attention_fp64(q, k2, v, lens, s)
+    np.testing.assert_allclose(O2, O, atol=1e-11)
+    np.testing.assert_allclose(LSE2, LSE + s * (q[0] @ a), rtol=1e-12)
+    assert np.all(np.isfinite(O2))
+
+
+def test_key_permutation_invariance():
+    q, k, v, lens, _ = rng_case(14, B=1, Hq=2, Hkv=1, D=8, L=(30,))
+    perm = np.random.default_rng(0).permutation(30)
+    O, LSE = decode_attention_fp64(q, k, v, lens, 0.4)
+    O2, LSE2 = decode_attention_fp64(q, k[:, perm], v[:, perm], lens, 0.4)
+    np.testing.assert_allclose(O2, O, atol=1e-14)
+    np.testing.assert_allclose(LSE2, LSE, rtol=1e-14)
+
+
+def test_paged_equals_contiguous_gather():
+    q, k, v, lens, pt = rng_case(15, B=3, Hq=4, Hkv=2, D=8, L=(13, 4, 9), paged=4)
+    ps = 4
+    cap = int(lens.max())
+    kc = np.zeros((3, cap, 2, 8)); vc = np.zeros((3, cap, 2, 8))
+    for b in range(3):
+        for t in range(lens[b]):
+            kc[b, t] = k[pt[b, t // ps], t % ps]
+            vc[b, t] = v[pt[b, t // ps], t % ps]
+    O, LSE = decode_attention_fp64(q, k, v, lens, 0.6, page_table=pt, page_size=ps)
+    O2, LSE2 = decode_attention_fp64(q, kc, vc, lens, 0.6)
+    np.testing.assert_array_equal(O, O2)
+    np.testing.assert_array_equal(LSE, LSE2)
+
+
+def test_gqa_equals_mha_with_repeated_heads():
+    q, k, v, lens, _ = rng_case(16, B=2, Hq=8, Hkv=2, D=8, L=(12, 7))
+    O, LSE = decode_attention_fp64(q, k, v, lens, 0.8)
+    k_rep = np.repeat(k, 4, axis=2)
+    v_rep = np.repeat(v, 4, axis=2)
+    O2, LSE2 = decode_attention_fp64(q, k_rep, v_rep, lens, 0.8)
+    # same sums, different BLAS blocking: equal up to fp64 rounding
+    np.testing.assert_allclose(O, O2, atol=1e-14)
+    np.testing.assert_allclose(LSE, LSE2, rtol=1e-14)
+
+
+def test_latent_shared_equals_materialised_v():
+    q, k, _, lens, pt = rng_case(17, B=2, Hq=4, Hkv=1, D=12, L=(9, 20), paged=4)
+    O, LSE = decode_attention_fp64(q, k, None, lens, 0.3, page_table=pt, page_size=4,
+                                   v_is_k_prefix=True, ov_depth=10)
+    v = np.ascontiguousarray(k[..., :10])
+    O2, LSE2 = decode_attention_fp64(q, k, v, lens, 0.3, page_table=pt, page_size=4)
+    np.testing.assert_array_equal(O, O2)
+    np.testing.assert_array_equal(LSE, LSE2)
+    assert O.shape[-1] == 10
+
+
+# ---------------------------------------------------------------------------
+# split-K: P-way combine equals the P = 1 result
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("chunk", [1, 3, 8, 16, 64])
+def test_splitk_combine_equals_definition(chunk):
+    q, k, v, lens, pt = rng_case(18, B=3, Hq=4, Hkv=2, D=8, L=(37, 16, 1), paged=8)
+    O, LSE = decode_attention_fp64(q, k, v, lens, 0.45, page_table=pt, page_size=8)
+    O2, LSE2 = decode_attention_splitk_fp64(q, k, v, lens, 0.45, chunk, page_table=pt, page_size=8)
+    np.testing.assert_allclose(O2, O, atol=1e-14)
+    np.testing.assert_allclose(LSE2, LSE, rtol=1e-14)
+
+
+def test_partitions_are_normalised_and_empty_ones_are_neutral():
+    q, k, v, lens, _ = rng_case(19, B=2, Hq=2, Hkv=1, D=8, L=(10, 3))
+    m, l, O = partition_partials_fp64(q, k, v, lens, 1.0, chunk=4, num_partitions=5)
+    # sequence 1 has one partition; partitions 1..4 are empty
+    assert np.all(np.isneginf(m[1, :, 1:])) and np.all(l[1, :, 1:] == 0) and np.all(O[1, :, 1:] == 0)
+    # a normalised partial of constant V is V itself
+    v2 = np.ones_like(v)
+    _, _, O1 = partition_partials_fp64(q, k, v2, lens, 1.0, chunk=4, num_partitions=3)
+    np.testing.assert_allclose(O1[0], 1.0, atol=1e-15)
+    # the combine of a single partition returns it unchanged
+    Oc, Lc = combine_fp64(m[1, :, :1], l[1, :, :1], O[1, :, :1], 1.0)
+    np.testing.assert_array_equal(Oc, O[1, :, 0])
+    np.testing.assert_allclose(Lc, m[1, :, 0] + np.log(l[1, :, 0]), rtol=1e-15)
+
+
+def test_combine_is_order_independent_and_all_empty_row():
+    r = np.random.default_rng(3)
+    m = r.standard_normal((5, 6)) * 3
+    l = r.uniform(0.5, 4, (5, 6))
+    O = r.standard_normal((5, 6, 7))
+    perm = r.permutation(6)
+    a, la = combine_fp64(m, l, O, 0.7)
+    b, lb = combine_fp64(m[:, perm], l[:, perm], O[:, perm], 0.7)
+    np.testing.assert_allclose(a, b, atol=1e-14)
+    np.testing.assert_allclose(la, lb, rtol=1e-14)
+    z, lz = combine_fp64(np.full((1, 3), -np.inf), np.zeros((1, 3)), np.zeros((1, 3, 2)), 1.0)
+    assert np.all(z == 0) and np.isneginf(lz[0])
+
+
+# ---------------------------------------------------------------------------
+# bf16 cast: torch's fp32 -> bf16 cast (round-to-nearest-even) as the library pin
+# ---------------------------------------------------------------------------
+def test_bf16_round_matches_torch_on_fp32_values():
+    r = np.random.default_rng(4)
+    x = np.concatenate([
+        r.standard_normal(20000) * 10.0 ** r.integers(-30, 30, 20000),
+        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 2.0 ** -130, 3 * 2.0 ** -134,
+                  3.3895313892515355e38, 3.39e38, -3.4e38, 0.0, 65504.0]),
+    ]).astype(np.float32)
+    ours = bf16_round_fp64(x.astype(np.float64))
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_bf16_ties_to_even():
+    assert bf16_round_fp64(np.array([1 + 2 ** -8]))[0] == 1.0
+    assert bf16_round_fp64(np.array([1 + 3 * 2 ** -8]))[0] == 1 + 2 ** -6
+    assert bf16_round_fp64(np.array([1 + 2 ** -8 + 2 ** -40]))[0] == 1 + 2 ** -7
+
+
+# ---------------------------------------------------------------------------
+# hand-derived golden fixtures (the pages print no worked example)
+# ---------------------------------------------------------------------------
+def _load_golden():
+    out = []
+    for fn in sorted(os.listdir(GOLDEN)):
+        if fn.endswith(".json"):
+            with open(os.path.join(GOLDEN, fn)) as f:
+                out.append((fn, json.load(f)))
+    return out
+
+
+@pytest.mark.parametrize("fn,case", _load_golden(), ids=[f for f, _ in _load_golden()])
+def test_golden_fixture(fn, case):
+    kind = case["kind"]
+    if kind == "attention":
+        q = np.array(case["q"], dtype=np.float64)
+        k = np.array(case["k_cache"], dtype=np.float64)
+        v = np.array(case["v_cache"], dtype=np.float64)
+        pt = np.array(case["page_table"]) if case.get("page_table") is not None else None
+        O, LSE = decode_attention_fp64(q, k, v, np.array(case["seq_lens"]), case["scale"],
+                                       page_table=pt, page_size=case.get("page_size", 0))
+        np.testing.assert_allclose(O, np.array(case["expected_o"]), atol=1e-14)
+        np.testing.assert_allclose(LSE, np.array(case["expected_lse"]), rtol=1e-14)
+        if "chunk" in case:
+            O2, L2 = decode_attention_splitk_fp64(q, k, v, np.array(case["seq_lens"]), case["scale"],
+                                                  case["chunk"], page_table=pt,
+                                                  page_size=case.get("page_size", 0))
+            np.testing.assert_allclose(O2, np.array(case["expected_o"]), atol=1e-14)
+            np.testing.assert_allclose(L2, np.array(case["expected_lse"]), rtol=1e-14)
+    elif kind == "combine":
+        O, LSE = combine_fp64(np.array(case["m"]), np.array(case["l"]), np.array(case["o"]),
+                              case["scale"])
+        np.testing.assert_allclose(O, np.array(case["expected_o"]), atol=1e-14)
+        np.testing.assert_allclose(LSE, np.array(case["expected_lse"]), rtol=1e-14)
+    else:
+        raise AssertionError(kind)
