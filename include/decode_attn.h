@@ -1,0 +1,165 @@
+/*
+ * decode_attn.h -- split-KV decode attention with the log-sum-exp combine,
+ * for AMD Instinct MI355X (gfx950). Plain C ABI: no C++ or framework types.
+ *
+ * What it computes. For every sequence b and query head h (one query per
+ * sequence, i.e. decode), with kv head k = h / g and g = Hq / Hkv:
+ *     O[b,h,:] = softmax_t(scale * q[b,h,:] . K[b,t,k,:]) @ V[b,t,k,:],  t < L_b
+ *     LSE[b,h] = ln sum_t exp(scale * q[b,h,:] . K[b,t,k,:])
+ * The keys of each sequence are cut into partitions of `chunk_tokens` keys.
+ * Pass 1 (partition kernel) gives every partition its row max m_p (raw q.k
+ * units), row sum l_p = sum_t exp(scale*(x_t - m_p)) and NORMALISED partial
+ * O_p (fa4_splitk_combine_write, second paragraph). Pass 2 merges them with
+ * the combine of fa4_splitk_combine_write (first paragraph):
+ *     Gmax = max_p m_p,  e_p = exp2((m_p - Gmax) * c),  c = scale * log2(e)
+ *     Gsum = sum_p l_p e_p,  w_p = l_p e_p / Gsum,  O = sum_p w_p O_p
+ * and casts O to bf16 (round to nearest even). LSE = scale*Gmax + ln Gsum.
+ * GQA heads that share a kv head are processed together so K/V are read once
+ * (FA4Config, BM_eff). The cache is contiguous or paged (FA4Config,
+ * v_row_major: a block-indirected paged cache). In the latent-shared layout V
+ * is the first ov_depth columns of each K row (FA4Config, shared_kv_cols and
+ * rope_depth: K = 512 non-rotary columns followed by 64 rotary ones).
+ *
+ * Conventions for every entry point:
+ *  - Pointers named as device pointers must be device (or managed) memory of
+ *    the current HIP device; the caller owns all memory. The library never
+ *    allocates, frees or retains a pointer after the call returns.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
+ *    No call synchronises with the host.
+ *  - Return value: DA_OK (0) or a negative da_status. On error nothing has
+ *    been enqueued (except DA_EHIP, where a launch failed), and
+ *    da_last_error() returns a message for the calling thread.
+ */
+#ifndef DECODE_ATTN_H
+#define DECODE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DA_OK = 0,
+  DA_EINVAL = -1,        /* bad argument: null pointer, bad size, inconsistent shape */
+  DA_EUNSUPPORTED = -2,  /* well-formed problem this build has no kernel for */
+  DA_EWORKSPACE = -3,    /* workspace pointer null/misaligned or smaller than needed */
+  DA_EHIP = -4           /* a HIP runtime call or kernel launch failed */
+} da_status;
+
+typedef enum { DA_F32 = 0, DA_BF16 = 1 } da_dtype;
+
+typedef enum {
+  DA_KERNEL_AUTO = 0,    /* library's choice */
+  DA_KERNEL_FMA = 1,     /* vector-ALU partition kernel (fp32 or bf16, group <= 16, depth 128) */
+  DA_KERNEL_MFMA = 2     /* matrix-core partition kernel (bf16 only) */
+} da_kernel;
+
+/* Shape and layout of one decode step. All sizes are element counts. */
+typedef struct da_problem {
+  int32_t batch;             /* B >= 1 */
+  int32_t num_q_heads;       /* Hq >= 1 */
+  int32_t num_kv_heads;      /* Hkv >= 1, Hq % Hkv == 0; g = Hq / Hkv (FA4Config, group) */
+  int32_t qk_depth;          /* Dqk: q/K row length */
+  int32_t ov_depth;          /* Dv: V row length and output depth */
+  int32_t dtype;             /* da_dtype of q, K and V; the output is always bf16 */
+  int32_t page_size;         /* 0 = contiguous cache; > 0 = paged cache, keys per page */
+  int32_t max_pages_per_seq; /* paged: row stride of page_table (entries per sequence) */
+  int32_t num_pages;         /* paged: pages in the pool (page_table entries must be < this) */
+  int32_t kv_capacity;       /* contiguous: key slots per sequence in the cache */
+  int32_t max_seq_len;       /* host-side upper bound of seq_lens[]; sizes the grid */
+  int32_t v_is_k_prefix;     /* 1 = latent-shared: V[t] = K[t][0:ov_depth], v_cache unused */
+  int32_t kernel;            /* da_kernel: AUTO, or force a partition-kernel family */
+} da_problem;
+
+/*
+ * Layouts (row-major, dense):
+ *   q          [B][Hq][Dqk]                        dtype
+ *   k_cache    contiguous: [B][kv_capacity][Hkv][Dqk]; paged: [num_pages][page_size][Hkv][Dqk]
+ *   v_cache    same as k_cache with Dv (ignored when v_is_k_prefix)
+ *   page_table int32 [B][max_pages_per_seq]; key t of sequence b is slot t % page_size of
+ *              page page_table[b][t / page_size]. Entries at or beyond ceil(L_b / page_size)
+ *              are never read (padding may be any value, e.g. -1).
+ *   seq_lens   int32 [B]; L_b keys are attended (no mask). Values < 0 count as 0; values above
+ *              max_seq_len (or kv_capacity, contiguous) are clamped to it.
+ *   out        bf16 [B][Hq][Dv]
+ *   lse_out    fp32 [B][Hq] natural-log LSE (optional); -inf for L_b == 0
+ *   o_f32_out  fp32 [B][Hq][Dv] O before the bf16 cast (optional); 0 for L_b == 0
+ *   part_ml    fp32 [B][Hq][max_splits][2] partition (m_p, l_p); m_p in raw q.k units
+ *   part_o     fp32 [B][Hq][max_splits][Dv] normalised partition output O_p
+ * Partition p of sequence b covers keys [p*chunk_tokens, min((p+1)*chunk_tokens, L_b));
+ * sequence b has P_b = ceil(L_b / chunk_tokens) partitions (at most max_splits).
+ * A page_table entry outside [0, num_pages) is clamped into range (no fault; the
+ * output of that sequence is then unspecified).
+ */
+
+/* DA_OK if a kernel exists for this problem, else DA_EINVAL / DA_EUNSUPPORTED with a
+ * message (FA4Config, supported). Supported: dtype f32 or bf16 with Dqk == Dv == 128
+ * and g <= 16 (f32 runs the vector-ALU kernel); bf16 latent-shared Dqk == 576,
+ * Dv == 512, Hkv == 1. */
+int da_supported(const da_problem* p);
+
+/* Split selection (FA4Config, with_splitk: partitions of the K/V sequence).
+ * num_splits > 0: chunk_tokens = ceil(max_seq_len / num_splits) rounded up to a multiple
+ * of the key tile (32) and of page_size when that is a multiple of 32.
+ * num_splits == 0: automatic choice for the device's num_cus compute units
+ * (num_cus <= 0: query the current device). Writes chunk_tokens and
+ * max_splits = ceil(max_seq_len / chunk_tokens) (>= 1). */
+int da_choose_splits(const da_problem* p, int32_t num_splits, int32_t num_cus,
+                     int32_t* chunk_tokens, int32_t* max_splits);
+
+/* Bytes of workspace decode_attn_splitk needs for this problem and num_splits
+ * (same num_splits / num_cus rule as da_choose_splits with num_cus queried). */
+int da_workspace_bytes(const da_problem* p, int32_t num_splits, size_t* bytes);
+
+/* The whole decode step: partition kernel, then LSE combine.
+ * q, k_cache, v_cache, page_table (NULL iff page_size == 0), seq_lens: device, read only.
+ * scale: finite and > 0 (softmax scale, e.g. 1/sqrt(Dqk)).
+ * num_splits: 0 = automatic, else the fixed number of partitions (see da_choose_splits).
+ * out: device bf16 [B][Hq][Dv]; lse_out, o_f32_out: optional device outputs (NULL = skip).
+ * workspace: device, 256-byte aligned, at least da_workspace_bytes() bytes; its
+ * contents on entry do not matter and are clobbered. */
+int decode_attn_splitk(const da_problem* p, const void* q, const void* k_cache,
+                       const void* v_cache, const int32_t* page_table, const int32_t* seq_lens,
+                       float scale, int32_t num_splits, void* out, float* lse_out,
+                       float* o_f32_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Pass 1 only (fa4_splitk_combine_write, second paragraph: each partition stages its
+ * normalised O and its (max, sum)). Writes part_ml / part_o (device, layouts above) for
+ * p < P_b; entries for p >= P_b are not written. chunk_tokens must be a positive multiple
+ * of 32 and max_splits >= ceil(max_seq_len / chunk_tokens). */
+int decode_attn_partition(const da_problem* p, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* page_table,
+                          const int32_t* seq_lens, float scale, int32_t chunk_tokens,
+                          int32_t max_splits, float* part_o, float* part_ml, void* stream);
+
+/* Pass 2 only: the LSE combine of fa4_splitk_combine_write (first paragraph) over the
+ * P_b partials of every row, then the bf16 cast. Reads part_ml / part_o entries p < P_b
+ * (device). A partition with l_p == 0 has weight 0. Writes out (required), lse_out and
+ * o_f32_out (optional). Same chunk_tokens / max_splits rules as decode_attn_partition. */
+int decode_attn_combine(const da_problem* p, const int32_t* seq_lens, float scale,
+                        int32_t chunk_tokens, int32_t max_splits, const float* part_o,
+                        const float* part_ml, void* out, float* lse_out, float* o_f32_out,
+                        void* stream);
+
+/* Measurement probes (not part of attention). da_read_probe streams n_bytes
+ * (a positive multiple of 16) from device src with 16-byte loads and writes one
+ * fp32 per workgroup (at most 4096) into device sink, so the reads cannot be
+ * elided. da_copy_probe copies n_bytes (multiple of 16) from src to dst (device,
+ * non-overlapping): a plain copy of known size against which hardware traffic
+ * counters are calibrated. */
+int da_read_probe(const void* src, size_t n_bytes, float* sink, void* stream);
+int da_copy_probe(const void* src, void* dst, size_t n_bytes, void* stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* da_last_error(void);
+
+/* Library version string. */
+const char* da_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DECODE_ATTN_H */

@@ -1,0 +1,154 @@
+"""Thin PyTorch binding of the C ABI: argument marshalling only.
+
+Every step of the decode step runs in the HIP library; this module checks
+tensor shapes/devices, passes ``data_ptr()`` values and the current HIP
+stream, and allocates outputs and the workspace with PyTorch.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import DaProblem, check
+
+_DTYPES = {torch.float32: _lib.DA_F32, torch.bfloat16: _lib.DA_BF16}
+_KERNELS = {"auto": _lib.DA_KERNEL_AUTO, "fma": _lib.DA_KERNEL_FMA, "mfma": _lib.DA_KERNEL_MFMA}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def make_problem(q, k_cache, v_cache=None, page_table=None, *, page_size=0, max_seq_len=None,
+                 v_is_k_prefix=False, ov_depth=None, kernel="auto", num_pages=None) -> DaProblem:
+    """Describe one decode step from its tensors (shapes as in include/decode_attn.h)."""
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [B, Hq, Dqk] and k_cache 4-D")
+    if q.dtype not in _DTYPES or k_cache.dtype != q.dtype or (v_cache is not None and v_cache.dtype != q.dtype):
+        raise ValueError("q, k_cache and v_cache must share dtype float32 or bfloat16")
+    B, Hq, Dqk = q.shape
+    Hkv = k_cache.shape[2]
+    if k_cache.shape[3] != Dqk:
+        raise ValueError("k_cache depth must equal q depth")
+    if v_is_k_prefix:
+        Dv = int(ov_depth if ov_depth is not None else Dqk)
+    else:
+        if v_cache is None:
+            raise ValueError("v_cache is required unless v_is_k_prefix")
+        Dv = v_cache.shape[3]
+        if tuple(v_cache.shape[:3]) != tuple(k_cache.shape[:3]):
+            raise ValueError("v_cache must match k_cache in its first three dimensions")
+    p = DaProblem()
+    p.batch, p.num_q_heads, p.num_kv_heads, p.qk_depth, p.ov_depth = B, Hq, Hkv, Dqk, Dv
+    p.dtype = _DTYPES[q.dtype]
+    p.kernel = _KERNELS[kernel]
+    p.v_is_k_prefix = 1 if v_is_k_prefix else 0
+    if page_table is not None:
+        if page_size <= 0 or k_cache.shape[1] != page_size:
+            raise ValueError("paged cache: page_size must be > 0 and equal k_cache.shape[1]")
+        p.page_size = page_size
+        p.max_pages_per_seq = page_table.shape[1]
+        p.num_pages = k_cache.shape[0] if num_pages is None else num_pages
+        cap = page_table.shape[1] * page_size
+    else:
+        p.page_size = 0
+        if k_cache.shape[0] != B:
+            raise ValueError("contiguous cache must be [B, L_cap, Hkv, Dqk]")
+        p.kv_capacity = k_cache.shape[1]
+        cap = k_cache.shape[1]
+    p.max_seq_len = cap if max_seq_len is None else int(max_seq_len)
+    return p
+
+
+def _check_tensors(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous and on the GPU")
+
+
+def choose_splits(problem: DaProblem, num_splits=0, num_cus=0):
+    lib = _lib.load()
+    C, P = ctypes.c_int32(), ctypes.c_int32()
+    check(lib.da_choose_splits(ctypes.byref(problem), num_splits, num_cus, ctypes.byref(C), ctypes.byref(P)))
+    return C.value, P.value
+
+
+def workspace_bytes(problem: DaProblem, num_splits=0):
+    lib = _lib.load()
+    n = ctypes.c_size_t()
+    check(lib.da_workspace_bytes(ctypes.byref(problem), num_splits, ctypes.byref(n)))
+    return n.value
+
+
+def decode_attn(q, k_cache, v_cache, page_table, seq_lens, scale, num_splits=0, *, page_size=0,
+                max_seq_len=None, v_is_k_prefix=False, ov_depth=None, out=None, lse=None, o32=None,
+                return_lse=False, return_o32=False, workspace=None, kernel="auto"):
+    """The whole split-K decode step. Returns out (bf16 [B, Hq, Dv]) or (out, lse, o32)."""
+    lib = _lib.load()
+    prob = make_problem(q, k_cache, v_cache, page_table, page_size=page_size, max_seq_len=max_seq_len,
+                        v_is_k_prefix=v_is_k_prefix, ov_depth=ov_depth, kernel=kernel)
+    _check_tensors(q, k_cache, v_cache, page_table, seq_lens)
+    B, Hq, Dv = prob.batch, prob.num_q_heads, prob.ov_depth
+    if out is None:
+        out = torch.empty((B, Hq, Dv), dtype=torch.bfloat16, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if return_o32 and o32 is None:
+        o32 = torch.empty((B, Hq, Dv), dtype=torch.float32, device=q.device)
+    need = workspace_bytes(prob, num_splits)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    check(lib.decode_attn_splitk(ctypes.byref(prob), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+                                 _ptr(seq_lens), float(scale), int(num_splits), _ptr(out), _ptr(lse), _ptr(o32),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
+    if return_lse or return_o32:
+        return out, lse, o32
+    return out
+
+
+def partition(q, k_cache, v_cache, page_table, seq_lens, scale, chunk_tokens, max_splits, *, page_size=0,
+              max_seq_len=None, v_is_k_prefix=False, ov_depth=None, part_o=None, part_ml=None, kernel="auto"):
+    """Pass 1 only. Returns (part_o [B,Hq,P,Dv], part_ml [B,Hq,P,2]) fp32."""
+    lib = _lib.load()
+    prob = make_problem(q, k_cache, v_cache, page_table, page_size=page_size, max_seq_len=max_seq_len,
+                        v_is_k_prefix=v_is_k_prefix, ov_depth=ov_depth, kernel=kernel)
+    _check_tensors(q, k_cache, v_cache, page_table, seq_lens)
+    B, Hq, Dv = prob.batch, prob.num_q_heads, prob.ov_depth
+    if part_o is None:
+        part_o = torch.zeros((B, Hq, max_splits, Dv), dtype=torch.float32, device=q.device)
+    if part_ml is None:
+        part_ml = torch.zeros((B, Hq, max_splits, 2), dtype=torch.float32, device=q.device)
+    check(lib.decode_attn_partition(ctypes.byref(prob), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+                                    _ptr(seq_lens), float(scale), int(chunk_tokens), int(max_splits),
+                                    _ptr(part_o), _ptr(part_ml), _stream()))
+    return part_o, part_ml
+
+
+def combine(problem: DaProblem, seq_lens, scale, chunk_tokens, max_splits, part_o, part_ml, *, out=None,
+            lse=None, o32=None):
+    """Pass 2 only (the LSE combine). Returns (out bf16, lse fp32, o32 fp32)."""
+    lib = _lib.load()
+    _check_tensors(seq_lens, part_o, part_ml)
+    B, Hq, Dv = problem.batch, problem.num_q_heads, problem.ov_depth
+    dev = part_o.device
+    out = torch.empty((B, Hq, Dv), dtype=torch.bfloat16, device=dev) if out is None else out
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if lse is None else lse
+    o32 = torch.empty((B, Hq, Dv), dtype=torch.float32, device=dev) if o32 is None else o32
+    check(lib.decode_attn_combine(ctypes.byref(problem), _ptr(seq_lens), float(scale), int(chunk_tokens),
+                                  int(max_splits), _ptr(part_o), _ptr(part_ml), _ptr(out), _ptr(lse), _ptr(o32),
+                                  _stream()))
+    return out, lse, o32
+
+
+def case_call(case, device="cuda", **kw):
+    """Run a lse_combine_amd.inputs.Case already moved to ``device`` (see ``to_device``)."""
+    return decode_attn(case.q, case.k_cache, case.v_cache, case.page_table, case.seq_lens, case.scale,
+                       case.num_splits, page_size=case.page_size, v_is_k_prefix=case.v_is_k_prefix,
+                       ov_depth=case.ov_depth, **kw)

@@ -1,0 +1,372 @@
+// C ABI of the split-KV decode-attention library: validation, split selection,
+// workspace sizing and the launches of the two passes on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "da_internal.h"
+#include "decode_attn.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return DA_OK;
+}
+
+enum Variant { kVarFma = 0, kVarMfma128 = 1, kVarLatent = 2 };
+
+constexpr int kTileKeys = 32;  // key tile of every partition kernel; chunks are multiples of it
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int device_num_cus() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// Shape checks shared by every entry point; picks the partition-kernel family.
+int check_problem(const da_problem* p, Variant* var) {
+  if (!p) return fail(DA_EINVAL, "problem is NULL");
+  if (p->batch < 1 || p->batch > 65535) return fail(DA_EINVAL, "batch must be in [1, 65535] (got %d)", p->batch);
+  if (p->num_q_heads < 1 || p->num_kv_heads < 1 || p->num_kv_heads > 65535)
+    return fail(DA_EINVAL, "num_q_heads and num_kv_heads must be >= 1 (got %d, %d)", p->num_q_heads, p->num_kv_heads);
+  if (p->num_q_heads % p->num_kv_heads)
+    return fail(DA_EINVAL, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)", p->num_q_heads, p->num_kv_heads);
+  if (p->qk_depth < 1 || p->ov_depth < 1) return fail(DA_EINVAL, "depths must be >= 1");
+  if (p->dtype != DA_F32 && p->dtype != DA_BF16) return fail(DA_EINVAL, "dtype must be DA_F32 or DA_BF16 (got %d)", p->dtype);
+  if (p->page_size < 0) return fail(DA_EINVAL, "page_size must be >= 0");
+  if (p->max_seq_len < 0) return fail(DA_EINVAL, "max_seq_len must be >= 0");
+  if (p->page_size > 0) {
+    if (p->num_pages < 1) return fail(DA_EINVAL, "paged cache needs num_pages >= 1");
+    if ((int64_t)p->max_pages_per_seq * p->page_size < p->max_seq_len)
+      return fail(DA_EINVAL, "page table row (%d pages of %d) cannot hold max_seq_len %d keys", p->max_pages_per_seq,
+                  p->page_size, p->max_seq_len);
+  } else {
+    if (p->kv_capacity < 1) return fail(DA_EINVAL, "contiguous cache needs kv_capacity >= 1");
+  }
+  if (p->v_is_k_prefix && p->ov_depth > p->qk_depth)
+    return fail(DA_EINVAL, "latent-shared V (ov_depth %d) must fit in the K row (qk_depth %d)", p->ov_depth, p->qk_depth);
+  if (p->kernel < DA_KERNEL_AUTO || p->kernel > DA_KERNEL_MFMA) return fail(DA_EINVAL, "unknown kernel hint %d", p->kernel);
+  const int g = p->num_q_heads / p->num_kv_heads;
+
+  if (p->qk_depth == 576 && p->ov_depth == 512) {
+    if (p->dtype != DA_BF16 || !p->v_is_k_prefix || p->num_kv_heads != 1 || g % 16 != 0 || p->kernel == DA_KERNEL_FMA)
+      return fail(DA_EUNSUPPORTED,
+                  "depth 576/512 is supported only as bf16 latent-shared attention with one kv head and a multiple "
+                  "of 16 q heads (matrix-core kernel)");
+    *var = kVarLatent;
+    return fail(DA_EUNSUPPORTED, "latent-shared 576/512 kernel is not built into this version");
+  }
+  if (p->qk_depth != 128 || p->ov_depth != 128)
+    return fail(DA_EUNSUPPORTED, "supported depths: 128/128, or 576/512 latent-shared (got %d/%d)", p->qk_depth,
+                p->ov_depth);
+  if (g > 16) return fail(DA_EUNSUPPORTED, "depth-128 kernels fuse at most 16 q heads per kv head (group %d)", g);
+  if (p->dtype == DA_F32) {
+    if (p->kernel == DA_KERNEL_MFMA) return fail(DA_EUNSUPPORTED, "the matrix-core kernel needs bf16 inputs");
+    *var = kVarFma;
+  } else if (p->kernel == DA_KERNEL_FMA || (p->kernel == DA_KERNEL_AUTO && g == 1)) {
+    *var = kVarFma;
+  } else {
+    *var = kVarMfma128;
+  }
+  return DA_OK;
+}
+
+int chunk_unit(const da_problem* p) {
+  if (p->page_size > 0 && p->page_size % kTileKeys == 0 && p->page_size <= 4096) return p->page_size;
+  return kTileKeys;
+}
+
+int page_mode(const da_problem* p) {
+  if (p->page_size == 0) return da::kContiguous;
+  return (p->page_size % kTileKeys == 0) ? da::kPagedAligned : da::kPagedGeneral;
+}
+
+// Workgroups of the partition kernel that fit on one compute unit at once.
+int wgs_per_cu(Variant v, int waves) {
+  if (v == kVarMfma128) return waves >= 8 ? 1 : 2;
+  return 2;
+}
+
+int choose(const da_problem* p, Variant var, int32_t num_splits, int cus, int32_t* chunk_out, int32_t* splits_out) {
+  if (num_splits < 0) return fail(DA_EINVAL, "num_splits must be >= 0 (0 = automatic)");
+  const int unit = chunk_unit(p);
+  const int64_t maxlen = p->max_seq_len > 0 ? p->max_seq_len : 1;
+  int64_t C;
+  if (num_splits > 0) {
+    C = ceil_div(maxlen, num_splits);
+  } else {
+    // Automatic: the host does not see seq_lens (no device sync), so it plans for an
+    // average length of max_seq_len / 2 and aims at about four rounds of workgroups
+    // over the whole chip; chunks stay within [256, 8192] keys.
+    const int slots = cus * wgs_per_cu(var, 4);
+    const int64_t est_units = (int64_t)p->batch * p->num_kv_heads * ((maxlen + 1) / 2);
+    C = ceil_div(est_units, 4LL * slots);
+    if (C < 256) C = 256;
+    if (C > 8192) C = 8192;
+  }
+  C = ceil_div(C, unit) * unit;
+  if (C > ceil_div(maxlen, unit) * unit) C = ceil_div(maxlen, unit) * unit;
+  if (C < unit) C = unit;
+  const int64_t P = ceil_div(maxlen, C);
+  if (C > INT32_MAX || P > INT32_MAX) return fail(DA_EINVAL, "split selection overflow");
+  *chunk_out = (int32_t)C;
+  *splits_out = (int32_t)P;
+  return DA_OK;
+}
+
+void ws_layout(const da_problem* p, int32_t max_splits, size_t* ml_off, size_t* o_off, size_t* total) {
+  const size_t rows = (size_t)p->batch * p->num_q_heads * (size_t)max_splits;
+  const size_t ml = (rows * 2 * sizeof(float) + 255) & ~(size_t)255;
+  const size_t o = (rows * (size_t)p->ov_depth * sizeof(float) + 255) & ~(size_t)255;
+  *ml_off = 0;
+  *o_off = ml;
+  *total = ml + o;
+}
+
+int check_split_args(const da_problem* p, int32_t chunk, int32_t max_splits) {
+  if (chunk <= 0 || chunk % kTileKeys) return fail(DA_EINVAL, "chunk_tokens must be a positive multiple of %d (got %d)", kTileKeys, chunk);
+  const int64_t maxlen = p->max_seq_len > 0 ? p->max_seq_len : 1;
+  if (max_splits < ceil_div(maxlen, chunk))
+    return fail(DA_EINVAL, "max_splits %d < ceil(max_seq_len %d / chunk_tokens %d)", max_splits, p->max_seq_len, chunk);
+  return DA_OK;
+}
+
+int check_inputs(const da_problem* p, const void* q, const void* k, const void* v, const int32_t* pt,
+                 const int32_t* lens) {
+  if (!q || !k || !lens) return fail(DA_EINVAL, "q, k_cache and seq_lens must be non-NULL");
+  if (!p->v_is_k_prefix && !v) return fail(DA_EINVAL, "v_cache must be non-NULL unless v_is_k_prefix");
+  if (p->page_size > 0 && !pt) return fail(DA_EINVAL, "page_table must be non-NULL for a paged cache");
+  if (p->page_size == 0 && pt) return fail(DA_EINVAL, "page_table must be NULL for a contiguous cache");
+  return DA_OK;
+}
+
+da::PartArgs part_args(const da_problem* p, const void* q, const void* k, const void* v, const int32_t* pt,
+                       const int32_t* lens, float scale, int32_t chunk, int32_t max_splits) {
+  da::PartArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = p->v_is_k_prefix ? k : v;
+  a.page_table = pt;
+  a.seq_lens = lens;
+  a.B = p->batch;
+  a.Hq = p->num_q_heads;
+  a.Hkv = p->num_kv_heads;
+  a.g = p->num_q_heads / p->num_kv_heads;
+  a.Dqk = p->qk_depth;
+  a.Dv = p->ov_depth;
+  a.v_row_len = p->v_is_k_prefix ? p->qk_depth : p->ov_depth;
+  a.page_size = p->page_size;
+  a.pt_stride = p->max_pages_per_seq;
+  a.num_pages = p->num_pages;
+  a.kv_capacity = p->kv_capacity;
+  a.max_seq_len = p->max_seq_len;
+  a.chunk = chunk;
+  a.max_splits = max_splits;
+  a.scale = scale;
+  a.c = scale * 1.4426950408889634f;
+  return a;
+}
+
+int launch_partition(const da_problem* p, Variant var, const da::PartArgs& a, hipStream_t s, int cus) {
+  (void)hipGetLastError();
+  hipError_t e;
+  const int pm = page_mode(p);
+  switch (var) {
+    case kVarFma:
+      e = da::launch_partition_fma(a, p->dtype == DA_F32 ? 0 : 1, pm, s);
+      break;
+    case kVarMfma128: {
+      const int64_t grid = (int64_t)a.B * a.Hkv * a.max_splits;
+      const int waves = grid < 2LL * cus ? 8 : 4;
+      e = da::launch_partition_mfma128(a, pm, waves, s);
+      break;
+    }
+    default:
+      e = da::launch_partition_latent(a, pm, s);
+      break;
+  }
+  if (e != hipSuccess) return fail(DA_EHIP, "partition kernel launch failed: %s", hipGetErrorString(e));
+  return DA_OK;
+}
+
+int launch_combine(const da_problem* p, const int32_t* lens, float scale, int32_t chunk, int32_t max_splits,
+                   const float* po, const float* pml, void* out, float* lse, float* o32, int skip_single,
+                   hipStream_t s) {
+  da::CombineArgs c;
+  memset(&c, 0, sizeof(c));
+  c.part_o = po;
+  c.part_ml = pml;
+  c.seq_lens = lens;
+  c.out = (uint16_t*)out;
+  c.lse = lse;
+  c.o32 = o32;
+  c.B = p->batch;
+  c.Hq = p->num_q_heads;
+  c.Dv = p->ov_depth;
+  c.chunk = chunk;
+  c.max_splits = max_splits;
+  c.max_seq_len = p->max_seq_len;
+  c.kv_cap_clamp = p->page_size == 0 ? p->kv_capacity : 0;
+  c.skip_single = skip_single;
+  c.scale = scale;
+  c.c = scale * 1.4426950408889634f;
+  (void)hipGetLastError();
+  const hipError_t e = da::launch_combine(c, s);
+  if (e != hipSuccess) return fail(DA_EHIP, "combine kernel launch failed: %s", hipGetErrorString(e));
+  return DA_OK;
+}
+
+int check_scale(float scale) {
+  if (!std::isfinite(scale) || scale <= 0.f) return fail(DA_EINVAL, "scale must be finite and > 0");
+  return DA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int da_supported(const da_problem* p) {
+  Variant v;
+  const int r = check_problem(p, &v);
+  return r == DA_OK ? ok() : r;
+}
+
+int da_choose_splits(const da_problem* p, int32_t num_splits, int32_t num_cus, int32_t* chunk_tokens,
+                     int32_t* max_splits) {
+  Variant v;
+  int r = check_problem(p, &v);
+  if (r) return r;
+  if (!chunk_tokens || !max_splits) return fail(DA_EINVAL, "output pointers must be non-NULL");
+  r = choose(p, v, num_splits, num_cus > 0 ? num_cus : device_num_cus(), chunk_tokens, max_splits);
+  return r ? r : ok();
+}
+
+int da_workspace_bytes(const da_problem* p, int32_t num_splits, size_t* bytes) {
+  Variant v;
+  int r = check_problem(p, &v);
+  if (r) return r;
+  if (!bytes) return fail(DA_EINVAL, "bytes must be non-NULL");
+  int32_t C, P;
+  r = choose(p, v, num_splits, device_num_cus(), &C, &P);
+  if (r) return r;
+  size_t a, b;
+  ws_layout(p, P, &a, &b, bytes);
+  return ok();
+}
+
+int decode_attn_splitk(const da_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* page_table, const int32_t* seq_lens, float scale, int32_t num_splits,
+                       void* out, float* lse_out, float* o_f32_out, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  Variant var;
+  int r = check_problem(p, &var);
+  if (r) return r;
+  if ((r = check_inputs(p, q, k_cache, v_cache, page_table, seq_lens))) return r;
+  if ((r = check_scale(scale))) return r;
+  if (!out) return fail(DA_EINVAL, "out must be non-NULL");
+  const int cus = device_num_cus();
+  int32_t C, P;
+  if ((r = choose(p, var, num_splits, cus, &C, &P))) return r;
+  size_t ml_off, o_off, need;
+  ws_layout(p, P, &ml_off, &o_off, &need);
+  if (!workspace || ((uintptr_t)workspace & 255))
+    return fail(DA_EWORKSPACE, "workspace must be non-NULL and 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(DA_EWORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  float* pml = (float*)((char*)workspace + ml_off);
+  float* po = (float*)((char*)workspace + o_off);
+  hipStream_t s = (hipStream_t)stream;
+  da::PartArgs a = part_args(p, q, k_cache, v_cache, page_table, seq_lens, scale, C, P);
+  a.part_o = po;
+  a.part_ml = pml;
+  a.out = (uint16_t*)out;
+  a.lse = lse_out;
+  a.o32 = o_f32_out;
+  a.direct_single = 1;
+  if ((r = launch_partition(p, var, a, s, cus))) return r;
+  if ((r = launch_combine(p, seq_lens, scale, C, P, po, pml, out, lse_out, o_f32_out, 1, s))) return r;
+  return ok();
+}
+
+int decode_attn_partition(const da_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* page_table, const int32_t* seq_lens, float scale, int32_t chunk_tokens,
+                          int32_t max_splits, float* part_o, float* part_ml, void* stream) {
+  Variant var;
+  int r = check_problem(p, &var);
+  if (r) return r;
+  if ((r = check_inputs(p, q, k_cache, v_cache, page_table, seq_lens))) return r;
+  if ((r = check_scale(scale))) return r;
+  if ((r = check_split_args(p, chunk_tokens, max_splits))) return r;
+  if (!part_o || !part_ml) return fail(DA_EINVAL, "part_o and part_ml must be non-NULL");
+  da::PartArgs a = part_args(p, q, k_cache, v_cache, page_table, seq_lens, scale, chunk_tokens, max_splits);
+  a.part_o = part_o;
+  a.part_ml = part_ml;
+  a.direct_single = 0;
+  if ((r = launch_partition(p, var, a, (hipStream_t)stream, device_num_cus()))) return r;
+  return ok();
+}
+
+int decode_attn_combine(const da_problem* p, const int32_t* seq_lens, float scale, int32_t chunk_tokens,
+                        int32_t max_splits, const float* part_o, const float* part_ml, void* out, float* lse_out,
+                        float* o_f32_out, void* stream) {
+  Variant var;
+  int r = check_problem(p, &var);
+  if (r && r != DA_EUNSUPPORTED) return r;
+  if (p->ov_depth != 128 && p->ov_depth != 512)
+    return fail(DA_EUNSUPPORTED, "combine supports ov_depth 128 or 512 (got %d)", p->ov_depth);
+  if (!seq_lens || !part_o || !part_ml || !out) return fail(DA_EINVAL, "seq_lens, part_o, part_ml and out must be non-NULL");
+  if ((r = check_scale(scale))) return r;
+  if ((r = check_split_args(p, chunk_tokens, max_splits))) return r;
+  if ((r = launch_combine(p, seq_lens, scale, chunk_tokens, max_splits, part_o, part_ml, out, lse_out, o_f32_out, 0,
+                          (hipStream_t)stream)))
+    return r;
+  return ok();
+}
+
+int da_read_probe(const void* src, size_t n_bytes, float* sink, void* stream) {
+  if (!src || !sink || n_bytes == 0 || n_bytes % 16) return fail(DA_EINVAL, "read probe needs src, sink and n_bytes % 16 == 0");
+  (void)hipGetLastError();
+  const hipError_t e = da::launch_read_probe(src, n_bytes, sink, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(DA_EHIP, "read probe launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int da_copy_probe(const void* src, void* dst, size_t n_bytes, void* stream) {
+  if (!src || !dst || n_bytes == 0 || n_bytes % 16) return fail(DA_EINVAL, "copy probe needs src, dst and n_bytes % 16 == 0");
+  (void)hipGetLastError();
+  const hipError_t e = da::launch_copy_probe(src, dst, n_bytes, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(DA_EHIP, "copy probe launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char* da_last_error(void) { return g_err; }
+
+const char* da_version(void) { return "decode_attn 0.1 (gfx950)"; }
+
+}  // extern "C"

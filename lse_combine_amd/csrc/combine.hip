@@ -1,0 +1,114 @@
+// Split-K pass 2: the log-sum-exp combine (fa4_splitk_combine_write, first paragraph),
+// plus the measurement probes.
+//
+// One thread per (row, 16-byte depth slice): as on the pages each thread forms the
+// per-row weights itself (no cross-lane exchange) and owns a band of depth columns;
+// the threads of a row together cover the whole depth, the analogue of the pages'
+// reduce-scatter band ownership. Rows are (sequence, q head) pairs; a row reads the
+// (m_p, l_p) and normalised O_p of its P_b partitions:
+//     Gmax = max_p m_p,   e_p = l_p * exp2((m_p - Gmax) * c),   Gsum = sum_p e_p
+//     O = sum_p e_p O_p / Gsum   (= sum_p w_p O_p with w_p = e_p / Gsum)
+//     LSE = scale * Gmax + ln Gsum,   out = bf16(O) (round to nearest even)
+// Partitions with l_p == 0 are skipped (weight 0); a row with no keys gets O = 0 and
+// LSE = -inf.
+#include "da_device.h"
+
+namespace da {
+namespace {
+
+template <int DV>
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  constexpr int TPR = DV / 4;          // threads per row
+  constexpr int RPB = 256 / TPR;       // rows per block
+  const int tid = threadIdx.x;
+  const int r_in = tid / TPR, ch = tid % TPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + r_in;
+  if (row >= (int64_t)a.B * a.Hq) return;
+  const int b = (int)(row / a.Hq);
+  int L = a.seq_lens[b];
+  L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
+  if (a.kv_cap_clamp > 0 && L > a.kv_cap_clamp) L = a.kv_cap_clamp;
+  const int P_b = min((L + a.chunk - 1) / a.chunk, a.max_splits);
+  if (a.skip_single && P_b == 1) return;
+
+  const float* ml = a.part_ml + row * a.max_splits * 2;
+  const float* po = a.part_o + row * a.max_splits * DV + ch * 4;
+  float M = -INFINITY;
+  for (int p = 0; p < P_b; ++p) {
+    const float2 v = *(const float2*)(ml + 2 * p);
+    if (v.y > 0.f) M = fmaxf(M, v.x);
+  }
+  float Gs = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int p = 0; p < P_b; ++p) {
+    const float2 v = *(const float2*)(ml + 2 * p);
+    if (v.y > 0.f) {
+      const float e = v.y * exp2_fast((v.x - M) * a.c);
+      Gs += e;
+      acc += e * *(const f32x4*)(po + (int64_t)p * DV);
+    }
+  }
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  float lse = -INFINITY;
+  if (Gs > 0.f) {
+    o = acc * (1.f / Gs);
+    lse = a.scale * M + logf(Gs);
+  }
+  u32x2 pk;
+  pk[0] = pack_bf16x2(o[0], o[1]);
+  pk[1] = pack_bf16x2(o[2], o[3]);
+  *(u32x2*)(a.out + row * DV + ch * 4) = pk;
+  if (a.o32) *(f32x4*)(a.o32 + row * DV + ch * 4) = o;
+  if (a.lse && ch == 0) a.lse[row] = lse;
+}
+
+__global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* src, size_t n16, float* sink) {
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
+    acc ^= __builtin_nontemporal_load(src + i);
+  }
+  uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  for (int o = 32; o >= 1; o >>= 1) x ^= __shfl_xor(x, o);
+  if ((threadIdx.x & 63) == 0 && x == 0x7fc00001u) sink[blockIdx.x] = 1.f;  // keeps the loads alive
+}
+
+__global__ __launch_bounds__(256) void copy_probe_kernel(const u32x4* src, u32x4* dst, size_t n16) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+}  // namespace
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
+  const int64_t rows = (int64_t)a.B * a.Hq;
+  if (a.Dv == 128) {
+    dim3 grid((unsigned)((rows + 7) / 8));
+    hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(256), 0, s, a);
+  } else {
+    dim3 grid((unsigned)((rows + 1) / 2));
+    hipLaunchKernelGGL(combine_kernel<512>, grid, dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_read_probe(const void* src, size_t n_bytes, float* sink, hipStream_t s) {
+  const size_t n16 = n_bytes / 16;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks == 0) blocks = 1;
+  hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const u32x4*)src, n16, sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_probe(const void* src, void* dst, size_t n_bytes, hipStream_t s) {
+  const size_t n16 = n_bytes / 16;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks == 0) blocks = 1;
+  hipLaunchKernelGGL(copy_probe_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const u32x4*)src, (u32x4*)dst, n16);
+  return hipGetLastError();
+}
+
+}  // namespace da

@@ -1,0 +1,90 @@
+// Device-side helpers shared by the partition and combine kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "da_internal.h"
+
+namespace da {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define DA_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// fp32 -> bf16 bits, round to nearest even (hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Sequence length actually attended: negative -> 0, clamped to the grid's bound and,
+// for a contiguous cache, to its capacity.
+__device__ __forceinline__ int attended_len(const PartArgs& a, int b, bool contiguous) {
+  int L = a.seq_lens[b];
+  L = L < 0 ? 0 : L;
+  L = L > a.max_seq_len ? a.max_seq_len : L;
+  if (contiguous && L > a.kv_capacity) L = a.kv_capacity;
+  return L;
+}
+
+// Cache row (token slot) of key t of sequence b.
+template <int PM>
+__device__ __forceinline__ int64_t key_row(const PartArgs& a, int b, int t) {
+  if (PM == kContiguous) return (int64_t)b * a.kv_capacity + t;
+  const int pi = t / a.page_size;
+  int page = a.page_table[(int64_t)b * a.pt_stride + pi];
+  page = page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
+  return (int64_t)page * a.page_size + (t - pi * a.page_size);
+}
+
+// Store one float4 of a finished (head, depth) unit: either the final outputs of a
+// single-partition row or the normalised partial of partition p.
+__device__ __forceinline__ void store_unit(const PartArgs& a, int b, int hq, int p, bool direct,
+                                           int d0, f32x4 o, float M, float Lsum, bool write_ml) {
+  const int64_t row = (int64_t)b * a.Hq + hq;
+  if (direct) {
+    u32x2 pk;
+    pk[0] = pack_bf16x2(o[0], o[1]);
+    pk[1] = pack_bf16x2(o[2], o[3]);
+    *(u32x2*)(a.out + row * a.Dv + d0) = pk;
+    if (a.o32) *(f32x4*)(a.o32 + row * a.Dv + d0) = o;
+    if (write_ml && a.lse) a.lse[row] = a.scale * M + logf(Lsum);
+  } else {
+    const int64_t pr = row * a.max_splits + p;
+    *(f32x4*)(a.part_o + pr * a.Dv + d0) = o;
+    if (write_ml) {
+      float2 ml;
+      ml.x = M;
+      ml.y = Lsum;
+      *(float2*)(a.part_ml + pr * 2) = ml;
+    }
+  }
+}
+
+}  // namespace da

@@ -1,0 +1,57 @@
+// Internal declarations shared by the host API and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace da {
+
+enum PageMode : int {
+  kContiguous = 0,   // row of key t in sequence b = b * kv_capacity + t
+  kPagedAligned = 1, // paged with page_size % 32 == 0: a 32-key tile never crosses a page
+  kPagedGeneral = 2  // paged, any page_size: per-key page lookup
+};
+
+// Everything the partition kernels need; passed by value as the kernel argument.
+struct PartArgs {
+  const void* q;            // [B][Hq][Dqk]
+  const void* k;            // cache rows of Dqk elements, see key_row()
+  const void* v;            // cache rows of v_row_len elements (== k when V is a K prefix)
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  float* part_o;            // [B][Hq][max_splits][Dv]
+  float* part_ml;           // [B][Hq][max_splits][2]
+  uint16_t* out;            // bf16 [B][Hq][Dv]; written directly by single-partition rows
+  float* lse;               // optional
+  float* o32;               // optional
+  int32_t B, Hq, Hkv, g, Dqk, Dv;
+  int32_t v_row_len;        // elements between consecutive (row, kv-head) V vectors / Hkv
+  int32_t page_size, pt_stride, num_pages, kv_capacity, max_seq_len;
+  int32_t chunk, max_splits;
+  int32_t direct_single;    // 1: rows whose sequence has a single partition write out/lse/o32
+  float scale;              // softmax scale
+  float c;                  // scale * log2(e)
+};
+
+struct CombineArgs {
+  const float* part_o;
+  const float* part_ml;
+  const int32_t* seq_lens;
+  uint16_t* out;
+  float* lse;
+  float* o32;
+  int32_t B, Hq, Dv;
+  int32_t chunk, max_splits, max_seq_len, kv_cap_clamp;  // kv_cap_clamp: 0 = none
+  int32_t skip_single;      // 1: rows with one partition were finished by pass 1
+  float scale, c;
+};
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_partition_fma(const PartArgs& a, int dtype, int page_mode, hipStream_t s);
+hipError_t launch_partition_mfma128(const PartArgs& a, int page_mode, int waves, hipStream_t s);
+hipError_t launch_partition_latent(const PartArgs& a, int page_mode, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_read_probe(const void* src, size_t n_bytes, float* sink, hipStream_t s);
+hipError_t launch_copy_probe(const void* src, void* dst, size_t n_bytes, hipStream_t s);
+
+}  // namespace da

@@ -179,3 +179,13 @@ def workload(name: str, **overrides) -> Case:
     spec = dict(WORKLOADS[name])
     spec.update(overrides)
     return make_case(name, **spec)
+
+
+def to_device(case: Case, device="cuda") -> Case:
+    """Copy of ``case`` with every tensor moved to ``device`` (bit-identical values)."""
+    def mv(t):
+        return None if t is None else t.to(device).contiguous()
+    return Case(name=case.name, q=mv(case.q), k_cache=mv(case.k_cache), v_cache=mv(case.v_cache),
+                seq_lens=mv(case.seq_lens), page_table=mv(case.page_table), page_size=case.page_size,
+                scale=case.scale, num_splits=case.num_splits, v_is_k_prefix=case.v_is_k_prefix,
+                ov_depth=case.ov_depth, meta=dict(case.meta))

@@ -1,0 +1,61 @@
+"""Helpers for parity tests: run the oracle on a Case and compare with the GPU outputs.
+
+Tolerances (derived from the arithmetic; the fp32 partials and the bf16 cast):
+  out (bf16)   |gpu - O| <= 1e-2 + 1e-2 |O| elementwise
+  o32 (fp32)   max_d |gpu - O| <= 1e-5 max_d |O| per row
+  lse (fp32)   |gpu - LSE| <= 1e-5 |LSE|
+"""
+
+import numpy as np
+import torch
+
+from oracle import decode_attention_fp64
+
+OUT_ATOL, OUT_RTOL = 1e-2, 1e-2
+O32_ROW_RTOL = 1e-5
+LSE_RTOL = 1e-5
+
+
+def np32(t):
+    return None if t is None else t.detach().cpu().float().numpy()
+
+
+def oracle_for(case, batch_rows=None):
+    """fp64 oracle (O, LSE) for all sequences or the listed batch rows."""
+    q = np32(case.q)
+    k = np32(case.k_cache)
+    v = None if case.v_cache is None else np32(case.v_cache)
+    lens = case.seq_lens.cpu().numpy().astype(np.int64)
+    pt = None if case.page_table is None else case.page_table.cpu().numpy()
+    if batch_rows is not None:
+        q = q[batch_rows]
+        lens = lens[batch_rows]
+        if pt is not None:
+            pt = pt[batch_rows]
+        else:
+            k = k[batch_rows]
+            v = None if v is None else v[batch_rows]
+    lens = np.maximum(lens, 0)
+    return decode_attention_fp64(q, k, v, lens, case.scale, page_table=pt, page_size=case.page_size,
+                                 v_is_k_prefix=case.v_is_k_prefix, ov_depth=case.ov_depth)
+
+
+def assert_parity(out, lse, o32, O, LSE, o32_row_rtol=O32_ROW_RTOL, lse_rtol=LSE_RTOL, what=""):
+    out = np32(out).astype(np.float64)
+    err = np.abs(out - O)
+    bound = OUT_ATOL + OUT_RTOL * np.abs(O)
+    assert np.all(err <= bound), f"{what} bf16 out: max excess {(err - bound).max():.3e}"
+    if o32 is not None:
+        o = np32(o32).astype(np.float64)
+        row_err = np.abs(o - O).max(axis=-1)
+        row_ref = np.abs(O).max(axis=-1)
+        live = row_ref > 0
+        rel = row_err[live] / row_ref[live]
+        assert np.all(row_err[~live] == 0), f"{what} o32: nonzero output for an empty row"
+        assert rel.size == 0 or rel.max() <= o32_row_rtol, f"{what} o32 row-relative error {rel.max():.3e}"
+    if lse is not None:
+        l = np32(lse).astype(np.float64)
+        fin = np.isfinite(LSE)
+        assert np.array_equal(np.isneginf(l), np.isneginf(LSE)), f"{what} lse: -inf rows differ"
+        rel = np.abs(l[fin] - LSE[fin]) / np.abs(LSE[fin])
+        assert rel.size == 0 or rel.max() <= lse_rtol, f"{what} lse relative error {rel.max():.3e}"

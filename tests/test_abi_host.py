@@ -1,0 +1,151 @@
+"""Host-side checks of the C ABI (no GPU needed): symbols, validation, split
+selection, workspace sizing and error paths. Nothing here launches a kernel."""
+
+import ctypes
+import math
+
+import pytest
+
+from lse_combine_amd import _lib
+from lse_combine_amd._lib import (DA_EINVAL, DA_EUNSUPPORTED, DA_EWORKSPACE, DA_OK, DaProblem)
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def prob(**kw):
+    p = DaProblem()
+    base = dict(batch=2, num_q_heads=16, num_kv_heads=2, qk_depth=128, ov_depth=128, dtype=1, page_size=64,
+                max_pages_per_seq=64, num_pages=128, kv_capacity=0, max_seq_len=4096, v_is_k_prefix=0, kernel=0)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(p, k, v)
+    return p
+
+
+def test_exports_every_declared_function(lib):
+    names = _lib.header_functions()
+    assert {"decode_attn_splitk", "decode_attn_partition", "decode_attn_combine", "da_supported",
+            "da_choose_splits", "da_workspace_bytes", "da_last_error", "da_version",
+            "da_read_probe", "da_copy_probe"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert b"gfx950" in lib.da_version()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), DA_OK),
+    (dict(dtype=0), DA_OK),
+    (dict(num_q_heads=2, num_kv_heads=2), DA_OK),
+    (dict(num_q_heads=32, num_kv_heads=2), DA_OK),             # group 16
+    (dict(num_q_heads=34, num_kv_heads=2), DA_EUNSUPPORTED),   # group 17
+    (dict(num_q_heads=15, num_kv_heads=2), DA_EINVAL),         # not a multiple
+    (dict(qk_depth=64, ov_depth=64), DA_EUNSUPPORTED),
+    (dict(dtype=7), DA_EINVAL),
+    (dict(batch=0), DA_EINVAL),
+    (dict(page_size=-1), DA_EINVAL),
+    (dict(max_pages_per_seq=10), DA_EINVAL),                   # 10 * 64 < 4096
+    (dict(page_size=0, kv_capacity=0), DA_EINVAL),
+    (dict(page_size=0, kv_capacity=4096), DA_OK),
+    (dict(dtype=0, kernel=2), DA_EUNSUPPORTED),                # matrix cores need bf16
+    (dict(kernel=5), DA_EINVAL),
+    (dict(v_is_k_prefix=1, ov_depth=600, qk_depth=576), DA_EINVAL),
+    (dict(num_q_heads=128, num_kv_heads=2, qk_depth=576, ov_depth=512, v_is_k_prefix=1), DA_EUNSUPPORTED),
+])
+def test_supported(lib, kw, code):
+    p = prob(**kw)
+    assert lib.da_supported(ctypes.byref(p)) == code
+    if code != DA_OK:
+        assert lib.da_last_error()
+
+
+def test_supported_null(lib):
+    assert lib.da_supported(None) == DA_EINVAL
+    assert b"NULL" in lib.da_last_error()
+
+
+def splits(lib, p, n, cus=256):
+    C, P = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.da_choose_splits(ctypes.byref(p), n, cus, ctypes.byref(C), ctypes.byref(P)) == DA_OK
+    return C.value, P.value
+
+
+def test_fixed_splits_match_the_named_workloads(lib):
+    # tiny: L 1024, 4 partitions of 256 keys, contiguous
+    assert splits(lib, prob(batch=1, num_q_heads=1, num_kv_heads=1, dtype=0, page_size=0, kv_capacity=1024,
+                            max_seq_len=1024), 4) == (256, 4)
+    # GQA: L 4096, 8 splits
+    assert splits(lib, prob(batch=8, num_q_heads=32, num_kv_heads=8, page_size=0, kv_capacity=4096,
+                            max_seq_len=4096), 8) == (512, 8)
+    # long: L 131072, page 64, 64 splits
+    assert splits(lib, prob(batch=1, num_q_heads=32, num_kv_heads=4, max_pages_per_seq=2048,
+                            max_seq_len=131072), 64) == (2048, 64)
+
+
+@pytest.mark.parametrize("L,n,ps", [(1000, 3, 0), (1000, 3, 64), (77, 5, 0), (5000, 7, 16), (1, 1, 0),
+                                    (4096, 4096, 0), (32768, 0, 64), (131072, 0, 64), (100, 0, 48)])
+def test_split_invariants(lib, L, n, ps):
+    kw = dict(max_seq_len=L)
+    if ps:
+        kw.update(page_size=ps, max_pages_per_seq=-(-L // ps))
+    else:
+        kw.update(page_size=0, kv_capacity=L)
+    C, P = splits(lib, prob(**kw), n)
+    assert C % 32 == 0 and C >= 32
+    if ps and ps % 32 == 0:
+        assert C % ps == 0
+    assert P == math.ceil(L / C) and (P - 1) * C < L <= P * C   # no empty trailing partition
+    if n:
+        assert P <= n
+
+
+def test_workspace_bytes(lib):
+    p = prob(batch=3, num_q_heads=8, num_kv_heads=1, max_seq_len=1000, max_pages_per_seq=16)
+    n = ctypes.c_size_t()
+    assert lib.da_workspace_bytes(ctypes.byref(p), 4, ctypes.byref(n)) == DA_OK
+    C, P = splits(lib, p, 4)
+    rows = 3 * 8 * P
+    align = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert n.value == align(rows * 2 * 4) + align(rows * 128 * 4)
+
+
+def call_splitk(lib, p, scale=0.1, ws=FAKE, ws_bytes=1 << 30, q=FAKE, k=FAKE, v=FAKE, pt=FAKE, lens=FAKE, out=FAKE):
+    return lib.decode_attn_splitk(ctypes.byref(p), q, k, v, pt, lens, scale, 0, out, None, None, ws, ws_bytes, None)
+
+
+def test_error_paths_return_codes_without_launching(lib):
+    p = prob()
+    assert call_splitk(lib, p, q=None) == DA_EINVAL
+    assert call_splitk(lib, p, pt=None) == DA_EINVAL                     # paged needs a table
+    assert call_splitk(lib, prob(page_size=0, kv_capacity=4096)) == DA_EINVAL  # contiguous must not get one
+    assert call_splitk(lib, p, out=None) == DA_EINVAL
+    assert call_splitk(lib, p, scale=0.0) == DA_EINVAL
+    assert call_splitk(lib, p, scale=float("nan")) == DA_EINVAL
+    assert call_splitk(lib, p, scale=-1.0) == DA_EINVAL
+    assert call_splitk(lib, p, ws=None) == DA_EWORKSPACE
+    assert call_splitk(lib, p, ws=ctypes.c_void_p(0x1008)) == DA_EWORKSPACE   # misaligned
+    assert call_splitk(lib, p, ws_bytes=16) == DA_EWORKSPACE
+    assert b"workspace too small" in lib.da_last_error()
+    assert call_splitk(lib, prob(num_q_heads=15)) == DA_EINVAL
+
+
+def test_partition_and_combine_argument_checks(lib):
+    p = prob()
+    f = lib.decode_attn_partition
+    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, 100, 64, FAKE, FAKE, None) == DA_EINVAL  # chunk % 32
+    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, 256, 8, FAKE, FAKE, None) == DA_EINVAL   # splits
+    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, 256, 16, None, FAKE, None) == DA_EINVAL
+    c = lib.decode_attn_combine
+    assert c(ctypes.byref(p), FAKE, 0.1, 256, 16, FAKE, FAKE, None, None, None, None) == DA_EINVAL
+    assert c(ctypes.byref(p), FAKE, 0.1, 33, 16, FAKE, FAKE, FAKE, None, None, None) == DA_EINVAL
+    assert c(ctypes.byref(prob(ov_depth=96, qk_depth=96)), FAKE, 0.1, 256, 16, FAKE, FAKE, FAKE, None, None,
+             None) == DA_EUNSUPPORTED
+
+
+def test_probe_argument_checks(lib):
+    assert lib.da_read_probe(FAKE, 15, FAKE, None) == DA_EINVAL
+    assert lib.da_copy_probe(FAKE, None, 16, None) == DA_EINVAL

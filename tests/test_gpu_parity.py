@@ -1,0 +1,196 @@
+"""GPU parity: the HIP decode step (through the C ABI) against the fp64 oracle.
+
+Sizes span several key tiles, partitions and ragged tails while the oracle
+finishes in seconds. Tolerances are stated in parity_utils.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from lse_combine_amd import api
+from lse_combine_amd.inputs import make_case, to_device, workload
+from oracle import combine_fp64, partition_partials_fp64
+from parity_utils import assert_parity, np32, oracle_for
+
+pytestmark = pytest.mark.gpu
+
+
+def run(case, **kw):
+    dc = to_device(case)
+    out, lse, o32 = api.case_call(dc, return_lse=True, return_o32=True, **kw)
+    torch.cuda.synchronize()
+    return out, lse, o32
+
+
+def check_case(case, what, **kw):
+    print(f"[parity] {what}", flush=True)
+    out, lse, o32 = run(case, **kw)
+    O, LSE = oracle_for(case)
+    assert_parity(out, lse, o32, O, LSE, what=what)
+    return out, lse, o32
+
+
+# ---------------------------------------------------------------------------
+# kernel families x layouts x group sizes, reduced sizes with ragged tails
+# ---------------------------------------------------------------------------
+CASES = [
+    # name, make_case kwargs, kernel
+    ("tiny_fp32_full", dict(batch=1, num_q_heads=1, num_kv_heads=1, qk_depth=128, dtype=torch.float32,
+                            seq_lens=[1024], num_splits=4, seed=1), "auto"),
+    ("fp32_g4_contig_ragged", dict(batch=3, num_q_heads=8, num_kv_heads=2, qk_depth=128, dtype=torch.float32,
+                                   seq_lens=[1000, 77, 300], num_splits=3, seed=21), "auto"),
+    ("fp32_g16_paged16", dict(batch=2, num_q_heads=16, num_kv_heads=1, qk_depth=128, dtype=torch.float32,
+                              page_size=16, seq_lens=[517, 1201], num_splits=0, seed=22), "auto"),
+    ("bf16_g1_fma", dict(batch=3, num_q_heads=4, num_kv_heads=4, qk_depth=128, seq_lens=[2049, 1, 640],
+                         num_splits=5, seed=23), "auto"),
+    ("bf16_g1_mfma", dict(batch=3, num_q_heads=4, num_kv_heads=4, qk_depth=128, seq_lens=[2049, 1, 640],
+                          num_splits=5, seed=23), "mfma"),
+    ("bf16_g4_contig", dict(batch=2, num_q_heads=8, num_kv_heads=2, qk_depth=128, seq_lens=[4096, 1000],
+                            num_splits=8, seed=24), "auto"),
+    ("bf16_g4_fma", dict(batch=2, num_q_heads=8, num_kv_heads=2, qk_depth=128, seq_lens=[4096, 1000],
+                         num_splits=8, seed=24), "fma"),
+    ("bf16_g8_paged64_auto", dict(batch=5, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=64,
+                                  len_range=(1, 5000), num_splits=0, seed=25), "auto"),
+    ("bf16_g8_paged64_splits7", dict(batch=4, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=64,
+                                     len_range=(100, 3000), num_splits=7, seed=26), "auto"),
+    ("bf16_g6_paged32", dict(batch=3, num_q_heads=12, num_kv_heads=2, qk_depth=128, page_size=32,
+                             seq_lens=[33, 1500, 64], num_splits=2, seed=27), "auto"),
+    ("bf16_g16_paged32", dict(batch=2, num_q_heads=32, num_kv_heads=2, qk_depth=128, page_size=32,
+                              seq_lens=[777, 2048], num_splits=3, seed=28), "auto"),
+    ("bf16_g8_paged16_general", dict(batch=3, num_q_heads=8, num_kv_heads=1, qk_depth=128, page_size=16,
+                                     seq_lens=[1000, 15, 257], num_splits=4, seed=29), "auto"),
+    ("bf16_g2_paged48_general", dict(batch=2, num_q_heads=4, num_kv_heads=2, qk_depth=128, page_size=48,
+                                     seq_lens=[1000, 97], num_splits=0, seed=30), "auto"),
+    ("bf16_g8_one_split", dict(batch=3, num_q_heads=8, num_kv_heads=1, qk_depth=128, page_size=64,
+                               seq_lens=[3000, 64, 1], num_splits=1, seed=31), "auto"),
+    ("bf16_g8_v_is_k", dict(batch=2, num_q_heads=8, num_kv_heads=1, qk_depth=128, page_size=64,
+                            seq_lens=[700, 1300], num_splits=3, seed=32, v_is_k_prefix=True), "auto"),
+]
+
+
+@pytest.mark.parametrize("name,kw,kernel", CASES, ids=[c[0] for c in CASES])
+def test_parity(name, kw, kernel):
+    case = make_case(name, **kw)
+    check_case(case, name, kernel=kernel)
+
+
+def test_empty_and_tiny_sequences():
+    # L = 0 rows give O = 0 and LSE = -inf; L = 1 gives V_0
+    case = make_case("edge", batch=4, num_q_heads=8, num_kv_heads=1, qk_depth=128, page_size=64,
+                     seq_lens=[0, 1, 2, 65], num_splits=0, seed=40)
+    out, lse, o32 = check_case(case, "empty/tiny")
+    assert torch.all(out[0].float() == 0) and torch.all(torch.isneginf(lse[0]))
+
+
+def test_poisoned_unattended_slots_are_never_read():
+    for pg, kern in [(64, "auto"), (16, "auto"), (0, "auto"), (64, "fma")]:
+        case = make_case("poison", batch=3, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=pg,
+                         seq_lens=[100, 1, 1025], num_splits=3, seed=41, poison=True, spare_pages=3)
+        out, lse, o32 = check_case(case, f"poison ps={pg} {kern}", kernel=kern)
+        assert torch.isfinite(o32).all()
+
+
+def test_large_logits_overflow_safety():
+    # q scaled by 64: raw scores reach several hundred; the fp32 score's own rounding
+    # (~1e-4 absolute) then bounds the O agreement, so o32 is checked at 1e-4
+    case = make_case("big", batch=2, num_q_heads=8, num_kv_heads=1, qk_depth=128, page_size=64,
+                     seq_lens=[3000, 500], num_splits=4, seed=42, q_scale=64.0)
+    out, lse, o32 = run(case)
+    O, LSE = oracle_for(case)
+    assert torch.isfinite(o32).all()
+    assert_parity(out, lse, o32, O, LSE, o32_row_rtol=1e-4, what="large logits")
+
+
+def test_determinism_bitwise():
+    case = make_case("det", batch=4, num_q_heads=32, num_kv_heads=4, qk_depth=128, page_size=64,
+                     len_range=(500, 6000), num_splits=0, seed=43)
+    dc = to_device(case)
+    a = api.case_call(dc, return_lse=True, return_o32=True)
+    b = api.case_call(dc, return_lse=True, return_o32=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_seq_len_above_max_is_clamped():
+    # seq_lens may not exceed max_seq_len; larger values are clamped to it
+    case = make_case("clamp", batch=2, num_q_heads=8, num_kv_heads=1, qk_depth=128, page_size=64,
+                     seq_lens=[1000, 800], num_splits=0, seed=44)
+    dc = to_device(case)
+    out, lse, o32 = api.case_call(dc, return_lse=True, return_o32=True, max_seq_len=640)
+    torch.cuda.synchronize()
+    case.seq_lens = torch.tensor([640, 640], dtype=torch.int32)
+    O, LSE = oracle_for(case)
+    assert_parity(out, lse, o32, O, LSE, what="clamped")
+
+
+# ---------------------------------------------------------------------------
+# pass 1 and pass 2 separately
+# ---------------------------------------------------------------------------
+def test_partition_partials_match_oracle():
+    case = make_case("parts", batch=3, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=64,
+                     seq_lens=[1000, 64, 2500], seed=45)
+    dc = to_device(case)
+    chunk, P = 512, 5
+    po, pml = api.partition(dc.q, dc.k_cache, dc.v_cache, dc.page_table, dc.seq_lens, case.scale, chunk, P,
+                            page_size=64)
+    torch.cuda.synchronize()
+    m, l, O = partition_partials_fp64(np32(case.q), np32(case.k_cache), np32(case.v_cache),
+                                      case.seq_lens.numpy(), case.scale, chunk, P,
+                                      page_table=case.page_table.numpy(), page_size=64)
+    po, pml = np32(po), np32(pml)
+    live = l > 0
+    np.testing.assert_allclose(pml[..., 0][live], m[live], rtol=1e-5, atol=1e-4)
+    np.testing.assert_allclose(pml[..., 1][live], l[live], rtol=1e-5)
+    err = np.abs(po - O).max(-1)[live]
+    ref = np.abs(O).max(-1)[live]
+    assert (err / ref).max() <= 1e-5
+
+
+@pytest.mark.parametrize("Dv,P", [(128, 4), (128, 64), (512, 8)])
+def test_combine_only_on_oracle_partials(Dv, P):
+    # oracle partials (with empty partitions) fed to the HIP combine
+    r = np.random.default_rng(Dv + P)
+    B, Hq, chunk = 3, 8, 64
+    lens = np.array([P * chunk, chunk // 2, (P // 2) * chunk + 3])
+    m = r.standard_normal((B, Hq, P)) * 4
+    l = r.uniform(0.5, 30.0, (B, Hq, P))
+    O = r.standard_normal((B, Hq, P, Dv)) * 0.1
+    for b in range(B):
+        pb = -(-lens[b] // chunk)
+        m[b, :, pb:] = -np.inf
+        l[b, :, pb:] = 0
+        O[b, :, pb:] = 0
+    m32, l32, O32 = m.astype(np.float32), l.astype(np.float32), O.astype(np.float32)
+    Oref, Lref = combine_fp64(m32, l32, O32, 0.125)
+    prob = api._lib.DaProblem()
+    prob.batch, prob.num_q_heads, prob.num_kv_heads = B, Hq, 1
+    prob.qk_depth = 576 if Dv == 512 else 128
+    prob.ov_depth, prob.dtype, prob.page_size, prob.kv_capacity = Dv, 1, 0, P * chunk
+    prob.max_seq_len = P * chunk
+    prob.v_is_k_prefix = 1 if Dv == 512 else 0
+    ml = torch.from_numpy(np.stack([m32, l32], -1)).cuda().contiguous()
+    po = torch.from_numpy(O32).cuda().contiguous()
+    lens_t = torch.from_numpy(lens.astype(np.int32)).cuda()
+    out, lse, o32 = api.combine(prob, lens_t, 0.125, chunk, P, po, ml)
+    torch.cuda.synchronize()
+    assert_parity(out, lse, o32, Oref, Lref, what=f"combine Dv={Dv} P={P}")
+
+
+# ---------------------------------------------------------------------------
+# the named workloads at full size
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny", "gqa", "long"])
+def test_workload_full(name):
+    check_case(workload(name), f"workload {name}")
+
+
+def test_workload_paged_gqa_sampled():
+    case = workload("paged_gqa")
+    print("[parity] workload paged_gqa (sampled rows)", flush=True)
+    out, lse, o32 = run(case)
+    lens = case.seq_lens.numpy()
+    rows = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 7, 19, 31})
+    O, LSE = oracle_for(case, batch_rows=rows)
+    assert_parity(out[rows], lse[rows], o32[rows], O, LSE, what="paged_gqa sampled")
