@@ -152,3 +152,35 @@ def case_call(case, device="cuda", **kw):
     return decode_attn(case.q, case.k_cache, case.v_cache, case.page_table, case.seq_lens, case.scale,
                        case.num_splits, page_size=case.page_size, v_is_k_prefix=case.v_is_k_prefix,
                        ov_depth=case.ov_depth, **kw)
+
+
+class DecodePlan:
+    """Pre-marshalled arguments for repeated decode steps on fixed buffers.
+
+    Holds the problem description, the device pointers and a workspace so that
+    ``run()`` is a single C call (useful when the host must keep up with short
+    steps, and under graph capture: the call allocates nothing).
+    """
+
+    def __init__(self, q, k_cache, v_cache, page_table, seq_lens, scale, num_splits=0, *, page_size=0,
+                 max_seq_len=None, v_is_k_prefix=False, ov_depth=None, kernel="auto", out=None, lse=None,
+                 o32=None):
+        self.lib = _lib.load()
+        self.prob = make_problem(q, k_cache, v_cache, page_table, page_size=page_size, max_seq_len=max_seq_len,
+                                 v_is_k_prefix=v_is_k_prefix, ov_depth=ov_depth, kernel=kernel)
+        _check_tensors(q, k_cache, v_cache, page_table, seq_lens)
+        B, Hq, Dv = self.prob.batch, self.prob.num_q_heads, self.prob.ov_depth
+        self.out = torch.empty((B, Hq, Dv), dtype=torch.bfloat16, device=q.device) if out is None else out
+        self.lse, self.o32 = lse, o32
+        need = workspace_bytes(self.prob, num_splits)
+        self.workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        self.chunk, self.max_splits = choose_splits(self.prob, num_splits)
+        self._keep = (q, k_cache, v_cache, page_table, seq_lens)
+        self._args = (ctypes.byref(self.prob), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+                      _ptr(seq_lens), float(scale), int(num_splits), _ptr(self.out), _ptr(lse), _ptr(o32),
+                      _ptr(self.workspace), self.workspace.numel())
+
+    def run(self, stream=None):
+        s = _stream() if stream is None else ctypes.c_void_p(stream)
+        check(self.lib.decode_attn_splitk(*self._args, s))
+        return self.out

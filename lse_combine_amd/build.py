@@ -16,10 +16,13 @@ INCLUDE = os.path.join(ROOT, "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 VALU ops are disabled on purpose: the compiler may otherwise form
-# v_pk_{add,mul,fma}_f32 from plain float code.
+# v_pk_{add,mul,fma}_f32 from plain float code. -fno-honor-nans lets fmaxf lower to a
+# single v_max (the kernels never produce NaN from finite inputs; -inf is used and kept).
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no NaN inputs are assumed (max/min need no canonicalisation); infinities stay honoured
+    "-fno-honor-nans",
     "-Wall", "-Wno-unused-function", "-Wno-unused-result",
 ]
 

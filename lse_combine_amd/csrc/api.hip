@@ -101,16 +101,32 @@ int chunk_unit(const da_problem* p) {
   return kTileKeys;
 }
 
+int log2_exact(int v) {
+  if (v <= 0 || (v & (v - 1))) return -1;
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return s;
+}
+
 int page_mode(const da_problem* p) {
   if (p->page_size == 0) return da::kContiguous;
-  return (p->page_size % kTileKeys == 0) ? da::kPagedAligned : da::kPagedGeneral;
+  return (p->page_size >= kTileKeys && log2_exact(p->page_size) >= 0) ? da::kPagedAligned : da::kPagedGeneral;
+}
+
+// Matrix-core kernel shape: HG kv heads per workgroup (their waves read whole token
+// rows of the cache together) times KS key splits per kv head, HG * KS = 8 waves.
+// HG is as large as possible while the grid still offers a workgroup per CU (one
+// 8-wave workgroup per CU fits at three waves per SIMD).
+void mfma_shape(const da_problem* p, int32_t max_splits, int cus, int* HG, int* KS) {
+  int hg = p->num_kv_heads < 8 ? p->num_kv_heads : 8;
+  auto wgs = [&](int h) { return (int64_t)max_splits * ((p->num_kv_heads + h - 1) / h) * p->batch; };
+  while (hg > 1 && wgs(hg) < (int64_t)cus) hg = (hg + 1) / 2;
+  *HG = hg;
+  *KS = 8 / hg > 0 ? 8 / hg : 1;
 }
 
 // Workgroups of the partition kernel that fit on one compute unit at once.
-int wgs_per_cu(Variant v, int waves) {
-  if (v == kVarMfma128) return waves >= 8 ? 1 : 2;
-  return 2;
-}
+int wgs_per_cu(Variant v) { return v == kVarMfma128 ? 1 : 2; }
 
 int choose(const da_problem* p, Variant var, int32_t num_splits, int cus, int32_t* chunk_out, int32_t* splits_out) {
   if (num_splits < 0) return fail(DA_EINVAL, "num_splits must be >= 0 (0 = automatic)");
@@ -123,7 +139,7 @@ int choose(const da_problem* p, Variant var, int32_t num_splits, int cus, int32_
     // Automatic: the host does not see seq_lens (no device sync), so it plans for an
     // average length of max_seq_len / 2 and aims at about four rounds of workgroups
     // over the whole chip; chunks stay within [256, 8192] keys.
-    const int slots = cus * wgs_per_cu(var, 4);
+    const int slots = cus * wgs_per_cu(var);
     const int64_t est_units = (int64_t)p->batch * p->num_kv_heads * ((maxlen + 1) / 2);
     C = ceil_div(est_units, 4LL * slots);
     if (C < 256) C = 256;
@@ -165,34 +181,6 @@ int check_inputs(const da_problem* p, const void* q, const void* k, const void* 
   return DA_OK;
 }
 
-da::PartArgs part_args(const da_problem* p, const void* q, const void* k, const void* v, const int32_t* pt,
-                       const int32_t* lens, float scale, int32_t chunk, int32_t max_splits) {
-  da::PartArgs a;
-  memset(&a, 0, sizeof(a));
-  a.q = q;
-  a.k = k;
-  a.v = p->v_is_k_prefix ? k : v;
-  a.page_table = pt;
-  a.seq_lens = lens;
-  a.B = p->batch;
-  a.Hq = p->num_q_heads;
-  a.Hkv = p->num_kv_heads;
-  a.g = p->num_q_heads / p->num_kv_heads;
-  a.Dqk = p->qk_depth;
-  a.Dv = p->ov_depth;
-  a.v_row_len = p->v_is_k_prefix ? p->qk_depth : p->ov_depth;
-  a.page_size = p->page_size;
-  a.pt_stride = p->max_pages_per_seq;
-  a.num_pages = p->num_pages;
-  a.kv_capacity = p->kv_capacity;
-  a.max_seq_len = p->max_seq_len;
-  a.chunk = chunk;
-  a.max_splits = max_splits;
-  a.scale = scale;
-  a.c = scale * 1.4426950408889634f;
-  return a;
-}
-
 int launch_partition(const da_problem* p, Variant var, const da::PartArgs& a, hipStream_t s, int cus) {
   (void)hipGetLastError();
   hipError_t e;
@@ -202,9 +190,9 @@ int launch_partition(const da_problem* p, Variant var, const da::PartArgs& a, hi
       e = da::launch_partition_fma(a, p->dtype == DA_F32 ? 0 : 1, pm, s);
       break;
     case kVarMfma128: {
-      const int64_t grid = (int64_t)a.B * a.Hkv * a.max_splits;
-      const int waves = grid < 2LL * cus ? 8 : 4;
-      e = da::launch_partition_mfma128(a, pm, waves, s);
+      int HG, KS;
+      mfma_shape(p, a.max_splits, cus, &HG, &KS);
+      e = da::launch_partition_mfma128(a, pm, HG, KS, s);
       break;
     }
     default:
@@ -248,6 +236,42 @@ int check_scale(float scale) {
 }
 
 }  // namespace
+
+namespace da {
+
+int page_shift_of(int page_size) { return log2_exact(page_size); }
+
+// Kernel arguments of a partition launch (shared with the tools that time kernels directly).
+PartArgs build_part_args(const da_problem* p, const void* q, const void* k, const void* v, const int32_t* pt,
+                       const int32_t* lens, float scale, int32_t chunk, int32_t max_splits) {
+  PartArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = p->v_is_k_prefix ? k : v;
+  a.page_table = pt;
+  a.seq_lens = lens;
+  a.B = p->batch;
+  a.Hq = p->num_q_heads;
+  a.Hkv = p->num_kv_heads;
+  a.g = p->num_q_heads / p->num_kv_heads;
+  a.Dqk = p->qk_depth;
+  a.Dv = p->ov_depth;
+  a.v_row_len = p->v_is_k_prefix ? p->qk_depth : p->ov_depth;
+  a.page_size = p->page_size;
+  a.page_shift = page_shift_of(p->page_size);
+  a.pt_stride = p->max_pages_per_seq;
+  a.num_pages = p->num_pages;
+  a.kv_capacity = p->kv_capacity;
+  a.max_seq_len = p->max_seq_len;
+  a.chunk = chunk;
+  a.max_splits = max_splits;
+  a.scale = scale;
+  a.c = scale * 1.4426950408889634f;
+  return a;
+}
+
+}  // namespace da
 
 extern "C" {
 
@@ -302,7 +326,7 @@ int decode_attn_splitk(const da_problem* p, const void* q, const void* k_cache, 
   float* pml = (float*)((char*)workspace + ml_off);
   float* po = (float*)((char*)workspace + o_off);
   hipStream_t s = (hipStream_t)stream;
-  da::PartArgs a = part_args(p, q, k_cache, v_cache, page_table, seq_lens, scale, C, P);
+  da::PartArgs a = da::build_part_args(p, q, k_cache, v_cache, page_table, seq_lens, scale, C, P);
   a.part_o = po;
   a.part_ml = pml;
   a.out = (uint16_t*)out;
@@ -324,7 +348,7 @@ int decode_attn_partition(const da_problem* p, const void* q, const void* k_cach
   if ((r = check_scale(scale))) return r;
   if ((r = check_split_args(p, chunk_tokens, max_splits))) return r;
   if (!part_o || !part_ml) return fail(DA_EINVAL, "part_o and part_ml must be non-NULL");
-  da::PartArgs a = part_args(p, q, k_cache, v_cache, page_table, seq_lens, scale, chunk_tokens, max_splits);
+  da::PartArgs a = da::build_part_args(p, q, k_cache, v_cache, page_table, seq_lens, scale, chunk_tokens, max_splits);
   a.part_o = part_o;
   a.part_ml = part_ml;
   a.direct_single = 0;

@@ -17,9 +17,10 @@ namespace da {
 namespace {
 
 template <int DV>
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+__global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
   constexpr int TPR = DV / 4;          // threads per row
-  constexpr int RPB = 256 / TPR;       // rows per block
+  constexpr int RPB = 128 / TPR;       // rows per block
+  constexpr int kBatch = 8;            // partitions whose loads are in flight together
   const int tid = threadIdx.x;
   const int r_in = tid / TPR, ch = tid % TPR;
   const int64_t row = (int64_t)blockIdx.x * RPB + r_in;
@@ -31,22 +32,37 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int P_b = min((L + a.chunk - 1) / a.chunk, a.max_splits);
   if (a.skip_single && P_b == 1) return;
 
-  const float* ml = a.part_ml + row * a.max_splits * 2;
+  const float2* ml = (const float2*)(a.part_ml + row * a.max_splits * 2);
   const float* po = a.part_o + row * a.max_splits * DV + ch * 4;
+  // Gmax over the live partitions
   float M = -INFINITY;
-  for (int p = 0; p < P_b; ++p) {
-    const float2 v = *(const float2*)(ml + 2 * p);
-    if (v.y > 0.f) M = fmaxf(M, v.x);
+  for (int p0 = 0; p0 < P_b; p0 += kBatch) {
+    float2 v[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) v[i] = (p0 + i < P_b) ? ml[p0 + i] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+      if (v[i].y > 0.f) M = fmaxf(M, v[i].x);
   }
+  // weights e_p = l_p exp2((m_p - Gmax) c) and the weighted sum of the partial outputs
   float Gs = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int p = 0; p < P_b; ++p) {
-    const float2 v = *(const float2*)(ml + 2 * p);
-    if (v.y > 0.f) {
-      const float e = v.y * exp2_fast((v.x - M) * a.c);
-      Gs += e;
-      acc += e * *(const f32x4*)(po + (int64_t)p * DV);
+  for (int p0 = 0; p0 < P_b; p0 += kBatch) {
+    float2 v[kBatch];
+    f32x4 o[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const bool in = p0 + i < P_b;
+      v[i] = in ? ml[p0 + i] : make_float2(-INFINITY, 0.f);
+      o[i] = in ? *(const f32x4*)(po + (int64_t)(p0 + i) * DV) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (v[i].y > 0.f) {
+        const float e = v[i].y * exp2_fast((v[i].x - M) * a.c);
+        Gs += e;
+        acc += e * o[i];
+      }
     }
   }
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
@@ -84,11 +100,11 @@ __global__ __launch_bounds__(256) void copy_probe_kernel(const u32x4* src, u32x4
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.B * a.Hq;
   if (a.Dv == 128) {
-    dim3 grid((unsigned)((rows + 7) / 8));
-    hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(256), 0, s, a);
+    dim3 grid((unsigned)((rows + 3) / 4));
+    hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(128), 0, s, a);
   } else {
-    dim3 grid((unsigned)((rows + 1) / 2));
-    hipLaunchKernelGGL(combine_kernel<512>, grid, dim3(256), 0, s, a);
+    dim3 grid((unsigned)rows);
+    hipLaunchKernelGGL(combine_kernel<512>, grid, dim3(128), 0, s, a);
   }
   return hipGetLastError();
 }

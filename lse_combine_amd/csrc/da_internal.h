@@ -4,11 +4,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "decode_attn.h"
+
 namespace da {
 
 enum PageMode : int {
   kContiguous = 0,   // row of key t in sequence b = b * kv_capacity + t
-  kPagedAligned = 1, // paged with page_size % 32 == 0: a 32-key tile never crosses a page
+  kPagedAligned = 1, // paged, page_size a power of two >= 32: a 32-key tile never crosses a page
   kPagedGeneral = 2  // paged, any page_size: per-key page lookup
 };
 
@@ -27,6 +29,7 @@ struct PartArgs {
   int32_t B, Hq, Hkv, g, Dqk, Dv;
   int32_t v_row_len;        // elements between consecutive (row, kv-head) V vectors / Hkv
   int32_t page_size, pt_stride, num_pages, kv_capacity, max_seq_len;
+  int32_t page_shift;       // log2(page_size) when it is a power of two, else -1
   int32_t chunk, max_splits;
   int32_t direct_single;    // 1: rows whose sequence has a single partition write out/lse/o32
   float scale;              // softmax scale
@@ -46,9 +49,15 @@ struct CombineArgs {
   float scale, c;
 };
 
+// Kernel arguments of a partition launch for a validated problem (api.hip).
+PartArgs build_part_args(const ::da_problem* p, const void* q, const void* k, const void* v,
+                         const int32_t* page_table, const int32_t* seq_lens, float scale, int32_t chunk,
+                         int32_t max_splits);
+
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_partition_fma(const PartArgs& a, int dtype, int page_mode, hipStream_t s);
-hipError_t launch_partition_mfma128(const PartArgs& a, int page_mode, int waves, hipStream_t s);
+hipError_t launch_partition_mfma128(const PartArgs& a, int page_mode, int kv_heads_per_wg, int key_splits,
+                                    hipStream_t s);
 hipError_t launch_partition_latent(const PartArgs& a, int page_mode, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_read_probe(const void* src, size_t n_bytes, float* sink, hipStream_t s);

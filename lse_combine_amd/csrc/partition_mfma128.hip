@@ -1,35 +1,45 @@
 // Split-K pass 1 on the matrix cores for bf16 caches with Dqk = Dv = 128 and a GQA
 // group of up to 16 q heads per kv head (FA4Config: fused GQA tiles, BM_eff).
 //
-// One workgroup per (partition, kv head, sequence); NW waves split the
-// partition's keys in 32-key tiles (tile i goes to wave i % NW) and each keeps
-// its own online-softmax state. Per tile, with v_mfma_f32_16x16x32_bf16:
+// Work decomposition. A workgroup covers one partition p of one sequence b for HG
+// kv heads, with KS waves per kv head splitting the partition's keys (NW = HG * KS
+// <= 16 waves). Wave w serves kv head kg*HG + w % HG and takes the 32-key tiles
+// ks, ks + KS, ... (ks = w / HG). With HG = 8 the waves of a workgroup read the
+// eight 256-byte kv-head slices of the same tokens, i.e. whole 2 KB token rows of
+// the paged cache; HG shrinks when that would leave too few workgroups for the chip.
 //
-//   S^T[key][col] = K[key][:] . q[col][:]      A = K rows straight from HBM (16-byte
-//                                              loads already in the A-operand layout),
+// Per tile, with v_mfma_f32_16x16x32_bf16:
+//   S^T[key][col] = K[key][:] . q[col][:]      A = K rows, 16-byte loads that land
+//                                              directly in the A-operand layout,
 //                                              B = q (16 columns, see below)
-//   p = exp2((x - m_new) * c)                  online softmax in fp32; every lane owns
-//                                              one column and 8 keys, so the row max
-//                                              needs two cross-lane steps
+//   p = exp2((x - m_new) * c)                  online softmax in fp32; a lane owns one
+//                                              column and 8 keys, so the tile max needs
+//                                              two cross-lane steps
 //   O^T[d][col] += V^T[d][key] . P^T[key][col] A = V^T read from LDS with the gfx950
 //                                              transposing read ds_read_b64_tr_b16,
-//                                              B = P^T taken from the S^T registers as is
+//                                              B = P^T straight from the S^T registers
 //
-// P must not be rounded to bf16 before P.V (the fp32 O must stay within 1e-5), so
-// P is split as p = hi + lo with hi = bf16(p), lo = bf16(p - hi) (about 16
-// significant bits). When g <= 8 the 16 MFMA columns hold the g heads twice:
-// columns 0-7 carry hi, columns 8-15 carry lo (the scores of both copies are the
-// same), so hi and lo cost one MFMA; the two halves of O^T are summed at the end.
-// For 8 < g <= 16 a second MFMA per depth block adds the lo part.
+// P must not be rounded to bf16 before P.V (the fp32 O must stay within 1e-5), so it
+// is split as p = hi + lo, hi = bf16(p), lo = bf16(p - hi) (about 16 significant
+// bits). When g <= 8 the 16 MFMA columns hold the g heads twice: columns 0-7 carry hi
+// and 8-15 carry lo (their scores are equal), so hi and lo cost one MFMA and the two
+// column halves of O^T are added at the end. For 8 < g <= 16 a second MFMA per depth
+// block adds the lo part.
 //
-// After the key loop the waves merge their (m, l, O) through LDS with the
-// log-sum-exp weights (fa4_lse_combine_write: fragments merged with per-row
-// scales) and the workgroup stores the normalised partial and (m, l)
+// Addressing: tiles are 32 keys and partitions start on multiples of 32, so with a
+// contiguous cache or pages of a power of two >= 32 keys a tile is 32 consecutive cache
+// rows: the tile base is a scalar and every lane adds a fixed 32-bit offset. The page
+// indices of the partition are staged in LDS once, so no dependent page-table load
+// sits between consecutive prefetches. One register tile per wave: the next tile's K
+// and V (16 KB per wave) are requested once the current tile sits in LDS and in the
+// score MFMAs, so they are in flight during its softmax and P.V; the small register
+// footprint lets three waves share a SIMD.
+//
+// Epilogue: with KS = 1 every wave stores its own normalised partial and (m, l)
 // (fa4_splitk_combine_write, second paragraph), or the finished bf16 row when the
-// sequence has a single partition.
-//
-// Loads are software-pipelined: the next tile's K and V (16 KB per wave) are in
-// flight while the current tile is computed.
+// sequence has a single partition. With KS > 1 the waves of a kv head first merge
+// their (m, l, O) through LDS with the log-sum-exp weights (fa4_lse_combine_write:
+// fragments merged with per-row scales).
 #include "da_device.h"
 
 namespace da {
@@ -37,44 +47,90 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kTile = 32;
+constexpr int kMaxWaves = 16;
 constexpr int kVBytes = kTile * kD * 2;       // one wave's V tile in LDS
 constexpr int kWaveBytes = kVBytes + 256;     // + merge (m, l) for up to 16 heads
+constexpr int kMaxLdsPages = 512;             // page indices of one segment staged in LDS
 
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
-struct Tile {
+// Buffer-resource dword 3 for raw (untyped) dword loads on gfx9-family parts.
+constexpr int kRsrcWord3 = 0x00020000;
+// Cache policy of the K/V loads: non-temporal (each byte is read once per step).
+constexpr int kLoadNT = 2;
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kLoadNT));
+}
+
+struct KTile {
   u32x4 k[2][4];  // K rows: [key block][depth step], 8 bf16 each
-  u32x4 v[8];     // V: 8 x 16 bytes, stored to LDS as loaded
 };
+
+// Wait until at most n vector-memory operations of this wave are outstanding
+// (s_waitcnt vmcnt(n), other counters untouched); n < 16. The compiler fences keep
+// the LDS reads that depend on a direct-to-LDS load after the wait.
+__device__ __forceinline__ void wait_vm(int n) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if (n == 0) __builtin_amdgcn_s_waitcnt(0x0F70);
+  else __builtin_amdgcn_s_waitcnt(0x0F70 | 8);   // only 0 and 8 are used
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-template <int NW, bool HL, int PM>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
-void partition_mfma128_kernel(PartArgs a) {
-  const int p = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int L = attended_len(a, b, PM == kContiguous);
+// max over the four lanes n, n+16, n+32, n+48 (the four key groups of a column).
+// (v_permlane32_swap / v_permlane16_swap would do this on the VALU, but this compiler
+// folds the two results of a swap of a value with itself into one, losing half the
+// lanes; the LDS permute is used instead.)
+__device__ __forceinline__ float max_over_key_groups(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+
+template <bool HL, int PM>
+// four waves per SIMD (<= 128 VGPRs); general paging needs a few more registers
+__global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(PM == kPagedGeneral ? 3 : 4)))
+void partition_gqa_kernel(PartArgs a, int HG, int KS) {
+  const int p = blockIdx.x, kg = blockIdx.y, b = blockIdx.z;
+  // sequence length (loaded by a vector load: state that it is uniform)
+  const int L = __builtin_amdgcn_readfirstlane(attended_len(a, b, PM == kContiguous));
   const int start = p * a.chunk;
   if (start >= L) return;
   const int end = min(start + a.chunk, L);
   const int P_b = min((L + a.chunk - 1) / a.chunk, a.max_splits);
   const bool direct = a.direct_single && P_b == 1;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
+  const int NW = HG * KS;
+  const int member = w % HG, ks = w / HG;
+  const int kvh = kg * HG + member;
+  const bool wave_active = kvh < a.Hkv;
   const int n = lane & 15, qd = lane >> 4;
   const int g = a.g;
   const int hc = HL ? (n & 7) : n;          // head index of this lane's MFMA column
   const bool col_valid = hc < g;
   const bool is_lo = HL && n >= 8;
+  const float lo_mask = is_lo ? 1.f : 0.f;
 
-  __shared__ __attribute__((aligned(16))) char smem[NW * kWaveBytes];
+  extern __shared__ __attribute__((aligned(16))) char smem[];   // NW * kWaveBytes (launch size)
+  __shared__ int pages_s[kMaxLdsPages];
   char* vt = smem + w * kWaveBytes;
+  int first_page = 0;   // page index held by pages_s[0] in the current segment
+
+  // zero this wave's V tile once: direct-to-LDS loads outside the buffer range may leave
+  // rows untouched, and those rows must hold finite values (they meet p = 0)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) *(u32x4*)(vt + (i * 64 + lane) * 16) = u32x4{0u, 0u, 0u, 0u};
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the zeros are in place before any load lands
 
   // q as the B operand of S^T = K q^T: column n, depth 32j + 8qd .. +8.
   bf16x8 qf[4];
   {
-    const uint16_t* qrow =
-        (const uint16_t*)a.q + ((int64_t)b * a.Hq + (int64_t)kvh * g + (col_valid ? hc : 0)) * kD;
+    const int kv_safe = wave_active ? kvh : 0;
+    const uint16_t* qrow = (const uint16_t*)a.q +
+                           ((int64_t)b * a.Hq + (int64_t)kv_safe * g + (col_valid ? hc : 0)) * kD;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       u32x4 v = *(const u32x4*)(qrow + 32 * j + 8 * qd);
@@ -83,12 +139,12 @@ void partition_mfma128_kernel(PartArgs a) {
     }
   }
 
-  const uint16_t* kc = (const uint16_t*)a.k;
-  const uint16_t* vc = (const uint16_t*)a.v;
-  const int64_t kstride = (int64_t)a.Hkv * kD;
-  const int64_t vstride = (int64_t)a.Hkv * a.v_row_len;
-  const int64_t koff = (int64_t)kvh * kD;
-  const int64_t voff = (int64_t)kvh * a.v_row_len;
+  const char* kc = (const char*)a.k;
+  const char* vc = (const char*)a.v;
+  const uint32_t krow_bytes = (uint32_t)a.Hkv * kD * 2;          // bytes between tokens (K)
+  const uint32_t vrow_bytes = (uint32_t)a.Hkv * a.v_row_len * 2; // bytes between tokens (V)
+  const uint32_t kslice = (uint32_t)(wave_active ? kvh : 0) * kD * 2;
+  const uint32_t vslice = (uint32_t)(wave_active ? kvh : 0) * a.v_row_len * 2;
   const float c = a.c;
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -96,49 +152,92 @@ void partition_mfma128_kernel(PartArgs a) {
 #pragma unroll
   for (int db = 0; db < 8; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // cache row of key kk (0..31) of the tile starting at t0; keys past the end are
-  // clamped to the last valid key (loaded but given p = 0)
-  auto row_of = [&](int t0, int kk) -> int64_t {
-    const int last = end - 1 - t0;
-    kk = kk < last ? kk : last;
+  // first cache row of the tile starting at t0 (contiguous / aligned pages: the tile
+  // is 32 consecutive rows), and the row of key t in the general paged case
+  auto tile_row0 = [&](int t0) -> int64_t {
     if constexpr (PM == kContiguous) {
-      return (int64_t)b * a.kv_capacity + t0 + kk;
-    } else if constexpr (PM == kPagedAligned) {
-      const int pi = t0 / a.page_size;    // the whole tile sits in this page
-      int page = a.page_table[(int64_t)b * a.pt_stride + pi];
-      page = page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
-      return (int64_t)page * a.page_size + (t0 - pi * a.page_size) + kk;
+      return (int64_t)b * a.kv_capacity + t0;
     } else {
-      return key_row<PM>(a, b, t0 + kk);
+      const int pi = t0 >> a.page_shift;   // pages are a power of two >= 32 keys
+      // an LDS value read at a uniform address: tell the compiler it is uniform; index and
+      // value are clamped so that no cache address can leave the page pool
+      const int slot = min(max(pi - first_page, 0), kMaxLdsPages - 1);
+      int page = __builtin_amdgcn_readfirstlane(pages_s[slot]);
+      page = min(max(page, 0), a.num_pages - 1);
+      return ((int64_t)page << a.page_shift) + (t0 & (a.page_size - 1));
+    }
+  };
+  auto general_row = [&](int t) -> int64_t {
+    const int pi = t / a.page_size;
+    const int slot = min(max(pi - first_page, 0), kMaxLdsPages - 1);
+    const int page = min(max(pages_s[slot], 0), a.num_pages - 1);
+    return (int64_t)page * a.page_size + (t - pi * a.page_size);
+  };
+
+  // Per-lane byte offset of K inside a 16-row half tile: key n, 16-byte depth chunk qd
+  // (+64 bytes per MFMA step, an immediate).
+  const uint32_t koff = (uint32_t)n * krow_bytes + 16 * qd;
+
+  // K of the tile at t0 into registers (A operand of the score MFMAs).
+  auto load_k = [&](KTile& T, int t0) {
+    const int last = min(kTile - 1, end - 1 - t0);
+    if constexpr (PM != kPagedGeneral) {
+      // The tile is 32 consecutive cache rows: a scalar base per 16-row half. Each half's
+      // buffer range covers only its valid rows, so on a ragged last tile the loads of
+      // missing keys return zeros without touching memory (their scores are masked).
+      const int64_t row0 = tile_row0(t0);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        // (the clamp is selected as a vector op; readfirstlane keeps the descriptor scalar)
+        const int rows = __builtin_amdgcn_readfirstlane(min(max(last + 1 - 16 * h, 0), 16));
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(kc + (row0 + 16 * h) * krow_bytes + kslice), 0, rows * krow_bytes, kRsrcWord3);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) T.k[h][j] = buf_load16(rk, koff + 64 * j, 0);
+      }
+    } else {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const char* kp = kc + general_row(t0 + min(n + 16 * blk, last)) * krow_bytes + kslice + 16 * qd;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) T.k[blk][j] = __builtin_nontemporal_load((const u32x4*)(kp + 64 * j));
+      }
     }
   };
 
-  auto load_tile = [&](Tile& T, int it) {
-    const int t0 = start + it * kTile;
+  // V of the tile at t0 straight into this wave's LDS tile (8 direct-to-LDS 16-byte loads,
+  // 1 KB each: load i fills stage rows 4i..4i+3, lane (qd, n) writes row 4i + qd, chunk
+  // slot n with the swizzled source chunk n ^ (row & 15)). Rows past the end of a ragged
+  // tile are outside the buffer range and deliver zeros.
+  auto load_v = [&](int t0) {
+    const int last = min(kTile - 1, end - 1 - t0);
+    if constexpr (PM != kPagedGeneral) {
+      const int64_t row0 = tile_row0(t0);
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const uint16_t* kp = kc + row_of(t0, n + 16 * blk) * kstride + koff + 8 * qd;
+      for (int h = 0; h < 2; ++h) {
+        const int rows = __builtin_amdgcn_readfirstlane(min(max(last + 1 - 16 * h, 0), 16));
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(vc + (row0 + 16 * h) * vrow_bytes + vslice), 0, rows * vrow_bytes, kRsrcWord3);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) T.k[blk][j] = __builtin_nontemporal_load((const u32x4*)(kp + 32 * j));
-    }
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * i + qd;   // row within the half; the swizzle repeats per half
+          const uint32_t voff = (uint32_t)r * vrow_bytes + 16 * (n ^ (r & 15));
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (DA_LDS void*)(vt + (4 * h + i) * 1024), 16, voff, 0, 0,
+                                                   kLoadNT);
+        }
+      }
+    } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 4 * i + qd;             // tile row this lane stages
-      const int chunk = n ^ (r & 15);       // XOR swizzle of 16-byte chunks within the row
-      const uint16_t* vp = vc + row_of(t0, r) * vstride + voff + 8 * chunk;
-      T.v[i] = __builtin_nontemporal_load((const u32x4*)vp);
+      for (int i = 0; i < 8; ++i) {
+        const int r = 4 * i + qd;
+        const char* vp = vc + general_row(t0 + min(r, last)) * vrow_bytes + vslice + 16 * (n ^ (r & 15));
+        __builtin_amdgcn_global_load_lds((const void*)vp, (DA_LDS void*)(vt + i * 1024), 16, 0, 0);
+      }
     }
   };
 
-  auto compute = [&](const Tile& T, int it) {
-    const int t0 = start + it * kTile;
-    const int nvalid = min(kTile, end - t0);
-    // stage V (row-major, swizzled) for the transposing reads
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *(u32x4*)(vt + (i * 64 + lane) * 16) = T.v[i];
-
-    // S^T = K q^T for keys 0-15 and 16-31
-    f32x4 s[2];
+  // phase A: S^T = K q^T for keys 0-15 and 16-31; afterwards the K registers are free
+  auto score = [&](const KTile& T, f32x4* s) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       s[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -146,16 +245,23 @@ void partition_mfma128_kernel(PartArgs a) {
       for (int j = 0; j < 4; ++j)
         s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(T.k[blk][j]), qf[j], s[blk], 0, 0, 0);
     }
+  };
 
+  // phase B: online softmax and P.V. On a ragged tile the scores of missing keys are set
+  // to -inf first; exp2(-inf) = 0 then removes them from the sums.
+  auto softmax_pv = [&](f32x4* s, int t0, bool k_in_flight) {
+    const int nvalid = end - t0;
+    if (nvalid < kTile) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (16 * blk + 4 * qd + i >= nvalid) s[blk][i] = -INFINITY;
+    }
     // online softmax: this lane holds keys 16*blk + 4*qd + i of column n
-    float mx = -INFINITY;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (16 * blk + 4 * qd + i < nvalid) mx = fmaxf(mx, s[blk][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    mx = max_over_key_groups(mx);
     const float mn = fmaxf(m_run, mx);
     const float alpha = exp2_fast((m_run - mn) * c);
     const float mc = mn * c;
@@ -165,34 +271,39 @@ void partition_mfma128_kernel(PartArgs a) {
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool ok = 16 * blk + 4 * qd + i < nvalid;
-        pr[blk][i] = ok ? exp2_fast(fmaf(s[blk][i], c, -mc)) : 0.f;
+        pr[blk][i] = exp2_fast(fmaf(s[blk][i], c, -mc));
         psum += pr[blk][i];
       }
     l_run = fmaf(l_run, alpha, psum);
     m_run = mn;
+    // the running max rarely moves once a few tiles are in: skip the rescale then
+    if (__ballot(alpha != 1.f)) {
 #pragma unroll
-    for (int db = 0; db < 8; ++db) o[db] *= alpha;
+      for (int db = 0; db < 8; ++db) o[db] *= alpha;
+    }
 
-    // P^T as the B operand: k-slots 0-3 = keys 4qd..+3, 4-7 = keys 16+4qd..+3
-    uint32_t hw[4], lw[4];
+    // P^T as the B operand: k-slots 0-3 = keys 4qd..+3, 4-7 = keys 16+4qd..+3.
+    // hi columns take bf16(p); lo columns take bf16(p - float(bf16(p))).
+    uint32_t pw[4], lw[4];
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) {
       const int blk = s2 >> 1, i0 = (s2 & 1) * 2;
       const float p0 = pr[blk][i0], p1 = pr[blk][i0 + 1];
       const uint32_t h = pack_bf16x2(p0, p1);
-      hw[s2] = h;
-      lw[s2] = pack_bf16x2(p0 - bf16lo(h), p1 - bf16hi(h));
+      if constexpr (HL) {
+        pw[s2] = pack_bf16x2(fmaf(-lo_mask, bf16lo(h), p0), fmaf(-lo_mask, bf16hi(h), p1));
+      } else {
+        pw[s2] = h;
+        lw[s2] = pack_bf16x2(p0 - bf16lo(h), p1 - bf16hi(h));
+      }
     }
-    bf16x8 pb_hi, pb_lo;
-    if constexpr (HL) {
-      u32x4 sel = is_lo ? u32x4{lw[0], lw[1], lw[2], lw[3]} : u32x4{hw[0], hw[1], hw[2], hw[3]};
-      pb_hi = as_bf16x8(sel);
-    } else {
-      pb_hi = as_bf16x8(u32x4{hw[0], hw[1], hw[2], hw[3]});
-      pb_lo = as_bf16x8(u32x4{lw[0], lw[1], lw[2], lw[3]});
-    }
+    const bf16x8 pb_hi = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
+    bf16x8 pb_lo;
+    if constexpr (!HL) pb_lo = as_bf16x8(u32x4{lw[0], lw[1], lw[2], lw[3]});
 
+    // V of this tile must have landed in LDS: it was requested before the 8 K loads of
+    // the next tile, which may stay in flight
+    wait_vm(k_in_flight ? 8 : 0);
     // V^T A operand: lane (n, qd) gets depth 16db + n of keys 4qd..+3 and 16+4qd..+3
     const int r0 = 4 * qd + (n >> 2);
 #pragma unroll
@@ -213,20 +324,44 @@ void partition_mfma128_kernel(PartArgs a) {
     }
   };
 
-  const int n_tiles = (end - start + kTile - 1) / kTile;
-  int it = w;
-  if (it < n_tiles) {
-    Tile A, B;
-    load_tile(A, it);
-    while (true) {
-      load_tile(B, min(it + NW, n_tiles - 1));
-      compute(A, it);
-      it += NW;
-      if (it >= n_tiles) break;
-      load_tile(A, min(it + NW, n_tiles - 1));
-      compute(B, it);
-      it += NW;
-      if (it >= n_tiles) break;
+  // Segments: the page indices of up to kMaxLdsPages pages are staged in LDS at a time
+  // (one segment for every page size >= 32 with chunks up to 16K keys).
+  int seg_len = end - start;
+  if constexpr (PM != kContiguous) {
+    const int cap = ((kMaxLdsPages - 1) * a.page_size) / kTile * kTile;
+    seg_len = min(seg_len, cap);
+  }
+  for (int s0 = start; s0 < end; s0 += seg_len) {
+    const int s1 = min(s0 + seg_len, end);
+    if constexpr (PM != kContiguous) {
+      __syncthreads();
+      first_page = s0 / a.page_size;
+      const int n_pages = (s1 - 1) / a.page_size - first_page + 1;
+      const int32_t* pt = a.page_table + (int64_t)b * a.pt_stride + first_page;
+      for (int i = tid; i < n_pages; i += NW * 64) {
+        const int page = pt[i];
+        pages_s[i] = page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
+      }
+      __syncthreads();
+    }
+    const int n_tiles = (s1 - s0 + kTile - 1) / kTile;
+    if (wave_active && ks < n_tiles) {
+      // One tile buffer: the next tile's K and V (16 KB per wave) are requested as soon
+      // as the current tile has been moved to LDS and into the score MFMAs, and stay in
+      // flight through the softmax and P.V of the current tile.
+      KTile T;
+      load_k(T, s0 + ks * kTile);
+      load_v(s0 + ks * kTile);
+      for (int it = ks; it < n_tiles; it += KS) {
+        const bool has_next = it + KS < n_tiles;
+        f32x4 s[2];
+        score(T, s);
+        if (has_next) load_k(T, s0 + (it + KS) * kTile);
+        softmax_pv(s, s0 + it * kTile, has_next);
+        // the transposing reads of this tile are complete (their data fed the MFMAs):
+        // the LDS tile can take the next V
+        if (has_next) load_v(s0 + (it + KS) * kTile);
+      }
     }
   }
 
@@ -240,9 +375,23 @@ void partition_mfma128_kernel(PartArgs a) {
       for (int i = 0; i < 4; ++i) o[db][i] += __shfl_xor(o[db][i], 8);
   }
 
-  // merge the waves through LDS (each wave reuses its own V region)
+  if (KS == 1) {
+    // one wave per kv head: store straight from registers
+    if (wave_active && col_valid && !is_lo) {
+      const float inv = 1.f / l_run;
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+        store_unit(a, b, kvh * g + hc, p, direct, 16 * db + 4 * qd, o[db] * inv, m_run, l_run,
+                   db == 0 && qd == 0);
+    }
+    return;
+  }
+
+  // KS > 1: merge the key splits of each kv head through LDS (each wave reuses its own
+  // V region; waves that saw no tile hold m = -inf, l = 0, O = 0 and get weight 0)
   float* mo = (float*)vt;                      // [16][128] O of this wave
   float* mml = (float*)(vt + kVBytes);         // m[16], l[16]
+  __syncthreads();
   if (col_valid && !is_lo) {
 #pragma unroll
     for (int db = 0; db < 8; ++db) *(f32x4*)(mo + hc * kD + 16 * db + 4 * qd) = o[db];
@@ -253,36 +402,41 @@ void partition_mfma128_kernel(PartArgs a) {
   }
   __syncthreads();
   constexpr int kUnits = kD / 4;
-  for (int u = tid; u < g * kUnits; u += NW * 64) {
-    const int h = u / kUnits, d0 = (u % kUnits) * 4;
+  const int units = HG * g * kUnits;
+  for (int u = tid; u < units; u += NW * 64) {
+    const int mem = u / (g * kUnits);
+    const int h = (u / kUnits) % g, d0 = (u % kUnits) * 4;
+    const int kv2 = kg * HG + mem;
+    if (kv2 >= a.Hkv) continue;
     float M = -INFINITY;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, ((const float*)(smem + ww * kWaveBytes + kVBytes))[h]);
+    for (int s2 = 0; s2 < KS; ++s2)
+      M = fmaxf(M, ((const float*)(smem + (s2 * HG + mem) * kWaveBytes + kVBytes))[h]);
     float Ls = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-      const float* ml = (const float*)(smem + ww * kWaveBytes + kVBytes);
+    for (int s2 = 0; s2 < KS; ++s2) {
+      const char* reg = smem + (s2 * HG + mem) * kWaveBytes;
+      const float* ml = (const float*)(reg + kVBytes);
       const float e = exp2_fast((ml[h] - M) * c);
       Ls = fmaf(ml[16 + h], e, Ls);
-      acc += e * *(const f32x4*)((const float*)(smem + ww * kWaveBytes) + h * kD + d0);
+      acc += e * *(const f32x4*)((const float*)reg + h * kD + d0);
     }
-    store_unit(a, b, kvh * g + h, p, direct, d0, acc * (1.f / Ls), M, Ls, d0 == 0);
+    store_unit(a, b, kv2 * g + h, p, direct, d0, acc * (1.f / Ls), M, Ls, d0 == 0);
   }
 }
 
-template <int NW, bool HL>
-hipError_t launch_nw(const PartArgs& a, int pm, hipStream_t s) {
-  dim3 grid(a.max_splits, a.Hkv, a.B), block(NW * 64);
+template <bool HL>
+hipError_t launch_hl(const PartArgs& a, int pm, int HG, int KS, hipStream_t s) {
+  dim3 grid(a.max_splits, (a.Hkv + HG - 1) / HG, a.B), block(HG * KS * 64);
+  const size_t lds = (size_t)HG * KS * kWaveBytes;
   switch (pm) {
     case kContiguous:
-      hipLaunchKernelGGL((partition_mfma128_kernel<NW, HL, kContiguous>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((partition_gqa_kernel<HL, kContiguous>), grid, block, lds, s, a, HG, KS);
       break;
     case kPagedAligned:
-      hipLaunchKernelGGL((partition_mfma128_kernel<NW, HL, kPagedAligned>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((partition_gqa_kernel<HL, kPagedAligned>), grid, block, lds, s, a, HG, KS);
       break;
     default:
-      hipLaunchKernelGGL((partition_mfma128_kernel<NW, HL, kPagedGeneral>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((partition_gqa_kernel<HL, kPagedGeneral>), grid, block, lds, s, a, HG, KS);
       break;
   }
   return hipGetLastError();
@@ -290,10 +444,10 @@ hipError_t launch_nw(const PartArgs& a, int pm, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_partition_mfma128(const PartArgs& a, int page_mode, int waves, hipStream_t s) {
-  const bool hl = a.g <= 8;
-  if (waves >= 8) return hl ? launch_nw<8, true>(a, page_mode, s) : launch_nw<8, false>(a, page_mode, s);
-  return hl ? launch_nw<4, true>(a, page_mode, s) : launch_nw<4, false>(a, page_mode, s);
+// HG kv heads per workgroup, KS key splits per kv head (HG * KS <= 16).
+hipError_t launch_partition_mfma128(const PartArgs& a, int page_mode, int HG, int KS, hipStream_t s) {
+  if (HG < 1 || KS < 1 || HG * KS > kMaxWaves) return hipErrorInvalidValue;
+  return a.g <= 8 ? launch_hl<true>(a, page_mode, HG, KS, s) : launch_hl<false>(a, page_mode, HG, KS, s);
 }
 
 }  // namespace da
