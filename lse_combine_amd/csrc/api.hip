@@ -79,7 +79,7 @@ int check_problem(const da_problem* p, Variant* var) {
                   "depth 576/512 is supported only as bf16 latent-shared attention with one kv head and a multiple "
                   "of 16 q heads (matrix-core kernel)");
     *var = kVarLatent;
-    return fail(DA_EUNSUPPORTED, "latent-shared 576/512 kernel is not built into this version");
+    return DA_OK;
   }
   if (p->qk_depth != 128 || p->ov_depth != 128)
     return fail(DA_EUNSUPPORTED, "supported depths: 128/128, or 576/512 latent-shared (got %d/%d)", p->qk_depth,
@@ -147,6 +147,11 @@ int choose(const da_problem* p, Variant var, int32_t num_splits, int cus, int32_
   }
   C = ceil_div(C, unit) * unit;
   if (C > ceil_div(maxlen, unit) * unit) C = ceil_div(maxlen, unit) * unit;
+  if (var == kVarLatent && p->page_size > 0) {
+    // the latent kernel stages one partition's page indices in LDS (at most 256 pages)
+    const int64_t cap = (255LL * p->page_size) / kTileKeys * kTileKeys;
+    if (C > cap) C = cap / unit * unit > 0 ? cap / unit * unit : kTileKeys;
+  }
   if (C < unit) C = unit;
   const int64_t P = ceil_div(maxlen, C);
   if (C > INT32_MAX || P > INT32_MAX) return fail(DA_EINVAL, "split selection overflow");
@@ -166,6 +171,8 @@ void ws_layout(const da_problem* p, int32_t max_splits, size_t* ml_off, size_t* 
 
 int check_split_args(const da_problem* p, int32_t chunk, int32_t max_splits) {
   if (chunk <= 0 || chunk % kTileKeys) return fail(DA_EINVAL, "chunk_tokens must be a positive multiple of %d (got %d)", kTileKeys, chunk);
+  if (p->qk_depth == 576 && p->page_size > 0 && (int64_t)chunk > 255LL * p->page_size)
+    return fail(DA_EUNSUPPORTED, "latent-shared kernel: chunk_tokens must be <= 255 pages (%d keys)", 255 * p->page_size);
   const int64_t maxlen = p->max_seq_len > 0 ? p->max_seq_len : 1;
   if (max_splits < ceil_div(maxlen, chunk))
     return fail(DA_EINVAL, "max_splits %d < ceil(max_seq_len %d / chunk_tokens %d)", max_splits, p->max_seq_len, chunk);

@@ -55,6 +55,10 @@ def test_exports_every_declared_function(lib):
     (dict(kernel=5), DA_EINVAL),
     (dict(v_is_k_prefix=1, ov_depth=600, qk_depth=576), DA_EINVAL),
     (dict(num_q_heads=128, num_kv_heads=2, qk_depth=576, ov_depth=512, v_is_k_prefix=1), DA_EUNSUPPORTED),
+    (dict(num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1), DA_OK),
+    (dict(num_q_heads=24, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1), DA_EUNSUPPORTED),
+    (dict(num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=0), DA_EUNSUPPORTED),
+    (dict(num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1, dtype=0), DA_EUNSUPPORTED),
 ])
 def test_supported(lib, kw, code):
     p = prob(**kw)
@@ -84,6 +88,9 @@ def test_fixed_splits_match_the_named_workloads(lib):
     # long: L 131072, page 64, 64 splits
     assert splits(lib, prob(batch=1, num_q_heads=32, num_kv_heads=4, max_pages_per_seq=2048,
                             max_seq_len=131072), 64) == (2048, 64)
+    # latent-shared: L 8192, page 64, 8 splits
+    assert splits(lib, prob(batch=16, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512,
+                            v_is_k_prefix=1, max_pages_per_seq=128, max_seq_len=8192), 8) == (1024, 8)
 
 
 @pytest.mark.parametrize("L,n,ps", [(1000, 3, 0), (1000, 3, 64), (77, 5, 0), (5000, 7, 16), (1, 1, 0),

@@ -66,6 +66,18 @@ CASES = [
                                seq_lens=[3000, 64, 1], num_splits=1, seed=31), "auto"),
     ("bf16_g8_v_is_k", dict(batch=2, num_q_heads=8, num_kv_heads=1, qk_depth=128, page_size=64,
                             seq_lens=[700, 1300], num_splits=3, seed=32, v_is_k_prefix=True), "auto"),
+    # latent-shared: one kv head, K rows of 576 (512 + 64 rotary), V = K[..., :512]
+    ("latent_g64_paged64", dict(batch=2, num_q_heads=64, num_kv_heads=1, qk_depth=576, ov_depth=512,
+                                page_size=64, seq_lens=[700, 1313], num_splits=3, seed=33,
+                                v_is_k_prefix=True), "auto"),
+    ("latent_g128_paged64_one_split", dict(batch=2, num_q_heads=128, num_kv_heads=1, qk_depth=576,
+                                           ov_depth=512, page_size=64, seq_lens=[90, 31], num_splits=1,
+                                           seed=34, v_is_k_prefix=True), "auto"),
+    ("latent_g16_contig", dict(batch=3, num_q_heads=16, num_kv_heads=1, qk_depth=576, ov_depth=512,
+                               seq_lens=[100, 33, 1], num_splits=2, seed=35, v_is_k_prefix=True), "auto"),
+    ("latent_g48_paged16_general", dict(batch=2, num_q_heads=48, num_kv_heads=1, qk_depth=576, ov_depth=512,
+                                        page_size=16, seq_lens=[517, 64], num_splits=0, seed=36,
+                                        v_is_k_prefix=True), "auto"),
 ]
 
 
@@ -181,7 +193,7 @@ def test_combine_only_on_oracle_partials(Dv, P):
 # ---------------------------------------------------------------------------
 # the named workloads at full size
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("name", ["tiny", "gqa", "long"])
+@pytest.mark.parametrize("name", ["tiny", "gqa", "long", "latent"])
 def test_workload_full(name):
     check_case(workload(name), f"workload {name}")
 
