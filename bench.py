@@ -88,8 +88,7 @@ def main():
     chunk, max_splits = api.choose_splits(prob, case.num_splits)
     B, Hq, Dv = prob.batch, prob.num_q_heads, prob.ov_depth
     out = torch.empty((B, Hq, Dv), dtype=torch.bfloat16, device=dev)
-    part_o = torch.empty((B, Hq, max_splits, Dv), dtype=torch.float32, device=dev)
-    part_ml = torch.empty((B, Hq, max_splits, 2), dtype=torch.float32, device=dev)
+    part_o, part_ml = api.alloc_partials(prob, chunk, max_splits, dev)
     comb = (torch.empty_like(out), torch.empty((B, Hq), dtype=torch.float32, device=dev),
             torch.empty((B, Hq, Dv), dtype=torch.float32, device=dev))
 

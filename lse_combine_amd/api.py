@@ -113,18 +113,43 @@ def decode_attn(q, k_cache, v_cache, page_table, seq_lens, scale, num_splits=0, 
     return out
 
 
+def alloc_partials(problem: DaProblem, chunk_tokens, max_splits, device):
+    """Buffers for pass 1 / pass 2 of the split API.
+
+    Fixed chunks (chunk_tokens > 0): part_o [B, Hq, max_splits, Dv] and part_ml
+    [B, Hq, max_splits, 2]. Equal-share schedule (chunk_tokens == 0, max_splits =
+    workers): part_o [slots, Hq, Dv] with slots = max_splits + B, and part_ml a flat
+    fp32 buffer of slots * Hq (m, l) pairs followed by the int32 (first slot, count)
+    pair of each sequence (see ``slot_table``).
+    """
+    B, Hq, Dv = problem.batch, problem.num_q_heads, problem.ov_depth
+    f32 = dict(dtype=torch.float32, device=device)
+    if chunk_tokens == 0:
+        slots = max_splits + B
+        return torch.zeros((slots, Hq, Dv), **f32), torch.zeros(slots * Hq * 2 + 2 * B, **f32)
+    return torch.zeros((B, Hq, max_splits, Dv), **f32), torch.zeros((B, Hq, max_splits, 2), **f32)
+
+
+def slot_table(problem: DaProblem, max_splits, part_ml):
+    """Equal-share schedule: split part_ml into (ml [slots, Hq, 2] fp32, table [B, 2] int32)."""
+    B, Hq = problem.batch, problem.num_q_heads
+    slots = max_splits + B
+    ml = part_ml[:slots * Hq * 2].view(slots, Hq, 2)
+    table = part_ml[slots * Hq * 2:slots * Hq * 2 + 2 * B].view(torch.int32).view(B, 2)
+    return ml, table
+
+
 def partition(q, k_cache, v_cache, page_table, seq_lens, scale, chunk_tokens, max_splits, *, page_size=0,
               max_seq_len=None, v_is_k_prefix=False, ov_depth=None, part_o=None, part_ml=None, kernel="auto"):
-    """Pass 1 only. Returns (part_o [B,Hq,P,Dv], part_ml [B,Hq,P,2]) fp32."""
+    """Pass 1 only. Returns (part_o, part_ml) fp32 in the layout ``alloc_partials`` describes."""
     lib = _lib.load()
     prob = make_problem(q, k_cache, v_cache, page_table, page_size=page_size, max_seq_len=max_seq_len,
                         v_is_k_prefix=v_is_k_prefix, ov_depth=ov_depth, kernel=kernel)
     _check_tensors(q, k_cache, v_cache, page_table, seq_lens)
-    B, Hq, Dv = prob.batch, prob.num_q_heads, prob.ov_depth
-    if part_o is None:
-        part_o = torch.zeros((B, Hq, max_splits, Dv), dtype=torch.float32, device=q.device)
-    if part_ml is None:
-        part_ml = torch.zeros((B, Hq, max_splits, 2), dtype=torch.float32, device=q.device)
+    if part_o is None or part_ml is None:
+        po, pml = alloc_partials(prob, chunk_tokens, max_splits, q.device)
+        part_o = po if part_o is None else part_o
+        part_ml = pml if part_ml is None else part_ml
     check(lib.decode_attn_partition(ctypes.byref(prob), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
                                     _ptr(seq_lens), float(scale), int(chunk_tokens), int(max_splits),
                                     _ptr(part_o), _ptr(part_ml), _stream()))

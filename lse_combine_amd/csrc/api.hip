@@ -125,11 +125,35 @@ void mfma_shape(const da_problem* p, int32_t max_splits, int cus, int* HG, int* 
   *KS = 8 / hg > 0 ? 8 / hg : 1;
 }
 
+// Equal-share schedule shape (automatic splits on the matrix-core kernel): one 8-wave
+// workgroup per CU. HG kv heads per workgroup as in mfma_shape, shrunk while even the
+// largest possible problem (every sequence at max_seq_len) could not give each CU a share
+// of kMinShareTiles tiles; W workers per head group so that W x groups ~ CUs.
+void share_shape(const da_problem* p, int cus, int* HG, int* KS, int* W) {
+  const int64_t tiles_max = (int64_t)p->batch * ceil_div(p->max_seq_len > 0 ? p->max_seq_len : 1, kTileKeys);
+  int hg = p->num_kv_heads < 8 ? p->num_kv_heads : 8;
+  auto groups = [&](int h) { return (int64_t)((p->num_kv_heads + h - 1) / h); };
+  while (hg > 1 && (tiles_max / da::kMinShareTiles) * groups(hg) < (int64_t)cus) hg = (hg + 1) / 2;
+  *HG = hg;
+  *KS = 8 / hg > 0 ? 8 / hg : 1;
+  const int64_t w = ceil_div(cus, groups(hg));
+  *W = (int)(w < 1 ? 1 : w);
+}
+
 // Workgroups of the partition kernel that fit on one compute unit at once.
 int wgs_per_cu(Variant v) { return v == kVarMfma128 ? 1 : 2; }
 
 int choose(const da_problem* p, Variant var, int32_t num_splits, int cus, int32_t* chunk_out, int32_t* splits_out) {
   if (num_splits < 0) return fail(DA_EINVAL, "num_splits must be >= 0 (0 = automatic)");
+  if (num_splits == 0 && var == kVarMfma128) {
+    // automatic on the matrix-core kernel: equal shares of all keys over one workgroup
+    // per CU (chunk 0 names this schedule; max_splits = workers)
+    int HG, KS, W;
+    share_shape(p, cus, &HG, &KS, &W);
+    *chunk_out = 0;
+    *splits_out = W;
+    return DA_OK;
+  }
   const int unit = chunk_unit(p);
   const int64_t maxlen = p->max_seq_len > 0 ? p->max_seq_len : 1;
   int64_t C;
@@ -160,17 +184,40 @@ int choose(const da_problem* p, Variant var, int32_t num_splits, int cus, int32_
   return DA_OK;
 }
 
-void ws_layout(const da_problem* p, int32_t max_splits, size_t* ml_off, size_t* o_off, size_t* total) {
-  const size_t rows = (size_t)p->batch * p->num_q_heads * (size_t)max_splits;
-  const size_t ml = (rows * 2 * sizeof(float) + 255) & ~(size_t)255;
+// Partial rows of a schedule: fixed chunks B * Hq * max_splits; equal shares
+// (chunk == 0) (max_splits + B) slots of Hq rows each.
+size_t partial_rows(const da_problem* p, int32_t chunk, int32_t max_splits) {
+  if (chunk == 0) return ((size_t)max_splits + (size_t)p->batch) * (size_t)p->num_q_heads;
+  return (size_t)p->batch * p->num_q_heads * (size_t)max_splits;
+}
+
+// Workspace: part_ml (fp32 pairs; with equal shares followed by the int32 (first slot,
+// count) table of the B sequences), then part_o, each padded to 256 bytes.
+void ws_layout(const da_problem* p, int32_t chunk, int32_t max_splits, size_t* ml_off, size_t* o_off,
+               size_t* total) {
+  const size_t rows = partial_rows(p, chunk, max_splits);
+  const size_t meta = chunk == 0 ? (size_t)p->batch * 2 * sizeof(int32_t) : 0;
+  const size_t ml = (rows * 2 * sizeof(float) + meta + 255) & ~(size_t)255;
   const size_t o = (rows * (size_t)p->ov_depth * sizeof(float) + 255) & ~(size_t)255;
   *ml_off = 0;
   *o_off = ml;
   *total = ml + o;
 }
 
-int check_split_args(const da_problem* p, int32_t chunk, int32_t max_splits) {
-  if (chunk <= 0 || chunk % kTileKeys) return fail(DA_EINVAL, "chunk_tokens must be a positive multiple of %d (got %d)", kTileKeys, chunk);
+// The (first slot, count) table that follows the (m, l) pairs in part_ml (equal shares).
+int32_t* meta_of(const da_problem* p, int32_t max_splits, const float* part_ml) {
+  return (int32_t*)(part_ml + partial_rows(p, 0, max_splits) * 2);
+}
+
+int check_split_args(const da_problem* p, Variant var, int32_t chunk, int32_t max_splits) {
+  if (chunk == 0) {
+    if (var != kVarMfma128)
+      return fail(DA_EUNSUPPORTED, "chunk_tokens 0 (equal-share schedule) needs the matrix-core depth-128 kernel");
+    if (max_splits < 1 || max_splits > 65535)
+      return fail(DA_EINVAL, "equal-share schedule: max_splits (workers) must be in [1, 65535] (got %d)", max_splits);
+    return DA_OK;
+  }
+  if (chunk < 0 || chunk % kTileKeys) return fail(DA_EINVAL, "chunk_tokens must be 0 or a positive multiple of %d (got %d)", kTileKeys, chunk);
   if (p->qk_depth == 576 && p->page_size > 0 && (int64_t)chunk > 255LL * p->page_size)
     return fail(DA_EUNSUPPORTED, "latent-shared kernel: chunk_tokens must be <= 255 pages (%d keys)", 255 * p->page_size);
   const int64_t maxlen = p->max_seq_len > 0 ? p->max_seq_len : 1;
@@ -198,7 +245,12 @@ int launch_partition(const da_problem* p, Variant var, const da::PartArgs& a, hi
       break;
     case kVarMfma128: {
       int HG, KS;
-      mfma_shape(p, a.max_splits, cus, &HG, &KS);
+      if (a.workers > 0) {
+        int W;
+        share_shape(p, cus, &HG, &KS, &W);
+      } else {
+        mfma_shape(p, a.max_splits, cus, &HG, &KS);
+      }
       e = da::launch_partition_mfma128(a, pm, HG, KS, s);
       break;
     }
@@ -229,6 +281,10 @@ int launch_combine(const da_problem* p, const int32_t* lens, float scale, int32_
   c.max_seq_len = p->max_seq_len;
   c.kv_cap_clamp = p->page_size == 0 ? p->kv_capacity : 0;
   c.skip_single = skip_single;
+  if (chunk == 0) {
+    c.meta = meta_of(p, max_splits, pml);
+    c.slots = max_splits + p->batch;
+  }
   c.scale = scale;
   c.c = scale * 1.4426950408889634f;
   (void)hipGetLastError();
@@ -273,6 +329,7 @@ PartArgs build_part_args(const da_problem* p, const void* q, const void* k, cons
   a.max_seq_len = p->max_seq_len;
   a.chunk = chunk;
   a.max_splits = max_splits;
+  a.workers = chunk == 0 ? max_splits : 0;
   a.scale = scale;
   a.c = scale * 1.4426950408889634f;
   return a;
@@ -307,7 +364,7 @@ int da_workspace_bytes(const da_problem* p, int32_t num_splits, size_t* bytes) {
   r = choose(p, v, num_splits, device_num_cus(), &C, &P);
   if (r) return r;
   size_t a, b;
-  ws_layout(p, P, &a, &b, bytes);
+  ws_layout(p, C, P, &a, &b, bytes);
   return ok();
 }
 
@@ -325,7 +382,7 @@ int decode_attn_splitk(const da_problem* p, const void* q, const void* k_cache, 
   int32_t C, P;
   if ((r = choose(p, var, num_splits, cus, &C, &P))) return r;
   size_t ml_off, o_off, need;
-  ws_layout(p, P, &ml_off, &o_off, &need);
+  ws_layout(p, C, P, &ml_off, &o_off, &need);
   if (!workspace || ((uintptr_t)workspace & 255))
     return fail(DA_EWORKSPACE, "workspace must be non-NULL and 256-byte aligned");
   if (workspace_bytes < need)
@@ -336,6 +393,7 @@ int decode_attn_splitk(const da_problem* p, const void* q, const void* k_cache, 
   da::PartArgs a = da::build_part_args(p, q, k_cache, v_cache, page_table, seq_lens, scale, C, P);
   a.part_o = po;
   a.part_ml = pml;
+  if (C == 0) a.meta = meta_of(p, P, pml);
   a.out = (uint16_t*)out;
   a.lse = lse_out;
   a.o32 = o_f32_out;
@@ -353,11 +411,12 @@ int decode_attn_partition(const da_problem* p, const void* q, const void* k_cach
   if (r) return r;
   if ((r = check_inputs(p, q, k_cache, v_cache, page_table, seq_lens))) return r;
   if ((r = check_scale(scale))) return r;
-  if ((r = check_split_args(p, chunk_tokens, max_splits))) return r;
+  if ((r = check_split_args(p, var, chunk_tokens, max_splits))) return r;
   if (!part_o || !part_ml) return fail(DA_EINVAL, "part_o and part_ml must be non-NULL");
   da::PartArgs a = da::build_part_args(p, q, k_cache, v_cache, page_table, seq_lens, scale, chunk_tokens, max_splits);
   a.part_o = part_o;
   a.part_ml = part_ml;
+  if (chunk_tokens == 0) a.meta = meta_of(p, max_splits, part_ml);
   a.direct_single = 0;
   if ((r = launch_partition(p, var, a, (hipStream_t)stream, device_num_cus()))) return r;
   return ok();
@@ -366,14 +425,14 @@ int decode_attn_partition(const da_problem* p, const void* q, const void* k_cach
 int decode_attn_combine(const da_problem* p, const int32_t* seq_lens, float scale, int32_t chunk_tokens,
                         int32_t max_splits, const float* part_o, const float* part_ml, void* out, float* lse_out,
                         float* o_f32_out, void* stream) {
-  Variant var;
+  Variant var = kVarFma;
   int r = check_problem(p, &var);
   if (r && r != DA_EUNSUPPORTED) return r;
   if (p->ov_depth != 128 && p->ov_depth != 512)
     return fail(DA_EUNSUPPORTED, "combine supports ov_depth 128 or 512 (got %d)", p->ov_depth);
   if (!seq_lens || !part_o || !part_ml || !out) return fail(DA_EINVAL, "seq_lens, part_o, part_ml and out must be non-NULL");
   if ((r = check_scale(scale))) return r;
-  if ((r = check_split_args(p, chunk_tokens, max_splits))) return r;
+  if ((r = check_split_args(p, var, chunk_tokens, max_splits))) return r;
   if ((r = launch_combine(p, seq_lens, scale, chunk_tokens, max_splits, part_o, part_ml, out, lse_out, o_f32_out, 0,
                           (hipStream_t)stream)))
     return r;

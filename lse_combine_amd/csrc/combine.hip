@@ -10,7 +10,9 @@
 //     O = sum_p e_p O_p / Gsum   (= sum_p w_p O_p with w_p = e_p / Gsum)
 //     LSE = scale * Gmax + ln Gsum,   out = bf16(O) (round to nearest even)
 // Partitions with l_p == 0 are skipped (weight 0); a row with no keys gets O = 0 and
-// LSE = -inf.
+// LSE = -inf. With fixed chunks a row's partials are contiguous ([B][Hq][max_splits]);
+// with the equal-share schedule they sit in consecutive slots ([slot][Hq]) named by the
+// per-sequence (first slot, count) table that pass 1 wrote.
 #include "da_device.h"
 
 namespace da {
@@ -26,20 +28,34 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
   const int64_t row = (int64_t)blockIdx.x * RPB + r_in;
   if (row >= (int64_t)a.B * a.Hq) return;
   const int b = (int)(row / a.Hq);
-  int L = a.seq_lens[b];
-  L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
-  if (a.kv_cap_clamp > 0 && L > a.kv_cap_clamp) L = a.kv_cap_clamp;
-  const int P_b = min((L + a.chunk - 1) / a.chunk, a.max_splits);
+  // partials of this row: P_b of them, `stride` partial rows apart, from partial row `first`
+  int P_b;
+  int64_t first, stride;
+  if (a.meta) {
+    // equal-share schedule: slots first .. first + P_b - 1 hold all heads of sequence b
+    // (clamped to the slots that exist, so a stale table cannot send loads astray)
+    const int s0 = min(max(a.meta[2 * b], 0), a.slots - 1);
+    P_b = min(max(a.meta[2 * b + 1], 0), a.slots - s0);
+    first = (int64_t)s0 * a.Hq + (row - (int64_t)b * a.Hq);
+    stride = a.Hq;
+  } else {
+    int L = a.seq_lens[b];
+    L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
+    if (a.kv_cap_clamp > 0 && L > a.kv_cap_clamp) L = a.kv_cap_clamp;
+    P_b = min((L + a.chunk - 1) / a.chunk, a.max_splits);
+    first = row * a.max_splits;
+    stride = 1;
+  }
   if (a.skip_single && P_b == 1) return;
 
-  const float2* ml = (const float2*)(a.part_ml + row * a.max_splits * 2);
-  const float* po = a.part_o + row * a.max_splits * DV + ch * 4;
+  const float2* ml = (const float2*)a.part_ml + first;
+  const float* po = a.part_o + first * DV + ch * 4;
   // Gmax over the live partitions
   float M = -INFINITY;
   for (int p0 = 0; p0 < P_b; p0 += kBatch) {
     float2 v[kBatch];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) v[i] = (p0 + i < P_b) ? ml[p0 + i] : make_float2(-INFINITY, 0.f);
+    for (int i = 0; i < kBatch; ++i) v[i] = (p0 + i < P_b) ? ml[(p0 + i) * stride] : make_float2(-INFINITY, 0.f);
 #pragma unroll
     for (int i = 0; i < kBatch; ++i)
       if (v[i].y > 0.f) M = fmaxf(M, v[i].x);
@@ -53,8 +69,8 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const bool in = p0 + i < P_b;
-      v[i] = in ? ml[p0 + i] : make_float2(-INFINITY, 0.f);
-      o[i] = in ? *(const f32x4*)(po + (int64_t)(p0 + i) * DV) : f32x4{0.f, 0.f, 0.f, 0.f};
+      v[i] = in ? ml[(p0 + i) * stride] : make_float2(-INFINITY, 0.f);
+      o[i] = in ? *(const f32x4*)(po + (p0 + i) * stride * DV) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {

@@ -63,6 +63,39 @@ __device__ __forceinline__ int64_t key_row(const PartArgs& a, int b, int t) {
   return (int64_t)page * a.page_size + (t - pi * a.page_size);
 }
 
+__device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+template <typename T>
+__device__ __forceinline__ T wave_incl_scan(T v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const T u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+// Value of lane j (j uniform) as a wave-uniform value.
+__device__ __forceinline__ int lane_value(int v, int j) { return __builtin_amdgcn_readlane(v, j); }
+__device__ __forceinline__ int64_t lane_value(int64_t v, int j) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, j);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), j);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Equal-share schedule. The 32-key tiles of all sequences, concatenated in batch order,
+// number U; worker w of W takes tiles [floor(w U / W), floor((w + 1) U / W)). This is
+// the worker whose share holds tile t (0 <= t < U, 1 <= W <= U).
+__device__ __forceinline__ int64_t share_owner(int64_t t, int64_t U, int64_t W) {
+  return ((t + 1) * W + U - 1) / U - 1;
+}
+
 // Store one float4 of a finished (head, depth) unit: either the final outputs of a
 // single-partition row or the normalised partial of partition p.
 __device__ __forceinline__ void store_unit(const PartArgs& a, int b, int hq, int p, bool direct,
@@ -76,7 +109,8 @@ __device__ __forceinline__ void store_unit(const PartArgs& a, int b, int hq, int
     if (a.o32) *(f32x4*)(a.o32 + row * a.Dv + d0) = o;
     if (write_ml && a.lse) a.lse[row] = a.scale * M + logf(Lsum);
   } else {
-    const int64_t pr = row * a.max_splits + p;
+    // fixed chunks: p is the partition of sequence b; equal shares: p is the slot
+    const int64_t pr = a.workers ? (int64_t)p * a.Hq + hq : row * a.max_splits + p;
     *(f32x4*)(a.part_o + pr * a.Dv + d0) = o;
     if (write_ml) {
       float2 ml;

@@ -21,8 +21,9 @@ struct PartArgs {
   const void* v;            // cache rows of v_row_len elements (== k when V is a K prefix)
   const int32_t* page_table;
   const int32_t* seq_lens;
-  float* part_o;            // [B][Hq][max_splits][Dv]
-  float* part_ml;           // [B][Hq][max_splits][2]
+  float* part_o;            // fixed chunks: [B][Hq][max_splits][Dv]; equal shares: [slots][Hq][Dv]
+  float* part_ml;           // fixed chunks: [B][Hq][max_splits][2];  equal shares: [slots][Hq][2]
+  int32_t* meta;            // equal shares: [B][2] (first slot, partition count) per sequence
   uint16_t* out;            // bf16 [B][Hq][Dv]; written directly by single-partition rows
   float* lse;               // optional
   float* o32;               // optional
@@ -31,6 +32,8 @@ struct PartArgs {
   int32_t page_size, pt_stride, num_pages, kv_capacity, max_seq_len;
   int32_t page_shift;       // log2(page_size) when it is a power of two, else -1
   int32_t chunk, max_splits;
+  int32_t workers;          // 0: fixed chunks of `chunk` keys; > 0: equal-share schedule over
+                            // this many workers (grid.x), slots = workers + B
   int32_t direct_single;    // 1: rows whose sequence has a single partition write out/lse/o32
   float scale;              // softmax scale
   float c;                  // scale * log2(e)
@@ -39,6 +42,8 @@ struct PartArgs {
 struct CombineArgs {
   const float* part_o;
   const float* part_ml;
+  const int32_t* meta;      // equal shares: per-sequence (first slot, count); NULL: fixed chunks
+  int32_t slots;            // equal shares: number of slots (workers + B)
   const int32_t* seq_lens;
   uint16_t* out;
   float* lse;
@@ -48,6 +53,10 @@ struct CombineArgs {
   int32_t skip_single;      // 1: rows with one partition were finished by pass 1
   float scale, c;
 };
+
+// Equal-share schedule: a workgroup (worker) gets at least this many 32-key tiles
+// (when there are that many), so small problems are not cut into slivers.
+constexpr int kMinShareTiles = 8;
 
 // Kernel arguments of a partition launch for a validated problem (api.hip).
 PartArgs build_part_args(const ::da_problem* p, const void* q, const void* k, const void* v,

@@ -47,7 +47,7 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kTile = 32;
-constexpr int kMaxWaves = 16;
+constexpr int kMaxWaves = 8;
 constexpr int kVBytes = kTile * kD * 2;       // one wave's V tile in LDS
 constexpr int kWaveBytes = kVBytes + 256;     // + merge (m, l) for up to 16 heads
 constexpr int kMaxLdsPages = 512;             // page indices of one segment staged in LDS
@@ -88,42 +88,33 @@ __device__ __forceinline__ float max_over_key_groups(float v) {
   return fmaxf(v, __shfl_xor(v, 32));
 }
 
-template <bool HL, int PM>
-// four waves per SIMD (<= 128 VGPRs); general paging needs a few more registers
-__global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(PM == kPagedGeneral ? 3 : 4)))
-void partition_gqa_kernel(PartArgs a, int HG, int KS) {
-  const int p = blockIdx.x, kg = blockIdx.y, b = blockIdx.z;
-  // sequence length (loaded by a vector load: state that it is uniform)
-  const int L = __builtin_amdgcn_readfirstlane(attended_len(a, b, PM == kContiguous));
-  const int start = p * a.chunk;
-  if (start >= L) return;
-  const int end = min(start + a.chunk, L);
-  const int P_b = min((L + a.chunk - 1) / a.chunk, a.max_splits);
-  const bool direct = a.direct_single && P_b == 1;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
-  const int NW = HG * KS;
-  const int member = w % HG, ks = w / HG;
-  const int kvh = kg * HG + member;
-  const bool wave_active = kvh < a.Hkv;
-  const int n = lane & 15, qd = lane >> 4;
-  const int g = a.g;
-  const int hc = HL ? (n & 7) : n;          // head index of this lane's MFMA column
-  const bool col_valid = hc < g;
-  const bool is_lo = HL && n >= 8;
-  const float lo_mask = is_lo ? 1.f : 0.f;
-
-  extern __shared__ __attribute__((aligned(16))) char smem[];   // NW * kWaveBytes (launch size)
-  __shared__ int pages_s[kMaxLdsPages];
-  char* vt = smem + w * kWaveBytes;
-  int first_page = 0;   // page index held by pages_s[0] in the current segment
-
-  // zero this wave's V tile once: direct-to-LDS loads outside the buffer range may leave
-  // rows untouched, and those rows must hold finite values (they meet p = 0)
+// Zero a wave's V tile once per launch: direct-to-LDS loads outside the buffer range
+// leave their rows untouched, and those rows must hold finite values (they meet p = 0).
+__device__ __forceinline__ void zero_v_tile(char* vt, int lane) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) *(u32x4*)(vt + (i * 64 + lane) * 16) = u32x4{0u, 0u, 0u, 0u};
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the zeros are in place before any load lands
+}
+
+// Per-wave constants of a workgroup: its place in the (kv head, key split) grid and the
+// lane's MFMA coordinates.
+struct WaveInfo {
+  int HG, KS, NW, w, ks, kvh, lane, n, qd, hc;
+  bool wave_active, col_valid, is_lo;
+};
+
+// One piece of work: keys [start, end) of sequence b for this workgroup's kv heads.
+// Writes the normalised partial and (m, l) of partition / slot p, or the finished bf16
+// row when `direct` (the sequence has a single partition).
+template <bool HL, int PM>
+__device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv, char* smem, int* pages_s, int b,
+                                          int start, int end, int p, bool direct) {
+  const int lane = wv.lane, n = wv.n, qd = wv.qd, hc = wv.hc, kvh = wv.kvh, ks = wv.ks, KS = wv.KS;
+  const int g = a.g;
+  const bool wave_active = wv.wave_active, col_valid = wv.col_valid, is_lo = wv.is_lo;
+  const float lo_mask = is_lo ? 1.f : 0.f;
+  char* vt = smem + wv.w * kWaveBytes;
+  int first_page = 0;   // page index held by pages_s[0] in the current segment
 
   // q as the B operand of S^T = K q^T: column n, depth 32j + 8qd .. +8.
   bf16x8 qf[4];
@@ -151,7 +142,7 @@ void partition_gqa_kernel(PartArgs a, int HG, int KS) {
   f32x4 o[8];
 #pragma unroll
   for (int db = 0; db < 8; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-
+  const int tid = threadIdx.x, NW = wv.NW, HG = wv.HG, kg = blockIdx.y;
   // first cache row of the tile starting at t0 (contiguous / aligned pages: the tile
   // is 32 consecutive rows), and the row of key t in the general paged case
   auto tile_row0 = [&](int t0) -> int64_t {
@@ -422,11 +413,181 @@ void partition_gqa_kernel(PartArgs a, int HG, int KS) {
     }
     store_unit(a, b, kv2 * g + h, p, direct, d0, acc * (1.f / Ls), M, Ls, d0 == 0);
   }
+  // the merge read other waves' V tiles: the next piece may refill them only after this
+  __syncthreads();
+}
+
+// A piece of work as wave 0 of a workgroup publishes it to the other waves.
+struct Piece {
+  int b, start, end, slot_direct;   // slot_direct = slot * 2 + (sequence has one partition)
+};
+struct PieceTable {
+  Piece row[64];      // indexed by lane = sequence within the current chunk of 64
+  uint32_t mask_lo, mask_hi;
+  int done;
+  // scan state, kept here rather than in registers across the pieces (wave 0 only)
+  int c0, slot_base;
+  int64_t U, Wact, ts, te, tile_base;
+};
+
+template <bool HL, int PM>
+// one 8-wave workgroup per CU (two waves per SIMD): the tile loop needs about 160 VGPRs,
+// and eight waves per CU already keep the memory system busy under the equal-share schedule
+__global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void partition_gqa_kernel(PartArgs a, int HG, int KS) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];   // NW * kWaveBytes (launch size)
+  __shared__ int pages_s[kMaxLdsPages];
+  __shared__ PieceTable table;
+  WaveInfo wv;
+  wv.HG = HG;
+  wv.KS = KS;
+  wv.NW = HG * KS;
+  wv.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, uniform
+  wv.ks = wv.w / HG;
+  wv.kvh = blockIdx.y * HG + wv.w % HG;
+  wv.wave_active = wv.kvh < a.Hkv;
+  wv.lane = threadIdx.x & 63;
+  wv.n = wv.lane & 15;
+  wv.qd = wv.lane >> 4;
+  wv.hc = HL ? (wv.n & 7) : wv.n;          // head index of this lane's MFMA column
+  wv.col_valid = wv.hc < a.g;
+  wv.is_lo = HL && wv.n >= 8;
+  const int lane = wv.lane;
+
+  if (a.workers == 0) {
+    // fixed chunks: partition blockIdx.x of sequence blockIdx.z (sequence length loaded by a
+    // vector load: state that it is uniform)
+    const int L = __builtin_amdgcn_readfirstlane(attended_len(a, blockIdx.z, PM == kContiguous));
+    if ((int)blockIdx.x * a.chunk >= L) return;
+  }
+  zero_v_tile(smem + wv.w * kWaveBytes, lane);
+
+  // Equal shares: worker wid = blockIdx.x takes tiles [ts, te) of the U 32-key tiles of
+  // all sequences concatenated in batch order (at least kMinShareTiles per worker, so
+  // fewer workers than launched may be active). Each sequence the share meets is one
+  // piece, stored in slot (first slot of the sequence) + (wid - first worker of the
+  // sequence). Wave 0 scans seq_lens 64 sequences at a time and publishes the pieces of
+  // each chunk in LDS; every wave then runs them in order.
+  const int wid = blockIdx.x;
+  uint64_t pending = 0;
+  bool fixed_taken = false;
+  if (a.workers > 0 && wv.w == 0) {
+    int64_t U = 0;
+    for (int c = 0; c < a.B; c += 64) {
+      const int bb = c + lane;
+      const int64_t nt = bb < a.B ? (attended_len(a, bb, PM == kContiguous) + kTile - 1) / kTile : 0;
+      U += wave_sum_i64(nt);
+    }
+    U = lane_value(U, 0);
+    int64_t Wact = U / kMinShareTiles;
+    Wact = Wact < 1 ? 1 : (Wact > a.workers ? a.workers : Wact);
+    if (lane == 0) {
+      table.U = U;
+      table.Wact = Wact;
+      table.ts = (int64_t)wid * U / Wact;
+      table.te = (int64_t)(wid + 1) * U / Wact;
+      table.tile_base = 0;   // tiles of the sequences before the current chunk
+      table.slot_base = 0;   // slots of the sequences before the current chunk
+      table.c0 = -64;
+    }
+  }
+
+  for (;;) {
+    int b, start, end, p;
+    bool direct;
+    if (a.workers == 0) {
+      if (fixed_taken) break;
+      fixed_taken = true;
+      b = blockIdx.z;
+      p = blockIdx.x;
+      const int L = __builtin_amdgcn_readfirstlane(attended_len(a, b, PM == kContiguous));
+      start = p * a.chunk;
+      end = min(start + a.chunk, L);
+      direct = a.direct_single && min((L + a.chunk - 1) / a.chunk, a.max_splits) == 1;
+    } else {
+      while (pending == 0) {
+        __syncthreads();   // every wave is done with the previous table
+        if (wv.w == 0) {
+          const int64_t U = table.U, Wact = table.Wact, ts = table.ts, te = table.te;
+          int64_t tile_base = table.tile_base;
+          int slot_base = table.slot_base;
+          const int c0 = table.c0 + 64;
+          // past the end of this share nothing is left, except for the last worker, which
+          // also writes the (first slot, count) of empty sequences at the very end
+          const bool done = wid >= Wact || c0 >= a.B || (tile_base >= te && wid != Wact - 1);
+          uint64_t mask = 0;
+          if (!done) {
+            const int bb = c0 + lane;
+            const int len = bb < a.B ? attended_len(a, bb, PM == kContiguous) : 0;
+            const int64_t nt = (len + kTile - 1) / kTile;
+            const int64_t incl = wave_incl_scan(nt);
+            const int64_t pre = tile_base + incl - nt;   // first tile of sequence bb
+            int64_t first = 0;                           // worker holding that tile
+            int count = 0;                               // partitions of sequence bb
+            if (nt > 0) {
+              first = share_owner(pre, U, Wact);
+              count = (int)(share_owner(pre + nt - 1, U, Wact) - first + 1);
+            }
+            const int sincl = wave_incl_scan(count);
+            const int slot = slot_base + sincl - count;
+            // (first slot, count) of each sequence for the combine, written by exactly one
+            // worker: the one whose share holds the sequence's first tile (the last one
+            // for trailing empty sequences)
+            if (blockIdx.y == 0 && bb < a.B) {
+              const int64_t writer = pre < U ? share_owner(pre, U, Wact) : Wact - 1;
+              if (writer == wid) {
+                a.meta[2 * bb] = slot;
+                a.meta[2 * bb + 1] = count;
+              }
+            }
+            const bool mine = bb < a.B && nt > 0 && pre < te && pre + nt > ts;
+            mask = __ballot(mine);
+            if (mine) {
+              const int64_t lo = (ts > pre ? ts : pre) - pre;
+              const int64_t hi = (te < pre + nt ? te : pre + nt) - pre;
+              Piece pc;
+              pc.b = bb;
+              pc.start = (int)lo * kTile;
+              pc.end = min((int)hi * kTile, len);
+              pc.slot_direct = (slot + (int)(wid - first)) * 2 + (count == 1 ? 1 : 0);
+              table.row[lane] = pc;
+            }
+            tile_base += lane_value(incl, 63);
+            slot_base += lane_value(sincl, 63);
+          }
+          if (lane == 0) {
+            table.mask_lo = (uint32_t)mask;
+            table.mask_hi = (uint32_t)(mask >> 32);
+            table.done = done ? 1 : 0;
+            table.c0 = c0;
+            table.tile_base = tile_base;
+            table.slot_base = slot_base;
+          }
+        }
+        __syncthreads();
+        if (__builtin_amdgcn_readfirstlane(table.done)) break;
+        pending = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)table.mask_hi) << 32) |
+                  (uint32_t)__builtin_amdgcn_readfirstlane((int)table.mask_lo);
+      }
+      if (pending == 0) break;
+      const int j = __builtin_ctzll(pending);
+      pending &= pending - 1;
+      b = __builtin_amdgcn_readfirstlane(table.row[j].b);
+      start = __builtin_amdgcn_readfirstlane(table.row[j].start);
+      end = __builtin_amdgcn_readfirstlane(table.row[j].end);
+      const int sd = __builtin_amdgcn_readfirstlane(table.row[j].slot_direct);
+      p = sd >> 1;
+      direct = a.direct_single && (sd & 1);
+    }
+    run_piece<HL, PM>(a, wv, smem, pages_s, b, start, end, p, direct);
+  }
 }
 
 template <bool HL>
 hipError_t launch_hl(const PartArgs& a, int pm, int HG, int KS, hipStream_t s) {
-  dim3 grid(a.max_splits, (a.Hkv + HG - 1) / HG, a.B), block(HG * KS * 64);
+  const unsigned groups = (unsigned)((a.Hkv + HG - 1) / HG);
+  const dim3 grid = a.workers > 0 ? dim3((unsigned)a.workers, groups, 1) : dim3((unsigned)a.max_splits, groups, (unsigned)a.B);
+  const dim3 block(HG * KS * 64);
   const size_t lds = (size_t)HG * KS * kWaveBytes;
   switch (pm) {
     case kContiguous:

@@ -11,5 +11,7 @@ from .decode_attention import (  # noqa: F401
     combine_fp64,
     decode_attention_fp64,
     decode_attention_splitk_fp64,
+    equal_share_pieces,
     partition_partials_fp64,
+    range_partials_fp64,
 )

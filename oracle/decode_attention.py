@@ -20,6 +20,9 @@ What is computed (single query per sequence, i.e. decode):
 * ``partition_partials_fp64`` -- pass 1 of split-K as the pages describe it:
   each key partition yields its row max, row sum and NORMALISED partial O
   (fa4_splitk_combine_write, second paragraph).
+* ``equal_share_pieces`` / ``range_partials_fp64`` -- the partition boundaries
+  of the equal-share schedule the automatic split uses, and pass 1 over such
+  explicit key ranges.
 * ``combine_fp64`` -- pass 2, the combine formula of fa4_splitk_combine_write
   (first paragraph) written out in the pages' exp2 form:
       Gmax = max_p max_p,  Gsum = sum_p sum_p * exp2((max_p - Gmax) * c),
@@ -159,6 +162,78 @@ def partition_partials_fp64(q, k_cache, v_cache, seq_lens, scale, chunk, num_par
                 m[b, hs, p] = mp[:, 0]
                 l[b, hs, p] = lp[:, 0]
                 O[b, hs, p] = (e @ V[lo:hi]) / lp
+    return m, l, O
+
+
+def equal_share_pieces(seq_lens, workers, tile=32, min_tiles=8):
+    """Partition boundaries of the equal-share split schedule.
+
+    The pages fix the number of partitions per sequence at compile time and say
+    nothing about how a runtime would cut a batch of unequal sequences; this is
+    the schedule the automatic split uses instead of fixed-length chunks. The
+    ``tile``-key tiles of all sequences are laid end to end in batch order and
+    numbered 0 .. U-1 (sequence b has ceil(L_b / tile) of them). With
+    W = min(workers, max(1, floor(U / min_tiles))) workers (so a worker owns at
+    least min_tiles tiles whenever U >= min_tiles), worker w owns tiles
+    floor(w U / W) .. floor((w + 1) U / W) - 1. Every non-empty overlap of a
+    worker's tiles with a sequence's tiles is one partition of that sequence;
+    partitions are numbered (slots) sequence by sequence, and by worker within a
+    sequence.
+
+    Returns (pieces, first, count): pieces is a list of (b, key_start, key_end,
+    slot) with key_end clipped to L_b; first[b] / count[b] are the first slot and
+    the number of partitions of sequence b (first[b] = the next free slot and
+    count[b] = 0 for an empty sequence).
+    """
+    lens = [max(0, int(x)) for x in seq_lens]
+    tiles = [-(-L // tile) for L in lens]
+    U = sum(tiles)
+    W = min(int(workers), max(1, U // min_tiles))
+    bounds = [w * U // W for w in range(W + 1)]
+    pieces, first, count = [], [], []
+    slot, pre = 0, 0
+    for b, (L, n) in enumerate(zip(lens, tiles)):
+        first.append(slot)
+        c = 0
+        for w in range(W):
+            lo, hi = max(bounds[w], pre), min(bounds[w + 1], pre + n)
+            if lo < hi:
+                pieces.append((b, (lo - pre) * tile, min((hi - pre) * tile, L), slot))
+                slot += 1
+                c += 1
+        count.append(c)
+        pre += n
+    return pieces, first, count
+
+
+def range_partials_fp64(q, k_cache, v_cache, seq_lens, scale, pieces, page_table=None, page_size=0,
+                        v_is_k_prefix=False, ov_depth=None):
+    """Pass-1 partials over explicit key ranges.
+
+    pieces: (b, key_start, key_end, slot) tuples as ``equal_share_pieces``
+    returns. For each piece and q head: the raw-unit max m, the sum
+    l = sum_t exp(scale * (x_t - m)) and the normalised O over keys
+    key_start .. key_end - 1 of sequence b (fa4_splitk_combine_write, second
+    paragraph). Returns (m [S, Hq], l [S, Hq], O [S, Hq, Dv]) indexed by slot,
+    S = 1 + the largest slot; slots no piece names hold (-inf, 0, 0).
+    """
+    B, Hq, Hkv, g, Dqk, Dv = _dims(q, k_cache, v_cache, v_is_k_prefix, ov_depth)
+    S = 1 + max((pc[3] for pc in pieces), default=-1)
+    m = np.full((S, Hq), -np.inf)
+    l = np.zeros((S, Hq))
+    O = np.zeros((S, Hq, Dv))
+    for b, lo, hi, slot in pieces:
+        for kvh in range(Hkv):
+            qg, K, V = _gather(q, k_cache, v_cache, b, kvh, g, hi, page_table, page_size,
+                               v_is_k_prefix, Dv)
+            x = qg @ K[lo:hi].T
+            mp = x.max(axis=1, keepdims=True)
+            e = np.exp(scale * (x - mp))
+            lp = e.sum(axis=1, keepdims=True)
+            hs = slice(kvh * g, (kvh + 1) * g)
+            m[slot, hs] = mp[:, 0]
+            l[slot, hs] = lp[:, 0]
+            O[slot, hs] = (e @ V[lo:hi]) / lp
     return m, l, O
 
 

@@ -93,10 +93,12 @@ def test_fixed_splits_match_the_named_workloads(lib):
                             v_is_k_prefix=1, max_pages_per_seq=128, max_seq_len=8192), 8) == (1024, 8)
 
 
-@pytest.mark.parametrize("L,n,ps", [(1000, 3, 0), (1000, 3, 64), (77, 5, 0), (5000, 7, 16), (1, 1, 0),
-                                    (4096, 4096, 0), (32768, 0, 64), (131072, 0, 64), (100, 0, 48)])
-def test_split_invariants(lib, L, n, ps):
-    kw = dict(max_seq_len=L)
+@pytest.mark.parametrize("L,n,ps,dtype", [(1000, 3, 0, 1), (1000, 3, 64, 1), (77, 5, 0, 1), (5000, 7, 16, 1),
+                                          (1, 1, 0, 1), (4096, 4096, 0, 1), (32768, 0, 64, 0), (131072, 0, 64, 0),
+                                          (100, 0, 48, 0)])
+def test_split_invariants(lib, L, n, ps, dtype):
+    # fixed chunks: explicit splits, and the automatic choice of the vector-ALU kernel (fp32)
+    kw = dict(max_seq_len=L, dtype=dtype)
     if ps:
         kw.update(page_size=ps, max_pages_per_seq=-(-L // ps))
     else:
@@ -108,6 +110,34 @@ def test_split_invariants(lib, L, n, ps):
     assert P == math.ceil(L / C) and (P - 1) * C < L <= P * C   # no empty trailing partition
     if n:
         assert P <= n
+
+
+@pytest.mark.parametrize("B,Hkv,L,cus,hg", [(32, 8, 32768, 256, 8), (8, 8, 4096, 256, 4), (1, 4, 131072, 256, 4),
+                                             (1, 1, 100, 256, 1), (2, 2, 300, 80, 1), (64, 8, 512, 304, 2)])
+def test_automatic_split_is_equal_shares_on_matrix_cores(lib, B, Hkv, L, cus, hg):
+    # bf16 GQA, automatic: chunk 0 names the equal-share schedule, max_splits the workers per
+    # kv-head group; one 8-wave workgroup per CU in total
+    p = prob(batch=B, num_q_heads=8 * Hkv, num_kv_heads=Hkv, max_seq_len=L, max_pages_per_seq=-(-L // 64))
+    C, W = splits(lib, p, 0, cus)
+    groups = -(-Hkv // hg)
+    assert C == 0 and W == -(-cus // groups)
+
+
+def test_equal_share_workspace_and_checks(lib):
+    p = prob(batch=3, num_q_heads=8, num_kv_heads=1, max_seq_len=1000, max_pages_per_seq=16)
+    n = ctypes.c_size_t()
+    assert lib.da_workspace_bytes(ctypes.byref(p), 0, ctypes.byref(n)) == DA_OK
+    C, W = splits(lib, p, 0)
+    assert C == 0
+    align = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    rows = (W + 3) * 8
+    assert n.value >= align(rows * 2 * 4 + 3 * 2 * 4) + align(rows * 128 * 4)
+    f = lib.decode_attn_partition
+    # chunk 0 needs the matrix-core kernel and 1 <= workers <= 65535
+    fp32 = prob(dtype=0)
+    assert f(ctypes.byref(fp32), FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, 0, 8, FAKE, FAKE, None) == DA_EUNSUPPORTED
+    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, 0, 0, FAKE, FAKE, None) == DA_EINVAL
+    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, -32, 8, FAKE, FAKE, None) == DA_EINVAL
 
 
 def test_workspace_bytes(lib):

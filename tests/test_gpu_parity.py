@@ -10,7 +10,7 @@ import torch
 
 from lse_combine_amd import api
 from lse_combine_amd.inputs import make_case, to_device, workload
-from oracle import combine_fp64, partition_partials_fp64
+from oracle import combine_fp64, equal_share_pieces, partition_partials_fp64, range_partials_fp64
 from parity_utils import assert_parity, np32, oracle_for
 
 pytestmark = pytest.mark.gpu
@@ -96,11 +96,30 @@ def test_empty_and_tiny_sequences():
 
 
 def test_poisoned_unattended_slots_are_never_read():
-    for pg, kern in [(64, "auto"), (16, "auto"), (0, "auto"), (64, "fma")]:
+    for pg, kern, n in [(64, "auto", 3), (16, "auto", 3), (0, "auto", 3), (64, "fma", 3), (64, "auto", 0),
+                        (0, "auto", 0)]:
         case = make_case("poison", batch=3, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=pg,
-                         seq_lens=[100, 1, 1025], num_splits=3, seed=41, poison=True, spare_pages=3)
-        out, lse, o32 = check_case(case, f"poison ps={pg} {kern}", kernel=kern)
+                         seq_lens=[100, 1, 1025], num_splits=n, seed=41, poison=True, spare_pages=3)
+        out, lse, o32 = check_case(case, f"poison ps={pg} {kern} splits={n}", kernel=kern)
         assert torch.isfinite(o32).all()
+
+
+@pytest.mark.parametrize("lens", [[0, 0, 0], [0] * 70 + [5], [3000] + [0] * 100 + [1, 2]],
+                         ids=["all_empty", "70_empty_then_one", "long_then_100_empty"])
+def test_automatic_split_edge_batches(lens):
+    case = make_case("auto_edge", batch=len(lens), num_q_heads=8, num_kv_heads=1, qk_depth=128, page_size=64,
+                     seq_lens=lens, num_splits=0, seed=46)
+    out, lse, o32 = check_case(case, f"auto edge B={len(lens)}")
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert torch.all(out[b].float() == 0) and torch.all(torch.isneginf(lse[b]))
+
+
+def test_automatic_split_many_sequences():
+    # more than 64 sequences: the schedule scans seq_lens in several chunks
+    case = make_case("auto_many", batch=150, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=32,
+                     len_range=(0, 700), num_splits=0, seed=47)
+    check_case(case, "auto B=150")
 
 
 def test_large_logits_overflow_safety():
@@ -158,6 +177,52 @@ def test_partition_partials_match_oracle():
     err = np.abs(po - O).max(-1)[live]
     ref = np.abs(O).max(-1)[live]
     assert (err / ref).max() <= 1e-5
+
+
+EQUAL_SHARE = [
+    # name, make_case kwargs, workers
+    ("ragged_paged64", dict(batch=5, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=64,
+                            seq_lens=[1000, 0, 2500, 64, 1], seed=50), 7),
+    ("many_short_contig", dict(batch=53, num_q_heads=8, num_kv_heads=1, qk_depth=128,
+                               seq_lens=[40] * 50 + [0] * 3, seed=51), 5),
+    ("two_scan_chunks", dict(batch=150, num_q_heads=8, num_kv_heads=2, qk_depth=128, page_size=32,
+                             len_range=(0, 300), seed=52), 9),
+    ("fewer_active_workers", dict(batch=2, num_q_heads=32, num_kv_heads=4, qk_depth=128, page_size=16,
+                                  seq_lens=[100, 50], seed=53), 64),
+    ("g16_two_mfma", dict(batch=3, num_q_heads=32, num_kv_heads=2, qk_depth=128, page_size=64,
+                          seq_lens=[3000, 5, 700], seed=54), 11),
+]
+
+
+@pytest.mark.parametrize("name,kw,workers", EQUAL_SHARE, ids=[c[0] for c in EQUAL_SHARE])
+def test_equal_share_partials_match_oracle(name, kw, workers):
+    print(f"[parity] equal shares {name} workers={workers}", flush=True)
+    case = make_case(name, num_splits=0, **kw)
+    dc = to_device(case)
+    prob = api.make_problem(dc.q, dc.k_cache, dc.v_cache, dc.page_table, page_size=case.page_size)
+    po_t, pml_t = api.partition(dc.q, dc.k_cache, dc.v_cache, dc.page_table, dc.seq_lens, case.scale, 0,
+                                workers, page_size=case.page_size)
+    torch.cuda.synchronize()
+    lens = case.seq_lens.numpy().astype(np.int64)
+    pieces, first, count = equal_share_pieces(lens, workers)
+    ml_t, table = api.slot_table(prob, workers, pml_t)
+    # the (first slot, count) table is integer work: exact
+    np.testing.assert_array_equal(table.cpu().numpy(), np.stack([first, count], -1))
+    pt = None if case.page_table is None else case.page_table.numpy()
+    m, l, O = range_partials_fp64(np32(case.q), np32(case.k_cache), np32(case.v_cache), lens, case.scale, pieces,
+                                  page_table=pt, page_size=case.page_size)
+    S = len(pieces)
+    ml, po = np32(ml_t)[:S], np32(po_t)[:S]
+    np.testing.assert_allclose(ml[..., 0], m, rtol=1e-5, atol=1e-4)
+    np.testing.assert_allclose(ml[..., 1], l, rtol=1e-5)
+    err = np.abs(po - O).max(-1)
+    ref = np.abs(O).max(-1)
+    assert (err / ref).max() <= 1e-5
+    # pass 2 on these partials gives the definition
+    out, lse, o32 = api.combine(prob, dc.seq_lens, case.scale, 0, workers, po_t, pml_t)
+    torch.cuda.synchronize()
+    Oref, Lref = oracle_for(case)
+    assert_parity(out, lse, o32, Oref, Lref, what=f"equal shares {name} combine")
 
 
 @pytest.mark.parametrize("Dv,P", [(128, 4), (128, 64), (512, 8)])

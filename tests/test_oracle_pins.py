@@ -20,7 +20,9 @@ from oracle import (
     combine_fp64,
     decode_attention_fp64,
     decode_attention_splitk_fp64,
+    equal_share_pieces,
     partition_partials_fp64,
+    range_partials_fp64,
 )
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -320,3 +322,84 @@ def test_golden_fixture(fn, case):
         np.testing.assert_allclose(LSE, np.array(case["expected_lse"]), rtol=1e-14)
     else:
         raise AssertionError(kind)
+
+
+# ---------------------------------------------------------------------------
+# the equal-share schedule of the automatic split and pass 1 over its ranges
+# ---------------------------------------------------------------------------
+def test_equal_share_pieces_worked_example():
+    # worked by hand: tiles of 32 keys per sequence [4, 0, 2, 2], U = 8; 3 workers with
+    # at least 2 tiles each -> W = min(3, 8 // 2) = 3, shares [0, 2), [2, 5), [5, 8)
+    pieces, first, count = equal_share_pieces([100, 0, 33, 64], workers=3, tile=32, min_tiles=2)
+    assert pieces == [(0, 0, 64, 0), (0, 64, 100, 1), (2, 0, 32, 2), (2, 32, 33, 3), (3, 0, 64, 4)]
+    assert first == [0, 2, 2, 4] and count == [2, 0, 2, 1]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_equal_share_pieces_cover_and_balance(seed):
+    r = np.random.default_rng(seed)
+    B = int(r.integers(1, 40))
+    lens = r.integers(0, 3000, B)
+    lens[r.random(B) < 0.2] = 0
+    workers = int(r.integers(1, 300))
+    pieces, first, count = equal_share_pieces(lens, workers)
+    tiles = [-(-int(L) // 32) for L in lens]
+    U = sum(tiles)
+    W = min(workers, max(1, U // 8))
+    # every key of every sequence exactly once, in order, cut only at tile boundaries
+    for b in range(B):
+        mine = [pc for pc in pieces if pc[0] == b]
+        assert len(mine) == count[b]
+        assert [pc[3] for pc in mine] == list(range(first[b], first[b] + count[b]))
+        pos = 0
+        for _, lo, hi, _ in mine:
+            assert lo == pos and hi > lo and lo % 32 == 0
+            pos = hi
+        assert pos == lens[b]
+    # slots are 0 .. S-1 in order; at most one extra slot per sequence boundary
+    assert [pc[3] for pc in pieces] == list(range(len(pieces)))
+    assert len(pieces) <= (W + B - 1 if U else 0)
+    # brute force over the tiles in batch order: the tiles of one piece belong to one
+    # worker, different pieces of one worker lie in different sequences, and the shares
+    # differ by at most one tile and (with enough tiles) hold at least the minimum
+    tile_owner = []
+    for w in range(W):
+        tile_owner += [w] * ((w + 1) * U // W - w * U // W)
+    assert len(tile_owner) == U
+    seq_of_tile = [b for b in range(B) for _ in range(tiles[b])]
+    piece_worker = {}
+    pos = 0
+    for b, lo, hi, slot in pieces:
+        n = -(-(hi - lo) // 32)
+        ws = set(tile_owner[pos:pos + n])
+        assert len(ws) == 1 and set(seq_of_tile[pos:pos + n]) == {b}
+        piece_worker[slot] = ws.pop()
+        pos += n
+    assert pos == U
+    per_worker = {}
+    for b, lo, hi, slot in pieces:
+        per_worker.setdefault(piece_worker[slot], []).append(b)
+    assert all(len(set(bs)) == len(bs) for bs in per_worker.values())
+    if U:
+        shares = [tile_owner.count(w) for w in range(W)]
+        assert max(shares) - min(shares) <= 1
+        if U >= 8:
+            assert min(shares) >= 8
+
+
+def test_range_partials_combine_to_the_definition():
+    q, k, v, lens, pt = rng_case(31, B=4, Hq=6, Hkv=2, D=8, L=(100, 0, 33, 64), paged=16)
+    O, LSE = decode_attention_fp64(q, k, v, lens, 0.3, page_table=pt, page_size=16)
+    pieces, first, count = equal_share_pieces(lens, workers=3, tile=32, min_tiles=2)
+    m, l, Op = range_partials_fp64(q, k, v, lens, 0.3, pieces, page_table=pt, page_size=16)
+    for b in range(4):
+        sl = slice(first[b], first[b] + count[b])
+        Oc, Lc = combine_fp64(m[sl].T, l[sl].T, Op[sl].transpose(1, 0, 2), 0.3)
+        np.testing.assert_allclose(Oc, O[b], atol=1e-14)
+        np.testing.assert_allclose(Lc, LSE[b], rtol=1e-14)
+    # a piece that is a fixed chunk equals pass 1 with that chunk
+    mf, lf, Of = partition_partials_fp64(q, k, v, lens, 0.3, chunk=64, num_partitions=2,
+                                         page_table=pt, page_size=16)
+    np.testing.assert_allclose(m[0], mf[0, :, 0], rtol=1e-15)
+    np.testing.assert_allclose(l[0], lf[0, :, 0], rtol=1e-14)
+    np.testing.assert_allclose(Op[0], Of[0, :, 0], atol=1e-15)
