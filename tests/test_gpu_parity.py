@@ -225,7 +225,7 @@ def test_equal_share_partials_match_oracle(name, kw, workers):
     assert_parity(out, lse, o32, Oref, Lref, what=f"equal shares {name} combine")
 
 
-@pytest.mark.parametrize("Dv,P", [(128, 4), (128, 64), (512, 8)])
+@pytest.mark.parametrize("Dv,P", [(128, 4), (128, 16), (128, 24), (128, 64), (512, 8), (512, 20)])
 def test_combine_only_on_oracle_partials(Dv, P):
     # oracle partials (with empty partitions) fed to the HIP combine
     r = np.random.default_rng(Dv + P)
