@@ -44,7 +44,34 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 // byte offset of 16-byte chunk c of row r in a swizzled LDS row block
 __device__ __forceinline__ int swz(int r, int c) { return r * kRowBytes + ((c ^ (r & 7)) << 4); }
 
+// max over the four lanes n, n+16, n+32, n+48 on the VALU (v_permlane16/32_swap), without
+// the LDS permute unit that the tile's operand reads keep busy. Written out because the
+// compiler folds the two results of a swap of a value with itself into one; the s_nop
+// gives the two wait states a VALU write needs before a permlane reads it (the compiler
+// cannot see into the asm to insert them).
+__device__ __forceinline__ float max_over_key_groups(float v) {
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  v = fmaxf(a, b);
+  a = v;
+  b = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Buffer-resource dword 3 for raw (untyped) dword loads on gfx9-family parts.
+constexpr int kRsrcWord3 = 0x00020000;
+// Cache policy of the K loads: non-temporal (each byte is read once per head block).
+constexpr int kLoadNT = 2;
+// Fixed reference max: the exponentials are taken relative to the first tile's max
+// m_ref and the 128 accumulator registers are never rescaled inside the key loop. That
+// holds while every score stays within kHeadroomLog2 powers of two of m_ref (p <= 2^64,
+// far from fp32 overflow, and keys far below the max underflow harmlessly). A score
+// beyond that (rare; adversarial or huge logits) makes the workgroup run the partition
+// once more with m_ref = the partition's exact max. The exact max is tracked on the side.
+constexpr float kHeadroomLog2 = 64.f;
 
 template <int PM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
@@ -65,11 +92,20 @@ void partition_latent_kernel(PartArgs a) {
   const bool wave_active = head0 < g;
   const float c = a.c;
 
-  extern __shared__ __attribute__((aligned(16))) char smem[];   // 2 K tiles + q block
-  auto ktile = [&](int i) -> char* { return smem + (i & 1) * kTileBytes; };
-  char* qs = smem + 2 * kTileBytes;
+  // Two K tiles as two distinct LDS arrays: the compiler then sees that reads of one tile
+  // do not depend on the direct-to-LDS loads still filling the other, and waits for
+  // those loads only where a tile is consumed.
+  __shared__ __attribute__((aligned(16))) char kt0[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char kt1[kTileBytes];
+  extern __shared__ __attribute__((aligned(16))) char qs[];   // q block, kQBytes
   __shared__ int pages_s[kMaxLdsPages];
 
+  // Rows that a ragged tile does not load keep what the buffer held: zero both tiles
+  // once so that such rows are finite (their scores are masked, their V meets p = 0).
+  for (int i = tid; i < kTileBytes / 16; i += kThreads) {
+    *(u32x4*)(kt0 + i * 16) = u32x4{0u, 0u, 0u, 0u};
+    *(u32x4*)(kt1 + i * 16) = u32x4{0u, 0u, 0u, 0u};
+  }
   // q block -> LDS (rows beyond the group are zero)
   {
     const uint16_t* qb = (const uint16_t*)a.q + ((int64_t)b * a.Hq + (int64_t)hb * kHeadsPerWG) * kDqk;
@@ -80,7 +116,6 @@ void partition_latent_kernel(PartArgs a) {
       *(u32x4*)(qs + swz(h, ch)) = v;
     }
   }
-
   // page indices of the partition (one segment: chunks of at most (kMaxLdsPages-1)*page keys)
   int first_page = 0;
   if constexpr (PM != kContiguous) {
@@ -94,140 +129,169 @@ void partition_latent_kernel(PartArgs a) {
   }
   __syncthreads();
 
-  auto key_row = [&](int t) -> int64_t {   // cache row of key t (t < end)
-    if constexpr (PM == kContiguous) {
-      return (int64_t)b * a.kv_capacity + t;
+  // The K tile of keys t0 .. t0+31 lands in LDS by direct-to-LDS 16-byte loads: wave w
+  // fills the 1 KB blocks w, w+4, ..., so lane l of block j writes tile byte j*1024 + 16l,
+  // i.e. row r and chunk slot s of the swizzled layout, and loads the cache chunk
+  // s ^ (r & 7) of row r there (the XOR swizzle is its own inverse).
+  const char* kc = (const char*)a.k;
+  auto lane_chunk = [&](int i, int& r, int& gchunk) {
+    const int pos = (w + kWaves * i) * 1024 + lane * 16;
+    r = pos / kRowBytes;
+    const int slot = (pos - r * kRowBytes) >> 4;
+    gchunk = slot ^ (r & 7);
+  };
+  auto issue = [&](char* dst, int t0) {
+    const int last = min(kTile - 1, end - 1 - t0);   // rows 0..last hold keys
+    if constexpr (PM != kPagedGeneral) {
+      // 32 consecutive cache rows: one scalar base; the buffer range ends at the last
+      // valid row, so a ragged tile's missing rows are not read
+      int64_t row0;
+      if constexpr (PM == kContiguous) {
+        row0 = (int64_t)b * a.kv_capacity + t0;
+      } else {
+        const int slot = min(max((t0 >> a.page_shift) - first_page, 0), kMaxLdsPages - 1);
+        // (clamped before readfirstlane: a clamp after it may be done in vector registers,
+        // which makes the descriptor divergent and every load a waterfall loop)
+        const int page = __builtin_amdgcn_readfirstlane(min(max(pages_s[slot], 0), a.num_pages - 1));
+        row0 = ((int64_t)page << a.page_shift) + (t0 & (a.page_size - 1));
+      }
+      const int rows = __builtin_amdgcn_readfirstlane(last + 1);
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(kc + row0 * kRowBytes), 0, rows * kRowBytes, kRsrcWord3);
+#pragma unroll
+      for (int i = 0; i < kStage; ++i) {
+        int r, gc;
+        lane_chunk(i, r, gc);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (DA_LDS void*)(dst + (w + kWaves * i) * 1024), 16,
+                                                 (uint32_t)(r * kRowBytes + gc * 16), 0, 0, kLoadNT);
+      }
     } else {
-      const int pi = t / a.page_size;
-      const int slot = min(max(pi - first_page, 0), kMaxLdsPages - 1);
-      const int page = min(max(pages_s[slot], 0), a.num_pages - 1);
-      return (int64_t)page * a.page_size + (t - pi * a.page_size);
+      // any page size: every lane looks up its own row (rows past the end repeat the
+      // last key; their scores are masked)
+#pragma unroll
+      for (int i = 0; i < kStage; ++i) {
+        int r, gc;
+        lane_chunk(i, r, gc);
+        const int t = t0 + min(r, last);
+        const int pi = t / a.page_size;
+        const int slot = min(max(pi - first_page, 0), kMaxLdsPages - 1);
+        const int page = min(max(pages_s[slot], 0), a.num_pages - 1);
+        const int64_t row = (int64_t)page * a.page_size + (t - pi * a.page_size);
+        __builtin_amdgcn_global_load_lds((const void*)(kc + row * kRowBytes + gc * 16),
+                                         (DA_LDS void*)(dst + (w + kWaves * i) * 1024), 16, 0, 0);
+      }
     }
   };
 
-  // global -> registers for the tile at t0 (thread covers chunks tid + i*256; rows past
-  // the end reuse the last valid key, their scores are masked)
-  const uint16_t* kc = (const uint16_t*)a.k;
-  const int64_t krow = (int64_t)a.Hkv * kDqk;   // elements between cache rows (Hkv == 1)
-  auto fetch = [&](u32x4* st, int t0) {
-#pragma unroll
-    for (int i = 0; i < kStage; ++i) {
-      const int cid = tid + i * kThreads;
-      const int r = cid / kChunks, ch = cid % kChunks;
-      const int t = min(t0 + r, end - 1);
-      st[i] = __builtin_nontemporal_load((const u32x4*)(kc + key_row(t) * krow + ch * 8));
-    }
-  };
-  auto stage = [&](const u32x4* st, char* dst) {
-#pragma unroll
-    for (int i = 0; i < kStage; ++i) {
-      const int cid = tid + i * kThreads;
-      const int r = cid / kChunks, ch = cid % kChunks;
-      *(u32x4*)(dst + swz(r, ch)) = st[i];
-    }
-  };
-
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY;   // reference max of the exponentials (raw units)
+  float m_true = -INFINITY;  // exact running max
+  float l_run = 0.f;
+  bool beyond = false;       // a score exceeded m_ref by more than the headroom
   f32x4 o[kDv / 16];
+
+  auto compute = [&](const char* K, int t0) {
+    if (!wave_active) return;
+    // S^T = K q^T: keys 16*blk + (4qd..+3) of column (head) n
+    f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-  for (int db = 0; db < kDv / 16; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int n_tiles = (end - start + kTile - 1) / kTile;
-  u32x4 st[kStage];
-  fetch(st, start);
-  stage(st, ktile(0));
-  __syncthreads();
-
-  for (int it = 0; it < n_tiles; ++it) {
-    const int t0 = start + it * kTile;
-    const bool has_next = it + 1 < n_tiles;
-    if (has_next) fetch(st, t0 + kTile);
-    const char* K = ktile(it);
-
-    if (wave_active) {
-      // S^T = K q^T: keys 16*blk + (4qd..+3) of column (head) n
-      f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll 6
-      for (int j = 0; j < kChunks / 4; ++j) {
-        const bf16x8 qf = as_bf16x8(*(const u32x4*)(qs + swz(w * kHeadsPerWave + n, 4 * j + qd)));
+    for (int j = 0; j < kChunks / 4; ++j) {
+      const bf16x8 qf = as_bf16x8(*(const u32x4*)(qs + swz(w * kHeadsPerWave + n, 4 * j + qd)));
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-          const bf16x8 kf = as_bf16x8(*(const u32x4*)(K + swz(n + 16 * blk, 4 * j + qd)));
-          s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf, s[blk], 0, 0, 0);
-        }
+      for (int blk = 0; blk < 2; ++blk) {
+        const bf16x8 kf = as_bf16x8(*(const u32x4*)(K + swz(n + 16 * blk, 4 * j + qd)));
+        s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf, s[blk], 0, 0, 0);
       }
-      // online softmax (missing keys of a ragged tile get -inf, i.e. p = 0)
-      const int nvalid = end - t0;
-      if (nvalid < kTile) {
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (16 * blk + 4 * qd + i >= nvalid) s[blk][i] = -INFINITY;
-      }
-      float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                       fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mn = fmaxf(m_run, mx);
-      const float alpha = exp2_fast((m_run - mn) * c);
-      const float mc = mn * c;
-      float pr[2][4];
-      float psum = 0.f;
+    }
+    // online softmax (missing keys of a ragged tile get -inf, i.e. p = 0)
+    const int nvalid = end - t0;
+    if (nvalid < kTile) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pr[blk][i] = exp2_fast(fmaf(s[blk][i], c, -mc));
-          psum += pr[blk][i];
-        }
-      l_run = fmaf(l_run, alpha, psum);
-      m_run = mn;
-      if (__ballot(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < kDv / 16; ++db) o[db] *= alpha;
-      }
-      // P^T (B operand), hi and lo parts
-      uint32_t hw[4], lw[4];
-#pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {
-        const int blk = s2 >> 1, i0 = (s2 & 1) * 2;
-        const float p0 = pr[blk][i0], p1 = pr[blk][i0 + 1];
-        const uint32_t h = pack_bf16x2(p0, p1);
-        hw[s2] = h;
-        lw[s2] = pack_bf16x2(p0 - bf16lo(h), p1 - bf16hi(h));
-      }
-      const bf16x8 pb_hi = as_bf16x8(u32x4{hw[0], hw[1], hw[2], hw[3]});
-      const bf16x8 pb_lo = as_bf16x8(u32x4{lw[0], lw[1], lw[2], lw[3]});
-      // O^T += V^T P^T; V^T A operand: depth 16db + n of keys 4qd..+3 and 16+4qd..+3
-      const int ra = 4 * qd + (n >> 2), rb = ra + 16;
-      const int sub = (n & 1) * 8;
-#pragma unroll
-      for (int db = 0; db < kDv / 16; ++db) {
-        const int ch = 2 * db + ((n & 3) >> 1);
-        const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 DA_LDS*)(K + swz(ra, ch) + sub));
-        const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 DA_LDS*)(K + swz(rb, ch) + sub));
-        s16x8 v8;
-        v8[0] = va[0]; v8[1] = va[1]; v8[2] = va[2]; v8[3] = va[3];
-        v8[4] = vb[0]; v8[5] = vb[1]; v8[6] = vb[2]; v8[7] = vb[3];
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, v8);
-        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb_hi, o[db], 0, 0, 0);
-        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb_lo, o[db], 0, 0, 0);
-      }
+        for (int i = 0; i < 4; ++i)
+          if (16 * blk + 4 * qd + i >= nvalid) s[blk][i] = -INFINITY;
     }
-    if (has_next) stage(st, ktile(it + 1));
-    __syncthreads();
+    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    mx = max_over_key_groups(mx);
+    m_true = fmaxf(m_true, mx);
+    m_ref = m_ref == -INFINITY ? mx : m_ref;   // first tile of the pass: O and l are still 0
+    beyond = beyond || (mx - m_ref) * c > kHeadroomLog2;
+    const float mc = m_ref * c;
+    float pr[2][4];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pr[blk][i] = exp2_fast(fmaf(s[blk][i], c, -mc));
+        l_run += pr[blk][i];
+      }
+    // P^T (B operand), hi and lo parts
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      const int blk = s2 >> 1, i0 = (s2 & 1) * 2;
+      const float p0 = pr[blk][i0], p1 = pr[blk][i0 + 1];
+      const uint32_t h = pack_bf16x2(p0, p1);
+      hw[s2] = h;
+      lw[s2] = pack_bf16x2(p0 - bf16lo(h), p1 - bf16hi(h));
+    }
+    const bf16x8 pb_hi = as_bf16x8(u32x4{hw[0], hw[1], hw[2], hw[3]});
+    const bf16x8 pb_lo = as_bf16x8(u32x4{lw[0], lw[1], lw[2], lw[3]});
+    // O^T += V^T P^T; V^T A operand: depth 16db + n of keys 4qd..+3 and 16+4qd..+3
+    const int ra = 4 * qd + (n >> 2), rb = ra + 16;
+    const int sub = (n & 1) * 8;
+#pragma unroll
+    for (int db = 0; db < kDv / 16; ++db) {
+      const int ch = 2 * db + ((n & 3) >> 1);
+      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 DA_LDS*)(K + swz(ra, ch) + sub));
+      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 DA_LDS*)(K + swz(rb, ch) + sub));
+      s16x8 v8;
+      v8[0] = va[0]; v8[1] = va[1]; v8[2] = va[2]; v8[3] = va[3];
+      v8[4] = vb[0]; v8[5] = vb[1]; v8[6] = vb[2]; v8[7] = vb[3];
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, v8);
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb_hi, o[db], 0, 0, 0);
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb_lo, o[db], 0, 0, 0);
+    }
+  };
+
+  // Double buffer: tile it+1 is requested right after the barrier that retires tile it-1
+  // from the other buffer, and lands while tile it is computed. A second pass runs only
+  // if some score left the headroom of m_ref (then m_ref = the exact max: no second miss).
+  const int n_tiles = (end - start + kTile - 1) / kTile;
+  for (int pass = 0; pass < 2; ++pass) {
+    l_run = 0.f;
+#pragma unroll
+    for (int db = 0; db < kDv / 16; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    issue(kt0, start);
+    for (int it = 0; it < n_tiles; it += 2) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's part of tile it is in LDS
+      __syncthreads();                      // ... and every wave's; tile it-1 is retired
+      if (it + 1 < n_tiles) issue(kt1, start + (it + 1) * kTile);
+      compute(kt0, start + it * kTile);
+      if (it + 1 >= n_tiles) break;
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      if (it + 2 < n_tiles) issue(kt0, start + (it + 2) * kTile);
+      compute(kt1, start + (it + 1) * kTile);
+    }
+    // every wave is past its last LDS read before a second pass refills the tiles
+    if (!__syncthreads_or(beyond)) break;
+    m_ref = m_true;
+    beyond = false;
   }
 
-  // totals over the four key groups of each column, then store
+  // O and l are relative to m_ref; the partial reports the exact max, so its sum is
+  // rescaled once (the normalised O does not change).
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
   const int hq = head0 + n;   // q head of this lane's column (within the kv head's group)
   if (wave_active && hq < g) {
     const float inv = 1.f / l_run;
+    const float l_true = l_run * exp2_fast((m_ref - m_true) * c);
 #pragma unroll
     for (int db = 0; db < kDv / 16; ++db)
-      store_unit(a, b, hq, p, direct, 16 * db + 4 * qd, o[db] * inv, m_run, l_run, db == 0 && qd == 0);
+      store_unit(a, b, hq, p, direct, 16 * db + 4 * qd, o[db] * inv, m_true, l_true, db == 0 && qd == 0);
   }
 }
 
@@ -238,11 +302,17 @@ hipError_t launch_partition_latent(const PartArgs& a, int page_mode, hipStream_t
   // x = partition, y = 64-head block, z = sequence: with 8 partitions the two head blocks
   // of a (sequence, partition) are 8 workgroup ids apart (same XCD under round-robin dispatch)
   dim3 grid(a.max_splits, (a.g + kHeadsPerWG - 1) / kHeadsPerWG, a.B), block(kThreads);
-  const size_t lds = 2 * kTileBytes + kQBytes;
-  if (page_mode == kContiguous) {
-    hipLaunchKernelGGL(partition_latent_kernel<kContiguous>, grid, block, lds, s, a);
-  } else {
-    hipLaunchKernelGGL(partition_latent_kernel<kPagedGeneral>, grid, block, lds, s, a);
+  const size_t lds = kQBytes;   // (the two K tiles are static)
+  switch (page_mode) {
+    case kContiguous:
+      hipLaunchKernelGGL(partition_latent_kernel<kContiguous>, grid, block, lds, s, a);
+      break;
+    case kPagedAligned:
+      hipLaunchKernelGGL(partition_latent_kernel<kPagedAligned>, grid, block, lds, s, a);
+      break;
+    default:
+      hipLaunchKernelGGL(partition_latent_kernel<kPagedGeneral>, grid, block, lds, s, a);
+      break;
   }
   return hipGetLastError();
 }

@@ -153,8 +153,9 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
       // an LDS value read at a uniform address: tell the compiler it is uniform; index and
       // value are clamped so that no cache address can leave the page pool
       const int slot = min(max(pi - first_page, 0), kMaxLdsPages - 1);
-      int page = __builtin_amdgcn_readfirstlane(pages_s[slot]);
-      page = min(max(page, 0), a.num_pages - 1);
+      // (clamped before readfirstlane: a clamp after it may be done in vector registers,
+      // which makes the descriptor divergent and every load a waterfall loop)
+      const int page = __builtin_amdgcn_readfirstlane(min(max(pages_s[slot], 0), a.num_pages - 1));
       return ((int64_t)page << a.page_shift) + (t0 & (a.page_size - 1));
     }
   };

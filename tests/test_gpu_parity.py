@@ -133,6 +133,18 @@ def test_large_logits_overflow_safety():
     assert_parity(out, lse, o32, O, LSE, o32_row_rtol=1e-4, what="large logits")
 
 
+def test_latent_large_logits_take_the_second_pass():
+    # raw scores of several thousand: later tiles exceed the first tile's max by more than
+    # the kernel's fixed-reference headroom, so the partition is run again with its exact max
+    case = make_case("big_latent", batch=2, num_q_heads=64, num_kv_heads=1, qk_depth=576, ov_depth=512,
+                     page_size=64, seq_lens=[1300, 700], num_splits=2, seed=48, q_scale=64.0,
+                     v_is_k_prefix=True)
+    out, lse, o32 = run(case)
+    O, LSE = oracle_for(case)
+    assert torch.isfinite(o32).all()
+    assert_parity(out, lse, o32, O, LSE, o32_row_rtol=1e-4, what="latent large logits")
+
+
 def test_determinism_bitwise():
     case = make_case("det", batch=4, num_q_heads=32, num_kv_heads=4, qk_depth=128, page_size=64,
                      len_range=(500, 6000), num_splits=0, seed=43)
