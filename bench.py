@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--workload", default="paged_gqa")
     ap.add_argument("--num-splits", type=int, default=None, help="override the workload's split count")
     ap.add_argument("--kernel", default="auto", choices=["auto", "fma", "mfma"])
+    ap.add_argument("--combine", default="separate", choices=["separate", "fused"],
+                    help="LSE combine as its own launch, or by each group's last-arriving workgroup")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=30.0)
     ap.add_argument("--probe-gib", type=float, default=2.0, help="streaming-read probe size")
@@ -94,7 +96,7 @@ def main():
 
     plan = api.DecodePlan(dc.q, dc.k_cache, dc.v_cache, dc.page_table, dc.seq_lens, case.scale, case.num_splits,
                           page_size=case.page_size, v_is_k_prefix=case.v_is_k_prefix, ov_depth=case.ov_depth,
-                          kernel=args.kernel, out=out)
+                          kernel=args.kernel, out=out, fused=args.combine == "fused")
     step = plan.run
 
     # --- streaming-read probe and a copy of known size (counter calibration) ---
@@ -189,7 +191,7 @@ def main():
             "batch": B, "q_heads": Hq, "kv_heads": prob.num_kv_heads,
             "qk_depth": prob.qk_depth, "ov_depth": Dv, "page_size": case.page_size,
             "keys": tokens, "max_seq_len": int(case.seq_lens.max()),
-            "chunk_tokens": chunk, "max_splits": max_splits, "kernel": args.kernel,
+            "chunk_tokens": chunk, "max_splits": max_splits, "kernel": args.kernel, "combine": args.combine,
             "kv_bytes": kv_bytes,
         },
         "roofline": {

@@ -86,10 +86,21 @@ typedef struct da_problem {
  *   out        bf16 [B][Hq][Dv]
  *   lse_out    fp32 [B][Hq] natural-log LSE (optional); -inf for L_b == 0
  *   o_f32_out  fp32 [B][Hq][Dv] O before the bf16 cast (optional); 0 for L_b == 0
- *   part_ml    fp32 [B][Hq][max_splits][2] partition (m_p, l_p); m_p in raw q.k units
- *   part_o     fp32 [B][Hq][max_splits][Dv] normalised partition output O_p
- * Partition p of sequence b covers keys [p*chunk_tokens, min((p+1)*chunk_tokens, L_b));
- * sequence b has P_b = ceil(L_b / chunk_tokens) partitions (at most max_splits).
+ * Two split schedules name where partitions lie and where their partials go:
+ *  - fixed chunks (chunk_tokens > 0): partition p of sequence b covers keys
+ *    [p*chunk_tokens, min((p+1)*chunk_tokens, L_b)); sequence b has
+ *    P_b = ceil(L_b / chunk_tokens) partitions (at most max_splits);
+ *      part_ml  fp32 [B][Hq][max_splits][2] partition (m_p, l_p); m_p in raw q.k units
+ *      part_o   fp32 [B][Hq][max_splits][Dv] normalised partition output O_p
+ *  - equal shares (chunk_tokens == 0, max_splits = W workers; bf16 depth-128 matrix-core
+ *    kernel only): the 32-key tiles of all sequences, laid end to end in batch order and
+ *    numbered 0..U-1, are cut into W' = min(W, max(1, floor(U / 8))) shares, share w
+ *    holding tiles floor(w U / W') .. floor((w+1) U / W') - 1; every overlap of a share
+ *    with a sequence is one partition, and partitions are numbered ("slots") sequence
+ *    by sequence, then share by share. With S = W + B slots:
+ *      part_ml  fp32 [S][Hq][2] (m, l) followed by int32 [B][2] (first slot, count) per
+ *               sequence (written by pass 1, read by pass 2)
+ *      part_o   fp32 [S][Hq][Dv]
  * A page_table entry outside [0, num_pages) is clamped into range (no fault; the
  * output of that sequence is then unspecified).
  */
@@ -101,11 +112,13 @@ typedef struct da_problem {
 int da_supported(const da_problem* p);
 
 /* Split selection (FA4Config, with_splitk: partitions of the K/V sequence).
- * num_splits > 0: chunk_tokens = ceil(max_seq_len / num_splits) rounded up to a multiple
- * of the key tile (32) and of page_size when that is a multiple of 32.
- * num_splits == 0: automatic choice for the device's num_cus compute units
- * (num_cus <= 0: query the current device). Writes chunk_tokens and
- * max_splits = ceil(max_seq_len / chunk_tokens) (>= 1). */
+ * num_splits > 0: fixed chunks, chunk_tokens = ceil(max_seq_len / num_splits) rounded up
+ * to a multiple of the key tile (32) and of page_size when that is a multiple of 32;
+ * max_splits = ceil(max_seq_len / chunk_tokens) (>= 1).
+ * num_splits == 0: automatic choice for the device's num_cus compute units (num_cus <= 0:
+ * query the current device): on the bf16 depth-128 matrix-core kernel the equal-share
+ * schedule (chunk_tokens = 0, max_splits = workers, about one workgroup per CU), on the
+ * other kernels fixed chunks sized for a few waves of workgroups. */
 int da_choose_splits(const da_problem* p, int32_t num_splits, int32_t num_cus,
                      int32_t* chunk_tokens, int32_t* max_splits);
 
@@ -125,10 +138,28 @@ int decode_attn_splitk(const da_problem* p, const void* q, const void* k_cache,
                        float scale, int32_t num_splits, void* out, float* lse_out,
                        float* o_f32_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The whole decode step with the combine fused into pass 1 (fa4_splitk_combine_write,
+ * fourth paragraph: the writer that completes the set combines all). Every workgroup of
+ * a (sequence, kv-head group) stores its partial, publishes it device-wide and counts
+ * itself in on an arrival counter; the last one merges all partials of its heads and
+ * writes out / lse_out / o_f32_out, then resets the counter. This saves the second
+ * launch. Applied by the bf16 matrix-core depth-128 kernel when sequences have at most
+ * 16 partitions (other problems run the two launches of decode_attn_splitk; the outputs
+ * are the same either way). Same arguments and workspace size as decode_attn_splitk,
+ * with one more rule: the workspace must be zero-filled before its first use with this
+ * function (the counters live in it and every call leaves them at zero), and calls that
+ * share a workspace must not overlap. */
+int decode_attn_splitk_fused(const da_problem* p, const void* q, const void* k_cache,
+                             const void* v_cache, const int32_t* page_table,
+                             const int32_t* seq_lens, float scale, int32_t num_splits, void* out,
+                             float* lse_out, float* o_f32_out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /* Pass 1 only (fa4_splitk_combine_write, second paragraph: each partition stages its
  * normalised O and its (max, sum)). Writes part_ml / part_o (device, layouts above) for
  * p < P_b; entries for p >= P_b are not written. chunk_tokens must be a positive multiple
- * of 32 and max_splits >= ceil(max_seq_len / chunk_tokens). */
+ * of 32 with max_splits >= ceil(max_seq_len / chunk_tokens), or 0 (equal shares, 1 <=
+ * max_splits <= 65535; DA_EUNSUPPORTED unless the matrix-core depth-128 kernel runs). */
 int decode_attn_partition(const da_problem* p, const void* q, const void* k_cache,
                           const void* v_cache, const int32_t* page_table,
                           const int32_t* seq_lens, float scale, int32_t chunk_tokens,

@@ -89,8 +89,12 @@ def workspace_bytes(problem: DaProblem, num_splits=0):
 
 def decode_attn(q, k_cache, v_cache, page_table, seq_lens, scale, num_splits=0, *, page_size=0,
                 max_seq_len=None, v_is_k_prefix=False, ov_depth=None, out=None, lse=None, o32=None,
-                return_lse=False, return_o32=False, workspace=None, kernel="auto"):
-    """The whole split-K decode step. Returns out (bf16 [B, Hq, Dv]) or (out, lse, o32)."""
+                return_lse=False, return_o32=False, workspace=None, kernel="auto", fused=False):
+    """The whole split-K decode step. Returns out (bf16 [B, Hq, Dv]) or (out, lse, o32).
+
+    fused=True runs decode_attn_splitk_fused (the combine done by each group's last
+    workgroup); a workspace passed in must then have been zero-filled before its first use.
+    """
     lib = _lib.load()
     prob = make_problem(q, k_cache, v_cache, page_table, page_size=page_size, max_seq_len=max_seq_len,
                         v_is_k_prefix=v_is_k_prefix, ov_depth=ov_depth, kernel=kernel)
@@ -104,8 +108,9 @@ def decode_attn(q, k_cache, v_cache, page_table, seq_lens, scale, num_splits=0, 
         o32 = torch.empty((B, Hq, Dv), dtype=torch.float32, device=q.device)
     need = workspace_bytes(prob, num_splits)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    check(lib.decode_attn_splitk(ctypes.byref(prob), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
+    fn = lib.decode_attn_splitk_fused if fused else lib.decode_attn_splitk
+    check(fn(ctypes.byref(prob), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
                                  _ptr(seq_lens), float(scale), int(num_splits), _ptr(out), _ptr(lse), _ptr(o32),
                                  _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
     if return_lse or return_o32:
@@ -189,7 +194,7 @@ class DecodePlan:
 
     def __init__(self, q, k_cache, v_cache, page_table, seq_lens, scale, num_splits=0, *, page_size=0,
                  max_seq_len=None, v_is_k_prefix=False, ov_depth=None, kernel="auto", out=None, lse=None,
-                 o32=None):
+                 o32=None, fused=False):
         self.lib = _lib.load()
         self.prob = make_problem(q, k_cache, v_cache, page_table, page_size=page_size, max_seq_len=max_seq_len,
                                  v_is_k_prefix=v_is_k_prefix, ov_depth=ov_depth, kernel=kernel)
@@ -198,7 +203,9 @@ class DecodePlan:
         self.out = torch.empty((B, Hq, Dv), dtype=torch.bfloat16, device=q.device) if out is None else out
         self.lse, self.o32 = lse, o32
         need = workspace_bytes(self.prob, num_splits)
-        self.workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        # zero-filled once: the fused step keeps its arrival counters here
+        self.workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
+        self.fn = self.lib.decode_attn_splitk_fused if fused else self.lib.decode_attn_splitk
         self.chunk, self.max_splits = choose_splits(self.prob, num_splits)
         self._keep = (q, k_cache, v_cache, page_table, seq_lens)
         self._args = (ctypes.byref(self.prob), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
@@ -207,5 +214,5 @@ class DecodePlan:
 
     def run(self, stream=None):
         s = _stream() if stream is None else ctypes.c_void_p(stream)
-        check(self.lib.decode_attn_splitk(*self._args, s))
+        check(self.fn(*self._args, s))
         return self.out

@@ -192,16 +192,19 @@ size_t partial_rows(const da_problem* p, int32_t chunk, int32_t max_splits) {
 }
 
 // Workspace: part_ml (fp32 pairs; with equal shares followed by the int32 (first slot,
-// count) table of the B sequences), then part_o, each padded to 256 bytes.
+// count) table of the B sequences), then part_o, then the int32 arrival counters of the
+// fused combine ([B][Hkv]), each padded to 256 bytes.
 void ws_layout(const da_problem* p, int32_t chunk, int32_t max_splits, size_t* ml_off, size_t* o_off,
-               size_t* total) {
+               size_t* cnt_off, size_t* total) {
   const size_t rows = partial_rows(p, chunk, max_splits);
   const size_t meta = chunk == 0 ? (size_t)p->batch * 2 * sizeof(int32_t) : 0;
   const size_t ml = (rows * 2 * sizeof(float) + meta + 255) & ~(size_t)255;
   const size_t o = (rows * (size_t)p->ov_depth * sizeof(float) + 255) & ~(size_t)255;
+  const size_t cnt = ((size_t)p->batch * p->num_kv_heads * sizeof(int32_t) + 255) & ~(size_t)255;
   *ml_off = 0;
   *o_off = ml;
-  *total = ml + o;
+  *cnt_off = ml + o;
+  *total = ml + o + cnt;
 }
 
 // The (first slot, count) table that follows the (m, l) pairs in part_ml (equal shares).
@@ -298,6 +301,47 @@ int check_scale(float scale) {
   return DA_OK;
 }
 
+// The whole step. With `fused`, the matrix-core kernel combines in its last-arriving
+// workgroups (no second launch) wherever sequences have few partitions (up to 16, where
+// one workgroup's combine is short); elsewhere, and for the other kernels, the combine
+// is a launch of its own. The results are the same either way.
+int run_splitk(const da_problem* p, const void* q, const void* k_cache, const void* v_cache, const int32_t* page_table,
+               const int32_t* seq_lens, float scale, int32_t num_splits, void* out, float* lse_out, float* o_f32_out,
+               void* workspace, size_t workspace_bytes, void* stream, bool fused) {
+  Variant var;
+  int r = check_problem(p, &var);
+  if (r) return r;
+  if ((r = check_inputs(p, q, k_cache, v_cache, page_table, seq_lens))) return r;
+  if ((r = check_scale(scale))) return r;
+  if (!out) return fail(DA_EINVAL, "out must be non-NULL");
+  const int cus = device_num_cus();
+  int32_t C, P;
+  if ((r = choose(p, var, num_splits, cus, &C, &P))) return r;
+  size_t ml_off, o_off, cnt_off, need;
+  ws_layout(p, C, P, &ml_off, &o_off, &cnt_off, &need);
+  if (!workspace || ((uintptr_t)workspace & 255))
+    return fail(DA_EWORKSPACE, "workspace must be non-NULL and 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(DA_EWORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  float* pml = (float*)((char*)workspace + ml_off);
+  float* po = (float*)((char*)workspace + o_off);
+  hipStream_t s = (hipStream_t)stream;
+  da::PartArgs a = da::build_part_args(p, q, k_cache, v_cache, page_table, seq_lens, scale, C, P);
+  a.part_o = po;
+  a.part_ml = pml;
+  if (C == 0) a.meta = meta_of(p, P, pml);
+  a.out = (uint16_t*)out;
+  a.lse = lse_out;
+  a.o32 = o_f32_out;
+  a.direct_single = 1;
+  const int64_t per_seq = C == 0 ? (int64_t)P / p->batch + 1 : P;
+  const bool fuse = fused && var == kVarMfma128 && per_seq <= 16;
+  if (fuse) a.counters = (int32_t*)((char*)workspace + cnt_off);
+  if ((r = launch_partition(p, var, a, s, cus))) return r;
+  if (!fuse && (r = launch_combine(p, seq_lens, scale, C, P, po, pml, out, lse_out, o_f32_out, 1, s))) return r;
+  return ok();
+}
+
 }  // namespace
 
 namespace da {
@@ -363,8 +407,8 @@ int da_workspace_bytes(const da_problem* p, int32_t num_splits, size_t* bytes) {
   int32_t C, P;
   r = choose(p, v, num_splits, device_num_cus(), &C, &P);
   if (r) return r;
-  size_t a, b;
-  ws_layout(p, C, P, &a, &b, bytes);
+  size_t a, b, c;
+  ws_layout(p, C, P, &a, &b, &c, bytes);
   return ok();
 }
 
@@ -372,35 +416,16 @@ int decode_attn_splitk(const da_problem* p, const void* q, const void* k_cache, 
                        const int32_t* page_table, const int32_t* seq_lens, float scale, int32_t num_splits,
                        void* out, float* lse_out, float* o_f32_out, void* workspace, size_t workspace_bytes,
                        void* stream) {
-  Variant var;
-  int r = check_problem(p, &var);
-  if (r) return r;
-  if ((r = check_inputs(p, q, k_cache, v_cache, page_table, seq_lens))) return r;
-  if ((r = check_scale(scale))) return r;
-  if (!out) return fail(DA_EINVAL, "out must be non-NULL");
-  const int cus = device_num_cus();
-  int32_t C, P;
-  if ((r = choose(p, var, num_splits, cus, &C, &P))) return r;
-  size_t ml_off, o_off, need;
-  ws_layout(p, C, P, &ml_off, &o_off, &need);
-  if (!workspace || ((uintptr_t)workspace & 255))
-    return fail(DA_EWORKSPACE, "workspace must be non-NULL and 256-byte aligned");
-  if (workspace_bytes < need)
-    return fail(DA_EWORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
-  float* pml = (float*)((char*)workspace + ml_off);
-  float* po = (float*)((char*)workspace + o_off);
-  hipStream_t s = (hipStream_t)stream;
-  da::PartArgs a = da::build_part_args(p, q, k_cache, v_cache, page_table, seq_lens, scale, C, P);
-  a.part_o = po;
-  a.part_ml = pml;
-  if (C == 0) a.meta = meta_of(p, P, pml);
-  a.out = (uint16_t*)out;
-  a.lse = lse_out;
-  a.o32 = o_f32_out;
-  a.direct_single = 1;
-  if ((r = launch_partition(p, var, a, s, cus))) return r;
-  if ((r = launch_combine(p, seq_lens, scale, C, P, po, pml, out, lse_out, o_f32_out, 1, s))) return r;
-  return ok();
+  return run_splitk(p, q, k_cache, v_cache, page_table, seq_lens, scale, num_splits, out, lse_out, o_f32_out,
+                    workspace, workspace_bytes, stream, false);
+}
+
+int decode_attn_splitk_fused(const da_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* page_table, const int32_t* seq_lens, float scale, int32_t num_splits,
+                             void* out, float* lse_out, float* o_f32_out, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return run_splitk(p, q, k_cache, v_cache, page_table, seq_lens, scale, num_splits, out, lse_out, o_f32_out,
+                    workspace, workspace_bytes, stream, true);
 }
 
 int decode_attn_partition(const da_problem* p, const void* q, const void* k_cache, const void* v_cache,

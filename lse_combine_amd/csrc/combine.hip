@@ -20,7 +20,7 @@ namespace da {
 namespace {
 
 constexpr int kCombineThreads = 256;
-constexpr int kBatch = 8;   // partitions whose loads are in flight together, per thread
+constexpr int kBatch = 8;   // partitions whose loads are in flight together, per thread (fold_partials)
 
 // One (row, 4-wide depth slice) unit per thread and S threads per unit: thread subset s
 // takes partitions s, s + S, s + 2S, ... of the row and keeps a running (max, sum, O)
@@ -70,37 +70,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
   const float* po = a.part_o + first * DV + ch * 4;
   float M = -INFINITY, Ls = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (active) {
-    for (int p0 = sub; p0 < P_b; p0 += S * kBatch) {
-      float2 v[kBatch];
-      f32x4 o[kBatch];
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
-        const int p = p0 + i * S;
-        const bool in = p < P_b;
-        v[i] = in ? ml[p * stride] : make_float2(-INFINITY, 0.f);
-        o[i] = in ? *(const f32x4*)(po + p * stride * DV) : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-      float mb = M;
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i)
-        if (v[i].y > 0.f) mb = fmaxf(mb, v[i].x);
-      if (mb > M) {   // the running max grew: rescale what is summed so far
-        const float r = Ls > 0.f ? exp2_fast((M - mb) * a.c) : 0.f;
-        Ls *= r;
-        acc *= r;
-        M = mb;
-      }
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
-        if (v[i].y > 0.f) {
-          const float e = v[i].y * exp2_fast((v[i].x - M) * a.c);
-          Ls += e;
-          acc += e * o[i];
-        }
-      }
-    }
-  }
+  if (active) fold_partials<DV>(ml, po, stride, P_b, sub, S, a.c, M, Ls, acc);
   if constexpr (S > 1) {
     sM[sub][u] = M;
     sL[sub][u] = Ls;
@@ -124,18 +94,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
     M = G;
   }
   if (!active) return;
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  float lse = -INFINITY;
-  if (Ls > 0.f) {
-    o = acc * (1.f / Ls);
-    lse = a.scale * M + logf(Ls);
-  }
-  u32x2 pk;
-  pk[0] = pack_bf16x2(o[0], o[1]);
-  pk[1] = pack_bf16x2(o[2], o[3]);
-  *(u32x2*)(a.out + row * DV + ch * 4) = pk;
-  if (a.o32) *(f32x4*)(a.o32 + row * DV + ch * 4) = o;
-  if (a.lse && ch == 0) a.lse[row] = lse;
+  write_row_unit(a.out, a.o32, a.lse, row, DV, ch * 4, M, Ls, acc, a.scale);
 }
 
 __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* src, size_t n16, float* sink) {

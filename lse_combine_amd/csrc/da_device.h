@@ -96,6 +96,65 @@ __device__ __forceinline__ int64_t share_owner(int64_t t, int64_t U, int64_t W) 
   return ((t + 1) * W + U - 1) / U - 1;
 }
 
+// Folds partials j = j0, j0 + step, ... (< P) of one (row, 4-wide depth slice) unit into a
+// running (M, Ls, acc) with the combine's weights l_j exp2((m_j - M) c); when a batch
+// raises the running max, what was summed so far is rescaled (fa4_splitk_combine_write,
+// first paragraph). ml / po point at partial 0 of the row; partials are `stride` partial
+// rows apart; loads are issued eight at a time. Partials with l_j == 0 weigh nothing.
+template <int DV>
+__device__ __forceinline__ void fold_partials(const float2* ml, const float* po, int64_t stride, int P, int j0,
+                                              int step, float c, float& M, float& Ls, f32x4& acc) {
+  constexpr int kBatch = 8;
+  for (int p0 = j0; p0 < P; p0 += step * kBatch) {
+    float2 v[kBatch];
+    f32x4 o[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int p = p0 + i * step;
+      const bool in = p < P;
+      v[i] = in ? ml[p * stride] : make_float2(-INFINITY, 0.f);
+      o[i] = in ? *(const f32x4*)(po + p * stride * DV) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float mb = M;
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+      if (v[i].y > 0.f) mb = fmaxf(mb, v[i].x);
+    if (mb > M) {
+      const float r = Ls > 0.f ? exp2_fast((M - mb) * c) : 0.f;
+      Ls *= r;
+      acc *= r;
+      M = mb;
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (v[i].y > 0.f) {
+        const float e = v[i].y * exp2_fast((v[i].x - M) * c);
+        Ls += e;
+        acc += e * o[i];
+      }
+    }
+  }
+}
+
+// Final outputs of one (row, 4-wide slice) unit from its merged (M, Ls, acc): O = acc / Ls
+// as bf16 (round to nearest even) and optionally fp32, LSE = scale M + ln Ls (written by
+// the slice at depth 0). A row without keys gets O = 0 and LSE = -inf.
+__device__ __forceinline__ void write_row_unit(uint16_t* out, float* o32, float* lse, int64_t row, int Dv, int d0,
+                                               float M, float Ls, f32x4 acc, float scale) {
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  float l = -INFINITY;
+  if (Ls > 0.f) {
+    o = acc * (1.f / Ls);
+    l = scale * M + logf(Ls);
+  }
+  u32x2 pk;
+  pk[0] = pack_bf16x2(o[0], o[1]);
+  pk[1] = pack_bf16x2(o[2], o[3]);
+  *(u32x2*)(out + row * Dv + d0) = pk;
+  if (o32) *(f32x4*)(o32 + row * Dv + d0) = o;
+  if (lse && d0 == 0) lse[row] = l;
+}
+
 // Store one float4 of a finished (head, depth) unit: either the final outputs of a
 // single-partition row or the normalised partial of partition p.
 __device__ __forceinline__ void store_unit(const PartArgs& a, int b, int hq, int p, bool direct,

@@ -24,6 +24,8 @@ struct PartArgs {
   float* part_o;            // fixed chunks: [B][Hq][max_splits][Dv]; equal shares: [slots][Hq][Dv]
   float* part_ml;           // fixed chunks: [B][Hq][max_splits][2];  equal shares: [slots][Hq][2]
   int32_t* meta;            // equal shares: [B][2] (first slot, partition count) per sequence
+  int32_t* counters;        // fused combine: [B][head groups] arrival counters (zero between
+                            // calls); NULL: the combine is a separate launch
   uint16_t* out;            // bf16 [B][Hq][Dv]; written directly by single-partition rows
   float* lse;               // optional
   float* o32;               // optional

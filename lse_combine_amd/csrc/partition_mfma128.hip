@@ -103,12 +103,99 @@ struct WaveInfo {
   bool wave_active, col_valid, is_lo;
 };
 
+// KS > 1: merge the key splits of each kv head through LDS (each wave reuses its own V
+// region; waves that saw no tile hold m = -inf, l = 0, O = 0 and get weight 0), with the
+// log-sum-exp weights of the two-fragment combine (fa4_lse_combine_write).
+template <bool HL>
+__device__ __forceinline__ void merge_key_splits(const PartArgs& a, const WaveInfo& wv, char* smem, int b, int p,
+                                                 bool direct, const f32x4* o, float m_run, float l_run) {
+  const int tid = threadIdx.x, NW = wv.NW, HG = wv.HG, KS = wv.KS, kg = blockIdx.y;
+  const int hc = wv.hc, qd = wv.qd, g = a.g;
+  const bool col_valid = wv.col_valid, is_lo = wv.is_lo;
+  const float c = a.c;
+  char* vt = smem + wv.w * kWaveBytes;
+  float* mo = (float*)vt;                      // [16][128] O of this wave
+  float* mml = (float*)(vt + kVBytes);         // m[16], l[16]
+  __syncthreads();
+  if (col_valid && !is_lo) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db) *(f32x4*)(mo + hc * kD + 16 * db + 4 * qd) = o[db];
+    if (qd == 0) {
+      mml[hc] = m_run;
+      mml[16 + hc] = l_run;
+    }
+  }
+  __syncthreads();
+  constexpr int kUnits = kD / 4;
+  const int units = HG * g * kUnits;
+  for (int u = tid; u < units; u += NW * 64) {
+    const int mem = u / (g * kUnits);
+    const int h = (u / kUnits) % g, d0 = (u % kUnits) * 4;
+    const int kv2 = kg * HG + mem;
+    if (kv2 >= a.Hkv) continue;
+    float M = -INFINITY;
+    for (int s2 = 0; s2 < KS; ++s2)
+      M = fmaxf(M, ((const float*)(smem + (s2 * HG + mem) * kWaveBytes + kVBytes))[h]);
+    float Ls = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s2 = 0; s2 < KS; ++s2) {
+      const char* reg = smem + (s2 * HG + mem) * kWaveBytes;
+      const float* ml = (const float*)(reg + kVBytes);
+      const float e = exp2_fast((ml[h] - M) * c);
+      Ls = fmaf(ml[16 + h], e, Ls);
+      acc += e * *(const f32x4*)((const float*)reg + h * kD + d0);
+    }
+    store_unit(a, b, kv2 * g + h, p, direct, d0, acc * (1.f / Ls), M, Ls, d0 == 0);
+  }
+  // the merge read other waves' V tiles: the next piece may refill them only after this
+  __syncthreads();
+}
+
+// Last-arriving-workgroup combine (fa4_splitk_combine_write, fourth paragraph: the writer
+// that completes the set combines all). After storing its partial, every workgroup of a
+// (sequence, kv-head group) publishes it device-wide (agent-scope release) and counts
+// itself in; the one that brings the count to the number of partitions acquires the
+// others' partials and writes the final bf16 rows, LSE and fp32 O of the group's heads,
+// then returns the counter to zero for the next call. The counters (one int per
+// (sequence, group)) must be zero before the first call.
+__device__ __forceinline__ void fused_combine(const PartArgs& a, const WaveInfo& wv, int* flag_s, int b, int count,
+                                              int first_slot) {
+  const int tid = threadIdx.x, kg = blockIdx.y, HG = wv.HG, g = a.g;
+  __threadfence();   // release this workgroup's partial
+  __syncthreads();
+  int* cnt = a.counters + (int64_t)b * gridDim.y + kg;
+  if (tid == 0)
+    *flag_s = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == count - 1 ? 1 : 0;
+  __syncthreads();
+  if (!__builtin_amdgcn_readfirstlane(*flag_s)) return;
+  __threadfence();   // acquire the other workgroups' partials
+  const int kv_end = min((kg + 1) * HG, a.Hkv);
+  const int h0 = kg * HG * g, nh = (kv_end - kg * HG) * g;
+  constexpr int kUnits = kD / 4;
+  for (int u = tid; u < nh * kUnits; u += wv.NW * 64) {
+    const int h = h0 + u / kUnits, d0 = (u % kUnits) * 4;
+    const int64_t row = (int64_t)b * a.Hq + h;
+    // partial rows of this head: equal shares [slot][Hq], fixed chunks [B][Hq][max_splits]
+    const int64_t first = first_slot >= 0 ? (int64_t)first_slot * a.Hq + h : row * a.max_splits;
+    const int64_t stride = first_slot >= 0 ? a.Hq : 1;
+    float M = -INFINITY, Ls = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    fold_partials<kD>((const float2*)a.part_ml + first, a.part_o + first * kD + d0, stride, count, 0, 1, a.c, M,
+                      Ls, acc);
+    write_row_unit(a.out, a.o32, a.lse, row, kD, d0, M, Ls, acc, a.scale);
+  }
+  if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // One piece of work: keys [start, end) of sequence b for this workgroup's kv heads.
 // Writes the normalised partial and (m, l) of partition / slot p, or the finished bf16
 // row when `direct` (the sequence has a single partition).
 template <bool HL, int PM>
-__device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv, char* smem, int* pages_s, int b,
-                                          int start, int end, int p, bool direct) {
+__device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv, char* smem, int* pages_s,
+                                          int* flag_s, int b, int start, int end, int p, int count,
+                                          int first_slot) {
+  // (count = partitions of sequence b; first_slot = its first slot under equal shares, or -1)
+  const bool direct = a.direct_single && count == 1;
   const int lane = wv.lane, n = wv.n, qd = wv.qd, hc = wv.hc, kvh = wv.kvh, ks = wv.ks, KS = wv.KS;
   const int g = a.g;
   const bool wave_active = wv.wave_active, col_valid = wv.col_valid, is_lo = wv.is_lo;
@@ -376,51 +463,16 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
         store_unit(a, b, kvh * g + hc, p, direct, 16 * db + 4 * qd, o[db] * inv, m_run, l_run,
                    db == 0 && qd == 0);
     }
-    return;
+  } else {
+    merge_key_splits<HL>(a, wv, smem, b, p, direct, o, m_run, l_run);
   }
-
-  // KS > 1: merge the key splits of each kv head through LDS (each wave reuses its own
-  // V region; waves that saw no tile hold m = -inf, l = 0, O = 0 and get weight 0)
-  float* mo = (float*)vt;                      // [16][128] O of this wave
-  float* mml = (float*)(vt + kVBytes);         // m[16], l[16]
-  __syncthreads();
-  if (col_valid && !is_lo) {
-#pragma unroll
-    for (int db = 0; db < 8; ++db) *(f32x4*)(mo + hc * kD + 16 * db + 4 * qd) = o[db];
-    if (qd == 0) {
-      mml[hc] = m_run;
-      mml[16 + hc] = l_run;
-    }
-  }
-  __syncthreads();
-  constexpr int kUnits = kD / 4;
-  const int units = HG * g * kUnits;
-  for (int u = tid; u < units; u += NW * 64) {
-    const int mem = u / (g * kUnits);
-    const int h = (u / kUnits) % g, d0 = (u % kUnits) * 4;
-    const int kv2 = kg * HG + mem;
-    if (kv2 >= a.Hkv) continue;
-    float M = -INFINITY;
-    for (int s2 = 0; s2 < KS; ++s2)
-      M = fmaxf(M, ((const float*)(smem + (s2 * HG + mem) * kWaveBytes + kVBytes))[h]);
-    float Ls = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s2 = 0; s2 < KS; ++s2) {
-      const char* reg = smem + (s2 * HG + mem) * kWaveBytes;
-      const float* ml = (const float*)(reg + kVBytes);
-      const float e = exp2_fast((ml[h] - M) * c);
-      Ls = fmaf(ml[16 + h], e, Ls);
-      acc += e * *(const f32x4*)((const float*)reg + h * kD + d0);
-    }
-    store_unit(a, b, kv2 * g + h, p, direct, d0, acc * (1.f / Ls), M, Ls, d0 == 0);
-  }
-  // the merge read other waves' V tiles: the next piece may refill them only after this
-  __syncthreads();
+  if (a.counters && !direct) fused_combine(a, wv, flag_s, b, count, first_slot);
 }
 
 // A piece of work as wave 0 of a workgroup publishes it to the other waves.
 struct Piece {
-  int b, start, end, slot_direct;   // slot_direct = slot * 2 + (sequence has one partition)
+  int b, start, end, slot;
+  int first_slot, count;   // the sequence's first slot and number of partitions
 };
 struct PieceTable {
   Piece row[64];      // indexed by lane = sequence within the current chunk of 64
@@ -439,6 +491,7 @@ void partition_gqa_kernel(PartArgs a, int HG, int KS) {
   extern __shared__ __attribute__((aligned(16))) char smem[];   // NW * kWaveBytes (launch size)
   __shared__ int pages_s[kMaxLdsPages];
   __shared__ PieceTable table;
+  __shared__ int fuse_flag;
   WaveInfo wv;
   wv.HG = HG;
   wv.KS = KS;
@@ -494,8 +547,7 @@ void partition_gqa_kernel(PartArgs a, int HG, int KS) {
   }
 
   for (;;) {
-    int b, start, end, p;
-    bool direct;
+    int b, start, end, p, count, first_slot;
     if (a.workers == 0) {
       if (fixed_taken) break;
       fixed_taken = true;
@@ -504,7 +556,8 @@ void partition_gqa_kernel(PartArgs a, int HG, int KS) {
       const int L = __builtin_amdgcn_readfirstlane(attended_len(a, b, PM == kContiguous));
       start = p * a.chunk;
       end = min(start + a.chunk, L);
-      direct = a.direct_single && min((L + a.chunk - 1) / a.chunk, a.max_splits) == 1;
+      count = min((L + a.chunk - 1) / a.chunk, a.max_splits);
+      first_slot = -1;
     } else {
       while (pending == 0) {
         __syncthreads();   // every wave is done with the previous table
@@ -550,7 +603,9 @@ void partition_gqa_kernel(PartArgs a, int HG, int KS) {
               pc.b = bb;
               pc.start = (int)lo * kTile;
               pc.end = min((int)hi * kTile, len);
-              pc.slot_direct = (slot + (int)(wid - first)) * 2 + (count == 1 ? 1 : 0);
+              pc.slot = slot + (int)(wid - first);
+              pc.first_slot = slot;
+              pc.count = count;
               table.row[lane] = pc;
             }
             tile_base += lane_value(incl, 63);
@@ -576,11 +631,11 @@ void partition_gqa_kernel(PartArgs a, int HG, int KS) {
       b = __builtin_amdgcn_readfirstlane(table.row[j].b);
       start = __builtin_amdgcn_readfirstlane(table.row[j].start);
       end = __builtin_amdgcn_readfirstlane(table.row[j].end);
-      const int sd = __builtin_amdgcn_readfirstlane(table.row[j].slot_direct);
-      p = sd >> 1;
-      direct = a.direct_single && (sd & 1);
+      p = __builtin_amdgcn_readfirstlane(table.row[j].slot);
+      first_slot = __builtin_amdgcn_readfirstlane(table.row[j].first_slot);
+      count = __builtin_amdgcn_readfirstlane(table.row[j].count);
     }
-    run_piece<HL, PM>(a, wv, smem, pages_s, b, start, end, p, direct);
+    run_piece<HL, PM>(a, wv, smem, pages_s, &fuse_flag, b, start, end, p, count, first_slot);
   }
 }
 

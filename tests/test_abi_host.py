@@ -29,7 +29,8 @@ def prob(**kw):
 
 def test_exports_every_declared_function(lib):
     names = _lib.header_functions()
-    assert {"decode_attn_splitk", "decode_attn_partition", "decode_attn_combine", "da_supported",
+    assert {"decode_attn_splitk", "decode_attn_splitk_fused", "decode_attn_partition", "decode_attn_combine",
+            "da_supported",
             "da_choose_splits", "da_workspace_bytes", "da_last_error", "da_version",
             "da_read_probe", "da_copy_probe"} <= set(names)
     for n in names:
@@ -131,7 +132,7 @@ def test_equal_share_workspace_and_checks(lib):
     assert C == 0
     align = lambda x: (x + 255) // 256 * 256  # noqa: E731
     rows = (W + 3) * 8
-    assert n.value >= align(rows * 2 * 4 + 3 * 2 * 4) + align(rows * 128 * 4)
+    assert n.value == align(rows * 2 * 4 + 3 * 2 * 4) + align(rows * 128 * 4) + align(3 * 1 * 4)
     f = lib.decode_attn_partition
     # chunk 0 needs the matrix-core kernel and 1 <= workers <= 65535
     fp32 = prob(dtype=0)
@@ -147,7 +148,8 @@ def test_workspace_bytes(lib):
     C, P = splits(lib, p, 4)
     rows = 3 * 8 * P
     align = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    assert n.value == align(rows * 2 * 4) + align(rows * 128 * 4)
+    # (m, l) pairs, partial outputs, and the [B][Hkv] arrival counters of the fused combine
+    assert n.value == align(rows * 2 * 4) + align(rows * 128 * 4) + align(3 * 1 * 4)
 
 
 def call_splitk(lib, p, scale=0.1, ws=FAKE, ws_bytes=1 << 30, q=FAKE, k=FAKE, v=FAKE, pt=FAKE, lens=FAKE, out=FAKE):

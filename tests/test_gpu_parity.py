@@ -191,6 +191,36 @@ def test_partition_partials_match_oracle():
     assert (err / ref).max() <= 1e-5
 
 
+FUSED = [
+    ("paged64_auto", dict(batch=5, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=64,
+                          len_range=(1, 5000), num_splits=0, seed=60)),
+    ("contig_splits8", dict(batch=2, num_q_heads=8, num_kv_heads=2, qk_depth=128, seq_lens=[4096, 1000],
+                            num_splits=8, seed=61)),
+    ("one_kv_head_key_splits", dict(batch=3, num_q_heads=8, num_kv_heads=1, qk_depth=128, page_size=64,
+                                    seq_lens=[3000, 64, 1], num_splits=3, seed=62)),
+    ("g16_two_mfma", dict(batch=2, num_q_heads=32, num_kv_heads=2, qk_depth=128, page_size=32,
+                          seq_lens=[777, 2048], num_splits=3, seed=63)),
+    ("empty_and_single", dict(batch=4, num_q_heads=8, num_kv_heads=1, qk_depth=128, page_size=64,
+                              seq_lens=[0, 1, 2, 6500], num_splits=0, seed=64)),
+]
+
+
+@pytest.mark.parametrize("name,kw", FUSED, ids=[c[0] for c in FUSED])
+def test_fused_combine_matches_oracle_on_repeated_calls(name, kw):
+    # the last-arriving workgroup combines; its counters must return to zero, so three
+    # calls on one workspace all give the oracle's result
+    print(f"[parity] fused {name}", flush=True)
+    case = make_case(name, **kw)
+    dc = to_device(case)
+    prob = api.make_problem(dc.q, dc.k_cache, dc.v_cache, dc.page_table, page_size=case.page_size)
+    ws = torch.zeros(api.workspace_bytes(prob, case.num_splits), dtype=torch.uint8, device="cuda")
+    O, LSE = oracle_for(case)
+    for rep in range(3):
+        out, lse, o32 = api.case_call(dc, return_lse=True, return_o32=True, fused=True, workspace=ws)
+        torch.cuda.synchronize()
+        assert_parity(out, lse, o32, O, LSE, what=f"fused {name} call {rep}")
+
+
 EQUAL_SHARE = [
     # name, make_case kwargs, workers
     ("ragged_paged64", dict(batch=5, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=64,
