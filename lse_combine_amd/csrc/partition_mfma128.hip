@@ -161,14 +161,19 @@ __device__ __forceinline__ void merge_key_splits(const PartArgs& a, const WaveIn
 __device__ __forceinline__ void fused_combine(const PartArgs& a, const WaveInfo& wv, int* flag_s, int b, int count,
                                               int first_slot) {
   const int tid = threadIdx.x, kg = blockIdx.y, HG = wv.HG, g = a.g;
-  __threadfence();   // release this workgroup's partial
+  // The barrier completes every wave's partial stores; one thread then releases them at
+  // device scope (on this chip a write-back of the XCD's L2, so once per workgroup rather
+  // than once per wave), counts in, and, if last, acquires the others' partials.
   __syncthreads();
   int* cnt = a.counters + (int64_t)b * gridDim.y + kg;
-  if (tid == 0)
-    *flag_s = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == count - 1 ? 1 : 0;
+  if (tid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const int last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == count - 1;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    *flag_s = last ? 1 : 0;
+  }
   __syncthreads();
   if (!__builtin_amdgcn_readfirstlane(*flag_s)) return;
-  __threadfence();   // acquire the other workgroups' partials
   const int kv_end = min((kg + 1) * HG, a.Hkv);
   const int h0 = kg * HG * g, nh = (kv_end - kg * HG) * g;
   constexpr int kUnits = kD / 4;
