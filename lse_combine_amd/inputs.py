@@ -35,6 +35,10 @@ class Case:
     v_is_k_prefix: bool = False
     ov_depth: int = 0
     meta: dict = field(default_factory=dict)
+    # fp8 caches: the caches hold E4M3 codes (uint8) and these fp32 per-token scales,
+    # contiguous [B, Hkv, Lcap] / paged [N, Hkv, ps] (tokens innermost); None otherwise
+    k_scale: torch.Tensor | None = None
+    v_scale: torch.Tensor | None = None
 
     @property
     def batch(self):
@@ -53,17 +57,26 @@ class Case:
         return self.q.shape[2]
 
     @property
+    def kv_fp8(self):
+        return self.k_cache.dtype == torch.uint8
+
+    @property
     def dtype_name(self):
-        return {torch.float32: "f32", torch.bfloat16: "bf16"}[self.q.dtype]
+        q = {torch.float32: "f32", torch.bfloat16: "bf16"}[self.q.dtype]
+        return q + "/fp8-kv" if self.kv_fp8 else q
 
     def kv_bytes(self) -> int:
         """Bytes of K and V that attention must read (attended tokens only)."""
         tokens = int(self.seq_lens.clamp(min=0).sum())
-        es = self.q.element_size()
+        es = self.k_cache.element_size()
         if self.v_is_k_prefix:
             per_tok = self.num_kv_heads * self.qk_depth * es
         else:
             per_tok = self.num_kv_heads * (self.qk_depth + self.ov_depth) * es
+        # the per-token scales of an fp8 cache are read too (4 bytes per token and kv head)
+        for sc in (self.k_scale, self.v_scale):
+            if sc is not None:
+                per_tok += self.num_kv_heads * 4
         return tokens * per_tok
 
     def flops(self) -> int:
@@ -79,7 +92,7 @@ def _randn(gen, shape, dtype):
 def make_case(name="case", *, batch, num_q_heads, num_kv_heads, qk_depth, ov_depth=None,
               dtype=torch.bfloat16, page_size=0, seq_lens=None, len_range=None, kv_capacity=None,
               num_splits=0, seed=0, v_is_k_prefix=False, scale=None, poison=False,
-              spare_pages=0, q_scale=1.0, page_table_width=None) -> Case:
+              spare_pages=0, q_scale=1.0, page_table_width=None, kv_fp8=False, v_scaled=True) -> Case:
     """Build a seeded case.
 
     Exactly one of ``seq_lens`` (a list of lengths) or ``len_range``
@@ -89,6 +102,9 @@ def make_case(name="case", *, batch, num_q_heads, num_kv_heads, qk_depth, ov_dep
     cache slot that no sequence attends (tail of last pages, spare pages,
     contiguous slots past L_b) with NaN so that a kernel reading them shows up.
     ``q_scale`` multiplies q after the draw (large-logit tests).
+    ``kv_fp8``: K and V are drawn as above (fp32) and stored as E4M3 codes with a
+    per-(token, kv head) scale amax / 448 (``v_scaled=False``: V codes of the unscaled
+    values, no V scale); q stays in ``dtype``.
     """
     ov_depth = qk_depth if ov_depth is None else ov_depth
     gen = torch.Generator("cpu")
@@ -122,18 +138,37 @@ def make_case(name="case", *, batch, num_q_heads, num_kv_heads, qk_depth, ov_dep
     q = _randn(gen, (batch, num_q_heads, qk_depth), dtype)
     if q_scale != 1.0:
         q = (q.float() * q_scale).to(dtype)
-    k = _randn(gen, kv_shape_k, dtype)
-    v = None if v_is_k_prefix else _randn(gen, kv_shape_v, dtype)
+    kv_dtype = torch.float32 if kv_fp8 else dtype
+    k = _randn(gen, kv_shape_k, kv_dtype)
+    v = None if v_is_k_prefix else _randn(gen, kv_shape_v, kv_dtype)
+    k_scale = v_scale = None
+    if kv_fp8:
+        k, k_scale = _to_fp8(k, True)
+        if v is not None:
+            v, v_scale = _to_fp8(v, v_scaled)
     if poison:
         _poison(k, v, pos_lens, pt, page_size)
     sc = scale if scale is not None else 1.0 / math.sqrt(qk_depth)
     return Case(name=name, q=q, k_cache=k, v_cache=v, seq_lens=lens32, page_table=pt,
                 page_size=page_size, scale=sc, num_splits=num_splits,
-                v_is_k_prefix=v_is_k_prefix, ov_depth=ov_depth, meta={"seed": seed})
+                v_is_k_prefix=v_is_k_prefix, ov_depth=ov_depth, meta={"seed": seed},
+                k_scale=k_scale, v_scale=v_scale)
+
+
+FP8_E4M3_MAX = 448.0   # largest finite E4M3 magnitude
+
+
+def _to_fp8(x, scaled):
+    """fp32 [rows, slots, Hkv, D] -> (E4M3 codes as uint8, fp32 scales [rows, Hkv, slots])."""
+    if scaled:
+        s = (x.abs().amax(dim=-1) / FP8_E4M3_MAX).clamp(min=2.0 ** -30)
+        codes = (x / s[..., None]).to(torch.float8_e4m3fn).view(torch.uint8)
+        return codes, s.permute(0, 2, 1).contiguous()
+    return x.clamp(-FP8_E4M3_MAX, FP8_E4M3_MAX).to(torch.float8_e4m3fn).view(torch.uint8), None
 
 
 def _poison(k, v, lens, pt, page_size):
-    nan = float("nan")
+    nan = float("nan") if k.dtype != torch.uint8 else 0x7F   # (0x7F: an E4M3 NaN code)
     if pt is None:
         for b, L in enumerate(lens.tolist()):
             k[b, L:] = nan
@@ -172,6 +207,11 @@ WORKLOADS = {
     "latent": dict(seed=5, batch=16, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512,
                    dtype=torch.bfloat16, page_size=64, seq_lens=[8192] * 16, num_splits=8,
                    v_is_k_prefix=True),
+    # the paged GQA workload with an fp8 (E4M3) K/V cache and per-token K and V scales
+    # (same lengths, pages and draws; bf16 q)
+    "paged_gqa_fp8": dict(seed=3, batch=32, num_q_heads=64, num_kv_heads=8, qk_depth=128,
+                          dtype=torch.bfloat16, page_size=64, len_range=(512, 32768),
+                          num_splits=0, page_table_width=512, kv_fp8=True),
 }
 
 
@@ -188,4 +228,5 @@ def to_device(case: Case, device="cuda") -> Case:
     return Case(name=case.name, q=mv(case.q), k_cache=mv(case.k_cache), v_cache=mv(case.v_cache),
                 seq_lens=mv(case.seq_lens), page_table=mv(case.page_table), page_size=case.page_size,
                 scale=case.scale, num_splits=case.num_splits, v_is_k_prefix=case.v_is_k_prefix,
-                ov_depth=case.ov_depth, meta=dict(case.meta))
+                ov_depth=case.ov_depth, meta=dict(case.meta), k_scale=mv(case.k_scale),
+                v_scale=mv(case.v_scale))

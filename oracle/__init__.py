@@ -12,6 +12,7 @@ from .decode_attention import (  # noqa: F401
     decode_attention_fp64,
     decode_attention_splitk_fp64,
     equal_share_pieces,
+    fp8_e4m3_to_fp64,
     partition_partials_fp64,
     range_partials_fp64,
 )

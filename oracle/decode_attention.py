@@ -30,6 +30,9 @@ What is computed (single query per sequence, i.e. decode):
   with c = scale * log2(e) (the ``scale_log2e`` argument of that function).
 * ``bf16_round_fp64`` -- the final cast to bf16 (same paragraph), read as
   round-to-nearest-even.
+* ``fp8_e4m3_to_fp64`` -- the values of an fp8 (E4M3) cache; with per-token scales
+  the definition above runs on code value times scale (FA4Config: fp8 qkv_dtype with a
+  per-token scale_dtype for K).
 
 Readings where the pages are silent (each is listed in the design notes):
 the max is kept in raw q.k units; empty partitions contribute weight 0 and an
@@ -52,9 +55,43 @@ LOG2E = 1.0 / math.log(2.0)
 
 
 # ---------------------------------------------------------------------------
+# fp8 (E4M3, OCP "fn" variant) cache values
+# ---------------------------------------------------------------------------
+def fp8_e4m3_to_fp64(codes):
+    """Decode OCP FP8 E4M3 codes (uint8) to fp64, from the format's definition.
+
+    Bit 7 is the sign, bits 6-3 the exponent e (bias 7), bits 2-0 the mantissa m.
+    e = 0 encodes subnormals m/8 * 2^-6; otherwise the value is (1 + m/8) * 2^(e-7).
+    The variant has no infinities: e = 15 with m = 7 is NaN, so the largest finite
+    magnitude is 1.75 * 2^8 = 448.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    out = sign * mag
+    return np.where((e == 15) & (m == 7), np.nan, out)
+
+
+def _scale_rows(scales, b, kvh, L, page_table, page_size):
+    """Per-token scales of keys 0..L-1 of (sequence b, kv head kvh).
+
+    Layout (tokens innermost so that a tile's scales are contiguous): contiguous
+    [B, Hkv, L_cap]; paged [N_pages, Hkv, page_size].
+    """
+    t = np.arange(L)
+    s = np.asarray(scales)
+    if page_table is None:
+        return s[b, kvh, :L].astype(np.float64)
+    pages = np.asarray(page_table)[b, t // page_size]
+    return s[pages, kvh, t % page_size].astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
 # gathering one (sequence, kv-head) slice of the cache
 # ---------------------------------------------------------------------------
-def _key_rows(k_cache, b, kvh, L, page_table, page_size):
+def _key_rows(k_cache, b, kvh, L, page_table, page_size, scales=None):
     """Return the L key vectors of sequence b, kv head kvh, as fp64 [L, D].
 
     Contiguous layout: k_cache is [B, L_cap, Hkv, D] and key t is k_cache[b, t].
@@ -69,16 +106,24 @@ def _key_rows(k_cache, b, kvh, L, page_table, page_size):
     else:
         pages = np.asarray(page_table)[b, t // page_size]
         rows = k_cache[pages, t % page_size, kvh, :]
-    return np.asarray(rows, dtype=np.float64)
+    rows = np.asarray(rows)
+    if rows.dtype == np.uint8:
+        # fp8 cache: codes times the per-token scale (FA4Config, scale_dtype: per-token
+        # scaling of the quantised cache)
+        vals = fp8_e4m3_to_fp64(rows)
+        s = np.ones(L) if scales is None else _scale_rows(scales, b, kvh, L, page_table, page_size)
+        return vals * s[:, None]
+    return rows.astype(np.float64)
 
 
-def _gather(q, k_cache, v_cache, b, kvh, g, L, page_table, page_size, v_is_k_prefix, ov_depth):
+def _gather(q, k_cache, v_cache, b, kvh, g, L, page_table, page_size, v_is_k_prefix, ov_depth,
+            k_scale=None, v_scale=None):
     qg = np.asarray(q[b, kvh * g:(kvh + 1) * g, :], dtype=np.float64)
-    K = _key_rows(k_cache, b, kvh, L, page_table, page_size)
+    K = _key_rows(k_cache, b, kvh, L, page_table, page_size, k_scale)
     if v_is_k_prefix:
         V = K[:, :ov_depth]
     else:
-        V = _key_rows(v_cache, b, kvh, L, page_table, page_size)
+        V = _key_rows(v_cache, b, kvh, L, page_table, page_size, v_scale)
     return qg, K, V
 
 
@@ -98,10 +143,12 @@ def _dims(q, k_cache, v_cache, v_is_k_prefix, ov_depth):
 # the definition
 # ---------------------------------------------------------------------------
 def decode_attention_fp64(q, k_cache, v_cache, seq_lens, scale, page_table=None, page_size=0,
-                          v_is_k_prefix=False, ov_depth=None):
+                          v_is_k_prefix=False, ov_depth=None, k_scale=None, v_scale=None):
     """Full softmax(scale * q K^T) V per (sequence, head), in fp64.
 
     q: [B, Hq, Dqk]; caches as described in ``_key_rows``; seq_lens: [B].
+    fp8 caches (uint8 E4M3 codes) are read as code value times the per-token scale
+    (``k_scale`` / ``v_scale``, layout in ``_scale_rows``; a missing scale is 1).
     Returns (O [B, Hq, Dv] fp64, LSE [B, Hq] fp64, natural log).
     A sequence of length 0 gives O = 0 and LSE = -inf.
     """
@@ -114,7 +161,7 @@ def decode_attention_fp64(q, k_cache, v_cache, seq_lens, scale, page_table=None,
             continue
         for kvh in range(Hkv):
             qg, K, V = _gather(q, k_cache, v_cache, b, kvh, g, L, page_table, page_size,
-                               v_is_k_prefix, Dv)
+                               v_is_k_prefix, Dv, k_scale, v_scale)
             x = qg @ K.T                                   # [g, L] raw scores
             m = x.max(axis=1, keepdims=True)
             e = np.exp(scale * (x - m))

@@ -21,6 +21,7 @@ from oracle import (
     decode_attention_fp64,
     decode_attention_splitk_fp64,
     equal_share_pieces,
+    fp8_e4m3_to_fp64,
     partition_partials_fp64,
     range_partials_fp64,
 )
@@ -403,3 +404,64 @@ def test_range_partials_combine_to_the_definition():
     np.testing.assert_allclose(m[0], mf[0, :, 0], rtol=1e-15)
     np.testing.assert_allclose(l[0], lf[0, :, 0], rtol=1e-14)
     np.testing.assert_allclose(Op[0], Of[0, :, 0], atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# fp8 (E4M3) caches with per-token scales
+# ---------------------------------------------------------------------------
+def test_fp8_decode_matches_torch_on_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = fp8_e4m3_to_fp64(codes)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(lib))
+    assert np.array_equal(ours[~np.isnan(ours)], lib[~np.isnan(lib)])
+
+
+def test_fp8_decode_special_codes():
+    # worked from the format: sign | exponent (bias 7) | 3-bit mantissa
+    got = fp8_e4m3_to_fp64(np.array([0x00, 0x80, 0x01, 0x07, 0x08, 0x38, 0x3C, 0x7E, 0xFE, 0x7F, 0xFF],
+                                    dtype=np.uint8))
+    want = [0.0, -0.0, 2.0 ** -9, 7 * 2.0 ** -9, 2.0 ** -6, 1.0, 1.5, 448.0, -448.0]
+    np.testing.assert_array_equal(got[:9], want)
+    assert np.signbit(got[1]) and np.isnan(got[9]) and np.isnan(got[10])
+
+
+def _fp8_case(seed, paged):
+    from lse_combine_amd.inputs import make_case
+    return make_case("f8", batch=3, num_q_heads=4, num_kv_heads=2, qk_depth=8, page_size=4 if paged else 0,
+                     seq_lens=[9, 1, 6], seed=seed, kv_fp8=True, dtype=torch.float32)
+
+
+@pytest.mark.parametrize("paged", [0, 1])
+def test_fp8_cache_brute_force_with_torch_decode(paged):
+    c = _fp8_case(70 + paged, paged)
+    pt = None if c.page_table is None else c.page_table.numpy()
+    O, LSE = decode_attention_fp64(c.q.numpy(), c.k_cache.numpy(), c.v_cache.numpy(), c.seq_lens.numpy(),
+                                   c.scale, page_table=pt, page_size=c.page_size,
+                                   k_scale=c.k_scale.numpy(), v_scale=c.v_scale.numpy())
+    # the cache values as torch decodes them, times the scale of their (token, kv head);
+    # scales are stored tokens-innermost, the cache rows token-major
+    kd = c.k_cache.view(torch.float8_e4m3fn).double() * c.k_scale.double().permute(0, 2, 1)[..., None]
+    vd = c.v_cache.view(torch.float8_e4m3fn).double() * c.v_scale.double().permute(0, 2, 1)[..., None]
+    Ob, Lb = brute(c.q.double().numpy(), kd.numpy(), vd.numpy(), c.seq_lens.numpy(), c.scale, pt,
+                   c.page_size)
+    np.testing.assert_allclose(O, Ob, atol=1e-13)
+    np.testing.assert_allclose(LSE, Lb, rtol=1e-13)
+
+
+def test_fp8_scales_act_as_closed_forms():
+    c = _fp8_case(72, 1)
+    pt = c.page_table.numpy()
+    base = dict(page_table=pt, page_size=c.page_size)
+    args = (c.q.numpy(), c.k_cache.numpy(), c.v_cache.numpy(), c.seq_lens.numpy())
+    ks, vs = c.k_scale.numpy(), c.v_scale.numpy()
+    O, LSE = decode_attention_fp64(*args, c.scale, k_scale=ks, v_scale=vs, **base)
+    # all K scales times 4 = the softmax scale times 4
+    O4, L4 = decode_attention_fp64(*args, 4 * c.scale, k_scale=ks, v_scale=vs, **base)
+    O4b, L4b = decode_attention_fp64(*args, c.scale, k_scale=4 * ks, v_scale=vs, **base)
+    np.testing.assert_allclose(O4b, O4, atol=1e-14)
+    np.testing.assert_allclose(L4b, L4, rtol=1e-14)
+    # all V scales times 3 = O times 3, LSE unchanged
+    O3, L3 = decode_attention_fp64(*args, c.scale, k_scale=ks, v_scale=3 * vs.astype(np.float64), **base)
+    np.testing.assert_allclose(O3, 3 * O, atol=1e-14)
+    np.testing.assert_allclose(L3, LSE, rtol=1e-15)
