@@ -96,7 +96,8 @@ def main():
 
     plan = api.DecodePlan(dc.q, dc.k_cache, dc.v_cache, dc.page_table, dc.seq_lens, case.scale, case.num_splits,
                           page_size=case.page_size, v_is_k_prefix=case.v_is_k_prefix, ov_depth=case.ov_depth,
-                          kernel=args.kernel, out=out, fused=args.combine == "fused")
+                          kernel=args.kernel, out=out, fused=args.combine == "fused",
+                          k_scale=dc.k_scale, v_scale=dc.v_scale)
     step = plan.run
 
     # --- streaming-read probe and a copy of known size (counter calibration) ---
@@ -141,10 +142,19 @@ def main():
     # arguments are marshalled once so the host stays ahead of the GPU and the
     # events bracket only the kernels
     P_ = ctypes.c_void_p
-    part_args = (ctypes.byref(prob), P_(dc.q.data_ptr()), P_(dc.k_cache.data_ptr()),
-                 None if dc.v_cache is None else P_(dc.v_cache.data_ptr()),
-                 None if dc.page_table is None else P_(dc.page_table.data_ptr()), P_(dc.seq_lens.data_ptr()),
-                 float(case.scale), chunk, max_splits, P_(part_o.data_ptr()), P_(part_ml.data_ptr()), stream)
+
+    def ptr(t):
+        return None if t is None else P_(t.data_ptr())
+
+    if case.kv_fp8:
+        part_fn = lib.decode_attn_partition_fp8
+        part_args = (ctypes.byref(prob), ptr(dc.q), ptr(dc.k_cache), ptr(dc.v_cache), ptr(dc.k_scale),
+                     ptr(dc.v_scale), ptr(dc.page_table), ptr(dc.seq_lens), float(case.scale), chunk, max_splits,
+                     ptr(part_o), ptr(part_ml), stream)
+    else:
+        part_fn = lib.decode_attn_partition
+        part_args = (ctypes.byref(prob), ptr(dc.q), ptr(dc.k_cache), ptr(dc.v_cache), ptr(dc.page_table),
+                     ptr(dc.seq_lens), float(case.scale), chunk, max_splits, ptr(part_o), ptr(part_ml), stream)
     comb_args = (ctypes.byref(prob), P_(dc.seq_lens.data_ptr()), float(case.scale), chunk, max_splits,
                  P_(part_o.data_ptr()), P_(part_ml.data_ptr()), P_(comb[0].data_ptr()), P_(comb[1].data_ptr()),
                  P_(comb[2].data_ptr()), stream)
@@ -153,7 +163,7 @@ def main():
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_timed)]
     for i in range(n_timed):
         evs[i][0].record()
-        _lib.check(lib.decode_attn_partition(*part_args))
+        _lib.check(part_fn(*part_args))
         evs[i][1].record()
         _lib.check(lib.decode_attn_combine(*comb_args))
         evs[i][2].record()
@@ -185,7 +195,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": case.dtype_name,
-        "data": "synthetic (seeded torch.randn, bf16)",
+        "data": "synthetic (seeded torch.randn" + (", E4M3 K/V with per-token scales)" if case.kv_fp8 else ")"),
         "config": {
             "workload": case.name,
             "batch": B, "q_heads": Hq, "kv_heads": prob.num_kv_heads,
@@ -226,8 +236,11 @@ def cpu_baseline(case, kv_bytes, budget_s):
     lens = case.seq_lens.clamp(min=0).numpy().astype(np.int64)
     q = case.q.float().numpy()
     pt = None if case.page_table is None else case.page_table.numpy()
-    k = case.k_cache.float().numpy()
-    v = None if case.v_cache is None else case.v_cache.float().numpy()
+    # (fp8 caches stay raw E4M3 codes; the oracle decodes them with their scales)
+    k = case.k_cache.numpy() if case.kv_fp8 else case.k_cache.float().numpy()
+    v = None if case.v_cache is None else (case.v_cache.numpy() if case.kv_fp8 else case.v_cache.float().numpy())
+    ks = None if case.k_scale is None else case.k_scale.numpy()
+    vs = None if case.v_scale is None else case.v_scale.numpy()
     info = threadpoolctl.threadpool_info()
     blas = [i for i in info if i.get("user_api") == "blas"]
     threads = blas[0]["num_threads"] if blas else 1
@@ -236,7 +249,7 @@ def cpu_baseline(case, kv_bytes, budget_s):
     while len(times) < 3:
         t0 = time.perf_counter()
         decode_attention_fp64(q, k, v, lens, case.scale, page_table=pt, page_size=case.page_size,
-                              v_is_k_prefix=case.v_is_k_prefix, ov_depth=case.ov_depth)
+                              v_is_k_prefix=case.v_is_k_prefix, ov_depth=case.ov_depth, k_scale=ks, v_scale=vs)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_start + times[-1] > budget_s:
             break

@@ -48,7 +48,11 @@ typedef enum {
   DA_EHIP = -4           /* a HIP runtime call or kernel launch failed */
 } da_status;
 
-typedef enum { DA_F32 = 0, DA_BF16 = 1 } da_dtype;
+typedef enum {
+  DA_F32 = 0,
+  DA_BF16 = 1,
+  DA_FP8_E4M3 = 2        /* cache only (kv_dtype): OCP FP8 E4M3 codes with per-token scales */
+} da_dtype;
 
 typedef enum {
   DA_KERNEL_AUTO = 0,    /* library's choice */
@@ -71,6 +75,8 @@ typedef struct da_problem {
   int32_t max_seq_len;       /* host-side upper bound of seq_lens[]; sizes the grid */
   int32_t v_is_k_prefix;     /* 1 = latent-shared: V[t] = K[t][0:ov_depth], v_cache unused */
   int32_t kernel;            /* da_kernel: AUTO, or force a partition-kernel family */
+  int32_t kv_dtype;          /* 0: K and V have `dtype`; DA_FP8_E4M3: fp8 K / V caches (bf16 q),
+                                run through the *_fp8 entry points that take the scales */
 } da_problem;
 
 /*
@@ -154,6 +160,27 @@ int decode_attn_splitk_fused(const da_problem* p, const void* q, const void* k_c
                              const int32_t* seq_lens, float scale, int32_t num_splits, void* out,
                              float* lse_out, float* o_f32_out, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* The whole decode step over an fp8 cache (FA4Config: an fp8 qkv_dtype with a per-token
+ * scale_dtype for K). kv_dtype must be DA_FP8_E4M3, dtype DA_BF16 (q), Dqk == Dv == 128,
+ * group <= 16, and the cache contiguous or paged with page_size a power of two >= 32.
+ * k_cache / v_cache hold E4M3 codes (one byte each, same layouts as above); key t of kv
+ * head k reads k_scale * code (fp32 scale of that token and kv head) and V likewise with
+ * v_scale (NULL = 1). Scale layout, tokens innermost: contiguous [B][Hkv][kv_capacity],
+ * paged [num_pages][Hkv][page_size]. Everything else as decode_attn_splitk. */
+int decode_attn_splitk_fp8(const da_problem* p, const void* q, const void* k_cache,
+                           const void* v_cache, const float* k_scale, const float* v_scale,
+                           const int32_t* page_table, const int32_t* seq_lens, float scale,
+                           int32_t num_splits, void* out, float* lse_out, float* o_f32_out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Pass 1 only over an fp8 cache (scales as decode_attn_splitk_fp8, partials as
+ * decode_attn_partition). */
+int decode_attn_partition_fp8(const da_problem* p, const void* q, const void* k_cache,
+                              const void* v_cache, const float* k_scale, const float* v_scale,
+                              const int32_t* page_table, const int32_t* seq_lens, float scale,
+                              int32_t chunk_tokens, int32_t max_splits, float* part_o,
+                              float* part_ml, void* stream);
 
 /* Pass 1 only (fa4_splitk_combine_write, second paragraph: each partition stages its
  * normalised O and its (max, sum)). Writes part_ml / part_o (device, layouts above) for

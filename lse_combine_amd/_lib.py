@@ -12,14 +12,14 @@ LIB_PATH = os.path.join(PKG, "lib", "libdecode_attn.so")
 HEADER = os.path.join(ROOT, "include", "decode_attn.h")
 
 DA_OK, DA_EINVAL, DA_EUNSUPPORTED, DA_EWORKSPACE, DA_EHIP = 0, -1, -2, -3, -4
-DA_F32, DA_BF16 = 0, 1
+DA_F32, DA_BF16, DA_FP8_E4M3 = 0, 1, 2
 DA_KERNEL_AUTO, DA_KERNEL_FMA, DA_KERNEL_MFMA = 0, 1, 2
 
 
 class DaProblem(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "batch", "num_q_heads", "num_kv_heads", "qk_depth", "ov_depth", "dtype", "page_size",
-        "max_pages_per_seq", "num_pages", "kv_capacity", "max_seq_len", "v_is_k_prefix", "kernel")]
+        "max_pages_per_seq", "num_pages", "kv_capacity", "max_seq_len", "v_is_k_prefix", "kernel", "kv_dtype")]
 
 
 class DaError(RuntimeError):
@@ -39,6 +39,10 @@ _SIGS = {
                                           _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "decode_attn_splitk_fused": (ctypes.c_int, [ctypes.POINTER(DaProblem), _P, _P, _P, _P, _P, ctypes.c_float,
                                                 _I32, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "decode_attn_splitk_fp8": (ctypes.c_int, [ctypes.POINTER(DaProblem), _P, _P, _P, _P, _P, _P, _P,
+                                              ctypes.c_float, _I32, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "decode_attn_partition_fp8": (ctypes.c_int, [ctypes.POINTER(DaProblem), _P, _P, _P, _P, _P, _P, _P,
+                                                 ctypes.c_float, _I32, _I32, _P, _P, _P]),
     "decode_attn_partition": (ctypes.c_int, [ctypes.POINTER(DaProblem), _P, _P, _P, _P, _P, ctypes.c_float,
                                              _I32, _I32, _P, _P, _P]),
     "decode_attn_combine": (ctypes.c_int, [ctypes.POINTER(DaProblem), _P, ctypes.c_float, _I32, _I32, _P, _P,

@@ -31,8 +31,13 @@ def make_problem(q, k_cache, v_cache=None, page_table=None, *, page_size=0, max_
     """Describe one decode step from its tensors (shapes as in include/decode_attn.h)."""
     if q.dim() != 3 or k_cache.dim() != 4:
         raise ValueError("q must be [B, Hq, Dqk] and k_cache 4-D")
-    if q.dtype not in _DTYPES or k_cache.dtype != q.dtype or (v_cache is not None and v_cache.dtype != q.dtype):
-        raise ValueError("q, k_cache and v_cache must share dtype float32 or bfloat16")
+    fp8 = k_cache.dtype == torch.uint8   # E4M3 codes
+    if q.dtype not in _DTYPES:
+        raise ValueError("q must be float32 or bfloat16")
+    if not fp8 and (k_cache.dtype != q.dtype or (v_cache is not None and v_cache.dtype != q.dtype)):
+        raise ValueError("q, k_cache and v_cache must share dtype float32 or bfloat16 (or uint8 fp8 caches)")
+    if fp8 and v_cache is not None and v_cache.dtype != torch.uint8:
+        raise ValueError("an fp8 k_cache needs an fp8 (uint8) v_cache")
     B, Hq, Dqk = q.shape
     Hkv = k_cache.shape[2]
     if k_cache.shape[3] != Dqk:
@@ -48,6 +53,7 @@ def make_problem(q, k_cache, v_cache=None, page_table=None, *, page_size=0, max_
     p = DaProblem()
     p.batch, p.num_q_heads, p.num_kv_heads, p.qk_depth, p.ov_depth = B, Hq, Hkv, Dqk, Dv
     p.dtype = _DTYPES[q.dtype]
+    p.kv_dtype = _lib.DA_FP8_E4M3 if fp8 else 0
     p.kernel = _KERNELS[kernel]
     p.v_is_k_prefix = 1 if v_is_k_prefix else 0
     if page_table is not None:
@@ -89,7 +95,8 @@ def workspace_bytes(problem: DaProblem, num_splits=0):
 
 def decode_attn(q, k_cache, v_cache, page_table, seq_lens, scale, num_splits=0, *, page_size=0,
                 max_seq_len=None, v_is_k_prefix=False, ov_depth=None, out=None, lse=None, o32=None,
-                return_lse=False, return_o32=False, workspace=None, kernel="auto", fused=False):
+                return_lse=False, return_o32=False, workspace=None, kernel="auto", fused=False,
+                k_scale=None, v_scale=None):
     """The whole split-K decode step. Returns out (bf16 [B, Hq, Dv]) or (out, lse, o32).
 
     fused=True runs decode_attn_splitk_fused (the combine done by each group's last
@@ -109,10 +116,16 @@ def decode_attn(q, k_cache, v_cache, page_table, seq_lens, scale, num_splits=0, 
     need = workspace_bytes(prob, num_splits)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
-    fn = lib.decode_attn_splitk_fused if fused else lib.decode_attn_splitk
-    check(fn(ctypes.byref(prob), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
-                                 _ptr(seq_lens), float(scale), int(num_splits), _ptr(out), _ptr(lse), _ptr(o32),
-                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
+    ws = (_ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
+    if prob.kv_dtype:
+        _check_tensors(k_scale, v_scale)
+        check(lib.decode_attn_splitk_fp8(ctypes.byref(prob), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                         _ptr(v_scale), _ptr(page_table), _ptr(seq_lens), float(scale),
+                                         int(num_splits), _ptr(out), _ptr(lse), _ptr(o32), *ws))
+    else:
+        fn = lib.decode_attn_splitk_fused if fused else lib.decode_attn_splitk
+        check(fn(ctypes.byref(prob), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(seq_lens),
+                 float(scale), int(num_splits), _ptr(out), _ptr(lse), _ptr(o32), *ws))
     if return_lse or return_o32:
         return out, lse, o32
     return out
@@ -145,7 +158,8 @@ def slot_table(problem: DaProblem, max_splits, part_ml):
 
 
 def partition(q, k_cache, v_cache, page_table, seq_lens, scale, chunk_tokens, max_splits, *, page_size=0,
-              max_seq_len=None, v_is_k_prefix=False, ov_depth=None, part_o=None, part_ml=None, kernel="auto"):
+              max_seq_len=None, v_is_k_prefix=False, ov_depth=None, part_o=None, part_ml=None, kernel="auto",
+              k_scale=None, v_scale=None):
     """Pass 1 only. Returns (part_o, part_ml) fp32 in the layout ``alloc_partials`` describes."""
     lib = _lib.load()
     prob = make_problem(q, k_cache, v_cache, page_table, page_size=page_size, max_seq_len=max_seq_len,
@@ -155,9 +169,15 @@ def partition(q, k_cache, v_cache, page_table, seq_lens, scale, chunk_tokens, ma
         po, pml = alloc_partials(prob, chunk_tokens, max_splits, q.device)
         part_o = po if part_o is None else part_o
         part_ml = pml if part_ml is None else part_ml
-    check(lib.decode_attn_partition(ctypes.byref(prob), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
-                                    _ptr(seq_lens), float(scale), int(chunk_tokens), int(max_splits),
-                                    _ptr(part_o), _ptr(part_ml), _stream()))
+    if prob.kv_dtype:
+        check(lib.decode_attn_partition_fp8(ctypes.byref(prob), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                            _ptr(k_scale), _ptr(v_scale), _ptr(page_table), _ptr(seq_lens),
+                                            float(scale), int(chunk_tokens), int(max_splits), _ptr(part_o),
+                                            _ptr(part_ml), _stream()))
+    else:
+        check(lib.decode_attn_partition(ctypes.byref(prob), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                        _ptr(page_table), _ptr(seq_lens), float(scale), int(chunk_tokens),
+                                        int(max_splits), _ptr(part_o), _ptr(part_ml), _stream()))
     return part_o, part_ml
 
 
@@ -181,7 +201,7 @@ def case_call(case, device="cuda", **kw):
     """Run a lse_combine_amd.inputs.Case already moved to ``device`` (see ``to_device``)."""
     return decode_attn(case.q, case.k_cache, case.v_cache, case.page_table, case.seq_lens, case.scale,
                        case.num_splits, page_size=case.page_size, v_is_k_prefix=case.v_is_k_prefix,
-                       ov_depth=case.ov_depth, **kw)
+                       ov_depth=case.ov_depth, k_scale=case.k_scale, v_scale=case.v_scale, **kw)
 
 
 class DecodePlan:
@@ -194,7 +214,7 @@ class DecodePlan:
 
     def __init__(self, q, k_cache, v_cache, page_table, seq_lens, scale, num_splits=0, *, page_size=0,
                  max_seq_len=None, v_is_k_prefix=False, ov_depth=None, kernel="auto", out=None, lse=None,
-                 o32=None, fused=False):
+                 o32=None, fused=False, k_scale=None, v_scale=None):
         self.lib = _lib.load()
         self.prob = make_problem(q, k_cache, v_cache, page_table, page_size=page_size, max_seq_len=max_seq_len,
                                  v_is_k_prefix=v_is_k_prefix, ov_depth=ov_depth, kernel=kernel)
@@ -207,10 +227,16 @@ class DecodePlan:
         self.workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
         self.fn = self.lib.decode_attn_splitk_fused if fused else self.lib.decode_attn_splitk
         self.chunk, self.max_splits = choose_splits(self.prob, num_splits)
-        self._keep = (q, k_cache, v_cache, page_table, seq_lens)
-        self._args = (ctypes.byref(self.prob), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
-                      _ptr(seq_lens), float(scale), int(num_splits), _ptr(self.out), _ptr(lse), _ptr(o32),
-                      _ptr(self.workspace), self.workspace.numel())
+        self._keep = (q, k_cache, v_cache, page_table, seq_lens, k_scale, v_scale)
+        if self.prob.kv_dtype:
+            self.fn = self.lib.decode_attn_splitk_fp8
+            self._args = (ctypes.byref(self.prob), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                          _ptr(v_scale), _ptr(page_table), _ptr(seq_lens), float(scale), int(num_splits),
+                          _ptr(self.out), _ptr(lse), _ptr(o32), _ptr(self.workspace), self.workspace.numel())
+        else:
+            self._args = (ctypes.byref(self.prob), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+                          _ptr(seq_lens), float(scale), int(num_splits), _ptr(self.out), _ptr(lse), _ptr(o32),
+                          _ptr(self.workspace), self.workspace.numel())
 
     def run(self, stream=None):
         s = _stream() if stream is None else ctypes.c_void_p(stream)

@@ -72,6 +72,16 @@ int check_problem(const da_problem* p, Variant* var) {
     return fail(DA_EINVAL, "latent-shared V (ov_depth %d) must fit in the K row (qk_depth %d)", p->ov_depth, p->qk_depth);
   if (p->kernel < DA_KERNEL_AUTO || p->kernel > DA_KERNEL_MFMA) return fail(DA_EINVAL, "unknown kernel hint %d", p->kernel);
   const int g = p->num_q_heads / p->num_kv_heads;
+  if (p->kv_dtype != 0) {
+    if (p->kv_dtype != DA_FP8_E4M3) return fail(DA_EINVAL, "kv_dtype must be 0 or DA_FP8_E4M3 (got %d)", p->kv_dtype);
+    if (p->dtype != DA_BF16 || p->qk_depth != 128 || p->ov_depth != 128 || p->v_is_k_prefix || g > 16 ||
+        p->kernel == DA_KERNEL_FMA || (p->page_size > 0 && (p->page_size < kTileKeys || (p->page_size & (p->page_size - 1)))))
+      return fail(DA_EUNSUPPORTED,
+                  "fp8 caches are supported with bf16 q, depth 128/128, group <= 16 (matrix-core kernel), and a "
+                  "contiguous cache or pages of a power of two >= 32 keys");
+    *var = kVarMfma128;
+    return DA_OK;
+  }
 
   if (p->qk_depth == 576 && p->ov_depth == 512) {
     if (p->dtype != DA_BF16 || !p->v_is_k_prefix || p->num_kv_heads != 1 || g % 16 != 0 || p->kernel == DA_KERNEL_FMA)
@@ -301,16 +311,28 @@ int check_scale(float scale) {
   return DA_OK;
 }
 
+// fp8 caches come with their K scales through the *_fp8 entry points; the plain entry
+// points (which have no scale arguments) refuse them.
+int check_fp8_args(const da_problem* p, const float* k_scale) {
+  if (p->kv_dtype == DA_FP8_E4M3 && !k_scale)
+    return fail(DA_EINVAL, "fp8 caches need k_scale (use decode_attn_splitk_fp8 / decode_attn_partition_fp8)");
+  if (p->kv_dtype != DA_FP8_E4M3 && k_scale)
+    return fail(DA_EINVAL, "k_scale / v_scale are for fp8 caches (kv_dtype = DA_FP8_E4M3)");
+  return DA_OK;
+}
+
 // The whole step. With `fused`, the matrix-core kernel combines in its last-arriving
 // workgroups (no second launch) wherever sequences have few partitions (up to 16, where
 // one workgroup's combine is short); elsewhere, and for the other kernels, the combine
 // is a launch of its own. The results are the same either way.
 int run_splitk(const da_problem* p, const void* q, const void* k_cache, const void* v_cache, const int32_t* page_table,
                const int32_t* seq_lens, float scale, int32_t num_splits, void* out, float* lse_out, float* o_f32_out,
-               void* workspace, size_t workspace_bytes, void* stream, bool fused) {
+               void* workspace, size_t workspace_bytes, void* stream, bool fused, const float* k_scale = nullptr,
+               const float* v_scale = nullptr) {
   Variant var;
   int r = check_problem(p, &var);
   if (r) return r;
+  if ((r = check_fp8_args(p, k_scale))) return r;
   if ((r = check_inputs(p, q, k_cache, v_cache, page_table, seq_lens))) return r;
   if ((r = check_scale(scale))) return r;
   if (!out) return fail(DA_EINVAL, "out must be non-NULL");
@@ -334,6 +356,9 @@ int run_splitk(const da_problem* p, const void* q, const void* k_cache, const vo
   a.lse = lse_out;
   a.o32 = o_f32_out;
   a.direct_single = 1;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.kv_fp8 = p->kv_dtype == DA_FP8_E4M3;
   const int64_t per_seq = C == 0 ? (int64_t)P / p->batch + 1 : P;
   const bool fuse = fused && var == kVarMfma128 && per_seq <= 16;
   if (fuse) a.counters = (int32_t*)((char*)workspace + cnt_off);
@@ -428,12 +453,46 @@ int decode_attn_splitk_fused(const da_problem* p, const void* q, const void* k_c
                     workspace, workspace_bytes, stream, true);
 }
 
+int decode_attn_splitk_fp8(const da_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                           const float* k_scale, const float* v_scale, const int32_t* page_table,
+                           const int32_t* seq_lens, float scale, int32_t num_splits, void* out, float* lse_out,
+                           float* o_f32_out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!p) return fail(DA_EINVAL, "problem is NULL");
+  if (p->kv_dtype != DA_FP8_E4M3) return fail(DA_EINVAL, "decode_attn_splitk_fp8 needs kv_dtype = DA_FP8_E4M3");
+  return run_splitk(p, q, k_cache, v_cache, page_table, seq_lens, scale, num_splits, out, lse_out, o_f32_out,
+                    workspace, workspace_bytes, stream, false, k_scale, v_scale);
+}
+
+static int partition_impl(const da_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                          const float* k_scale, const float* v_scale, const int32_t* page_table,
+                          const int32_t* seq_lens, float scale, int32_t chunk_tokens, int32_t max_splits,
+                          float* part_o, float* part_ml, void* stream);
+
+int decode_attn_partition_fp8(const da_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                              const float* k_scale, const float* v_scale, const int32_t* page_table,
+                              const int32_t* seq_lens, float scale, int32_t chunk_tokens, int32_t max_splits,
+                              float* part_o, float* part_ml, void* stream) {
+  if (!p) return fail(DA_EINVAL, "problem is NULL");
+  if (p->kv_dtype != DA_FP8_E4M3) return fail(DA_EINVAL, "decode_attn_partition_fp8 needs kv_dtype = DA_FP8_E4M3");
+  return partition_impl(p, q, k_cache, v_cache, k_scale, v_scale, page_table, seq_lens, scale, chunk_tokens,
+                        max_splits, part_o, part_ml, stream);
+}
+
 int decode_attn_partition(const da_problem* p, const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* page_table, const int32_t* seq_lens, float scale, int32_t chunk_tokens,
                           int32_t max_splits, float* part_o, float* part_ml, void* stream) {
+  return partition_impl(p, q, k_cache, v_cache, nullptr, nullptr, page_table, seq_lens, scale, chunk_tokens,
+                        max_splits, part_o, part_ml, stream);
+}
+
+static int partition_impl(const da_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                          const float* k_scale, const float* v_scale, const int32_t* page_table,
+                          const int32_t* seq_lens, float scale, int32_t chunk_tokens, int32_t max_splits,
+                          float* part_o, float* part_ml, void* stream) {
   Variant var;
   int r = check_problem(p, &var);
   if (r) return r;
+  if ((r = check_fp8_args(p, k_scale))) return r;
   if ((r = check_inputs(p, q, k_cache, v_cache, page_table, seq_lens))) return r;
   if ((r = check_scale(scale))) return r;
   if ((r = check_split_args(p, var, chunk_tokens, max_splits))) return r;
@@ -443,6 +502,9 @@ int decode_attn_partition(const da_problem* p, const void* q, const void* k_cach
   a.part_ml = part_ml;
   if (chunk_tokens == 0) a.meta = meta_of(p, max_splits, part_ml);
   a.direct_single = 0;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.kv_fp8 = p->kv_dtype == DA_FP8_E4M3;
   if ((r = launch_partition(p, var, a, (hipStream_t)stream, device_num_cus()))) return r;
   return ok();
 }

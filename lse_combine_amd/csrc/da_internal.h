@@ -26,6 +26,9 @@ struct PartArgs {
   int32_t* meta;            // equal shares: [B][2] (first slot, partition count) per sequence
   int32_t* counters;        // fused combine: [B][head groups] arrival counters (zero between
                             // calls); NULL: the combine is a separate launch
+  const float* k_scale;     // fp8 caches: per-token scales, tokens innermost ([B][Hkv][Lcap]
+  const float* v_scale;     //   or [pages][Hkv][page]); v_scale may be NULL (1)
+  int32_t kv_fp8;           // 1: k / v hold E4M3 codes
   uint16_t* out;            // bf16 [B][Hq][Dv]; written directly by single-partition rows
   float* lse;               // optional
   float* o32;               // optional

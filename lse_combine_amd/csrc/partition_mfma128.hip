@@ -79,6 +79,24 @@ __device__ __forceinline__ void wait_vm(int n) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Four E4M3 codes (one dword, byte 0 first) as two packed bf16 pairs, through the
+// hardware fp8 -> fp32 conversion (OCP E4M3; exact, as is the fp32 -> bf16 step).
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  u32x2 r;
+  r[0] = pack_bf16x2(lo[0], lo[1]);
+  r[1] = pack_bf16x2(hi[0], hi[1]);
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  const u32x2 a = fp8x4_to_bf16x4(w0), b = fp8x4_to_bf16x4(w1);
+  return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
+}
+
 // max over the four lanes n, n+16, n+32, n+48 (the four key groups of a column).
 // (v_permlane32_swap / v_permlane16_swap would do this on the VALU, but this compiler
 // folds the two results of a swap of a value with itself into one, losing half the
@@ -195,7 +213,7 @@ __device__ __forceinline__ void fused_combine(const PartArgs& a, const WaveInfo&
 // One piece of work: keys [start, end) of sequence b for this workgroup's kv heads.
 // Writes the normalised partial and (m, l) of partition / slot p, or the finished bf16
 // row when `direct` (the sequence has a single partition).
-template <bool HL, int PM>
+template <bool HL, int PM, bool F8>
 __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv, char* smem, int* pages_s,
                                           int* flag_s, int b, int start, int end, int p, int count,
                                           int first_slot) {
@@ -208,7 +226,9 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
   char* vt = smem + wv.w * kWaveBytes;
   int first_page = 0;   // page index held by pages_s[0] in the current segment
 
-  // q as the B operand of S^T = K q^T: column n, depth 32j + 8qd .. +8.
+  // q as the B operand of S^T = K q^T: column n; MFMA step j covers depth 32j + 8qd .. +8
+  // (bf16 caches) or, matching the 16-value fp8 loads of K, depth 16(qd + 4(j/2)) + 8(j%2) .. +8
+  // (the order of the depth sum is free as long as q and K agree).
   bf16x8 qf[4];
   {
     const int kv_safe = wave_active ? kvh : 0;
@@ -216,7 +236,8 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
                            ((int64_t)b * a.Hq + (int64_t)kv_safe * g + (col_valid ? hc : 0)) * kD;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      u32x4 v = *(const u32x4*)(qrow + 32 * j + 8 * qd);
+      const int d0 = F8 ? 16 * (qd + 4 * (j >> 1)) + 8 * (j & 1) : 32 * j + 8 * qd;
+      u32x4 v = *(const u32x4*)(qrow + d0);
       if (!col_valid) v = u32x4{0u, 0u, 0u, 0u};
       qf[j] = as_bf16x8(v);
     }
@@ -224,10 +245,11 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
 
   const char* kc = (const char*)a.k;
   const char* vc = (const char*)a.v;
-  const uint32_t krow_bytes = (uint32_t)a.Hkv * kD * 2;          // bytes between tokens (K)
-  const uint32_t vrow_bytes = (uint32_t)a.Hkv * a.v_row_len * 2; // bytes between tokens (V)
-  const uint32_t kslice = (uint32_t)(wave_active ? kvh : 0) * kD * 2;
-  const uint32_t vslice = (uint32_t)(wave_active ? kvh : 0) * a.v_row_len * 2;
+  constexpr uint32_t es = F8 ? 1 : 2;                              // bytes per cache element
+  const uint32_t krow_bytes = (uint32_t)a.Hkv * kD * es;          // bytes between tokens (K)
+  const uint32_t vrow_bytes = (uint32_t)a.Hkv * a.v_row_len * es; // bytes between tokens (V)
+  const uint32_t kslice = (uint32_t)(wave_active ? kvh : 0) * kD * es;
+  const uint32_t vslice = (uint32_t)(wave_active ? kvh : 0) * a.v_row_len * es;
   const float c = a.c;
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -276,8 +298,14 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
         const int rows = __builtin_amdgcn_readfirstlane(min(max(last + 1 - 16 * h, 0), 16));
         const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(kc + (row0 + 16 * h) * krow_bytes + kslice), 0, rows * krow_bytes, kRsrcWord3);
+        if constexpr (F8) {
+          // 16 fp8 values per load: depth chunks qd and qd + 4 of the 128-byte row slice
 #pragma unroll
-        for (int j = 0; j < 4; ++j) T.k[h][j] = buf_load16(rk, koff + 64 * j, 0);
+          for (int jj = 0; jj < 2; ++jj) T.k[h][jj] = buf_load16(rk, koff + 64 * jj, 0);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) T.k[h][j] = buf_load16(rk, koff + 64 * j, 0);
+        }
       }
     } else {
 #pragma unroll
@@ -326,14 +354,77 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
     for (int blk = 0; blk < 2; ++blk) {
       s[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(T.k[blk][j]), qf[j], s[blk], 0, 0, 0);
+      for (int j = 0; j < 4; ++j) {
+        // fp8 K: the 8 values of step j are dwords 2(j%2), 2(j%2)+1 of load j/2, widened
+        // exactly to bf16 (every E4M3 value is a bf16 value)
+        const bf16x8 kf = F8 ? fp8x8_to_bf16x8(T.k[blk][j >> 1][2 * (j & 1)], T.k[blk][j >> 1][2 * (j & 1) + 1])
+                             : as_bf16x8(T.k[blk][j]);
+        s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[j], s[blk], 0, 0, 0);
+      }
     }
   };
 
-  // phase B: online softmax and P.V. On a ragged tile the scores of missing keys are set
-  // to -inf first; exp2(-inf) = 0 then removes them from the sums.
-  auto softmax_pv = [&](f32x4* s, int t0, bool k_in_flight) {
+  // per-token scales of the tile's keys that this lane holds (fp8 caches): keys
+  // 4qd .. 4qd+3 and 16+4qd .. 16+4qd+3, 16 contiguous bytes each in the tokens-innermost
+  // scale layout; missing keys of a ragged tile read 0 (their scores are masked anyway)
+  auto load_sc = [&](f32x4* ksc, f32x4* vsc, int t0) {
+    const int last = min(kTile - 1, end - 1 - t0);
+    const int kv_safe = wave_active ? kvh : 0;
+    int64_t base;
+    if constexpr (PM == kContiguous) {
+      base = ((int64_t)b * a.Hkv + kv_safe) * a.kv_capacity + t0;
+    } else {
+      const int slot = min(max((t0 >> a.page_shift) - first_page, 0), kMaxLdsPages - 1);
+      const int page = __builtin_amdgcn_readfirstlane(min(max(pages_s[slot], 0), a.num_pages - 1));
+      base = ((int64_t)page * a.Hkv + kv_safe) * a.page_size + (t0 & (a.page_size - 1));
+    }
+    const int nk = __builtin_amdgcn_readfirstlane(max(last + 1, 0));
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.k_scale + base), 0, nk * 4, kRsrcWord3);
+    ksc[0] = __builtin_bit_cast(f32x4, buf_load16(rk, 16 * qd, 0));
+    ksc[1] = __builtin_bit_cast(f32x4, buf_load16(rk, 64 + 16 * qd, 0));
+    if (a.v_scale) {
+      const __amdgpu_buffer_rsrc_t rv =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(a.v_scale + base), 0, nk * 4, kRsrcWord3);
+      vsc[0] = __builtin_bit_cast(f32x4, buf_load16(rv, 16 * qd, 0));
+      vsc[1] = __builtin_bit_cast(f32x4, buf_load16(rv, 64 + 16 * qd, 0));
+    } else {
+      vsc[0] = vsc[1] = f32x4{1.f, 1.f, 1.f, 1.f};
+    }
+  };
+
+  // fp8 V: the tile's 32 rows into registers (lane l: row l/2, 64-byte half l%2), then
+  // widened to bf16 and written to this wave's LDS tile in the swizzled layout that the
+  // transposing reads expect (source chunk c of row r at slot c ^ (r & 15))
+  auto load_v8 = [&](u32x4* vr, int t0) {
+    const int last = min(kTile - 1, end - 1 - t0);
+    const int64_t row0 = tile_row0(t0);
+    const int rows = __builtin_amdgcn_readfirstlane(max(last + 1, 0));
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vc + row0 * vrow_bytes + vslice), 0, rows * vrow_bytes, kRsrcWord3);
+    const uint32_t off = (uint32_t)(lane >> 1) * vrow_bytes + 64 * (lane & 1);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) vr[m] = buf_load16(rv, off + 16 * m, 0);
+  };
+  auto stage_v8 = [&](const u32x4* vr) {
+    const int r = lane >> 1;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int c0 = 8 * (lane & 1) + 2 * m;
+      *(bf16x8*)(vt + r * 256 + ((c0 ^ (r & 15)) << 4)) = fp8x8_to_bf16x8(vr[m][0], vr[m][1]);
+      *(bf16x8*)(vt + r * 256 + (((c0 + 1) ^ (r & 15)) << 4)) = fp8x8_to_bf16x8(vr[m][2], vr[m][3]);
+    }
+  };
+
+  // phase B: online softmax, giving P^T as the B operand of P.V. On a ragged tile the
+  // scores of missing keys are set to -inf first; exp2(-inf) = 0 then removes them from
+  // the sums. With fp8 caches the scores take the K scales of their keys first, and the
+  // V scales multiply p in the P.V operand only (l sums the unscaled p).
+  auto softmax_p = [&](f32x4* s, int t0, bf16x8& pb_hi, bf16x8& pb_lo, const f32x4* ksc, const f32x4* vsc) {
+    if constexpr (F8) {
+      s[0] *= ksc[0];
+      s[1] *= ksc[1];
+    }
     const int nvalid = end - t0;
     if (nvalid < kTile) {
 #pragma unroll
@@ -372,7 +463,8 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) {
       const int blk = s2 >> 1, i0 = (s2 & 1) * 2;
-      const float p0 = pr[blk][i0], p1 = pr[blk][i0 + 1];
+      const float p0 = F8 ? pr[blk][i0] * vsc[blk][i0] : pr[blk][i0];
+      const float p1 = F8 ? pr[blk][i0 + 1] * vsc[blk][i0 + 1] : pr[blk][i0 + 1];
       const uint32_t h = pack_bf16x2(p0, p1);
       if constexpr (HL) {
         pw[s2] = pack_bf16x2(fmaf(-lo_mask, bf16lo(h), p0), fmaf(-lo_mask, bf16hi(h), p1));
@@ -381,13 +473,12 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
         lw[s2] = pack_bf16x2(p0 - bf16lo(h), p1 - bf16hi(h));
       }
     }
-    const bf16x8 pb_hi = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
-    bf16x8 pb_lo;
+    pb_hi = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
     if constexpr (!HL) pb_lo = as_bf16x8(u32x4{lw[0], lw[1], lw[2], lw[3]});
+  };
 
-    // V of this tile must have landed in LDS: it was requested before the 8 K loads of
-    // the next tile, which may stay in flight
-    wait_vm(k_in_flight ? 8 : 0);
+  // phase C: O^T += V^T P^T, V^T read transposed from the LDS tile
+  auto pv = [&](const bf16x8& pb_hi, const bf16x8& pb_lo) {
     // V^T A operand: lane (n, qd) gets depth 16db + n of keys 4qd..+3 and 16+4qd..+3
     const int r0 = 4 * qd + (n >> 2);
 #pragma unroll
@@ -434,17 +525,48 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
       // as the current tile has been moved to LDS and into the score MFMAs, and stay in
       // flight through the softmax and P.V of the current tile.
       KTile T;
-      load_k(T, s0 + ks * kTile);
-      load_v(s0 + ks * kTile);
-      for (int it = ks; it < n_tiles; it += KS) {
-        const bool has_next = it + KS < n_tiles;
-        f32x4 s[2];
-        score(T, s);
-        if (has_next) load_k(T, s0 + (it + KS) * kTile);
-        softmax_pv(s, s0 + it * kTile, has_next);
-        // the transposing reads of this tile are complete (their data fed the MFMAs):
-        // the LDS tile can take the next V
-        if (has_next) load_v(s0 + (it + KS) * kTile);
+      if constexpr (F8) {
+        // fp8: K, V and the scales of the next tile are in flight (in registers) through
+        // the softmax and P.V of the current one. (Two tiles in flight measured slower:
+        // this path is bound by the per-tile instruction chain, not by memory latency.)
+        u32x4 vr[4];
+        f32x4 ksc[2], vsc[2];
+        load_k(T, s0 + ks * kTile);
+        load_v8(vr, s0 + ks * kTile);
+        load_sc(ksc, vsc, s0 + ks * kTile);
+        for (int it = ks; it < n_tiles; it += KS) {
+          const bool has_next = it + KS < n_tiles;
+          const int tn = s0 + (it + KS) * kTile;
+          f32x4 s[2];
+          score(T, s);
+          if (has_next) load_k(T, tn);
+          stage_v8(vr);
+          bf16x8 pb_hi, pb_lo;
+          softmax_p(s, s0 + it * kTile, pb_hi, pb_lo, ksc, vsc);
+          if (has_next) {
+            load_v8(vr, tn);
+            load_sc(ksc, vsc, tn);
+          }
+          pv(pb_hi, pb_lo);
+        }
+      } else {
+        load_k(T, s0 + ks * kTile);
+        load_v(s0 + ks * kTile);
+        for (int it = ks; it < n_tiles; it += KS) {
+          const bool has_next = it + KS < n_tiles;
+          f32x4 s[2];
+          score(T, s);
+          if (has_next) load_k(T, s0 + (it + KS) * kTile);
+          bf16x8 pb_hi, pb_lo;
+          softmax_p(s, s0 + it * kTile, pb_hi, pb_lo, nullptr, nullptr);
+          // V of this tile must have landed in LDS: it was requested before the 8 K loads
+          // of the next tile, which may stay in flight
+          wait_vm(has_next ? 8 : 0);
+          pv(pb_hi, pb_lo);
+          // the transposing reads of this tile are complete (their data fed the MFMAs):
+          // the LDS tile can take the next V
+          if (has_next) load_v(s0 + (it + KS) * kTile);
+        }
       }
     }
   }
@@ -488,7 +610,7 @@ struct PieceTable {
   int64_t U, Wact, ts, te, tile_base;
 };
 
-template <bool HL, int PM>
+template <bool HL, int PM, bool F8>
 // one 8-wave workgroup per CU (two waves per SIMD): the tile loop needs about 160 VGPRs,
 // and eight waves per CU already keep the memory system busy under the equal-share schedule
 __global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
@@ -640,7 +762,7 @@ void partition_gqa_kernel(PartArgs a, int HG, int KS) {
       first_slot = __builtin_amdgcn_readfirstlane(table.row[j].first_slot);
       count = __builtin_amdgcn_readfirstlane(table.row[j].count);
     }
-    run_piece<HL, PM>(a, wv, smem, pages_s, &fuse_flag, b, start, end, p, count, first_slot);
+    run_piece<HL, PM, F8>(a, wv, smem, pages_s, &fuse_flag, b, start, end, p, count, first_slot);
   }
 }
 
@@ -650,15 +772,29 @@ hipError_t launch_hl(const PartArgs& a, int pm, int HG, int KS, hipStream_t s) {
   const dim3 grid = a.workers > 0 ? dim3((unsigned)a.workers, groups, 1) : dim3((unsigned)a.max_splits, groups, (unsigned)a.B);
   const dim3 block(HG * KS * 64);
   const size_t lds = (size_t)HG * KS * kWaveBytes;
+  if (a.kv_fp8) {
+    // fp8 caches: contiguous or pages of a power of two >= 32 keys
+    switch (pm) {
+      case kContiguous:
+        hipLaunchKernelGGL((partition_gqa_kernel<HL, kContiguous, true>), grid, block, lds, s, a, HG, KS);
+        break;
+      case kPagedAligned:
+        hipLaunchKernelGGL((partition_gqa_kernel<HL, kPagedAligned, true>), grid, block, lds, s, a, HG, KS);
+        break;
+      default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (pm) {
     case kContiguous:
-      hipLaunchKernelGGL((partition_gqa_kernel<HL, kContiguous>), grid, block, lds, s, a, HG, KS);
+      hipLaunchKernelGGL((partition_gqa_kernel<HL, kContiguous, false>), grid, block, lds, s, a, HG, KS);
       break;
     case kPagedAligned:
-      hipLaunchKernelGGL((partition_gqa_kernel<HL, kPagedAligned>), grid, block, lds, s, a, HG, KS);
+      hipLaunchKernelGGL((partition_gqa_kernel<HL, kPagedAligned, false>), grid, block, lds, s, a, HG, KS);
       break;
     default:
-      hipLaunchKernelGGL((partition_gqa_kernel<HL, kPagedGeneral>), grid, block, lds, s, a, HG, KS);
+      hipLaunchKernelGGL((partition_gqa_kernel<HL, kPagedGeneral, false>), grid, block, lds, s, a, HG, KS);
       break;
   }
   return hipGetLastError();

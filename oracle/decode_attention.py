@@ -254,7 +254,7 @@ def equal_share_pieces(seq_lens, workers, tile=32, min_tiles=8):
 
 
 def range_partials_fp64(q, k_cache, v_cache, seq_lens, scale, pieces, page_table=None, page_size=0,
-                        v_is_k_prefix=False, ov_depth=None):
+                        v_is_k_prefix=False, ov_depth=None, k_scale=None, v_scale=None):
     """Pass-1 partials over explicit key ranges.
 
     pieces: (b, key_start, key_end, slot) tuples as ``equal_share_pieces``
@@ -272,7 +272,7 @@ def range_partials_fp64(q, k_cache, v_cache, seq_lens, scale, pieces, page_table
     for b, lo, hi, slot in pieces:
         for kvh in range(Hkv):
             qg, K, V = _gather(q, k_cache, v_cache, b, kvh, g, hi, page_table, page_size,
-                               v_is_k_prefix, Dv)
+                               v_is_k_prefix, Dv, k_scale, v_scale)
             x = qg @ K[lo:hi].T
             mp = x.max(axis=1, keepdims=True)
             e = np.exp(scale * (x - mp))

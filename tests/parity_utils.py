@@ -17,7 +17,11 @@ LSE_RTOL = 1e-5
 
 
 def np32(t):
-    return None if t is None else t.detach().cpu().float().numpy()
+    """fp32 numpy copy of a tensor; fp8 caches (uint8 codes) stay raw codes."""
+    if t is None:
+        return None
+    t = t.detach().cpu()
+    return t.numpy() if t.dtype == torch.uint8 else t.float().numpy()
 
 
 def oracle_for(case, batch_rows=None):
@@ -27,6 +31,8 @@ def oracle_for(case, batch_rows=None):
     v = None if case.v_cache is None else np32(case.v_cache)
     lens = case.seq_lens.cpu().numpy().astype(np.int64)
     pt = None if case.page_table is None else case.page_table.cpu().numpy()
+    ks = None if case.k_scale is None else case.k_scale.cpu().numpy()
+    vs = None if case.v_scale is None else case.v_scale.cpu().numpy()
     if batch_rows is not None:
         q = q[batch_rows]
         lens = lens[batch_rows]
@@ -35,9 +41,12 @@ def oracle_for(case, batch_rows=None):
         else:
             k = k[batch_rows]
             v = None if v is None else v[batch_rows]
+            ks = None if ks is None else ks[batch_rows]
+            vs = None if vs is None else vs[batch_rows]
     lens = np.maximum(lens, 0)
     return decode_attention_fp64(q, k, v, lens, case.scale, page_table=pt, page_size=case.page_size,
-                                 v_is_k_prefix=case.v_is_k_prefix, ov_depth=case.ov_depth)
+                                 v_is_k_prefix=case.v_is_k_prefix, ov_depth=case.ov_depth, k_scale=ks,
+                                 v_scale=vs)
 
 
 def assert_parity(out, lse, o32, O, LSE, o32_row_rtol=O32_ROW_RTOL, lse_rtol=LSE_RTOL, what=""):

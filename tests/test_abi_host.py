@@ -188,3 +188,32 @@ def test_partition_and_combine_argument_checks(lib):
 def test_probe_argument_checks(lib):
     assert lib.da_read_probe(FAKE, 15, FAKE, None) == DA_EINVAL
     assert lib.da_copy_probe(FAKE, None, 16, None) == DA_EINVAL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kv_dtype=2), DA_OK),                                   # paged 64, bf16 q
+    (dict(kv_dtype=2, page_size=0, kv_capacity=4096), DA_OK),    # contiguous
+    (dict(kv_dtype=2, page_size=16, max_pages_per_seq=256), DA_EUNSUPPORTED),   # page below the tile
+    (dict(kv_dtype=2, page_size=48, max_pages_per_seq=100), DA_EUNSUPPORTED),   # not a power of two
+    (dict(kv_dtype=2, dtype=0), DA_EUNSUPPORTED),                # fp32 q
+    (dict(kv_dtype=2, kernel=1), DA_EUNSUPPORTED),               # vector-ALU kernel
+    (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1),
+     DA_EUNSUPPORTED),
+    (dict(kv_dtype=7), DA_EINVAL),
+])
+def test_fp8_cache_support(lib, kw, code):
+    assert lib.da_supported(ctypes.byref(prob(**kw))) == code
+
+
+def test_fp8_entry_points_need_their_scales(lib):
+    p8 = prob(kv_dtype=2)
+    # the plain entry point has no scale argument: an fp8 problem is refused
+    assert call_splitk(lib, p8) == DA_EINVAL
+    assert b"k_scale" in lib.da_last_error()
+    f = lib.decode_attn_splitk_fp8
+    args = (FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 0.1, 0, FAKE, None, None, FAKE, 1 << 30, None)
+    assert f(ctypes.byref(p8), *args) == DA_EINVAL                 # k_scale NULL
+    assert f(ctypes.byref(prob()), *args) == DA_EINVAL             # not an fp8 problem
+    g = lib.decode_attn_partition_fp8
+    assert g(ctypes.byref(prob()), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 0.1, 256, 16, FAKE, FAKE,
+             None) == DA_EINVAL

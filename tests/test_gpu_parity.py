@@ -305,6 +305,62 @@ def test_workload_full(name):
     check_case(workload(name), f"workload {name}")
 
 
+FP8 = [
+    ("paged64_auto_g8", dict(batch=5, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=64,
+                             len_range=(1, 5000), num_splits=0, seed=80)),
+    ("contig_splits8_g4", dict(batch=2, num_q_heads=8, num_kv_heads=2, qk_depth=128, seq_lens=[4096, 1000],
+                               num_splits=8, seed=81)),
+    ("paged32_g16_two_mfma", dict(batch=2, num_q_heads=32, num_kv_heads=2, qk_depth=128, page_size=32,
+                                  seq_lens=[777, 2048], num_splits=3, seed=82)),
+    ("no_v_scale", dict(batch=3, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=64,
+                        seq_lens=[1000, 64, 2500], num_splits=0, seed=83, v_scaled=False)),
+    ("one_kv_head_key_splits", dict(batch=4, num_q_heads=8, num_kv_heads=1, qk_depth=128, page_size=64,
+                                    seq_lens=[0, 1, 3000, 65], num_splits=3, seed=84)),
+    ("poisoned_tails", dict(batch=3, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=64,
+                            seq_lens=[100, 1, 1025], num_splits=0, seed=85, poison=True, spare_pages=3)),
+]
+
+
+@pytest.mark.parametrize("name,kw", FP8, ids=[c[0] for c in FP8])
+def test_fp8_cache_parity(name, kw):
+    # E4M3 caches with per-token scales against the oracle on the same codes and scales
+    case = make_case(name, kv_fp8=True, **kw)
+    out, lse, o32 = check_case(case, f"fp8 {name}")
+    assert torch.isfinite(o32).all()
+
+
+def test_fp8_partition_partials_match_oracle():
+    case = make_case("f8parts", batch=3, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=64,
+                     seq_lens=[1000, 64, 2500], seed=86, kv_fp8=True)
+    dc = to_device(case)
+    chunk, P = 512, 5
+    po, pml = api.partition(dc.q, dc.k_cache, dc.v_cache, dc.page_table, dc.seq_lens, case.scale, chunk, P,
+                            page_size=64, k_scale=dc.k_scale, v_scale=dc.v_scale)
+    torch.cuda.synchronize()
+    pieces = [(b, p * chunk, min((p + 1) * chunk, int(L)), b * P + p)
+              for b, L in enumerate(case.seq_lens.tolist()) for p in range(P) if p * chunk < L]
+    m, l, O = range_partials_fp64(np32(case.q), np32(case.k_cache), np32(case.v_cache), case.seq_lens.numpy(),
+                                  case.scale, pieces, page_table=case.page_table.numpy(), page_size=64,
+                                  k_scale=case.k_scale.numpy(), v_scale=case.v_scale.numpy())
+    po, pml = np32(po), np32(pml)   # [B, Hq, P, ...]
+    for b, lo, hi, sl in pieces:
+        p = sl % P
+        np.testing.assert_allclose(pml[b, :, p, 0], m[sl], rtol=1e-5, atol=1e-4)
+        np.testing.assert_allclose(pml[b, :, p, 1], l[sl], rtol=1e-5)
+        err = np.abs(po[b, :, p] - O[sl]).max(-1)
+        assert (err / np.abs(O[sl]).max(-1)).max() <= 1e-5
+
+
+def test_workload_paged_gqa_fp8_sampled():
+    case = workload("paged_gqa_fp8")
+    print("[parity] workload paged_gqa_fp8 (sampled rows)", flush=True)
+    out, lse, o32 = run(case)
+    lens = case.seq_lens.numpy()
+    rows = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 11, 31})
+    O, LSE = oracle_for(case, batch_rows=rows)
+    assert_parity(out[rows], lse[rows], o32[rows], O, LSE, what="paged_gqa_fp8 sampled")
+
+
 def test_workload_paged_gqa_sampled():
     case = workload("paged_gqa")
     print("[parity] workload paged_gqa (sampled rows)", flush=True)
