@@ -46,7 +46,11 @@ class Case:
 
     @property
     def num_q_heads(self):
-        return self.q.shape[1]
+        return self.q.shape[-2]
+
+    @property
+    def q_len(self):
+        return self.q.shape[1] if self.q.dim() == 4 else 1
 
     @property
     def num_kv_heads(self):
@@ -54,7 +58,7 @@ class Case:
 
     @property
     def qk_depth(self):
-        return self.q.shape[2]
+        return self.q.shape[-1]
 
     @property
     def kv_fp8(self):
@@ -81,7 +85,7 @@ class Case:
 
     def flops(self) -> int:
         tokens = int(self.seq_lens.clamp(min=0).sum())
-        return 2 * self.num_q_heads * tokens * (self.qk_depth + self.ov_depth)
+        return 2 * self.q_len * self.num_q_heads * tokens * (self.qk_depth + self.ov_depth)
 
 
 def _randn(gen, shape, dtype):
@@ -92,7 +96,8 @@ def _randn(gen, shape, dtype):
 def make_case(name="case", *, batch, num_q_heads, num_kv_heads, qk_depth, ov_depth=None,
               dtype=torch.bfloat16, page_size=0, seq_lens=None, len_range=None, kv_capacity=None,
               num_splits=0, seed=0, v_is_k_prefix=False, scale=None, poison=False,
-              spare_pages=0, q_scale=1.0, page_table_width=None, kv_fp8=False, v_scaled=True) -> Case:
+              spare_pages=0, q_scale=1.0, page_table_width=None, kv_fp8=False, v_scaled=True,
+              q_len=1) -> Case:
     """Build a seeded case.
 
     Exactly one of ``seq_lens`` (a list of lengths) or ``len_range``
@@ -102,6 +107,7 @@ def make_case(name="case", *, batch, num_q_heads, num_kv_heads, qk_depth, ov_dep
     cache slot that no sequence attends (tail of last pages, spare pages,
     contiguous slots past L_b) with NaN so that a kernel reading them shows up.
     ``q_scale`` multiplies q after the draw (large-logit tests).
+    ``q_len`` > 1: q is [B, q_len, Hq, Dqk], the sequences' last q_len positions.
     ``kv_fp8``: K and V are drawn as above (fp32) and stored as E4M3 codes with a
     per-(token, kv head) scale amax / 448 (``v_scaled=False``: V codes of the unscaled
     values, no V scale); q stays in ``dtype``.
@@ -135,7 +141,8 @@ def make_case(name="case", *, batch, num_q_heads, num_kv_heads, qk_depth, ov_dep
         cap = kv_capacity or max(1, int(pos_lens.max()) if batch else 1)
         kv_shape_k = (batch, cap, num_kv_heads, qk_depth)
         kv_shape_v = (batch, cap, num_kv_heads, ov_depth)
-    q = _randn(gen, (batch, num_q_heads, qk_depth), dtype)
+    q_shape = (batch, num_q_heads, qk_depth) if q_len == 1 else (batch, q_len, num_q_heads, qk_depth)
+    q = _randn(gen, q_shape, dtype)
     if q_scale != 1.0:
         q = (q.float() * q_scale).to(dtype)
     kv_dtype = torch.float32 if kv_fp8 else dtype
@@ -207,6 +214,11 @@ WORKLOADS = {
     "latent": dict(seed=5, batch=16, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512,
                    dtype=torch.bfloat16, page_size=64, seq_lens=[8192] * 16, num_splits=8,
                    v_is_k_prefix=True),
+    # the paged GQA workload with two queries per sequence (e.g. one speculative token):
+    # 2 x 8 (query, head) columns per kv head
+    "paged_gqa_q2": dict(seed=3, batch=32, num_q_heads=64, num_kv_heads=8, qk_depth=128,
+                         dtype=torch.bfloat16, page_size=64, len_range=(512, 32768),
+                         num_splits=0, page_table_width=512, q_len=2),
     # the paged GQA workload with an fp8 (E4M3) K/V cache and per-token K and V scales
     # (same lengths, pages and draws; bf16 q)
     "paged_gqa_fp8": dict(seed=3, batch=32, num_q_heads=64, num_kv_heads=8, qk_depth=128,

@@ -151,7 +151,20 @@ def decode_attention_fp64(q, k_cache, v_cache, seq_lens, scale, page_table=None,
     (``k_scale`` / ``v_scale``, layout in ``_scale_rows``; a missing scale is 1).
     Returns (O [B, Hq, Dv] fp64, LSE [B, Hq] fp64, natural log).
     A sequence of length 0 gives O = 0 and LSE = -inf.
+
+    Several queries per sequence: q [B, q_len, Hq, Dqk] holds the sequence's last q_len
+    positions, and query i attends the keys up to its own position, t < L_b - q_len + 1 + i
+    (the pages fix no mask for this case; this is the causal reading among the new
+    tokens). Returns O [B, q_len, Hq, Dv] and LSE [B, q_len, Hq].
     """
+    q_arr = np.asarray(q)
+    if q_arr.ndim == 4:
+        ql = q_arr.shape[1]
+        lens = np.asarray(seq_lens, dtype=np.int64)
+        outs = [decode_attention_fp64(q_arr[:, i], k_cache, v_cache, np.clip(lens - ql + 1 + i, 0, lens), scale,
+                                      page_table, page_size, v_is_k_prefix, ov_depth, k_scale, v_scale)
+                for i in range(ql)]
+        return np.stack([o for o, _ in outs], 1), np.stack([l for _, l in outs], 1)
     B, Hq, Hkv, g, Dqk, Dv = _dims(q, k_cache, v_cache, v_is_k_prefix, ov_depth)
     O = np.zeros((B, Hq, Dv), dtype=np.float64)
     LSE = np.full((B, Hq), -np.inf, dtype=np.float64)

@@ -465,3 +465,34 @@ def test_fp8_scales_act_as_closed_forms():
     O3, L3 = decode_attention_fp64(*args, c.scale, k_scale=ks, v_scale=3 * vs.astype(np.float64), **base)
     np.testing.assert_allclose(O3, 3 * O, atol=1e-14)
     np.testing.assert_allclose(L3, LSE, rtol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# several queries per sequence (causal among the last q_len positions)
+# ---------------------------------------------------------------------------
+def brute_multiquery(q4, k, v, lens, scale, pt=None, ps=0):
+    # each query i of q_len, at position L - q_len + i, over the keys up to that position
+    B, ql = q4.shape[:2]
+    Os, Ls = [], []
+    for i in range(ql):
+        li = [max(0, min(int(L), int(L) - ql + 1 + i)) for L in lens]
+        o, l = brute(q4[:, i], k, v, li, scale, pt, ps)
+        Os.append(o)
+        Ls.append(l)
+    return np.stack(Os, 1), np.stack(Ls, 1)
+
+
+@pytest.mark.parametrize("paged", [0, 4])
+def test_multiquery_brute_force(paged):
+    q, k, v, lens, pt = rng_case(90 + paged, B=3, Hq=4, Hkv=2, D=8, L=(7, 2, 5), paged=paged)
+    r = np.random.default_rng(91)
+    q4 = r.standard_normal((3, 3, 4, 8))          # q_len 3 (one sequence shorter than q_len)
+    O, LSE = decode_attention_fp64(q4, k, v, lens, 0.6, page_table=pt, page_size=paged)
+    Ob, Lb = brute_multiquery(q4, k, v, lens, 0.6, pt, paged)
+    np.testing.assert_allclose(O, Ob, atol=1e-13)
+    np.testing.assert_allclose(LSE, Lb, rtol=1e-13)
+    # the last query sees the whole sequence: it is the single-query result
+    O1, L1 = decode_attention_fp64(q4[:, -1], k, v, lens, 0.6, page_table=pt, page_size=paged)
+    np.testing.assert_allclose(O[:, -1], O1, atol=0)
+    # a sequence of 2 keys with q_len 3: query 0 sees nothing (O = 0, LSE = -inf)
+    assert np.all(O[1, 0] == 0) and np.all(np.isneginf(LSE[1, 0]))
