@@ -89,10 +89,12 @@ def main():
                             v_is_k_prefix=case.v_is_k_prefix, ov_depth=case.ov_depth, kernel=args.kernel)
     chunk, max_splits = api.choose_splits(prob, case.num_splits)
     B, Hq, Dv = prob.batch, prob.num_q_heads, prob.ov_depth
-    out = torch.empty((B, Hq, Dv), dtype=torch.bfloat16, device=dev)
+    rows = api.row_shape(prob)   # (B, Hq), or (B, q_len, Hq) with several queries per sequence
+    out = torch.empty(rows + (Dv,), dtype=torch.bfloat16, device=dev)
     part_o, part_ml = api.alloc_partials(prob, chunk, max_splits, dev)
-    comb = (torch.empty_like(out), torch.empty((B, Hq), dtype=torch.float32, device=dev),
-            torch.empty((B, Hq, Dv), dtype=torch.float32, device=dev))
+    comb = (torch.empty_like(out), torch.empty(rows, dtype=torch.float32, device=dev),
+            torch.empty(rows + (Dv,), dtype=torch.float32, device=dev))
+    api.check_outputs(prob, *comb)
 
     plan = api.DecodePlan(dc.q, dc.k_cache, dc.v_cache, dc.page_table, dc.seq_lens, case.scale, case.num_splits,
                           page_size=case.page_size, v_is_k_prefix=case.v_is_k_prefix, ov_depth=case.ov_depth,
@@ -198,7 +200,7 @@ def main():
         "data": "synthetic (seeded torch.randn" + (", E4M3 K/V with per-token scales)" if case.kv_fp8 else ")"),
         "config": {
             "workload": case.name,
-            "batch": B, "q_heads": Hq, "kv_heads": prob.num_kv_heads,
+            "batch": B, "q_len": max(1, prob.q_len), "q_heads": Hq, "kv_heads": prob.num_kv_heads,
             "qk_depth": prob.qk_depth, "ov_depth": Dv, "page_size": case.page_size,
             "keys": tokens, "max_seq_len": int(case.seq_lens.max()),
             "chunk_tokens": chunk, "max_splits": max_splits, "kernel": args.kernel, "combine": args.combine,

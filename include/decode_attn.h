@@ -77,10 +77,15 @@ typedef struct da_problem {
   int32_t kernel;            /* da_kernel: AUTO, or force a partition-kernel family */
   int32_t kv_dtype;          /* 0: K and V have `dtype`; DA_FP8_E4M3: fp8 K / V caches (bf16 q),
                                 run through the *_fp8 entry points that take the scales */
+  int32_t q_len;             /* queries per sequence (0 or 1: one, plain decode; > 1: the
+                                sequence's last q_len positions, e.g. speculative tokens) */
 } da_problem;
 
 /*
- * Layouts (row-major, dense):
+ * Layouts (row-major, dense). With q_len > 1 every [B][Hq] below reads [B][q_len][Hq]
+ * (q, out, lse_out, o_f32_out) and the partials have q_len * Hq rows per sequence; query i
+ * (0-based) stands at position L_b - q_len + i of its sequence and attends the keys up to
+ * and including that position (keys t < L_b - q_len + 1 + i: causal among the new tokens).
  *   q          [B][Hq][Dqk]                        dtype
  *   k_cache    contiguous: [B][kv_capacity][Hkv][Dqk]; paged: [num_pages][page_size][Hkv][Dqk]
  *   v_cache    same as k_cache with Dv (ignored when v_is_k_prefix)

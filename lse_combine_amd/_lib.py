@@ -19,7 +19,7 @@ DA_KERNEL_AUTO, DA_KERNEL_FMA, DA_KERNEL_MFMA = 0, 1, 2
 class DaProblem(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "batch", "num_q_heads", "num_kv_heads", "qk_depth", "ov_depth", "dtype", "page_size",
-        "max_pages_per_seq", "num_pages", "kv_capacity", "max_seq_len", "v_is_k_prefix", "kernel", "kv_dtype")]
+        "max_pages_per_seq", "num_pages", "kv_capacity", "max_seq_len", "v_is_k_prefix", "kernel", "kv_dtype", "q_len")]
 
 
 class DaError(RuntimeError):

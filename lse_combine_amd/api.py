@@ -28,9 +28,15 @@ def _stream():
 
 def make_problem(q, k_cache, v_cache=None, page_table=None, *, page_size=0, max_seq_len=None,
                  v_is_k_prefix=False, ov_depth=None, kernel="auto", num_pages=None) -> DaProblem:
-    """Describe one decode step from its tensors (shapes as in include/decode_attn.h)."""
-    if q.dim() != 3 or k_cache.dim() != 4:
-        raise ValueError("q must be [B, Hq, Dqk] and k_cache 4-D")
+    """Describe one decode step from its tensors (shapes as in include/decode_attn.h).
+
+    q is [B, Hq, Dqk], or [B, q_len, Hq, Dqk] for several queries per sequence.
+    """
+    if q.dim() not in (3, 4) or k_cache.dim() != 4:
+        raise ValueError("q must be [B, Hq, Dqk] or [B, q_len, Hq, Dqk] and k_cache 4-D")
+    q_len = q.shape[1] if q.dim() == 4 else 1
+    if q.dim() == 4:
+        q = q[:, 0]
     fp8 = k_cache.dtype == torch.uint8   # E4M3 codes
     if q.dtype not in _DTYPES:
         raise ValueError("q must be float32 or bfloat16")
@@ -54,6 +60,7 @@ def make_problem(q, k_cache, v_cache=None, page_table=None, *, page_size=0, max_
     p.batch, p.num_q_heads, p.num_kv_heads, p.qk_depth, p.ov_depth = B, Hq, Hkv, Dqk, Dv
     p.dtype = _DTYPES[q.dtype]
     p.kv_dtype = _lib.DA_FP8_E4M3 if fp8 else 0
+    p.q_len = q_len
     p.kernel = _KERNELS[kernel]
     p.v_is_k_prefix = 1 if v_is_k_prefix else 0
     if page_table is not None:
@@ -71,6 +78,31 @@ def make_problem(q, k_cache, v_cache=None, page_table=None, *, page_size=0, max_
         cap = k_cache.shape[1]
     p.max_seq_len = cap if max_seq_len is None else int(max_seq_len)
     return p
+
+
+def row_shape(problem: DaProblem):
+    """Leading shape of out / lse: (B, Hq), or (B, q_len, Hq) with several queries."""
+    if problem.q_len > 1:
+        return (problem.batch, problem.q_len, problem.num_q_heads)
+    return (problem.batch, problem.num_q_heads)
+
+
+def check_outputs(problem: DaProblem, out=None, lse=None, o32=None):
+    """Refuse output buffers that do not hold every (query, head) row: the library writes
+    through raw pointers and cannot see their sizes."""
+    rows = row_shape(problem)
+    n = 1
+    for d in rows:
+        n *= d
+    for t, per_row, dtype, name in ((out, problem.ov_depth, torch.bfloat16, "out"), (lse, 1, torch.float32, "lse"),
+                                    (o32, problem.ov_depth, torch.float32, "o32")):
+        if t is None:
+            continue
+        if t.dtype != dtype or t.numel() != n * per_row or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape "
+                             f"{rows + ((per_row,) if per_row > 1 else ())}")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on the GPU")
 
 
 def _check_tensors(*ts):
@@ -106,13 +138,15 @@ def decode_attn(q, k_cache, v_cache, page_table, seq_lens, scale, num_splits=0, 
     prob = make_problem(q, k_cache, v_cache, page_table, page_size=page_size, max_seq_len=max_seq_len,
                         v_is_k_prefix=v_is_k_prefix, ov_depth=ov_depth, kernel=kernel)
     _check_tensors(q, k_cache, v_cache, page_table, seq_lens)
-    B, Hq, Dv = prob.batch, prob.num_q_heads, prob.ov_depth
+    rows = row_shape(prob)
+    Dv = prob.ov_depth
     if out is None:
-        out = torch.empty((B, Hq, Dv), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty(rows + (Dv,), dtype=torch.bfloat16, device=q.device)
     if return_lse and lse is None:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        lse = torch.empty(rows, dtype=torch.float32, device=q.device)
     if return_o32 and o32 is None:
-        o32 = torch.empty((B, Hq, Dv), dtype=torch.float32, device=q.device)
+        o32 = torch.empty(rows + (Dv,), dtype=torch.float32, device=q.device)
+    check_outputs(prob, out, lse, o32)
     need = workspace_bytes(prob, num_splits)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
@@ -140,7 +174,8 @@ def alloc_partials(problem: DaProblem, chunk_tokens, max_splits, device):
     fp32 buffer of slots * Hq (m, l) pairs followed by the int32 (first slot, count)
     pair of each sequence (see ``slot_table``).
     """
-    B, Hq, Dv = problem.batch, problem.num_q_heads, problem.ov_depth
+    B, Dv = problem.batch, problem.ov_depth
+    Hq = problem.num_q_heads * max(1, problem.q_len)   # rows per sequence
     f32 = dict(dtype=torch.float32, device=device)
     if chunk_tokens == 0:
         slots = max_splits + B
@@ -150,7 +185,7 @@ def alloc_partials(problem: DaProblem, chunk_tokens, max_splits, device):
 
 def slot_table(problem: DaProblem, max_splits, part_ml):
     """Equal-share schedule: split part_ml into (ml [slots, Hq, 2] fp32, table [B, 2] int32)."""
-    B, Hq = problem.batch, problem.num_q_heads
+    B, Hq = problem.batch, problem.num_q_heads * max(1, problem.q_len)
     slots = max_splits + B
     ml = part_ml[:slots * Hq * 2].view(slots, Hq, 2)
     table = part_ml[slots * Hq * 2:slots * Hq * 2 + 2 * B].view(torch.int32).view(B, 2)
@@ -186,11 +221,12 @@ def combine(problem: DaProblem, seq_lens, scale, chunk_tokens, max_splits, part_
     """Pass 2 only (the LSE combine). Returns (out bf16, lse fp32, o32 fp32)."""
     lib = _lib.load()
     _check_tensors(seq_lens, part_o, part_ml)
-    B, Hq, Dv = problem.batch, problem.num_q_heads, problem.ov_depth
+    rows, Dv = row_shape(problem), problem.ov_depth
     dev = part_o.device
-    out = torch.empty((B, Hq, Dv), dtype=torch.bfloat16, device=dev) if out is None else out
-    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if lse is None else lse
-    o32 = torch.empty((B, Hq, Dv), dtype=torch.float32, device=dev) if o32 is None else o32
+    out = torch.empty(rows + (Dv,), dtype=torch.bfloat16, device=dev) if out is None else out
+    lse = torch.empty(rows, dtype=torch.float32, device=dev) if lse is None else lse
+    o32 = torch.empty(rows + (Dv,), dtype=torch.float32, device=dev) if o32 is None else o32
+    check_outputs(problem, out, lse, o32)
     check(lib.decode_attn_combine(ctypes.byref(problem), _ptr(seq_lens), float(scale), int(chunk_tokens),
                                   int(max_splits), _ptr(part_o), _ptr(part_ml), _ptr(out), _ptr(lse), _ptr(o32),
                                   _stream()))
@@ -219,8 +255,9 @@ class DecodePlan:
         self.prob = make_problem(q, k_cache, v_cache, page_table, page_size=page_size, max_seq_len=max_seq_len,
                                  v_is_k_prefix=v_is_k_prefix, ov_depth=ov_depth, kernel=kernel)
         _check_tensors(q, k_cache, v_cache, page_table, seq_lens)
-        B, Hq, Dv = self.prob.batch, self.prob.num_q_heads, self.prob.ov_depth
-        self.out = torch.empty((B, Hq, Dv), dtype=torch.bfloat16, device=q.device) if out is None else out
+        self.out = (torch.empty(row_shape(self.prob) + (self.prob.ov_depth,), dtype=torch.bfloat16, device=q.device)
+                    if out is None else out)
+        check_outputs(self.prob, self.out, lse, o32)
         self.lse, self.o32 = lse, o32
         need = workspace_bytes(self.prob, num_splits)
         # zero-filled once: the fused step keeps its arrival counters here

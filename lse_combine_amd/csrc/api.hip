@@ -34,6 +34,11 @@ constexpr int kTileKeys = 32;  // key tile of every partition kernel; chunks are
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+int q_len_of(const da_problem* p) { return p->q_len <= 0 ? 1 : p->q_len; }
+
+// Output / partial rows per sequence: one per (query, head).
+int64_t rows_per_seq(const da_problem* p) { return (int64_t)q_len_of(p) * p->num_q_heads; }
+
 int device_num_cus() {
   static std::mutex mu;
   static int cache[64] = {0};
@@ -72,6 +77,18 @@ int check_problem(const da_problem* p, Variant* var) {
     return fail(DA_EINVAL, "latent-shared V (ov_depth %d) must fit in the K row (qk_depth %d)", p->ov_depth, p->qk_depth);
   if (p->kernel < DA_KERNEL_AUTO || p->kernel > DA_KERNEL_MFMA) return fail(DA_EINVAL, "unknown kernel hint %d", p->kernel);
   const int g = p->num_q_heads / p->num_kv_heads;
+  const int ql = q_len_of(p);
+  if (ql < 1 || ql > 16) return fail(DA_EINVAL, "q_len must be in [0, 16] (got %d)", p->q_len);
+  if (ql > 1) {
+    // several queries per sequence: the matrix-core depth-128 kernel packs q_len x group
+    // (query, head) columns into its 16 MFMA columns
+    if ((p->dtype != DA_BF16 && p->kv_dtype != DA_FP8_E4M3) || p->qk_depth != 128 || p->ov_depth != 128 ||
+        p->v_is_k_prefix || ql * g > 16 || p->kernel == DA_KERNEL_FMA ||
+        (p->page_size > 0 && (p->page_size < kTileKeys || (p->page_size & (p->page_size - 1)))))
+      return fail(DA_EUNSUPPORTED,
+                  "q_len > 1 is supported on the bf16 (or fp8-cache) depth-128 matrix-core kernel with q_len x group "
+                  "<= 16 and a contiguous cache or pages of a power of two >= 32 keys");
+  }
   if (p->kv_dtype != 0) {
     if (p->kv_dtype != DA_FP8_E4M3) return fail(DA_EINVAL, "kv_dtype must be 0 or DA_FP8_E4M3 (got %d)", p->kv_dtype);
     if (p->dtype != DA_BF16 || p->qk_depth != 128 || p->ov_depth != 128 || p->v_is_k_prefix || g > 16 ||
@@ -98,7 +115,7 @@ int check_problem(const da_problem* p, Variant* var) {
   if (p->dtype == DA_F32) {
     if (p->kernel == DA_KERNEL_MFMA) return fail(DA_EUNSUPPORTED, "the matrix-core kernel needs bf16 inputs");
     *var = kVarFma;
-  } else if (p->kernel == DA_KERNEL_FMA || (p->kernel == DA_KERNEL_AUTO && g == 1)) {
+  } else if (p->kernel == DA_KERNEL_FMA || (p->kernel == DA_KERNEL_AUTO && g == 1 && ql == 1)) {
     *var = kVarFma;
   } else {
     *var = kVarMfma128;
@@ -194,11 +211,11 @@ int choose(const da_problem* p, Variant var, int32_t num_splits, int cus, int32_
   return DA_OK;
 }
 
-// Partial rows of a schedule: fixed chunks B * Hq * max_splits; equal shares
-// (chunk == 0) (max_splits + B) slots of Hq rows each.
+// Partial rows of a schedule (R = q_len x Hq rows per sequence): fixed chunks
+// B * R * max_splits; equal shares (chunk == 0) (max_splits + B) slots of R rows each.
 size_t partial_rows(const da_problem* p, int32_t chunk, int32_t max_splits) {
-  if (chunk == 0) return ((size_t)max_splits + (size_t)p->batch) * (size_t)p->num_q_heads;
-  return (size_t)p->batch * p->num_q_heads * (size_t)max_splits;
+  if (chunk == 0) return ((size_t)max_splits + (size_t)p->batch) * (size_t)rows_per_seq(p);
+  return (size_t)p->batch * (size_t)rows_per_seq(p) * (size_t)max_splits;
 }
 
 // Workspace: part_ml (fp32 pairs; with equal shares followed by the int32 (first slot,
@@ -287,7 +304,7 @@ int launch_combine(const da_problem* p, const int32_t* lens, float scale, int32_
   c.lse = lse;
   c.o32 = o32;
   c.B = p->batch;
-  c.Hq = p->num_q_heads;
+  c.Hq = (int32_t)rows_per_seq(p);
   c.Dv = p->ov_depth;
   c.chunk = chunk;
   c.max_splits = max_splits;
@@ -384,7 +401,9 @@ PartArgs build_part_args(const da_problem* p, const void* q, const void* k, cons
   a.page_table = pt;
   a.seq_lens = lens;
   a.B = p->batch;
-  a.Hq = p->num_q_heads;
+  a.Hq = (int32_t)rows_per_seq(p);
+  a.Hq1 = p->num_q_heads;
+  a.q_len = q_len_of(p);
   a.Hkv = p->num_kv_heads;
   a.g = p->num_q_heads / p->num_kv_heads;
   a.Dqk = p->qk_depth;

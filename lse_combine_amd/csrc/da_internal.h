@@ -16,7 +16,7 @@ enum PageMode : int {
 
 // Everything the partition kernels need; passed by value as the kernel argument.
 struct PartArgs {
-  const void* q;            // [B][Hq][Dqk]
+  const void* q;            // [B][q_len][heads][Dqk] = [B][Hq][Dqk]
   const void* k;            // cache rows of Dqk elements, see key_row()
   const void* v;            // cache rows of v_row_len elements (== k when V is a K prefix)
   const int32_t* page_table;
@@ -32,7 +32,8 @@ struct PartArgs {
   uint16_t* out;            // bf16 [B][Hq][Dv]; written directly by single-partition rows
   float* lse;               // optional
   float* o32;               // optional
-  int32_t B, Hq, Hkv, g, Dqk, Dv;
+  int32_t B, Hq, Hkv, g, Dqk, Dv;   // Hq: rows per sequence (q_len x heads)
+  int32_t Hq1, q_len;               // heads; queries per sequence (>= 1)
   int32_t v_row_len;        // elements between consecutive (row, kv-head) V vectors / Hkv
   int32_t page_size, pt_stride, num_pages, kv_capacity, max_seq_len;
   int32_t page_shift;       // log2(page_size) when it is a power of two, else -1

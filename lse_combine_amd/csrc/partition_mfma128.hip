@@ -118,6 +118,7 @@ __device__ __forceinline__ void zero_v_tile(char* vt, int lane) {
 // lane's MFMA coordinates.
 struct WaveInfo {
   int HG, KS, NW, w, ks, kvh, lane, n, qd, hc;
+  int qi, hh;   // the (query, head-in-group) pair of this lane's MFMA column
   bool wave_active, col_valid, is_lo;
 };
 
@@ -145,25 +146,32 @@ __device__ __forceinline__ void merge_key_splits(const PartArgs& a, const WaveIn
   }
   __syncthreads();
   constexpr int kUnits = kD / 4;
-  const int units = HG * g * kUnits;
+  const int cols = a.q_len * g;   // (query, head) columns per kv head
+  const int units = HG * cols * kUnits;
   for (int u = tid; u < units; u += NW * 64) {
-    const int mem = u / (g * kUnits);
-    const int h = (u / kUnits) % g, d0 = (u % kUnits) * 4;
+    const int mem = u / (cols * kUnits);
+    const int h = (u / kUnits) % cols, d0 = (u % kUnits) * 4;
     const int kv2 = kg * HG + mem;
     if (kv2 >= a.Hkv) continue;
+    // (a split that saw no key of this column holds l = 0 and weighs nothing)
     float M = -INFINITY;
-    for (int s2 = 0; s2 < KS; ++s2)
-      M = fmaxf(M, ((const float*)(smem + (s2 * HG + mem) * kWaveBytes + kVBytes))[h]);
+    for (int s2 = 0; s2 < KS; ++s2) {
+      const float* ml = (const float*)(smem + (s2 * HG + mem) * kWaveBytes + kVBytes);
+      if (ml[16 + h] > 0.f) M = fmaxf(M, ml[h]);
+    }
     float Ls = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int s2 = 0; s2 < KS; ++s2) {
       const char* reg = smem + (s2 * HG + mem) * kWaveBytes;
       const float* ml = (const float*)(reg + kVBytes);
-      const float e = exp2_fast((ml[h] - M) * c);
-      Ls = fmaf(ml[16 + h], e, Ls);
-      acc += e * *(const f32x4*)((const float*)reg + h * kD + d0);
+      if (ml[16 + h] > 0.f) {
+        const float e = exp2_fast((ml[h] - M) * c);
+        Ls = fmaf(ml[16 + h], e, Ls);
+        acc += e * *(const f32x4*)((const float*)reg + h * kD + d0);
+      }
     }
-    store_unit(a, b, kv2 * g + h, p, direct, d0, acc * (1.f / Ls), M, Ls, d0 == 0);
+    const int row = (h / g) * a.Hq1 + kv2 * g + h % g;
+    store_unit(a, b, row, p, direct, d0, acc * (Ls > 0.f ? 1.f / Ls : 0.f), M, Ls, d0 == 0);
   }
   // the merge read other waves' V tiles: the next piece may refill them only after this
   __syncthreads();
@@ -193,10 +201,12 @@ __device__ __forceinline__ void fused_combine(const PartArgs& a, const WaveInfo&
   __syncthreads();
   if (!__builtin_amdgcn_readfirstlane(*flag_s)) return;
   const int kv_end = min((kg + 1) * HG, a.Hkv);
-  const int h0 = kg * HG * g, nh = (kv_end - kg * HG) * g;
+  const int cols = a.q_len * g, ncol = (kv_end - kg * HG) * cols;
   constexpr int kUnits = kD / 4;
-  for (int u = tid; u < nh * kUnits; u += wv.NW * 64) {
-    const int h = h0 + u / kUnits, d0 = (u % kUnits) * 4;
+  for (int u = tid; u < ncol * kUnits; u += wv.NW * 64) {
+    const int cc = u / kUnits, d0 = (u % kUnits) * 4;
+    const int kv = kg * HG + cc / cols, col = cc % cols;
+    const int h = (col / g) * a.Hq1 + kv * g + col % g;   // row within the sequence
     const int64_t row = (int64_t)b * a.Hq + h;
     // partial rows of this head: equal shares [slot][Hq], fixed chunks [B][Hq][max_splits]
     const int64_t first = first_slot >= 0 ? (int64_t)first_slot * a.Hq + h : row * a.max_splits;
@@ -225,6 +235,9 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
   const float lo_mask = is_lo ? 1.f : 0.f;
   char* vt = smem + wv.w * kWaveBytes;
   int first_page = 0;   // page index held by pages_s[0] in the current segment
+  // keys this lane's column attends: query qi of q_len sees keys t < L - q_len + 1 + qi
+  const int L_seq = __builtin_amdgcn_readfirstlane(attended_len(a, b, PM == kContiguous));
+  const int col_end = min(end, L_seq - a.q_len + 1 + wv.qi);
 
   // q as the B operand of S^T = K q^T: column n; MFMA step j covers depth 32j + 8qd .. +8
   // (bf16 caches) or, matching the 16-value fp8 loads of K, depth 16(qd + 4(j/2)) + 8(j%2) .. +8
@@ -233,7 +246,7 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
   {
     const int kv_safe = wave_active ? kvh : 0;
     const uint16_t* qrow = (const uint16_t*)a.q +
-                           ((int64_t)b * a.Hq + (int64_t)kv_safe * g + (col_valid ? hc : 0)) * kD;
+                           ((int64_t)b * a.Hq + (int64_t)wv.qi * a.Hq1 + (int64_t)kv_safe * g + wv.hh) * kD;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int d0 = F8 ? 16 * (qd + 4 * (j >> 1)) + 8 * (j & 1) : 32 * j + 8 * qd;
@@ -425,8 +438,8 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
       s[0] *= ksc[0];
       s[1] *= ksc[1];
     }
-    const int nvalid = end - t0;
-    if (nvalid < kTile) {
+    const int nvalid = col_end - t0;   // this column's keys in the tile (may be <= 0)
+    if (__ballot(nvalid < kTile)) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
@@ -438,8 +451,10 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
                      fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
     mx = max_over_key_groups(mx);
     const float mn = fmaxf(m_run, mx);
-    const float alpha = exp2_fast((m_run - mn) * c);
-    const float mc = mn * c;
+    // (a column that has seen no key yet keeps m = -inf; its p and l stay 0)
+    const float mref = mn == -INFINITY ? 0.f : mn;
+    const float alpha = exp2_fast((m_run - mref) * c);
+    const float mc = mref * c;
     float pr[2][4];
     float psum = 0.f;
 #pragma unroll
@@ -584,11 +599,11 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
   if (KS == 1) {
     // one wave per kv head: store straight from registers
     if (wave_active && col_valid && !is_lo) {
-      const float inv = 1.f / l_run;
+      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+      const int row = wv.qi * a.Hq1 + kvh * g + wv.hh;
 #pragma unroll
       for (int db = 0; db < 8; ++db)
-        store_unit(a, b, kvh * g + hc, p, direct, 16 * db + 4 * qd, o[db] * inv, m_run, l_run,
-                   db == 0 && qd == 0);
+        store_unit(a, b, row, p, direct, 16 * db + 4 * qd, o[db] * inv, m_run, l_run, db == 0 && qd == 0);
     }
   } else {
     merge_key_splits<HL>(a, wv, smem, b, p, direct, o, m_run, l_run);
@@ -630,8 +645,10 @@ void partition_gqa_kernel(PartArgs a, int HG, int KS) {
   wv.lane = threadIdx.x & 63;
   wv.n = wv.lane & 15;
   wv.qd = wv.lane >> 4;
-  wv.hc = HL ? (wv.n & 7) : wv.n;          // head index of this lane's MFMA column
-  wv.col_valid = wv.hc < a.g;
+  wv.hc = HL ? (wv.n & 7) : wv.n;          // (query, head) column of this lane
+  wv.col_valid = wv.hc < a.q_len * a.g;
+  wv.qi = wv.col_valid ? wv.hc / a.g : 0;
+  wv.hh = wv.col_valid ? wv.hc % a.g : 0;
   wv.is_lo = HL && wv.n >= 8;
   const int lane = wv.lane;
 
@@ -805,7 +822,7 @@ hipError_t launch_hl(const PartArgs& a, int pm, int HG, int KS, hipStream_t s) {
 // HG kv heads per workgroup, KS key splits per kv head (HG * KS <= 16).
 hipError_t launch_partition_mfma128(const PartArgs& a, int page_mode, int HG, int KS, hipStream_t s) {
   if (HG < 1 || KS < 1 || HG * KS > kMaxWaves) return hipErrorInvalidValue;
-  return a.g <= 8 ? launch_hl<true>(a, page_mode, HG, KS, s) : launch_hl<false>(a, page_mode, HG, KS, s);
+  return a.q_len * a.g <= 8 ? launch_hl<true>(a, page_mode, HG, KS, s) : launch_hl<false>(a, page_mode, HG, KS, s);
 }
 
 }  // namespace da

@@ -217,3 +217,50 @@ def test_fp8_entry_points_need_their_scales(lib):
     g = lib.decode_attn_partition_fp8
     assert g(ctypes.byref(prob()), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 0.1, 256, 16, FAKE, FAKE,
              None) == DA_EINVAL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q_len=2), DA_OK),                                        # 2 x 8 columns
+    (dict(q_len=2, page_size=0, kv_capacity=4096), DA_OK),
+    (dict(q_len=3, num_q_heads=16, num_kv_heads=2), DA_EUNSUPPORTED),   # 24 columns
+    (dict(q_len=2, dtype=0), DA_EUNSUPPORTED),                     # vector-ALU kernel
+    (dict(q_len=2, page_size=16, max_pages_per_seq=256), DA_EUNSUPPORTED),
+    (dict(q_len=2, kv_dtype=2), DA_OK),
+    (dict(q_len=17), DA_EINVAL),
+    (dict(q_len=2, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1), DA_EUNSUPPORTED),
+])
+def test_multiquery_support(lib, kw, code):
+    assert lib.da_supported(ctypes.byref(prob(**kw))) == code
+
+
+def test_multiquery_workspace_rows(lib):
+    p1, p2 = prob(batch=3, num_q_heads=8, num_kv_heads=1, max_seq_len=1000, max_pages_per_seq=16), \
+        prob(batch=3, num_q_heads=8, num_kv_heads=1, max_seq_len=1000, max_pages_per_seq=16, q_len=2)
+    n1, n2 = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.da_workspace_bytes(ctypes.byref(p1), 4, ctypes.byref(n1)) == DA_OK
+    assert lib.da_workspace_bytes(ctypes.byref(p2), 4, ctypes.byref(n2)) == DA_OK
+    C, P = splits(lib, p1, 4)
+    align = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    rows = 3 * 8 * 2 * P   # (query, head) rows
+    assert n2.value == align(rows * 2 * 4) + align(rows * 128 * 4) + align(3 * 1 * 4)
+
+
+def test_binding_refuses_output_buffers_without_every_row():
+    """The library writes B * q_len * Hq rows through raw pointers; the binding checks
+    the caller's buffers hold them all before anything is launched."""
+    import torch
+    from lse_combine_amd import api
+    p1 = prob(batch=3, num_q_heads=8, num_kv_heads=1, max_seq_len=1000, max_pages_per_seq=16)
+    p2 = prob(batch=3, num_q_heads=8, num_kv_heads=1, max_seq_len=1000, max_pages_per_seq=16, q_len=2)
+    assert api.row_shape(p1) == (3, 8) and api.row_shape(p2) == (3, 2, 8)
+    too_small = torch.empty((3, 8, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="shape"):
+        api.check_outputs(p2, out=too_small)
+    with pytest.raises(ValueError, match="shape"):
+        api.check_outputs(p2, lse=torch.empty((3, 8), dtype=torch.float32))
+    with pytest.raises(ValueError, match="shape"):
+        api.check_outputs(p1, o32=torch.empty((3, 8, 128), dtype=torch.bfloat16))
+    # right size and type: only the device is left to object on a CPU-only host
+    with pytest.raises(ValueError, match="GPU"):
+        api.check_outputs(p2, out=torch.empty((3, 2, 8, 128), dtype=torch.bfloat16))
+    api.check_outputs(p1)   # nothing given, nothing to check

@@ -351,6 +351,54 @@ def test_fp8_partition_partials_match_oracle():
         assert (err / np.abs(O[sl]).max(-1)).max() <= 1e-5
 
 
+MULTIQ = [
+    ("q2_g8_paged64_auto", dict(batch=5, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=64,
+                                len_range=(1, 5000), num_splits=0, seed=100, q_len=2)),
+    ("q2_g4_contig_splits8", dict(batch=2, num_q_heads=8, num_kv_heads=2, qk_depth=128, seq_lens=[4096, 1000],
+                                  num_splits=8, seed=101, q_len=2)),
+    ("q4_g4_short_sequences", dict(batch=4, num_q_heads=8, num_kv_heads=2, qk_depth=128, page_size=32,
+                                   seq_lens=[1, 3, 100, 2000], num_splits=0, seed=102, q_len=4)),
+    ("q3_g2_one_kv_head_key_splits", dict(batch=3, num_q_heads=2, num_kv_heads=1, qk_depth=128, page_size=64,
+                                          seq_lens=[2, 700, 3000], num_splits=3, seed=103, q_len=3)),
+    ("q2_g8_fp8_cache", dict(batch=3, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=64,
+                             seq_lens=[33, 1000, 2500], num_splits=0, seed=104, q_len=2, kv_fp8=True)),
+]
+
+
+@pytest.mark.parametrize("name,kw", MULTIQ, ids=[c[0] for c in MULTIQ])
+def test_multiquery_parity(name, kw):
+    # q_len queries per sequence, each attending the keys up to its own position
+    case = make_case(name, **kw)
+    out, lse, o32 = check_case(case, f"multi-query {name}")
+    for b, L in enumerate(case.seq_lens.tolist()):
+        for i in range(case.q_len):
+            if L - case.q_len + 1 + i <= 0:   # a query with no key before it
+                assert torch.all(out[b, i].float() == 0) and torch.all(torch.isneginf(lse[b, i]))
+
+
+def test_multiquery_fused_combine():
+    case = make_case("mq_fused", batch=4, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=64,
+                     len_range=(1, 4000), num_splits=0, seed=105, q_len=2)
+    dc = to_device(case)
+    O, LSE = oracle_for(case)
+    prob = api.make_problem(dc.q, dc.k_cache, dc.v_cache, dc.page_table, page_size=case.page_size)
+    ws = torch.zeros(api.workspace_bytes(prob, 0), dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        out, lse, o32 = api.case_call(dc, return_lse=True, return_o32=True, fused=True, workspace=ws)
+        torch.cuda.synchronize()
+        assert_parity(out, lse, o32, O, LSE, what=f"multi-query fused call {rep}")
+
+
+def test_workload_paged_gqa_q2_sampled():
+    case = workload("paged_gqa_q2")
+    print("[parity] workload paged_gqa_q2 (sampled rows)", flush=True)
+    out, lse, o32 = run(case)
+    lens = case.seq_lens.numpy()
+    rows = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 23})
+    O, LSE = oracle_for(case, batch_rows=rows)
+    assert_parity(out[rows], lse[rows], o32[rows], O, LSE, what="paged_gqa_q2 sampled")
+
+
 def test_workload_paged_gqa_fp8_sampled():
     case = workload("paged_gqa_fp8")
     print("[parity] workload paged_gqa_fp8 (sampled rows)", flush=True)
