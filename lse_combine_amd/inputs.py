@@ -39,6 +39,9 @@ class Case:
     # contiguous [B, Hkv, Lcap] / paged [N, Hkv, ps] (tokens innermost); None otherwise
     k_scale: torch.Tensor | None = None
     v_scale: torch.Tensor | None = None
+    # rotary columns stored apart: the last Dqk - nope columns of every K row, bf16, in the
+    # cache's layout ([..., Hkv, rope]); k_cache then holds the first nope columns
+    k_rope: torch.Tensor | None = None
 
     @property
     def batch(self):
@@ -69,14 +72,20 @@ class Case:
         q = {torch.float32: "f32", torch.bfloat16: "bf16"}[self.q.dtype]
         return q + "/fp8-kv" if self.kv_fp8 else q
 
+    @property
+    def nope_depth(self):
+        """K columns held by k_cache (all of them unless the rotary ones are stored apart)."""
+        return self.k_cache.shape[-1]
+
     def kv_bytes(self) -> int:
         """Bytes of K and V that attention must read (attended tokens only)."""
         tokens = int(self.seq_lens.clamp(min=0).sum())
         es = self.k_cache.element_size()
-        if self.v_is_k_prefix:
-            per_tok = self.num_kv_heads * self.qk_depth * es
-        else:
-            per_tok = self.num_kv_heads * (self.qk_depth + self.ov_depth) * es
+        per_tok = self.num_kv_heads * self.nope_depth * es
+        if not self.v_is_k_prefix:
+            per_tok += self.num_kv_heads * self.ov_depth * es
+        if self.k_rope is not None:
+            per_tok += self.num_kv_heads * self.k_rope.shape[-1] * self.k_rope.element_size()
         # the per-token scales of an fp8 cache are read too (4 bytes per token and kv head)
         for sc in (self.k_scale, self.v_scale):
             if sc is not None:
@@ -97,7 +106,7 @@ def make_case(name="case", *, batch, num_q_heads, num_kv_heads, qk_depth, ov_dep
               dtype=torch.bfloat16, page_size=0, seq_lens=None, len_range=None, kv_capacity=None,
               num_splits=0, seed=0, v_is_k_prefix=False, scale=None, poison=False,
               spare_pages=0, q_scale=1.0, page_table_width=None, kv_fp8=False, v_scaled=True,
-              q_len=1) -> Case:
+              q_len=1, rope_apart=0) -> Case:
     """Build a seeded case.
 
     Exactly one of ``seq_lens`` (a list of lengths) or ``len_range``
@@ -111,6 +120,9 @@ def make_case(name="case", *, batch, num_q_heads, num_kv_heads, qk_depth, ov_dep
     ``kv_fp8``: K and V are drawn as above (fp32) and stored as E4M3 codes with a
     per-(token, kv head) scale amax / 448 (``v_scaled=False``: V codes of the unscaled
     values, no V scale); q stays in ``dtype``.
+    ``rope_apart`` > 0: the last ``rope_apart`` columns of every K row (drawn with the
+    rest) are stored apart as bf16 (``k_rope``); k_cache keeps the first
+    qk_depth - rope_apart columns (quantised alone when ``kv_fp8``).
     """
     ov_depth = qk_depth if ov_depth is None else ov_depth
     gen = torch.Generator("cpu")
@@ -148,6 +160,11 @@ def make_case(name="case", *, batch, num_q_heads, num_kv_heads, qk_depth, ov_dep
     kv_dtype = torch.float32 if kv_fp8 else dtype
     k = _randn(gen, kv_shape_k, kv_dtype)
     v = None if v_is_k_prefix else _randn(gen, kv_shape_v, kv_dtype)
+    k_rope = None
+    if rope_apart:
+        nope = qk_depth - rope_apart
+        k_rope = k[..., nope:].to(torch.bfloat16).contiguous()
+        k = k[..., :nope].contiguous()
     k_scale = v_scale = None
     if kv_fp8:
         k, k_scale = _to_fp8(k, True)
@@ -155,11 +172,13 @@ def make_case(name="case", *, batch, num_q_heads, num_kv_heads, qk_depth, ov_dep
             v, v_scale = _to_fp8(v, v_scaled)
     if poison:
         _poison(k, v, pos_lens, pt, page_size)
+        if k_rope is not None:
+            _poison(k_rope, None, pos_lens, pt, page_size)
     sc = scale if scale is not None else 1.0 / math.sqrt(qk_depth)
     return Case(name=name, q=q, k_cache=k, v_cache=v, seq_lens=lens32, page_table=pt,
                 page_size=page_size, scale=sc, num_splits=num_splits,
                 v_is_k_prefix=v_is_k_prefix, ov_depth=ov_depth, meta={"seed": seed},
-                k_scale=k_scale, v_scale=v_scale)
+                k_scale=k_scale, v_scale=v_scale, k_rope=k_rope)
 
 
 FP8_E4M3_MAX = 448.0   # largest finite E4M3 magnitude
@@ -224,6 +243,17 @@ WORKLOADS = {
     "paged_gqa_fp8": dict(seed=3, batch=32, num_q_heads=64, num_kv_heads=8, qk_depth=128,
                           dtype=torch.bfloat16, page_size=64, len_range=(512, 32768),
                           num_splits=0, page_table_width=512, kv_fp8=True),
+    # GLM-style widths, one kv head per q head: qk 256 = 192 nope + 64 rotary columns (the
+    # rotary ones stored apart as bf16), V / output 256 (not the nope width); batch 32,
+    # 16 heads, bf16, page 64, L_b ~ U[512, 8192], automatic splits
+    "paged_glm": dict(seed=6, batch=32, num_q_heads=16, num_kv_heads=16, qk_depth=256, ov_depth=256,
+                      dtype=torch.bfloat16, page_size=64, len_range=(512, 8192), num_splits=0,
+                      page_table_width=128, rope_apart=64),
+    # the same with the nope columns and V as fp8 (E4M3) with per-token scales; the rotary
+    # columns stay bf16
+    "paged_glm_fp8": dict(seed=6, batch=32, num_q_heads=16, num_kv_heads=16, qk_depth=256, ov_depth=256,
+                          dtype=torch.bfloat16, page_size=64, len_range=(512, 8192), num_splits=0,
+                          page_table_width=128, rope_apart=64, kv_fp8=True),
 }
 
 
@@ -241,4 +271,4 @@ def to_device(case: Case, device="cuda") -> Case:
                 seq_lens=mv(case.seq_lens), page_table=mv(case.page_table), page_size=case.page_size,
                 scale=case.scale, num_splits=case.num_splits, v_is_k_prefix=case.v_is_k_prefix,
                 ov_depth=case.ov_depth, meta=dict(case.meta), k_scale=mv(case.k_scale),
-                v_scale=mv(case.v_scale))
+                v_scale=mv(case.v_scale), k_rope=mv(case.k_rope))

@@ -33,6 +33,12 @@ What is computed (single query per sequence, i.e. decode):
 * ``fp8_e4m3_to_fp64`` -- the values of an fp8 (E4M3) cache; with per-token scales
   the definition above runs on code value times scale (FA4Config: fp8 qkv_dtype with a
   per-token scale_dtype for K).
+* rotary columns stored apart (``k_rope``): the last Dqk - nope columns of every
+  K row live in a tensor of their own with their own dtype (FA4Config: rope_depth
+  is the padded qk depth minus the padded nope depth, not minus the V depth, and
+  rope_dtype may differ from the qkv dtype). The definition runs on the row
+  [K nope columns | rotary columns]; per-token scales of an fp8 cache belong to
+  the quantised nope columns only (reading: the rotary tensor is not quantised).
 
 Readings where the pages are silent (each is listed in the design notes):
 the max is kept in raw q.k units; empty partitions contribute weight 0 and an
@@ -117,9 +123,12 @@ def _key_rows(k_cache, b, kvh, L, page_table, page_size, scales=None):
 
 
 def _gather(q, k_cache, v_cache, b, kvh, g, L, page_table, page_size, v_is_k_prefix, ov_depth,
-            k_scale=None, v_scale=None):
+            k_scale=None, v_scale=None, k_rope=None):
     qg = np.asarray(q[b, kvh * g:(kvh + 1) * g, :], dtype=np.float64)
     K = _key_rows(k_cache, b, kvh, L, page_table, page_size, k_scale)
+    if k_rope is not None:
+        # the rotary columns follow the nope columns of the same row (no scale of their own)
+        K = np.concatenate([K, _key_rows(k_rope, b, kvh, L, page_table, page_size)], axis=1)
     if v_is_k_prefix:
         V = K[:, :ov_depth]
     else:
@@ -127,11 +136,14 @@ def _gather(q, k_cache, v_cache, b, kvh, g, L, page_table, page_size, v_is_k_pre
     return qg, K, V
 
 
-def _dims(q, k_cache, v_cache, v_is_k_prefix, ov_depth):
+def _dims(q, k_cache, v_cache, v_is_k_prefix, ov_depth, k_rope=None):
     B, Hq, Dqk = q.shape
     Hkv = k_cache.shape[2]
     if Hq % Hkv:
         raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    width = k_cache.shape[3] + (0 if k_rope is None else k_rope.shape[3])
+    if width != Dqk:
+        raise ValueError(f"K row width {width} (nope + rotary columns) must equal the q depth {Dqk}")
     if v_is_k_prefix:
         Dv = Dqk if ov_depth is None else int(ov_depth)
     else:
@@ -143,12 +155,14 @@ def _dims(q, k_cache, v_cache, v_is_k_prefix, ov_depth):
 # the definition
 # ---------------------------------------------------------------------------
 def decode_attention_fp64(q, k_cache, v_cache, seq_lens, scale, page_table=None, page_size=0,
-                          v_is_k_prefix=False, ov_depth=None, k_scale=None, v_scale=None):
+                          v_is_k_prefix=False, ov_depth=None, k_scale=None, v_scale=None, k_rope=None):
     """Full softmax(scale * q K^T) V per (sequence, head), in fp64.
 
     q: [B, Hq, Dqk]; caches as described in ``_key_rows``; seq_lens: [B].
     fp8 caches (uint8 E4M3 codes) are read as code value times the per-token scale
     (``k_scale`` / ``v_scale``, layout in ``_scale_rows``; a missing scale is 1).
+    ``k_rope``: the rotary columns of every K row, stored apart in the cache's layout
+    ([..., Hkv, Dqk - nope]); ``k_cache`` then holds the first nope columns.
     Returns (O [B, Hq, Dv] fp64, LSE [B, Hq] fp64, natural log).
     A sequence of length 0 gives O = 0 and LSE = -inf.
 
@@ -162,10 +176,10 @@ def decode_attention_fp64(q, k_cache, v_cache, seq_lens, scale, page_table=None,
         ql = q_arr.shape[1]
         lens = np.asarray(seq_lens, dtype=np.int64)
         outs = [decode_attention_fp64(q_arr[:, i], k_cache, v_cache, np.clip(lens - ql + 1 + i, 0, lens), scale,
-                                      page_table, page_size, v_is_k_prefix, ov_depth, k_scale, v_scale)
+                                      page_table, page_size, v_is_k_prefix, ov_depth, k_scale, v_scale, k_rope)
                 for i in range(ql)]
         return np.stack([o for o, _ in outs], 1), np.stack([l for _, l in outs], 1)
-    B, Hq, Hkv, g, Dqk, Dv = _dims(q, k_cache, v_cache, v_is_k_prefix, ov_depth)
+    B, Hq, Hkv, g, Dqk, Dv = _dims(q, k_cache, v_cache, v_is_k_prefix, ov_depth, k_rope)
     O = np.zeros((B, Hq, Dv), dtype=np.float64)
     LSE = np.full((B, Hq), -np.inf, dtype=np.float64)
     for b in range(B):
@@ -174,7 +188,7 @@ def decode_attention_fp64(q, k_cache, v_cache, seq_lens, scale, page_table=None,
             continue
         for kvh in range(Hkv):
             qg, K, V = _gather(q, k_cache, v_cache, b, kvh, g, L, page_table, page_size,
-                               v_is_k_prefix, Dv, k_scale, v_scale)
+                               v_is_k_prefix, Dv, k_scale, v_scale, k_rope)
             x = qg @ K.T                                   # [g, L] raw scores
             m = x.max(axis=1, keepdims=True)
             e = np.exp(scale * (x - m))
@@ -267,7 +281,7 @@ def equal_share_pieces(seq_lens, workers, tile=32, min_tiles=8):
 
 
 def range_partials_fp64(q, k_cache, v_cache, seq_lens, scale, pieces, page_table=None, page_size=0,
-                        v_is_k_prefix=False, ov_depth=None, k_scale=None, v_scale=None):
+                        v_is_k_prefix=False, ov_depth=None, k_scale=None, v_scale=None, k_rope=None):
     """Pass-1 partials over explicit key ranges.
 
     pieces: (b, key_start, key_end, slot) tuples as ``equal_share_pieces``
@@ -277,7 +291,7 @@ def range_partials_fp64(q, k_cache, v_cache, seq_lens, scale, pieces, page_table
     paragraph). Returns (m [S, Hq], l [S, Hq], O [S, Hq, Dv]) indexed by slot,
     S = 1 + the largest slot; slots no piece names hold (-inf, 0, 0).
     """
-    B, Hq, Hkv, g, Dqk, Dv = _dims(q, k_cache, v_cache, v_is_k_prefix, ov_depth)
+    B, Hq, Hkv, g, Dqk, Dv = _dims(q, k_cache, v_cache, v_is_k_prefix, ov_depth, k_rope)
     S = 1 + max((pc[3] for pc in pieces), default=-1)
     m = np.full((S, Hq), -np.inf)
     l = np.zeros((S, Hq))
@@ -285,7 +299,7 @@ def range_partials_fp64(q, k_cache, v_cache, seq_lens, scale, pieces, page_table
     for b, lo, hi, slot in pieces:
         for kvh in range(Hkv):
             qg, K, V = _gather(q, k_cache, v_cache, b, kvh, g, hi, page_table, page_size,
-                               v_is_k_prefix, Dv, k_scale, v_scale)
+                               v_is_k_prefix, Dv, k_scale, v_scale, k_rope)
             x = qg @ K[lo:hi].T
             mp = x.max(axis=1, keepdims=True)
             e = np.exp(scale * (x - mp))

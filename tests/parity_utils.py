@@ -33,6 +33,7 @@ def oracle_for(case, batch_rows=None):
     pt = None if case.page_table is None else case.page_table.cpu().numpy()
     ks = None if case.k_scale is None else case.k_scale.cpu().numpy()
     vs = None if case.v_scale is None else case.v_scale.cpu().numpy()
+    kr = np32(case.k_rope)
     if batch_rows is not None:
         q = q[batch_rows]
         lens = lens[batch_rows]
@@ -43,10 +44,11 @@ def oracle_for(case, batch_rows=None):
             v = None if v is None else v[batch_rows]
             ks = None if ks is None else ks[batch_rows]
             vs = None if vs is None else vs[batch_rows]
+            kr = None if kr is None else kr[batch_rows]
     lens = np.maximum(lens, 0)
     return decode_attention_fp64(q, k, v, lens, case.scale, page_table=pt, page_size=case.page_size,
                                  v_is_k_prefix=case.v_is_k_prefix, ov_depth=case.ov_depth, k_scale=ks,
-                                 v_scale=vs)
+                                 v_scale=vs, k_rope=kr)
 
 
 def assert_parity(out, lse, o32, O, LSE, o32_row_rtol=O32_ROW_RTOL, lse_rtol=LSE_RTOL, what=""):

@@ -496,3 +496,44 @@ def test_multiquery_brute_force(paged):
     np.testing.assert_allclose(O[:, -1], O1, atol=0)
     # a sequence of 2 keys with q_len 3: query 0 sees nothing (O = 0, LSE = -inf)
     assert np.all(O[1, 0] == 0) and np.all(np.isneginf(LSE[1, 0]))
+
+
+# ---------------------------------------------------------------------------
+# rotary columns stored apart (own tensor, own dtype), V depth != nope depth
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("paged", [0, 4])
+def test_rope_apart_is_the_row_nope_then_rotary(paged):
+    # splitting a K row into [nope | rotary] storage changes nothing; the other order would
+    q, k, v, lens, pt = rng_case(95 + paged, B=3, Hq=4, Hkv=2, D=10, Dv=7, L=(9, 1, 6), paged=paged)
+    O, LSE = decode_attention_fp64(q, k, v, lens, 0.4, page_table=pt, page_size=paged)
+    Oa, La = decode_attention_fp64(q, k[..., :6], v, lens, 0.4, page_table=pt, page_size=paged, k_rope=k[..., 6:])
+    np.testing.assert_array_equal(Oa, O)
+    np.testing.assert_array_equal(La, LSE)
+    Ob, Lb = brute(q, k, v, lens, 0.4, pt, paged)
+    np.testing.assert_allclose(Oa, Ob, atol=1e-13)
+    Ow, _ = decode_attention_fp64(q, k[..., 4:], v, lens, 0.4, page_table=pt, page_size=paged, k_rope=k[..., :4])
+    assert np.abs(Ow - O).max() > 1e-3
+    with pytest.raises(ValueError):
+        decode_attention_fp64(q, k[..., :6], v, lens, 0.4, page_table=pt, page_size=paged, k_rope=k[..., 7:])
+
+
+@pytest.mark.parametrize("paged", [0, 1])
+def test_fp8_nope_with_bf16_rotary_brute_force_with_torch_decode(paged):
+    # GLM-style shape in miniature: nope 8 (fp8, per-token scales) + 4 rotary (bf16) and
+    # V depth 10 != nope; the scales apply to the nope columns only
+    from lse_combine_amd.inputs import make_case
+    c = make_case("glm", batch=3, num_q_heads=4, num_kv_heads=2, qk_depth=12, ov_depth=10,
+                  page_size=4 if paged else 0, seq_lens=[9, 1, 6], seed=96 + paged, kv_fp8=True,
+                  dtype=torch.float32, rope_apart=4)
+    assert c.k_cache.shape[-1] == 8 and c.k_rope.shape[-1] == 4 and c.k_rope.dtype == torch.bfloat16
+    pt = None if c.page_table is None else c.page_table.numpy()
+    O, LSE = decode_attention_fp64(c.q.numpy(), c.k_cache.numpy(), c.v_cache.numpy(), c.seq_lens.numpy(),
+                                   c.scale, page_table=pt, page_size=c.page_size, k_scale=c.k_scale.numpy(),
+                                   v_scale=c.v_scale.numpy(), k_rope=c.k_rope.float().numpy())
+    kn = c.k_cache.view(torch.float8_e4m3fn).double() * c.k_scale.double().permute(0, 2, 1)[..., None]
+    kd = torch.cat([kn, c.k_rope.double()], dim=-1)
+    vd = c.v_cache.view(torch.float8_e4m3fn).double() * c.v_scale.double().permute(0, 2, 1)[..., None]
+    Ob, Lb = brute(c.q.double().numpy(), kd.numpy(), vd.numpy(), c.seq_lens.numpy(), c.scale, pt, c.page_size)
+    np.testing.assert_allclose(O, Ob, atol=1e-13)
+    np.testing.assert_allclose(LSE, Lb, rtol=1e-13)
+    assert O.shape[-1] == 10
