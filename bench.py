@@ -86,7 +86,8 @@ def main():
     print(f"[bench] workload {case.name}: {tokens} keys, KV {kv_bytes / 1e9:.3f} GB", file=sys.stderr, flush=True)
 
     prob = api.make_problem(dc.q, dc.k_cache, dc.v_cache, dc.page_table, page_size=case.page_size,
-                            v_is_k_prefix=case.v_is_k_prefix, ov_depth=case.ov_depth, kernel=args.kernel)
+                            v_is_k_prefix=case.v_is_k_prefix, ov_depth=case.ov_depth, kernel=args.kernel,
+                            k_rope=dc.k_rope)
     chunk, max_splits = api.choose_splits(prob, case.num_splits)
     B, Hq, Dv = prob.batch, prob.num_q_heads, prob.ov_depth
     rows = api.row_shape(prob)   # (B, Hq), or (B, q_len, Hq) with several queries per sequence
@@ -99,7 +100,7 @@ def main():
     plan = api.DecodePlan(dc.q, dc.k_cache, dc.v_cache, dc.page_table, dc.seq_lens, case.scale, case.num_splits,
                           page_size=case.page_size, v_is_k_prefix=case.v_is_k_prefix, ov_depth=case.ov_depth,
                           kernel=args.kernel, out=out, fused=args.combine == "fused",
-                          k_scale=dc.k_scale, v_scale=dc.v_scale)
+                          k_scale=dc.k_scale, v_scale=dc.v_scale, k_rope=dc.k_rope)
     step = plan.run
 
     # --- streaming-read probe and a copy of known size (counter calibration) ---
@@ -148,7 +149,14 @@ def main():
     def ptr(t):
         return None if t is None else P_(t.data_ptr())
 
-    if case.kv_fp8:
+    if case.k_rope is not None:
+        kv = _lib.DaKv(dc.k_cache.data_ptr(), dc.v_cache.data_ptr(), dc.k_rope.data_ptr(),
+                       None if dc.k_scale is None else dc.k_scale.data_ptr(),
+                       None if dc.v_scale is None else dc.v_scale.data_ptr())
+        part_fn = lib.decode_attn_partition_kv
+        part_args = (ctypes.byref(prob), ptr(dc.q), ctypes.byref(kv), ptr(dc.page_table), ptr(dc.seq_lens),
+                     float(case.scale), chunk, max_splits, ptr(part_o), ptr(part_ml), stream)
+    elif case.kv_fp8:
         part_fn = lib.decode_attn_partition_fp8
         part_args = (ctypes.byref(prob), ptr(dc.q), ptr(dc.k_cache), ptr(dc.v_cache), ptr(dc.k_scale),
                      ptr(dc.v_scale), ptr(dc.page_table), ptr(dc.seq_lens), float(case.scale), chunk, max_splits,
@@ -197,11 +205,12 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": case.dtype_name,
-        "data": "synthetic (seeded torch.randn" + (", E4M3 K/V with per-token scales)" if case.kv_fp8 else ")"),
+        "data": "synthetic (seeded torch.randn" + (", E4M3 K/V with per-token scales" if case.kv_fp8 else "")
+                + (", rotary K columns stored apart in bf16" if case.k_rope is not None else "") + ")",
         "config": {
             "workload": case.name,
             "batch": B, "q_len": max(1, prob.q_len), "q_heads": Hq, "kv_heads": prob.num_kv_heads,
-            "qk_depth": prob.qk_depth, "ov_depth": Dv, "page_size": case.page_size,
+            "qk_depth": prob.qk_depth, "ov_depth": Dv, "nope_depth": prob.nope_depth, "page_size": case.page_size,
             "keys": tokens, "max_seq_len": int(case.seq_lens.max()),
             "chunk_tokens": chunk, "max_splits": max_splits, "kernel": args.kernel, "combine": args.combine,
             "kv_bytes": kv_bytes,
@@ -243,6 +252,7 @@ def cpu_baseline(case, kv_bytes, budget_s):
     v = None if case.v_cache is None else (case.v_cache.numpy() if case.kv_fp8 else case.v_cache.float().numpy())
     ks = None if case.k_scale is None else case.k_scale.numpy()
     vs = None if case.v_scale is None else case.v_scale.numpy()
+    kr = None if case.k_rope is None else case.k_rope.float().numpy()
     info = threadpoolctl.threadpool_info()
     blas = [i for i in info if i.get("user_api") == "blas"]
     threads = blas[0]["num_threads"] if blas else 1
@@ -251,7 +261,8 @@ def cpu_baseline(case, kv_bytes, budget_s):
     while len(times) < 3:
         t0 = time.perf_counter()
         decode_attention_fp64(q, k, v, lens, case.scale, page_table=pt, page_size=case.page_size,
-                              v_is_k_prefix=case.v_is_k_prefix, ov_depth=case.ov_depth, k_scale=ks, v_scale=vs)
+                              v_is_k_prefix=case.v_is_k_prefix, ov_depth=case.ov_depth, k_scale=ks, v_scale=vs,
+                              k_rope=kr)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_start + times[-1] > budget_s:
             break

@@ -79,6 +79,14 @@ typedef struct da_problem {
                                 run through the *_fp8 entry points that take the scales */
   int32_t q_len;             /* queries per sequence (0 or 1: one, plain decode; > 1: the
                                 sequence's last q_len positions, e.g. speculative tokens) */
+  int32_t nope_depth;        /* 0: k_cache rows hold all qk_depth columns. > 0: k_cache holds the
+                                first nope_depth ("nope") columns of every K row and a separate
+                                tensor (da_kv.k_rope) the last qk_depth - nope_depth rotary ones
+                                (FA4Config, rope_depth: the q.K depth minus the nope depth, which
+                                need not equal ov_depth) */
+  int32_t rope_dtype;        /* da_dtype of the rotary columns stored apart (FA4Config,
+                                rope_dtype); DA_BF16 is the one supported. Ignored when
+                                nope_depth == 0 */
 } da_problem;
 
 /*
@@ -88,6 +96,8 @@ typedef struct da_problem {
  * and including that position (keys t < L_b - q_len + 1 + i: causal among the new tokens).
  *   q          [B][Hq][Dqk]                        dtype
  *   k_cache    contiguous: [B][kv_capacity][Hkv][Dqk]; paged: [num_pages][page_size][Hkv][Dqk]
+ *              (with nope_depth > 0: nope_depth columns instead of Dqk)
+ *   k_rope     nope_depth > 0 only: same layout with Dqk - nope_depth columns, rope_dtype
  *   v_cache    same as k_cache with Dv (ignored when v_is_k_prefix)
  *   page_table int32 [B][max_pages_per_seq]; key t of sequence b is slot t % page_size of
  *              page page_table[b][t / page_size]. Entries at or beyond ceil(L_b / page_size)
@@ -119,7 +129,10 @@ typedef struct da_problem {
 /* DA_OK if a kernel exists for this problem, else DA_EINVAL / DA_EUNSUPPORTED with a
  * message (FA4Config, supported). Supported: dtype f32 or bf16 with Dqk == Dv == 128
  * and g <= 16 (f32 runs the vector-ALU kernel); bf16 latent-shared Dqk == 576,
- * Dv == 512, Hkv == 1. */
+ * Dv == 512, Hkv == 1; and on the matrix-core kernel (bf16 q, separate K and V, q_len x
+ * g <= 16, contiguous cache or pages of a power of two >= 32 keys) the depth pairs
+ * Dqk/Dv 192/128 and 256/256, with the K cache in bf16 or fp8 and optionally the 64
+ * rotary columns stored apart in bf16 (nope_depth 128 or 192). */
 int da_supported(const da_problem* p);
 
 /* Split selection (FA4Config, with_splitk: partitions of the K/V sequence).
@@ -167,8 +180,9 @@ int decode_attn_splitk_fused(const da_problem* p, const void* q, const void* k_c
                              size_t workspace_bytes, void* stream);
 
 /* The whole decode step over an fp8 cache (FA4Config: an fp8 qkv_dtype with a per-token
- * scale_dtype for K). kv_dtype must be DA_FP8_E4M3, dtype DA_BF16 (q), Dqk == Dv == 128,
- * group <= 16, and the cache contiguous or paged with page_size a power of two >= 32.
+ * scale_dtype for K). kv_dtype must be DA_FP8_E4M3, dtype DA_BF16 (q), a matrix-core depth
+ * pair (see da_supported), and the cache contiguous or paged with page_size a power of two
+ * >= 32.
  * k_cache / v_cache hold E4M3 codes (one byte each, same layouts as above); key t of kv
  * head k reads k_scale * code (fp32 scale of that token and kv head) and V likewise with
  * v_scale (NULL = 1). Scale layout, tokens innermost: contiguous [B][Hkv][kv_capacity],
@@ -186,6 +200,33 @@ int decode_attn_partition_fp8(const da_problem* p, const void* q, const void* k_
                               const int32_t* page_table, const int32_t* seq_lens, float scale,
                               int32_t chunk_tokens, int32_t max_splits, float* part_o,
                               float* part_ml, void* stream);
+
+/* The cache tensors of one step, for the entry points that take them together. Host
+ * struct, read during the call only; the pointers are device pointers. */
+typedef struct da_kv {
+  const void* k_cache;   /* K rows: all qk_depth columns, or the first nope_depth of them */
+  const void* v_cache;   /* V rows (ignored when v_is_k_prefix) */
+  const void* k_rope;    /* nope_depth > 0: the other qk_depth - nope_depth columns of every K
+                            row (rope_dtype, k_cache's layout); else NULL */
+  const float* k_scale;  /* fp8 caches: per-token scales of k_cache's columns (layout as for
+                            decode_attn_splitk_fp8; the rotary columns have none); else NULL */
+  const float* v_scale;  /* fp8 caches: per-token V scales, NULL = 1; else NULL */
+} da_kv;
+
+/* The whole decode step with the caches described by `kv`: every problem the library
+ * supports, including rotary columns stored apart (nope_depth > 0) and fp8 caches.
+ * fused != 0 runs it as decode_attn_splitk_fused (same workspace rules), else as
+ * decode_attn_splitk. Other arguments as decode_attn_splitk. */
+int decode_attn_splitk_kv(const da_problem* p, const void* q, const da_kv* kv,
+                          const int32_t* page_table, const int32_t* seq_lens, float scale,
+                          int32_t num_splits, int32_t fused, void* out, float* lse_out,
+                          float* o_f32_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Pass 1 only with the caches described by `kv` (partials as decode_attn_partition). */
+int decode_attn_partition_kv(const da_problem* p, const void* q, const da_kv* kv,
+                             const int32_t* page_table, const int32_t* seq_lens, float scale,
+                             int32_t chunk_tokens, int32_t max_splits, float* part_o,
+                             float* part_ml, void* stream);
 
 /* Pass 1 only (fa4_splitk_combine_write, second paragraph: each partition stages its
  * normalised O and its (max, sum)). Writes part_ml / part_o (device, layouts above) for

@@ -19,7 +19,13 @@ DA_KERNEL_AUTO, DA_KERNEL_FMA, DA_KERNEL_MFMA = 0, 1, 2
 class DaProblem(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "batch", "num_q_heads", "num_kv_heads", "qk_depth", "ov_depth", "dtype", "page_size",
-        "max_pages_per_seq", "num_pages", "kv_capacity", "max_seq_len", "v_is_k_prefix", "kernel", "kv_dtype", "q_len")]
+        "max_pages_per_seq", "num_pages", "kv_capacity", "max_seq_len", "v_is_k_prefix", "kernel", "kv_dtype", "q_len",
+        "nope_depth", "rope_dtype")]
+
+
+class DaKv(ctypes.Structure):
+    """The cache tensors of one step (da_kv): device pointers, NULL where unused."""
+    _fields_ = [(name, ctypes.c_void_p) for name in ("k_cache", "v_cache", "k_rope", "k_scale", "v_scale")]
 
 
 class DaError(RuntimeError):
@@ -43,6 +49,10 @@ _SIGS = {
                                               ctypes.c_float, _I32, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "decode_attn_partition_fp8": (ctypes.c_int, [ctypes.POINTER(DaProblem), _P, _P, _P, _P, _P, _P, _P,
                                                  ctypes.c_float, _I32, _I32, _P, _P, _P]),
+    "decode_attn_splitk_kv": (ctypes.c_int, [ctypes.POINTER(DaProblem), _P, ctypes.POINTER(DaKv), _P, _P,
+                                             ctypes.c_float, _I32, _I32, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "decode_attn_partition_kv": (ctypes.c_int, [ctypes.POINTER(DaProblem), _P, ctypes.POINTER(DaKv), _P, _P,
+                                                ctypes.c_float, _I32, _I32, _P, _P, _P]),
     "decode_attn_partition": (ctypes.c_int, [ctypes.POINTER(DaProblem), _P, _P, _P, _P, _P, ctypes.c_float,
                                              _I32, _I32, _P, _P, _P]),
     "decode_attn_combine": (ctypes.c_int, [ctypes.POINTER(DaProblem), _P, ctypes.c_float, _I32, _I32, _P, _P,

@@ -22,15 +22,24 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _kv(k_cache, v_cache, k_rope=None, k_scale=None, v_scale=None):
+    """da_kv of the cache tensors (the tensors must outlive its use)."""
+    def addr(t):
+        return None if t is None else t.data_ptr()
+    return _lib.DaKv(addr(k_cache), addr(v_cache), addr(k_rope), addr(k_scale), addr(v_scale))
+
+
 def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
 def make_problem(q, k_cache, v_cache=None, page_table=None, *, page_size=0, max_seq_len=None,
-                 v_is_k_prefix=False, ov_depth=None, kernel="auto", num_pages=None) -> DaProblem:
+                 v_is_k_prefix=False, ov_depth=None, kernel="auto", num_pages=None, k_rope=None) -> DaProblem:
     """Describe one decode step from its tensors (shapes as in include/decode_attn.h).
 
     q is [B, Hq, Dqk], or [B, q_len, Hq, Dqk] for several queries per sequence.
+    k_rope (bf16, k_cache's layout) holds the last Dqk - nope rotary columns of every K row
+    when they are stored apart; k_cache then holds the first nope columns.
     """
     if q.dim() not in (3, 4) or k_cache.dim() != 4:
         raise ValueError("q must be [B, Hq, Dqk] or [B, q_len, Hq, Dqk] and k_cache 4-D")
@@ -46,7 +55,14 @@ def make_problem(q, k_cache, v_cache=None, page_table=None, *, page_size=0, max_
         raise ValueError("an fp8 k_cache needs an fp8 (uint8) v_cache")
     B, Hq, Dqk = q.shape
     Hkv = k_cache.shape[2]
-    if k_cache.shape[3] != Dqk:
+    nope = 0
+    if k_rope is not None:
+        if k_rope.dtype != torch.bfloat16 or tuple(k_rope.shape[:3]) != tuple(k_cache.shape[:3]):
+            raise ValueError("k_rope must be bfloat16 and match k_cache in its first three dimensions")
+        nope = k_cache.shape[3]
+        if nope + k_rope.shape[3] != Dqk:
+            raise ValueError("k_cache depth + k_rope depth must equal q depth")
+    elif k_cache.shape[3] != Dqk:
         raise ValueError("k_cache depth must equal q depth")
     if v_is_k_prefix:
         Dv = int(ov_depth if ov_depth is not None else Dqk)
@@ -61,6 +77,8 @@ def make_problem(q, k_cache, v_cache=None, page_table=None, *, page_size=0, max_
     p.dtype = _DTYPES[q.dtype]
     p.kv_dtype = _lib.DA_FP8_E4M3 if fp8 else 0
     p.q_len = q_len
+    p.nope_depth = nope
+    p.rope_dtype = _lib.DA_BF16 if nope else 0
     p.kernel = _KERNELS[kernel]
     p.v_is_k_prefix = 1 if v_is_k_prefix else 0
     if page_table is not None:
@@ -128,15 +146,17 @@ def workspace_bytes(problem: DaProblem, num_splits=0):
 def decode_attn(q, k_cache, v_cache, page_table, seq_lens, scale, num_splits=0, *, page_size=0,
                 max_seq_len=None, v_is_k_prefix=False, ov_depth=None, out=None, lse=None, o32=None,
                 return_lse=False, return_o32=False, workspace=None, kernel="auto", fused=False,
-                k_scale=None, v_scale=None):
+                k_scale=None, v_scale=None, k_rope=None):
     """The whole split-K decode step. Returns out (bf16 [B, Hq, Dv]) or (out, lse, o32).
 
     fused=True runs decode_attn_splitk_fused (the combine done by each group's last
     workgroup); a workspace passed in must then have been zero-filled before its first use.
+    fp8 caches take k_scale / v_scale; rotary columns stored apart take k_rope (both run
+    through the entry points that accept those tensors).
     """
     lib = _lib.load()
     prob = make_problem(q, k_cache, v_cache, page_table, page_size=page_size, max_seq_len=max_seq_len,
-                        v_is_k_prefix=v_is_k_prefix, ov_depth=ov_depth, kernel=kernel)
+                        v_is_k_prefix=v_is_k_prefix, ov_depth=ov_depth, kernel=kernel, k_rope=k_rope)
     _check_tensors(q, k_cache, v_cache, page_table, seq_lens)
     rows = row_shape(prob)
     Dv = prob.ov_depth
@@ -151,7 +171,13 @@ def decode_attn(q, k_cache, v_cache, page_table, seq_lens, scale, num_splits=0, 
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
     ws = (_ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
-    if prob.kv_dtype:
+    if k_rope is not None or (prob.kv_dtype and fused):
+        _check_tensors(k_rope, k_scale, v_scale)
+        kv = _kv(k_cache, v_cache, k_rope, k_scale, v_scale)
+        check(lib.decode_attn_splitk_kv(ctypes.byref(prob), _ptr(q), ctypes.byref(kv), _ptr(page_table),
+                                        _ptr(seq_lens), float(scale), int(num_splits), int(bool(fused)), _ptr(out),
+                                        _ptr(lse), _ptr(o32), *ws))
+    elif prob.kv_dtype:
         _check_tensors(k_scale, v_scale)
         check(lib.decode_attn_splitk_fp8(ctypes.byref(prob), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
                                          _ptr(v_scale), _ptr(page_table), _ptr(seq_lens), float(scale),
@@ -194,17 +220,23 @@ def slot_table(problem: DaProblem, max_splits, part_ml):
 
 def partition(q, k_cache, v_cache, page_table, seq_lens, scale, chunk_tokens, max_splits, *, page_size=0,
               max_seq_len=None, v_is_k_prefix=False, ov_depth=None, part_o=None, part_ml=None, kernel="auto",
-              k_scale=None, v_scale=None):
+              k_scale=None, v_scale=None, k_rope=None):
     """Pass 1 only. Returns (part_o, part_ml) fp32 in the layout ``alloc_partials`` describes."""
     lib = _lib.load()
     prob = make_problem(q, k_cache, v_cache, page_table, page_size=page_size, max_seq_len=max_seq_len,
-                        v_is_k_prefix=v_is_k_prefix, ov_depth=ov_depth, kernel=kernel)
+                        v_is_k_prefix=v_is_k_prefix, ov_depth=ov_depth, kernel=kernel, k_rope=k_rope)
     _check_tensors(q, k_cache, v_cache, page_table, seq_lens)
     if part_o is None or part_ml is None:
         po, pml = alloc_partials(prob, chunk_tokens, max_splits, q.device)
         part_o = po if part_o is None else part_o
         part_ml = pml if part_ml is None else part_ml
-    if prob.kv_dtype:
+    if k_rope is not None:
+        _check_tensors(k_rope, k_scale, v_scale)
+        kv = _kv(k_cache, v_cache, k_rope, k_scale, v_scale)
+        check(lib.decode_attn_partition_kv(ctypes.byref(prob), _ptr(q), ctypes.byref(kv), _ptr(page_table),
+                                           _ptr(seq_lens), float(scale), int(chunk_tokens), int(max_splits),
+                                           _ptr(part_o), _ptr(part_ml), _stream()))
+    elif prob.kv_dtype:
         check(lib.decode_attn_partition_fp8(ctypes.byref(prob), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                             _ptr(k_scale), _ptr(v_scale), _ptr(page_table), _ptr(seq_lens),
                                             float(scale), int(chunk_tokens), int(max_splits), _ptr(part_o),
@@ -237,7 +269,8 @@ def case_call(case, device="cuda", **kw):
     """Run a lse_combine_amd.inputs.Case already moved to ``device`` (see ``to_device``)."""
     return decode_attn(case.q, case.k_cache, case.v_cache, case.page_table, case.seq_lens, case.scale,
                        case.num_splits, page_size=case.page_size, v_is_k_prefix=case.v_is_k_prefix,
-                       ov_depth=case.ov_depth, k_scale=case.k_scale, v_scale=case.v_scale, **kw)
+                       ov_depth=case.ov_depth, k_scale=case.k_scale, v_scale=case.v_scale, k_rope=case.k_rope,
+                       **kw)
 
 
 class DecodePlan:
@@ -250,10 +283,10 @@ class DecodePlan:
 
     def __init__(self, q, k_cache, v_cache, page_table, seq_lens, scale, num_splits=0, *, page_size=0,
                  max_seq_len=None, v_is_k_prefix=False, ov_depth=None, kernel="auto", out=None, lse=None,
-                 o32=None, fused=False, k_scale=None, v_scale=None):
+                 o32=None, fused=False, k_scale=None, v_scale=None, k_rope=None):
         self.lib = _lib.load()
         self.prob = make_problem(q, k_cache, v_cache, page_table, page_size=page_size, max_seq_len=max_seq_len,
-                                 v_is_k_prefix=v_is_k_prefix, ov_depth=ov_depth, kernel=kernel)
+                                 v_is_k_prefix=v_is_k_prefix, ov_depth=ov_depth, kernel=kernel, k_rope=k_rope)
         _check_tensors(q, k_cache, v_cache, page_table, seq_lens)
         self.out = (torch.empty(row_shape(self.prob) + (self.prob.ov_depth,), dtype=torch.bfloat16, device=q.device)
                     if out is None else out)
@@ -264,8 +297,14 @@ class DecodePlan:
         self.workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
         self.fn = self.lib.decode_attn_splitk_fused if fused else self.lib.decode_attn_splitk
         self.chunk, self.max_splits = choose_splits(self.prob, num_splits)
-        self._keep = (q, k_cache, v_cache, page_table, seq_lens, k_scale, v_scale)
-        if self.prob.kv_dtype:
+        self._keep = (q, k_cache, v_cache, page_table, seq_lens, k_scale, v_scale, k_rope)
+        if k_rope is not None or (self.prob.kv_dtype and fused):
+            self.fn = self.lib.decode_attn_splitk_kv
+            self.kv = _kv(k_cache, v_cache, k_rope, k_scale, v_scale)
+            self._args = (ctypes.byref(self.prob), _ptr(q), ctypes.byref(self.kv), _ptr(page_table), _ptr(seq_lens),
+                          float(scale), int(num_splits), int(bool(fused)), _ptr(self.out), _ptr(lse), _ptr(o32),
+                          _ptr(self.workspace), self.workspace.numel())
+        elif self.prob.kv_dtype:
             self.fn = self.lib.decode_attn_splitk_fp8
             self._args = (ctypes.byref(self.prob), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
                           _ptr(v_scale), _ptr(page_table), _ptr(seq_lens), float(scale), int(num_splits),

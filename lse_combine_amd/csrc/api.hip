@@ -28,7 +28,7 @@ int ok() {
   return DA_OK;
 }
 
-enum Variant { kVarFma = 0, kVarMfma128 = 1, kVarLatent = 2 };
+enum Variant { kVarFma = 0, kVarMfma = 1, kVarLatent = 2 };
 
 constexpr int kTileKeys = 32;  // key tile of every partition kernel; chunks are multiples of it
 
@@ -79,24 +79,32 @@ int check_problem(const da_problem* p, Variant* var) {
   const int g = p->num_q_heads / p->num_kv_heads;
   const int ql = q_len_of(p);
   if (ql < 1 || ql > 16) return fail(DA_EINVAL, "q_len must be in [0, 16] (got %d)", p->q_len);
-  if (ql > 1) {
-    // several queries per sequence: the matrix-core depth-128 kernel packs q_len x group
-    // (query, head) columns into its 16 MFMA columns
-    if ((p->dtype != DA_BF16 && p->kv_dtype != DA_FP8_E4M3) || p->qk_depth != 128 || p->ov_depth != 128 ||
-        p->v_is_k_prefix || ql * g > 16 || p->kernel == DA_KERNEL_FMA ||
-        (p->page_size > 0 && (p->page_size < kTileKeys || (p->page_size & (p->page_size - 1)))))
+  if (p->kv_dtype != 0 && p->kv_dtype != DA_FP8_E4M3)
+    return fail(DA_EINVAL, "kv_dtype must be 0 or DA_FP8_E4M3 (got %d)", p->kv_dtype);
+  if (p->nope_depth < 0 || (p->nope_depth > 0 && p->nope_depth >= p->qk_depth))
+    return fail(DA_EINVAL, "nope_depth must be 0 (every K column in k_cache) or in [1, qk_depth) (got %d of %d)",
+                p->nope_depth, p->qk_depth);
+  // Features only the matrix-core kernel has: several queries per sequence, fp8 caches,
+  // the wider depth pairs and rotary columns stored apart.
+  const bool d128 = p->qk_depth == 128 && p->ov_depth == 128;
+  const bool wide = (p->qk_depth == 192 && p->ov_depth == 128) || (p->qk_depth == 256 && p->ov_depth == 256);
+  if (ql > 1 || p->kv_dtype == DA_FP8_E4M3 || wide || p->nope_depth > 0) {
+    const bool aligned_pages = p->page_size == 0 || (p->page_size >= kTileKeys && !(p->page_size & (p->page_size - 1)));
+    if (!d128 && !wide)
       return fail(DA_EUNSUPPORTED,
-                  "q_len > 1 is supported on the bf16 (or fp8-cache) depth-128 matrix-core kernel with q_len x group "
-                  "<= 16 and a contiguous cache or pages of a power of two >= 32 keys");
-  }
-  if (p->kv_dtype != 0) {
-    if (p->kv_dtype != DA_FP8_E4M3) return fail(DA_EINVAL, "kv_dtype must be 0 or DA_FP8_E4M3 (got %d)", p->kv_dtype);
-    if (p->dtype != DA_BF16 || p->qk_depth != 128 || p->ov_depth != 128 || p->v_is_k_prefix || g > 16 ||
-        p->kernel == DA_KERNEL_FMA || (p->page_size > 0 && (p->page_size < kTileKeys || (p->page_size & (p->page_size - 1)))))
+                  "several queries per sequence, fp8 caches and rotary columns stored apart are supported at "
+                  "depths (q.K / V) 128/128, 192/128 and 256/256 (got %d/%d)", p->qk_depth, p->ov_depth);
+    if (p->nope_depth > 0 && (d128 || p->qk_depth - p->nope_depth != 64))
+      return fail(DA_EUNSUPPORTED, "rotary columns stored apart: 64 of them at depth 192/128 or 256/256 "
+                                   "(nope_depth 128 or 192; got %d of %d)", p->nope_depth, p->qk_depth);
+    if (p->nope_depth > 0 && p->rope_dtype != DA_BF16)
+      return fail(DA_EUNSUPPORTED, "rotary columns stored apart must be bf16 (rope_dtype %d)", p->rope_dtype);
+    if (p->dtype != DA_BF16 || p->v_is_k_prefix || ql * g > 16 || p->kernel == DA_KERNEL_FMA ||
+        (!aligned_pages && !(d128 && ql == 1 && p->kv_dtype == 0)))
       return fail(DA_EUNSUPPORTED,
-                  "fp8 caches are supported with bf16 q, depth 128/128, group <= 16 (matrix-core kernel), and a "
-                  "contiguous cache or pages of a power of two >= 32 keys");
-    *var = kVarMfma128;
+                  "this problem needs the matrix-core kernel: bf16 q, separate K and V caches, q_len x group <= 16 "
+                  "(q_len %d, group %d), and a contiguous cache or pages of a power of two >= 32 keys", ql, g);
+    *var = kVarMfma;
     return DA_OK;
   }
 
@@ -118,7 +126,7 @@ int check_problem(const da_problem* p, Variant* var) {
   } else if (p->kernel == DA_KERNEL_FMA || (p->kernel == DA_KERNEL_AUTO && g == 1 && ql == 1)) {
     *var = kVarFma;
   } else {
-    *var = kVarMfma128;
+    *var = kVarMfma;
   }
   return DA_OK;
 }
@@ -168,11 +176,11 @@ void share_shape(const da_problem* p, int cus, int* HG, int* KS, int* W) {
 }
 
 // Workgroups of the partition kernel that fit on one compute unit at once.
-int wgs_per_cu(Variant v) { return v == kVarMfma128 ? 1 : 2; }
+int wgs_per_cu(Variant v) { return v == kVarMfma ? 1 : 2; }
 
 int choose(const da_problem* p, Variant var, int32_t num_splits, int cus, int32_t* chunk_out, int32_t* splits_out) {
   if (num_splits < 0) return fail(DA_EINVAL, "num_splits must be >= 0 (0 = automatic)");
-  if (num_splits == 0 && var == kVarMfma128) {
+  if (num_splits == 0 && var == kVarMfma) {
     // automatic on the matrix-core kernel: equal shares of all keys over one workgroup
     // per CU (chunk 0 names this schedule; max_splits = workers)
     int HG, KS, W;
@@ -241,8 +249,8 @@ int32_t* meta_of(const da_problem* p, int32_t max_splits, const float* part_ml) 
 
 int check_split_args(const da_problem* p, Variant var, int32_t chunk, int32_t max_splits) {
   if (chunk == 0) {
-    if (var != kVarMfma128)
-      return fail(DA_EUNSUPPORTED, "chunk_tokens 0 (equal-share schedule) needs the matrix-core depth-128 kernel");
+    if (var != kVarMfma)
+      return fail(DA_EUNSUPPORTED, "chunk_tokens 0 (equal-share schedule) needs the matrix-core kernel");
     if (max_splits < 1 || max_splits > 65535)
       return fail(DA_EINVAL, "equal-share schedule: max_splits (workers) must be in [1, 65535] (got %d)", max_splits);
     return DA_OK;
@@ -273,7 +281,7 @@ int launch_partition(const da_problem* p, Variant var, const da::PartArgs& a, hi
     case kVarFma:
       e = da::launch_partition_fma(a, p->dtype == DA_F32 ? 0 : 1, pm, s);
       break;
-    case kVarMfma128: {
+    case kVarMfma: {
       int HG, KS;
       if (a.workers > 0) {
         int W;
@@ -281,7 +289,7 @@ int launch_partition(const da_problem* p, Variant var, const da::PartArgs& a, hi
       } else {
         mfma_shape(p, a.max_splits, cus, &HG, &KS);
       }
-      e = da::launch_partition_mfma128(a, pm, HG, KS, s);
+      e = da::launch_partition_mfma(a, pm, HG, KS, s);
       break;
     }
     default:
@@ -328,29 +336,51 @@ int check_scale(float scale) {
   return DA_OK;
 }
 
-// fp8 caches come with their K scales through the *_fp8 entry points; the plain entry
-// points (which have no scale arguments) refuse them.
-int check_fp8_args(const da_problem* p, const float* k_scale) {
-  if (p->kv_dtype == DA_FP8_E4M3 && !k_scale)
-    return fail(DA_EINVAL, "fp8 caches need k_scale (use decode_attn_splitk_fp8 / decode_attn_partition_fp8)");
-  if (p->kv_dtype != DA_FP8_E4M3 && k_scale)
+// The cache tensors must match the problem: fp8 caches come with their K scales (the
+// plain entry points, which have no scale arguments, refuse them), and rotary columns
+// stored apart come with their tensor.
+int check_kv_args(const da_problem* p, const da_kv& kv) {
+  if (p->kv_dtype == DA_FP8_E4M3 && !kv.k_scale)
+    return fail(DA_EINVAL, "fp8 caches need k_scale (use decode_attn_splitk_fp8 / decode_attn_splitk_kv)");
+  if (p->kv_dtype != DA_FP8_E4M3 && (kv.k_scale || kv.v_scale))
     return fail(DA_EINVAL, "k_scale / v_scale are for fp8 caches (kv_dtype = DA_FP8_E4M3)");
+  if (p->nope_depth > 0 && !kv.k_rope)
+    return fail(DA_EINVAL, "nope_depth > 0: the rotary columns (k_rope) are needed (use decode_attn_splitk_kv)");
+  if (p->nope_depth == 0 && kv.k_rope) return fail(DA_EINVAL, "k_rope is for nope_depth > 0");
   return DA_OK;
+}
+
+da_kv make_kv(const void* k, const void* v, const float* k_scale = nullptr, const float* v_scale = nullptr) {
+  da_kv kv;
+  kv.k_cache = k;
+  kv.v_cache = v;
+  kv.k_rope = nullptr;
+  kv.k_scale = k_scale;
+  kv.v_scale = v_scale;
+  return kv;
+}
+
+// Cache pointers and the fp8 / rotary-column fields of the kernel arguments.
+void set_kv_args(const da_problem* p, const da_kv& kv, da::PartArgs* a) {
+  a->k_scale = kv.k_scale;
+  a->v_scale = kv.v_scale;
+  a->kv_fp8 = p->kv_dtype == DA_FP8_E4M3;
+  a->k_rope = kv.k_rope;
+  a->Dk = p->nope_depth > 0 ? p->nope_depth : p->qk_depth;
 }
 
 // The whole step. With `fused`, the matrix-core kernel combines in its last-arriving
 // workgroups (no second launch) wherever sequences have few partitions (up to 16, where
 // one workgroup's combine is short); elsewhere, and for the other kernels, the combine
 // is a launch of its own. The results are the same either way.
-int run_splitk(const da_problem* p, const void* q, const void* k_cache, const void* v_cache, const int32_t* page_table,
-               const int32_t* seq_lens, float scale, int32_t num_splits, void* out, float* lse_out, float* o_f32_out,
-               void* workspace, size_t workspace_bytes, void* stream, bool fused, const float* k_scale = nullptr,
-               const float* v_scale = nullptr) {
+int run_splitk(const da_problem* p, const void* q, const da_kv& kv, const int32_t* page_table, const int32_t* seq_lens,
+               float scale, int32_t num_splits, void* out, float* lse_out, float* o_f32_out, void* workspace,
+               size_t workspace_bytes, void* stream, bool fused) {
   Variant var;
   int r = check_problem(p, &var);
   if (r) return r;
-  if ((r = check_fp8_args(p, k_scale))) return r;
-  if ((r = check_inputs(p, q, k_cache, v_cache, page_table, seq_lens))) return r;
+  if ((r = check_kv_args(p, kv))) return r;
+  if ((r = check_inputs(p, q, kv.k_cache, kv.v_cache, page_table, seq_lens))) return r;
   if ((r = check_scale(scale))) return r;
   if (!out) return fail(DA_EINVAL, "out must be non-NULL");
   const int cus = device_num_cus();
@@ -365,7 +395,7 @@ int run_splitk(const da_problem* p, const void* q, const void* k_cache, const vo
   float* pml = (float*)((char*)workspace + ml_off);
   float* po = (float*)((char*)workspace + o_off);
   hipStream_t s = (hipStream_t)stream;
-  da::PartArgs a = da::build_part_args(p, q, k_cache, v_cache, page_table, seq_lens, scale, C, P);
+  da::PartArgs a = da::build_part_args(p, q, kv.k_cache, kv.v_cache, page_table, seq_lens, scale, C, P);
   a.part_o = po;
   a.part_ml = pml;
   if (C == 0) a.meta = meta_of(p, P, pml);
@@ -373,11 +403,9 @@ int run_splitk(const da_problem* p, const void* q, const void* k_cache, const vo
   a.lse = lse_out;
   a.o32 = o_f32_out;
   a.direct_single = 1;
-  a.k_scale = k_scale;
-  a.v_scale = v_scale;
-  a.kv_fp8 = p->kv_dtype == DA_FP8_E4M3;
+  set_kv_args(p, kv, &a);
   const int64_t per_seq = C == 0 ? (int64_t)P / p->batch + 1 : P;
-  const bool fuse = fused && var == kVarMfma128 && per_seq <= 16;
+  const bool fuse = fused && var == kVarMfma && per_seq <= 16;
   if (fuse) a.counters = (int32_t*)((char*)workspace + cnt_off);
   if ((r = launch_partition(p, var, a, s, cus))) return r;
   if (!fuse && (r = launch_combine(p, seq_lens, scale, C, P, po, pml, out, lse_out, o_f32_out, 1, s))) return r;
@@ -407,6 +435,7 @@ PartArgs build_part_args(const da_problem* p, const void* q, const void* k, cons
   a.Hkv = p->num_kv_heads;
   a.g = p->num_q_heads / p->num_kv_heads;
   a.Dqk = p->qk_depth;
+  a.Dk = p->nope_depth > 0 ? p->nope_depth : p->qk_depth;
   a.Dv = p->ov_depth;
   a.v_row_len = p->v_is_k_prefix ? p->qk_depth : p->ov_depth;
   a.page_size = p->page_size;
@@ -460,16 +489,16 @@ int decode_attn_splitk(const da_problem* p, const void* q, const void* k_cache, 
                        const int32_t* page_table, const int32_t* seq_lens, float scale, int32_t num_splits,
                        void* out, float* lse_out, float* o_f32_out, void* workspace, size_t workspace_bytes,
                        void* stream) {
-  return run_splitk(p, q, k_cache, v_cache, page_table, seq_lens, scale, num_splits, out, lse_out, o_f32_out,
-                    workspace, workspace_bytes, stream, false);
+  return run_splitk(p, q, make_kv(k_cache, v_cache), page_table, seq_lens, scale, num_splits, out, lse_out,
+                    o_f32_out, workspace, workspace_bytes, stream, false);
 }
 
 int decode_attn_splitk_fused(const da_problem* p, const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* page_table, const int32_t* seq_lens, float scale, int32_t num_splits,
                              void* out, float* lse_out, float* o_f32_out, void* workspace, size_t workspace_bytes,
                              void* stream) {
-  return run_splitk(p, q, k_cache, v_cache, page_table, seq_lens, scale, num_splits, out, lse_out, o_f32_out,
-                    workspace, workspace_bytes, stream, true);
+  return run_splitk(p, q, make_kv(k_cache, v_cache), page_table, seq_lens, scale, num_splits, out, lse_out,
+                    o_f32_out, workspace, workspace_bytes, stream, true);
 }
 
 int decode_attn_splitk_fp8(const da_problem* p, const void* q, const void* k_cache, const void* v_cache,
@@ -478,12 +507,19 @@ int decode_attn_splitk_fp8(const da_problem* p, const void* q, const void* k_cac
                            float* o_f32_out, void* workspace, size_t workspace_bytes, void* stream) {
   if (!p) return fail(DA_EINVAL, "problem is NULL");
   if (p->kv_dtype != DA_FP8_E4M3) return fail(DA_EINVAL, "decode_attn_splitk_fp8 needs kv_dtype = DA_FP8_E4M3");
-  return run_splitk(p, q, k_cache, v_cache, page_table, seq_lens, scale, num_splits, out, lse_out, o_f32_out,
-                    workspace, workspace_bytes, stream, false, k_scale, v_scale);
+  return run_splitk(p, q, make_kv(k_cache, v_cache, k_scale, v_scale), page_table, seq_lens, scale, num_splits, out,
+                    lse_out, o_f32_out, workspace, workspace_bytes, stream, false);
 }
 
-static int partition_impl(const da_problem* p, const void* q, const void* k_cache, const void* v_cache,
-                          const float* k_scale, const float* v_scale, const int32_t* page_table,
+int decode_attn_splitk_kv(const da_problem* p, const void* q, const da_kv* kv, const int32_t* page_table,
+                          const int32_t* seq_lens, float scale, int32_t num_splits, int32_t fused, void* out,
+                          float* lse_out, float* o_f32_out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!kv) return fail(DA_EINVAL, "kv is NULL");
+  return run_splitk(p, q, *kv, page_table, seq_lens, scale, num_splits, out, lse_out, o_f32_out, workspace,
+                    workspace_bytes, stream, fused != 0);
+}
+
+static int partition_impl(const da_problem* p, const void* q, const da_kv& kv, const int32_t* page_table,
                           const int32_t* seq_lens, float scale, int32_t chunk_tokens, int32_t max_splits,
                           float* part_o, float* part_ml, void* stream);
 
@@ -493,37 +529,42 @@ int decode_attn_partition_fp8(const da_problem* p, const void* q, const void* k_
                               float* part_o, float* part_ml, void* stream) {
   if (!p) return fail(DA_EINVAL, "problem is NULL");
   if (p->kv_dtype != DA_FP8_E4M3) return fail(DA_EINVAL, "decode_attn_partition_fp8 needs kv_dtype = DA_FP8_E4M3");
-  return partition_impl(p, q, k_cache, v_cache, k_scale, v_scale, page_table, seq_lens, scale, chunk_tokens,
-                        max_splits, part_o, part_ml, stream);
+  return partition_impl(p, q, make_kv(k_cache, v_cache, k_scale, v_scale), page_table, seq_lens, scale,
+                        chunk_tokens, max_splits, part_o, part_ml, stream);
 }
 
 int decode_attn_partition(const da_problem* p, const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* page_table, const int32_t* seq_lens, float scale, int32_t chunk_tokens,
                           int32_t max_splits, float* part_o, float* part_ml, void* stream) {
-  return partition_impl(p, q, k_cache, v_cache, nullptr, nullptr, page_table, seq_lens, scale, chunk_tokens,
-                        max_splits, part_o, part_ml, stream);
+  return partition_impl(p, q, make_kv(k_cache, v_cache), page_table, seq_lens, scale, chunk_tokens, max_splits,
+                        part_o, part_ml, stream);
 }
 
-static int partition_impl(const da_problem* p, const void* q, const void* k_cache, const void* v_cache,
-                          const float* k_scale, const float* v_scale, const int32_t* page_table,
+int decode_attn_partition_kv(const da_problem* p, const void* q, const da_kv* kv, const int32_t* page_table,
+                             const int32_t* seq_lens, float scale, int32_t chunk_tokens, int32_t max_splits,
+                             float* part_o, float* part_ml, void* stream) {
+  if (!kv) return fail(DA_EINVAL, "kv is NULL");
+  return partition_impl(p, q, *kv, page_table, seq_lens, scale, chunk_tokens, max_splits, part_o, part_ml, stream);
+}
+
+static int partition_impl(const da_problem* p, const void* q, const da_kv& kv, const int32_t* page_table,
                           const int32_t* seq_lens, float scale, int32_t chunk_tokens, int32_t max_splits,
                           float* part_o, float* part_ml, void* stream) {
   Variant var;
   int r = check_problem(p, &var);
   if (r) return r;
-  if ((r = check_fp8_args(p, k_scale))) return r;
-  if ((r = check_inputs(p, q, k_cache, v_cache, page_table, seq_lens))) return r;
+  if ((r = check_kv_args(p, kv))) return r;
+  if ((r = check_inputs(p, q, kv.k_cache, kv.v_cache, page_table, seq_lens))) return r;
   if ((r = check_scale(scale))) return r;
   if ((r = check_split_args(p, var, chunk_tokens, max_splits))) return r;
   if (!part_o || !part_ml) return fail(DA_EINVAL, "part_o and part_ml must be non-NULL");
-  da::PartArgs a = da::build_part_args(p, q, k_cache, v_cache, page_table, seq_lens, scale, chunk_tokens, max_splits);
+  da::PartArgs a =
+      da::build_part_args(p, q, kv.k_cache, kv.v_cache, page_table, seq_lens, scale, chunk_tokens, max_splits);
   a.part_o = part_o;
   a.part_ml = part_ml;
   if (chunk_tokens == 0) a.meta = meta_of(p, max_splits, part_ml);
   a.direct_single = 0;
-  a.k_scale = k_scale;
-  a.v_scale = v_scale;
-  a.kv_fp8 = p->kv_dtype == DA_FP8_E4M3;
+  set_kv_args(p, kv, &a);
   if ((r = launch_partition(p, var, a, (hipStream_t)stream, device_num_cus()))) return r;
   return ok();
 }
@@ -534,8 +575,8 @@ int decode_attn_combine(const da_problem* p, const int32_t* seq_lens, float scal
   Variant var = kVarFma;
   int r = check_problem(p, &var);
   if (r && r != DA_EUNSUPPORTED) return r;
-  if (p->ov_depth != 128 && p->ov_depth != 512)
-    return fail(DA_EUNSUPPORTED, "combine supports ov_depth 128 or 512 (got %d)", p->ov_depth);
+  if (p->ov_depth != 128 && p->ov_depth != 256 && p->ov_depth != 512)
+    return fail(DA_EUNSUPPORTED, "combine supports ov_depth 128, 256 or 512 (got %d)", p->ov_depth);
   if (!seq_lens || !part_o || !part_ml || !out) return fail(DA_EINVAL, "seq_lens, part_o, part_ml and out must be non-NULL");
   if ((r = check_scale(scale))) return r;
   if ((r = check_split_args(p, var, chunk_tokens, max_splits))) return r;

@@ -132,6 +132,15 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
       case 4: go(combine_kernel<128, 4>, 2); break;
       default: go(combine_kernel<128, 8>, 1); break;
     }
+  } else if (a.Dv == 256) {
+    auto go = [&](auto kern, int rpb) {
+      hipLaunchKernelGGL(kern, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(kCombineThreads), 0, s, a);
+    };
+    switch (S) {
+      case 1: go(combine_kernel<256, 1>, 4); break;
+      case 2: go(combine_kernel<256, 2>, 2); break;
+      default: go(combine_kernel<256, 4>, 1); break;
+    }
   } else {
     if (S == 1)
       hipLaunchKernelGGL((combine_kernel<512, 1>), dim3((unsigned)((rows + 1) / 2)), dim3(kCombineThreads), 0, s, a);

@@ -17,7 +17,8 @@ enum PageMode : int {
 // Everything the partition kernels need; passed by value as the kernel argument.
 struct PartArgs {
   const void* q;            // [B][q_len][heads][Dqk] = [B][Hq][Dqk]
-  const void* k;            // cache rows of Dqk elements, see key_row()
+  const void* k;            // cache rows of Dk elements, see key_row()
+  const void* k_rope;       // rotary columns stored apart: rows of Dqk - Dk bf16 elements (or NULL)
   const void* v;            // cache rows of v_row_len elements (== k when V is a K prefix)
   const int32_t* page_table;
   const int32_t* seq_lens;
@@ -33,6 +34,7 @@ struct PartArgs {
   float* lse;               // optional
   float* o32;               // optional
   int32_t B, Hq, Hkv, g, Dqk, Dv;   // Hq: rows per sequence (q_len x heads)
+  int32_t Dk;                       // K cache columns (Dqk, or the nope part when k_rope)
   int32_t Hq1, q_len;               // heads; queries per sequence (>= 1)
   int32_t v_row_len;        // elements between consecutive (row, kv-head) V vectors / Hkv
   int32_t page_size, pt_stride, num_pages, kv_capacity, max_seq_len;
@@ -71,8 +73,14 @@ PartArgs build_part_args(const ::da_problem* p, const void* q, const void* k, co
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_partition_fma(const PartArgs& a, int dtype, int page_mode, hipStream_t s);
-hipError_t launch_partition_mfma128(const PartArgs& a, int page_mode, int kv_heads_per_wg, int key_splits,
-                                    hipStream_t s);
+// matrix-core kernel: dispatch over the depth shapes (partition_mfma128.hip), and the
+// wider shapes' own translation units
+hipError_t launch_partition_mfma(const PartArgs& a, int page_mode, int kv_heads_per_wg, int key_splits,
+                                 hipStream_t s);
+hipError_t launch_partition_mfma_d192(const PartArgs& a, int page_mode, int kv_heads_per_wg, int key_splits,
+                                      hipStream_t s);
+hipError_t launch_partition_mfma_d256(const PartArgs& a, int page_mode, int kv_heads_per_wg, int key_splits,
+                                      hipStream_t s);
 hipError_t launch_partition_latent(const PartArgs& a, int page_mode, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_read_probe(const void* src, size_t n_bytes, float* sink, hipStream_t s);

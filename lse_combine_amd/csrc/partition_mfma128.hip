@@ -1,828 +1,15 @@
-// Split-K pass 1 on the matrix cores for bf16 caches with Dqk = Dv = 128 and a GQA
-// group of up to 16 q heads per kv head (FA4Config: fused GQA tiles, BM_eff).
-//
-// Work decomposition. A workgroup covers one partition p of one sequence b for HG
-// kv heads, with KS waves per kv head splitting the partition's keys (NW = HG * KS
-// <= 16 waves). Wave w serves kv head kg*HG + w % HG and takes the 32-key tiles
-// ks, ks + KS, ... (ks = w / HG). With HG = 8 the waves of a workgroup read the
-// eight 256-byte kv-head slices of the same tokens, i.e. whole 2 KB token rows of
-// the paged cache; HG shrinks when that would leave too few workgroups for the chip.
-//
-// Per tile, with v_mfma_f32_16x16x32_bf16:
-//   S^T[key][col] = K[key][:] . q[col][:]      A = K rows, 16-byte loads that land
-//                                              directly in the A-operand layout,
-//                                              B = q (16 columns, see below)
-//   p = exp2((x - m_new) * c)                  online softmax in fp32; a lane owns one
-//                                              column and 8 keys, so the tile max needs
-//                                              two cross-lane steps
-//   O^T[d][col] += V^T[d][key] . P^T[key][col] A = V^T read from LDS with the gfx950
-//                                              transposing read ds_read_b64_tr_b16,
-//                                              B = P^T straight from the S^T registers
-//
-// P must not be rounded to bf16 before P.V (the fp32 O must stay within 1e-5), so it
-// is split as p = hi + lo, hi = bf16(p), lo = bf16(p - hi) (about 16 significant
-// bits). When g <= 8 the 16 MFMA columns hold the g heads twice: columns 0-7 carry hi
-// and 8-15 carry lo (their scores are equal), so hi and lo cost one MFMA and the two
-// column halves of O^T are added at the end. For 8 < g <= 16 a second MFMA per depth
-// block adds the lo part.
-//
-// Addressing: tiles are 32 keys and partitions start on multiples of 32, so with a
-// contiguous cache or pages of a power of two >= 32 keys a tile is 32 consecutive cache
-// rows: the tile base is a scalar and every lane adds a fixed 32-bit offset. The page
-// indices of the partition are staged in LDS once, so no dependent page-table load
-// sits between consecutive prefetches. One register tile per wave: the next tile's K
-// and V (16 KB per wave) are requested once the current tile sits in LDS and in the
-// score MFMAs, so they are in flight during its softmax and P.V; the small register
-// footprint lets three waves share a SIMD.
-//
-// Epilogue: with KS = 1 every wave stores its own normalised partial and (m, l)
-// (fa4_splitk_combine_write, second paragraph), or the finished bf16 row when the
-// sequence has a single partition. With KS > 1 the waves of a kv head first merge
-// their (m, l, O) through LDS with the log-sum-exp weights (fa4_lse_combine_write:
-// fragments merged with per-row scales).
-#include "da_device.h"
+// Matrix-core partition kernel, depth 128/128 (q.K and V), bf16 or fp8 caches, and the
+// dispatch over the depth shapes of the same kernel (the wider shapes live in their own
+// translation units so that they compile in parallel).
+#include "partition_mfma.h"
 
 namespace da {
-namespace {
 
-constexpr int kD = 128;
-constexpr int kTile = 32;
-constexpr int kMaxWaves = 8;
-constexpr int kVBytes = kTile * kD * 2;       // one wave's V tile in LDS
-constexpr int kWaveBytes = kVBytes + 256;     // + merge (m, l) for up to 16 heads
-constexpr int kMaxLdsPages = 512;             // page indices of one segment staged in LDS
-
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-
-// Buffer-resource dword 3 for raw (untyped) dword loads on gfx9-family parts.
-constexpr int kRsrcWord3 = 0x00020000;
-// Cache policy of the K/V loads: non-temporal (each byte is read once per step).
-constexpr int kLoadNT = 2;
-
-__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kLoadNT));
-}
-
-struct KTile {
-  u32x4 k[2][4];  // K rows: [key block][depth step], 8 bf16 each
-};
-
-// Wait until at most n vector-memory operations of this wave are outstanding
-// (s_waitcnt vmcnt(n), other counters untouched); n < 16. The compiler fences keep
-// the LDS reads that depend on a direct-to-LDS load after the wait.
-__device__ __forceinline__ void wait_vm(int n) {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  if (n == 0) __builtin_amdgcn_s_waitcnt(0x0F70);
-  else __builtin_amdgcn_s_waitcnt(0x0F70 | 8);   // only 0 and 8 are used
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-// Four E4M3 codes (one dword, byte 0 first) as two packed bf16 pairs, through the
-// hardware fp8 -> fp32 conversion (OCP E4M3; exact, as is the fp32 -> bf16 step).
-__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
-  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-  u32x2 r;
-  r[0] = pack_bf16x2(lo[0], lo[1]);
-  r[1] = pack_bf16x2(hi[0], hi[1]);
-  return r;
-}
-
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
-  const u32x2 a = fp8x4_to_bf16x4(w0), b = fp8x4_to_bf16x4(w1);
-  return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
-}
-
-// max over the four lanes n, n+16, n+32, n+48 (the four key groups of a column).
-// (v_permlane32_swap / v_permlane16_swap would do this on the VALU, but this compiler
-// folds the two results of a swap of a value with itself into one, losing half the
-// lanes; the LDS permute is used instead.)
-__device__ __forceinline__ float max_over_key_groups(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
-}
-
-// Zero a wave's V tile once per launch: direct-to-LDS loads outside the buffer range
-// leave their rows untouched, and those rows must hold finite values (they meet p = 0).
-__device__ __forceinline__ void zero_v_tile(char* vt, int lane) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) *(u32x4*)(vt + (i * 64 + lane) * 16) = u32x4{0u, 0u, 0u, 0u};
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the zeros are in place before any load lands
-}
-
-// Per-wave constants of a workgroup: its place in the (kv head, key split) grid and the
-// lane's MFMA coordinates.
-struct WaveInfo {
-  int HG, KS, NW, w, ks, kvh, lane, n, qd, hc;
-  int qi, hh;   // the (query, head-in-group) pair of this lane's MFMA column
-  bool wave_active, col_valid, is_lo;
-};
-
-// KS > 1: merge the key splits of each kv head through LDS (each wave reuses its own V
-// region; waves that saw no tile hold m = -inf, l = 0, O = 0 and get weight 0), with the
-// log-sum-exp weights of the two-fragment combine (fa4_lse_combine_write).
-template <bool HL>
-__device__ __forceinline__ void merge_key_splits(const PartArgs& a, const WaveInfo& wv, char* smem, int b, int p,
-                                                 bool direct, const f32x4* o, float m_run, float l_run) {
-  const int tid = threadIdx.x, NW = wv.NW, HG = wv.HG, KS = wv.KS, kg = blockIdx.y;
-  const int hc = wv.hc, qd = wv.qd, g = a.g;
-  const bool col_valid = wv.col_valid, is_lo = wv.is_lo;
-  const float c = a.c;
-  char* vt = smem + wv.w * kWaveBytes;
-  float* mo = (float*)vt;                      // [16][128] O of this wave
-  float* mml = (float*)(vt + kVBytes);         // m[16], l[16]
-  __syncthreads();
-  if (col_valid && !is_lo) {
-#pragma unroll
-    for (int db = 0; db < 8; ++db) *(f32x4*)(mo + hc * kD + 16 * db + 4 * qd) = o[db];
-    if (qd == 0) {
-      mml[hc] = m_run;
-      mml[16 + hc] = l_run;
-    }
-  }
-  __syncthreads();
-  constexpr int kUnits = kD / 4;
-  const int cols = a.q_len * g;   // (query, head) columns per kv head
-  const int units = HG * cols * kUnits;
-  for (int u = tid; u < units; u += NW * 64) {
-    const int mem = u / (cols * kUnits);
-    const int h = (u / kUnits) % cols, d0 = (u % kUnits) * 4;
-    const int kv2 = kg * HG + mem;
-    if (kv2 >= a.Hkv) continue;
-    // (a split that saw no key of this column holds l = 0 and weighs nothing)
-    float M = -INFINITY;
-    for (int s2 = 0; s2 < KS; ++s2) {
-      const float* ml = (const float*)(smem + (s2 * HG + mem) * kWaveBytes + kVBytes);
-      if (ml[16 + h] > 0.f) M = fmaxf(M, ml[h]);
-    }
-    float Ls = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s2 = 0; s2 < KS; ++s2) {
-      const char* reg = smem + (s2 * HG + mem) * kWaveBytes;
-      const float* ml = (const float*)(reg + kVBytes);
-      if (ml[16 + h] > 0.f) {
-        const float e = exp2_fast((ml[h] - M) * c);
-        Ls = fmaf(ml[16 + h], e, Ls);
-        acc += e * *(const f32x4*)((const float*)reg + h * kD + d0);
-      }
-    }
-    const int row = (h / g) * a.Hq1 + kv2 * g + h % g;
-    store_unit(a, b, row, p, direct, d0, acc * (Ls > 0.f ? 1.f / Ls : 0.f), M, Ls, d0 == 0);
-  }
-  // the merge read other waves' V tiles: the next piece may refill them only after this
-  __syncthreads();
-}
-
-// Last-arriving-workgroup combine (fa4_splitk_combine_write, fourth paragraph: the writer
-// that completes the set combines all). After storing its partial, every workgroup of a
-// (sequence, kv-head group) publishes it device-wide (agent-scope release) and counts
-// itself in; the one that brings the count to the number of partitions acquires the
-// others' partials and writes the final bf16 rows, LSE and fp32 O of the group's heads,
-// then returns the counter to zero for the next call. The counters (one int per
-// (sequence, group)) must be zero before the first call.
-__device__ __forceinline__ void fused_combine(const PartArgs& a, const WaveInfo& wv, int* flag_s, int b, int count,
-                                              int first_slot) {
-  const int tid = threadIdx.x, kg = blockIdx.y, HG = wv.HG, g = a.g;
-  // The barrier completes every wave's partial stores; one thread then releases them at
-  // device scope (on this chip a write-back of the XCD's L2, so once per workgroup rather
-  // than once per wave), counts in, and, if last, acquires the others' partials.
-  __syncthreads();
-  int* cnt = a.counters + (int64_t)b * gridDim.y + kg;
-  if (tid == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const int last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == count - 1;
-    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    *flag_s = last ? 1 : 0;
-  }
-  __syncthreads();
-  if (!__builtin_amdgcn_readfirstlane(*flag_s)) return;
-  const int kv_end = min((kg + 1) * HG, a.Hkv);
-  const int cols = a.q_len * g, ncol = (kv_end - kg * HG) * cols;
-  constexpr int kUnits = kD / 4;
-  for (int u = tid; u < ncol * kUnits; u += wv.NW * 64) {
-    const int cc = u / kUnits, d0 = (u % kUnits) * 4;
-    const int kv = kg * HG + cc / cols, col = cc % cols;
-    const int h = (col / g) * a.Hq1 + kv * g + col % g;   // row within the sequence
-    const int64_t row = (int64_t)b * a.Hq + h;
-    // partial rows of this head: equal shares [slot][Hq], fixed chunks [B][Hq][max_splits]
-    const int64_t first = first_slot >= 0 ? (int64_t)first_slot * a.Hq + h : row * a.max_splits;
-    const int64_t stride = first_slot >= 0 ? a.Hq : 1;
-    float M = -INFINITY, Ls = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    fold_partials<kD>((const float2*)a.part_ml + first, a.part_o + first * kD + d0, stride, count, 0, 1, a.c, M,
-                      Ls, acc);
-    write_row_unit(a.out, a.o32, a.lse, row, kD, d0, M, Ls, acc, a.scale);
-  }
-  if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// One piece of work: keys [start, end) of sequence b for this workgroup's kv heads.
-// Writes the normalised partial and (m, l) of partition / slot p, or the finished bf16
-// row when `direct` (the sequence has a single partition).
-template <bool HL, int PM, bool F8>
-__device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv, char* smem, int* pages_s,
-                                          int* flag_s, int b, int start, int end, int p, int count,
-                                          int first_slot) {
-  // (count = partitions of sequence b; first_slot = its first slot under equal shares, or -1)
-  const bool direct = a.direct_single && count == 1;
-  const int lane = wv.lane, n = wv.n, qd = wv.qd, hc = wv.hc, kvh = wv.kvh, ks = wv.ks, KS = wv.KS;
-  const int g = a.g;
-  const bool wave_active = wv.wave_active, col_valid = wv.col_valid, is_lo = wv.is_lo;
-  const float lo_mask = is_lo ? 1.f : 0.f;
-  char* vt = smem + wv.w * kWaveBytes;
-  int first_page = 0;   // page index held by pages_s[0] in the current segment
-  // keys this lane's column attends: query qi of q_len sees keys t < L - q_len + 1 + qi
-  const int L_seq = __builtin_amdgcn_readfirstlane(attended_len(a, b, PM == kContiguous));
-  const int col_end = min(end, L_seq - a.q_len + 1 + wv.qi);
-
-  // q as the B operand of S^T = K q^T: column n; MFMA step j covers depth 32j + 8qd .. +8
-  // (bf16 caches) or, matching the 16-value fp8 loads of K, depth 16(qd + 4(j/2)) + 8(j%2) .. +8
-  // (the order of the depth sum is free as long as q and K agree).
-  bf16x8 qf[4];
-  {
-    const int kv_safe = wave_active ? kvh : 0;
-    const uint16_t* qrow = (const uint16_t*)a.q +
-                           ((int64_t)b * a.Hq + (int64_t)wv.qi * a.Hq1 + (int64_t)kv_safe * g + wv.hh) * kD;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d0 = F8 ? 16 * (qd + 4 * (j >> 1)) + 8 * (j & 1) : 32 * j + 8 * qd;
-      u32x4 v = *(const u32x4*)(qrow + d0);
-      if (!col_valid) v = u32x4{0u, 0u, 0u, 0u};
-      qf[j] = as_bf16x8(v);
-    }
-  }
-
-  const char* kc = (const char*)a.k;
-  const char* vc = (const char*)a.v;
-  constexpr uint32_t es = F8 ? 1 : 2;                              // bytes per cache element
-  const uint32_t krow_bytes = (uint32_t)a.Hkv * kD * es;          // bytes between tokens (K)
-  const uint32_t vrow_bytes = (uint32_t)a.Hkv * a.v_row_len * es; // bytes between tokens (V)
-  const uint32_t kslice = (uint32_t)(wave_active ? kvh : 0) * kD * es;
-  const uint32_t vslice = (uint32_t)(wave_active ? kvh : 0) * a.v_row_len * es;
-  const float c = a.c;
-
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 o[8];
-#pragma unroll
-  for (int db = 0; db < 8; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int tid = threadIdx.x, NW = wv.NW, HG = wv.HG, kg = blockIdx.y;
-  // first cache row of the tile starting at t0 (contiguous / aligned pages: the tile
-  // is 32 consecutive rows), and the row of key t in the general paged case
-  auto tile_row0 = [&](int t0) -> int64_t {
-    if constexpr (PM == kContiguous) {
-      return (int64_t)b * a.kv_capacity + t0;
-    } else {
-      const int pi = t0 >> a.page_shift;   // pages are a power of two >= 32 keys
-      // an LDS value read at a uniform address: tell the compiler it is uniform; index and
-      // value are clamped so that no cache address can leave the page pool
-      const int slot = min(max(pi - first_page, 0), kMaxLdsPages - 1);
-      // (clamped before readfirstlane: a clamp after it may be done in vector registers,
-      // which makes the descriptor divergent and every load a waterfall loop)
-      const int page = __builtin_amdgcn_readfirstlane(min(max(pages_s[slot], 0), a.num_pages - 1));
-      return ((int64_t)page << a.page_shift) + (t0 & (a.page_size - 1));
-    }
-  };
-  auto general_row = [&](int t) -> int64_t {
-    const int pi = t / a.page_size;
-    const int slot = min(max(pi - first_page, 0), kMaxLdsPages - 1);
-    const int page = min(max(pages_s[slot], 0), a.num_pages - 1);
-    return (int64_t)page * a.page_size + (t - pi * a.page_size);
-  };
-
-  // Per-lane byte offset of K inside a 16-row half tile: key n, 16-byte depth chunk qd
-  // (+64 bytes per MFMA step, an immediate).
-  const uint32_t koff = (uint32_t)n * krow_bytes + 16 * qd;
-
-  // K of the tile at t0 into registers (A operand of the score MFMAs).
-  auto load_k = [&](KTile& T, int t0) {
-    const int last = min(kTile - 1, end - 1 - t0);
-    if constexpr (PM != kPagedGeneral) {
-      // The tile is 32 consecutive cache rows: a scalar base per 16-row half. Each half's
-      // buffer range covers only its valid rows, so on a ragged last tile the loads of
-      // missing keys return zeros without touching memory (their scores are masked).
-      const int64_t row0 = tile_row0(t0);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        // (the clamp is selected as a vector op; readfirstlane keeps the descriptor scalar)
-        const int rows = __builtin_amdgcn_readfirstlane(min(max(last + 1 - 16 * h, 0), 16));
-        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(kc + (row0 + 16 * h) * krow_bytes + kslice), 0, rows * krow_bytes, kRsrcWord3);
-        if constexpr (F8) {
-          // 16 fp8 values per load: depth chunks qd and qd + 4 of the 128-byte row slice
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj) T.k[h][jj] = buf_load16(rk, koff + 64 * jj, 0);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) T.k[h][j] = buf_load16(rk, koff + 64 * j, 0);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        const char* kp = kc + general_row(t0 + min(n + 16 * blk, last)) * krow_bytes + kslice + 16 * qd;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) T.k[blk][j] = __builtin_nontemporal_load((const u32x4*)(kp + 64 * j));
-      }
-    }
-  };
-
-  // V of the tile at t0 straight into this wave's LDS tile (8 direct-to-LDS 16-byte loads,
-  // 1 KB each: load i fills stage rows 4i..4i+3, lane (qd, n) writes row 4i + qd, chunk
-  // slot n with the swizzled source chunk n ^ (row & 15)). Rows past the end of a ragged
-  // tile are outside the buffer range and deliver zeros.
-  auto load_v = [&](int t0) {
-    const int last = min(kTile - 1, end - 1 - t0);
-    if constexpr (PM != kPagedGeneral) {
-      const int64_t row0 = tile_row0(t0);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int rows = __builtin_amdgcn_readfirstlane(min(max(last + 1 - 16 * h, 0), 16));
-        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(vc + (row0 + 16 * h) * vrow_bytes + vslice), 0, rows * vrow_bytes, kRsrcWord3);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * i + qd;   // row within the half; the swizzle repeats per half
-          const uint32_t voff = (uint32_t)r * vrow_bytes + 16 * (n ^ (r & 15));
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (DA_LDS void*)(vt + (4 * h + i) * 1024), 16, voff, 0, 0,
-                                                   kLoadNT);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = 4 * i + qd;
-        const char* vp = vc + general_row(t0 + min(r, last)) * vrow_bytes + vslice + 16 * (n ^ (r & 15));
-        __builtin_amdgcn_global_load_lds((const void*)vp, (DA_LDS void*)(vt + i * 1024), 16, 0, 0);
-      }
-    }
-  };
-
-  // phase A: S^T = K q^T for keys 0-15 and 16-31; afterwards the K registers are free
-  auto score = [&](const KTile& T, f32x4* s) {
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      s[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // fp8 K: the 8 values of step j are dwords 2(j%2), 2(j%2)+1 of load j/2, widened
-        // exactly to bf16 (every E4M3 value is a bf16 value)
-        const bf16x8 kf = F8 ? fp8x8_to_bf16x8(T.k[blk][j >> 1][2 * (j & 1)], T.k[blk][j >> 1][2 * (j & 1) + 1])
-                             : as_bf16x8(T.k[blk][j]);
-        s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[j], s[blk], 0, 0, 0);
-      }
-    }
-  };
-
-  // per-token scales of the tile's keys that this lane holds (fp8 caches): keys
-  // 4qd .. 4qd+3 and 16+4qd .. 16+4qd+3, 16 contiguous bytes each in the tokens-innermost
-  // scale layout; missing keys of a ragged tile read 0 (their scores are masked anyway)
-  auto load_sc = [&](f32x4* ksc, f32x4* vsc, int t0) {
-    const int last = min(kTile - 1, end - 1 - t0);
-    const int kv_safe = wave_active ? kvh : 0;
-    int64_t base;
-    if constexpr (PM == kContiguous) {
-      base = ((int64_t)b * a.Hkv + kv_safe) * a.kv_capacity + t0;
-    } else {
-      const int slot = min(max((t0 >> a.page_shift) - first_page, 0), kMaxLdsPages - 1);
-      const int page = __builtin_amdgcn_readfirstlane(min(max(pages_s[slot], 0), a.num_pages - 1));
-      base = ((int64_t)page * a.Hkv + kv_safe) * a.page_size + (t0 & (a.page_size - 1));
-    }
-    const int nk = __builtin_amdgcn_readfirstlane(max(last + 1, 0));
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(a.k_scale + base), 0, nk * 4, kRsrcWord3);
-    ksc[0] = __builtin_bit_cast(f32x4, buf_load16(rk, 16 * qd, 0));
-    ksc[1] = __builtin_bit_cast(f32x4, buf_load16(rk, 64 + 16 * qd, 0));
-    if (a.v_scale) {
-      const __amdgpu_buffer_rsrc_t rv =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(a.v_scale + base), 0, nk * 4, kRsrcWord3);
-      vsc[0] = __builtin_bit_cast(f32x4, buf_load16(rv, 16 * qd, 0));
-      vsc[1] = __builtin_bit_cast(f32x4, buf_load16(rv, 64 + 16 * qd, 0));
-    } else {
-      vsc[0] = vsc[1] = f32x4{1.f, 1.f, 1.f, 1.f};
-    }
-  };
-
-  // fp8 V: the tile's 32 rows into registers (lane l: row l/2, 64-byte half l%2), then
-  // widened to bf16 and written to this wave's LDS tile in the swizzled layout that the
-  // transposing reads expect (source chunk c of row r at slot c ^ (r & 15))
-  auto load_v8 = [&](u32x4* vr, int t0) {
-    const int last = min(kTile - 1, end - 1 - t0);
-    const int64_t row0 = tile_row0(t0);
-    const int rows = __builtin_amdgcn_readfirstlane(max(last + 1, 0));
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(vc + row0 * vrow_bytes + vslice), 0, rows * vrow_bytes, kRsrcWord3);
-    const uint32_t off = (uint32_t)(lane >> 1) * vrow_bytes + 64 * (lane & 1);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) vr[m] = buf_load16(rv, off + 16 * m, 0);
-  };
-  auto stage_v8 = [&](const u32x4* vr) {
-    const int r = lane >> 1;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int c0 = 8 * (lane & 1) + 2 * m;
-      *(bf16x8*)(vt + r * 256 + ((c0 ^ (r & 15)) << 4)) = fp8x8_to_bf16x8(vr[m][0], vr[m][1]);
-      *(bf16x8*)(vt + r * 256 + (((c0 + 1) ^ (r & 15)) << 4)) = fp8x8_to_bf16x8(vr[m][2], vr[m][3]);
-    }
-  };
-
-  // phase B: online softmax, giving P^T as the B operand of P.V. On a ragged tile the
-  // scores of missing keys are set to -inf first; exp2(-inf) = 0 then removes them from
-  // the sums. With fp8 caches the scores take the K scales of their keys first, and the
-  // V scales multiply p in the P.V operand only (l sums the unscaled p).
-  auto softmax_p = [&](f32x4* s, int t0, bf16x8& pb_hi, bf16x8& pb_lo, const f32x4* ksc, const f32x4* vsc) {
-    if constexpr (F8) {
-      s[0] *= ksc[0];
-      s[1] *= ksc[1];
-    }
-    const int nvalid = col_end - t0;   // this column's keys in the tile (may be <= 0)
-    if (__ballot(nvalid < kTile)) {
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (16 * blk + 4 * qd + i >= nvalid) s[blk][i] = -INFINITY;
-    }
-    // online softmax: this lane holds keys 16*blk + 4*qd + i of column n
-    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    mx = max_over_key_groups(mx);
-    const float mn = fmaxf(m_run, mx);
-    // (a column that has seen no key yet keeps m = -inf; its p and l stay 0)
-    const float mref = mn == -INFINITY ? 0.f : mn;
-    const float alpha = exp2_fast((m_run - mref) * c);
-    const float mc = mref * c;
-    float pr[2][4];
-    float psum = 0.f;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pr[blk][i] = exp2_fast(fmaf(s[blk][i], c, -mc));
-        psum += pr[blk][i];
-      }
-    l_run = fmaf(l_run, alpha, psum);
-    m_run = mn;
-    // the running max rarely moves once a few tiles are in: skip the rescale then
-    if (__ballot(alpha != 1.f)) {
-#pragma unroll
-      for (int db = 0; db < 8; ++db) o[db] *= alpha;
-    }
-
-    // P^T as the B operand: k-slots 0-3 = keys 4qd..+3, 4-7 = keys 16+4qd..+3.
-    // hi columns take bf16(p); lo columns take bf16(p - float(bf16(p))).
-    uint32_t pw[4], lw[4];
-#pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) {
-      const int blk = s2 >> 1, i0 = (s2 & 1) * 2;
-      const float p0 = F8 ? pr[blk][i0] * vsc[blk][i0] : pr[blk][i0];
-      const float p1 = F8 ? pr[blk][i0 + 1] * vsc[blk][i0 + 1] : pr[blk][i0 + 1];
-      const uint32_t h = pack_bf16x2(p0, p1);
-      if constexpr (HL) {
-        pw[s2] = pack_bf16x2(fmaf(-lo_mask, bf16lo(h), p0), fmaf(-lo_mask, bf16hi(h), p1));
-      } else {
-        pw[s2] = h;
-        lw[s2] = pack_bf16x2(p0 - bf16lo(h), p1 - bf16hi(h));
-      }
-    }
-    pb_hi = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
-    if constexpr (!HL) pb_lo = as_bf16x8(u32x4{lw[0], lw[1], lw[2], lw[3]});
-  };
-
-  // phase C: O^T += V^T P^T, V^T read transposed from the LDS tile
-  auto pv = [&](const bf16x8& pb_hi, const bf16x8& pb_lo) {
-    // V^T A operand: lane (n, qd) gets depth 16db + n of keys 4qd..+3 and 16+4qd..+3
-    const int r0 = 4 * qd + (n >> 2);
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const int ch = 2 * db + ((n & 3) >> 1);
-      const int sub = (n & 1) * 8;
-      const int ra = r0, rb = r0 + 16;
-      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (s16x4 DA_LDS*)(vt + ra * 256 + ((ch ^ (ra & 15)) << 4) + sub));
-      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (s16x4 DA_LDS*)(vt + rb * 256 + ((ch ^ (rb & 15)) << 4) + sub));
-      s16x8 v8;
-      v8[0] = va[0]; v8[1] = va[1]; v8[2] = va[2]; v8[3] = va[3];
-      v8[4] = vb[0]; v8[5] = vb[1]; v8[6] = vb[2]; v8[7] = vb[3];
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, v8);
-      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb_hi, o[db], 0, 0, 0);
-      if constexpr (!HL) o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb_lo, o[db], 0, 0, 0);
-    }
-  };
-
-  // Segments: the page indices of up to kMaxLdsPages pages are staged in LDS at a time
-  // (one segment for every page size >= 32 with chunks up to 16K keys).
-  int seg_len = end - start;
-  if constexpr (PM != kContiguous) {
-    const int cap = ((kMaxLdsPages - 1) * a.page_size) / kTile * kTile;
-    seg_len = min(seg_len, cap);
-  }
-  for (int s0 = start; s0 < end; s0 += seg_len) {
-    const int s1 = min(s0 + seg_len, end);
-    if constexpr (PM != kContiguous) {
-      __syncthreads();
-      first_page = s0 / a.page_size;
-      const int n_pages = (s1 - 1) / a.page_size - first_page + 1;
-      const int32_t* pt = a.page_table + (int64_t)b * a.pt_stride + first_page;
-      for (int i = tid; i < n_pages; i += NW * 64) {
-        const int page = pt[i];
-        pages_s[i] = page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
-      }
-      __syncthreads();
-    }
-    const int n_tiles = (s1 - s0 + kTile - 1) / kTile;
-    if (wave_active && ks < n_tiles) {
-      // One tile buffer: the next tile's K and V (16 KB per wave) are requested as soon
-      // as the current tile has been moved to LDS and into the score MFMAs, and stay in
-      // flight through the softmax and P.V of the current tile.
-      KTile T;
-      if constexpr (F8) {
-        // fp8: K, V and the scales of the next tile are in flight (in registers) through
-        // the softmax and P.V of the current one. (Two tiles in flight measured slower:
-        // this path is bound by the per-tile instruction chain, not by memory latency.)
-        u32x4 vr[4];
-        f32x4 ksc[2], vsc[2];
-        load_k(T, s0 + ks * kTile);
-        load_v8(vr, s0 + ks * kTile);
-        load_sc(ksc, vsc, s0 + ks * kTile);
-        for (int it = ks; it < n_tiles; it += KS) {
-          const bool has_next = it + KS < n_tiles;
-          const int tn = s0 + (it + KS) * kTile;
-          f32x4 s[2];
-          score(T, s);
-          if (has_next) load_k(T, tn);
-          stage_v8(vr);
-          bf16x8 pb_hi, pb_lo;
-          softmax_p(s, s0 + it * kTile, pb_hi, pb_lo, ksc, vsc);
-          if (has_next) {
-            load_v8(vr, tn);
-            load_sc(ksc, vsc, tn);
-          }
-          pv(pb_hi, pb_lo);
-        }
-      } else {
-        load_k(T, s0 + ks * kTile);
-        load_v(s0 + ks * kTile);
-        for (int it = ks; it < n_tiles; it += KS) {
-          const bool has_next = it + KS < n_tiles;
-          f32x4 s[2];
-          score(T, s);
-          if (has_next) load_k(T, s0 + (it + KS) * kTile);
-          bf16x8 pb_hi, pb_lo;
-          softmax_p(s, s0 + it * kTile, pb_hi, pb_lo, nullptr, nullptr);
-          // V of this tile must have landed in LDS: it was requested before the 8 K loads
-          // of the next tile, which may stay in flight
-          wait_vm(has_next ? 8 : 0);
-          pv(pb_hi, pb_lo);
-          // the transposing reads of this tile are complete (their data fed the MFMAs):
-          // the LDS tile can take the next V
-          if (has_next) load_v(s0 + (it + KS) * kTile);
-        }
-      }
-    }
-  }
-
-  // this wave's totals: sum l over the four key groups; fold the lo columns into hi
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  if constexpr (HL) {
-#pragma unroll
-    for (int db = 0; db < 8; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[db][i] += __shfl_xor(o[db][i], 8);
-  }
-
-  if (KS == 1) {
-    // one wave per kv head: store straight from registers
-    if (wave_active && col_valid && !is_lo) {
-      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-      const int row = wv.qi * a.Hq1 + kvh * g + wv.hh;
-#pragma unroll
-      for (int db = 0; db < 8; ++db)
-        store_unit(a, b, row, p, direct, 16 * db + 4 * qd, o[db] * inv, m_run, l_run, db == 0 && qd == 0);
-    }
-  } else {
-    merge_key_splits<HL>(a, wv, smem, b, p, direct, o, m_run, l_run);
-  }
-  if (a.counters && !direct) fused_combine(a, wv, flag_s, b, count, first_slot);
-}
-
-// A piece of work as wave 0 of a workgroup publishes it to the other waves.
-struct Piece {
-  int b, start, end, slot;
-  int first_slot, count;   // the sequence's first slot and number of partitions
-};
-struct PieceTable {
-  Piece row[64];      // indexed by lane = sequence within the current chunk of 64
-  uint32_t mask_lo, mask_hi;
-  int done;
-  // scan state, kept here rather than in registers across the pieces (wave 0 only)
-  int c0, slot_base;
-  int64_t U, Wact, ts, te, tile_base;
-};
-
-template <bool HL, int PM, bool F8>
-// one 8-wave workgroup per CU (two waves per SIMD): the tile loop needs about 160 VGPRs,
-// and eight waves per CU already keep the memory system busy under the equal-share schedule
-__global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
-void partition_gqa_kernel(PartArgs a, int HG, int KS) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];   // NW * kWaveBytes (launch size)
-  __shared__ int pages_s[kMaxLdsPages];
-  __shared__ PieceTable table;
-  __shared__ int fuse_flag;
-  WaveInfo wv;
-  wv.HG = HG;
-  wv.KS = KS;
-  wv.NW = HG * KS;
-  wv.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, uniform
-  wv.ks = wv.w / HG;
-  wv.kvh = blockIdx.y * HG + wv.w % HG;
-  wv.wave_active = wv.kvh < a.Hkv;
-  wv.lane = threadIdx.x & 63;
-  wv.n = wv.lane & 15;
-  wv.qd = wv.lane >> 4;
-  wv.hc = HL ? (wv.n & 7) : wv.n;          // (query, head) column of this lane
-  wv.col_valid = wv.hc < a.q_len * a.g;
-  wv.qi = wv.col_valid ? wv.hc / a.g : 0;
-  wv.hh = wv.col_valid ? wv.hc % a.g : 0;
-  wv.is_lo = HL && wv.n >= 8;
-  const int lane = wv.lane;
-
-  if (a.workers == 0) {
-    // fixed chunks: partition blockIdx.x of sequence blockIdx.z (sequence length loaded by a
-    // vector load: state that it is uniform)
-    const int L = __builtin_amdgcn_readfirstlane(attended_len(a, blockIdx.z, PM == kContiguous));
-    if ((int)blockIdx.x * a.chunk >= L) return;
-  }
-  zero_v_tile(smem + wv.w * kWaveBytes, lane);
-
-  // Equal shares: worker wid = blockIdx.x takes tiles [ts, te) of the U 32-key tiles of
-  // all sequences concatenated in batch order (at least kMinShareTiles per worker, so
-  // fewer workers than launched may be active). Each sequence the share meets is one
-  // piece, stored in slot (first slot of the sequence) + (wid - first worker of the
-  // sequence). Wave 0 scans seq_lens 64 sequences at a time and publishes the pieces of
-  // each chunk in LDS; every wave then runs them in order.
-  const int wid = blockIdx.x;
-  uint64_t pending = 0;
-  bool fixed_taken = false;
-  if (a.workers > 0 && wv.w == 0) {
-    int64_t U = 0;
-    for (int c = 0; c < a.B; c += 64) {
-      const int bb = c + lane;
-      const int64_t nt = bb < a.B ? (attended_len(a, bb, PM == kContiguous) + kTile - 1) / kTile : 0;
-      U += wave_sum_i64(nt);
-    }
-    U = lane_value(U, 0);
-    int64_t Wact = U / kMinShareTiles;
-    Wact = Wact < 1 ? 1 : (Wact > a.workers ? a.workers : Wact);
-    if (lane == 0) {
-      table.U = U;
-      table.Wact = Wact;
-      table.ts = (int64_t)wid * U / Wact;
-      table.te = (int64_t)(wid + 1) * U / Wact;
-      table.tile_base = 0;   // tiles of the sequences before the current chunk
-      table.slot_base = 0;   // slots of the sequences before the current chunk
-      table.c0 = -64;
-    }
-  }
-
-  for (;;) {
-    int b, start, end, p, count, first_slot;
-    if (a.workers == 0) {
-      if (fixed_taken) break;
-      fixed_taken = true;
-      b = blockIdx.z;
-      p = blockIdx.x;
-      const int L = __builtin_amdgcn_readfirstlane(attended_len(a, b, PM == kContiguous));
-      start = p * a.chunk;
-      end = min(start + a.chunk, L);
-      count = min((L + a.chunk - 1) / a.chunk, a.max_splits);
-      first_slot = -1;
-    } else {
-      while (pending == 0) {
-        __syncthreads();   // every wave is done with the previous table
-        if (wv.w == 0) {
-          const int64_t U = table.U, Wact = table.Wact, ts = table.ts, te = table.te;
-          int64_t tile_base = table.tile_base;
-          int slot_base = table.slot_base;
-          const int c0 = table.c0 + 64;
-          // past the end of this share nothing is left, except for the last worker, which
-          // also writes the (first slot, count) of empty sequences at the very end
-          const bool done = wid >= Wact || c0 >= a.B || (tile_base >= te && wid != Wact - 1);
-          uint64_t mask = 0;
-          if (!done) {
-            const int bb = c0 + lane;
-            const int len = bb < a.B ? attended_len(a, bb, PM == kContiguous) : 0;
-            const int64_t nt = (len + kTile - 1) / kTile;
-            const int64_t incl = wave_incl_scan(nt);
-            const int64_t pre = tile_base + incl - nt;   // first tile of sequence bb
-            int64_t first = 0;                           // worker holding that tile
-            int count = 0;                               // partitions of sequence bb
-            if (nt > 0) {
-              first = share_owner(pre, U, Wact);
-              count = (int)(share_owner(pre + nt - 1, U, Wact) - first + 1);
-            }
-            const int sincl = wave_incl_scan(count);
-            const int slot = slot_base + sincl - count;
-            // (first slot, count) of each sequence for the combine, written by exactly one
-            // worker: the one whose share holds the sequence's first tile (the last one
-            // for trailing empty sequences)
-            if (blockIdx.y == 0 && bb < a.B) {
-              const int64_t writer = pre < U ? share_owner(pre, U, Wact) : Wact - 1;
-              if (writer == wid) {
-                a.meta[2 * bb] = slot;
-                a.meta[2 * bb + 1] = count;
-              }
-            }
-            const bool mine = bb < a.B && nt > 0 && pre < te && pre + nt > ts;
-            mask = __ballot(mine);
-            if (mine) {
-              const int64_t lo = (ts > pre ? ts : pre) - pre;
-              const int64_t hi = (te < pre + nt ? te : pre + nt) - pre;
-              Piece pc;
-              pc.b = bb;
-              pc.start = (int)lo * kTile;
-              pc.end = min((int)hi * kTile, len);
-              pc.slot = slot + (int)(wid - first);
-              pc.first_slot = slot;
-              pc.count = count;
-              table.row[lane] = pc;
-            }
-            tile_base += lane_value(incl, 63);
-            slot_base += lane_value(sincl, 63);
-          }
-          if (lane == 0) {
-            table.mask_lo = (uint32_t)mask;
-            table.mask_hi = (uint32_t)(mask >> 32);
-            table.done = done ? 1 : 0;
-            table.c0 = c0;
-            table.tile_base = tile_base;
-            table.slot_base = slot_base;
-          }
-        }
-        __syncthreads();
-        if (__builtin_amdgcn_readfirstlane(table.done)) break;
-        pending = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)table.mask_hi) << 32) |
-                  (uint32_t)__builtin_amdgcn_readfirstlane((int)table.mask_lo);
-      }
-      if (pending == 0) break;
-      const int j = __builtin_ctzll(pending);
-      pending &= pending - 1;
-      b = __builtin_amdgcn_readfirstlane(table.row[j].b);
-      start = __builtin_amdgcn_readfirstlane(table.row[j].start);
-      end = __builtin_amdgcn_readfirstlane(table.row[j].end);
-      p = __builtin_amdgcn_readfirstlane(table.row[j].slot);
-      first_slot = __builtin_amdgcn_readfirstlane(table.row[j].first_slot);
-      count = __builtin_amdgcn_readfirstlane(table.row[j].count);
-    }
-    run_piece<HL, PM, F8>(a, wv, smem, pages_s, &fuse_flag, b, start, end, p, count, first_slot);
-  }
-}
-
-template <bool HL>
-hipError_t launch_hl(const PartArgs& a, int pm, int HG, int KS, hipStream_t s) {
-  const unsigned groups = (unsigned)((a.Hkv + HG - 1) / HG);
-  const dim3 grid = a.workers > 0 ? dim3((unsigned)a.workers, groups, 1) : dim3((unsigned)a.max_splits, groups, (unsigned)a.B);
-  const dim3 block(HG * KS * 64);
-  const size_t lds = (size_t)HG * KS * kWaveBytes;
-  if (a.kv_fp8) {
-    // fp8 caches: contiguous or pages of a power of two >= 32 keys
-    switch (pm) {
-      case kContiguous:
-        hipLaunchKernelGGL((partition_gqa_kernel<HL, kContiguous, true>), grid, block, lds, s, a, HG, KS);
-        break;
-      case kPagedAligned:
-        hipLaunchKernelGGL((partition_gqa_kernel<HL, kPagedAligned, true>), grid, block, lds, s, a, HG, KS);
-        break;
-      default:
-        return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-  }
-  switch (pm) {
-    case kContiguous:
-      hipLaunchKernelGGL((partition_gqa_kernel<HL, kContiguous, false>), grid, block, lds, s, a, HG, KS);
-      break;
-    case kPagedAligned:
-      hipLaunchKernelGGL((partition_gqa_kernel<HL, kPagedAligned, false>), grid, block, lds, s, a, HG, KS);
-      break;
-    default:
-      hipLaunchKernelGGL((partition_gqa_kernel<HL, kPagedGeneral, false>), grid, block, lds, s, a, HG, KS);
-      break;
-  }
-  return hipGetLastError();
-}
-
-}  // namespace
-
-// HG kv heads per workgroup, KS key splits per kv head (HG * KS <= 16).
-hipError_t launch_partition_mfma128(const PartArgs& a, int page_mode, int HG, int KS, hipStream_t s) {
-  if (HG < 1 || KS < 1 || HG * KS > kMaxWaves) return hipErrorInvalidValue;
-  return a.q_len * a.g <= 8 ? launch_hl<true>(a, page_mode, HG, KS, s) : launch_hl<false>(a, page_mode, HG, KS, s);
+hipError_t launch_partition_mfma(const PartArgs& a, int page_mode, int HG, int KS, hipStream_t s) {
+  if (a.Dqk == 128 && a.Dv == 128 && a.Dk == 128) return mfma::launch_shape<mfma::Shape128>(a, page_mode, HG, KS, s);
+  if (a.Dqk == 192 && a.Dv == 128) return launch_partition_mfma_d192(a, page_mode, HG, KS, s);
+  if (a.Dqk == 256 && a.Dv == 256) return launch_partition_mfma_d256(a, page_mode, HG, KS, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace da

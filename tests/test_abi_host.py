@@ -264,3 +264,63 @@ def test_binding_refuses_output_buffers_without_every_row():
     with pytest.raises(ValueError, match="GPU"):
         api.check_outputs(p2, out=torch.empty((3, 2, 8, 128), dtype=torch.bfloat16))
     api.check_outputs(p1)   # nothing given, nothing to check
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qk_depth=256, ov_depth=256), DA_OK),
+    (dict(qk_depth=256, ov_depth=256, nope_depth=192, rope_dtype=1), DA_OK),
+    (dict(qk_depth=256, ov_depth=256, nope_depth=192, rope_dtype=1, kv_dtype=2), DA_OK),
+    (dict(qk_depth=192, ov_depth=128, nope_depth=128, rope_dtype=1), DA_OK),
+    (dict(qk_depth=192, ov_depth=128, kv_dtype=2, q_len=2), DA_OK),
+    (dict(qk_depth=256, ov_depth=256, num_q_heads=2, num_kv_heads=2), DA_OK),    # one q head per kv head
+    (dict(qk_depth=256, ov_depth=256, nope_depth=192, rope_dtype=0), DA_EUNSUPPORTED),   # fp32 rotary
+    (dict(qk_depth=256, ov_depth=256, nope_depth=128, rope_dtype=1), DA_EUNSUPPORTED),   # 128 rotary
+    (dict(qk_depth=128, ov_depth=128, nope_depth=64, rope_dtype=1), DA_EUNSUPPORTED),
+    (dict(qk_depth=256, ov_depth=256, nope_depth=256, rope_dtype=1), DA_EINVAL),
+    (dict(qk_depth=256, ov_depth=256, nope_depth=-1), DA_EINVAL),
+    (dict(qk_depth=256, ov_depth=128), DA_EUNSUPPORTED),
+    (dict(qk_depth=256, ov_depth=256, dtype=0), DA_EUNSUPPORTED),
+    (dict(qk_depth=256, ov_depth=256, page_size=16, max_pages_per_seq=256), DA_EUNSUPPORTED),
+    (dict(qk_depth=256, ov_depth=256, kernel=1), DA_EUNSUPPORTED),
+    (dict(qk_depth=256, ov_depth=256, num_q_heads=34, num_kv_heads=2), DA_EUNSUPPORTED),   # group 17
+])
+def test_wide_depth_support(lib, kw, code):
+    assert lib.da_supported(ctypes.byref(prob(**kw))) == code, lib.da_last_error()
+
+
+def test_wide_depth_workspace_and_splits(lib):
+    p = prob(batch=3, num_q_heads=8, num_kv_heads=8, qk_depth=256, ov_depth=256, nope_depth=192, rope_dtype=1,
+             max_seq_len=1000, max_pages_per_seq=16)
+    C, P = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.da_choose_splits(ctypes.byref(p), 0, 256, ctypes.byref(C), ctypes.byref(P)) == DA_OK
+    assert C.value == 0 and P.value >= 1   # equal shares on the matrix-core kernel
+    n = ctypes.c_size_t()
+    assert lib.da_workspace_bytes(ctypes.byref(p), 4, ctypes.byref(n)) == DA_OK
+    # fixed chunks: B * Hq * P (m, l) pairs and B * Hq * P * 256 fp32 partial outputs (+ counters)
+    need = lambda x: -(-x // 256) * 256
+    assert n.value == need(3 * 8 * 4 * 8) + need(3 * 8 * 4 * 256 * 4) + need(3 * 8 * 4)
+
+
+def test_rotary_columns_apart_need_their_tensor(lib):
+    from lse_combine_amd._lib import DaKv
+    p = prob(qk_depth=256, ov_depth=256, nope_depth=192, rope_dtype=1)
+    # the plain entry point has no place for them
+    assert call_splitk(lib, p) == DA_EINVAL
+    assert b"k_rope" in lib.da_last_error()
+    kv = DaKv(0x1000, 0x1000, None, None, None)
+    r = lib.decode_attn_splitk_kv(ctypes.byref(p), FAKE, ctypes.byref(kv), FAKE, FAKE, 0.1, 0, 0, FAKE, None, None,
+                                  FAKE, 1 << 30, None)
+    assert r == DA_EINVAL and b"k_rope" in lib.da_last_error()
+    p0 = prob(qk_depth=256, ov_depth=256)
+    kv = DaKv(0x1000, 0x1000, 0x1000, None, None)
+    r = lib.decode_attn_splitk_kv(ctypes.byref(p0), FAKE, ctypes.byref(kv), FAKE, FAKE, 0.1, 0, 0, FAKE, None, None,
+                                  FAKE, 1 << 30, None)
+    assert r == DA_EINVAL
+    assert lib.decode_attn_splitk_kv(ctypes.byref(p0), FAKE, None, FAKE, FAKE, 0.1, 0, 0, FAKE, None, None, FAKE,
+                                     1 << 30, None) == DA_EINVAL
+    # fp8 caches need their K scales here too
+    p8 = prob(qk_depth=256, ov_depth=256, nope_depth=192, rope_dtype=1, kv_dtype=2)
+    kv = DaKv(0x1000, 0x1000, 0x1000, None, None)
+    r = lib.decode_attn_partition_kv(ctypes.byref(p8), FAKE, ctypes.byref(kv), FAKE, FAKE, 0.1, 256, 16, FAKE, FAKE,
+                                     None)
+    assert r == DA_EINVAL and b"k_scale" in lib.da_last_error()

@@ -267,7 +267,8 @@ def test_equal_share_partials_match_oracle(name, kw, workers):
     assert_parity(out, lse, o32, Oref, Lref, what=f"equal shares {name} combine")
 
 
-@pytest.mark.parametrize("Dv,P", [(128, 4), (128, 16), (128, 24), (128, 64), (512, 8), (512, 20)])
+@pytest.mark.parametrize("Dv,P", [(128, 4), (128, 16), (128, 24), (128, 64), (256, 8), (256, 40), (512, 8),
+                                  (512, 20)])
 def test_combine_only_on_oracle_partials(Dv, P):
     # oracle partials (with empty partitions) fed to the HIP combine
     r = np.random.default_rng(Dv + P)
@@ -285,7 +286,7 @@ def test_combine_only_on_oracle_partials(Dv, P):
     Oref, Lref = combine_fp64(m32, l32, O32, 0.125)
     prob = api._lib.DaProblem()
     prob.batch, prob.num_q_heads, prob.num_kv_heads = B, Hq, 1
-    prob.qk_depth = 576 if Dv == 512 else 128
+    prob.qk_depth = {128: 128, 256: 256, 512: 576}[Dv]
     prob.ov_depth, prob.dtype, prob.page_size, prob.kv_capacity = Dv, 1, 0, P * chunk
     prob.max_seq_len = P * chunk
     prob.v_is_k_prefix = 1 if Dv == 512 else 0
@@ -417,3 +418,103 @@ def test_workload_paged_gqa_sampled():
     rows = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 7, 19, 31})
     O, LSE = oracle_for(case, batch_rows=rows)
     assert_parity(out[rows], lse[rows], o32[rows], O, LSE, what="paged_gqa sampled")
+
+
+# ---------------------------------------------------------------------------
+# wider depth pairs: q.K 192 / V 128 and q.K 256 / V 256 (nope 192 != V 256), with the
+# 64 rotary columns in the K rows or stored apart in bf16, bf16 or fp8 caches
+# ---------------------------------------------------------------------------
+WIDE = [
+    ("d256_apart_g1_paged64_auto", dict(batch=4, num_q_heads=4, num_kv_heads=4, qk_depth=256, ov_depth=256,
+                                        page_size=64, len_range=(1, 3000), num_splits=0, seed=110,
+                                        rope_apart=64)),
+    ("d256_apart_g4_contig_splits3", dict(batch=2, num_q_heads=8, num_kv_heads=2, qk_depth=256, ov_depth=256,
+                                          seq_lens=[2000, 77], num_splits=3, seed=111, rope_apart=64)),
+    ("d256_inline_g8_paged32", dict(batch=3, num_q_heads=16, num_kv_heads=2, qk_depth=256, ov_depth=256,
+                                    page_size=32, seq_lens=[1500, 1, 640], num_splits=0, seed=112)),
+    ("d256_apart_g16_key_splits", dict(batch=2, num_q_heads=16, num_kv_heads=1, qk_depth=256, ov_depth=256,
+                                       page_size=64, seq_lens=[3000, 100], num_splits=2, seed=113,
+                                       rope_apart=64)),
+    ("d192_apart_g8_paged64", dict(batch=3, num_q_heads=16, num_kv_heads=2, qk_depth=192, ov_depth=128,
+                                   page_size=64, seq_lens=[1000, 33, 2100], num_splits=0, seed=114,
+                                   rope_apart=64)),
+    ("d192_inline_g4_contig", dict(batch=2, num_q_heads=8, num_kv_heads=2, qk_depth=192, ov_depth=128,
+                                   seq_lens=[700, 1300], num_splits=0, seed=115)),
+    ("d256_apart_fp8_g1_paged64", dict(batch=4, num_q_heads=4, num_kv_heads=4, qk_depth=256, ov_depth=256,
+                                       page_size=64, len_range=(1, 3000), num_splits=0, seed=116,
+                                       rope_apart=64, kv_fp8=True)),
+    ("d256_inline_fp8_g8_contig", dict(batch=2, num_q_heads=16, num_kv_heads=2, qk_depth=256, ov_depth=256,
+                                       seq_lens=[1200, 45], num_splits=2, seed=117, kv_fp8=True)),
+    ("d192_apart_fp8_g8_noscale_v", dict(batch=3, num_q_heads=16, num_kv_heads=2, qk_depth=192, ov_depth=128,
+                                         page_size=64, seq_lens=[900, 1, 2048], num_splits=0, seed=118,
+                                         rope_apart=64, kv_fp8=True, v_scaled=False)),
+    ("d256_apart_q2_g4", dict(batch=3, num_q_heads=8, num_kv_heads=2, qk_depth=256, ov_depth=256, page_size=64,
+                              seq_lens=[1, 600, 2500], num_splits=0, seed=119, rope_apart=64, q_len=2)),
+    ("d256_apart_poisoned", dict(batch=3, num_q_heads=4, num_kv_heads=2, qk_depth=256, ov_depth=256,
+                                 page_size=64, seq_lens=[100, 1, 1025], num_splits=0, seed=120, rope_apart=64,
+                                 poison=True, spare_pages=3)),
+]
+
+
+@pytest.mark.parametrize("name,kw", WIDE, ids=[c[0] for c in WIDE])
+def test_wide_depth_parity(name, kw):
+    case = make_case(name, **kw)
+    out, lse, o32 = check_case(case, f"wide depth {name}")
+    assert torch.isfinite(o32).all()
+
+
+def test_wide_depth_fused_combine():
+    case = make_case("wide_fused", batch=4, num_q_heads=8, num_kv_heads=2, qk_depth=256, ov_depth=256,
+                     page_size=64, len_range=(1, 4000), num_splits=0, seed=121, rope_apart=64, kv_fp8=True)
+    dc = to_device(case)
+    O, LSE = oracle_for(case)
+    prob = api.make_problem(dc.q, dc.k_cache, dc.v_cache, dc.page_table, page_size=case.page_size,
+                            k_rope=dc.k_rope)
+    ws = torch.zeros(api.workspace_bytes(prob, 0), dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        out, lse, o32 = api.case_call(dc, return_lse=True, return_o32=True, fused=True, workspace=ws)
+        torch.cuda.synchronize()
+        assert_parity(out, lse, o32, O, LSE, what=f"wide depth fused call {rep}")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_wide_depth_equal_share_partials(fp8):
+    print(f"[parity] wide depth equal-share partials fp8={fp8}", flush=True)
+    case = make_case("wide_parts", batch=3, num_q_heads=4, num_kv_heads=4, qk_depth=256, ov_depth=256,
+                     page_size=64, seq_lens=[1000, 64, 2500], seed=122, rope_apart=64, kv_fp8=fp8)
+    dc = to_device(case)
+    workers = 6
+    prob = api.make_problem(dc.q, dc.k_cache, dc.v_cache, dc.page_table, page_size=64, k_rope=dc.k_rope)
+    po_t, pml_t = api.partition(dc.q, dc.k_cache, dc.v_cache, dc.page_table, dc.seq_lens, case.scale, 0, workers,
+                                page_size=64, k_scale=dc.k_scale, v_scale=dc.v_scale, k_rope=dc.k_rope)
+    torch.cuda.synchronize()
+    lens = case.seq_lens.numpy().astype(np.int64)
+    pieces, first, count = equal_share_pieces(lens, workers)
+    ml_t, table = api.slot_table(prob, workers, pml_t)
+    np.testing.assert_array_equal(table.cpu().numpy(), np.stack([first, count], -1))
+    ks = None if case.k_scale is None else case.k_scale.numpy()
+    vs = None if case.v_scale is None else case.v_scale.numpy()
+    m, l, O = range_partials_fp64(np32(case.q), np32(case.k_cache), np32(case.v_cache), lens, case.scale, pieces,
+                                  page_table=case.page_table.numpy(), page_size=64, k_scale=ks, v_scale=vs,
+                                  k_rope=np32(case.k_rope))
+    S = len(pieces)
+    ml, po = np32(ml_t)[:S], np32(po_t)[:S]
+    np.testing.assert_allclose(ml[..., 0], m, rtol=1e-5, atol=1e-4)
+    np.testing.assert_allclose(ml[..., 1], l, rtol=1e-5)
+    err = np.abs(po - O).max(-1)
+    assert (err / np.abs(O).max(-1)).max() <= 1e-5
+    out, lse, o32 = api.combine(prob, dc.seq_lens, case.scale, 0, workers, po_t, pml_t)
+    torch.cuda.synchronize()
+    Oref, Lref = oracle_for(case)
+    assert_parity(out, lse, o32, Oref, Lref, what="wide depth equal shares combine")
+
+
+@pytest.mark.parametrize("name", ["paged_glm", "paged_glm_fp8"])
+def test_workload_glm_style_sampled(name):
+    case = workload(name)
+    print(f"[parity] workload {name} (sampled rows)", flush=True)
+    out, lse, o32 = run(case)
+    lens = case.seq_lens.numpy()
+    rows = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 13, 31})
+    O, LSE = oracle_for(case, batch_rows=rows)
+    assert_parity(out[rows], lse[rows], o32[rows], O, LSE, what=f"{name} sampled")
