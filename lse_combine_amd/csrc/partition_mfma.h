@@ -107,6 +107,11 @@ __device__ __forceinline__ void wait_vm() {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Four E4M3 codes (one dword, byte 0 first) as two packed bf16 pairs, through the
@@ -464,30 +469,6 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
     }
   };
 
-  // fp8 V: the tile's 32 rows into registers (lane l: row l/2, half l%2 of the DV-byte
-  // row), then widened to bf16 and written to this wave's LDS tile in the swizzled layout
-  // that the transposing reads expect (source chunk c of row r at slot c ^ (r & 15))
-  constexpr int kV8Loads = S::DV / 32;
-  auto load_v8 = [&](u32x4* vr, int t0) {
-    const int last = min(kTile - 1, end - 1 - t0);
-    const int64_t row0 = tile_row0(t0);
-    const int rows = __builtin_amdgcn_readfirstlane(max(last + 1, 0));
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(vc + row0 * vrow_bytes + vslice), 0, rows * vrow_bytes, kRsrcWord3);
-    const uint32_t off = (uint32_t)(lane >> 1) * vrow_bytes + (S::DV / 2) * (lane & 1);
-#pragma unroll
-    for (int m = 0; m < kV8Loads; ++m) vr[m] = buf_load16(rv, off + 16 * m, 0);
-  };
-  auto stage_v8 = [&](const u32x4* vr) {
-    const int r = lane >> 1;
-#pragma unroll
-    for (int m = 0; m < kV8Loads; ++m) {
-      const int c0 = (S::DV / 16) * (lane & 1) + 2 * m;
-      *(bf16x8*)(vt + r * S::kVRow + ((c0 ^ (r & 15)) << 4)) = fp8x8_to_bf16x8(vr[m][0], vr[m][1]);
-      *(bf16x8*)(vt + r * S::kVRow + (((c0 + 1) ^ (r & 15)) << 4)) = fp8x8_to_bf16x8(vr[m][2], vr[m][3]);
-    }
-  };
-
   // phase B: online softmax, giving P^T as the B operand of P.V. On a ragged tile the
   // scores of missing keys are set to -inf first; exp2(-inf) = 0 then removes them from
   // the sums. With fp8 caches the scores take the K scales of their keys first, and the
@@ -560,24 +541,70 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
   };
 
   // phase C: O^T += V^T P^T, V^T read transposed from the LDS tile
-  auto pv = [&](const bf16x8& pb_hi, const bf16x8& pb_lo) {
+  // (O blocks DB0 .. DB0 + NB - 1 from a bf16 tile of rows of ROW bytes whose 16-byte chunk c
+  // of row r sits at slot c ^ (r & XM))
+  auto pv_tile = [&](auto db0_c, auto nb_c, auto row_c, auto xm_c, const char* tile, const bf16x8& pb_hi,
+                     const bf16x8& pb_lo) {
+    constexpr int DB0 = decltype(db0_c)::value, NB = decltype(nb_c)::value;
+    constexpr int ROW = decltype(row_c)::value, XM = decltype(xm_c)::value;
     // V^T A operand: lane (n, qd) gets depth 16db + n of keys 4qd..+3 and 16+4qd..+3
     const int r0 = 4 * qd + (n >> 2);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < NB; ++db) {
       const int ch = 2 * db + ((n & 3) >> 1);
       const int sub = (n & 1) * 8;
       const int ra = r0, rb = r0 + 16;
       const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (s16x4 DA_LDS*)(vt + ra * S::kVRow + ((ch ^ (ra & 15)) << 4) + sub));
+          (s16x4 DA_LDS*)(tile + ra * ROW + ((ch ^ (ra & XM)) << 4) + sub));
       const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (s16x4 DA_LDS*)(vt + rb * S::kVRow + ((ch ^ (rb & 15)) << 4) + sub));
+          (s16x4 DA_LDS*)(tile + rb * ROW + ((ch ^ (rb & XM)) << 4) + sub));
       s16x8 v8;
       v8[0] = va[0]; v8[1] = va[1]; v8[2] = va[2]; v8[3] = va[3];
       v8[4] = vb[0]; v8[5] = vb[1]; v8[6] = vb[2]; v8[7] = vb[3];
       const bf16x8 vf = __builtin_bit_cast(bf16x8, v8);
-      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb_hi, o[db], 0, 0, 0);
-      if constexpr (!HL) o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb_lo, o[db], 0, 0, 0);
+      o[DB0 + db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb_hi, o[DB0 + db], 0, 0, 0);
+      if constexpr (!HL) o[DB0 + db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb_lo, o[DB0 + db], 0, 0, 0);
+    }
+  };
+  auto pv = [&](const bf16x8& pb_hi, const bf16x8& pb_lo) {
+    pv_tile(IntC<0>{}, IntC<DB>{}, IntC<S::kVRow>{}, IntC<15>{}, vt, pb_hi, pb_lo);
+  };
+
+  // fp8 V through LDS: the tile's 32 rows of DV codes land, direct-to-LDS and
+  // unswizzled, in the upper half of the wave's region; each depth half is then widened to
+  // a 32 x DV/2 bf16 tile in the lower half (the swizzled layout of the transposing reads)
+  // and consumed by P.V before the other half is widened. No registers hold V in flight.
+  char* const v8_stage = vt + S::kVBytes / 2;
+  constexpr int kV8Chunks = S::DV / 16;             // 16-byte chunks per fp8 row
+  constexpr int kV8Rows = 64 / kV8Chunks;           // rows per 1 KB direct-to-LDS load
+  constexpr int kV8PerHalf = 16 / kV8Rows;          // loads per 16-row half tile
+  constexpr int kHalfXm = S::DV / 16 - 1 < 15 ? S::DV / 16 - 1 : 15;   // swizzle of the half-depth tile
+  auto load_v8_lds = [&](int t0) {
+    const int last = min(kTile - 1, end - 1 - t0);
+    const int64_t row0 = tile_row0(t0);
+    const int rr = lane / kV8Chunks, cc = lane % kV8Chunks;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int rows = __builtin_amdgcn_readfirstlane(min(max(last + 1 - 16 * h, 0), 16));
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(vc + (row0 + 16 * h) * vrow_bytes + vslice), 0, rows * vrow_bytes, kRsrcWord3);
+#pragma unroll
+      for (int i = 0; i < kV8PerHalf; ++i) {
+        const int r = kV8Rows * i + rr;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (DA_LDS void*)(v8_stage + (kV8PerHalf * h + i) * 1024), 16,
+                                                 (uint32_t)r * vrow_bytes + 16 * cc, 0, 0, kLoadNT);
+      }
+    }
+  };
+  auto widen_half = [&](int hd) {
+    constexpr int kCph = S::DV / 32;                // 16-value fp8 chunks per half row
+#pragma unroll
+    for (int k = 0; k < 32 * kCph / 64; ++k) {
+      const int u = lane + 64 * k;
+      const int r = u / kCph, c8 = u % kCph;
+      const u32x4 w = *(const u32x4*)(v8_stage + r * S::DV + hd * (S::DV / 2) + 16 * c8);
+      *(bf16x8*)(vt + r * S::DV + (((2 * c8) ^ (r & kHalfXm)) << 4)) = fp8x8_to_bf16x8(w[0], w[1]);
+      *(bf16x8*)(vt + r * S::DV + (((2 * c8 + 1) ^ (r & kHalfXm)) << 4)) = fp8x8_to_bf16x8(w[2], w[3]);
     }
   };
 
@@ -608,13 +635,13 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
       // softmax and P.V of the current tile.
       KT T;
       if constexpr (F8) {
-        // fp8: K, V and the scales of the next tile are in flight (in registers) through
-        // the softmax and P.V of the current one. (Two tiles in flight measured slower:
-        // this path is bound by the per-tile instruction chain, not by memory latency.)
-        u32x4 vr[kV8Loads];
+        // fp8: K and the scales of the next tile in flight in registers, its V codes in LDS.
+        // (V widened in registers and then written to LDS needed more registers than two
+        // waves per SIMD have at V depth 256, and measured slower at 128 too.)
+        constexpr int kKLoads = 2 * (KT::NL + S::NR);
         f32x4 ksc[2], vsc[2];
         load_k(T, s0 + ks * kTile);
-        load_v8(vr, s0 + ks * kTile);
+        load_v8_lds(s0 + ks * kTile);
         load_sc(ksc, vsc, s0 + ks * kTile);
         for (int it = ks; it < n_tiles; it += KS) {
           const bool has_next = it + KS < n_tiles;
@@ -622,14 +649,20 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
           f32x4 s[2], sr[2];
           score(T, s, sr);
           if (has_next) load_k(T, tn);
-          stage_v8(vr);
           bf16x8 pb_hi, pb_lo;
           softmax_p(s, sr, s0 + it * kTile, pb_hi, pb_lo, ksc, vsc);
+          // this tile's V codes are in LDS: they were requested before the next tile's K
+          if (has_next) wait_vm<kKLoads>();
+          else wait_vm<0>();
+          widen_half(0);
+          pv_tile(IntC<0>{}, IntC<DB / 2>{}, IntC<S::DV>{}, IntC<kHalfXm>{}, vt, pb_hi, pb_lo);
+          widen_half(1);
+          // the staging area has been read: the next tile's V may land there
           if (has_next) {
-            load_v8(vr, tn);
+            load_v8_lds(tn);
             load_sc(ksc, vsc, tn);
           }
-          pv(pb_hi, pb_lo);
+          pv_tile(IntC<DB / 2>{}, IntC<DB / 2>{}, IntC<S::DV>{}, IntC<kHalfXm>{}, vt, pb_hi, pb_lo);
         }
       } else {
         // loads issued per tile: K (and rotary) first, then V; V of the current tile must
