@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_partition_mfma128_paged_gqa.json")
-KERNEL_SOURCES = ["partition_mfma128.hip", "da_device.h", "da_internal.h"]
+KERNEL_SOURCES = ["partition_mfma.h", "partition_mfma128.hip", "da_device.h", "da_internal.h"]
 
 
 def kernel_source_hash():
