@@ -54,6 +54,7 @@ namespace mfma {
 constexpr int kTile = 32;
 constexpr int kMaxWaves = 8;
 constexpr int kMaxLdsPages = 512;             // page indices of one segment staged in LDS
+constexpr int kLdsBytes = 160 * 1024;         // LDS of one compute unit (gfx950)
 
 // Depths of one instantiation. DR > 0: the last DR columns of every K row are stored apart
 // (bf16, k_rope); the K cache holds the first DK = DQK - DR.
@@ -69,7 +70,12 @@ struct MShape {
   static constexpr int DB = DV / 16;           // 16-deep blocks of O
   static constexpr int kVRow = DV * 2;         // bytes of one bf16 V row in LDS
   static constexpr int kVBytes = kTile * kVRow;       // one wave's V tile in LDS
-  static constexpr int kWaveBytes = kVBytes + 256;    // + merge (m, l) for up to 16 columns
+  // fp8 caches stage V codes (32 x DV bytes per tile) beside a half-depth bf16 tile; at
+  // V depth 128 the region has room for two staged tiles (two tiles in flight)
+  static constexpr int kV8Tiles = DV == 128 ? 2 : 1;
+  static constexpr int kRegionBytes = kV8Tiles == 2 ? 3 * kTile * DV : kVBytes;
+  static_assert(kRegionBytes >= kVBytes, "the region holds a bf16 V tile");
+  static constexpr int kWaveBytes = kRegionBytes + 256;   // + merge (m, l) for up to 16 columns
   static_assert(DK % 64 == 0 && DR % 32 == 0 && (DV == 128 || DV == 256), "unsupported depths");
 };
 
@@ -106,6 +112,40 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Buffer resource of `bytes` bytes at `base` (raw, stride 0), as four scalar words.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t addr = (uint64_t)base;
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = kRsrcWord3;
+  return r;
+}
+
+// Direct-to-LDS 16-byte buffer load (the 64 lanes fill 1 KB at LDS address lds_base, lane
+// l at 16 l; a lane outside the buffer range writes nothing), non-temporal, written as
+// inline assembly: the compiler does not see an LDS write, so it adds no wait of its own
+// before later LDS reads (it would wait for the most recent such load, whatever it
+// fills). Every consumer waits explicitly (wait_vm). M0, which holds the LDS base of the
+// instruction, is saved and restored around it.
+__device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t voff, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen nt lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"(lds_base)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const DA_LDS char*)p;
+}
 
 template <int V>
 struct IntC {
@@ -144,7 +184,7 @@ __device__ __forceinline__ float max_over_key_groups(float v) {
 template <class S>
 __device__ __forceinline__ void zero_v_tile(char* vt, int lane) {
 #pragma unroll
-  for (int i = 0; i < S::kVBytes / 1024; ++i) *(u32x4*)(vt + (i * 64 + lane) * 16) = u32x4{0u, 0u, 0u, 0u};
+  for (int i = 0; i < S::kRegionBytes / 1024; ++i) *(u32x4*)(vt + (i * 64 + lane) * 16) = u32x4{0u, 0u, 0u, 0u};
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the zeros are in place before any load lands
 }
 
@@ -169,7 +209,7 @@ __device__ __forceinline__ void merge_key_splits(const PartArgs& a, const WaveIn
   constexpr int DV = S::DV;
   char* vt = smem + wv.w * S::kWaveBytes;
   float* mo = (float*)vt;                      // [16][DV] O of this wave
-  float* mml = (float*)(vt + S::kVBytes);      // m[16], l[16]
+  float* mml = (float*)(vt + S::kRegionBytes);   // m[16], l[16]
   __syncthreads();
   if (col_valid && !is_lo) {
 #pragma unroll
@@ -191,14 +231,14 @@ __device__ __forceinline__ void merge_key_splits(const PartArgs& a, const WaveIn
     // (a split that saw no key of this column holds l = 0 and weighs nothing)
     float M = -INFINITY;
     for (int s2 = 0; s2 < KS; ++s2) {
-      const float* ml = (const float*)(smem + (s2 * HG + mem) * S::kWaveBytes + S::kVBytes);
+      const float* ml = (const float*)(smem + (s2 * HG + mem) * S::kWaveBytes + S::kRegionBytes);
       if (ml[16 + h] > 0.f) M = fmaxf(M, ml[h]);
     }
     float Ls = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int s2 = 0; s2 < KS; ++s2) {
       const char* reg = smem + (s2 * HG + mem) * S::kWaveBytes;
-      const float* ml = (const float*)(reg + S::kVBytes);
+      const float* ml = (const float*)(reg + S::kRegionBytes);
       if (ml[16 + h] > 0.f) {
         const float e = exp2_fast((ml[h] - M) * c);
         Ls = fmaf(ml[16 + h], e, Ls);
@@ -343,8 +383,10 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
   const uint32_t roff = (uint32_t)n * rrow_bytes + 16 * qd;
 
   // K of the tile at t0 into registers (A operand of the score MFMAs).
-  auto load_k = [&](KT& T, int t0) {
-    const int last = min(kTile - 1, end - 1 - t0);
+  // (valid = false: the loads are issued with an empty buffer range, i.e. they return
+  // zeros without touching memory; loops that always issue the same loads use this)
+  auto load_k = [&](KT& T, int t0, bool valid = true) {
+    const int last = valid ? min(kTile - 1, end - 1 - t0) : -1;
     if constexpr (PM != kPagedGeneral) {
       // The tile is 32 consecutive cache rows: a scalar base per 16-row half. Each half's
       // buffer range covers only its valid rows, so on a ragged last tile the loads of
@@ -443,8 +485,8 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
   // per-token scales of the tile's keys that this lane holds (fp8 caches): keys
   // 4qd .. 4qd+3 and 16+4qd .. 16+4qd+3, 16 contiguous bytes each in the tokens-innermost
   // scale layout; missing keys of a ragged tile read 0 (their scores are masked anyway)
-  auto load_sc = [&](f32x4* ksc, f32x4* vsc, int t0) {
-    const int last = min(kTile - 1, end - 1 - t0);
+  auto load_sc = [&](f32x4* ksc, f32x4* vsc, int t0, bool valid = true) {
+    const int last = valid ? min(kTile - 1, end - 1 - t0) : -1;
     const int kv_safe = wave_active ? kvh : 0;
     int64_t base;
     if constexpr (PM == kContiguous) {
@@ -459,15 +501,14 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
         __builtin_amdgcn_make_buffer_rsrc((void*)(a.k_scale + base), 0, nk * 4, kRsrcWord3);
     ksc[0] = __builtin_bit_cast(f32x4, buf_load16(rk, 16 * qd, 0));
     ksc[1] = __builtin_bit_cast(f32x4, buf_load16(rk, 64 + 16 * qd, 0));
-    if (a.v_scale) {
-      const __amdgpu_buffer_rsrc_t rv =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(a.v_scale + base), 0, nk * 4, kRsrcWord3);
-      vsc[0] = __builtin_bit_cast(f32x4, buf_load16(rv, 16 * qd, 0));
-      vsc[1] = __builtin_bit_cast(f32x4, buf_load16(rv, 64 + 16 * qd, 0));
-    } else {
-      vsc[0] = vsc[1] = f32x4{1.f, 1.f, 1.f, 1.f};
-    }
+    // the V scales are loaded in every case (from the K scales when there are none, then
+    // replaced by 1 where they are used): the same loads on every path
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((a.v_scale ? a.v_scale : a.k_scale) + base), 0, nk * 4, kRsrcWord3);
+    vsc[0] = __builtin_bit_cast(f32x4, buf_load16(rv, 16 * qd, 0));
+    vsc[1] = __builtin_bit_cast(f32x4, buf_load16(rv, 64 + 16 * qd, 0));
   };
+  const bool has_vscale = a.v_scale != nullptr;
 
   // phase B: online softmax, giving P^T as the B operand of P.V. On a ragged tile the
   // scores of missing keys are set to -inf first; exp2(-inf) = 0 then removes them from
@@ -526,8 +567,8 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) {
       const int blk = s2 >> 1, i0 = (s2 & 1) * 2;
-      const float p0 = F8 ? pr[blk][i0] * vsc[blk][i0] : pr[blk][i0];
-      const float p1 = F8 ? pr[blk][i0 + 1] * vsc[blk][i0 + 1] : pr[blk][i0 + 1];
+      const float p0 = F8 ? pr[blk][i0] * (has_vscale ? vsc[blk][i0] : 1.f) : pr[blk][i0];
+      const float p1 = F8 ? pr[blk][i0 + 1] * (has_vscale ? vsc[blk][i0 + 1] : 1.f) : pr[blk][i0 + 1];
       const uint32_t h = pack_bf16x2(p0, p1);
       if constexpr (HL) {
         pw[s2] = pack_bf16x2(fmaf(-lo_mask, bf16lo(h), p0), fmaf(-lo_mask, bf16hi(h), p1));
@@ -574,13 +615,31 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
   // unswizzled, in the upper half of the wave's region; each depth half is then widened to
   // a 32 x DV/2 bf16 tile in the lower half (the swizzled layout of the transposing reads)
   // and consumed by P.V before the other half is widened. No registers hold V in flight.
-  char* const v8_stage = vt + S::kVBytes / 2;
+  // staging tile(s) of 32 x DV codes after the half-depth bf16 tile (32 x DV bytes)
+  char* const v8_stage = vt + kTile * S::DV;
   constexpr int kV8Chunks = S::DV / 16;             // 16-byte chunks per fp8 row
   constexpr int kV8Rows = 64 / kV8Chunks;           // rows per 1 KB direct-to-LDS load
   constexpr int kV8PerHalf = 16 / kV8Rows;          // loads per 16-row half tile
   constexpr int kHalfXm = S::DV / 16 - 1 < 15 ? S::DV / 16 - 1 : 15;   // swizzle of the half-depth tile
-  auto load_v8_lds = [&](int t0) {
-    const int last = min(kTile - 1, end - 1 - t0);
+  // (the same loads through lds_dma16, for loops whose waits are all explicit)
+  auto load_v8_lds_asm = [&](char* stage, int t0, bool valid) {
+    const int last = valid ? min(kTile - 1, end - 1 - t0) : -1;
+    const int64_t row0 = tile_row0(t0);
+    const int rr = lane / kV8Chunks, cc = lane % kV8Chunks;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int rows = __builtin_amdgcn_readfirstlane(min(max(last + 1 - 16 * h, 0), 16));
+      const u32x4 rv = rsrc_words(vc + (row0 + 16 * h) * vrow_bytes + vslice, (uint32_t)rows * vrow_bytes);
+#pragma unroll
+      for (int i = 0; i < kV8PerHalf; ++i) {
+        const int r = kV8Rows * i + rr;
+        lds_dma16(rv, (uint32_t)r * vrow_bytes + 16 * cc,
+                  __builtin_amdgcn_readfirstlane(lds_addr(stage + (kV8PerHalf * h + i) * 1024)));
+      }
+    }
+  };
+  auto load_v8_lds = [&](char* stage, int t0, bool valid = true) {
+    const int last = valid ? min(kTile - 1, end - 1 - t0) : -1;
     const int64_t row0 = tile_row0(t0);
     const int rr = lane / kV8Chunks, cc = lane % kV8Chunks;
 #pragma unroll
@@ -591,20 +650,20 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
 #pragma unroll
       for (int i = 0; i < kV8PerHalf; ++i) {
         const int r = kV8Rows * i + rr;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (DA_LDS void*)(v8_stage + (kV8PerHalf * h + i) * 1024), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (DA_LDS void*)(stage + (kV8PerHalf * h + i) * 1024), 16,
                                                  (uint32_t)r * vrow_bytes + 16 * cc, 0, 0, kLoadNT);
       }
     }
   };
-  auto widen_half = [&](int hd) {
+  auto widen_half = [&](char* work, const char* stage, int hd) {
     constexpr int kCph = S::DV / 32;                // 16-value fp8 chunks per half row
 #pragma unroll
     for (int k = 0; k < 32 * kCph / 64; ++k) {
       const int u = lane + 64 * k;
       const int r = u / kCph, c8 = u % kCph;
-      const u32x4 w = *(const u32x4*)(v8_stage + r * S::DV + hd * (S::DV / 2) + 16 * c8);
-      *(bf16x8*)(vt + r * S::DV + (((2 * c8) ^ (r & kHalfXm)) << 4)) = fp8x8_to_bf16x8(w[0], w[1]);
-      *(bf16x8*)(vt + r * S::DV + (((2 * c8 + 1) ^ (r & kHalfXm)) << 4)) = fp8x8_to_bf16x8(w[2], w[3]);
+      const u32x4 w = *(const u32x4*)(stage + r * S::DV + hd * (S::DV / 2) + 16 * c8);
+      *(bf16x8*)(work + r * S::DV + (((2 * c8) ^ (r & kHalfXm)) << 4)) = fp8x8_to_bf16x8(w[0], w[1]);
+      *(bf16x8*)(work + r * S::DV + (((2 * c8 + 1) ^ (r & kHalfXm)) << 4)) = fp8x8_to_bf16x8(w[2], w[3]);
     }
   };
 
@@ -634,14 +693,62 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
       // has been moved to LDS and into the score MFMAs, and stay in flight through the
       // softmax and P.V of the current tile.
       KT T;
-      if constexpr (F8) {
-        // fp8: K and the scales of the next tile in flight in registers, its V codes in LDS.
-        // (V widened in registers and then written to LDS needed more registers than two
-        // waves per SIMD have at V depth 256, and measured slower at 128 too.)
+      if constexpr (F8 && S::kV8Tiles == 2) {
+        // fp8 at V depth 128, two tiles in flight (a tile is half the bytes of bf16, so one
+        // tile per wave leaves too few bytes in flight to cover the memory latency). Tiles
+        // alternate between (T, ksc0, vsc0, stage 0) and (T1, ksc1, vsc1, stage 1); the
+        // loads of tile j are issued in the order K, scales, V, two tiles ahead: K after
+        // the scores of tile j - 2, the scales after its softmax, V after its staged codes
+        // were consumed. At the wait for tile j's V, the loads issued after it are those of
+        // tile j + 1 and the K and scales of tile j + 2.
+        constexpr int kK = 2 * (KT::NL + S::NR), kSc = 4, kV = 2 * kV8PerHalf;
+        KT T1;
+        f32x4 ksc0[2], vsc0[2], ksc1[2], vsc1[2];
+        // the wave's region: the half-depth bf16 tile, then the two staging tiles (their
+        // loads are issued as inline assembly: the compiler adds no waits for them, and the
+        // explicit wait below is the only one)
+        char* const work = vt;
+        char* const stage0 = vt + kTile * S::DV;
+        char* const stage1 = vt + 2 * kTile * S::DV;
+        auto issue = [&](KT& TT, f32x4* ksc, f32x4* vsc, char* stage, int t0, bool valid) {
+          load_k(TT, t0, valid);
+          load_sc(ksc, vsc, t0, valid);
+          load_v8_lds_asm(stage, t0, valid);
+        };
+        // Every step issues the same loads (those past the last tile with an empty range), so
+        // that a single count holds at the wait and the compiler sees one straight path.
+        auto step = [&](KT& TT, f32x4* ksc, f32x4* vsc, char* stage, int it) {
+          const bool has2 = it + 2 * KS < n_tiles;
+          const int t2 = s0 + (it + 2 * KS) * kTile;
+          f32x4 s[2], sr[2];
+          score(TT, s, sr);
+          load_k(TT, t2, has2);
+          bf16x8 pb_hi, pb_lo;
+          softmax_p(s, sr, s0 + it * kTile, pb_hi, pb_lo, ksc, vsc);
+          load_sc(ksc, vsc, t2, has2);
+          wait_vm<2 * kK + 2 * kSc + kV>();
+          widen_half(work, stage, 0);
+          pv_tile(IntC<0>{}, IntC<DB / 2>{}, IntC<S::DV>{}, IntC<kHalfXm>{}, work, pb_hi, pb_lo);
+          widen_half(work, stage, 1);
+          pv_tile(IntC<DB / 2>{}, IntC<DB / 2>{}, IntC<S::DV>{}, IntC<kHalfXm>{}, work, pb_hi, pb_lo);
+          // this stage has been read: tile j + 2 may land there
+          load_v8_lds_asm(stage, t2, has2);
+        };
+        issue(T, ksc0, vsc0, stage0, s0 + ks * kTile, true);
+        issue(T1, ksc1, vsc1, stage1, s0 + (ks + KS) * kTile, ks + KS < n_tiles);
+        for (int it = ks; it < n_tiles; it += 2 * KS) {
+          step(T, ksc0, vsc0, stage0, it);
+          if (it + KS < n_tiles) step(T1, ksc1, vsc1, stage1, it + KS);
+        }
+        wait_vm<0>();   // the empty-range loads past the last tile have retired
+      } else if constexpr (F8) {
+        // fp8 (wide V): K and the scales of the next tile in flight in registers, its V
+        // codes in LDS. (V widened in registers and then written to LDS needed more
+        // registers than two waves per SIMD have at V depth 256.)
         constexpr int kKLoads = 2 * (KT::NL + S::NR);
         f32x4 ksc[2], vsc[2];
         load_k(T, s0 + ks * kTile);
-        load_v8_lds(s0 + ks * kTile);
+        load_v8_lds(v8_stage, s0 + ks * kTile);
         load_sc(ksc, vsc, s0 + ks * kTile);
         for (int it = ks; it < n_tiles; it += KS) {
           const bool has_next = it + KS < n_tiles;
@@ -654,12 +761,12 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
           // this tile's V codes are in LDS: they were requested before the next tile's K
           if (has_next) wait_vm<kKLoads>();
           else wait_vm<0>();
-          widen_half(0);
+          widen_half(vt, v8_stage, 0);
           pv_tile(IntC<0>{}, IntC<DB / 2>{}, IntC<S::DV>{}, IntC<kHalfXm>{}, vt, pb_hi, pb_lo);
-          widen_half(1);
+          widen_half(vt, v8_stage, 1);
           // the staging area has been read: the next tile's V may land there
           if (has_next) {
-            load_v8_lds(tn);
+            load_v8_lds(v8_stage, tn);
             load_sc(ksc, vsc, tn);
           }
           pv_tile(IntC<DB / 2>{}, IntC<DB / 2>{}, IntC<S::DV>{}, IntC<kHalfXm>{}, vt, pb_hi, pb_lo);
@@ -735,9 +842,13 @@ template <bool HL, int PM, bool F8, class S>
 __global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void partition_gqa_kernel(PartArgs a, int HG, int KS) {
   extern __shared__ __attribute__((aligned(16))) char smem[];   // NW * S::kWaveBytes (launch size)
+
   __shared__ int pages_s[kMaxLdsPages];
   __shared__ PieceTable table;
   __shared__ int fuse_flag;
+  // everything a workgroup of kMaxWaves waves holds must fit the compute unit's LDS
+  static_assert(kMaxWaves * S::kWaveBytes + sizeof(pages_s) + sizeof(PieceTable) + sizeof(int) <= kLdsBytes,
+                "LDS budget");
   WaveInfo wv;
   wv.HG = HG;
   wv.KS = KS;
@@ -763,6 +874,7 @@ void partition_gqa_kernel(PartArgs a, int HG, int KS) {
     if ((int)blockIdx.x * a.chunk >= L) return;
   }
   zero_v_tile<S>(smem + wv.w * S::kWaveBytes, lane);
+
 
   // Equal shares: worker wid = blockIdx.x takes tiles [ts, te) of the U 32-key tiles of
   // all sequences concatenated in batch order (at least kMinShareTiles per worker, so
