@@ -625,6 +625,8 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
   auto load_v8_lds_asm = [&](char* stage, int t0, bool valid) {
     const int last = valid ? min(kTile - 1, end - 1 - t0) : -1;
     const int64_t row0 = tile_row0(t0);
+    // (no LDS wait is needed here: the staging tile's reads fed the widening arithmetic,
+    // so they have completed before this point)
     const int rr = lane / kV8Chunks, cc = lane % kV8Chunks;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -734,12 +736,21 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
           // this stage has been read: tile j + 2 may land there
           load_v8_lds_asm(stage, t2, has2);
         };
+        // (earlier LDS writes of this wave to the staging tiles, e.g. the zero fill, are
+        // complete before the first loads land there)
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
         issue(T, ksc0, vsc0, stage0, s0 + ks * kTile, true);
         issue(T1, ksc1, vsc1, stage1, s0 + (ks + KS) * kTile, ks + KS < n_tiles);
-        for (int it = ks; it < n_tiles; it += 2 * KS) {
+        // (pairs of tiles with no branch inside, so that the compiler's own waits for the K
+        // registers see the same loads in flight on every path; an odd last tile after)
+        int it = ks;
+        for (; it + KS < n_tiles; it += 2 * KS) {
           step(T, ksc0, vsc0, stage0, it);
-          if (it + KS < n_tiles) step(T1, ksc1, vsc1, stage1, it + KS);
+          step(T1, ksc1, vsc1, stage1, it + KS);
         }
+        if (it < n_tiles) step(T, ksc0, vsc0, stage0, it);
         wait_vm<0>();   // the empty-range loads past the last tile have retired
       } else if constexpr (F8) {
         // fp8 (wide V): K and the scales of the next tile in flight in registers, its V
