@@ -518,3 +518,33 @@ def test_workload_glm_style_sampled(name):
     rows = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 13, 31})
     O, LSE = oracle_for(case, batch_rows=rows)
     assert_parity(out[rows], lse[rows], o32[rows], O, LSE, what=f"{name} sampled")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_pieces_longer_than_one_page_segment(fp8):
+    # Two workers for one long sequence: each piece spans more than the 511 page indices
+    # staged in LDS at a time, so the kernel runs it as several segments (the fp8 loop keeps
+    # two tiles in flight and must not prefetch across a segment boundary).
+    print(f"[parity] multi-segment pieces fp8={fp8}", flush=True)
+    case = make_case("segments", batch=2, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=32,
+                     seq_lens=[40000, 333], seed=123, kv_fp8=fp8)
+    dc = to_device(case)
+    workers = 2
+    prob = api.make_problem(dc.q, dc.k_cache, dc.v_cache, dc.page_table, page_size=32)
+    po_t, pml_t = api.partition(dc.q, dc.k_cache, dc.v_cache, dc.page_table, dc.seq_lens, case.scale, 0, workers,
+                                page_size=32, k_scale=dc.k_scale, v_scale=dc.v_scale)
+    torch.cuda.synchronize()
+    lens = case.seq_lens.numpy().astype(np.int64)
+    pieces, first, count = equal_share_pieces(lens, workers)
+    assert max(hi - lo for _, lo, hi, _ in pieces) > 511 * 32
+    ks = None if case.k_scale is None else case.k_scale.numpy()
+    vs = None if case.v_scale is None else case.v_scale.numpy()
+    m, l, O = range_partials_fp64(np32(case.q), np32(case.k_cache), np32(case.v_cache), lens, case.scale, pieces,
+                                  page_table=case.page_table.numpy(), page_size=32, k_scale=ks, v_scale=vs)
+    ml_t, table = api.slot_table(prob, workers, pml_t)
+    S = len(pieces)
+    ml, po = np32(ml_t)[:S], np32(po_t)[:S]
+    np.testing.assert_allclose(ml[..., 0], m, rtol=1e-5, atol=1e-4)
+    np.testing.assert_allclose(ml[..., 1], l, rtol=1e-5)
+    err = np.abs(po - O).max(-1)
+    assert (err / np.abs(O).max(-1)).max() <= 1e-5
