@@ -152,16 +152,14 @@ struct IntC {
   static constexpr int value = V;
 };
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// Four E4M3 codes (one dword, byte 0 first) as two packed bf16 pairs, through the
-// hardware fp8 -> fp32 conversion (OCP E4M3; exact, as is the fp32 -> bf16 step).
+// Four E4M3 codes (one dword, byte 0 first) as two packed bf16 pairs, through the gfx950
+// scaled conversion with scale 1 (one instruction per pair; OCP E4M3, exact, since every
+// E4M3 value is a bf16 value; checked on all 256 codes on the GPU).
 __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
-  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
   u32x2 r;
-  r[0] = pack_bf16x2(lo[0], lo[1]);
-  r[1] = pack_bf16x2(hi[0], hi[1]);
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
   return r;
 }
 
