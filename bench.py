@@ -192,7 +192,7 @@ def main():
             traffic = tr.get("hbm_bytes_per_launch")
 
     result = {
-        "metric": "decode attention us/step + KV-read GB/s (% of HBM peak), 1 GPU",
+        "metric": "decode attention \u00b5s/step + KV-read GB/s (% of HBM peak), 1 GPU",
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
