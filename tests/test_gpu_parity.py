@@ -548,3 +548,35 @@ def test_pieces_longer_than_one_page_segment(fp8):
     np.testing.assert_allclose(ml[..., 1], l, rtol=1e-5)
     err = np.abs(po - O).max(-1)
     assert (err / np.abs(O).max(-1)).max() <= 1e-5
+
+
+# ---------------------------------------------------------------------------
+# size limits
+# ---------------------------------------------------------------------------
+def test_half_million_key_sequence():
+    # 2^19 keys in one sequence (8192 pages of 64): key, page and tile counts far beyond the
+    # workloads', through the automatic (equal-share) schedule
+    L = 1 << 19
+    case = make_case("512K", batch=1, num_q_heads=8, num_kv_heads=1, qk_depth=128, page_size=64, seq_lens=[L],
+                     num_splits=0, seed=124)
+    print("[parity] one sequence of 2^19 keys", flush=True)
+    out, lse, o32 = run(case)
+    O, LSE = oracle_for(case)
+    assert_parity(out, lse, o32, O, LSE, what="2^19 keys")
+
+
+def test_many_sequences_and_sixteen_queries():
+    # 4096 sequences of 1-40 keys (the schedule scans lengths 64 at a time) and, separately,
+    # 16 queries per sequence with one q head per kv head (all 16 MFMA columns in use)
+    case = make_case("many", batch=4096, num_q_heads=2, num_kv_heads=1, qk_depth=128, page_size=32,
+                     len_range=(0, 40), num_splits=0, seed=125)
+    print("[parity] 4096 short sequences", flush=True)
+    out, lse, o32 = run(case)
+    O, LSE = oracle_for(case)
+    assert_parity(out, lse, o32, O, LSE, what="4096 sequences")
+    case = make_case("q16", batch=3, num_q_heads=2, num_kv_heads=2, qk_depth=128, page_size=64,
+                     seq_lens=[15, 700, 2049], num_splits=0, seed=126, q_len=16)
+    print("[parity] q_len 16, one q head per kv head", flush=True)
+    out, lse, o32 = run(case)
+    O, LSE = oracle_for(case)
+    assert_parity(out, lse, o32, O, LSE, what="q_len 16")
