@@ -57,7 +57,7 @@ typedef enum {
 typedef enum {
   DA_KERNEL_AUTO = 0,    /* library's choice */
   DA_KERNEL_FMA = 1,     /* vector-ALU partition kernel (fp32 or bf16, group <= 16, depth 128) */
-  DA_KERNEL_MFMA = 2     /* matrix-core partition kernel (bf16 only) */
+  DA_KERNEL_MFMA = 2     /* matrix-core partition kernel (bf16 q; bf16 or fp8 caches) */
 } da_kernel;
 
 /* Shape and layout of one decode step. All sizes are element counts. */
