@@ -73,7 +73,10 @@ struct MShape {
   // fp8 caches stage V codes (32 x DV bytes per tile) beside a half-depth bf16 tile; at
   // V depth 128 the region has room for two staged tiles (two tiles in flight)
   static constexpr int kV8Tiles = DV == 128 ? 2 : 1;
-  static constexpr int kRegionBytes = kV8Tiles == 2 ? 3 * kTile * DV : kVBytes;
+  // bf16 caches at depth 128/128 also stage the K tile (32 x 256 bytes) in the region
+  static constexpr bool kKLds = DQK == 128 && DV == 128 && DR == 0;
+  static constexpr int kRegionBytes = kKLds ? 2 * kVBytes : (kV8Tiles == 2 ? 3 * kTile * DV : kVBytes);
+  static_assert(!kKLds || 3 * kTile * DV <= 2 * kVBytes, "the fp8 staging fits the region");
   static_assert(kRegionBytes >= kVBytes, "the region holds a bf16 V tile");
   static constexpr int kWaveBytes = kRegionBytes + 256;   // + merge (m, l) for up to 16 columns
   static_assert(DK % 64 == 0 && DR % 32 == 0 && (DV == 128 || DV == 256), "unsupported depths");
@@ -780,6 +783,72 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
           }
           pv_tile(IntC<DB / 2>{}, IntC<DB / 2>{}, IntC<S::DV>{}, IntC<kHalfXm>{}, vt, pb_hi, pb_lo);
         }
+      } else if constexpr (S::kKLds && PM != kPagedGeneral) {
+        // K through LDS as well: both tiles arrive by direct-to-LDS loads of 4 rows x 256
+        // bytes per instruction (16 rows x 64 bytes, the register layout of the A operand,
+        // streams markedly slower), issued as inline assembly with explicit waits. The K tile
+        // sits after the V tile in the wave's region, rows swizzled like V.
+        char* const kt = vt + S::kVBytes;
+        constexpr int kKD = 2 * kLoadsPerHalf, kVD = 2 * kLoadsPerHalf;   // loads per tile
+        auto load_tile_asm = [&](char* dst, const char* cache, uint32_t row_bytes, uint32_t slice, int t0) {
+          const int last = min(kTile - 1, end - 1 - t0);
+          const int64_t row0 = tile_row0(t0);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int rows = __builtin_amdgcn_readfirstlane(min(max(last + 1 - 16 * h, 0), 16));
+            const u32x4 rs = rsrc_words(cache + (row0 + 16 * h) * row_bytes + slice, (uint32_t)rows * row_bytes);
+#pragma unroll
+            for (int i = 0; i < kLoadsPerHalf; ++i) {
+              const int r = kRpi * i + v_row;
+              lds_dma16(rs, (uint32_t)r * row_bytes + 16 * (v_slot ^ (r & 15)),
+                        __builtin_amdgcn_readfirstlane(lds_addr(dst + (kLoadsPerHalf * h + i) * 1024)));
+            }
+          }
+        };
+        // S^T = K q^T with the K rows read from the LDS tile (chunk 4j + qd of row n + 16 blk)
+        auto score_lds = [&](f32x4* s) {
+#pragma unroll
+          for (int blk = 0; blk < 2; ++blk) {
+            s[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int r = n + 16 * blk;
+#pragma unroll
+            for (int j = 0; j < NJK; ++j) {
+              const bf16x8 kf = as_bf16x8(*(const u32x4*)(kt + r * S::kVRow + (((4 * j + qd) ^ (r & 15)) << 4)));
+              s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[j], s[blk], 0, 0, 0);
+            }
+          }
+        };
+        auto lds_quiet = [&] {   // this wave's LDS reads are complete (before a tile is refilled)
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          __builtin_amdgcn_s_waitcnt(0xC07F);
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        };
+        lds_quiet();
+        load_tile_asm(kt, kc, krow_bytes, kslice, s0 + ks * kTile);
+        load_tile_asm(vt, vc, vrow_bytes, vslice, s0 + ks * kTile);
+        for (int it = ks; it < n_tiles; it += KS) {
+          const bool has_next = it + KS < n_tiles;
+          const int tn = s0 + (it + KS) * kTile;
+          // this tile's K has landed (its V, requested after it, may still be in flight)
+          wait_vm<kVD>();
+          f32x4 s[2];
+          score_lds(s);
+          if (has_next) {
+            lds_quiet();
+            load_tile_asm(kt, kc, krow_bytes, kslice, tn);
+          }
+          bf16x8 pb_hi, pb_lo;
+          softmax_p(s, nullptr, s0 + it * kTile, pb_hi, pb_lo, nullptr, nullptr);
+          // this tile's V has landed (the next tile's K may stay in flight)
+          if (has_next) wait_vm<kKD>();
+          else wait_vm<0>();
+          pv(pb_hi, pb_lo);
+          if (has_next) {
+            lds_quiet();
+            load_tile_asm(vt, vc, vrow_bytes, vslice, tn);
+          }
+        }
+        wait_vm<0>();
       } else {
         // loads issued per tile: K (and rotary) first, then V; V of the current tile must
         // be in LDS before P.V while the next tile's K loads may stay in flight
