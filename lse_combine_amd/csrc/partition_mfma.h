@@ -7,14 +7,16 @@
 //
 // Work decomposition. A workgroup covers one partition p of one sequence b for HG
 // kv heads, with KS waves per kv head splitting the partition's keys (NW = HG * KS
-// <= 16 waves). Wave w serves kv head kg*HG + w % HG and takes the 32-key tiles
+// <= 8 waves). Wave w serves kv head kg*HG + w % HG and takes the 32-key tiles
 // ks, ks + KS, ... (ks = w / HG). With HG = 8 the waves of a workgroup read the
 // eight 256-byte kv-head slices of the same tokens, i.e. whole 2 KB token rows of
 // the paged cache; HG shrinks when that would leave too few workgroups for the chip.
+// Under the equal-share schedule a workgroup runs the pieces of its share one by one.
 //
 // Per tile, with v_mfma_f32_16x16x32_bf16:
-//   S^T[key][col] = K[key][:] . q[col][:]      A = K rows, 16-byte loads that land
-//                                              directly in the A-operand layout,
+//   S^T[key][col] = K[key][:] . q[col][:]      A = K rows: read from the wave's LDS K tile
+//                                              (bf16, depth 128) or loaded straight into
+//                                              the A-operand layout (wider depths, fp8),
 //                                              B = q (16 columns, see below)
 //   p = exp2((x - m_new) * c)                  online softmax in fp32; a lane owns one
 //                                              column and 8 keys, so the tile max needs
@@ -34,10 +36,9 @@
 // contiguous cache or pages of a power of two >= 32 keys a tile is 32 consecutive cache
 // rows: the tile base is a scalar and every lane adds a fixed 32-bit offset. The page
 // indices of the partition are staged in LDS once, so no dependent page-table load
-// sits between consecutive prefetches. One register tile per wave: the next tile's K
-// and V (16 KB per wave) are requested once the current tile sits in LDS and in the
-// score MFMAs, so they are in flight during its softmax and P.V; the small register
-// footprint lets three waves share a SIMD.
+// sits between consecutive prefetches. Loads run one tile ahead: the next tile's K is
+// requested once the current tile's scores are done and its V once the current P.V is
+// done (bf16); fp8 caches, half the bytes per tile, keep two tiles in flight.
 //
 // Epilogue: with KS = 1 every wave stores its own normalised partial and (m, l)
 // (fa4_splitk_combine_write, second paragraph), or the finished bf16 row when the
