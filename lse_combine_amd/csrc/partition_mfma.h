@@ -950,7 +950,10 @@ void partition_gqa_kernel(PartArgs a, int HG, int KS) {
     // fixed chunks: partition blockIdx.x of sequence blockIdx.z (sequence length loaded by a
     // vector load: state that it is uniform)
     const int L = __builtin_amdgcn_readfirstlane(attended_len(a, blockIdx.z, PM == kContiguous));
-    if ((int)blockIdx.x * a.chunk >= L) return;
+    // (with the fused combine there is no combine launch to write the rows of an empty
+    // sequence: its first workgroup writes them, as a piece without keys)
+    const bool empty_rows = L == 0 && blockIdx.x == 0 && a.counters && a.direct_single;
+    if ((int)blockIdx.x * a.chunk >= L && !empty_rows) return;
   }
   zero_v_tile<S>(smem + wv.w * S::kWaveBytes, lane);
 
@@ -996,6 +999,7 @@ void partition_gqa_kernel(PartArgs a, int HG, int KS) {
       start = p * a.chunk;
       end = min(start + a.chunk, L);
       count = min((L + a.chunk - 1) / a.chunk, a.max_splits);
+      if (L == 0) count = 1;   // the empty rows of the fused combine: finished in place
       first_slot = -1;
     } else {
       while (pending == 0) {
@@ -1026,25 +1030,33 @@ void partition_gqa_kernel(PartArgs a, int HG, int KS) {
             // (first slot, count) of each sequence for the combine, written by exactly one
             // worker: the one whose share holds the sequence's first tile (the last one
             // for trailing empty sequences)
-            if (blockIdx.y == 0 && bb < a.B) {
-              const int64_t writer = pre < U ? share_owner(pre, U, Wact) : Wact - 1;
-              if (writer == wid) {
-                a.meta[2 * bb] = slot;
-                a.meta[2 * bb + 1] = count;
-              }
+            const int64_t writer = pre < U ? share_owner(pre, U, Wact) : Wact - 1;
+            if (blockIdx.y == 0 && bb < a.B && writer == wid) {
+              a.meta[2 * bb] = slot;
+              a.meta[2 * bb + 1] = count;
             }
-            const bool mine = bb < a.B && nt > 0 && pre < te && pre + nt > ts;
+            // With the fused combine no combine launch writes the rows of an empty sequence:
+            // the same worker takes them as a piece without keys, finished in place.
+            const bool empty_rows = bb < a.B && nt == 0 && writer == wid && a.counters && a.direct_single;
+            const bool mine = (bb < a.B && nt > 0 && pre < te && pre + nt > ts) || empty_rows;
             mask = __ballot(mine);
             if (mine) {
-              const int64_t lo = (ts > pre ? ts : pre) - pre;
-              const int64_t hi = (te < pre + nt ? te : pre + nt) - pre;
               Piece pc;
               pc.b = bb;
-              pc.start = (int)lo * kTile;
-              pc.end = min((int)hi * kTile, len);
-              pc.slot = slot + (int)(wid - first);
-              pc.first_slot = slot;
-              pc.count = count;
+              if (nt == 0) {
+                pc.start = pc.end = 0;
+                pc.slot = slot;
+                pc.first_slot = slot;
+                pc.count = 1;
+              } else {
+                const int64_t lo = (ts > pre ? ts : pre) - pre;
+                const int64_t hi = (te < pre + nt ? te : pre + nt) - pre;
+                pc.start = (int)lo * kTile;
+                pc.end = min((int)hi * kTile, len);
+                pc.slot = slot + (int)(wid - first);
+                pc.first_slot = slot;
+                pc.count = count;
+              }
               table.row[lane] = pc;
             }
             tile_base += lane_value(incl, 63);

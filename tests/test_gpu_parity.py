@@ -221,6 +221,43 @@ def test_fused_combine_matches_oracle_on_repeated_calls(name, kw):
         assert_parity(out, lse, o32, O, LSE, what=f"fused {name} call {rep}")
 
 
+FUSED_EMPTY = [
+    ("fixed8_bf16", dict(batch=5, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=64,
+                         seq_lens=[0, 1, 33, 0, 2442], num_splits=8, seed=65)),
+    ("fixed3_fp8_d192", dict(batch=4, num_q_heads=8, num_kv_heads=2, qk_depth=192, ov_depth=128, page_size=32,
+                             seq_lens=[31, 0, 32, 0], num_splits=3, kv_fp8=True, seed=66)),
+    ("fixed1_contig", dict(batch=3, num_q_heads=8, num_kv_heads=1, qk_depth=128, seq_lens=[0, 2, 700],
+                           num_splits=1, seed=67)),
+    ("auto_bf16", dict(batch=6, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=64,
+                       seq_lens=[0, 3000, 0, 5, 0, 0], num_splits=0, seed=68)),
+    ("auto_all_empty", dict(batch=3, num_q_heads=8, num_kv_heads=1, qk_depth=128, page_size=64,
+                            seq_lens=[0, 0, 0], num_splits=0, seed=69)),
+]
+
+
+@pytest.mark.parametrize("name,kw", FUSED_EMPTY, ids=[c[0] for c in FUSED_EMPTY])
+def test_fused_combine_writes_rows_of_empty_sequences(name, kw):
+    # with the fused combine there is no combine launch: the rows of a sequence without
+    # keys (O = 0, LSE = -inf) must still be written; outputs start as NaN to show it
+    print(f"[parity] fused empty rows {name}", flush=True)
+    case = make_case(name, **kw)
+    dc = to_device(case)
+    prob = api.make_problem(dc.q, dc.k_cache, dc.v_cache, dc.page_table, page_size=case.page_size,
+                            ov_depth=case.ov_depth, k_rope=dc.k_rope)
+    ws = torch.zeros(api.workspace_bytes(prob, case.num_splits), dtype=torch.uint8, device="cuda")
+    rows = api.row_shape(prob)
+    out = torch.empty(rows + (prob.ov_depth,), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(rows, dtype=torch.float32, device="cuda")
+    o32 = torch.empty(rows + (prob.ov_depth,), dtype=torch.float32, device="cuda")
+    O, LSE = oracle_for(case)
+    for rep in range(2):
+        for t in (out, lse, o32):
+            t.fill_(float("nan"))
+        api.case_call(dc, out=out, lse=lse, o32=o32, fused=True, workspace=ws)
+        torch.cuda.synchronize()
+        assert_parity(out, lse, o32, O, LSE, what=f"fused empty rows {name} call {rep}")
+
+
 EQUAL_SHARE = [
     # name, make_case kwargs, workers
     ("ragged_paged64", dict(batch=5, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=64,
