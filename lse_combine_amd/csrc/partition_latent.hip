@@ -61,10 +61,6 @@ __device__ __forceinline__ float max_over_key_groups(float v) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Buffer-resource dword 3 for raw (untyped) dword loads on gfx9-family parts.
-constexpr int kRsrcWord3 = 0x00020000;
-// Cache policy of the K loads: non-temporal (each byte is read once per head block).
-constexpr int kLoadNT = 2;
 // Fixed reference max: the exponentials are taken relative to the first tile's max
 // m_ref and the 128 accumulator registers are never rescaled inside the key loop. That
 // holds while every score stays within kHeadroomLog2 powers of two of m_ref (p <= 2^64,

@@ -85,10 +85,6 @@ struct MShape {
 
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
-// Buffer-resource dword 3 for raw (untyped) dword loads on gfx9-family parts.
-constexpr int kRsrcWord3 = 0x00020000;
-// Cache policy of the K/V loads: non-temporal (each byte is read once per step).
-constexpr int kLoadNT = 2;
 
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kLoadNT));
@@ -103,53 +99,7 @@ struct KTile {
   u32x4 r[2][S::NR > 0 ? S::NR : 1];
 };
 
-// Wait until at most N vector-memory operations of this wave are outstanding
-// (s_waitcnt vmcnt(N), other counters untouched; gfx9 encoding: vmcnt bits 3:0 and 15:14,
-// expcnt 6:4 and lgkmcnt 11:8 at their no-wait maxima). The compiler fences keep the LDS
-// reads that depend on a direct-to-LDS load after the wait.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-// Buffer resource of `bytes` bytes at `base` (raw, stride 0), as four scalar words.
-__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
-  const uint64_t addr = (uint64_t)base;
-  u32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)addr);
-  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32) & 0xffffu);
-  r[2] = __builtin_amdgcn_readfirstlane(bytes);
-  r[3] = kRsrcWord3;
-  return r;
-}
-
-// Direct-to-LDS 16-byte buffer load (the 64 lanes fill 1 KB at LDS address lds_base, lane
-// l at 16 l; a lane outside the buffer range writes nothing), non-temporal, written as
-// inline assembly: the compiler does not see an LDS write, so it adds no wait of its own
-// before later LDS reads (it would wait for the most recent such load, whatever it
-// fills). Every consumer waits explicitly (wait_vm). M0, which holds the LDS base of the
-// instruction, is saved and restored around it.
-__device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t voff, uint32_t lds_base) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen nt lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(rsrc), "s"(lds_base)
-      : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const DA_LDS char*)p;
-}
 
 template <int V>
 struct IntC {
