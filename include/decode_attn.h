@@ -113,8 +113,8 @@ typedef struct da_problem {
  *    P_b = ceil(L_b / chunk_tokens) partitions (at most max_splits);
  *      part_ml  fp32 [B][Hq][max_splits][2] partition (m_p, l_p); m_p in raw q.k units
  *      part_o   fp32 [B][Hq][max_splits][Dv] normalised partition output O_p
- *  - equal shares (chunk_tokens == 0, max_splits = W workers; bf16 depth-128 matrix-core
- *    kernel only): the 32-key tiles of all sequences, laid end to end in batch order and
+ *  - equal shares (chunk_tokens == 0, max_splits = W workers; matrix-core kernel only):
+ *    the 32-key tiles of all sequences, laid end to end in batch order and
  *    numbered 0..U-1, are cut into W' = min(W, max(1, floor(U / 8))) shares, share w
  *    holding tiles floor(w U / W') .. floor((w+1) U / W') - 1; every overlap of a share
  *    with a sequence is one partition, and partitions are numbered ("slots") sequence
@@ -140,9 +140,10 @@ int da_supported(const da_problem* p);
  * to a multiple of the key tile (32) and of page_size when that is a multiple of 32;
  * max_splits = ceil(max_seq_len / chunk_tokens) (>= 1).
  * num_splits == 0: automatic choice for the device's num_cus compute units (num_cus <= 0:
- * query the current device): on the bf16 depth-128 matrix-core kernel the equal-share
- * schedule (chunk_tokens = 0, max_splits = workers, about one workgroup per CU), on the
- * other kernels fixed chunks sized for a few waves of workgroups. */
+ * query the current device): on the matrix-core kernel (bf16 q with separate K and V, any
+ * of its depth pairs and cache dtypes) the equal-share schedule (chunk_tokens = 0,
+ * max_splits = workers, about one workgroup per CU), on the other kernels fixed chunks
+ * sized for a few waves of workgroups. */
 int da_choose_splits(const da_problem* p, int32_t num_splits, int32_t num_cus,
                      int32_t* chunk_tokens, int32_t* max_splits);
 
@@ -167,9 +168,10 @@ int decode_attn_splitk(const da_problem* p, const void* q, const void* k_cache,
  * a (sequence, kv-head group) stores its partial, publishes it device-wide and counts
  * itself in on an arrival counter; the last one merges all partials of its heads and
  * writes out / lse_out / o_f32_out, then resets the counter. This saves the second
- * launch. Applied by the bf16 matrix-core depth-128 kernel when sequences have at most
- * 16 partitions (other problems run the two launches of decode_attn_splitk; the outputs
- * are the same either way). Same arguments and workspace size as decode_attn_splitk,
+ * launch. Applied by the matrix-core kernel (every depth pair and cache dtype it serves)
+ * when sequences have at most 16 partitions (other problems run the two launches of
+ * decode_attn_splitk; the outputs are the same either way). Rows of a sequence without
+ * keys are written too (O = 0, LSE = -inf), by one workgroup that holds no keys. Same arguments and workspace size as decode_attn_splitk,
  * with one more rule: the workspace must be zero-filled before its first use with this
  * function (the counters live in it and every call leaves them at zero), and calls that
  * share a workspace must not overlap. */

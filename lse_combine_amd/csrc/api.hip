@@ -117,8 +117,9 @@ int check_problem(const da_problem* p, Variant* var) {
     return DA_OK;
   }
   if (p->qk_depth != 128 || p->ov_depth != 128)
-    return fail(DA_EUNSUPPORTED, "supported depths: 128/128, or 576/512 latent-shared (got %d/%d)", p->qk_depth,
-                p->ov_depth);
+    return fail(DA_EUNSUPPORTED,
+                "supported depths (q.K / V): 128/128; 192/128 and 256/256 with bf16 q on the matrix-core kernel; "
+                "576/512 latent-shared (got %d/%d)", p->qk_depth, p->ov_depth);
   if (g > 16) return fail(DA_EUNSUPPORTED, "depth-128 kernels fuse at most 16 q heads per kv head (group %d)", g);
   if (p->dtype == DA_F32) {
     if (p->kernel == DA_KERNEL_MFMA) return fail(DA_EUNSUPPORTED, "the matrix-core kernel needs bf16 inputs");
