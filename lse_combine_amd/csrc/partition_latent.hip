@@ -4,17 +4,25 @@
 // Every q head of a sequence attends the same rows, so q.K and P.V are dense
 // contractions (about 240 flop per byte of KV) and run on v_mfma_f32_16x16x32_bf16.
 //
-// Workgroup = (partition p, block of 64 q heads, sequence b); four waves, each owning
-// 16 heads (one MFMA column block) and their full 512-wide output:
-//   S^T[key][head] = K[key][0:576] . q[head][0:576]   A = K from the LDS tile,
-//                                                      B = q from LDS (18 k-steps)
-//   O^T[d][head]  += V^T[d][key] . P^T[key][head]       A = V^T read transposed from the
-//                                                      same LDS tile (ds_read_b64_tr_b16),
-//                                                      B = P^T from the S^T registers
+// Workgroup = (partition p, block of 64 q heads, sequence b); eight waves, two per SIMD.
+// Wave w owns the 16 heads of head block w/2 (one MFMA column block) and depth half w%2
+// of both products:
+//   S^T[key][head] partial = K[key][288h : 288h+288] . q[head][288h : 288h+288]
+//       A = K from the LDS tile, B = q held in registers (9 k-steps); the two waves of a
+//       pair add their partials through a 2 KB-per-wave LDS exchange, so both hold the
+//       full scores and take the same softmax
+//   O^T[d][head] += V^T[d][key] . P^T[key][head]   for d in depth half w%2 of V (256)
+//       A = V^T read transposed from the same LDS tile (ds_read_b64_tr_b16); B = P^T from
+//       the score registers
+// Splitting both products by depth halves the fp32 accumulators a wave holds (64
+// registers for 16 heads x 256 columns), so that two waves fit on each SIMD and hide each
+// other's LDS operand latency; with one wave per SIMD the operand reads, not the matrix
+// cores, set the pace.
 // P is split hi/lo in bf16 (two MFMAs per depth block) so that the fp32 O keeps ~16
 // significant bits of the weights. The K tile (32 keys x 1152 B, 16-byte chunks XOR
-// swizzled within groups of 8) is double-buffered in LDS: the next tile's global loads
-// are in flight while the current tile is computed. The two head blocks of a
+// swizzled within groups of 8) is double-buffered in LDS: the next tile's direct-to-LDS
+// loads are in flight while the current tile is computed (a third buffer, two tiles in
+// flight, measured slower). The two head blocks of a
 // (sequence, partition) get workgroup ids 8 apart, so they run on the same XCD and the
 // second read of each K tile is an L2 hit.
 // Epilogue as in the GQA kernel: normalised partial + (m, l) per head, or the finished
@@ -31,13 +39,19 @@ constexpr int kTile = 32;
 constexpr int kChunks = kDqk / 8;               // 16-byte chunks per K row (72)
 constexpr int kRowBytes = kDqk * 2;             // 1152
 constexpr int kTileBytes = kTile * kRowBytes;   // 36 KB
-constexpr int kHeadsPerWave = 16;
-constexpr int kWaves = 4;
-constexpr int kHeadsPerWG = kHeadsPerWave * kWaves;   // 64
-constexpr int kQBytes = kHeadsPerWG * kRowBytes;      // 72 KB
+// MFMA column blocks (16 heads) per wave: each K / V operand read serves all of them,
+// at 64 accumulator registers each (two blocks measured no faster at one wave per SIMD)
+constexpr int kCB = 1;
+constexpr int kHeadsPerWave = 16 * kCB;
+constexpr int kWaves = 8;                             // 4 head blocks x 2 depth halves
+constexpr int kHeadsPerWG = kHeadsPerWave * kWaves / 2;   // 64
+constexpr int kQkSteps = kDqk / 2 / 32;               // k-steps of 32 per depth half of q.K (9)
+constexpr int kDvBlocks = kDv / 2 / 16;               // 16-wide depth blocks per half of V (16)
 constexpr int kThreads = kWaves * 64;
-constexpr int kStage = (kTile * kChunks) / kThreads;  // 16-byte chunks per thread per tile (9)
+constexpr int kTileBlocks = kTileBytes / 1024;         // 1 KB direct-to-LDS loads per tile (36)
+constexpr int kStage = (kTileBlocks + kWaves - 1) / kWaves;   // ... per wave, at most (5)
 constexpr int kMaxLdsPages = 256;
+constexpr int kRing = 2;   // K tiles in LDS: one in flight while the other is computed
 
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
@@ -70,9 +84,9 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 constexpr float kHeadroomLog2 = 64.f;
 
 template <int PM>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void partition_latent_kernel(PartArgs a) {
-  const int p = blockIdx.x, hb = blockIdx.y, b = blockIdx.z;
+  const int p = blockIdx.x, hblk = blockIdx.y, b = blockIdx.z;
   const int L = __builtin_amdgcn_readfirstlane(attended_len(a, b, PM == kContiguous));
   const int start = p * a.chunk;
   if (start >= L) return;
@@ -82,34 +96,37 @@ void partition_latent_kernel(PartArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int dh = w & 1;                      // depth half of q.K and of V
   const int n = lane & 15, qd = lane >> 4;
   const int g = a.g;
-  const int head0 = hb * kHeadsPerWG + w * kHeadsPerWave;   // first q head of this wave
-  const bool wave_active = head0 < g;
+  const int head0 = hblk * kHeadsPerWG + (w >> 1) * kHeadsPerWave;   // first q head of this wave
   const float c = a.c;
 
-  // Two K tiles as two distinct LDS arrays: the compiler then sees that reads of one tile
-  // do not depend on the direct-to-LDS loads still filling the other, and waits for
-  // those loads only where a tile is consumed.
-  __shared__ __attribute__((aligned(16))) char kt0[kTileBytes];
-  __shared__ __attribute__((aligned(16))) char kt1[kTileBytes];
-  extern __shared__ __attribute__((aligned(16))) char qs[];   // q block, kQBytes
+  // Two K tiles. Their direct-to-LDS loads are inline assembly (lds_dma16): the compiler
+  // sees no LDS write and adds no wait of its own before the LDS reads of the other tile;
+  // a tile is read only after the explicit wait and barrier at the top of its step.
+  constexpr int kRingX = 2;
+  __shared__ __attribute__((aligned(16))) char ktile[kRingX][kTileBytes];
+  // partial scores of each wave, lane-major (16 floats per lane), read by its partner
+  __shared__ __attribute__((aligned(16))) f32x4 xchg[kWaves][2 * kCB][64];
   __shared__ int pages_s[kMaxLdsPages];
 
   // Rows that a ragged tile does not load keep what the buffer held: zero both tiles
   // once so that such rows are finite (their scores are masked, their V meets p = 0).
-  for (int i = tid; i < kTileBytes / 16; i += kThreads) {
-    *(u32x4*)(kt0 + i * 16) = u32x4{0u, 0u, 0u, 0u};
-    *(u32x4*)(kt1 + i * 16) = u32x4{0u, 0u, 0u, 0u};
-  }
-  // q block -> LDS (rows beyond the group are zero)
-  {
-    const uint16_t* qb = (const uint16_t*)a.q + ((int64_t)b * a.Hq + (int64_t)hb * kHeadsPerWG) * kDqk;
-    for (int cid = tid; cid < kHeadsPerWG * kChunks; cid += kThreads) {
-      const int h = cid / kChunks, ch = cid % kChunks;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (hb * kHeadsPerWG + h < g) v = *(const u32x4*)(qb + (int64_t)h * kDqk + ch * 8);
-      *(u32x4*)(qs + swz(h, ch)) = v;
+  for (int i = tid; i < kRingX * kTileBytes / 16; i += kThreads) *(u32x4*)(&ktile[0][0] + i * 16) = u32x4{0u, 0u, 0u, 0u};
+  // q as the B operand of S^T = K q^T, in registers for the wave's whole piece: column
+  // block cb, k-step j holds depth 288 dh + 32 j + 8 qd .. +8 of head head0 + 16 cb + n
+  // (zero past the group)
+  bf16x8 qf[kCB][kQkSteps];
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb) {
+    const int h = head0 + 16 * cb + n;
+    const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)b * a.Hq + (h < g ? h : 0)) * kDqk + 288 * dh + 8 * qd;
+#pragma unroll
+    for (int j = 0; j < kQkSteps; ++j) {
+      u32x4 v = *(const u32x4*)(qrow + 32 * j);
+      if (h >= g) v = u32x4{0u, 0u, 0u, 0u};
+      qf[cb][j] = as_bf16x8(v);
     }
   }
   // page indices of the partition (one segment: chunks of at most (kMaxLdsPages-1)*page keys)
@@ -152,20 +169,21 @@ void partition_latent_kernel(PartArgs a) {
         row0 = ((int64_t)page << a.page_shift) + (t0 & (a.page_size - 1));
       }
       const int rows = __builtin_amdgcn_readfirstlane(last + 1);
-      const __amdgpu_buffer_rsrc_t rk =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(kc + row0 * kRowBytes), 0, rows * kRowBytes, kRsrcWord3);
+      const u32x4 rk = rsrc_words(kc + row0 * kRowBytes, (uint32_t)(rows * kRowBytes));
+      const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(dst) + w * 1024);
 #pragma unroll
       for (int i = 0; i < kStage; ++i) {
+        if (w + kWaves * i >= kTileBlocks) break;   // (uniform: the tile has 36 blocks of 1 KB)
         int r, gc;
         lane_chunk(i, r, gc);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (DA_LDS void*)(dst + (w + kWaves * i) * 1024), 16,
-                                                 (uint32_t)(r * kRowBytes + gc * 16), 0, 0, kLoadNT);
+        lds_dma16(rk, (uint32_t)(r * kRowBytes + gc * 16), lb + kWaves * 1024 * i);
       }
     } else {
       // any page size: every lane looks up its own row (rows past the end repeat the
       // last key; their scores are masked)
 #pragma unroll
       for (int i = 0; i < kStage; ++i) {
+        if (w + kWaves * i >= kTileBlocks) break;
         int r, gc;
         lane_chunk(i, r, gc);
         const int t = t0 + min(r, last);
@@ -179,75 +197,141 @@ void partition_latent_kernel(PartArgs a) {
     }
   };
 
-  float m_ref = -INFINITY;   // reference max of the exponentials (raw units)
-  float m_true = -INFINITY;  // exact running max
-  float l_run = 0.f;
+  // per column block cb: reference max of the exponentials (raw units), exact running
+  // max, running sum (this lane's keys)
+  float m_ref[kCB], m_true[kCB], l_run[kCB];
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb) {
+    m_ref[cb] = -INFINITY;
+    m_true[cb] = -INFINITY;
+    l_run[cb] = 0.f;
+  }
   bool beyond = false;       // a score exceeded m_ref by more than the headroom
-  f32x4 o[kDv / 16];
+  f32x4 o[kCB][kDvBlocks];
 
   auto compute = [&](const char* K, int t0) {
-    if (!wave_active) return;
-    // S^T = K q^T: keys 16*blk + (4qd..+3) of column (head) n
-    f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    // S^T partial over this wave's depth half: keys 16 blk + (4qd..+3) of column n of
+    // column block cb; each K operand serves every column block
+    // (k-step j of depth half dh is chunk 4 jj + qd, jj = 9 dh + j, of row r; under the
+    // swizzle that is byte 128 (jj >> 1) + 16 ((4 (jj & 1) + qd) ^ (r & 7)) of the row, so
+    // two per-lane bases per row, one per parity of jj, and constant offsets cover all
+    // k-steps)
+    f32x4 s[kCB][2];
 #pragma unroll
-    for (int j = 0; j < kChunks / 4; ++j) {
-      const bf16x8 qf = as_bf16x8(*(const u32x4*)(qs + swz(w * kHeadsPerWave + n, 4 * j + qd)));
+    for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        const bf16x8 kf = as_bf16x8(*(const u32x4*)(K + swz(n + 16 * blk, 4 * j + qd)));
-        s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf, s[blk], 0, 0, 0);
-      }
-    }
+      for (int blk = 0; blk < 2; ++blk) s[cb][blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const DA_LDS char* KL = (const DA_LDS char*)K;
+    // k-step j = 2m (even) of depth half dh reads from pe + 128 m, j = 2m + 1 from po + 128 m
+    const int kr = n * kRowBytes;   // row n of key block 0; block 1 is 16 rows on
+    const DA_LDS char* pe = KL + kr + 16 * ((4 * dh + qd) ^ (n & 7)) + 512 * dh;
+    const DA_LDS char* po = KL + kr + 16 * ((4 * (1 - dh) + qd) ^ (n & 7)) + 640 * dh;
+    bf16x8 kf[kQkSteps][2];
+#pragma unroll
+    for (int j = 0; j < kQkSteps; ++j)
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+        kf[j][blk] = as_bf16x8(*(const DA_LDS u32x4*)((j & 1 ? po : pe) + 128 * (j >> 1) + 16 * blk * kRowBytes));
+    // (all 18 operand reads are issued before the first product)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < kQkSteps; ++j)
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int cb = 0; cb < kCB; ++cb)
+          s[cb][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j][blk], qf[cb][j], s[cb][blk], 0, 0, 0);
+    // the partner wave (other depth half, same heads) adds its partial: both waves then
+    // hold the full scores. A wave rewrites its slot only after the next tile's barrier,
+    // which its partner passes after reading it.
+#pragma unroll
+    for (int k = 0; k < 2 * kCB; ++k) xchg[w][k][lane] = s[k >> 1][k & 1];
+    __syncthreads();
+    f32x4 sp[2 * kCB];
+#pragma unroll
+    for (int k = 0; k < 2 * kCB; ++k) sp[k] = xchg[w ^ 1][k][lane];
+    // O^T += V^T P^T over this wave's depth half; V^T A operand: depth 16 db + n of keys
+    // 4qd..+3 and 16+4qd..+3, shared by every column block. Depth block d = 16 dh + db is
+    // chunk 2d + ((n & 3) >> 1) of rows ra and rb = ra + 16; under the swizzle that is byte
+    // 128 (d >> 2) + 16 ((2 (d & 3) + ((n & 3) >> 1)) ^ (ra & 7)) of the row (rb & 7 =
+    // ra & 7): four per-lane bases and constant offsets
+    const int ra = 4 * qd + (n >> 2);
+    const int sub = (n & 1) * 8;
+    const DA_LDS char* vbase[4];
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4)
+      vbase[v4] = KL + ra * kRowBytes + 16 * ((2 * v4 + ((n & 3) >> 1)) ^ (ra & 7)) + sub + 128 * 4 * dh;
+    auto load_v = [&](int db) {
+      const DA_LDS char* pa = vbase[db & 3] + 128 * (db >> 2);
+      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 DA_LDS*)pa);
+      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 DA_LDS*)(pa + 16 * kRowBytes));
+      s16x8 v8;
+      v8[0] = va[0]; v8[1] = va[1]; v8[2] = va[2]; v8[3] = va[3];
+      v8[4] = vb[0]; v8[5] = vb[1]; v8[6] = vb[2]; v8[7] = vb[3];
+      return __builtin_bit_cast(bf16x8, v8);
+    };
+    // the first V^T operands are requested before the softmax, the rest kAhead depth
+    // blocks ahead of their products (the scheduling barriers keep that order)
+    constexpr int kAhead = 6;
+    bf16x8 vf[kDvBlocks];
+#pragma unroll
+    for (int db = 0; db < kAhead; ++db) vf[db] = load_v(db);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 2 * kCB; ++k) s[k >> 1][k & 1] += sp[k];
     // online softmax (missing keys of a ragged tile get -inf, i.e. p = 0)
     const int nvalid = end - t0;
     if (nvalid < kTile) {
 #pragma unroll
+      for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (16 * blk + 4 * qd + i >= nvalid) s[cb][blk][i] = -INFINITY;
+    }
+    bf16x8 pb_hi[kCB], pb_lo[kCB];
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+      const f32x4* sc = s[cb];
+      float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                       fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+      mx = max_over_key_groups(mx);
+      m_true[cb] = fmaxf(m_true[cb], mx);
+      m_ref[cb] = m_ref[cb] == -INFINITY ? mx : m_ref[cb];   // first tile of the pass: O and l are still 0
+      beyond = beyond || (mx - m_ref[cb]) * c > kHeadroomLog2;
+      const float mc = m_ref[cb] * c;
+      float pr[2][4];
+#pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (16 * blk + 4 * qd + i >= nvalid) s[blk][i] = -INFINITY;
-    }
-    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    mx = max_over_key_groups(mx);
-    m_true = fmaxf(m_true, mx);
-    m_ref = m_ref == -INFINITY ? mx : m_ref;   // first tile of the pass: O and l are still 0
-    beyond = beyond || (mx - m_ref) * c > kHeadroomLog2;
-    const float mc = m_ref * c;
-    float pr[2][4];
+        for (int i = 0; i < 4; ++i) {
+          pr[blk][i] = exp2_fast(fmaf(sc[blk][i], c, -mc));
+          l_run[cb] += pr[blk][i];
+        }
+      // P^T (B operand), hi and lo parts
+      uint32_t hw[4], lw[4];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pr[blk][i] = exp2_fast(fmaf(s[blk][i], c, -mc));
-        l_run += pr[blk][i];
+      for (int s2 = 0; s2 < 4; ++s2) {
+        const int blk = s2 >> 1, i0 = (s2 & 1) * 2;
+        const float p0 = pr[blk][i0], p1 = pr[blk][i0 + 1];
+        const uint32_t hv = pack_bf16x2(p0, p1);
+        hw[s2] = hv;
+        lw[s2] = pack_bf16x2(p0 - bf16lo(hv), p1 - bf16hi(hv));
       }
-    // P^T (B operand), hi and lo parts
-    uint32_t hw[4], lw[4];
-#pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) {
-      const int blk = s2 >> 1, i0 = (s2 & 1) * 2;
-      const float p0 = pr[blk][i0], p1 = pr[blk][i0 + 1];
-      const uint32_t h = pack_bf16x2(p0, p1);
-      hw[s2] = h;
-      lw[s2] = pack_bf16x2(p0 - bf16lo(h), p1 - bf16hi(h));
+      pb_hi[cb] = as_bf16x8(u32x4{hw[0], hw[1], hw[2], hw[3]});
+      pb_lo[cb] = as_bf16x8(u32x4{lw[0], lw[1], lw[2], lw[3]});
     }
-    const bf16x8 pb_hi = as_bf16x8(u32x4{hw[0], hw[1], hw[2], hw[3]});
-    const bf16x8 pb_lo = as_bf16x8(u32x4{lw[0], lw[1], lw[2], lw[3]});
-    // O^T += V^T P^T; V^T A operand: depth 16db + n of keys 4qd..+3 and 16+4qd..+3
-    const int ra = 4 * qd + (n >> 2), rb = ra + 16;
-    const int sub = (n & 1) * 8;
 #pragma unroll
-    for (int db = 0; db < kDv / 16; ++db) {
-      const int ch = 2 * db + ((n & 3) >> 1);
-      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 DA_LDS*)(K + swz(ra, ch) + sub));
-      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 DA_LDS*)(K + swz(rb, ch) + sub));
-      s16x8 v8;
-      v8[0] = va[0]; v8[1] = va[1]; v8[2] = va[2]; v8[3] = va[3];
-      v8[4] = vb[0]; v8[5] = vb[1]; v8[6] = vb[2]; v8[7] = vb[3];
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, v8);
-      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb_hi, o[db], 0, 0, 0);
-      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb_lo, o[db], 0, 0, 0);
+    for (int db = 0; db < kDvBlocks; ++db) {
+      if (db + kAhead < kDvBlocks) vf[db + kAhead] = load_v(db + kAhead);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int cb = 0; cb < kCB; ++cb) {
+        o[cb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pb_hi[cb], o[cb][db], 0, 0, 0);
+        o[cb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pb_lo[cb], o[cb][db], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -256,49 +340,54 @@ void partition_latent_kernel(PartArgs a) {
   // if some score left the headroom of m_ref (then m_ref = the exact max: no second miss).
   const int n_tiles = (end - start + kTile - 1) / kTile;
   for (int pass = 0; pass < 2; ++pass) {
-    l_run = 0.f;
 #pragma unroll
-    for (int db = 0; db < kDv / 16; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    issue(kt0, start);
-    for (int it = 0; it < n_tiles; it += 2) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's part of tile it is in LDS
-      __syncthreads();                      // ... and every wave's; tile it-1 is retired
-      if (it + 1 < n_tiles) issue(kt1, start + (it + 1) * kTile);
-      compute(kt0, start + it * kTile);
-      if (it + 1 >= n_tiles) break;
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      __syncthreads();
-      if (it + 2 < n_tiles) issue(kt0, start + (it + 2) * kTile);
-      compute(kt1, start + (it + 1) * kTile);
+    for (int cb = 0; cb < kCB; ++cb) {
+      l_run[cb] = 0.f;
+#pragma unroll
+      for (int db = 0; db < kDvBlocks; ++db) o[cb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    issue(ktile[0], start);
+    for (int it = 0; it < n_tiles; ++it) {
+      wait_vm<0>();      // this wave's part of tile it is in LDS
+      __syncthreads();   // ... and every wave's; tile it-1 is retired (its reads have returned)
+      if (it + 1 < n_tiles) issue(ktile[(it + 1) & 1], start + (it + 1) * kTile);
+      compute(ktile[it & 1], start + it * kTile);
     }
     // every wave is past its last LDS read before a second pass refills the tiles
     if (!__syncthreads_or(beyond)) break;
-    m_ref = m_true;
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) m_ref[cb] = m_true[cb];
     beyond = false;
   }
 
   // O and l are relative to m_ref; the partial reports the exact max, so its sum is
-  // rescaled once (the normalised O does not change).
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  const int hq = head0 + n;   // q head of this lane's column (within the kv head's group)
-  if (wave_active && hq < g) {
-    const float inv = 1.f / l_run;
-    const float l_true = l_run * exp2_fast((m_ref - m_true) * c);
+  // rescaled once (the normalised O does not change). Both waves of a pair hold the
+  // same (m, l): the depth-half-0 wave writes them.
 #pragma unroll
-    for (int db = 0; db < kDv / 16; ++db)
-      store_unit(a, b, hq, p, direct, 16 * db + 4 * qd, o[db] * inv, m_true, l_true, db == 0 && qd == 0);
+  for (int cb = 0; cb < kCB; ++cb) {
+    float l = l_run[cb];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const int hq = head0 + 16 * cb + n;   // q head of this lane's column (within the kv head's group)
+    if (hq < g) {
+      const float inv = 1.f / l;
+      const float l_true = l * exp2_fast((m_ref[cb] - m_true[cb]) * c);
+#pragma unroll
+      for (int db = 0; db < kDvBlocks; ++db)
+        store_unit(a, b, hq, p, direct, 256 * dh + 16 * db + 4 * qd, o[cb][db] * inv, m_true[cb], l_true,
+                   db == 0 && qd == 0 && dh == 0);
+    }
   }
 }
 
 }  // namespace
 
 hipError_t launch_partition_latent(const PartArgs& a, int page_mode, hipStream_t s) {
-  if (a.Dqk != kDqk || a.Dv != kDv || a.Hkv != 1 || a.g % kHeadsPerWave) return hipErrorInvalidValue;
+  if (a.Dqk != kDqk || a.Dv != kDv || a.Hkv != 1 || a.g % 16) return hipErrorInvalidValue;
   // x = partition, y = 64-head block, z = sequence: with 8 partitions the two head blocks
   // of a (sequence, partition) are 8 workgroup ids apart (same XCD under round-robin dispatch)
   dim3 grid(a.max_splits, (a.g + kHeadsPerWG - 1) / kHeadsPerWG, a.B), block(kThreads);
-  const size_t lds = kQBytes;   // (the two K tiles are static)
+  const size_t lds = 0;   // (the K tiles and the exchange are static)
   switch (page_mode) {
     case kContiguous:
       hipLaunchKernelGGL(partition_latent_kernel<kContiguous>, grid, block, lds, s, a);
