@@ -39,8 +39,9 @@ constexpr int kTile = 32;
 constexpr int kChunks = kDqk / 8;               // 16-byte chunks per K row (72)
 constexpr int kRowBytes = kDqk * 2;             // 1152
 constexpr int kTileBytes = kTile * kRowBytes;   // 36 KB
-// MFMA column blocks (16 heads) per wave: each K / V operand read serves all of them,
-// at 64 accumulator registers each (two blocks measured no faster at one wave per SIMD)
+// MFMA column blocks (16 heads) per wave: each K / V operand read serves all of them, at
+// 64 accumulator registers each. Two blocks leave room for one wave per SIMD only, and
+// measured no faster.
 constexpr int kCB = 1;
 constexpr int kHeadsPerWave = 16 * kCB;
 constexpr int kWaves = 8;                             // 4 head blocks x 2 depth halves
@@ -105,15 +106,15 @@ void partition_latent_kernel(PartArgs a) {
   // Two K tiles. Their direct-to-LDS loads are inline assembly (lds_dma16): the compiler
   // sees no LDS write and adds no wait of its own before the LDS reads of the other tile;
   // a tile is read only after the explicit wait and barrier at the top of its step.
-  constexpr int kRingX = 2;
-  __shared__ __attribute__((aligned(16))) char ktile[kRingX][kTileBytes];
-  // partial scores of each wave, lane-major (16 floats per lane), read by its partner
+  __shared__ __attribute__((aligned(16))) char ktile[kRing][kTileBytes];
+  // partial scores of each wave, lane-major (8 floats per lane and column block), read by
+  // its partner
   __shared__ __attribute__((aligned(16))) f32x4 xchg[kWaves][2 * kCB][64];
   __shared__ int pages_s[kMaxLdsPages];
 
   // Rows that a ragged tile does not load keep what the buffer held: zero both tiles
   // once so that such rows are finite (their scores are masked, their V meets p = 0).
-  for (int i = tid; i < kRingX * kTileBytes / 16; i += kThreads) *(u32x4*)(&ktile[0][0] + i * 16) = u32x4{0u, 0u, 0u, 0u};
+  for (int i = tid; i < kRing * kTileBytes / 16; i += kThreads) *(u32x4*)(&ktile[0][0] + i * 16) = u32x4{0u, 0u, 0u, 0u};
   // q as the B operand of S^T = K q^T, in registers for the wave's whole piece: column
   // block cb, k-step j holds depth 288 dh + 32 j + 8 qd .. +8 of head head0 + 16 cb + n
   // (zero past the group)
@@ -143,7 +144,7 @@ void partition_latent_kernel(PartArgs a) {
   __syncthreads();
 
   // The K tile of keys t0 .. t0+31 lands in LDS by direct-to-LDS 16-byte loads: wave w
-  // fills the 1 KB blocks w, w+4, ..., so lane l of block j writes tile byte j*1024 + 16l,
+  // fills the 1 KB blocks w, w+8, ..., so lane l of block j writes tile byte j*1024 + 16l,
   // i.e. row r and chunk slot s of the swizzled layout, and loads the cache chunk
   // s ^ (r & 7) of row r there (the XOR swizzle is its own inverse).
   const char* kc = (const char*)a.k;
