@@ -78,6 +78,10 @@ CASES = [
     ("latent_g48_paged16_general", dict(batch=2, num_q_heads=48, num_kv_heads=1, qk_depth=576, ov_depth=512,
                                         page_size=16, seq_lens=[517, 64], num_splits=0, seed=36,
                                         v_is_k_prefix=True), "auto"),
+    # 80 heads: one full block of 64 and a second block with one of its four head blocks
+    ("latent_g80_paged32", dict(batch=3, num_q_heads=80, num_kv_heads=1, qk_depth=576, ov_depth=512,
+                                page_size=32, seq_lens=[1025, 32, 2], num_splits=4, seed=37,
+                                v_is_k_prefix=True), "auto"),
 ]
 
 
@@ -131,6 +135,26 @@ def test_large_logits_overflow_safety():
     O, LSE = oracle_for(case)
     assert torch.isfinite(o32).all()
     assert_parity(out, lse, o32, O, LSE, o32_row_rtol=1e-4, what="large logits")
+
+
+def test_latent_fused_entry_point_falls_back_to_two_launches():
+    # the fused entry point on a latent-shared problem runs the partition and combine
+    # launches; outputs (rows of an empty sequence included) match the oracle
+    print("[parity] latent through the fused entry point", flush=True)
+    case = make_case("latent_fused", batch=3, num_q_heads=64, num_kv_heads=1, qk_depth=576, ov_depth=512,
+                     page_size=64, seq_lens=[900, 0, 65], num_splits=2, seed=38, v_is_k_prefix=True)
+    dc = to_device(case)
+    prob = api.make_problem(dc.q, dc.k_cache, dc.v_cache, dc.page_table, page_size=case.page_size,
+                            v_is_k_prefix=True, ov_depth=case.ov_depth)
+    ws = torch.zeros(api.workspace_bytes(prob, case.num_splits), dtype=torch.uint8, device="cuda")
+    rows = api.row_shape(prob)
+    out = torch.full(rows + (prob.ov_depth,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full(rows, float("nan"), dtype=torch.float32, device="cuda")
+    o32 = torch.full(rows + (prob.ov_depth,), float("nan"), dtype=torch.float32, device="cuda")
+    api.case_call(dc, out=out, lse=lse, o32=o32, fused=True, workspace=ws)
+    torch.cuda.synchronize()
+    O, LSE = oracle_for(case)
+    assert_parity(out, lse, o32, O, LSE, what="latent fused entry point")
 
 
 def test_latent_large_logits_take_the_second_pass():
