@@ -9,6 +9,9 @@ A step is one call of decode_attn_splitk (partition kernel + LSE combine) on
 inputs already resident in HBM. Output: one JSON line with
   value          KV-read GB/s of the whole step (algorithmic bytes: attended keys
                  x kv heads x (Dqk + Dv) x 2 B) ; us_per_step alongside
+  step_us_events per-step HIP-event times (p10 / median / p90): back to back, and with
+                 the Infinity Cache flushed before every step (1 GiB read and written
+                 outside the events), so that inputs under 256 MiB are not served from it
   roofline       the partition kernel alone, timed with HIP events on its stream,
                  against the 8 TB/s HBM peak; traffic from the committed
                  rocprofv3 counter summary when it matches the current source
@@ -141,6 +144,31 @@ def main():
     s_per_step = (t1 - t0) / args.steps
     value = kv_bytes / s_per_step / 1e9
 
+    # --- per-step HIP-event times: back to back, and after flushing the Infinity Cache ---
+    # (a step's inputs under 256 MiB can otherwise be served from the memory-side cache of
+    # the step before; the flush reads and writes 1 GiB outside the events)
+    flush_buf = torch.zeros(1 << 30, dtype=torch.uint8, device=dev)
+    n_ev = max(args.steps, 10)
+
+    def event_steps(flush):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+        for e0, e1 in evs:
+            if flush:
+                flush_buf.add_(1)
+            e0.record()
+            step()
+            e1.record()
+        torch.cuda.synchronize()
+        us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+        pick = lambda f: us[min(len(us) - 1, int(f * len(us)))]
+        med = statistics.median(us)
+        return {"p10": round(pick(0.1), 2), "median": round(med, 2), "p90": round(pick(0.9), 2),
+                "kv_GBps_median": round(kv_bytes / (med * 1e-6) / 1e9, 1)}
+
+    step_hot = event_steps(False)
+    step_flushed = event_steps(True)
+    del flush_buf
+
     # --- the partition kernel alone (same kernels, launched pass by pass) ---
     # arguments are marshalled once so the host stays ahead of the GPU and the
     # events bracket only the kernels
@@ -201,6 +229,8 @@ def main():
         "ms_per_step": round(s_per_step * 1e3, 4),
         "us_per_step": round(s_per_step * 1e6, 2),
         "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
+        "step_us_events": step_hot,
+        "step_us_events_cache_flushed": step_flushed,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
