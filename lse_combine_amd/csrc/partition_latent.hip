@@ -5,26 +5,29 @@
 // contractions (about 240 flop per byte of KV) and run on v_mfma_f32_16x16x32_bf16.
 //
 // Workgroup = (partition p, block of 64 q heads, sequence b); eight waves, two per SIMD.
-// Wave w owns the 16 heads of head block w/2 (one MFMA column block) and depth half w%2
-// of both products:
-//   S^T[key][head] partial = K[key][288h : 288h+288] . q[head][288h : 288h+288]
-//       A = K from the LDS tile, B = q held in registers (9 k-steps); the two waves of a
-//       pair add their partials through a 2 KB-per-wave LDS exchange, so both hold the
-//       full scores and take the same softmax
-//   O^T[d][head] += V^T[d][key] . P^T[key][head]   for d in depth half w%2 of V (256)
-//       A = V^T read transposed from the same LDS tile (ds_read_b64_tr_b16); B = P^T from
-//       the score registers
-// Splitting both products by depth halves the fp32 accumulators a wave holds (64
-// registers for 16 heads x 256 columns), so that two waves fit on each SIMD and hide each
-// other's LDS operand latency; with one wave per SIMD the operand reads, not the matrix
-// cores, set the pace.
+// Each wave has two roles, one per product:
+//   q.K: wave w takes the 16 heads of head block w/2 (one MFMA column block) and the 16
+//       keys of key half w%2 of each 32-key tile, over the full 576-column depth:
+//         S^T[key][head] = K[key][:] . q[head][:]
+//       A = K from the LDS tile, B = q held in registers (18 k-steps). Its softmax needs
+//       nothing from other waves: the exponentials are taken against a fixed reference
+//       max (below), and the running max and sum are reduced once at the end.
+//   P.V: wave w takes the 64 columns 64 w .. 64 w + 63 of V for all 64 heads:
+//         O^T[d][head] += V^T[d][key] . P^T[key][head]
+//       A = V^T read transposed from the same LDS tile (ds_read_b64_tr_b16); B = P^T, which
+//       every wave writes to an 8 KB LDS buffer in the B-operand layout after its softmax
+//       and reads back for all four head blocks after one barrier.
+// Each V element is then read from LDS once per tile and workgroup, not once per head
+// block, and each K element once per head block. Both roles keep a wave's fp32
+// accumulators at 64 registers (16 x 256 fp32 in total per product), so two waves fit on
+// each SIMD and hide each other's LDS operand latency.
 // P is split hi/lo in bf16 (two MFMAs per depth block) so that the fp32 O keeps ~16
 // significant bits of the weights. The K tile (32 keys x 1152 B, 16-byte chunks XOR
 // swizzled within groups of 8) is double-buffered in LDS: the next tile's direct-to-LDS
 // loads are in flight while the current tile is computed (a third buffer, two tiles in
-// flight, measured slower). The two head blocks of a
-// (sequence, partition) get workgroup ids 8 apart, so they run on the same XCD and the
-// second read of each K tile is an L2 hit.
+// flight, measured slower). The two 64-head workgroups of a (sequence, partition) get
+// workgroup ids 8 apart, so they run on the same XCD and the second read of each K tile
+// is an L2 hit.
 // Epilogue as in the GQA kernel: normalised partial + (m, l) per head, or the finished
 // bf16 row when the sequence has a single partition (fa4_splitk_combine_write, second
 // paragraph; fa4_scale_write_output for the single-partition case).
@@ -36,18 +39,12 @@ namespace {
 constexpr int kDqk = 576;
 constexpr int kDv = 512;
 constexpr int kTile = 32;
-constexpr int kChunks = kDqk / 8;               // 16-byte chunks per K row (72)
 constexpr int kRowBytes = kDqk * 2;             // 1152
 constexpr int kTileBytes = kTile * kRowBytes;   // 36 KB
-// MFMA column blocks (16 heads) per wave: each K / V operand read serves all of them, at
-// 64 accumulator registers each. Two blocks leave room for one wave per SIMD only, and
-// measured no faster.
-constexpr int kCB = 1;
-constexpr int kHeadsPerWave = 16 * kCB;
-constexpr int kWaves = 8;                             // 4 head blocks x 2 depth halves
-constexpr int kHeadsPerWG = kHeadsPerWave * kWaves / 2;   // 64
-constexpr int kQkSteps = kDqk / 2 / 32;               // k-steps of 32 per depth half of q.K (9)
-constexpr int kDvBlocks = kDv / 2 / 16;               // 16-wide depth blocks per half of V (16)
+constexpr int kWaves = 8;
+constexpr int kHeadsPerWG = 64;                        // 4 head blocks of 16 (MFMA columns)
+constexpr int kQkSteps = kDqk / 32;                    // k-steps of 32 over the q.K depth (18)
+constexpr int kDvBlocks = kDv / kWaves / 16;           // 16-wide depth blocks of a wave's V slice (4)
 constexpr int kThreads = kWaves * 64;
 constexpr int kTileBlocks = kTileBytes / 1024;         // 1 KB direct-to-LDS loads per tile (36)
 constexpr int kStage = (kTileBlocks + kWaves - 1) / kWaves;   // ... per wave, at most (5)
@@ -77,7 +74,7 @@ __device__ __forceinline__ float max_over_key_groups(float v) {
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // Fixed reference max: the exponentials are taken relative to the first tile's max
-// m_ref and the 128 accumulator registers are never rescaled inside the key loop. That
+// m_ref and the accumulators are never rescaled inside the key loop. That
 // holds while every score stays within kHeadroomLog2 powers of two of m_ref (p <= 2^64,
 // far from fp32 overflow, and keys far below the max underflow harmlessly). A score
 // beyond that (rare; adversarial or huge logits) makes the workgroup run the partition
@@ -97,37 +94,39 @@ void partition_latent_kernel(PartArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int dh = w & 1;                      // depth half of q.K and of V
+  const int kh = w & 1, hb = w >> 1;        // q.K role: key half kh of head block hb
   const int n = lane & 15, qd = lane >> 4;
   const int g = a.g;
-  const int head0 = hblk * kHeadsPerWG + (w >> 1) * kHeadsPerWave;   // first q head of this wave
+  const int head0 = hblk * kHeadsPerWG + 16 * hb;   // first q head of the q.K role
   const float c = a.c;
 
   // Two K tiles. Their direct-to-LDS loads are inline assembly (lds_dma16): the compiler
   // sees no LDS write and adds no wait of its own before the LDS reads of the other tile;
   // a tile is read only after the explicit wait and barrier at the top of its step.
   __shared__ __attribute__((aligned(16))) char ktile[kRing][kTileBytes];
-  // partial scores of each wave, lane-major (8 floats per lane and column block), read by
-  // its partner
-  __shared__ __attribute__((aligned(16))) f32x4 xchg[kWaves][2 * kCB][64];
+  // P of the tile for P.V, hi and lo bf16 parts per head block, lane-major in the B-operand
+  // layout: lane (n, qd) reads 16 bytes, the k-slots 8 qd .. 8 qd + 7 of head n, whose first
+  // 8 bytes the wave of key half 0 writes (keys 4 qd .. +3) and whose last 8 the wave of key
+  // half 1 (keys 16 + 4 qd .. +3)
+  __shared__ __attribute__((aligned(16))) char pbuf[4][2][64][16];
+  // per wave and head: first-tile maxima, then the final (max, sum, reference)
+  __shared__ float xm[kWaves][16], xl[kWaves][16], xr[kWaves][16];
   __shared__ int pages_s[kMaxLdsPages];
 
   // Rows that a ragged tile does not load keep what the buffer held: zero both tiles
   // once so that such rows are finite (their scores are masked, their V meets p = 0).
   for (int i = tid; i < kRing * kTileBytes / 16; i += kThreads) *(u32x4*)(&ktile[0][0] + i * 16) = u32x4{0u, 0u, 0u, 0u};
-  // q as the B operand of S^T = K q^T, in registers for the wave's whole piece: column
-  // block cb, k-step j holds depth 288 dh + 32 j + 8 qd .. +8 of head head0 + 16 cb + n
-  // (zero past the group)
-  bf16x8 qf[kCB][kQkSteps];
-#pragma unroll
-  for (int cb = 0; cb < kCB; ++cb) {
-    const int h = head0 + 16 * cb + n;
-    const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)b * a.Hq + (h < g ? h : 0)) * kDqk + 288 * dh + 8 * qd;
+  // q as the B operand of S^T = K q^T over the full depth, in registers for the whole
+  // piece: k-step j holds depth 32 j + 8 qd .. +8 of head head0 + n (zero past the group)
+  bf16x8 qf[kQkSteps];
+  {
+    const int h = head0 + n;
+    const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)b * a.Hq + (h < g ? h : 0)) * kDqk + 8 * qd;
 #pragma unroll
     for (int j = 0; j < kQkSteps; ++j) {
       u32x4 v = *(const u32x4*)(qrow + 32 * j);
       if (h >= g) v = u32x4{0u, 0u, 0u, 0u};
-      qf[cb][j] = as_bf16x8(v);
+      qf[j] = as_bf16x8(v);
     }
   }
   // page indices of the partition (one segment: chunks of at most (kMaxLdsPages-1)*page keys)
@@ -198,185 +197,169 @@ void partition_latent_kernel(PartArgs a) {
     }
   };
 
-  // per column block cb: reference max of the exponentials (raw units), exact running
-  // max, running sum (this lane's keys)
-  float m_ref[kCB], m_true[kCB], l_run[kCB];
-#pragma unroll
-  for (int cb = 0; cb < kCB; ++cb) {
-    m_ref[cb] = -INFINITY;
-    m_true[cb] = -INFINITY;
-    l_run[cb] = 0.f;
-  }
+  // q.K role (head head0 + n, this lane's keys): reference max of the exponentials (raw
+  // units), exact running max and running sum
+  float m_ref = -INFINITY, m_lane = -INFINITY, l_lane = 0.f;
   bool beyond = false;       // a score exceeded m_ref by more than the headroom
-  f32x4 o[kCB][kDvBlocks];
+  // P.V role: O^T of depth block db of this wave's 64 columns and head block hb2
+  f32x4 o[kDvBlocks][4];
 
-  auto compute = [&](const char* K, int t0) {
-    // S^T partial over this wave's depth half: keys 16 blk + (4qd..+3) of column n of
-    // column block cb; each K operand serves every column block
-    // (k-step j of depth half dh is chunk 4 jj + qd, jj = 9 dh + j, of row r; under the
-    // swizzle that is byte 128 (jj >> 1) + 16 ((4 (jj & 1) + qd) ^ (r & 7)) of the row, so
-    // two per-lane bases per row, one per parity of jj, and constant offsets cover all
-    // k-steps)
-    f32x4 s[kCB][2];
-#pragma unroll
-    for (int cb = 0; cb < kCB; ++cb)
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) s[cb][blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const char* K, int t0, bool first) {
     const DA_LDS char* KL = (const DA_LDS char*)K;
-    // k-step j = 2m (even) of depth half dh reads from pe + 128 m, j = 2m + 1 from po + 128 m
-    const int kr = n * kRowBytes;   // row n of key block 0; block 1 is 16 rows on
-    const DA_LDS char* pe = KL + kr + 16 * ((4 * dh + qd) ^ (n & 7)) + 512 * dh;
-    const DA_LDS char* po = KL + kr + 16 * ((4 * (1 - dh) + qd) ^ (n & 7)) + 640 * dh;
-    bf16x8 kf[kQkSteps][2];
+    // S^T over the full q.K depth for keys 16 kh + 4 qd + i of head n. The A operand of
+    // k-step j is chunk 4 j + qd of row r = 16 kh + n; under the swizzle that is byte
+    // 128 (j >> 1) + 16 ((4 (j & 1) + qd) ^ (r & 7)) of the row (r & 7 = n & 7): two per-lane
+    // bases, one per parity of j, and constant offsets
+    const int kr = (16 * kh + n) * kRowBytes;
+    const DA_LDS char* pe = KL + kr + 16 * (qd ^ (n & 7));
+    const DA_LDS char* po = KL + kr + 16 * ((4 + qd) ^ (n & 7));
+    // the operand reads run kQkAhead k-steps ahead of their products (the scheduling
+    // barriers keep that order); even and odd k-steps accumulate apart, two independent
+    // chains of products
+    constexpr int kQkAhead = 10;
+    bf16x8 kf[kQkSteps];
+    auto load_k = [&](int j) { return as_bf16x8(*(const DA_LDS u32x4*)((j & 1 ? po : pe) + 128 * (j >> 1))); };
 #pragma unroll
-    for (int j = 0; j < kQkSteps; ++j)
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-        kf[j][blk] = as_bf16x8(*(const DA_LDS u32x4*)((j & 1 ? po : pe) + 128 * (j >> 1) + 16 * blk * kRowBytes));
-    // (all 18 operand reads are issued before the first product)
+    for (int j = 0; j < kQkAhead; ++j) kf[j] = load_k(j);
     __builtin_amdgcn_sched_barrier(0);
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < kQkSteps; ++j)
+    for (int j = 0; j < kQkSteps; j += 2) {
+      if (j + kQkAhead < kQkSteps) kf[j + kQkAhead] = load_k(j + kQkAhead);
+      if (j + 1 + kQkAhead < kQkSteps) kf[j + 1 + kQkAhead] = load_k(j + 1 + kQkAhead);
+      __builtin_amdgcn_sched_barrier(0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j], qf[j], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j + 1], qf[j + 1], s1, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    f32x4 sc = s0 + s1;
+    // keys past the end of a ragged tile get -inf (p = 0)
+    if (end - t0 < kTile) {
+      const int nvalid = end - t0 - 16 * kh - 4 * qd;
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
+      for (int i = 0; i < 4; ++i)
+        if (i >= nvalid) sc[i] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    m_lane = fmaxf(m_lane, mx);
+    if (first) {
+      // the reference of the first pass: the first tile's max over both key halves (O and
+      // l are still 0); one exchange per pass, the other tiles need no cross-lane step
+      mx = max_over_key_groups(mx);
+      if (qd == 0) xm[w][n] = mx;
+      __syncthreads();
+      m_ref = fmaxf(mx, xm[w ^ 1][n]);
+    }
+    beyond = beyond || (mx - m_ref) * c > kHeadroomLog2;
+    const float mc = m_ref * c;
+    float pr[4];
 #pragma unroll
-        for (int cb = 0; cb < kCB; ++cb)
-          s[cb][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j][blk], qf[cb][j], s[cb][blk], 0, 0, 0);
-    // the partner wave (other depth half, same heads) adds its partial: both waves then
-    // hold the full scores. A wave rewrites its slot only after the next tile's barrier,
-    // which its partner passes after reading it.
-#pragma unroll
-    for (int k = 0; k < 2 * kCB; ++k) xchg[w][k][lane] = s[k >> 1][k & 1];
-    __syncthreads();
-    f32x4 sp[2 * kCB];
-#pragma unroll
-    for (int k = 0; k < 2 * kCB; ++k) sp[k] = xchg[w ^ 1][k][lane];
-    // O^T += V^T P^T over this wave's depth half; V^T A operand: depth 16 db + n of keys
-    // 4qd..+3 and 16+4qd..+3, shared by every column block. Depth block d = 16 dh + db is
-    // chunk 2d + ((n & 3) >> 1) of rows ra and rb = ra + 16; under the swizzle that is byte
-    // 128 (d >> 2) + 16 ((2 (d & 3) + ((n & 3) >> 1)) ^ (ra & 7)) of the row (rb & 7 =
-    // ra & 7): four per-lane bases and constant offsets
+    for (int i = 0; i < 4; ++i) {
+      pr[i] = exp2_fast(fmaf(sc[i], c, -mc));
+      l_lane += pr[i];
+    }
+    // hi and lo parts of P into the buffer (8 bytes each per lane)
+    const uint32_t h0 = pack_bf16x2(pr[0], pr[1]), h1 = pack_bf16x2(pr[2], pr[3]);
+    const uint32_t l0 = pack_bf16x2(pr[0] - bf16lo(h0), pr[1] - bf16hi(h0));
+    const uint32_t l1 = pack_bf16x2(pr[2] - bf16lo(h1), pr[3] - bf16hi(h1));
+    *(u32x2*)&pbuf[hb][0][lane][8 * kh] = u32x2{h0, h1};
+    *(u32x2*)&pbuf[hb][1][lane][8 * kh] = u32x2{l0, l1};
+    // O^T += V^T P^T over depth blocks d = 4 w + db of V, for all four head blocks. The V^T
+    // A operand of depth 16 d + n holds keys 4 qd .. +3 and 16 + 4 qd .. +3 (the k-slot order
+    // of the P buffer); depth block d is chunk 2 d + ((n & 3) >> 1) of rows ra and ra + 16,
+    // under the swizzle byte 128 (d >> 2) + 16 ((2 (d & 3) + ((n & 3) >> 1)) ^ (ra & 7)) of
+    // the row (d >> 2 = w, d & 3 = db)
     const int ra = 4 * qd + (n >> 2);
     const int sub = (n & 1) * 8;
-    const DA_LDS char* vbase[4];
+    bf16x8 vf[kDvBlocks];
 #pragma unroll
-    for (int v4 = 0; v4 < 4; ++v4)
-      vbase[v4] = KL + ra * kRowBytes + 16 * ((2 * v4 + ((n & 3) >> 1)) ^ (ra & 7)) + sub + 128 * 4 * dh;
-    auto load_v = [&](int db) {
-      const DA_LDS char* pa = vbase[db & 3] + 128 * (db >> 2);
+    for (int db = 0; db < kDvBlocks; ++db) {
+      const DA_LDS char* pa = KL + ra * kRowBytes + 16 * ((2 * db + ((n & 3) >> 1)) ^ (ra & 7)) + sub + 128 * w;
       const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 DA_LDS*)pa);
       const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 DA_LDS*)(pa + 16 * kRowBytes));
       s16x8 v8;
       v8[0] = va[0]; v8[1] = va[1]; v8[2] = va[2]; v8[3] = va[3];
       v8[4] = vb[0]; v8[5] = vb[1]; v8[6] = vb[2]; v8[7] = vb[3];
-      return __builtin_bit_cast(bf16x8, v8);
-    };
-    // the first V^T operands are requested before the softmax, the rest kAhead depth
-    // blocks ahead of their products (the scheduling barriers keep that order)
-    constexpr int kAhead = 6;
-    bf16x8 vf[kDvBlocks];
-#pragma unroll
-    for (int db = 0; db < kAhead; ++db) vf[db] = load_v(db);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int k = 0; k < 2 * kCB; ++k) s[k >> 1][k & 1] += sp[k];
-    // online softmax (missing keys of a ragged tile get -inf, i.e. p = 0)
-    const int nvalid = end - t0;
-    if (nvalid < kTile) {
-#pragma unroll
-      for (int cb = 0; cb < kCB; ++cb)
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (16 * blk + 4 * qd + i >= nvalid) s[cb][blk][i] = -INFINITY;
+      vf[db] = __builtin_bit_cast(bf16x8, v8);
     }
-    bf16x8 pb_hi[kCB], pb_lo[kCB];
+    __syncthreads();   // every wave's P of this tile is in the buffer
+    bf16x8 ph[4], pl[4];
 #pragma unroll
-    for (int cb = 0; cb < kCB; ++cb) {
-      const f32x4* sc = s[cb];
-      float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                       fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-      mx = max_over_key_groups(mx);
-      m_true[cb] = fmaxf(m_true[cb], mx);
-      m_ref[cb] = m_ref[cb] == -INFINITY ? mx : m_ref[cb];   // first tile of the pass: O and l are still 0
-      beyond = beyond || (mx - m_ref[cb]) * c > kHeadroomLog2;
-      const float mc = m_ref[cb] * c;
-      float pr[2][4];
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pr[blk][i] = exp2_fast(fmaf(sc[blk][i], c, -mc));
-          l_run[cb] += pr[blk][i];
-        }
-      // P^T (B operand), hi and lo parts
-      uint32_t hw[4], lw[4];
-#pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {
-        const int blk = s2 >> 1, i0 = (s2 & 1) * 2;
-        const float p0 = pr[blk][i0], p1 = pr[blk][i0 + 1];
-        const uint32_t hv = pack_bf16x2(p0, p1);
-        hw[s2] = hv;
-        lw[s2] = pack_bf16x2(p0 - bf16lo(hv), p1 - bf16hi(hv));
-      }
-      pb_hi[cb] = as_bf16x8(u32x4{hw[0], hw[1], hw[2], hw[3]});
-      pb_lo[cb] = as_bf16x8(u32x4{lw[0], lw[1], lw[2], lw[3]});
+    for (int hb2 = 0; hb2 < 4; ++hb2) {
+      ph[hb2] = as_bf16x8(*(const u32x4*)&pbuf[hb2][0][lane][0]);
+      pl[hb2] = as_bf16x8(*(const u32x4*)&pbuf[hb2][1][lane][0]);
     }
+    // head block by head block (the first products need only the first P reads); the hi
+    // products of the four depth blocks, then their lo products, so that no product waits
+    // for the one just before it
 #pragma unroll
-    for (int db = 0; db < kDvBlocks; ++db) {
-      if (db + kAhead < kDvBlocks) vf[db + kAhead] = load_v(db + kAhead);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int hb2 = 0; hb2 < 4; ++hb2) {
 #pragma unroll
-      for (int cb = 0; cb < kCB; ++cb) {
-        o[cb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pb_hi[cb], o[cb][db], 0, 0, 0);
-        o[cb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pb_lo[cb], o[cb][db], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      for (int db = 0; db < kDvBlocks; ++db)
+        o[db][hb2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], ph[hb2], o[db][hb2], 0, 0, 0);
+#pragma unroll
+      for (int db = 0; db < kDvBlocks; ++db)
+        o[db][hb2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pl[hb2], o[db][hb2], 0, 0, 0);
     }
   };
 
   // Double buffer: tile it+1 is requested right after the barrier that retires tile it-1
-  // from the other buffer, and lands while tile it is computed. A second pass runs only
-  // if some score left the headroom of m_ref (then m_ref = the exact max: no second miss).
+  // from the other buffer (and the P buffer of tile it-1), and lands while tile it is
+  // computed. A second pass runs only if some score left the headroom of m_ref (then
+  // m_ref = the exact max: no second miss).
   const int n_tiles = (end - start + kTile - 1) / kTile;
   for (int pass = 0; pass < 2; ++pass) {
+    l_lane = 0.f;
 #pragma unroll
-    for (int cb = 0; cb < kCB; ++cb) {
-      l_run[cb] = 0.f;
+    for (int db = 0; db < kDvBlocks; ++db)
 #pragma unroll
-      for (int db = 0; db < kDvBlocks; ++db) o[cb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+      for (int hb2 = 0; hb2 < 4; ++hb2) o[db][hb2] = f32x4{0.f, 0.f, 0.f, 0.f};
     issue(ktile[0], start);
     for (int it = 0; it < n_tiles; ++it) {
       wait_vm<0>();      // this wave's part of tile it is in LDS
-      __syncthreads();   // ... and every wave's; tile it-1 is retired (its reads have returned)
+      __syncthreads();   // ... and every wave's; tile it-1 and its P are retired
       if (it + 1 < n_tiles) issue(ktile[(it + 1) & 1], start + (it + 1) * kTile);
-      compute(ktile[it & 1], start + it * kTile);
+      compute(ktile[it & 1], start + it * kTile, pass == 0 && it == 0);
     }
     // every wave is past its last LDS read before a second pass refills the tiles
     if (!__syncthreads_or(beyond)) break;
-#pragma unroll
-    for (int cb = 0; cb < kCB; ++cb) m_ref[cb] = m_true[cb];
+    // second pass: the reference is each head's exact max over the partition
+    const float mt = max_over_key_groups(m_lane);
+    if (qd == 0) xm[w][n] = mt;
+    __syncthreads();
+    m_ref = fmaxf(mt, xm[w ^ 1][n]);
     beyond = false;
+    __syncthreads();   // (xm is written again before it is next read)
   }
 
-  // O and l are relative to m_ref; the partial reports the exact max, so its sum is
-  // rescaled once (the normalised O does not change). Both waves of a pair hold the
-  // same (m, l): the depth-half-0 wave writes them.
-#pragma unroll
-  for (int cb = 0; cb < kCB; ++cb) {
-    float l = l_run[cb];
+  // (max, sum) per head: the q.K role reduces this wave's over its key groups and publishes
+  // it; the P.V role reads those of the heads it holds. O and l are relative to m_ref; the
+  // partial reports the exact max, so its sum is rescaled once (the normalised O does not
+  // change).
+  {
+    const float mt = max_over_key_groups(m_lane);
+    float l = l_lane;
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
-    const int hq = head0 + 16 * cb + n;   // q head of this lane's column (within the kv head's group)
+    if (qd == 0) {
+      xm[w][n] = mt;
+      xl[w][n] = l;
+      xr[w][n] = m_ref;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int hb2 = 0; hb2 < 4; ++hb2) {
+    const int hq = hblk * kHeadsPerWG + 16 * hb2 + n;   // q head of this lane's column
     if (hq < g) {
-      const float inv = 1.f / l;
-      const float l_true = l * exp2_fast((m_ref[cb] - m_true[cb]) * c);
+      const float M = fmaxf(xm[2 * hb2][n], xm[2 * hb2 + 1][n]);
+      const float L = xl[2 * hb2][n] + xl[2 * hb2 + 1][n];   // both halves share m_ref
+      const float inv = 1.f / L;
+      const float l_true = L * exp2_fast((xr[2 * hb2][n] - M) * c);
 #pragma unroll
       for (int db = 0; db < kDvBlocks; ++db)
-        store_unit(a, b, hq, p, direct, 256 * dh + 16 * db + 4 * qd, o[cb][db] * inv, m_true[cb], l_true,
-                   db == 0 && qd == 0 && dh == 0);
+        store_unit(a, b, hq, p, direct, 64 * w + 16 * db + 4 * qd, o[db][hb2] * inv, M, l_true,
+                   w == 0 && db == 0 && qd == 0);
     }
   }
 }
