@@ -22,12 +22,13 @@
 // accumulators at 64 registers (16 x 256 fp32 in total per product), so two waves fit on
 // each SIMD and hide each other's LDS operand latency.
 // P is split hi/lo in bf16 (two MFMAs per depth block) so that the fp32 O keeps ~16
-// significant bits of the weights. The K tile (32 keys x 1152 B, 16-byte chunks XOR
-// swizzled within groups of 8) is double-buffered in LDS: the next tile's direct-to-LDS
-// loads are in flight while the current tile is computed (a third buffer, two tiles in
-// flight, measured slower). The two 64-head workgroups of a (sequence, partition) get
-// workgroup ids 8 apart, so they run on the same XCD and the second read of each K tile
-// is an L2 hit.
+// significant bits of the weights. K tiles (32 keys x 1152 B, 16-byte chunks XOR swizzled
+// within groups of 8) pass through three LDS slots: in the step for tile t, tile t - 1
+// feeds P.V, tile t feeds q.K and tile t + 1 is in flight, so one barrier per tile
+// suffices (P of tile t - 1 is written before it, P of tile t after it), and the first K
+// operands of q.K are read while the P.V products run. (Two tiles in flight measured
+// slower.) The two 64-head workgroups of a (sequence, partition) get workgroup ids 8
+// apart, so they run on the same XCD and the second read of each K tile is an L2 hit.
 // Epilogue as in the GQA kernel: normalised partial + (m, l) per head, or the finished
 // bf16 row when the sequence has a single partition (fa4_splitk_combine_write, second
 // paragraph; fa4_scale_write_output for the single-partition case).
@@ -49,7 +50,7 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kTileBlocks = kTileBytes / 1024;         // 1 KB direct-to-LDS loads per tile (36)
 constexpr int kStage = (kTileBlocks + kWaves - 1) / kWaves;   // ... per wave, at most (5)
 constexpr int kMaxLdsPages = 256;
-constexpr int kRing = 2;   // K tiles in LDS: one in flight while the other is computed
+constexpr int kRing = 3;   // K tiles in LDS: one feeds P.V, one q.K, one is in flight
 
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
@@ -100,15 +101,15 @@ void partition_latent_kernel(PartArgs a) {
   const int head0 = hblk * kHeadsPerWG + 16 * hb;   // first q head of the q.K role
   const float c = a.c;
 
-  // Two K tiles. Their direct-to-LDS loads are inline assembly (lds_dma16): the compiler
+  // Three K tiles. Their direct-to-LDS loads are inline assembly (lds_dma16): the compiler
   // sees no LDS write and adds no wait of its own before the LDS reads of the other tile;
   // a tile is read only after the explicit wait and barrier at the top of its step.
   __shared__ __attribute__((aligned(16))) char ktile[kRing][kTileBytes];
-  // P of the tile for P.V, hi and lo bf16 parts per head block, lane-major in the B-operand
-  // layout: lane (n, qd) reads 16 bytes, the k-slots 8 qd .. 8 qd + 7 of head n, whose first
-  // 8 bytes the wave of key half 0 writes (keys 4 qd .. +3) and whose last 8 the wave of key
-  // half 1 (keys 16 + 4 qd .. +3)
-  __shared__ __attribute__((aligned(16))) char pbuf[4][2][64][16];
+  // P of a tile for P.V (two buffers: tile t uses buffer t & 1), hi and lo bf16 parts per
+  // head block, lane-major in the B-operand layout: lane (n, qd) reads 16 bytes, the k-slots
+  // 8 qd .. 8 qd + 7 of head n, whose first 8 bytes the wave of key half 0 writes (keys
+  // 4 qd .. +3) and whose last 8 the wave of key half 1 (keys 16 + 4 qd .. +3)
+  __shared__ __attribute__((aligned(16))) char pbuf[2][4][2][64][16];
   // per wave and head: first-tile maxima, then the final (max, sum, reference)
   __shared__ float xm[kWaves][16], xl[kWaves][16], xr[kWaves][16];
   __shared__ int pages_s[kMaxLdsPages];
@@ -204,29 +205,87 @@ void partition_latent_kernel(PartArgs a) {
   // P.V role: O^T of depth block db of this wave's 64 columns and head block hb2
   f32x4 o[kDvBlocks][4];
 
-  auto compute = [&](const char* K, int t0, bool first) {
-    const DA_LDS char* KL = (const DA_LDS char*)K;
-    // S^T over the full q.K depth for keys 16 kh + 4 qd + i of head n. The A operand of
-    // k-step j is chunk 4 j + qd of row r = 16 kh + n; under the swizzle that is byte
-    // 128 (j >> 1) + 16 ((4 (j & 1) + qd) ^ (r & 7)) of the row (r & 7 = n & 7): two per-lane
-    // bases, one per parity of j, and constant offsets
-    const int kr = (16 * kh + n) * kRowBytes;
-    const DA_LDS char* pe = KL + kr + 16 * (qd ^ (n & 7));
-    const DA_LDS char* po = KL + kr + 16 * ((4 + qd) ^ (n & 7));
-    // the operand reads run kQkAhead k-steps ahead of their products (the scheduling
-    // barriers keep that order); even and odd k-steps accumulate apart, two independent
-    // chains of products
-    constexpr int kQkAhead = 10;
+  // q.K operands: the A operand of k-step j is chunk 4 j + qd of row r = 16 kh + n; under
+  // the swizzle that is byte 128 (j >> 1) + 16 ((4 (j & 1) + qd) ^ (r & 7)) of the row
+  // (r & 7 = n & 7): two per-lane offsets, one per parity of j, and constant offsets
+  const int kr = (16 * kh + n) * kRowBytes;
+  const int k_even = kr + 16 * (qd ^ (n & 7)), k_odd = kr + 16 * ((4 + qd) ^ (n & 7));
+  auto load_k = [&](const DA_LDS char* KL, int j) {
+    return as_bf16x8(*(const DA_LDS u32x4*)(KL + (j & 1 ? k_odd : k_even) + 128 * (j >> 1)));
+  };
+  // P.V operands: the V^T A operand of depth 16 d + n holds keys 4 qd .. +3 and 16 + 4 qd ..
+  // +3 (the k-slot order of the P buffer); depth block d = 4 w + db is chunk 2 d + ((n & 3)
+  // >> 1) of rows ra and ra + 16, under the swizzle byte 128 (d >> 2) + 16 ((2 (d & 3) +
+  // ((n & 3) >> 1)) ^ (ra & 7)) of the row (d >> 2 = w, d & 3 = db)
+  const int ra = 4 * qd + (n >> 2);
+  const int v_off = ra * kRowBytes + (n & 1) * 8 + 128 * w;
+  auto load_v = [&](const DA_LDS char* KL, int db) {
+    const DA_LDS char* pa = KL + v_off + 16 * ((2 * db + ((n & 3) >> 1)) ^ (ra & 7));
+    const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 DA_LDS*)pa);
+    const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 DA_LDS*)(pa + 16 * kRowBytes));
+    s16x8 v8;
+    v8[0] = va[0]; v8[1] = va[1]; v8[2] = va[2]; v8[3] = va[3];
+    v8[4] = vb[0]; v8[5] = vb[1]; v8[6] = vb[2]; v8[7] = vb[3];
+    return __builtin_bit_cast(bf16x8, v8);
+  };
+  // K operands of q.K issued ahead of their products; the first kEarly of them go out
+  // during the P.V products of the tile before, so that their latency hides behind those
+  // (not with per-lane page lookups: that form, for page sizes that are not a power of two
+  // >= 32 keys, already spills about 10 registers)
+  constexpr int kEarly = PM == kPagedGeneral ? 0 : 4;
+  constexpr int kQkAhead = 8;
+
+  const int n_tiles = (end - start + kTile - 1) / kTile;
+  // Step it: P.V of tile it - 1 (its P is in buffer (it - 1) & 1 since the barrier before),
+  // then q.K and the softmax of tile it, whose P goes to buffer it & 1.
+  auto step = [&](int it, bool first) {
+    const bool has_pv = it >= 1, has_qk = it < n_tiles;
+    const DA_LDS char* KQ = (const DA_LDS char*)ktile[it % kRing];
+    const DA_LDS char* KV = (const DA_LDS char*)ktile[(it + kRing - 1) % kRing];
     bf16x8 kf[kQkSteps];
-    auto load_k = [&](int j) { return as_bf16x8(*(const DA_LDS u32x4*)((j & 1 ? po : pe) + 128 * (j >> 1))); };
+    if (has_pv) {
+      bf16x8 vf[kDvBlocks], ph[4], pl[4];
 #pragma unroll
-    for (int j = 0; j < kQkAhead; ++j) kf[j] = load_k(j);
+      for (int db = 0; db < kDvBlocks; ++db) vf[db] = load_v(KV, db);
+#pragma unroll
+      for (int hb2 = 0; hb2 < 4; ++hb2) {
+        ph[hb2] = as_bf16x8(*(const u32x4*)&pbuf[(it - 1) & 1][hb2][0][lane][0]);
+        pl[hb2] = as_bf16x8(*(const u32x4*)&pbuf[(it - 1) & 1][hb2][1][lane][0]);
+      }
+      if (has_qk) {
+#pragma unroll
+        for (int j = 0; j < kEarly; ++j) kf[j] = load_k(KQ, j);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // O^T += V^T P^T for the wave's 4 depth blocks and all 4 head blocks: head block by
+      // head block, the hi products of the 4 depth blocks, then their lo products, so that
+      // no product waits for the one just before it
+#pragma unroll
+      for (int hb2 = 0; hb2 < 4; ++hb2) {
+#pragma unroll
+        for (int db = 0; db < kDvBlocks; ++db)
+          o[db][hb2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], ph[hb2], o[db][hb2], 0, 0, 0);
+#pragma unroll
+        for (int db = 0; db < kDvBlocks; ++db)
+          o[db][hb2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pl[hb2], o[db][hb2], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kEarly; ++j) kf[j] = load_k(KQ, j);
+    }
+    if (!has_qk) return;
+    // S^T over the full q.K depth for keys 16 kh + 4 qd + i of head n; even and odd k-steps
+    // accumulate apart, two independent chains of products
+    const int t0 = start + it * kTile;
+#pragma unroll
+    for (int j = kEarly; j < kQkAhead; ++j) kf[j] = load_k(KQ, j);
     __builtin_amdgcn_sched_barrier(0);
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < kQkSteps; j += 2) {
-      if (j + kQkAhead < kQkSteps) kf[j + kQkAhead] = load_k(j + kQkAhead);
-      if (j + 1 + kQkAhead < kQkSteps) kf[j + 1 + kQkAhead] = load_k(j + 1 + kQkAhead);
+      if (j + kQkAhead < kQkSteps) kf[j + kQkAhead] = load_k(KQ, j + kQkAhead);
+      if (j + 1 + kQkAhead < kQkSteps) kf[j + 1 + kQkAhead] = load_k(KQ, j + 1 + kQkAhead);
       __builtin_amdgcn_sched_barrier(0);
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j], qf[j], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j + 1], qf[j + 1], s1, 0, 0, 0);
@@ -262,52 +321,14 @@ void partition_latent_kernel(PartArgs a) {
     const uint32_t h0 = pack_bf16x2(pr[0], pr[1]), h1 = pack_bf16x2(pr[2], pr[3]);
     const uint32_t l0 = pack_bf16x2(pr[0] - bf16lo(h0), pr[1] - bf16hi(h0));
     const uint32_t l1 = pack_bf16x2(pr[2] - bf16lo(h1), pr[3] - bf16hi(h1));
-    *(u32x2*)&pbuf[hb][0][lane][8 * kh] = u32x2{h0, h1};
-    *(u32x2*)&pbuf[hb][1][lane][8 * kh] = u32x2{l0, l1};
-    // O^T += V^T P^T over depth blocks d = 4 w + db of V, for all four head blocks. The V^T
-    // A operand of depth 16 d + n holds keys 4 qd .. +3 and 16 + 4 qd .. +3 (the k-slot order
-    // of the P buffer); depth block d is chunk 2 d + ((n & 3) >> 1) of rows ra and ra + 16,
-    // under the swizzle byte 128 (d >> 2) + 16 ((2 (d & 3) + ((n & 3) >> 1)) ^ (ra & 7)) of
-    // the row (d >> 2 = w, d & 3 = db)
-    const int ra = 4 * qd + (n >> 2);
-    const int sub = (n & 1) * 8;
-    bf16x8 vf[kDvBlocks];
-#pragma unroll
-    for (int db = 0; db < kDvBlocks; ++db) {
-      const DA_LDS char* pa = KL + ra * kRowBytes + 16 * ((2 * db + ((n & 3) >> 1)) ^ (ra & 7)) + sub + 128 * w;
-      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 DA_LDS*)pa);
-      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 DA_LDS*)(pa + 16 * kRowBytes));
-      s16x8 v8;
-      v8[0] = va[0]; v8[1] = va[1]; v8[2] = va[2]; v8[3] = va[3];
-      v8[4] = vb[0]; v8[5] = vb[1]; v8[6] = vb[2]; v8[7] = vb[3];
-      vf[db] = __builtin_bit_cast(bf16x8, v8);
-    }
-    __syncthreads();   // every wave's P of this tile is in the buffer
-    bf16x8 ph[4], pl[4];
-#pragma unroll
-    for (int hb2 = 0; hb2 < 4; ++hb2) {
-      ph[hb2] = as_bf16x8(*(const u32x4*)&pbuf[hb2][0][lane][0]);
-      pl[hb2] = as_bf16x8(*(const u32x4*)&pbuf[hb2][1][lane][0]);
-    }
-    // head block by head block (the first products need only the first P reads); the hi
-    // products of the four depth blocks, then their lo products, so that no product waits
-    // for the one just before it
-#pragma unroll
-    for (int hb2 = 0; hb2 < 4; ++hb2) {
-#pragma unroll
-      for (int db = 0; db < kDvBlocks; ++db)
-        o[db][hb2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], ph[hb2], o[db][hb2], 0, 0, 0);
-#pragma unroll
-      for (int db = 0; db < kDvBlocks; ++db)
-        o[db][hb2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pl[hb2], o[db][hb2], 0, 0, 0);
-    }
+    *(u32x2*)&pbuf[it & 1][hb][0][lane][8 * kh] = u32x2{h0, h1};
+    *(u32x2*)&pbuf[it & 1][hb][1][lane][8 * kh] = u32x2{l0, l1};
   };
 
-  // Double buffer: tile it+1 is requested right after the barrier that retires tile it-1
-  // from the other buffer (and the P buffer of tile it-1), and lands while tile it is
-  // computed. A second pass runs only if some score left the headroom of m_ref (then
+  // Three K tiles: during step it, tile it - 1 feeds P.V, tile it feeds q.K and tile it + 1
+  // is in flight (requested right after the barrier that retires tile it - 2). One barrier
+  // per tile. A second pass runs only if some score left the headroom of m_ref (then
   // m_ref = the exact max: no second miss).
-  const int n_tiles = (end - start + kTile - 1) / kTile;
   for (int pass = 0; pass < 2; ++pass) {
     l_lane = 0.f;
 #pragma unroll
@@ -315,11 +336,12 @@ void partition_latent_kernel(PartArgs a) {
 #pragma unroll
       for (int hb2 = 0; hb2 < 4; ++hb2) o[db][hb2] = f32x4{0.f, 0.f, 0.f, 0.f};
     issue(ktile[0], start);
-    for (int it = 0; it < n_tiles; ++it) {
-      wait_vm<0>();      // this wave's part of tile it is in LDS
-      __syncthreads();   // ... and every wave's; tile it-1 and its P are retired
-      if (it + 1 < n_tiles) issue(ktile[(it + 1) & 1], start + (it + 1) * kTile);
-      compute(ktile[it & 1], start + it * kTile, pass == 0 && it == 0);
+    for (int it = 0; it <= n_tiles; ++it) {
+      wait_vm<0>();      // this wave's part of tile it is in LDS (none is in flight at the end)
+      __syncthreads();   // ... and every wave's; P of tile it - 1 is written; tile it - 2 and
+                         // the P buffer of tile it - 2 are retired
+      if (it + 1 < n_tiles) issue(ktile[(it + 1) % kRing], start + (it + 1) * kTile);
+      step(it, pass == 0 && it == 0);
     }
     // every wave is past its last LDS read before a second pass refills the tiles
     if (!__syncthreads_or(beyond)) break;
