@@ -4,6 +4,8 @@ Sizes span several key tiles, partitions and ragged tails while the oracle
 finishes in seconds. Tolerances are stated in parity_utils.
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -641,3 +643,55 @@ def test_many_sequences_and_sixteen_queries():
     out, lse, o32 = run(case)
     O, LSE = oracle_for(case)
     assert_parity(out, lse, o32, O, LSE, what="q_len 16")
+
+
+def pages_past(dc, min_offset_bytes):
+    """The device case ``dc`` with its pages moved past ``min_offset_bytes`` of larger pools.
+
+    Every pool-shaped tensor (first dimension = pages: K, V, their fp8 scales, the rotary
+    columns) gets ``shift`` zero pages in front, and the page table points past them. The
+    attended values do not change, so the oracle of the original case still applies."""
+    page_bytes = dc.k_cache[0].numel() * dc.k_cache.element_size()
+    shift = -(-min_offset_bytes // page_bytes)
+
+    def grow(t):
+        if t is None:
+            return None
+        big = torch.zeros((t.shape[0] + shift,) + tuple(t.shape[1:]), dtype=t.dtype, device=t.device)
+        big[shift:] = t
+        return big
+
+    pt = dc.page_table.clone()
+    pt[pt >= 0] += shift
+    return dataclasses.replace(dc, k_cache=grow(dc.k_cache), v_cache=grow(dc.v_cache), k_scale=grow(dc.k_scale),
+                               v_scale=grow(dc.v_scale), k_rope=grow(dc.k_rope), page_table=pt)
+
+
+BEYOND_4G = [
+    ("gqa_bf16_auto", dict(batch=3, num_q_heads=32, num_kv_heads=8, qk_depth=128, page_size=64,
+                           seq_lens=[700, 3000, 64], num_splits=0, seed=130)),
+    ("gqa_fp8_splits3", dict(batch=2, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=64,
+                             seq_lens=[2500, 333], num_splits=3, seed=131, kv_fp8=True)),
+    ("latent_splits4", dict(batch=2, num_q_heads=64, num_kv_heads=1, qk_depth=576, ov_depth=512,
+                            v_is_k_prefix=True, page_size=64, seq_lens=[1500, 300], num_splits=4, seed=132)),
+    ("d256_rotary_apart", dict(batch=2, num_q_heads=8, num_kv_heads=8, qk_depth=256, ov_depth=256,
+                               page_size=64, seq_lens=[1200, 65], num_splits=0, seed=133, rope_apart=64)),
+    ("fp32_g1_vector_alu", dict(batch=2, num_q_heads=2, num_kv_heads=2, qk_depth=128, dtype=torch.float32,
+                                page_size=64, seq_lens=[900, 130], num_splits=2, seed=134)),
+]
+
+
+@pytest.mark.parametrize("name,kw", BEYOND_4G, ids=[c[0] for c in BEYOND_4G])
+def test_pages_beyond_4gib(name, kw):
+    # caches of serving size: the attended pages sit past 4.5 GiB of each pool, so every
+    # byte offset into the cache needs more than 32 bits (and row indices times row bytes
+    # overflow 32-bit arithmetic)
+    case = make_case(name, **kw)
+    dc = pages_past(to_device(case), 9 << 29)
+    print(f"[parity] {name}: pages past 4.5 GiB ({dc.k_cache.shape[0]} pages)", flush=True)
+    out, lse, o32 = api.case_call(dc, return_lse=True, return_o32=True)
+    torch.cuda.synchronize()
+    O, LSE = oracle_for(case)
+    assert_parity(out, lse, o32, O, LSE, what=f"{name} beyond 4 GiB")
+    del dc, out, lse, o32
+    torch.cuda.empty_cache()
