@@ -695,3 +695,52 @@ def test_pages_beyond_4gib(name, kw):
     assert_parity(out, lse, o32, O, LSE, what=f"{name} beyond 4 GiB")
     del dc, out, lse, o32
     torch.cuda.empty_cache()
+
+
+def capacity_past(dc, min_offset_bytes):
+    """The contiguous device case ``dc`` with each sequence's capacity grown (zero rows after
+    the original ones) so that sequence 1 starts past ``min_offset_bytes`` of the cache."""
+    row_bytes = dc.k_cache[0, 0].numel() * dc.k_cache.element_size()
+    cap = max(dc.k_cache.shape[1], -(-min_offset_bytes // row_bytes))
+
+    def grow(t):
+        if t is None:
+            return None
+        if t.dim() == 3:   # fp8 scales, tokens innermost: [B][Hkv][L_cap]
+            big = torch.zeros(t.shape[:2] + (cap,), dtype=t.dtype, device=t.device)
+            big[:, :, :t.shape[2]] = t
+            return big
+        big = torch.zeros((t.shape[0], cap) + tuple(t.shape[2:]), dtype=t.dtype, device=t.device)
+        big[:, :t.shape[1]] = t
+        return big
+
+    return dataclasses.replace(dc, k_cache=grow(dc.k_cache), v_cache=grow(dc.v_cache), k_scale=grow(dc.k_scale),
+                               v_scale=grow(dc.v_scale), k_rope=grow(dc.k_rope))
+
+
+CONTIG_BEYOND_4G = [
+    ("gqa_bf16_splits8", dict(batch=3, num_q_heads=32, num_kv_heads=8, qk_depth=128, seq_lens=[4096, 1000, 33],
+                              num_splits=8, seed=140)),
+    ("gqa_fp8_auto", dict(batch=3, num_q_heads=16, num_kv_heads=2, qk_depth=128, seq_lens=[2000, 700, 64],
+                          num_splits=0, seed=141, kv_fp8=True)),
+    ("latent_splits2", dict(batch=3, num_q_heads=16, num_kv_heads=1, qk_depth=576, ov_depth=512,
+                            v_is_k_prefix=True, seq_lens=[900, 64, 300], num_splits=2, seed=142)),
+    ("d256_rotary_apart", dict(batch=3, num_q_heads=8, num_kv_heads=2, qk_depth=256, ov_depth=256,
+                               seq_lens=[1500, 77, 200], num_splits=3, seed=143, rope_apart=64)),
+    ("fp32_g4_vector_alu", dict(batch=3, num_q_heads=8, num_kv_heads=2, qk_depth=128, dtype=torch.float32,
+                                seq_lens=[800, 50, 129], num_splits=2, seed=144)),
+]
+
+
+@pytest.mark.parametrize("name,kw", CONTIG_BEYOND_4G, ids=[c[0] for c in CONTIG_BEYOND_4G])
+def test_contiguous_rows_beyond_4gib(name, kw):
+    # contiguous caches whose sequences 1 and 2 start past 2.25 and 4.5 GiB of the cache
+    case = make_case(name, **kw)
+    dc = capacity_past(to_device(case), 9 << 28)
+    print(f"[parity] {name}: capacity {dc.k_cache.shape[1]} rows per sequence", flush=True)
+    out, lse, o32 = api.case_call(dc, return_lse=True, return_o32=True)
+    torch.cuda.synchronize()
+    O, LSE = oracle_for(case)
+    assert_parity(out, lse, o32, O, LSE, what=f"{name} beyond 4 GiB")
+    del dc, out, lse, o32
+    torch.cuda.empty_cache()
