@@ -114,7 +114,7 @@ void partition_latent_kernel(PartArgs a) {
   __shared__ float xm[kWaves][16], xl[kWaves][16], xr[kWaves][16];
   __shared__ int pages_s[kMaxLdsPages];
 
-  // Rows that a ragged tile does not load keep what the buffer held: zero both tiles
+  // Rows that a ragged tile does not load keep what the slot held: zero the three slots
   // once so that such rows are finite (their scores are masked, their V meets p = 0).
   for (int i = tid; i < kRing * kTileBytes / 16; i += kThreads) *(u32x4*)(&ktile[0][0] + i * 16) = u32x4{0u, 0u, 0u, 0u};
   // q as the B operand of S^T = K q^T over the full depth, in registers for the whole
