@@ -171,12 +171,30 @@ def test_latent_large_logits_take_the_second_pass():
     assert_parity(out, lse, o32, O, LSE, o32_row_rtol=1e-4, what="latent large logits")
 
 
-def test_determinism_bitwise():
-    case = make_case("det", batch=4, num_q_heads=32, num_kv_heads=4, qk_depth=128, page_size=64,
-                     len_range=(500, 6000), num_splits=0, seed=43)
+DETERMINISM = [
+    ("gqa_paged_auto", dict(batch=4, num_q_heads=32, num_kv_heads=4, qk_depth=128, page_size=64,
+                            len_range=(500, 6000), num_splits=0, seed=43), {}),
+    ("gqa_paged_auto_fused", dict(batch=4, num_q_heads=32, num_kv_heads=4, qk_depth=128, page_size=64,
+                                  len_range=(500, 6000), num_splits=0, seed=44), {"fused": True}),
+    ("latent_splits4", dict(batch=3, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512,
+                            v_is_k_prefix=True, page_size=64, seq_lens=[3000, 700, 64], num_splits=4,
+                            seed=45), {}),
+    ("fp8_paged_auto", dict(batch=4, num_q_heads=32, num_kv_heads=4, qk_depth=128, page_size=64,
+                            len_range=(500, 6000), num_splits=0, seed=46, kv_fp8=True), {}),
+    ("d256_rotary_apart", dict(batch=3, num_q_heads=16, num_kv_heads=16, qk_depth=256, ov_depth=256,
+                               page_size=64, len_range=(1, 3000), num_splits=0, seed=47, rope_apart=64), {}),
+]
+
+
+@pytest.mark.parametrize("name,kw,call", DETERMINISM, ids=[c[0] for c in DETERMINISM])
+def test_determinism_bitwise(name, kw, call):
+    # two calls on the same inputs give bit-identical outputs (no atomics in any sum; the
+    # fused combine folds the partials in partition order, whichever workgroup arrives last)
+    case = make_case(name, **kw)
     dc = to_device(case)
-    a = api.case_call(dc, return_lse=True, return_o32=True)
-    b = api.case_call(dc, return_lse=True, return_o32=True)
+    print(f"[parity] determinism {name}", flush=True)
+    a = api.case_call(dc, return_lse=True, return_o32=True, **call)
+    b = api.case_call(dc, return_lse=True, return_o32=True, **call)
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
