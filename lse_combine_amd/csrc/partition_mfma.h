@@ -260,7 +260,7 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
   constexpr int DQK = S::DQK, DK = S::DK, DR = S::DR, DB = S::DB, NJ = S::NJ, NJK = S::NJK;
   typedef KTile<S, F8> KT;
   const bool direct = a.direct_single && count == 1;
-  const int lane = wv.lane, n = wv.n, qd = wv.qd, hc = wv.hc, kvh = wv.kvh, ks = wv.ks, KS = wv.KS;
+  const int lane = wv.lane, n = wv.n, qd = wv.qd, kvh = wv.kvh, ks = wv.ks, KS = wv.KS;
   const int g = a.g;
   const bool wave_active = wv.wave_active, col_valid = wv.col_valid, is_lo = wv.is_lo;
   const float lo_mask = is_lo ? 1.f : 0.f;
