@@ -54,9 +54,6 @@ constexpr int kRing = 3;   // K tiles in LDS: one feeds P.V, one q.K, one is in 
 
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
-// byte offset of 16-byte chunk c of row r in a swizzled LDS row block
-__device__ __forceinline__ int swz(int r, int c) { return r * kRowBytes + ((c ^ (r & 7)) << 4); }
-
 // max over the four lanes n, n+16, n+32, n+48 on the VALU (v_permlane16/32_swap), without
 // the LDS permute unit that the tile's operand reads keep busy. Written out because the
 // compiler folds the two results of a swap of a value with itself into one; the s_nop
@@ -257,6 +254,9 @@ void partition_latent_kernel(PartArgs a) {
         for (int j = 0; j < kEarly; ++j) kf[j] = load_k(KQ, j);
       }
       __builtin_amdgcn_sched_barrier(0);
+      // the wave's issue priority is raised for its products, so that where the two waves of
+      // a SIMD are in different phases the one with matrix-core work issues first
+      __builtin_amdgcn_s_setprio(1);
       // O^T += V^T P^T for the wave's 4 depth blocks and all 4 head blocks: head block by
       // head block, the hi products of the 4 depth blocks, then their lo products, so that
       // no product waits for the one just before it
@@ -270,6 +270,7 @@ void partition_latent_kernel(PartArgs a) {
           o[db][hb2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pl[hb2], o[db][hb2], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
     } else {
 #pragma unroll
       for (int j = 0; j < kEarly; ++j) kf[j] = load_k(KQ, j);
