@@ -6,15 +6,18 @@ KV length uniform in [512, 32768] (seed 3: 626 521 keys), page table a seeded
 random permutation of the page pool, splits chosen per sequence.
 
 A step is one call of decode_attn_splitk (partition kernel + LSE combine) on
-inputs already resident in HBM. Output: one JSON line with
-  value          KV-read GB/s of the whole step (algorithmic bytes: attended keys
-                 x kv heads x (Dqk + Dv) x 2 B) ; us_per_step alongside
-  step_us_events per-step HIP-event times (p10 / median / p90): back to back, and with
-                 the Infinity Cache flushed before every step (1 GiB read and written
-                 outside the events), so that inputs under 256 MiB are not served from it
-  roofline       the partition kernel alone, timed with HIP events on its stream,
-                 against the 8 TB/s HBM peak; traffic from the committed
-                 rocprofv3 counter summary when it matches the current source
+inputs already resident in HBM. The K timed steps run one at a time, each after the
+Infinity Cache has been flushed (1 GiB read and written outside the step's HIP events),
+so that no input is served from the memory-side cache of the step before. Output: one
+JSON line with
+  value / ms_per_step  KV-read GB/s of the whole step (algorithmic bytes: attended keys
+                 x kv heads x (Dqk + Dv) x 2 B) and the step time, both from the median
+                 of the K per-step HIP-event times (p10 / p90 in step_us_events_cache_flushed)
+  step_us_back_to_back  labelled extra: the same steps issued back to back without a flush
+                 (wall clock over K steps, and per-step event times)
+  roofline       the partition kernel alone, timed with HIP events on its stream (cache
+                 flushed before every launch), against the 8 TB/s HBM peak; traffic from the
+                 committed rocprofv3 counter summary when it matches the current source
   cpu_baseline   the fp64 CPU oracle timed on this host's cores
 Other workloads can be timed with --workload (not the reported line by default).
 """
@@ -108,6 +111,7 @@ def main():
 
     # --- streaming-read probe and a copy of known size (counter calibration) ---
     lib = _lib.load()
+    probe = _lib.load_probe()
     import ctypes
     probe_bytes = int(args.probe_gib * (1 << 30)) // 16 * 16
     probe_src = torch.empty(probe_bytes, dtype=torch.uint8, device=dev)
@@ -118,8 +122,9 @@ def main():
     for i in range(6):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        _lib.check(lib.da_read_probe(ctypes.c_void_p(probe_src.data_ptr()), probe_bytes,
-                                     ctypes.c_void_p(sink.data_ptr()), stream))
+        if probe.da_read_probe(ctypes.c_void_p(probe_src.data_ptr()), probe_bytes, ctypes.c_void_p(sink.data_ptr()),
+                               stream):
+            raise RuntimeError("read probe launch failed")
         e1.record()
         torch.cuda.synchronize()
         if i:
@@ -127,47 +132,59 @@ def main():
     read_probe_gbps = probe_bytes / statistics.median(probe_times) / 1e9
     copy_bytes = 256 << 20
     copy_dst = torch.empty(copy_bytes, dtype=torch.uint8, device=dev)
-    _lib.check(lib.da_copy_probe(ctypes.c_void_p(probe_src.data_ptr()), ctypes.c_void_p(copy_dst.data_ptr()),
-                                 copy_bytes, stream))
+    if probe.da_copy_probe(ctypes.c_void_p(probe_src.data_ptr()), ctypes.c_void_p(copy_dst.data_ptr()), copy_bytes,
+                           stream):
+        raise RuntimeError("copy probe launch failed")
     torch.cuda.synchronize()
     del probe_src, copy_dst
 
-    # --- the timed decode steps ---
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    s_per_step = (t1 - t0) / args.steps
-    value = kv_bytes / s_per_step / 1e9
-
-    # --- per-step HIP-event times: back to back, and after flushing the Infinity Cache ---
-    # (a step's inputs under 256 MiB can otherwise be served from the memory-side cache of
-    # the step before; the flush reads and writes 1 GiB outside the events)
+    # The Infinity Cache (256 MiB) is flushed before every timed step and launch: 1 GiB read
+    # and written outside the events, so that a step's inputs are never served from the
+    # memory-side cache of the step before.
     flush_buf = torch.zeros(1 << 30, dtype=torch.uint8, device=dev)
-    n_ev = max(args.steps, 10)
 
-    def event_steps(flush):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
-        for e0, e1 in evs:
-            if flush:
-                flush_buf.add_(1)
-            e0.record()
-            step()
-            e1.record()
-        torch.cuda.synchronize()
-        us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+    def summary(us):
+        us = sorted(us)
         pick = lambda f: us[min(len(us) - 1, int(f * len(us)))]
         med = statistics.median(us)
         return {"p10": round(pick(0.1), 2), "median": round(med, 2), "p90": round(pick(0.9), 2),
                 "kv_GBps_median": round(kv_bytes / (med * 1e-6) / 1e9, 1)}
 
-    step_hot = event_steps(False)
-    step_flushed = event_steps(True)
-    del flush_buf
+    # --- warm-up, then EXACTLY `steps` timed steps, each after a flush ---
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        flush_buf.add_(1)
+        e0.record()
+        step()
+        e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    flushed_us = [e0.elapsed_time(e1) * 1e3 for e0, e1 in evs]
+    step_flushed = summary(flushed_us)
+    s_per_step = statistics.median(flushed_us) * 1e-6
+    value = kv_bytes / s_per_step / 1e9
+
+    # --- labelled extra: the same steps back to back, with no flush in between ---
+    torch.cuda.synchronize()
+    b0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    b1 = time.perf_counter()
+    hot_wall_s = (b1 - b0) / args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in evs:
+        e0.record()
+        step()
+        e1.record()
+    torch.cuda.synchronize()
+    step_hot = summary([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
+    step_hot["wall_us_per_step"] = round(hot_wall_s * 1e6, 2)
+    step_hot["kv_GBps_wall"] = round(kv_bytes / hot_wall_s / 1e9, 1)
 
     # --- the partition kernel alone (same kernels, launched pass by pass) ---
     # arguments are marshalled once so the host stays ahead of the GPU and the
@@ -200,12 +217,14 @@ def main():
     n_timed = max(args.steps, 10)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_timed)]
     for i in range(n_timed):
+        flush_buf.add_(1)
         evs[i][0].record()
         _lib.check(part_fn(*part_args))
         evs[i][1].record()
         _lib.check(lib.decode_attn_combine(*comb_args))
         evs[i][2].record()
     torch.cuda.synchronize()
+    del flush_buf
     for e in evs:
         part_ms.append(e[0].elapsed_time(e[1]))
         comb_ms.append(e[1].elapsed_time(e[2]))
@@ -229,8 +248,10 @@ def main():
         "ms_per_step": round(s_per_step * 1e3, 4),
         "us_per_step": round(s_per_step * 1e6, 2),
         "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
-        "step_us_events": step_hot,
+        "timing": "median of the per-step HIP-event times, Infinity Cache flushed before every step",
+        "timed_region_wall_s": round(t1 - t0, 4),
         "step_us_events_cache_flushed": step_flushed,
+        "step_us_back_to_back": step_hot,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -249,15 +249,6 @@ int decode_attn_combine(const da_problem* p, const int32_t* seq_lens, float scal
                         const float* part_ml, void* out, float* lse_out, float* o_f32_out,
                         void* stream);
 
-/* Measurement probes (not part of attention). da_read_probe streams n_bytes
- * (a positive multiple of 16) from device src with 16-byte loads and writes one
- * fp32 per workgroup (at most 4096) into device sink, so the reads cannot be
- * elided. da_copy_probe copies n_bytes (multiple of 16) from src to dst (device,
- * non-overlapping): a plain copy of known size against which hardware traffic
- * counters are calibrated. */
-int da_read_probe(const void* src, size_t n_bytes, float* sink, void* stream);
-int da_copy_probe(const void* src, void* dst, size_t n_bytes, void* stream);
-
 /* Message of the last failed call on this thread ("" if none). */
 const char* da_last_error(void);
 

@@ -1,4 +1,5 @@
-"""ctypes loader for libdecode_attn.so (the C ABI declared in include/decode_attn.h)."""
+"""ctypes loaders for libdecode_attn.so (the C ABI declared in include/decode_attn.h) and
+for the benchmark's probe library libda_probe.so (include/da_probe.h)."""
 
 from __future__ import annotations
 
@@ -10,6 +11,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB_PATH = os.path.join(PKG, "lib", "libdecode_attn.so")
 HEADER = os.path.join(ROOT, "include", "decode_attn.h")
+PROBE_LIB_PATH = os.path.join(PKG, "lib", "libda_probe.so")
+PROBE_HEADER = os.path.join(ROOT, "include", "da_probe.h")
 
 DA_OK, DA_EINVAL, DA_EUNSUPPORTED, DA_EWORKSPACE, DA_EHIP = 0, -1, -2, -3, -4
 DA_F32, DA_BF16, DA_FP8_E4M3 = 0, 1, 2
@@ -57,13 +60,17 @@ _SIGS = {
                                              _I32, _I32, _P, _P, _P]),
     "decode_attn_combine": (ctypes.c_int, [ctypes.POINTER(DaProblem), _P, ctypes.c_float, _I32, _I32, _P, _P,
                                            _P, _P, _P, _P]),
-    "da_read_probe": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
-    "da_copy_probe": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
     "da_last_error": (ctypes.c_char_p, []),
     "da_version": (ctypes.c_char_p, []),
 }
 
+_PROBE_SIGS = {
+    "da_read_probe": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
+    "da_copy_probe": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
+}
+
 _lib = None
+_probe = None
 
 
 def load():
@@ -81,14 +88,29 @@ def load():
     return _lib
 
 
+def load_probe():
+    """Load the measurement-probe library (benchmark only)."""
+    global _probe
+    if _probe is None:
+        if not os.path.exists(PROBE_LIB_PATH):
+            raise RuntimeError(f"{PROBE_LIB_PATH} is missing: build it with __graft_entry__.build()")
+        lib = ctypes.CDLL(PROBE_LIB_PATH)
+        for name, (res, args) in _PROBE_SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _probe = lib
+    return _probe
+
+
 def check(code):
     if code != DA_OK:
         raise DaError(code, load().da_last_error().decode())
     return code
 
 
-def header_functions():
-    """Names of the functions include/decode_attn.h declares."""
-    text = open(HEADER).read()
+def header_functions(header=HEADER):
+    """Names of the functions a header (default include/decode_attn.h) declares."""
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(da_\w+|decode_attn_\w+)\s*\(", text, flags=re.M)))

@@ -1,4 +1,6 @@
-"""Build the HIP library (gfx950) in-tree: lse_combine_amd/lib/libdecode_attn.so."""
+"""Build the HIP libraries (gfx950) in-tree: lse_combine_amd/lib/libdecode_attn.so (the
+decode-attention library) and lse_combine_amd/lib/libda_probe.so (the benchmark's
+measurement probes, a library of its own)."""
 
 from __future__ import annotations
 
@@ -12,6 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libdecode_attn.so")
+PROBE_LIB = os.path.join(LIBDIR, "libda_probe.so")
+PROBE_SRC = os.path.join(CSRC, "probe", "probe.hip")
 INCLUDE = os.path.join(ROOT, "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -32,11 +36,11 @@ def sources():
 
 
 def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compile every HIP source for gfx950 and link the shared library. Always rebuilds."""
+    """Compile every HIP source for gfx950 and link both shared libraries. Always rebuilds."""
     os.makedirs(LIBDIR, exist_ok=True)
     objdir = os.path.join(ROOT, "_build", "obj")
     os.makedirs(objdir, exist_ok=True)
-    srcs = sources()
+    srcs = sources() + [PROBE_SRC]
     procs = []
     objs = []
     for src in srcs:
@@ -49,15 +53,20 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         if len(procs) >= jobs:
             _drain(procs)
     _drain(procs)
-    tmp = LIB + ".tmp"
+    _link(objs[:-1], LIB, verbose)
+    _link(objs[-1:], PROBE_LIB, verbose)
+    return LIB
+
+
+def _link(objs, lib, verbose):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     out = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if out.returncode != 0:
         raise RuntimeError("link failed:\n" + out.stdout)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
 
 
 def _drain(procs):

@@ -587,22 +587,6 @@ int decode_attn_combine(const da_problem* p, const int32_t* seq_lens, float scal
   return ok();
 }
 
-int da_read_probe(const void* src, size_t n_bytes, float* sink, void* stream) {
-  if (!src || !sink || n_bytes == 0 || n_bytes % 16) return fail(DA_EINVAL, "read probe needs src, sink and n_bytes % 16 == 0");
-  (void)hipGetLastError();
-  const hipError_t e = da::launch_read_probe(src, n_bytes, sink, (hipStream_t)stream);
-  if (e != hipSuccess) return fail(DA_EHIP, "read probe launch failed: %s", hipGetErrorString(e));
-  return ok();
-}
-
-int da_copy_probe(const void* src, void* dst, size_t n_bytes, void* stream) {
-  if (!src || !dst || n_bytes == 0 || n_bytes % 16) return fail(DA_EINVAL, "copy probe needs src, dst and n_bytes % 16 == 0");
-  (void)hipGetLastError();
-  const hipError_t e = da::launch_copy_probe(src, dst, n_bytes, (hipStream_t)stream);
-  if (e != hipSuccess) return fail(DA_EHIP, "copy probe launch failed: %s", hipGetErrorString(e));
-  return ok();
-}
-
 const char* da_last_error(void) { return g_err; }
 
 const char* da_version(void) { return "decode_attn 0.1 (gfx950)"; }

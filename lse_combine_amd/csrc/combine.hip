@@ -1,5 +1,4 @@
-// Split-K pass 2: the log-sum-exp combine (fa4_splitk_combine_write, first paragraph),
-// plus the measurement probes.
+// Split-K pass 2: the log-sum-exp combine (fa4_splitk_combine_write, first paragraph).
 //
 // Threads own (row, 16-byte depth slice) units: as on the pages each thread forms the
 // per-row weights itself and owns a band of depth columns; the threads of a row together
@@ -97,32 +96,6 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
   write_row_unit(a.out, a.o32, a.lse, row, DV, ch * 4, M, Ls, acc, a.scale);
 }
 
-// One workgroup per compute unit streams a contiguous share of the buffer, each thread
-// keeping four 16-byte loads in flight (of the layouts tried on MI355X, the fastest
-// plain streaming read: about 7.3 TB/s).
-constexpr int kProbeThreads = 512, kProbeUnroll = 4;
-__global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const u32x4* src, size_t n16, float* sink) {
-  const size_t b0 = n16 * blockIdx.x / gridDim.x, b1 = n16 * (blockIdx.x + 1) / gridDim.x;
-  u32x4 acc = {0u, 0u, 0u, 0u};
-  size_t i = b0 + threadIdx.x;
-  for (; i + (kProbeUnroll - 1) * kProbeThreads < b1; i += kProbeUnroll * kProbeThreads) {
-    u32x4 v[kProbeUnroll];
-#pragma unroll
-    for (int u = 0; u < kProbeUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * kProbeThreads);
-#pragma unroll
-    for (int u = 0; u < kProbeUnroll; ++u) acc ^= v[u];
-  }
-  for (; i < b1; i += kProbeThreads) acc ^= __builtin_nontemporal_load(src + i);
-  uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
-  for (int o = 32; o >= 1; o >>= 1) x ^= __shfl_xor(x, o);
-  if ((threadIdx.x & 63) == 0 && x == 0x7fc00001u) sink[blockIdx.x] = 1.f;  // keeps the loads alive
-}
-
-__global__ __launch_bounds__(256) void copy_probe_kernel(const u32x4* src, u32x4* dst, size_t n16) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
-}
-
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
@@ -157,28 +130,6 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
     else
       hipLaunchKernelGGL((combine_kernel<512, 2>), dim3((unsigned)rows), dim3(kCombineThreads), 0, s, a);
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_read_probe(const void* src, size_t n_bytes, float* sink, hipStream_t s) {
-  const size_t n16 = n_bytes / 16;
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    cus = 256;
-  size_t blocks = cus < 1 ? 1 : (size_t)cus;
-  if (blocks > 4096) blocks = 4096;
-  if (blocks > n16) blocks = n16 > 0 ? n16 : 1;
-  hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)blocks), dim3(kProbeThreads), 0, s, (const u32x4*)src, n16,
-                     sink);
-  return hipGetLastError();
-}
-
-hipError_t launch_copy_probe(const void* src, void* dst, size_t n_bytes, hipStream_t s) {
-  const size_t n16 = n_bytes / 16;
-  size_t blocks = (n16 + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
-  if (blocks == 0) blocks = 1;
-  hipLaunchKernelGGL(copy_probe_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const u32x4*)src, (u32x4*)dst, n16);
   return hipGetLastError();
 }
 

@@ -83,7 +83,5 @@ hipError_t launch_partition_mfma_d256(const PartArgs& a, int page_mode, int kv_h
                                       hipStream_t s);
 hipError_t launch_partition_latent(const PartArgs& a, int page_mode, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
-hipError_t launch_read_probe(const void* src, size_t n_bytes, float* sink, hipStream_t s);
-hipError_t launch_copy_probe(const void* src, void* dst, size_t n_bytes, hipStream_t s);
 
 }  // namespace da

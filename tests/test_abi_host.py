@@ -31,11 +31,24 @@ def test_exports_every_declared_function(lib):
     names = _lib.header_functions()
     assert {"decode_attn_splitk", "decode_attn_splitk_fused", "decode_attn_partition", "decode_attn_combine",
             "da_supported",
-            "da_choose_splits", "da_workspace_bytes", "da_last_error", "da_version",
-            "da_read_probe", "da_copy_probe"} <= set(names)
+            "da_choose_splits", "da_workspace_bytes", "da_last_error", "da_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert b"gfx950" in lib.da_version()
+
+
+def test_probe_library_is_apart_from_the_product():
+    # the measurement probes live in their own library and header; the attention library
+    # neither declares nor exports them
+    probe = _lib.load_probe()
+    names = _lib.header_functions(_lib.PROBE_HEADER)
+    assert set(names) == {"da_read_probe", "da_copy_probe"}
+    for n in names:
+        assert hasattr(probe, n), n
+        assert n not in _lib.header_functions()
+    prod = ctypes.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert not hasattr(prod, n), n
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -185,9 +198,10 @@ def test_partition_and_combine_argument_checks(lib):
              None) == DA_EUNSUPPORTED
 
 
-def test_probe_argument_checks(lib):
-    assert lib.da_read_probe(FAKE, 15, FAKE, None) == DA_EINVAL
-    assert lib.da_copy_probe(FAKE, None, 16, None) == DA_EINVAL
+def test_probe_argument_checks():
+    probe = _lib.load_probe()
+    assert probe.da_read_probe(FAKE, 15, FAKE, None) == DA_EINVAL
+    assert probe.da_copy_probe(FAKE, None, 16, None) == DA_EINVAL
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -382,9 +382,19 @@ def test_combine_only_on_oracle_partials(Dv, P):
 # ---------------------------------------------------------------------------
 # the named workloads at full size
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("name", ["tiny", "gqa", "long", "latent"])
+# Every (sequence, query, head) row of every named workload is compared element by element
+# with the oracle: the method is an exact re-association of the definition, so no row may
+# differ beyond the stated tolerances (the oracle runs the largest of these in seconds).
+FULL_WORKLOADS = ["tiny", "gqa", "paged_gqa", "long", "latent", "paged_gqa_q2", "paged_gqa_fp8", "paged_glm",
+                  "paged_glm_fp8"]
+
+
+@pytest.mark.parametrize("name", FULL_WORKLOADS)
 def test_workload_full(name):
-    check_case(workload(name), f"workload {name}")
+    out, lse, o32 = check_case(workload(name), f"workload {name} (all rows)")
+    assert torch.isfinite(o32).all()
+    del out, lse, o32
+    torch.cuda.empty_cache()
 
 
 FP8 = [
@@ -469,36 +479,6 @@ def test_multiquery_fused_combine():
         out, lse, o32 = api.case_call(dc, return_lse=True, return_o32=True, fused=True, workspace=ws)
         torch.cuda.synchronize()
         assert_parity(out, lse, o32, O, LSE, what=f"multi-query fused call {rep}")
-
-
-def test_workload_paged_gqa_q2_sampled():
-    case = workload("paged_gqa_q2")
-    print("[parity] workload paged_gqa_q2 (sampled rows)", flush=True)
-    out, lse, o32 = run(case)
-    lens = case.seq_lens.numpy()
-    rows = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 23})
-    O, LSE = oracle_for(case, batch_rows=rows)
-    assert_parity(out[rows], lse[rows], o32[rows], O, LSE, what="paged_gqa_q2 sampled")
-
-
-def test_workload_paged_gqa_fp8_sampled():
-    case = workload("paged_gqa_fp8")
-    print("[parity] workload paged_gqa_fp8 (sampled rows)", flush=True)
-    out, lse, o32 = run(case)
-    lens = case.seq_lens.numpy()
-    rows = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 11, 31})
-    O, LSE = oracle_for(case, batch_rows=rows)
-    assert_parity(out[rows], lse[rows], o32[rows], O, LSE, what="paged_gqa_fp8 sampled")
-
-
-def test_workload_paged_gqa_sampled():
-    case = workload("paged_gqa")
-    print("[parity] workload paged_gqa (sampled rows)", flush=True)
-    out, lse, o32 = run(case)
-    lens = case.seq_lens.numpy()
-    rows = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 7, 19, 31})
-    O, LSE = oracle_for(case, batch_rows=rows)
-    assert_parity(out[rows], lse[rows], o32[rows], O, LSE, what="paged_gqa sampled")
 
 
 # ---------------------------------------------------------------------------
@@ -588,17 +568,6 @@ def test_wide_depth_equal_share_partials(fp8):
     torch.cuda.synchronize()
     Oref, Lref = oracle_for(case)
     assert_parity(out, lse, o32, Oref, Lref, what="wide depth equal shares combine")
-
-
-@pytest.mark.parametrize("name", ["paged_glm", "paged_glm_fp8"])
-def test_workload_glm_style_sampled(name):
-    case = workload(name)
-    print(f"[parity] workload {name} (sampled rows)", flush=True)
-    out, lse, o32 = run(case)
-    lens = case.seq_lens.numpy()
-    rows = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 13, 31})
-    O, LSE = oracle_for(case, batch_rows=rows)
-    assert_parity(out[rows], lse[rows], o32[rows], O, LSE, what=f"{name} sampled")
 
 
 @pytest.mark.parametrize("fp8", [False, True])
