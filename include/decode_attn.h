@@ -163,6 +163,20 @@ int decode_attn_splitk(const da_problem* p, const void* q, const void* k_cache,
                        float scale, int32_t num_splits, void* out, float* lse_out,
                        float* o_f32_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The whole decode step of decode_attn_splitk (same arguments and results) without a
+ * workspace argument, for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation). The partials live in a
+ * fixed scratch array of 64 MiB that the library holds on every device it runs on for the
+ * life of the process; the call allocates and frees nothing. A problem whose workspace
+ * (da_workspace_bytes) exceeds 64 MiB returns DA_EWORKSPACE with nothing enqueued. Every
+ * call on one device uses that device's one array: calls that overlap on a device (other
+ * streams, other threads) race and must not be issued; calls ordered on one stream are
+ * safe (no state carries over from one call to the next). */
+int decode_attn_splitk_noalloc(const da_problem* p, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* page_table, const int32_t* seq_lens,
+                               float scale, int32_t num_splits, void* out, float* lse_out,
+                               float* o_f32_out, void* stream);
+
 /* The whole decode step with the combine fused into pass 1 (fa4_splitk_combine_write,
  * fourth paragraph: the writer that completes the set combines all). Every workgroup of
  * a (sequence, kv-head group) stores its partial, publishes it device-wide and counts

@@ -46,6 +46,8 @@ _SIGS = {
     "da_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(DaProblem), _I32, ctypes.POINTER(ctypes.c_size_t)]),
     "decode_attn_splitk": (ctypes.c_int, [ctypes.POINTER(DaProblem), _P, _P, _P, _P, _P, ctypes.c_float, _I32,
                                           _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "decode_attn_splitk_noalloc": (ctypes.c_int, [ctypes.POINTER(DaProblem), _P, _P, _P, _P, _P, ctypes.c_float,
+                                                  _I32, _P, _P, _P, _P]),
     "decode_attn_splitk_fused": (ctypes.c_int, [ctypes.POINTER(DaProblem), _P, _P, _P, _P, _P, ctypes.c_float,
                                                 _I32, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "decode_attn_splitk_fp8": (ctypes.c_int, [ctypes.POINTER(DaProblem), _P, _P, _P, _P, _P, _P, _P,

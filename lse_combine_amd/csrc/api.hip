@@ -494,6 +494,49 @@ int decode_attn_splitk(const da_problem* p, const void* q, const void* k_cache, 
                     o_f32_out, workspace, workspace_bytes, stream, false);
 }
 
+// Scratch memory of decode_attn_splitk_noalloc: the workspace of one step (fp32 partials,
+// the equal-share slot table) in a file-scope device array, so that the call allocates
+// nothing. Every device the library runs on holds its own copy, at its own address, until
+// the process ends. In host code the name `scratch` is a host-side stand-in, never a device
+// address: kernels and copies get the address from scratch_ptr().
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+// Device address of the current device's `scratch`, looked up once per device (with that
+// device current) and kept.
+static int scratch_ptr(void** out) {
+  static std::mutex mu;
+  static void* ptrs[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fail(DA_EHIP, "no usable current HIP device");
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptrs[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(DA_EHIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    ptrs[dev] = ptr;
+  }
+  *out = ptrs[dev];
+  return DA_OK;
+}
+
+int decode_attn_splitk_noalloc(const da_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* page_table, const int32_t* seq_lens, float scale, int32_t num_splits,
+                               void* out, float* lse_out, float* o_f32_out, void* stream) {
+  size_t need = 0;
+  int r = da_workspace_bytes(p, num_splits, &need);
+  if (r) return r;
+  if (need > kScratchBytes)
+    return fail(DA_EWORKSPACE,
+                "decode_attn_splitk_noalloc: this problem needs %zu bytes of workspace, more than the fixed "
+                "%zu-byte scratch array (use decode_attn_splitk with a workspace of its size)", need, kScratchBytes);
+  void* ws = nullptr;
+  if ((r = scratch_ptr(&ws))) return r;
+  return run_splitk(p, q, make_kv(k_cache, v_cache), page_table, seq_lens, scale, num_splits, out, lse_out,
+                    o_f32_out, ws, kScratchBytes, stream, false);
+}
+
 int decode_attn_splitk_fused(const da_problem* p, const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* page_table, const int32_t* seq_lens, float scale, int32_t num_splits,
                              void* out, float* lse_out, float* o_f32_out, void* workspace, size_t workspace_bytes,
