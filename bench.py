@@ -195,7 +195,8 @@ def main():
         return None if t is None else P_(t.data_ptr())
 
     if case.k_rope is not None:
-        kv = _lib.DaKv(dc.k_cache.data_ptr(), dc.v_cache.data_ptr(), dc.k_rope.data_ptr(),
+        kv = _lib.DaKv(dc.k_cache.data_ptr(), None if dc.v_cache is None else dc.v_cache.data_ptr(),
+                       dc.k_rope.data_ptr(),
                        None if dc.k_scale is None else dc.k_scale.data_ptr(),
                        None if dc.v_scale is None else dc.v_scale.data_ptr())
         part_fn = lib.decode_attn_partition_kv

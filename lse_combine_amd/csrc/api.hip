@@ -28,7 +28,7 @@ int ok() {
   return DA_OK;
 }
 
-enum Variant { kVarFma = 0, kVarMfma = 1, kVarLatent = 2 };
+enum Variant { kVarFma = 0, kVarMfma = 1, kVarShared = 2 };
 
 constexpr int kTileKeys = 32;  // key tile of every partition kernel; chunks are multiples of it
 
@@ -84,6 +84,30 @@ int check_problem(const da_problem* p, Variant* var) {
   if (p->nope_depth < 0 || (p->nope_depth > 0 && p->nope_depth >= p->qk_depth))
     return fail(DA_EINVAL, "nope_depth must be 0 (every K column in k_cache) or in [1, qk_depth) (got %d of %d)",
                 p->nope_depth, p->qk_depth);
+  // One kv head for many q heads: the shared-kv-head kernel (q.K and P.V as dense
+  // contractions over all q heads). MLA-style latent 576/512 with V = the first 512 nope
+  // columns, and GLM-style 256/256 (nope 192, V of its own) once q_len x group exceeds the
+  // 16 MFMA columns of the GQA kernel; the 64 rotary columns in the K rows or stored apart.
+  const bool latent = p->qk_depth == 576 && p->ov_depth == 512;
+  const bool glm_mqa = p->qk_depth == 256 && p->ov_depth == 256 && !p->v_is_k_prefix && p->num_kv_heads == 1 &&
+                       ql * g > 16;
+  if (latent || glm_mqa) {
+    const int nope_apart = latent ? 512 : 192;
+    if (p->dtype != DA_BF16 || p->num_kv_heads != 1 || (latent && !p->v_is_k_prefix) || p->kernel == DA_KERNEL_FMA)
+      return fail(DA_EUNSUPPORTED,
+                  "depth %d/%d with one kv head runs on the shared-kv-head matrix-core kernel: bf16, one kv head%s",
+                  p->qk_depth, p->ov_depth, latent ? ", V = the first 512 K columns (v_is_k_prefix)" : "");
+    if (p->nope_depth != 0 && p->nope_depth != nope_apart)
+      return fail(DA_EUNSUPPORTED, "shared-kv-head kernel at %d/%d: rotary columns apart need nope_depth %d (got %d)",
+                  p->qk_depth, p->ov_depth, nope_apart, p->nope_depth);
+    if (p->nope_depth > 0 && p->rope_dtype != DA_BF16)
+      return fail(DA_EUNSUPPORTED, "rotary columns stored apart must be bf16 (rope_dtype %d)", p->rope_dtype);
+    if (p->kv_dtype == DA_FP8_E4M3)
+      return fail(DA_EUNSUPPORTED, "the shared-kv-head kernel (depth %d/%d, one kv head) takes bf16 caches",
+                  p->qk_depth, p->ov_depth);
+    *var = kVarShared;
+    return DA_OK;
+  }
   // Features only the matrix-core kernel has: several queries per sequence, fp8 caches,
   // the wider depth pairs and rotary columns stored apart.
   const bool d128 = p->qk_depth == 128 && p->ov_depth == 128;
@@ -108,14 +132,6 @@ int check_problem(const da_problem* p, Variant* var) {
     return DA_OK;
   }
 
-  if (p->qk_depth == 576 && p->ov_depth == 512) {
-    if (p->dtype != DA_BF16 || !p->v_is_k_prefix || p->num_kv_heads != 1 || g % 16 != 0 || p->kernel == DA_KERNEL_FMA)
-      return fail(DA_EUNSUPPORTED,
-                  "depth 576/512 is supported only as bf16 latent-shared attention with one kv head and a multiple "
-                  "of 16 q heads (matrix-core kernel)");
-    *var = kVarLatent;
-    return DA_OK;
-  }
   if (p->qk_depth != 128 || p->ov_depth != 128)
     return fail(DA_EUNSUPPORTED,
                 "supported depths (q.K / V): 128/128; 192/128 and 256/256 with bf16 q on the matrix-core kernel; "
@@ -176,8 +192,9 @@ void share_shape(const da_problem* p, int cus, int* HG, int* KS, int* W) {
   *W = (int)(w < 1 ? 1 : w);
 }
 
-// Workgroups of the partition kernel that fit on one compute unit at once.
-int wgs_per_cu(Variant v) { return v == kVarMfma ? 1 : 2; }
+// Workgroups of the partition kernel that fit on one compute unit at once (the matrix-core
+// kernels take most of the LDS and two waves per SIMD).
+int wgs_per_cu(Variant v) { return v == kVarFma ? 2 : 1; }
 
 int choose(const da_problem* p, Variant var, int32_t num_splits, int cus, int32_t* chunk_out, int32_t* splits_out) {
   if (num_splits < 0) return fail(DA_EINVAL, "num_splits must be >= 0 (0 = automatic)");
@@ -200,15 +217,18 @@ int choose(const da_problem* p, Variant var, int32_t num_splits, int cus, int32_
     // average length of max_seq_len / 2 and aims at about four rounds of workgroups
     // over the whole chip; chunks stay within [256, 8192] keys.
     const int slots = cus * wgs_per_cu(var);
-    const int64_t est_units = (int64_t)p->batch * p->num_kv_heads * ((maxlen + 1) / 2);
+    // workgroups per (sequence, partition): kv heads, or 64-column blocks on the
+    // shared-kv-head kernel
+    const int64_t per_part = var == kVarShared ? ceil_div(rows_per_seq(p), 64) : p->num_kv_heads;
+    const int64_t est_units = (int64_t)p->batch * per_part * ((maxlen + 1) / 2);
     C = ceil_div(est_units, 4LL * slots);
     if (C < 256) C = 256;
     if (C > 8192) C = 8192;
   }
   C = ceil_div(C, unit) * unit;
   if (C > ceil_div(maxlen, unit) * unit) C = ceil_div(maxlen, unit) * unit;
-  if (var == kVarLatent && p->page_size > 0) {
-    // the latent kernel stages one partition's page indices in LDS (at most 256 pages)
+  if (var == kVarShared && p->page_size > 0) {
+    // the shared-kv-head kernel stages one partition's page indices in LDS (at most 256 pages)
     const int64_t cap = (255LL * p->page_size) / kTileKeys * kTileKeys;
     if (C > cap) C = cap / unit * unit > 0 ? cap / unit * unit : kTileKeys;
   }
@@ -257,8 +277,8 @@ int check_split_args(const da_problem* p, Variant var, int32_t chunk, int32_t ma
     return DA_OK;
   }
   if (chunk < 0 || chunk % kTileKeys) return fail(DA_EINVAL, "chunk_tokens must be 0 or a positive multiple of %d (got %d)", kTileKeys, chunk);
-  if (p->qk_depth == 576 && p->page_size > 0 && (int64_t)chunk > 255LL * p->page_size)
-    return fail(DA_EUNSUPPORTED, "latent-shared kernel: chunk_tokens must be <= 255 pages (%d keys)", 255 * p->page_size);
+  if (var == kVarShared && p->page_size > 0 && (int64_t)chunk > 255LL * p->page_size)
+    return fail(DA_EUNSUPPORTED, "shared-kv-head kernel: chunk_tokens must be <= 255 pages (%d keys)", 255 * p->page_size);
   const int64_t maxlen = p->max_seq_len > 0 ? p->max_seq_len : 1;
   if (max_splits < ceil_div(maxlen, chunk))
     return fail(DA_EINVAL, "max_splits %d < ceil(max_seq_len %d / chunk_tokens %d)", max_splits, p->max_seq_len, chunk);
@@ -294,7 +314,7 @@ int launch_partition(const da_problem* p, Variant var, const da::PartArgs& a, hi
       break;
     }
     default:
-      e = da::launch_partition_latent(a, pm, s);
+      e = da::launch_partition_shared(a, pm, s);
       break;
   }
   if (e != hipSuccess) return fail(DA_EHIP, "partition kernel launch failed: %s", hipGetErrorString(e));

@@ -46,7 +46,8 @@ __device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
 }
 
 // Direct-to-LDS 16-byte buffer load (the 64 lanes fill 1 KB at LDS address lds_base, lane
-// l at 16 l; a lane outside the buffer range writes nothing), non-temporal, written as
+// l at 16 l; a lane outside the buffer range reads nothing and writes zeros there, as an
+// out-of-range buffer load returns zeros), non-temporal, written as
 // inline assembly: the compiler does not see an LDS write, so it adds no wait of its own
 // before later LDS reads (it would wait for the most recent such load, whatever it
 // fills). Every consumer waits explicitly (wait_vm). M0, which holds the LDS base of the

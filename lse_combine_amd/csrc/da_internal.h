@@ -81,7 +81,8 @@ hipError_t launch_partition_mfma_d192(const PartArgs& a, int page_mode, int kv_h
                                       hipStream_t s);
 hipError_t launch_partition_mfma_d256(const PartArgs& a, int page_mode, int kv_heads_per_wg, int key_splits,
                                       hipStream_t s);
-hipError_t launch_partition_latent(const PartArgs& a, int page_mode, hipStream_t s);
+// one kv head for all q heads (latent 576/512, one-kv-head 256/256): partition_shared.hip
+hipError_t launch_partition_shared(const PartArgs& a, int page_mode, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 
 }  // namespace da

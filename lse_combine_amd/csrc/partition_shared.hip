@@ -1,0 +1,613 @@
+// Split-K pass 1 when one kv head serves every q head of a sequence (FA4Config,
+// use_shared_kv / shared_kv_cols: MLA-style latent attention, where V is the first ov_depth
+// columns of each K row, and one-kv-head attention with a V of its own whose depth need not
+// equal the nope depth, as FA4Config's with_splitk keeps for GLM-style configs). Every q
+// head reads the same K and V rows, so q.K and P.V are dense contractions (about 200 flop
+// per byte of KV) and run on v_mfma_f32_16x16x32_bf16.
+//
+// A K row is [nope columns | rotary columns] (FA4Config, rope_depth = q.K depth minus the
+// nope depth); the rotary columns sit in the K rows or in a tensor of their own (bf16,
+// FA4Config rope_dtype). The kernel only sees two column ranges with their own base and row
+// stride, so both forms run the same code.
+//
+// Workgroup = (partition p, block of 64 (query, head) columns, sequence b): eight waves,
+// two per SIMD, with one role each:
+//   waves 0-3, q.K and the softmax: wave w takes the 32 columns 32 (w/2) .. +31 (two MFMA
+//       column blocks, q in registers over the full q.K depth) and the 16 keys of key half
+//       w%2 of each 32-key tile. Every K operand read from LDS feeds two products. Its
+//       softmax needs nothing from other waves: the exponentials are taken against a fixed
+//       reference max (below). The probabilities go to LDS, split hi/lo in bf16, in the
+//       B-operand layout of P.V.
+//   waves 4-7, P.V: wave 4+v takes the V columns DV/4 v .. +DV/4-1 for all 64 columns
+//       (O^T in registers), reading V^T transposed from the LDS tile (ds_read_b64_tr_b16)
+//       and P from LDS.
+// Each SIMD thus holds one wave of each role: the softmax arithmetic of the one runs beside
+// the matrix-core products of the other instead of both waves stalling in the same phase.
+// Per 32-key tile and workgroup the LDS carries the tile once (direct-to-LDS loads), K
+// twice (two column pairs), V once, and P (8 KB) four times.
+//
+// Tiles pass through a ring of four LDS slots: in step s the q.K waves work on tile s, the
+// P.V waves on tile s - 1, and tiles s + 1 and s + 2 are in flight; one barrier per step. P
+// is double-buffered. (Four slots of the latent tile and the two P buffers fill the 160 KB
+// of LDS exactly: the page indices live in registers and the exchange arrays in a P buffer.
+// With one tile in flight a step waits for its whole tile, and a load-only copy streams at
+// about 2.8 TB/s.)
+//
+// P must not be rounded to bf16 before P.V (the fp32 O must stay within 1e-5), so it is
+// split as p = hi + lo, hi = bf16(p), lo = bf16(p - hi), and P.V runs both halves.
+//
+// Fixed reference max: the exponentials are taken relative to a per-column reference m_ref
+// (the first tile's max) and O is never rescaled inside the key loop. That holds while every
+// score stays within kHeadroomLog2 powers of two of m_ref; a score beyond that (adversarial
+// logits) makes the workgroup run its partition once more with m_ref = the partition's exact
+// max, which the q.K waves track on the side.
+//
+// Epilogue as in the GQA kernel: normalised partial + (m, l) per column, or the finished
+// bf16 row when the sequence has a single partition (fa4_splitk_combine_write, second
+// paragraph).
+#include "da_device.h"
+
+namespace da {
+namespace {
+
+constexpr int kTile = 32;
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kCols = 64;                 // (query, head) columns of a workgroup: 4 MFMA blocks of 16
+constexpr int kMaxLdsPages = 256;
+constexpr int kLdsBytes = 160 * 1024;
+constexpr float kHeadroomLog2 = 64.f;
+
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// Depths of one instantiation: DN nope columns and DR rotary columns make the q.K depth; V
+// has DV columns and is either the first DV nope columns (SHARED) or a cache of its own.
+template <int DN_, int DR_, int DV_, bool SHARED_>
+struct SShape {
+  static constexpr int DN = DN_, DR = DR_, DV = DV_;
+  static constexpr bool SHARED = SHARED_;
+  static constexpr int DQK = DN + DR;
+  static constexpr int NJ = DQK / 32;            // 32-deep k-steps of q.K
+  static constexpr int NJN = DN / 32;            // ... over the nope columns
+  static constexpr int kNRow = DN * 2;           // LDS bytes of one row, per region
+  static constexpr int kRRow = DR * 2;
+  static constexpr int kVRow = SHARED ? DN * 2 : DV * 2;
+  static constexpr int kNBytes = kTile * kNRow;  // region offsets inside a slot
+  static constexpr int kRBytes = kTile * kRRow;
+  static constexpr int kVOff = SHARED ? 0 : kNBytes + kRBytes;
+  static constexpr int kSlot = kNBytes + kRBytes + (SHARED ? 0 : kTile * DV * 2);
+  static constexpr int kBlocks = kSlot / 1024;   // 1 KB direct-to-LDS loads per tile
+  static constexpr int kPerWave = (kBlocks + kWaves - 1) / kWaves;
+  static constexpr int kVCols = DV / 4;          // V columns of one P.V wave
+  static constexpr int kDB = kVCols / 16;        // its 16-deep O blocks
+  static_assert(NJ % 2 == 0 && DN % 64 == 0 && DR % 64 == 0 && DV % 64 == 0, "depths");
+  static_assert(kNBytes % 1024 == 0 && kRBytes % 1024 == 0 && kSlot % 1024 == 0, "1 KB load blocks");
+  static_assert(!SHARED || DV <= DN, "a shared V is a prefix of the nope columns");
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// max over the four lanes n, n+16, n+32, n+48 on the VALU (v_permlane16/32_swap), keeping
+// the LDS permute unit free for the tile's operands. Written out because the compiler folds
+// the two results of a swap of a value with itself into one; the s_nop gives the two wait
+// states a VALU write needs before a permlane reads it.
+__device__ __forceinline__ float max_over_key_groups(float v) {
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  v = fmaxf(a, b);
+  a = v;
+  b = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
+}
+
+constexpr int kPBytes = 4 * 2 * 64 * 16;   // P of one tile: 4 column blocks x (hi, lo) x 64 lanes x 16 B
+
+// Per q.K wave, column block of its pair and column: maxima, sums, reference maxima; and one
+// flag per wave for the block-wide "any". They live in P buffer 1 whenever no P is live there.
+struct XArrays {
+  float xm[4][2][16], xl[4][2][16], xr[4][2][16];
+  int any[kWaves];
+};
+static_assert(sizeof(XArrays) <= kPBytes, "exchange arrays fit a P buffer");
+
+// XOR swizzle of the 16-byte chunks of a tile row, chosen per region from its row stride so
+// that the operand reads hit 16 different 16-byte bank groups (the LDS serves 256 bytes per
+// clock: 64 banks of 4 bytes). Physical chunk = logical chunk ^ swz(row), its own inverse.
+//  - rows of a multiple of 256 bytes (latent nope 1024, V 512): the K reads take one chunk
+//    of 16 consecutive rows, the transposing V reads two adjacent chunks of 8 rows, so
+//    swz(r) = 2 (r & 7) + ((r >> 3) & 1) (16 distinct values over 16 rows, whose halves are
+//    distinct over 8 rows); the XOR spans 16-chunk groups.
+//  - rows of 128 bytes mod 256 (rotary 128, GLM nope 384): consecutive rows alternate bank
+//    halves, so swz(r) = (r >> 1) & 7; the XOR stays within 8-chunk groups.
+template <int RB>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(RB % 256 == 0 || RB % 256 == 128, "row strides of 128 + 256 k or 256 k bytes");
+  if constexpr (RB % 256 == 0) return ((r & 7) << 1) | ((r >> 3) & 1);
+  else return (r >> 1) & 7;
+}
+
+template <class S, int R>
+struct SmemBase {
+  char tile[R][S::kSlot];
+  // P of a tile for P.V (tile s uses buffer s & 1): hi and lo bf16 parts per column block in
+  // the B-operand layout, [4 column blocks][hi, lo][key half][64 lanes][8 bytes]. Lane (n, qd)
+  // reads the k-slots 8 qd .. 8 qd + 7 of column n: the 8 bytes of key half 0 (keys 4 qd .. +3)
+  // and the 8 bytes of key half 1 (keys 16 + 4 qd .. +3), one ds_read2_b64; each key half's
+  // wave writes its 8 bytes per lane contiguously (no bank conflicts either way).
+  char pbuf[2][kPBytes];
+};
+template <class S, int R, bool LDS_PAGES>
+struct SharedSmem : SmemBase<S, R> {};
+template <class S, int R>
+struct SharedSmem<S, R, true> : SmemBase<S, R> {
+  int pages[kMaxLdsPages];   // page indices of the partition (per-key page lookup)
+};
+
+// Ring depth: R tiles in LDS, of which R - 2 are in flight (one feeds q.K, one P.V). With a
+// power-of-two page size or a contiguous cache the page indices live in registers and four
+// slots fit (two tiles in flight); the per-key page lookup keeps its indices in LDS and
+// three slots.
+template <int PM>
+constexpr int ring_of() { return PM == kPagedGeneral ? 3 : 4; }
+
+template <class S, int PM>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_row_bytes) {
+  constexpr int R = ring_of<PM>();
+  constexpr int A = R - 2;                      // tiles in flight
+  constexpr bool kLdsPages = PM == kPagedGeneral;
+  typedef SharedSmem<S, R, kLdsPages> Smem;
+  static_assert(sizeof(Smem) <= kLdsBytes, "LDS budget");
+  __shared__ __attribute__((aligned(16))) Smem sm;
+  XArrays& xa = *(XArrays*)sm.pbuf[1];
+
+  const int p = blockIdx.x, cblk = blockIdx.y, b = blockIdx.z;
+  const int L = __builtin_amdgcn_readfirstlane(attended_len(a, b, PM == kContiguous));
+  const int start = p * a.chunk;
+  if (start >= L) return;
+  const int end = min(start + a.chunk, L);
+  const int P_b = min((L + a.chunk - 1) / a.chunk, a.max_splits);
+  const bool direct = a.direct_single && P_b == 1;
+  const int ncols = a.Hq;                      // rows of the sequence = (query, head) columns
+  const int col0 = cblk * kCols;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, qd = lane >> 4;
+  const float c = a.c;
+  const int n_tiles = (end - start + kTile - 1) / kTile;
+
+  // A ragged tile's rows past the end are not loaded and keep what the slot held; they
+  // must be finite (their scores are masked, their V meets p = 0). A slot that a partition
+  // of more than R tiles reuses holds an earlier full tile; shorter partitions zero the
+  // slots first.
+  if (n_tiles <= R)
+    for (int i = tid; i < R * S::kSlot / 16; i += kThreads) *(u32x4*)(&sm.tile[0][0] + i * 16) = u32x4{0u, 0u, 0u, 0u};
+  int first_page = 0;
+  // page indices of the partition (at most kMaxLdsPages): in LDS for the per-key lookup, else
+  // lane l of register k holds page first_page + 64 k + l
+  int pg[kMaxLdsPages / 64];
+  if constexpr (PM != kContiguous) {
+    first_page = start / a.page_size;
+    const int n_pages = (end - 1) / a.page_size - first_page + 1;
+    const int32_t* pt = a.page_table + (int64_t)b * a.pt_stride + first_page;
+    if constexpr (kLdsPages) {
+      for (int i = tid; i < n_pages && i < kMaxLdsPages; i += kThreads) {
+        const int page = pt[i];
+        sm.pages[i] = page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kMaxLdsPages / 64; ++k) {
+        const int i = 64 * k + lane;
+        const int page = i < n_pages ? pt[i] : 0;
+        pg[k] = page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
+      }
+    }
+  }
+  __syncthreads();
+
+  // The tile of keys t0 .. t0 + 31 lands in LDS by direct-to-LDS 16-byte loads: 1 KB block j
+  // of the slot is loaded by wave j % 8 (its load i = j / 8). Within a region of rows of RB
+  // bytes, lane l of a block writes slot byte pos = 1024 j + 16 l - (region offset), i.e. row
+  // pos / RB and chunk slot (pos % RB) / 16, and loads the cache chunk slot ^ swz(row) of
+  // that row there.
+  // A wave issues its loads of a tile (kPerWave or kPerWave - 1 of them) on every step, past
+  // the last tile too, with an empty buffer range: such a load reads nothing and writes zeros
+  // into its LDS block, here a block of the retired slot being refilled. The wave's count is
+  // the same at every wait. (A lane outside the buffer range of a direct-to-LDS load writes
+  // zeros, so a wave's surplus block is skipped rather than loaded empty: it would land in a
+  // live block.)
+  const char* kc = (const char*)a.k;
+  const char* vc = (const char*)a.v;
+  const uint32_t krow = (uint32_t)a.Dk * 2;           // bytes between tokens in k_cache
+  const uint32_t vrow = (uint32_t)a.v_row_len * 2;    // ... in v_cache
+  // per load i of this wave: region base and row stride (uniform), lane offset
+  const char* lbase[S::kPerWave];
+  uint32_t lstride[S::kPerWave], loff[S::kPerWave];
+  bool lvalid[S::kPerWave];
+#pragma unroll
+  for (int i = 0; i < S::kPerWave; ++i) {
+    const int j = w + kWaves * i;
+    lvalid[i] = j < S::kBlocks;
+    // (the region follows from the block alone: regions are whole 1 KB blocks)
+    const int jb = (lvalid[i] ? j : 0) * 1024;
+    int q2, r, cs, gc;
+    if (jb < S::kNBytes) {
+      q2 = jb + lane * 16, lbase[i] = kc, lstride[i] = krow;
+      r = q2 / S::kNRow, cs = (q2 - r * S::kNRow) >> 4, gc = cs ^ swz<S::kNRow>(r);
+    } else if (jb < S::kNBytes + S::kRBytes) {
+      q2 = jb - S::kNBytes + lane * 16, lbase[i] = rope_base, lstride[i] = rope_row_bytes;
+      r = q2 / S::kRRow, cs = (q2 - r * S::kRRow) >> 4, gc = cs ^ swz<S::kRRow>(r);
+    } else {
+      q2 = jb - S::kNBytes - S::kRBytes + lane * 16, lbase[i] = vc, lstride[i] = vrow;
+      r = q2 / (S::DV * 2), cs = (q2 - r * (S::DV * 2)) >> 4, gc = cs ^ swz<S::DV * 2>(r);
+    }
+    loff[i] = (uint32_t)r * lstride[i] + 16u * (uint32_t)gc;
+  }
+  // cache row of the first key of the tile at t0 (the tile is 32 consecutive rows)
+  auto tile_row0 = [&](int t0) -> int64_t {
+    if constexpr (PM == kContiguous) {
+      return (int64_t)b * a.kv_capacity + t0;
+    } else {
+      const int pi = min(max((t0 >> a.page_shift) - first_page, 0), kMaxLdsPages - 1);
+      const int sel = pi >> 6;
+      const int v = sel == 0 ? pg[0] : sel == 1 ? pg[1] : sel == 2 ? pg[2] : pg[3];
+      const int page = __builtin_amdgcn_readlane(v, pi & 63);
+      return ((int64_t)page << a.page_shift) + (t0 & (a.page_size - 1));
+    }
+  };
+  auto issue = [&](int ti) {
+    char* dst = sm.tile[ti % R];
+    const int t0 = start + ti * kTile;
+    if constexpr (PM != kPagedGeneral) {
+      // 32 consecutive cache rows: one scalar base per region; the buffer range ends at the
+      // last valid row, so a ragged tile's missing rows are not read (and past the last tile
+      // nothing is)
+      const bool live = ti < n_tiles;
+      const int64_t row0 = live ? tile_row0(t0) : 0;
+      const uint32_t rows = live ? (uint32_t)__builtin_amdgcn_readfirstlane(min(kTile, end - t0)) : 0u;
+      const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(dst));
+#pragma unroll
+      for (int i = 0; i < S::kPerWave; ++i) {
+        if (!lvalid[i]) break;   // (uniform; only the last load of a wave can be surplus)
+        const u32x4 rs = rsrc_words(lbase[i] + row0 * lstride[i], rows * lstride[i]);
+        lds_dma16(rs, loff[i], lb + (w + kWaves * i) * 1024);
+      }
+    } else {
+      if (ti >= n_tiles) return;
+      // any page size: every lane looks up its own row (rows past the end repeat the last
+      // key; their scores are masked)
+      const int last = min(kTile - 1, end - 1 - t0);
+#pragma unroll
+      for (int i = 0; i < S::kPerWave; ++i) {
+        if (!lvalid[i]) continue;
+        const int j = w + kWaves * i;
+        const int r = (int)(loff[i] / lstride[i]);
+        const int t = t0 + min(r, last);
+        const int pi = t / a.page_size;
+        const int slot = min(max(pi - first_page, 0), kMaxLdsPages - 1);
+        const int page = min(max(sm.pages[slot], 0), a.num_pages - 1);
+        const int64_t row = (int64_t)page * a.page_size + (t - pi * a.page_size);
+        __builtin_amdgcn_global_load_lds((const void*)(lbase[i] + row * lstride[i] + (loff[i] - r * lstride[i])),
+                                         (DA_LDS void*)(dst + j * 1024), 16, 0, 0);
+      }
+    }
+  };
+  // tile s has landed (this wave's loads): the loads of the A - 1 tiles after it may stay in
+  // flight
+  // (blocks are dealt round-robin, so a wave has kPerWave or kPerWave - 1 of them)
+  const bool full_share = lvalid[S::kPerWave - 1];
+  auto wait_tile = [&] {
+    if constexpr (A == 2) {
+      if (full_share) wait_vm<S::kPerWave>();
+      else wait_vm<S::kPerWave - 1>();
+    } else {
+      wait_vm<0>();
+    }
+  };
+  // block-wide "any" (every wave calls it; two barriers, flags in P buffer 1)
+  auto block_any = [&](bool f) {
+    __syncthreads();
+    if (lane == 0) xa.any[w] = f ? 1 : 0;
+    __syncthreads();
+    int r = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) r |= xa.any[i];
+    return r != 0;
+  };
+
+  if (w < 4) {
+    // ------------------------------------------------------------------ q.K and softmax
+    const int cp = w >> 1, kh = w & 1;
+    // q as the B operand of S^T = K q^T: column block bi of the pair, k-step j holds depth
+    // 32 j + 8 qd .. +8 of column col0 + 32 cp + 16 bi + n (zero past the last column)
+    bf16x8 qf[2][S::NJ];
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+      const int col = col0 + 32 * cp + 16 * bi + n;
+      const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)b * ncols + (col < ncols ? col : 0)) * S::DQK + 8 * qd;
+#pragma unroll
+      for (int j = 0; j < S::NJ; ++j) {
+        u32x4 v = *(const u32x4*)(qrow + 32 * j);
+        if (col >= ncols) v = u32x4{0u, 0u, 0u, 0u};
+        qf[bi][j] = as_bf16x8(v);
+      }
+    }
+    // keys this lane's columns attend (query qi of q_len sees keys t < L - q_len + 1 + qi)
+    int col_end[2];
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+      const int col = col0 + 32 * cp + 16 * bi + n;
+      const int qi = col < ncols ? col / a.g : 0;
+      col_end[bi] = min(end, L - a.q_len + 1 + qi);
+    }
+    // K operands: k-step j reads logical chunk 4 j + qd of row r = 16 kh + n. The swizzle
+    // only changes the low 4 (wide rows) or 3 (narrow rows) bits of the chunk, so the offset
+    // is a per-lane part for j mod 4 (resp. mod 2) plus a constant.
+    const int r = 16 * kh + n;
+    constexpr bool kNW = S::kNRow % 256 == 0;
+    const int fn = swz<S::kNRow>(r), fr = swz<S::kRRow>(r);
+    int kn[4], kr[2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) kn[u] = r * S::kNRow + 16 * (((4 * u + qd) ^ fn) & (kNW ? 15 : 7));
+#pragma unroll
+    for (int u = 0; u < 2; ++u) kr[u] = S::kNBytes + r * S::kRRow + 16 * ((4 * u + qd) ^ fr);
+    auto load_k = [&](const DA_LDS char* KL, int j) {
+      int off;
+      if (j < S::NJN) off = kNW ? kn[j & 3] + 256 * (j >> 2) : kn[j & 1] + 128 * (j >> 1);
+      else off = kr[(j - S::NJN) & 1] + 128 * ((j - S::NJN) >> 1);
+      return as_bf16x8(*(const DA_LDS u32x4*)(KL + off));
+    };
+    // K operands in flight ahead of their products (q takes 4 NJ registers per column block)
+    constexpr int kAhead = S::NJ < 12 ? S::NJ : 12;
+
+    float m_ref[2], m_lane[2], l_lane[2];
+    bool beyond = false;
+    // Step s of the key loop: S^T of tile s over the full q.K depth (two chains per column
+    // block), then the softmax against m_ref and the P write.
+    auto qk_step = [&](int s, bool first) {
+      const DA_LDS char* KL = (const DA_LDS char*)sm.tile[s % R];
+      bf16x8 kf[S::NJ];
+#pragma unroll
+      for (int j = 0; j < kAhead; ++j) kf[j] = load_k(KL, j);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 acc[2][2];
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi) acc[bi][0] = acc[bi][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < S::NJ; ++j) {
+        acc[0][j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j], qf[0][j], acc[0][j & 1], 0, 0, 0);
+        acc[1][j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j], qf[1][j], acc[1][j & 1], 0, 0, 0);
+        if (j + kAhead < S::NJ) kf[j + kAhead] = load_k(KL, j + kAhead);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const int t0 = start + s * kTile;
+      float pr[2][4];
+      float mx[2];
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi) {
+        f32x4 sc = acc[bi][0] + acc[bi][1];
+        // keys past the end of a ragged tile, or past a query's own position, get -inf
+        const int nvalid = col_end[bi] - t0 - 16 * kh - 4 * qd;
+        if (__ballot(nvalid < 4)) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (i >= nvalid) sc[i] = -INFINITY;
+        }
+        mx[bi] = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        m_lane[bi] = fmaxf(m_lane[bi], mx[bi]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr[bi][i] = sc[i];
+      }
+      if (first) {
+        // the reference of the first pass: the first tile's max over both key halves; one
+        // exchange per pass, the other tiles need no cross-lane step (P buffer 1 holds no P
+        // before step 1)
+        float g4[2];
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi) {
+          g4[bi] = max_over_key_groups(mx[bi]);
+          if (qd == 0) xa.xm[w][bi][n] = g4[bi];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi) {
+          const float mt = fmaxf(g4[bi], xa.xm[w ^ 1][bi][n]);
+          // (a column with no key in this tile: any finite reference; a later key far above
+          // it sends the workgroup to the exact second pass)
+          m_ref[bi] = mt == -INFINITY ? 0.f : mt;
+        }
+      }
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi) {
+        beyond = beyond || (mx[bi] - m_ref[bi]) * c > kHeadroomLog2;
+        const float mc = m_ref[bi] * c;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pr[bi][i] = exp2_fast(fmaf(pr[bi][i], c, -mc));
+          l_lane[bi] += pr[bi][i];
+        }
+        // hi and lo parts of P into the buffer (8 bytes each per lane)
+        const uint32_t h0 = pack_bf16x2(pr[bi][0], pr[bi][1]), h1 = pack_bf16x2(pr[bi][2], pr[bi][3]);
+        const uint32_t l0 = pack_bf16x2(pr[bi][0] - bf16lo(h0), pr[bi][1] - bf16hi(h0));
+        const uint32_t l1 = pack_bf16x2(pr[bi][2] - bf16lo(h1), pr[bi][3] - bf16hi(h1));
+        char* pb = sm.pbuf[s & 1] + (((2 * cp + bi) * 2 * 2 + kh) * 64 + lane) * 8;
+        *(u32x2*)pb = u32x2{h0, h1};
+        *(u32x2*)(pb + 2 * 64 * 8) = u32x2{l0, l1};
+      }
+    };
+
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) m_lane[bi] = -INFINITY, m_ref[bi] = 0.f;
+    wait_vm<0>();   // q is in registers: from here on the only loads in flight are the tiles'
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi) l_lane[bi] = 0.f;
+#pragma unroll
+      for (int i = 0; i < A; ++i) issue(i);
+      for (int s = 0; s <= n_tiles; ++s) {
+        wait_tile();       // this wave's part of tile s is in LDS
+        __syncthreads();   // ... and every wave's; P of tile s - 1 is written; tile s - 2 is retired
+        issue(s + A);
+        if (s < n_tiles) qk_step(s, pass == 0 && s == 0);
+      }
+      wait_vm<0>();        // (the empty loads past the last tile)
+      if (!block_any(beyond)) break;
+      // second pass: the reference is each column's exact max over the partition
+      float g4[2];
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi) {
+        g4[bi] = max_over_key_groups(m_lane[bi]);
+        if (qd == 0) xa.xm[w][bi][n] = g4[bi];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi) {
+        const float mt = fmaxf(g4[bi], xa.xm[w ^ 1][bi][n]);
+        m_ref[bi] = mt == -INFINITY ? 0.f : mt;
+      }
+      beyond = false;
+      __syncthreads();   // (xm is written again before it is next read)
+    }
+    // (max, sum, reference) per column for the P.V waves
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+      const float mt = max_over_key_groups(m_lane[bi]);
+      float l = l_lane[bi];
+      l += __shfl_xor(l, 16);
+      l += __shfl_xor(l, 32);
+      if (qd == 0) {
+        xa.xm[w][bi][n] = mt;
+        xa.xl[w][bi][n] = l;
+        xa.xr[w][bi][n] = m_ref[bi];
+      }
+    }
+    __syncthreads();
+  } else {
+    // ------------------------------------------------------------------ P.V
+    const int v = w - 4;
+    // V^T A operand of 16-deep block D: lane (n, qd) holds depth 16 D + n of keys 4 qd .. +3
+    // and 16 + 4 qd .. +3 (the k-slot order of the P buffer); that is chunk 2 D + ((n & 3) >> 1)
+    // of rows ra and ra + 16, ra = 4 qd + (n >> 2), read transposed
+    const int ra = 4 * qd + (n >> 2);
+    const int v_off = S::kVOff + ra * S::kVRow + (n & 1) * 8;
+    auto load_v = [&](const DA_LDS char* KL, int db) {
+      const int ch = 2 * (v * S::kDB + db) + ((n & 3) >> 1);
+      const DA_LDS char* pa = KL + v_off + 16 * (ch ^ swz<S::kVRow>(ra));
+      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 DA_LDS*)pa);
+      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 DA_LDS*)(pa + 16 * S::kVRow));
+      s16x8 v8;
+      v8[0] = va[0]; v8[1] = va[1]; v8[2] = va[2]; v8[3] = va[3];
+      v8[4] = vb[0]; v8[5] = vb[1]; v8[6] = vb[2]; v8[7] = vb[3];
+      return __builtin_bit_cast(bf16x8, v8);
+    };
+    f32x4 o[S::kDB][4];
+    // O^T += V^T P^T for the wave's depth blocks and all four column blocks: every operand is
+    // requested first, then column block by column block the hi products of the depth blocks,
+    // then their lo products, so that no product waits for the one just before it
+    auto pv_step = [&](int s) {
+      const DA_LDS char* KL = (const DA_LDS char*)sm.tile[s % R];
+      const char* pb = sm.pbuf[s & 1] + lane * 8;
+      bf16x8 vf[S::kDB], ph[4], pl[4];
+#pragma unroll
+      for (int db = 0; db < S::kDB; ++db) vf[db] = load_v(KL, db);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const u32x2 h0 = *(const u32x2*)(pb + ((cb * 2 + 0) * 2 + 0) * 64 * 8);
+        const u32x2 h1 = *(const u32x2*)(pb + ((cb * 2 + 0) * 2 + 1) * 64 * 8);
+        const u32x2 l0 = *(const u32x2*)(pb + ((cb * 2 + 1) * 2 + 0) * 64 * 8);
+        const u32x2 l1 = *(const u32x2*)(pb + ((cb * 2 + 1) * 2 + 1) * 64 * 8);
+        ph[cb] = as_bf16x8(u32x4{h0[0], h0[1], h1[0], h1[1]});
+        pl[cb] = as_bf16x8(u32x4{l0[0], l0[1], l1[0], l1[1]});
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+#pragma unroll
+        for (int db = 0; db < S::kDB; ++db)
+          o[db][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], ph[cb], o[db][cb], 0, 0, 0);
+#pragma unroll
+        for (int db = 0; db < S::kDB; ++db)
+          o[db][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pl[cb], o[db][cb], 0, 0, 0);
+      }
+    };
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+      for (int db = 0; db < S::kDB; ++db)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) o[db][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < A; ++i) issue(i);
+      for (int s = 0; s <= n_tiles; ++s) {
+        wait_tile();
+        __syncthreads();
+        issue(s + A);
+        if (pass == 0 && s == 0) __syncthreads();   // (the q.K waves' first-tile exchange)
+        if (s >= 1) pv_step(s - 1);
+      }
+      wait_vm<0>();
+      if (!block_any(false)) break;
+      __syncthreads();   // (the q.K waves' exact-max exchange)
+      __syncthreads();
+    }
+    __syncthreads();   // the q.K waves have published (max, sum, reference)
+    // O and l are relative to m_ref; the partial reports the exact max M, so its sum is
+    // rescaled once (the normalised O does not change)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const int col = col0 + 16 * cb + n;
+      if (col >= ncols) continue;
+      const int qw = 2 * (cb >> 1), bi = cb & 1;
+      const float M = fmaxf(xa.xm[qw][bi][n], xa.xm[qw + 1][bi][n]);
+      const float Ls = xa.xl[qw][bi][n] + xa.xl[qw + 1][bi][n];   // both halves share m_ref
+      const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+      const float l_true = Ls > 0.f ? Ls * exp2_fast((xa.xr[qw][bi][n] - M) * c) : 0.f;
+#pragma unroll
+      for (int db = 0; db < S::kDB; ++db)
+        store_unit(a, b, col, p, direct, S::kVCols * v + 16 * db + 4 * qd, o[db][cb] * inv, M, l_true,
+                   v == 0 && db == 0 && qd == 0);
+    }
+  }
+}
+
+template <class S>
+hipError_t launch_shape(const PartArgs& a, int page_mode, hipStream_t s) {
+  // rotary columns: stored apart (k_rope rows of DR bf16), or the last DR of each K row
+  const char* rope = a.k_rope ? (const char*)a.k_rope : (const char*)a.k + S::DN * 2;
+  const uint32_t rope_row = a.k_rope ? (uint32_t)S::DR * 2 : (uint32_t)a.Dk * 2;
+  // x = partition, y = block of 64 columns, z = sequence: with 8 partitions the column blocks
+  // of a (sequence, partition) are 8 workgroup ids apart (same XCD under round-robin
+  // dispatch, so the second read of each tile is an L2 hit)
+  dim3 grid(a.max_splits, (a.Hq + kCols - 1) / kCols, a.B), block(kThreads);
+  switch (page_mode) {
+    case kContiguous:
+      hipLaunchKernelGGL((partition_shared_kernel<S, kContiguous>), grid, block, 0, s, a, rope, rope_row);
+      break;
+    case kPagedAligned:
+      hipLaunchKernelGGL((partition_shared_kernel<S, kPagedAligned>), grid, block, 0, s, a, rope, rope_row);
+      break;
+    default:
+      hipLaunchKernelGGL((partition_shared_kernel<S, kPagedGeneral>), grid, block, 0, s, a, rope, rope_row);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// One kv head for all q heads: MLA-style latent (q.K 576 = 512 nope + 64 rotary, V = the
+// first 512 nope columns) and one-kv-head GLM-style widths (q.K 256 = 192 nope + 64 rotary,
+// V 256 of its own). The rotary columns may be in the K rows or stored apart.
+hipError_t launch_partition_shared(const PartArgs& a, int page_mode, hipStream_t s) {
+  if (a.Hkv != 1 || a.kv_fp8) return hipErrorInvalidValue;
+  const bool rope_apart = a.k_rope != nullptr;
+  if (a.Dqk == 576 && a.Dv == 512 && a.v == a.k && a.Dk == (rope_apart ? 512 : 576))
+    return launch_shape<SShape<512, 64, 512, true>>(a, page_mode, s);
+  if (a.Dqk == 256 && a.Dv == 256 && a.v != a.k && a.Dk == (rope_apart ? 192 : 256))
+    return launch_shape<SShape<192, 64, 256, false>>(a, page_mode, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace da

@@ -249,6 +249,15 @@ WORKLOADS = {
     "paged_glm": dict(seed=6, batch=32, num_q_heads=16, num_kv_heads=16, qk_depth=256, ov_depth=256,
                       dtype=torch.bfloat16, page_size=64, len_range=(512, 8192), num_splits=0,
                       page_table_width=128, rope_apart=64),
+    # the latent workload with its 64 rotary columns stored apart (bf16 tensor of their own;
+    # the same draws, so the same values as "latent")
+    "latent_rope_apart": dict(seed=5, batch=16, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512,
+                              dtype=torch.bfloat16, page_size=64, seq_lens=[8192] * 16, num_splits=8,
+                              v_is_k_prefix=True, rope_apart=64),
+    # GLM-style widths with one kv head for all 128 q heads: q.K 256 = 192 nope + 64 rotary
+    # (stored apart, bf16), V 256 of its own; batch 16, L 8192, page 64, 8 splits
+    "glm_mqa": dict(seed=7, batch=16, num_q_heads=128, num_kv_heads=1, qk_depth=256, ov_depth=256,
+                    dtype=torch.bfloat16, page_size=64, seq_lens=[8192] * 16, num_splits=8, rope_apart=64),
     # the same with the nope columns and V as fp8 (E4M3) with per-token scales; the rotary
     # columns stay bf16
     "paged_glm_fp8": dict(seed=6, batch=32, num_q_heads=16, num_kv_heads=16, qk_depth=256, ov_depth=256,

@@ -70,7 +70,16 @@ def test_probe_library_is_apart_from_the_product():
     (dict(v_is_k_prefix=1, ov_depth=600, qk_depth=576), DA_EINVAL),
     (dict(num_q_heads=128, num_kv_heads=2, qk_depth=576, ov_depth=512, v_is_k_prefix=1), DA_EUNSUPPORTED),
     (dict(num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1), DA_OK),
-    (dict(num_q_heads=24, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1), DA_EUNSUPPORTED),
+    (dict(num_q_heads=24, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1), DA_OK),   # any head count
+    (dict(num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1, nope_depth=512,
+          rope_dtype=1), DA_OK),                                                                    # rotary apart
+    (dict(num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1, nope_depth=448,
+          rope_dtype=1), DA_EUNSUPPORTED),
+    (dict(num_q_heads=128, num_kv_heads=1, qk_depth=256, ov_depth=256), DA_OK),       # one kv head, own V
+    (dict(num_q_heads=128, num_kv_heads=1, qk_depth=256, ov_depth=256, nope_depth=192, rope_dtype=1), DA_OK),
+    (dict(num_q_heads=128, num_kv_heads=1, qk_depth=256, ov_depth=256, nope_depth=192, rope_dtype=0),
+     DA_EUNSUPPORTED),
+    (dict(num_q_heads=128, num_kv_heads=2, qk_depth=256, ov_depth=256), DA_EUNSUPPORTED),   # group 64 > 16
     (dict(num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=0), DA_EUNSUPPORTED),
     (dict(num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1, dtype=0), DA_EUNSUPPORTED),
 ])
@@ -241,7 +250,9 @@ def test_fp8_entry_points_need_their_scales(lib):
     (dict(q_len=2, page_size=16, max_pages_per_seq=256), DA_EUNSUPPORTED),
     (dict(q_len=2, kv_dtype=2), DA_OK),
     (dict(q_len=17), DA_EINVAL),
-    (dict(q_len=2, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1), DA_EUNSUPPORTED),
+    (dict(q_len=2, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1), DA_OK),
+    (dict(q_len=3, num_q_heads=32, num_kv_heads=1, qk_depth=256, ov_depth=256, nope_depth=192, rope_dtype=1),
+     DA_OK),                                                       # 96 columns on the shared-kv-head kernel
 ])
 def test_multiquery_support(lib, kw, code):
     assert lib.da_supported(ctypes.byref(prob(**kw))) == code

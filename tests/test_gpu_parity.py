@@ -171,6 +171,102 @@ def test_latent_large_logits_take_the_second_pass():
     assert_parity(out, lse, o32, O, LSE, o32_row_rtol=1e-4, what="latent large logits")
 
 
+# ---------------------------------------------------------------------------
+# the shared-kv-head kernel: one kv head for every q head. Latent rows (q.K 576 = 512 nope
+# + 64 rotary, V = the first 512 nope columns) and GLM-style widths with a V of its own
+# (q.K 256 = 192 nope + 64 rotary, V 256); rotary columns in the K rows or stored apart,
+# one or several queries, column counts that are not multiples of 16 or 64
+# ---------------------------------------------------------------------------
+LATENT = dict(num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=True)
+GLM_MQA = dict(num_kv_heads=1, qk_depth=256, ov_depth=256)
+SHARED = [
+    ("latent_apart_g64_paged64", dict(batch=2, num_q_heads=64, page_size=64, seq_lens=[700, 1313], num_splits=3,
+                                      seed=160, rope_apart=64, **LATENT)),
+    ("latent_apart_g128_contig", dict(batch=3, num_q_heads=128, seq_lens=[100, 33, 1], num_splits=2, seed=161,
+                                      rope_apart=64, **LATENT)),
+    ("latent_apart_g40_paged16_general", dict(batch=2, num_q_heads=40, page_size=16, seq_lens=[517, 64],
+                                              num_splits=0, seed=162, rope_apart=64, **LATENT)),
+    ("latent_q2_g64_paged64", dict(batch=3, num_q_heads=64, page_size=64, seq_lens=[1, 900, 2100], num_splits=3,
+                                   seed=163, q_len=2, **LATENT)),
+    ("latent_q3_g20_apart_paged32", dict(batch=2, num_q_heads=20, page_size=32, seq_lens=[2, 1500], num_splits=2,
+                                         seed=164, q_len=3, rope_apart=64, **LATENT)),
+    ("latent_g24_paged64", dict(batch=3, num_q_heads=24, page_size=64, seq_lens=[1025, 32, 2], num_splits=4,
+                                seed=165, **LATENT)),
+    ("latent_apart_poisoned", dict(batch=3, num_q_heads=64, page_size=64, seq_lens=[100, 1, 1025], num_splits=2,
+                                   seed=166, rope_apart=64, poison=True, spare_pages=3, **LATENT)),
+    ("glm_mqa_g64_apart_paged64", dict(batch=2, num_q_heads=64, page_size=64, seq_lens=[1500, 333], num_splits=3,
+                                       seed=170, rope_apart=64, **GLM_MQA)),
+    ("glm_mqa_g128_inline_contig", dict(batch=2, num_q_heads=128, seq_lens=[2000, 77], num_splits=2, seed=171,
+                                        **GLM_MQA)),
+    ("glm_mqa_g17_apart_paged64", dict(batch=3, num_q_heads=17, page_size=64, seq_lens=[1, 640, 3000],
+                                       num_splits=4, seed=172, rope_apart=64, **GLM_MQA)),
+    ("glm_mqa_q2_g32_apart_paged32", dict(batch=3, num_q_heads=32, page_size=32, seq_lens=[1, 700, 1700],
+                                          num_splits=2, seed=173, q_len=2, rope_apart=64, **GLM_MQA)),
+    ("glm_mqa_g64_apart_paged48_general", dict(batch=2, num_q_heads=64, page_size=48, seq_lens=[1000, 97],
+                                               num_splits=0, seed=174, rope_apart=64, **GLM_MQA)),
+    ("glm_mqa_apart_poisoned", dict(batch=3, num_q_heads=64, page_size=64, seq_lens=[100, 1, 1025], num_splits=2,
+                                    seed=175, rope_apart=64, poison=True, spare_pages=3, **GLM_MQA)),
+]
+
+
+@pytest.mark.parametrize("name,kw", SHARED, ids=[c[0] for c in SHARED])
+def test_shared_kv_head_parity(name, kw):
+    case = make_case(name, **kw)
+    out, lse, o32 = check_case(case, f"shared kv head {name}")
+    assert torch.isfinite(o32).all()
+    if case.q_len > 1:
+        for b, L in enumerate(case.seq_lens.tolist()):
+            for i in range(case.q_len):
+                if L - case.q_len + 1 + i <= 0:
+                    assert torch.all(out[b, i].float() == 0) and torch.all(torch.isneginf(lse[b, i]))
+
+
+@pytest.mark.parametrize("kw", [dict(rope_apart=64, **GLM_MQA), dict(rope_apart=64, **LATENT)],
+                         ids=["glm_mqa_apart", "latent_apart"])
+def test_shared_kv_head_large_logits_take_the_second_pass(kw):
+    case = make_case("big_shared", batch=2, num_q_heads=64, page_size=64, seq_lens=[1300, 700], num_splits=2,
+                     seed=176, q_scale=64.0, **kw)
+    out, lse, o32 = run(case)
+    O, LSE = oracle_for(case)
+    assert torch.isfinite(o32).all()
+    assert_parity(out, lse, o32, O, LSE, o32_row_rtol=1e-4, what="shared kv head large logits")
+
+
+@pytest.mark.parametrize("kw", [dict(rope_apart=64, **GLM_MQA), dict(q_len=2, **LATENT)],
+                         ids=["glm_mqa_apart", "latent_q2"])
+def test_shared_kv_head_partials_match_oracle(kw):
+    # pass 1 alone: every partition's (m, l) and normalised O against the oracle's partials
+    case = make_case("shared_parts", batch=2, num_q_heads=64, page_size=64, seq_lens=[1500, 333], seed=177, **kw)
+    dc = to_device(case)
+    chunk, P = 512, 3
+    po_t, pml_t = api.partition(dc.q, dc.k_cache, dc.v_cache, dc.page_table, dc.seq_lens, case.scale, chunk, P,
+                                page_size=64, v_is_k_prefix=case.v_is_k_prefix, ov_depth=case.ov_depth,
+                                k_rope=dc.k_rope)
+    torch.cuda.synchronize()
+    q = np32(case.q)
+    k = np32(case.k_cache)
+    if case.k_rope is not None:
+        k = np.concatenate([k, np32(case.k_rope)], axis=-1)
+    v = k[..., :case.ov_depth] if case.v_is_k_prefix else np32(case.v_cache)
+    lens = case.seq_lens.numpy().astype(np.int64)
+    ql = case.q_len
+    for i in range(ql):
+        qi = q[:, i] if ql > 1 else q
+        li = np.clip(lens - ql + 1 + i, 0, lens)
+        m, l, O = partition_partials_fp64(qi, k, v, li, case.scale, chunk, P, page_table=case.page_table.numpy(),
+                                          page_size=64)
+        rows = slice(i * case.q.shape[-2], (i + 1) * case.q.shape[-2])
+        ml = np32(pml_t)[:, rows]
+        po = np32(po_t)[:, rows]
+        for b in range(case.batch):
+            for pp in range(-(-int(lens[b]) // chunk)):
+                live = l[b, :, pp] > 0
+                np.testing.assert_allclose(ml[b, live, pp, 0], m[b, live, pp], rtol=1e-5, atol=1e-4)
+                np.testing.assert_allclose(ml[b, live, pp, 1], l[b, live, pp], rtol=1e-5)
+                err = np.abs(po[b, live, pp] - O[b, live, pp]).max(-1)
+                assert (err / np.abs(O[b, live, pp]).max(-1)).max() <= 1e-5
+
+
 DETERMINISM = [
     ("gqa_paged_auto", dict(batch=4, num_q_heads=32, num_kv_heads=4, qk_depth=128, page_size=64,
                             len_range=(500, 6000), num_splits=0, seed=43), {}),
@@ -386,7 +482,7 @@ def test_combine_only_on_oracle_partials(Dv, P):
 # with the oracle: the method is an exact re-association of the definition, so no row may
 # differ beyond the stated tolerances (the oracle runs the largest of these in seconds).
 FULL_WORKLOADS = ["tiny", "gqa", "paged_gqa", "long", "latent", "paged_gqa_q2", "paged_gqa_fp8", "paged_glm",
-                  "paged_glm_fp8"]
+                  "paged_glm_fp8", "latent_rope_apart", "glm_mqa"]
 
 
 @pytest.mark.parametrize("name", FULL_WORKLOADS)

@@ -537,3 +537,49 @@ def test_fp8_nope_with_bf16_rotary_brute_force_with_torch_decode(paged):
     np.testing.assert_allclose(O, Ob, atol=1e-13)
     np.testing.assert_allclose(LSE, Lb, rtol=1e-13)
     assert O.shape[-1] == 10
+
+
+# ---------------------------------------------------------------------------
+# one kv head for every q head: latent rows with the rotary columns stored apart, and a V
+# of its own whose depth differs from the nope depth; one and several queries
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("paged", [0, 4])
+@pytest.mark.parametrize("q_len", [1, 2])
+def test_latent_rows_with_rotary_apart_brute_force(paged, q_len):
+    # K row = [nope 8 | rotary 4], V = the first 6 nope columns (a prefix of the stored K
+    # columns, scale-free); brute force on the materialised full row and V
+    q, k, _, lens, pt = rng_case(200 + paged + q_len, B=3, Hq=6, Hkv=1, D=12, L=(9, 1, 14), paged=paged)
+    if q_len > 1:
+        q = np.random.default_rng(201).standard_normal((3, q_len, 6, 12))
+    O, LSE = decode_attention_fp64(q, k[..., :8], None, lens, 0.45, page_table=pt, page_size=paged,
+                                   v_is_k_prefix=True, ov_depth=6, k_rope=k[..., 8:])
+    v = np.ascontiguousarray(k[..., :6])
+    if q_len > 1:
+        Ob, Lb = brute_multiquery(q, k, v, lens, 0.45, pt, paged)
+    else:
+        Ob, Lb = brute(q, k, v, lens, 0.45, pt, paged)
+    np.testing.assert_allclose(O, Ob, atol=1e-13)
+    np.testing.assert_allclose(LSE, Lb, rtol=1e-13)
+    assert O.shape[-1] == 6
+    # a V taken from other columns of the row (here the last 6) gives another result
+    O_wrong, _ = decode_attention_fp64(q, k, np.ascontiguousarray(k[..., 6:]), lens, 0.45, page_table=pt,
+                                       page_size=paged)
+    assert np.abs(O_wrong - O).max() > 1e-3
+
+
+@pytest.mark.parametrize("paged", [0, 4])
+@pytest.mark.parametrize("q_len", [1, 3])
+def test_one_kv_head_own_v_depth_brute_force(paged, q_len):
+    # GLM-style widths in miniature with one kv head for all 8 q heads: K = [nope 6 | rotary
+    # 2] stored apart, V of depth 9 (!= nope 6) in a cache of its own
+    q, k, v, lens, pt = rng_case(210 + paged + q_len, B=2, Hq=8, Hkv=1, D=8, Dv=9, L=(11, 5), paged=paged)
+    if q_len > 1:
+        q = np.random.default_rng(211).standard_normal((2, q_len, 8, 8))
+    O, LSE = decode_attention_fp64(q, k[..., :6], v, lens, 0.5, page_table=pt, page_size=paged, k_rope=k[..., 6:])
+    if q_len > 1:
+        Ob, Lb = brute_multiquery(q, k, v, lens, 0.5, pt, paged)
+    else:
+        Ob, Lb = brute(q, k, v, lens, 0.5, pt, paged)
+    np.testing.assert_allclose(O, Ob, atol=1e-13)
+    np.testing.assert_allclose(LSE, Lb, rtol=1e-13)
+    assert O.shape[-1] == 9
