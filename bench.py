@@ -264,7 +264,8 @@ def main():
             "batch": B, "q_len": max(1, prob.q_len), "q_heads": Hq, "kv_heads": prob.num_kv_heads,
             "qk_depth": prob.qk_depth, "ov_depth": Dv, "nope_depth": prob.nope_depth, "page_size": case.page_size,
             "keys": tokens, "max_seq_len": int(case.seq_lens.max()),
-            "chunk_tokens": chunk, "max_splits": max_splits, "kernel": args.kernel, "combine": args.combine,
+            "num_splits": case.num_splits, "chunk_tokens": chunk, "max_splits": max_splits, "kernel": args.kernel,
+            "combine": args.combine,
             "kv_bytes": kv_bytes,
         },
         "roofline": {

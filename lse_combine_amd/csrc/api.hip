@@ -390,10 +390,9 @@ void set_kv_args(const da_problem* p, const da_kv& kv, da::PartArgs* a) {
   a->Dk = p->nope_depth > 0 ? p->nope_depth : p->qk_depth;
 }
 
-// The whole step. With `fused`, the matrix-core kernel combines in its last-arriving
-// workgroups (no second launch) wherever sequences have few partitions (up to 16, where
-// one workgroup's combine is short); elsewhere, and for the other kernels, the combine
-// is a launch of its own. The results are the same either way.
+// The whole step. With `fused`, the GQA matrix-core kernel combines in its last-arriving
+// workgroups (no second launch); the other kernels run the combine as a launch of its own.
+// The results are the same either way.
 int run_splitk(const da_problem* p, const void* q, const da_kv& kv, const int32_t* page_table, const int32_t* seq_lens,
                float scale, int32_t num_splits, void* out, float* lse_out, float* o_f32_out, void* workspace,
                size_t workspace_bytes, void* stream, bool fused) {
@@ -425,8 +424,7 @@ int run_splitk(const da_problem* p, const void* q, const da_kv& kv, const int32_
   a.o32 = o_f32_out;
   a.direct_single = 1;
   set_kv_args(p, kv, &a);
-  const int64_t per_seq = C == 0 ? (int64_t)P / p->batch + 1 : P;
-  const bool fuse = fused && var == kVarMfma && per_seq <= 16;
+  const bool fuse = fused && var == kVarMfma;
   if (fuse) a.counters = (int32_t*)((char*)workspace + cnt_off);
   if ((r = launch_partition(p, var, a, s, cus))) return r;
   if (!fuse && (r = launch_combine(p, seq_lens, scale, C, P, po, pml, out, lse_out, o_f32_out, 1, s))) return r;

@@ -17,6 +17,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define DA_LDS __attribute__((address_space(3)))
 
+template <int V>
+struct IntK {
+  static constexpr int value = V;
+};
+
 // Buffer-resource dword 3 for raw (untyped) dword loads on gfx9-family parts.
 constexpr int kRsrcWord3 = 0x00020000;
 // Cache policy of the K/V loads: non-temporal (each byte is read once per step).
@@ -152,11 +157,10 @@ __device__ __forceinline__ int64_t share_owner(int64_t t, int64_t U, int64_t W) 
 // running (M, Ls, acc) with the combine's weights l_j exp2((m_j - M) c); when a batch
 // raises the running max, what was summed so far is rescaled (fa4_splitk_combine_write,
 // first paragraph). ml / po point at partial 0 of the row; partials are `stride` partial
-// rows apart; loads are issued eight at a time. Partials with l_j == 0 weigh nothing.
-template <int DV>
+// rows apart; loads are issued kBatch at a time. Partials with l_j == 0 weigh nothing.
+template <int DV, int kBatch = 8>
 __device__ __forceinline__ void fold_partials(const float2* ml, const float* po, int64_t stride, int P, int j0,
                                               int step, float c, float& M, float& Ls, f32x4& acc) {
-  constexpr int kBatch = 8;
   for (int p0 = j0; p0 < P; p0 += step * kBatch) {
     float2 v[kBatch];
     f32x4 o[kBatch];
@@ -230,6 +234,90 @@ __device__ __forceinline__ void store_unit(const PartArgs& a, int b, int hq, int
       *(float2*)(a.part_ml + pr * 2) = ml;
     }
   }
+}
+
+// LDS a block of the combine needs to merge its S thread subsets (none for S = 1).
+template <int DV, int S, int NT>
+struct CombineLds {
+  static constexpr int kUnits = NT / S;
+  static constexpr int kBytes = S > 1 ? S * kUnits * (2 * 4 + 16) : 16;
+};
+
+// One block of the LSE combine (fa4_splitk_combine_write, first paragraph): NT threads own
+// (row, 4-wide depth slice) units, S threads per unit; block `blk` covers rows
+// blk * RPB .. +RPB-1. Thread subset s takes partitions s, s + S, ... of its row and keeps a
+// running (max, sum, O) for them (the same exp2 weights, rescaled when the running max
+// grows); the S results are merged through `lds` (CombineLds bytes) with the combine
+// formula. With S = 1 this is the plain per-thread combine; S > 1 shortens the dependent
+// load chain of rows with many partitions by a factor S. Every thread of the block calls it
+// (it holds a barrier when S > 1).
+template <int DV, int S, int NT>
+__device__ __forceinline__ void combine_rows(const CombineArgs& a, int64_t blk, int tid, char* lds) {
+  constexpr int TPR = DV / 4;                       // threads (units) per row
+  constexpr int UNITS = NT / S;                     // units per block
+  constexpr int RPB = UNITS / TPR;                  // rows per block
+  static_assert(RPB >= 1 && UNITS % TPR == 0, "block shape");
+  float* sM = (float*)lds;                          // [S][UNITS]
+  float* sL = sM + S * UNITS;                       // [S][UNITS]
+  f32x4* sO = (f32x4*)(sL + S * UNITS);             // [S][UNITS]
+
+  const int sub = tid / UNITS, u = tid % UNITS;
+  const int r_in = u / TPR, ch = u % TPR;
+  const int64_t row = blk * RPB + r_in;
+  const bool row_ok = row < (int64_t)a.B * a.Hq;
+  const int b = row_ok ? (int)(row / a.Hq) : 0;
+  // partials of this row: P_b of them, `stride` partial rows apart, from partial row `first`
+  int P_b = 0;
+  int64_t first = 0, stride = 1;
+  if (row_ok) {
+    if (a.meta) {
+      // equal-share schedule: slots first .. first + P_b - 1 hold all heads of sequence b
+      // (clamped to the slots that exist, so a stale table cannot send loads astray)
+      const int s0 = min(max(a.meta[2 * b], 0), a.slots - 1);
+      P_b = min(max(a.meta[2 * b + 1], 0), a.slots - s0);
+      first = (int64_t)s0 * a.Hq + (row - (int64_t)b * a.Hq);
+      stride = a.Hq;
+    } else {
+      int L = a.seq_lens[b];
+      L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
+      if (a.kv_cap_clamp > 0 && L > a.kv_cap_clamp) L = a.kv_cap_clamp;
+      P_b = min((L + a.chunk - 1) / a.chunk, a.max_splits);
+      first = row * a.max_splits;
+    }
+  }
+  // rows that pass 1 finished itself (single partition) are left alone; their threads
+  // still take part in the barrier below
+  const bool active = row_ok && !(a.skip_single && P_b == 1);
+
+  const float2* ml = (const float2*)a.part_ml + first;
+  const float* po = a.part_o + first * DV + ch * 4;
+  float M = -INFINITY, Ls = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (active) fold_partials<DV>(ml, po, stride, P_b, sub, S, a.c, M, Ls, acc);
+  if constexpr (S > 1) {
+    sM[sub * UNITS + u] = M;
+    sL[sub * UNITS + u] = Ls;
+    sO[sub * UNITS + u] = acc;
+    __syncthreads();
+    if (sub == 0) {
+      float G = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < S; ++t)
+        if (sL[t * UNITS + u] > 0.f) G = fmaxf(G, sM[t * UNITS + u]);
+      Ls = 0.f;
+      acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < S; ++t) {
+        if (sL[t * UNITS + u] > 0.f) {
+          const float e = exp2_fast((sM[t * UNITS + u] - G) * a.c);
+          Ls += sL[t * UNITS + u] * e;
+          acc += e * sO[t * UNITS + u];
+        }
+      }
+      M = G;
+    }
+  }
+  if (active && sub == 0) write_row_unit(a.out, a.o32, a.lse, row, DV, ch * 4, M, Ls, acc, a.scale);
 }
 
 }  // namespace da

@@ -206,18 +206,25 @@ __device__ __forceinline__ void merge_key_splits(const PartArgs& a, const WaveIn
 
 // Last-arriving-workgroup combine (fa4_splitk_combine_write, fourth paragraph: the writer
 // that completes the set combines all). After storing its partial, every workgroup of a
-// (sequence, kv-head group) publishes it device-wide (agent-scope release) and counts
-// itself in; the one that brings the count to the number of partitions acquires the
-// others' partials and writes the final bf16 rows, LSE and fp32 O of the group's heads,
-// then returns the counter to zero for the next call. The counters (one int per
-// (sequence, group)) must be zero before the first call.
+// (sequence, kv-head group) publishes it device-wide and counts itself in; the one that
+// brings the count to the number of partitions acquires the others' partials and writes the
+// final bf16 rows, LSE and fp32 O of the group's heads, then returns the counter to zero for
+// the next call. The counters (one int per (sequence, group)) must be zero before the first
+// call.
+// Publication: every wave waits until its own partial stores are complete (vmcnt(0)) before
+// the workgroup barrier, so that after the barrier all of them have reached the XCD's L2;
+// one thread then releases them at device scope (on this chip a write-back of that L2, done
+// once per workgroup rather than once per wave) and increments the counter. The workgroup
+// that completes the count saw every other workgroup's increment, each made after that
+// workgroup's release; its thread 0 acquires (an invalidation of its L2 and vector cache)
+// before the barrier after which its waves read the partials.
+// The fold uses every thread of the workgroup: NT / S (row, 4-wide slice) units at a time,
+// S threads per unit splitting the partitions (merged through LDS like the combine launch).
 template <class S>
-__device__ __forceinline__ void fused_combine(const PartArgs& a, const WaveInfo& wv, int* flag_s, int b, int count,
-                                              int first_slot) {
+__device__ __forceinline__ void fused_combine(const PartArgs& a, const WaveInfo& wv, char* smem, int* flag_s, int b,
+                                              int count, int first_slot) {
   const int tid = threadIdx.x, kg = blockIdx.y, HG = wv.HG, g = a.g;
-  // The barrier completes every wave's partial stores; one thread then releases them at
-  // device scope (on this chip a write-back of the XCD's L2, so once per workgroup rather
-  // than once per wave), counts in, and, if last, acquires the others' partials.
+  wait_vm<0>();   // this wave's partial stores are complete
   __syncthreads();
   int* cnt = a.counters + (int64_t)b * gridDim.y + kg;
   if (tid == 0) {
@@ -232,19 +239,61 @@ __device__ __forceinline__ void fused_combine(const PartArgs& a, const WaveInfo&
   const int cols = a.q_len * g, ncol = (kv_end - kg * HG) * cols;
   constexpr int DV = S::DV;
   constexpr int kUnits = DV / 4;
-  for (int u = tid; u < ncol * kUnits; u += wv.NW * 64) {
-    const int cc = u / kUnits, d0 = (u % kUnits) * 4;
-    const int kv = kg * HG + cc / cols, col = cc % cols;
-    const int h = (col / g) * a.Hq1 + kv * g + col % g;   // row within the sequence
-    const int64_t row = (int64_t)b * a.Hq + h;
-    // partial rows of this head: equal shares [slot][Hq], fixed chunks [B][Hq][max_splits]
-    const int64_t first = first_slot >= 0 ? (int64_t)first_slot * a.Hq + h : row * a.max_splits;
-    const int64_t stride = first_slot >= 0 ? a.Hq : 1;
+  const int NT = wv.NW * 64;
+  const int total = ncol * kUnits;
+  // (S threads per unit: 1 up to 16 partitions, 4 up to 64, else 16)
+  const int SUB = count <= 16 ? 1 : (count <= 64 ? 4 : 16);
+  const int UNITS = NT / SUB;
+  const int sub = tid / UNITS, ui = tid % UNITS;
+  // (the merge's LDS: the waves' tile regions, free by now)
+  float* sM = (float*)smem;                          // [SUB][UNITS]
+  float* sL = sM + SUB * UNITS;
+  f32x4* sO = (f32x4*)(sL + SUB * UNITS);
+  for (int u0 = 0; u0 < total; u0 += UNITS) {
+    const int u = u0 + ui;
+    const bool valid = u < total && sub < SUB;
+    int64_t row = 0, first = 0, stride = 1;
+    int d0 = 0;
+    if (valid) {
+      const int cc = u / kUnits;
+      d0 = (u % kUnits) * 4;
+      const int kv = kg * HG + cc / cols, col = cc % cols;
+      const int h = (col / g) * a.Hq1 + kv * g + col % g;   // row within the sequence
+      row = (int64_t)b * a.Hq + h;
+      // partial rows of this head: equal shares [slot][Hq], fixed chunks [B][Hq][max_splits]
+      first = first_slot >= 0 ? (int64_t)first_slot * a.Hq + h : row * a.max_splits;
+      stride = first_slot >= 0 ? a.Hq : 1;
+    }
     float M = -INFINITY, Ls = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    fold_partials<DV>((const float2*)a.part_ml + first, a.part_o + first * DV + d0, stride, count, 0, 1, a.c, M,
-                      Ls, acc);
-    write_row_unit(a.out, a.o32, a.lse, row, DV, d0, M, Ls, acc, a.scale);
+    if (valid)
+      fold_partials<DV>((const float2*)a.part_ml + first, a.part_o + first * DV + d0, stride, count, sub, SUB, a.c,
+                        M, Ls, acc);
+    if (SUB > 1) {
+      if (sub < SUB) {
+        sM[sub * UNITS + ui] = M;
+        sL[sub * UNITS + ui] = Ls;
+        sO[sub * UNITS + ui] = acc;
+      }
+      __syncthreads();
+      if (valid && sub == 0) {
+        float G = -INFINITY;
+        for (int t = 0; t < SUB; ++t)
+          if (sL[t * UNITS + ui] > 0.f) G = fmaxf(G, sM[t * UNITS + ui]);
+        Ls = 0.f;
+        acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < SUB; ++t) {
+          if (sL[t * UNITS + ui] > 0.f) {
+            const float e = exp2_fast((sM[t * UNITS + ui] - G) * a.c);
+            Ls += sL[t * UNITS + ui] * e;
+            acc += e * sO[t * UNITS + ui];
+          }
+        }
+        M = G;
+      }
+      __syncthreads();   // (the LDS is reused by the next units)
+    }
+    if (valid && sub == 0) write_row_unit(a.out, a.o32, a.lse, row, DV, d0, M, Ls, acc, a.scale);
   }
   if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -848,7 +897,7 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
   } else {
     merge_key_splits<HL, S>(a, wv, smem, b, p, direct, o, m_run, l_run);
   }
-  if (a.counters && !direct) fused_combine<S>(a, wv, flag_s, b, count, first_slot);
+  if (a.counters && !direct) fused_combine<S>(a, wv, smem, flag_s, b, count, first_slot);
 }
 
 // A piece of work as wave 0 of a workgroup publishes it to the other waves.

@@ -342,6 +342,18 @@ FUSED = [
                           seq_lens=[777, 2048], num_splits=3, seed=63)),
     ("empty_and_single", dict(batch=4, num_q_heads=8, num_kv_heads=1, qk_depth=128, page_size=64,
                               seq_lens=[0, 1, 2, 6500], num_splits=0, seed=64)),
+    # 64 partitions of one long sequence: the last workgroup folds 64 partials per row with
+    # 4 threads per unit (and 17..64 for the 20 splits of the second case)
+    ("long_64_splits", dict(batch=1, num_q_heads=32, num_kv_heads=4, qk_depth=128, page_size=64,
+                            seq_lens=[20000], num_splits=64, seed=70)),
+    ("splits20_two_seqs", dict(batch=2, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=32,
+                               seq_lens=[6000, 333], num_splits=20, seed=71)),
+    # 100 partitions: 16 threads per unit
+    ("splits100", dict(batch=1, num_q_heads=8, num_kv_heads=1, qk_depth=128, page_size=32,
+                       seq_lens=[6400], num_splits=100, seed=72)),
+    # one long sequence in a batch of short ones under equal shares: most workers meet it
+    ("auto_one_long_many_short", dict(batch=40, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=64,
+                                      seq_lens=[30000] + [64] * 39, num_splits=0, seed=74)),
 ]
 
 
