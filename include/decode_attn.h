@@ -56,7 +56,8 @@ typedef enum {
 
 typedef enum {
   DA_KERNEL_AUTO = 0,    /* library's choice */
-  DA_KERNEL_FMA = 1,     /* vector-ALU partition kernel (fp32 or bf16, group <= 16, depth 128) */
+  DA_KERNEL_FMA = 1,     /* vector-ALU partition kernel (fp32 or bf16, group <= 16, depth 128);
+                            the automatic choice for fp32 only */
   DA_KERNEL_MFMA = 2     /* matrix-core partition kernel (bf16 q; bf16 or fp8 caches) */
 } da_kernel;
 
@@ -127,12 +128,17 @@ typedef struct da_problem {
  */
 
 /* DA_OK if a kernel exists for this problem, else DA_EINVAL / DA_EUNSUPPORTED with a
- * message (FA4Config, supported). Supported: dtype f32 or bf16 with Dqk == Dv == 128
- * and g <= 16 (f32 runs the vector-ALU kernel); bf16 latent-shared Dqk == 576,
- * Dv == 512, Hkv == 1; and on the matrix-core kernel (bf16 q, separate K and V, q_len x
- * g <= 16, contiguous cache or pages of a power of two >= 32 keys) the depth pairs
- * Dqk/Dv 192/128 and 256/256, with the K cache in bf16 or fp8 and optionally the 64
- * rotary columns stored apart in bf16 (nope_depth 128 or 192). */
+ * message (FA4Config, supported). Supported:
+ *  - Dqk == Dv == 128, g <= 16, one query per sequence: f32 (vector-ALU kernel) or bf16
+ *    (matrix-core kernel; the vector-ALU one on request with DA_KERNEL_FMA);
+ *  - on the matrix-core kernel (bf16 q, separate K and V, q_len x g <= 16, contiguous
+ *    cache or pages of a power of two >= 32 keys) the depth pairs Dqk/Dv 128/128,
+ *    192/128 and 256/256, with the K/V cache in bf16 or fp8 and optionally the 64 rotary
+ *    columns stored apart in bf16 (nope_depth 128 or 192);
+ *  - with one kv head, on the shared-kv-head kernel (bf16, any number of q heads and
+ *    q_len): latent 576/512 with V = the first 512 K columns (v_is_k_prefix), and
+ *    256/256 with V of its own when q_len x Hq > 16; the 64 rotary columns in the K rows
+ *    or stored apart in bf16 (nope_depth 512 or 192). */
 int da_supported(const da_problem* p);
 
 /* Split selection (FA4Config, with_splitk: partitions of the K/V sequence).
@@ -182,9 +188,10 @@ int decode_attn_splitk_noalloc(const da_problem* p, const void* q, const void* k
  * a (sequence, kv-head group) stores its partial, publishes it device-wide and counts
  * itself in on an arrival counter; the last one merges all partials of its heads and
  * writes out / lse_out / o_f32_out, then resets the counter. This saves the second
- * launch. Applied by the matrix-core kernel (every depth pair and cache dtype it serves)
- * when sequences have at most 16 partitions (other problems run the two launches of
- * decode_attn_splitk; the outputs are the same either way). Rows of a sequence without
+ * launch. Applied by the GQA matrix-core kernel (every depth pair and cache dtype it
+ * serves, any number of partitions) and by the vector-ALU kernel; the shared-kv-head
+ * kernel runs the two launches of decode_attn_splitk (the outputs are the same either
+ * way). Rows of a sequence without
  * keys are written too (O = 0, LSE = -inf), by one workgroup that holds no keys. Same arguments and workspace size as decode_attn_splitk,
  * with one more rule: the workspace must be zero-filled before its first use with this
  * function (the counters live in it and every call leaves them at zero), and calls that

@@ -140,7 +140,10 @@ int check_problem(const da_problem* p, Variant* var) {
   if (p->dtype == DA_F32) {
     if (p->kernel == DA_KERNEL_MFMA) return fail(DA_EUNSUPPORTED, "the matrix-core kernel needs bf16 inputs");
     *var = kVarFma;
-  } else if (p->kernel == DA_KERNEL_FMA || (p->kernel == DA_KERNEL_AUTO && g == 1 && ql == 1)) {
+  } else if (p->kernel == DA_KERNEL_FMA) {
+    // (bf16 with one q head per kv head also runs on the matrix cores by default: 15 of the
+    // 16 MFMA columns idle still leave that kernel bound by HBM, at twice the vector-ALU
+    // kernel's rate)
     *var = kVarFma;
   } else {
     *var = kVarMfma;
@@ -390,8 +393,9 @@ void set_kv_args(const da_problem* p, const da_kv& kv, da::PartArgs* a) {
   a->Dk = p->nope_depth > 0 ? p->nope_depth : p->qk_depth;
 }
 
-// The whole step. With `fused`, the GQA matrix-core kernel combines in its last-arriving
-// workgroups (no second launch); the other kernels run the combine as a launch of its own.
+// The whole step. With `fused`, the GQA matrix-core kernel and the vector-ALU kernel
+// combine in their last-arriving workgroups (no second launch); the shared-kv-head kernel
+// runs the combine as a launch of its own.
 // The results are the same either way.
 int run_splitk(const da_problem* p, const void* q, const da_kv& kv, const int32_t* page_table, const int32_t* seq_lens,
                float scale, int32_t num_splits, void* out, float* lse_out, float* o_f32_out, void* workspace,
@@ -424,7 +428,7 @@ int run_splitk(const da_problem* p, const void* q, const da_kv& kv, const int32_
   a.o32 = o_f32_out;
   a.direct_single = 1;
   set_kv_args(p, kv, &a);
-  const bool fuse = fused && var == kVarMfma;
+  const bool fuse = fused && var != kVarShared;
   if (fuse) a.counters = (int32_t*)((char*)workspace + cnt_off);
   if ((r = launch_partition(p, var, a, s, cus))) return r;
   if (!fuse && (r = launch_combine(p, seq_lens, scale, C, P, po, pml, out, lse_out, o_f32_out, 1, s))) return r;

@@ -1,18 +1,28 @@
 // Split-K pass 1 on the vector ALU: one workgroup per (partition, kv head, sequence).
 //
-// Used for fp32 caches and for single-head groups, where q.K and P.V are not
-// dense enough to feed the matrix cores. Four waves split the partition's keys
-// in 64-key tiles (tile i goes to wave i % 4). Within a tile:
-//   scores   lane = key: x[h] = q[h] . K[key] for the g heads of the kv head
-//            (fused GQA tile, FA4Config BM_eff), q broadcast from LDS;
+// Used for fp32 caches (and for bf16 when asked for explicitly), where q.K and P.V do not
+// run on the matrix cores. Four waves split the partition's keys in 64-key tiles (tile i
+// goes to wave i % 4). Within a tile:
+//   K        coalesced 16-byte direct-to-LDS loads (consecutive lanes on consecutive
+//            16-byte chunks of a row, 1 KB per instruction, every load of the tile in
+//            flight at once) into the wave's LDS tile; the chunks of row r are rotated by r
+//            so that the reads below hit distinct banks;
+//   scores   lane = key: x[h] = q[h] . K[key] for the g heads of the kv head (fused GQA
+//            tile, FA4Config BM_eff), K from the LDS tile, q broadcast from LDS;
 //   softmax  online: running max m, per-lane running sum, O rescaled by
 //            exp2((m_old - m_new) * c) (FA4Config, num_correction_cols);
-//   P.V      lane = 16-byte depth slice of one key: O[h][d] += p[h][key] V[key][d].
-// The four waves then merge their (m, l, O) through LDS with the same
-// log-sum-exp weights as the split-K combine (fa4_lse_combine_write: two O
-// fragments merged with per-row scales), and the workgroup stores the
-// normalised partial and (m, l) of its partition (fa4_splitk_combine_write,
-// second paragraph), or the final bf16 row when the sequence has one partition.
+//   P.V      lane = 16-byte depth slice of one key, V read straight from the cache into
+//            registers (a row per LPR consecutive lanes: coalesced), issued with the K
+//            loads so that both arrive in one round trip: O[h][d] += p[h][key] V[key][d].
+// The cache rows of a tile's keys are found once per lane (key = lane) and handed to the
+// lanes that load them by readlane. q is loaded before the first tile and written to LDS
+// after that tile's loads are issued.
+// The four waves then merge their (m, l, O) through LDS with the same log-sum-exp weights
+// as the split-K combine (fa4_lse_combine_write: two O fragments merged with per-row
+// scales), and the workgroup stores the normalised partial and (m, l) of its partition
+// (fa4_splitk_combine_write, second paragraph), or the final bf16 row when the sequence has
+// one partition. With the fused combine the last workgroup of a (sequence, kv head) to store
+// its partial combines them (fa4_splitk_combine_write, fourth paragraph).
 #include "da_device.h"
 
 namespace da {
@@ -20,22 +30,25 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kWaves = 4;
+constexpr int kTile = 64;
 
 template <typename T>
 struct Vec16;
 template <>
 struct Vec16<float> {
   static constexpr int N = 4;
-  __device__ static void load(const float* p, float* out) {
-    f32x4 v = *(const f32x4*)p;
-    out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
+  __device__ static void unpack(u32x4 v, float* out) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t u = v[i];   // (a vector element is not addressable: copy it out first)
+      out[i] = __builtin_bit_cast(float, u);
+    }
   }
 };
 template <>
 struct Vec16<uint16_t> {
   static constexpr int N = 8;
-  __device__ static void load(const uint16_t* p, float* out) {
-    u32x4 v = *(const u32x4*)p;
+  __device__ static void unpack(u32x4 v, float* out) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       out[2 * i] = bf16lo(v[i]);
@@ -44,48 +57,72 @@ struct Vec16<uint16_t> {
   }
 };
 
+// LDS sizes of one workgroup
+template <typename T, int GMAX>
+struct FmaLds {
+  static constexpr int kRowBytes = kD * (int)sizeof(T);
+  static constexpr int kPBytes = kWaves * kTile * GMAX * 4;           // p during the key loop
+  static constexpr int kCBytes = kWaves * GMAX * (kD + 2) * 4;        // (m, l, O) for the merge
+  static constexpr int kTileBytes = kWaves * kTile * kRowBytes;       // the K tiles
+  static constexpr int kKtBytes = kTileBytes > kCBytes ? kTileBytes : kCBytes;
+  static constexpr int kBytes = kKtBytes + kPBytes + GMAX * kD * 4 + 16;
+};
+
 template <typename T, int GMAX, int PM>
 __global__ __launch_bounds__(kWaves * 64) void partition_fma_kernel(PartArgs a) {
-  constexpr int VEC = Vec16<T>::N;      // elements per 16-byte load
-  constexpr int LPR = kD / VEC;         // lanes covering one row in the P.V phase
+  typedef FmaLds<T, GMAX> Lds;
+  static_assert(Lds::kBytes <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(16))) char kt_s[Lds::kKtBytes];   // K tiles, then the merge arrays
+  __shared__ __attribute__((aligned(16))) float p_s[kWaves][kTile][GMAX];
+  __shared__ __attribute__((aligned(16))) float q_s[GMAX][kD];
+  __shared__ int last_s;                                                // fused combine: 1 = last
+  constexpr int VEC = Vec16<T>::N;      // elements per 16-byte chunk
+  constexpr int RB = Lds::kRowBytes;   // bytes of one K / V row of a kv head
+  constexpr int CPR = RB / 16;          // chunks per row
+  constexpr int RPI = 64 / CPR;         // rows per 1 KB load instruction
+  constexpr int NLD = kTile / RPI;      // load instructions per K tile
+  constexpr int LPR = CPR;              // lanes covering one V row in the P.V phase
   constexpr int TPI = 64 / LPR;         // keys per P.V load instruction
-  constexpr int kTile = 64;
+  constexpr int NV = kTile / TPI;       // P.V load instructions per tile
 
   const int p = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int L = attended_len(a, b, PM == kContiguous);
   const int start = p * a.chunk;
-  if (start >= L) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = a.g;
+  constexpr int kUnits = kD / 4;   // 4-wide depth slices of an output row
+  if (start >= L) {
+    // fused combine: the rows of a sequence without keys (O = 0, LSE = -inf) come from
+    // its first workgroup
+    if (a.counters && p == 0 && L == 0)
+      for (int u = tid; u < g * kUnits; u += kWaves * 64)
+        write_row_unit(a.out, a.o32, a.lse, (int64_t)b * a.Hq + kvh * g + u / kUnits, kD, (u % kUnits) * 4,
+                       -INFINITY, 0.f, f32x4{0.f, 0.f, 0.f, 0.f}, a.scale);
+    return;
+  }
   const int end = min(start + a.chunk, L);
   const int P_b = min((L + a.chunk - 1) / a.chunk, a.max_splits);
   const bool direct = a.direct_single && P_b == 1;
+  char* kt = kt_s + w * kTile * RB;   // this wave's K tile
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int g = a.g;
-
-  __shared__ float q_s[GMAX][kD];
-  __shared__ int64_t rows_s[kWaves][kTile];
-  // p_s during the key loop, then the per-wave (m, l, O) for the merge.
-  constexpr int kPBytes = kWaves * kTile * GMAX * 4;
-  constexpr int kCBytes = kWaves * GMAX * (kD + 2) * 4;
-  __shared__ __attribute__((aligned(16))) char scratch[kPBytes > kCBytes ? kPBytes : kCBytes];
-  float(*p_s)[kTile][GMAX] = (float(*)[kTile][GMAX])scratch;
-
+  // q of the g heads: loads issued now, written to LDS once the first tile's loads are out
+  constexpr int kQPer = (GMAX * kD + kWaves * 64 - 1) / (kWaves * 64);
   const T* q = (const T*)a.q + ((int64_t)b * a.Hq + (int64_t)kvh * g) * kD;
-  for (int i = tid; i < GMAX * kD; i += kWaves * 64) {
-    const int h = i / kD, d = i % kD;
-    float val = 0.f;
-    if (h < g) {
-      if constexpr (sizeof(T) == 4) val = ((const float*)q)[h * kD + d];
-      else val = bf16lo((uint32_t)((const uint16_t*)q)[h * kD + d]);
+  float qv[kQPer];
+#pragma unroll
+  for (int j = 0; j < kQPer; ++j) {
+    const int i = tid + j * kWaves * 64, h = i / kD;
+    qv[j] = 0.f;
+    if (i < GMAX * kD && h < g) {
+      if constexpr (sizeof(T) == 4) qv[j] = ((const float*)q)[i];
+      else qv[j] = bf16lo((uint32_t)((const uint16_t*)q)[i]);
     }
-    q_s[h][d] = val;
   }
-  __syncthreads();
 
-  const T* kc = (const T*)a.k;
-  const T* vc = (const T*)a.v;
-  const int64_t kstride = (int64_t)a.Hkv * a.Dqk;
-  const int64_t vstride = (int64_t)a.Hkv * a.v_row_len;
+  const char* kc = (const char*)a.k + (int64_t)kvh * RB;
+  const char* vc = (const char*)a.v + (int64_t)kvh * a.v_row_len * (int64_t)sizeof(T);
+  const int64_t kstride = (int64_t)a.Hkv * RB;                                  // bytes between K rows
+  const int64_t vstride = (int64_t)a.Hkv * a.v_row_len * (int64_t)sizeof(T);   // bytes between V rows
 
   float m[GMAX], lsum[GMAX], o[GMAX][VEC];
 #pragma unroll
@@ -97,24 +134,68 @@ __global__ __launch_bounds__(kWaves * 64) void partition_fma_kernel(PartArgs a) 
   }
   const int col0 = (lane % LPR) * VEC;
   const int tsub = lane / LPR;
-
   const int n_tiles = (end - start + kTile - 1) / kTile;
-  for (int it = w; it < n_tiles; it += kWaves) {
-    const int t0 = start + it * kTile;
-    const int t = t0 + lane;
-    const bool valid = t < end;
-    const int64_t row = key_row<PM>(a, b, valid ? t : end - 1);
-    rows_s[w][lane] = row;
 
-    // scores, lane = key
+  // Loads of tile `it`: every lane finds the cache row of key t0 + lane, then the rows the
+  // lane loads are taken from their owners by readlane (no LDS table between the loads).
+  //   K: load i, lane l fills tile row rr = RPI i + l / CPR at chunk slot l % CPR with that
+  //      row's chunk (slot - rr) mod CPR (rotation by the row), 1 KB per instruction;
+  //   V: load i, lane l reads the 16-byte slice col0 of key tsub + i TPI into vr[i].
+  u32x4 vr[NV];
+  auto issue = [&](int it) {
+    const int t = start + it * kTile + lane;
+    const int64_t row = key_row<PM>(a, b, t < end ? t : end - 1);   // keys past the end repeat the last
+    const int64_t ko = row * kstride, vo = row * vstride;
+    auto from = [&](int64_t v, int src) {
+      return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), src) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src));
+    };
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      int64_t off = from(ko, RPI * i);
+#pragma unroll
+      for (int r = 1; r < RPI; ++r) {
+        const int64_t alt = from(ko, RPI * i + r);
+        off = lane / CPR == r ? alt : off;
+      }
+      const int rr = RPI * i + lane / CPR;
+      const int c = ((lane % CPR) - rr) & (CPR - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(kc + off + 16 * c), (DA_LDS void*)(kt + i * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      int64_t off = from(vo, i * TPI);
+#pragma unroll
+      for (int r = 1; r < TPI; ++r) {
+        const int64_t alt = from(vo, i * TPI + r);
+        off = tsub == r ? alt : off;
+      }
+      vr[i] = *(const u32x4*)(vc + off + col0 * (int)sizeof(T));
+    }
+  };
+
+  if (w < n_tiles) issue(w);
+#pragma unroll
+  for (int j = 0; j < kQPer; ++j) {
+    const int i = tid + j * kWaves * 64;
+    if (i < GMAX * kD) q_s[i / kD][i % kD] = qv[j];
+  }
+  __syncthreads();   // (waits for the first tile's loads too: q, K and V arrive in one round trip)
+
+  for (int it = w; it < n_tiles; it += kWaves) {
+    if (it != w) issue(it);
+    const bool valid = start + it * kTile + lane < end;
+    wait_vm<NV>();   // the K tile is in LDS (its loads were issued first)
+
+    // scores, lane = key: chunk c of row `lane` sits at slot (c + lane) mod CPR
     float x[GMAX];
 #pragma unroll
     for (int h = 0; h < GMAX; ++h) x[h] = 0.f;
-    const T* krow = kc + row * kstride + (int64_t)kvh * a.Dqk;
-#pragma unroll 4
-    for (int c = 0; c < LPR; ++c) {
+    const char* myrow = kt + lane * RB;
+#pragma unroll 8
+    for (int c = 0; c < CPR; ++c) {
       float kv[VEC];
-      Vec16<T>::load(krow + c * VEC, kv);
+      Vec16<T>::unpack(*(const u32x4*)(myrow + 16 * ((c + lane) & (CPR - 1))), kv);
 #pragma unroll
       for (int h = 0; h < GMAX; ++h)
 #pragma unroll
@@ -138,12 +219,13 @@ __global__ __launch_bounds__(kWaves * 64) void partition_fma_kernel(PartArgs a) 
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // P.V, lane = (key subset, 16-byte depth slice)
-#pragma unroll 4
-    for (int j = tsub; j < kTile; j += TPI) {
-      const int64_t r = rows_s[w][j];
+    // P.V: O[h][d] += p[h][key] V[key][d]
+    wait_vm<0>();
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int j = tsub + i * TPI;
       float vv[VEC];
-      Vec16<T>::load(vc + r * vstride + (int64_t)kvh * a.v_row_len + col0, vv);
+      Vec16<T>::unpack(vr[i], vv);
 #pragma unroll
       for (int h = 0; h < GMAX; ++h) {
         const float pj = p_s[w][j][h];
@@ -165,8 +247,8 @@ __global__ __launch_bounds__(kWaves * 64) void partition_fma_kernel(PartArgs a) 
 #pragma unroll
       for (int s = LPR; s < 64; s <<= 1) o[h][e] += __shfl_xor(o[h][e], s);
   }
-  __syncthreads();
-  float* cm = (float*)scratch;                       // [kWaves][GMAX] max
+  __syncthreads();   // (the K tiles are free: the merge arrays take their place)
+  float* cm = (float*)kt_s;                         // [kWaves][GMAX] max
   float* cl = cm + kWaves * GMAX;                    // [kWaves][GMAX] sum
   float* co = cl + kWaves * GMAX;                    // [kWaves][GMAX][kD] O
   if (lane == 0) {
@@ -185,7 +267,6 @@ __global__ __launch_bounds__(kWaves * 64) void partition_fma_kernel(PartArgs a) 
   __syncthreads();
 
   // merge the waves (same LSE weights as the split-K combine) and store
-  constexpr int kUnits = kD / 4;
   for (int u = tid; u < g * kUnits; u += kWaves * 64) {
     const int h = u / kUnits, d0 = (u % kUnits) * 4;
     float M = -INFINITY;
@@ -203,6 +284,32 @@ __global__ __launch_bounds__(kWaves * 64) void partition_fma_kernel(PartArgs a) 
     const float inv = 1.f / Ls;
     store_unit(a, b, kvh * g + h, p, direct, d0, acc * inv, M, Ls, d0 == 0);
   }
+
+  if (!a.counters || direct) return;
+  // Fused combine: publish the partial (every wave's stores complete, then one device-scope
+  // release), count in on the (sequence, kv head) counter; the workgroup that completes the
+  // count acquires the others' partials and writes the g final rows.
+  wait_vm<0>();
+  __syncthreads();
+  int* cnt = a.counters + (int64_t)b * a.Hkv + kvh;
+  if (tid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const int last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == P_b - 1;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    last_s = last ? 1 : 0;
+  }
+  __syncthreads();
+  if (!__builtin_amdgcn_readfirstlane(last_s)) return;
+  for (int u = tid; u < g * kUnits; u += kWaves * 64) {
+    const int h = u / kUnits, d0 = (u % kUnits) * 4;
+    const int64_t row = (int64_t)b * a.Hq + kvh * g + h;
+    float M = -INFINITY, Ls = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    fold_partials<kD>((const float2*)a.part_ml + row * a.max_splits, a.part_o + row * a.max_splits * kD + d0, 1,
+                      P_b, 0, 1, a.c, M, Ls, acc);
+    write_row_unit(a.out, a.o32, a.lse, row, kD, d0, M, Ls, acc, a.scale);
+  }
+  if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <typename T, int GMAX>

@@ -258,6 +258,11 @@ WORKLOADS = {
     # (stored apart, bf16), V 256 of its own; batch 16, L 8192, page 64, 8 splits
     "glm_mqa": dict(seed=7, batch=16, num_q_heads=128, num_kv_heads=1, qk_depth=256, ov_depth=256,
                     dtype=torch.bfloat16, page_size=64, seq_lens=[8192] * 16, num_splits=8, rope_apart=64),
+    # one q head per kv head (multi-head attention, group 1): batch 32, 32 heads, head dim
+    # 128, bf16, page 64, L_b ~ U[512, 8192], automatic splits
+    "paged_mha": dict(seed=8, batch=32, num_q_heads=32, num_kv_heads=32, qk_depth=128,
+                      dtype=torch.bfloat16, page_size=64, len_range=(512, 8192), num_splits=0,
+                      page_table_width=128),
     # the same with the nope columns and V as fp8 (E4M3) with per-token scales; the rotary
     # columns stay bf16
     "paged_glm_fp8": dict(seed=6, batch=32, num_q_heads=16, num_kv_heads=16, qk_depth=256, ov_depth=256,

@@ -45,7 +45,9 @@ CASES = [
     ("fp32_g16_paged16", dict(batch=2, num_q_heads=16, num_kv_heads=1, qk_depth=128, dtype=torch.float32,
                               page_size=16, seq_lens=[517, 1201], num_splits=0, seed=22), "auto"),
     ("bf16_g1_fma", dict(batch=3, num_q_heads=4, num_kv_heads=4, qk_depth=128, seq_lens=[2049, 1, 640],
-                         num_splits=5, seed=23), "auto"),
+                         num_splits=5, seed=23), "fma"),
+    ("bf16_g1_auto", dict(batch=3, num_q_heads=4, num_kv_heads=4, qk_depth=128, page_size=64,
+                          seq_lens=[2049, 1, 640], num_splits=0, seed=23), "auto"),
     ("bf16_g1_mfma", dict(batch=3, num_q_heads=4, num_kv_heads=4, qk_depth=128, seq_lens=[2049, 1, 640],
                           num_splits=5, seed=23), "mfma"),
     ("bf16_g4_contig", dict(batch=2, num_q_heads=8, num_kv_heads=2, qk_depth=128, seq_lens=[4096, 1000],
@@ -354,6 +356,17 @@ FUSED = [
     # one long sequence in a batch of short ones under equal shares: most workers meet it
     ("auto_one_long_many_short", dict(batch=40, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=64,
                                       seq_lens=[30000] + [64] * 39, num_splits=0, seed=74)),
+    # the vector-ALU kernel: fp32 (its automatic choice) and bf16 on request
+    ("fp32_tiny", dict(batch=1, num_q_heads=1, num_kv_heads=1, qk_depth=128, dtype=torch.float32,
+                       seq_lens=[1024], num_splits=4, seed=75)),
+    ("fp32_g4_ragged_empty", dict(batch=4, num_q_heads=8, num_kv_heads=2, qk_depth=128, dtype=torch.float32,
+                                  seq_lens=[1000, 0, 77, 300], num_splits=3, seed=76)),
+    ("fp32_g16_paged16_auto", dict(batch=2, num_q_heads=16, num_kv_heads=1, qk_depth=128, dtype=torch.float32,
+                                   page_size=16, seq_lens=[517, 1201], num_splits=0, seed=77)),
+    ("fp32_g2_40_splits", dict(batch=2, num_q_heads=4, num_kv_heads=2, qk_depth=128, dtype=torch.float32,
+                               page_size=64, seq_lens=[5000, 130], num_splits=40, seed=78)),
+    ("bf16_fma_g8_paged64", dict(batch=3, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=64,
+                                 seq_lens=[3000, 0, 65], num_splits=6, seed=79, kernel="fma")),
 ]
 
 
@@ -362,13 +375,16 @@ def test_fused_combine_matches_oracle_on_repeated_calls(name, kw):
     # the last-arriving workgroup combines; its counters must return to zero, so three
     # calls on one workspace all give the oracle's result
     print(f"[parity] fused {name}", flush=True)
+    kw = dict(kw)
+    kernel = kw.pop("kernel", "auto")
     case = make_case(name, **kw)
     dc = to_device(case)
-    prob = api.make_problem(dc.q, dc.k_cache, dc.v_cache, dc.page_table, page_size=case.page_size)
+    prob = api.make_problem(dc.q, dc.k_cache, dc.v_cache, dc.page_table, page_size=case.page_size, kernel=kernel)
     ws = torch.zeros(api.workspace_bytes(prob, case.num_splits), dtype=torch.uint8, device="cuda")
     O, LSE = oracle_for(case)
     for rep in range(3):
-        out, lse, o32 = api.case_call(dc, return_lse=True, return_o32=True, fused=True, workspace=ws)
+        out, lse, o32 = api.case_call(dc, return_lse=True, return_o32=True, fused=True, workspace=ws,
+                                      kernel=kernel)
         torch.cuda.synchronize()
         assert_parity(out, lse, o32, O, LSE, what=f"fused {name} call {rep}")
 
@@ -494,7 +510,7 @@ def test_combine_only_on_oracle_partials(Dv, P):
 # with the oracle: the method is an exact re-association of the definition, so no row may
 # differ beyond the stated tolerances (the oracle runs the largest of these in seconds).
 FULL_WORKLOADS = ["tiny", "gqa", "paged_gqa", "long", "latent", "paged_gqa_q2", "paged_gqa_fp8", "paged_glm",
-                  "paged_glm_fp8", "latent_rope_apart", "glm_mqa"]
+                  "paged_glm_fp8", "latent_rope_apart", "glm_mqa", "paged_mha"]
 
 
 @pytest.mark.parametrize("name", FULL_WORKLOADS)
