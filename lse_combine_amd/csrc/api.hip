@@ -197,7 +197,9 @@ void share_shape(const da_problem* p, int cus, int* HG, int* KS, int* W) {
 
 // Workgroups of the partition kernel that fit on one compute unit at once (the matrix-core
 // kernels take most of the LDS and two waves per SIMD).
-int wgs_per_cu(Variant v) { return v == kVarFma ? 2 : 1; }
+// workgroups resident per CU (LDS-bound): the vector-ALU kernel holds four in bf16 (32-key
+// tiles), one in fp32 (64-key tiles); the matrix-core kernels one
+int wgs_per_cu(const da_problem* p, Variant v) { return v == kVarFma && p->dtype == DA_BF16 ? 4 : 1; }
 
 int choose(const da_problem* p, Variant var, int32_t num_splits, int cus, int32_t* chunk_out, int32_t* splits_out) {
   if (num_splits < 0) return fail(DA_EINVAL, "num_splits must be >= 0 (0 = automatic)");
@@ -219,7 +221,7 @@ int choose(const da_problem* p, Variant var, int32_t num_splits, int cus, int32_
     // Automatic: the host does not see seq_lens (no device sync), so it plans for an
     // average length of max_seq_len / 2 and aims at about four rounds of workgroups
     // over the whole chip; chunks stay within [256, 8192] keys.
-    const int slots = cus * wgs_per_cu(var);
+    const int slots = cus * wgs_per_cu(p, var);
     // workgroups per (sequence, partition): kv heads, or 64-column blocks on the
     // shared-kv-head kernel
     const int64_t per_part = var == kVarShared ? ceil_div(rows_per_seq(p), 64) : p->num_kv_heads;

@@ -1,4 +1,4 @@
-// Split-K pass 1 on the vector ALU: one workgroup per (partition, kv head, sequence).
+// Split-K pass 1 on the vector ALU: one workgroup per (kv head, partition, sequence).
 //
 // Used for fp32 caches (and for bf16 when asked for explicitly), where q.K and P.V do not
 // run on the matrix cores. Four waves split the partition's keys in 64-key tiles (tile i
@@ -14,9 +14,10 @@
 //   P.V      lane = 16-byte depth slice of one key, V read straight from the cache into
 //            registers (a row per LPR consecutive lanes: coalesced), issued with the K
 //            loads so that both arrive in one round trip: O[h][d] += p[h][key] V[key][d].
-// The cache rows of a tile's keys are found once per lane (key = lane) and handed to the
-// lanes that load them by readlane. q is loaded before the first tile and written to LDS
-// after that tile's loads are issued.
+// A tile's cache rows come from one page-table read per tile when tiles cannot straddle a
+// page, else from one read per lane (key = lane) handed to the lanes that load them by
+// readlane; either way the read is made one tile ahead. q is loaded before the first tile
+// and written to LDS after that tile's loads are issued.
 // The four waves then merge their (m, l, O) through LDS with the same log-sum-exp weights
 // as the split-K combine (fa4_lse_combine_write: two O fragments merged with per-row
 // scales), and the workgroup stores the normalised partial and (m, l) of its partition
@@ -30,7 +31,7 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kWaves = 4;
-constexpr int kTile = 64;
+constexpr int kTile = 64;   // keys per tile (one per lane in the scores)
 
 template <typename T>
 struct Vec16;
@@ -57,19 +58,22 @@ struct Vec16<uint16_t> {
   }
 };
 
-// LDS sizes of one workgroup
+// LDS sizes of one workgroup (64-key tiles). fp32 holds one workgroup per CU, bf16 two.
 template <typename T, int GMAX>
 struct FmaLds {
+  static constexpr int kMinWaves = sizeof(T) == 2 && GMAX <= 4 ? 2 : 1;   // waves per SIMD aimed at
   static constexpr int kRowBytes = kD * (int)sizeof(T);
-  static constexpr int kPBytes = kWaves * kTile * GMAX * 4;           // p during the key loop
+  static constexpr int kPBytes = kWaves * kTile * GMAX * 4;        // p during the key loop
   static constexpr int kCBytes = kWaves * GMAX * (kD + 2) * 4;        // (m, l, O) for the merge
-  static constexpr int kTileBytes = kWaves * kTile * kRowBytes;       // the K tiles
+  static constexpr int kTileBytes = kWaves * kTile * kRowBytes;   // one buffer of K tiles
   static constexpr int kKtBytes = kTileBytes > kCBytes ? kTileBytes : kCBytes;
   static constexpr int kBytes = kKtBytes + kPBytes + GMAX * kD * 4 + 16;
 };
 
-template <typename T, int GMAX, int PM>
-__global__ __launch_bounds__(kWaves * 64) void partition_fma_kernel(PartArgs a) {
+// AFF: every tile lies within one page (contiguous cache, or pages and chunks in multiples
+// of the tile), so its rows are consecutive.
+template <typename T, int GMAX, int PM, bool AFF>
+__global__ __launch_bounds__(kWaves * 64, (FmaLds<T, GMAX>::kMinWaves)) void partition_fma_kernel(PartArgs a) {
   typedef FmaLds<T, GMAX> Lds;
   static_assert(Lds::kBytes <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(16))) char kt_s[Lds::kKtBytes];   // K tiles, then the merge arrays
@@ -85,10 +89,13 @@ __global__ __launch_bounds__(kWaves * 64) void partition_fma_kernel(PartArgs a) 
   constexpr int TPI = 64 / LPR;         // keys per P.V load instruction
   constexpr int NV = kTile / TPI;       // P.V load instructions per tile
 
-  const int p = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  // kv heads fastest in the grid: the workgroups of all heads of one key range run together,
+  // so the rows of neighbouring heads (adjacent in the cache) are read at about the same time
+  const int kvh = blockIdx.x % a.Hkv, p = blockIdx.x / a.Hkv, b = blockIdx.y;
   const int L = attended_len(a, b, PM == kContiguous);
   const int start = p * a.chunk;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // (uniform: tile indices and page lookups stay scalar)
   const int g = a.g;
   constexpr int kUnits = kD / 4;   // 4-wide depth slices of an output row
   if (start >= L) {
@@ -103,7 +110,6 @@ __global__ __launch_bounds__(kWaves * 64) void partition_fma_kernel(PartArgs a) 
   const int end = min(start + a.chunk, L);
   const int P_b = min((L + a.chunk - 1) / a.chunk, a.max_splits);
   const bool direct = a.direct_single && P_b == 1;
-  char* kt = kt_s + w * kTile * RB;   // this wave's K tile
 
   // q of the g heads: loads issued now, written to LDS once the first tile's loads are out
   constexpr int kQPer = (GMAX * kD + kWaves * 64 - 1) / (kWaves * 64);
@@ -136,15 +142,56 @@ __global__ __launch_bounds__(kWaves * 64) void partition_fma_kernel(PartArgs a) 
   const int tsub = lane / LPR;
   const int n_tiles = (end - start + kTile - 1) / kTile;
 
-  // Loads of tile `it`: every lane finds the cache row of key t0 + lane, then the rows the
-  // lane loads are taken from their owners by readlane (no LDS table between the loads).
+  // Loads of tile `it` into K buffer `buf` and the registers vr.
   //   K: load i, lane l fills tile row rr = RPI i + l / CPR at chunk slot l % CPR with that
   //      row's chunk (slot - rr) mod CPR (rotation by the row), 1 KB per instruction;
   //   V: load i, lane l reads the 16-byte slice col0 of key tsub + i TPI into vr[i].
-  u32x4 vr[NV];
-  auto issue = [&](int it) {
-    const int t = start + it * kTile + lane;
-    const int64_t row = key_row<PM>(a, b, t < end ? t : end - 1);   // keys past the end repeat the last
+  // Keys past the end repeat the last key (masked in the softmax). With AFF the tile's rows
+  // are consecutive from the row of its first key; otherwise every lane finds the row of key
+  // t0 + lane and the rows a lane loads are taken from their owners by readlane. The
+  // page-table entries of a tile are read one tile ahead of its loads (page_entry), and
+  // turned into rows only when the tile is issued (row_of), so that the read is not waited
+  // for in front of the loads.
+  auto key_of = [&](int it) {
+    const int t0 = start + it * kTile;
+    return AFF ? t0 : min(t0 + lane, end - 1);
+  };
+  auto page_entry = [&](int t) -> int {
+    if constexpr (PM == kContiguous) {
+      return 0;
+    } else if constexpr (AFF) {
+      // one entry per tile, at a wave-uniform address: read through the scalar cache (the
+      // table is not written during the kernel), so that it is not waited for with the
+      // vector loads
+      typedef const __attribute__((address_space(4))) int32_t* ConstPtr;
+      return ((ConstPtr)a.page_table)[(int64_t)b * a.pt_stride + t / a.page_size];
+    } else {
+      return a.page_table[(int64_t)b * a.pt_stride + t / a.page_size];
+    }
+  };
+  auto row_of = [&](int t, int page) -> int64_t {
+    if constexpr (PM == kContiguous) return (int64_t)b * a.kv_capacity + t;
+    page = page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
+    return (int64_t)page * a.page_size + (t - (t / a.page_size) * a.page_size);
+  };
+  auto issue = [&](int it, u32x4(&vr)[NV], int64_t row) {
+    const int t0 = start + it * kTile;
+    const int last = end - 1 - t0;
+    char* ktb = kt_s + w * kTile * RB;
+    if constexpr (AFF) {
+      const int64_t r0 = row;
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const int rr = RPI * i + lane / CPR;
+        const int c = ((lane % CPR) - rr) & (CPR - 1);
+        const char* src = kc + (r0 + min(rr, last)) * kstride + 16 * c;
+        __builtin_amdgcn_global_load_lds((const void*)src, (DA_LDS void*)(ktb + i * 1024), 16, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        vr[i] = *(const u32x4*)(vc + (r0 + min(tsub + i * TPI, last)) * vstride + col0 * (int)sizeof(T));
+      return;
+    }
     const int64_t ko = row * kstride, vo = row * vstride;
     auto from = [&](int64_t v, int src) {
       return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), src) << 32) |
@@ -160,7 +207,7 @@ __global__ __launch_bounds__(kWaves * 64) void partition_fma_kernel(PartArgs a) 
       }
       const int rr = RPI * i + lane / CPR;
       const int c = ((lane % CPR) - rr) & (CPR - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(kc + off + 16 * c), (DA_LDS void*)(kt + i * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(kc + off + 16 * c), (DA_LDS void*)(ktb + i * 1024), 16, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -174,24 +221,15 @@ __global__ __launch_bounds__(kWaves * 64) void partition_fma_kernel(PartArgs a) 
     }
   };
 
-  if (w < n_tiles) issue(w);
-#pragma unroll
-  for (int j = 0; j < kQPer; ++j) {
-    const int i = tid + j * kWaves * 64;
-    if (i < GMAX * kD) q_s[i / kD][i % kD] = qv[j];
-  }
-  __syncthreads();   // (waits for the first tile's loads too: q, K and V arrive in one round trip)
-
-  for (int it = w; it < n_tiles; it += kWaves) {
-    if (it != w) issue(it);
+  // One tile's math, its K tile in LDS (the caller waited for it); the V registers are
+  // waited for by the compiler at their first use.
+  auto compute = [&](int it, const u32x4(&vr)[NV]) {
     const bool valid = start + it * kTile + lane < end;
-    wait_vm<NV>();   // the K tile is in LDS (its loads were issued first)
-
-    // scores, lane = key: chunk c of row `lane` sits at slot (c + lane) mod CPR
+    // scores, lane = key: chunk c of row r sits at slot (c + r) mod CPR
     float x[GMAX];
 #pragma unroll
     for (int h = 0; h < GMAX; ++h) x[h] = 0.f;
-    const char* myrow = kt + lane * RB;
+    const char* myrow = kt_s + (w * kTile + lane) * RB;
 #pragma unroll 8
     for (int c = 0; c < CPR; ++c) {
       float kv[VEC];
@@ -220,7 +258,6 @@ __global__ __launch_bounds__(kWaves * 64) void partition_fma_kernel(PartArgs a) 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // P.V: O[h][d] += p[h][key] V[key][d]
-    wait_vm<0>();
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int j = tsub + i * TPI;
@@ -236,6 +273,30 @@ __global__ __launch_bounds__(kWaves * 64) void partition_fma_kernel(PartArgs a) 
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  u32x4 va[NV];
+  int page_next = 0;
+  if (w < n_tiles) {
+    const int t = key_of(w), e = page_entry(t);
+    if (w + kWaves < n_tiles) page_next = page_entry(key_of(w + kWaves));
+    issue(w, va, row_of(t, e));
+  }
+#pragma unroll
+  for (int j = 0; j < kQPer; ++j) {
+    const int i = tid + j * kWaves * 64;
+    if (i < GMAX * kD) q_s[i / kD][i % kD] = qv[j];
+  }
+  __syncthreads();   // (waits for the first tile's loads too: q, K and V arrive in one round trip)
+
+  for (int it = w; it < n_tiles; it += kWaves) {
+    if (it != w) {
+      const int e = page_next;
+      if (it + kWaves < n_tiles) page_next = page_entry(key_of(it + kWaves));
+      issue(it, va, row_of(key_of(it), e));
+    }
+    wait_vm<NV>();   // the K tile is in LDS (its loads were issued before the V loads)
+    compute(it, va);
   }
 
   // finish this wave's (m, l, O)
@@ -314,15 +375,14 @@ __global__ __launch_bounds__(kWaves * 64) void partition_fma_kernel(PartArgs a) 
 
 template <typename T, int GMAX>
 hipError_t launch_t(const PartArgs& a, int pm, hipStream_t s) {
-  dim3 grid(a.max_splits, a.Hkv, a.B), block(kWaves * 64);
-  switch (pm) {
-    case kContiguous:
-      hipLaunchKernelGGL((partition_fma_kernel<T, GMAX, kContiguous>), grid, block, 0, s, a);
-      break;
-    default:
-      hipLaunchKernelGGL((partition_fma_kernel<T, GMAX, kPagedGeneral>), grid, block, 0, s, a);
-      break;
-  }
+  if ((int64_t)a.max_splits * a.Hkv > INT32_MAX || a.B > 65535) return hipErrorInvalidConfiguration;
+  dim3 grid((unsigned)(a.max_splits * a.Hkv), a.B), block(kWaves * 64);
+  if (pm == kContiguous)
+    hipLaunchKernelGGL((partition_fma_kernel<T, GMAX, kContiguous, true>), grid, block, 0, s, a);
+  else if (a.page_size % kTile == 0 && a.chunk % kTile == 0)
+    hipLaunchKernelGGL((partition_fma_kernel<T, GMAX, kPagedGeneral, true>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((partition_fma_kernel<T, GMAX, kPagedGeneral, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
