@@ -195,11 +195,9 @@ void share_shape(const da_problem* p, int cus, int* HG, int* KS, int* W) {
   *W = (int)(w < 1 ? 1 : w);
 }
 
-// Workgroups of the partition kernel that fit on one compute unit at once (the matrix-core
-// kernels take most of the LDS and two waves per SIMD).
-// workgroups resident per CU (LDS-bound): the vector-ALU kernel holds four in bf16 (32-key
-// tiles), one in fp32 (64-key tiles); the matrix-core kernels one
-int wgs_per_cu(const da_problem* p, Variant v) { return v == kVarFma && p->dtype == DA_BF16 ? 4 : 1; }
+// Workgroups of the partition kernel resident per compute unit (LDS-bound): the vector-ALU
+// kernel holds two in bf16, one in fp32; the matrix-core kernels one.
+int wgs_per_cu(const da_problem* p, Variant v) { return v == kVarFma && p->dtype == DA_BF16 ? 2 : 1; }
 
 int choose(const da_problem* p, Variant var, int32_t num_splits, int cus, int32_t* chunk_out, int32_t* splits_out) {
   if (num_splits < 0) return fail(DA_EINVAL, "num_splits must be >= 0 (0 = automatic)");

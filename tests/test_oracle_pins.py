@@ -583,3 +583,30 @@ def test_one_kv_head_own_v_depth_brute_force(paged, q_len):
     np.testing.assert_allclose(O, Ob, atol=1e-13)
     np.testing.assert_allclose(LSE, Lb, rtol=1e-13)
     assert O.shape[-1] == 9
+
+
+@pytest.mark.parametrize("paged", [0, 1])
+def test_fp8_latent_v_is_scaled_k_prefix_brute_force_with_torch_decode(paged):
+    # MLA-style latent in miniature over an fp8 cache: K row = [nope 8 as E4M3 codes with a
+    # per-token scale | rotary 4 in bf16, stored apart], V = the first 6 nope columns, so V
+    # is read as code x the token's K scale (no V scale of its own)
+    from lse_combine_amd.inputs import make_case
+    c = make_case("lat8", batch=3, num_q_heads=6, num_kv_heads=1, qk_depth=12, ov_depth=6,
+                  page_size=4 if paged else 0, seq_lens=[9, 1, 14], seed=230 + paged, kv_fp8=True,
+                  dtype=torch.float32, rope_apart=4, v_is_k_prefix=True)
+    assert c.v_cache is None and c.v_scale is None and c.k_cache.dtype == torch.uint8
+    pt = None if c.page_table is None else c.page_table.numpy()
+    O, LSE = decode_attention_fp64(c.q.numpy(), c.k_cache.numpy(), None, c.seq_lens.numpy(), c.scale,
+                                   page_table=pt, page_size=c.page_size, v_is_k_prefix=True, ov_depth=6,
+                                   k_scale=c.k_scale.numpy(), k_rope=c.k_rope.float().numpy())
+    kn = c.k_cache.view(torch.float8_e4m3fn).double() * c.k_scale.double().permute(0, 2, 1)[..., None]
+    kd = torch.cat([kn, c.k_rope.double()], dim=-1)
+    vd = kn[..., :6].contiguous()
+    Ob, Lb = brute(c.q.double().numpy(), kd.numpy(), vd.numpy(), c.seq_lens.numpy(), c.scale, pt, c.page_size)
+    np.testing.assert_allclose(O, Ob, atol=1e-13)
+    np.testing.assert_allclose(LSE, Lb, rtol=1e-13)
+    # V from the unscaled codes (the scale dropped on the V side) gives another result
+    Ow, _ = brute(c.q.double().numpy(), kd.numpy(),
+                  c.k_cache.view(torch.float8_e4m3fn).double()[..., :6].contiguous().numpy(),
+                  c.seq_lens.numpy(), c.scale, pt, c.page_size)
+    assert np.abs(Ow - O).max() > 1e-3
