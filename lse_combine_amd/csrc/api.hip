@@ -88,6 +88,8 @@ int check_problem(const da_problem* p, Variant* var) {
   // contractions over all q heads). MLA-style latent 576/512 with V = the first 512 nope
   // columns, and GLM-style 256/256 (nope 192, V of its own) once q_len x group exceeds the
   // 16 MFMA columns of the GQA kernel; the 64 rotary columns in the K rows or stored apart.
+  // The latent form also takes an fp8 cache: nope codes with per-token K scales, the rotary
+  // columns apart in bf16.
   const bool latent = p->qk_depth == 576 && p->ov_depth == 512;
   const bool glm_mqa = p->qk_depth == 256 && p->ov_depth == 256 && !p->v_is_k_prefix && p->num_kv_heads == 1 &&
                        ql * g > 16;
@@ -102,9 +104,14 @@ int check_problem(const da_problem* p, Variant* var) {
                   p->qk_depth, p->ov_depth, nope_apart, p->nope_depth);
     if (p->nope_depth > 0 && p->rope_dtype != DA_BF16)
       return fail(DA_EUNSUPPORTED, "rotary columns stored apart must be bf16 (rope_dtype %d)", p->rope_dtype);
-    if (p->kv_dtype == DA_FP8_E4M3)
-      return fail(DA_EUNSUPPORTED, "the shared-kv-head kernel (depth %d/%d, one kv head) takes bf16 caches",
-                  p->qk_depth, p->ov_depth);
+    if (p->kv_dtype == DA_FP8_E4M3 &&
+        (!latent || p->nope_depth != 512 ||
+         (p->page_size != 0 && !(p->page_size >= kTileKeys && (p->page_size & (p->page_size - 1)) == 0))))
+      return fail(DA_EUNSUPPORTED,
+                  "fp8 on the shared-kv-head kernel: the latent form (576/512) with the 64 rotary columns "
+                  "stored apart in bf16 (nope_depth 512) and a contiguous cache or pages of a power of two "
+                  ">= 32 keys (got depth %d/%d, nope_depth %d, page_size %d)",
+                  p->qk_depth, p->ov_depth, p->nope_depth, p->page_size);
     *var = kVarShared;
     return DA_OK;
   }
@@ -368,6 +375,8 @@ int check_kv_args(const da_problem* p, const da_kv& kv) {
     return fail(DA_EINVAL, "fp8 caches need k_scale (use decode_attn_splitk_fp8 / decode_attn_splitk_kv)");
   if (p->kv_dtype != DA_FP8_E4M3 && (kv.k_scale || kv.v_scale))
     return fail(DA_EINVAL, "k_scale / v_scale are for fp8 caches (kv_dtype = DA_FP8_E4M3)");
+  if (p->kv_dtype == DA_FP8_E4M3 && p->v_is_k_prefix && kv.v_scale)
+    return fail(DA_EINVAL, "with V the first ov_depth K columns, V is read with the K scales: v_scale must be NULL");
   if (p->nope_depth > 0 && !kv.k_rope)
     return fail(DA_EINVAL, "nope_depth > 0: the rotary columns (k_rope) are needed (use decode_attn_splitk_kv)");
   if (p->nope_depth == 0 && kv.k_rope) return fail(DA_EINVAL, "k_rope is for nope_depth > 0");

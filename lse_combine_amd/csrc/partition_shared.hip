@@ -62,27 +62,33 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 
 // Depths of one instantiation: DN nope columns and DR rotary columns make the q.K depth; V
 // has DV columns and is either the first DV nope columns (SHARED) or a cache of its own.
-template <int DN_, int DR_, int DV_, bool SHARED_>
+// F8: the nope columns are E4M3 codes with a per-token K scale (the rotary columns stay bf16,
+// stored apart); V, a prefix of them, is read as code x the token's K scale.
+template <int DN_, int DR_, int DV_, bool SHARED_, bool F8_ = false>
 struct SShape {
   static constexpr int DN = DN_, DR = DR_, DV = DV_;
-  static constexpr bool SHARED = SHARED_;
+  static constexpr bool SHARED = SHARED_, F8 = F8_;
   static constexpr int DQK = DN + DR;
   static constexpr int NJ = DQK / 32;            // 32-deep k-steps of q.K
   static constexpr int NJN = DN / 32;            // ... over the nope columns
-  static constexpr int kNRow = DN * 2;           // LDS bytes of one row, per region
+  static constexpr int kNRow = F8 ? DN : DN * 2; // LDS bytes of one row, per region
   static constexpr int kRRow = DR * 2;
-  static constexpr int kVRow = SHARED ? DN * 2 : DV * 2;
+  static constexpr int kVCols = DV / 4;          // V columns of one P.V wave
+  static constexpr int kDB = kVCols / 16;        // its 16-deep O blocks
+  // rows of the tile that the transposing V reads see: the nope rows (bf16, SHARED), the V
+  // rows of its own, or (F8) the wave's own bf16 copy of its V columns
+  static constexpr int kVRow = F8 ? kVCols * 2 : (SHARED ? DN * 2 : DV * 2);
   static constexpr int kNBytes = kTile * kNRow;  // region offsets inside a slot
   static constexpr int kRBytes = kTile * kRRow;
   static constexpr int kVOff = SHARED ? 0 : kNBytes + kRBytes;
-  static constexpr int kSlot = kNBytes + kRBytes + (SHARED ? 0 : kTile * DV * 2);
+  static constexpr int kScOff = kNBytes + kRBytes + (SHARED ? 0 : kTile * DV * 2);   // F8: K scales
+  static constexpr int kSlot = kScOff + (F8 ? 1024 : 0);
   static constexpr int kBlocks = kSlot / 1024;   // 1 KB direct-to-LDS loads per tile
   static constexpr int kPerWave = (kBlocks + kWaves - 1) / kWaves;
-  static constexpr int kVCols = DV / 4;          // V columns of one P.V wave
-  static constexpr int kDB = kVCols / 16;        // its 16-deep O blocks
   static_assert(NJ % 2 == 0 && DN % 64 == 0 && DR % 64 == 0 && DV % 64 == 0, "depths");
   static_assert(kNBytes % 1024 == 0 && kRBytes % 1024 == 0 && kSlot % 1024 == 0, "1 KB load blocks");
   static_assert(!SHARED || DV <= DN, "a shared V is a prefix of the nope columns");
+  static_assert(!F8 || (SHARED && DN == 512), "fp8: the latent form (nope rows of 512 codes, V a prefix)");
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -137,10 +143,18 @@ struct SmemBase {
   // wave writes its 8 bytes per lane contiguously (no bank conflicts either way).
   char pbuf[2][kPBytes];
 };
+// F8: each P.V wave's bf16 copy of its V columns of the tile it consumes (32 rows of
+// kVRow bytes, chunks swizzled for the transposing reads)
+template <class S, bool F8 = S::F8>
+struct VPriv {};
+template <class S>
+struct VPriv<S, true> {
+  char vpriv[4][kTile * S::kVRow];
+};
 template <class S, int R, bool LDS_PAGES>
-struct SharedSmem : SmemBase<S, R> {};
+struct SharedSmem : SmemBase<S, R>, VPriv<S> {};
 template <class S, int R>
-struct SharedSmem<S, R, true> : SmemBase<S, R> {
+struct SharedSmem<S, R, true> : SmemBase<S, R>, VPriv<S> {
   int pages[kMaxLdsPages];   // page indices of the partition (per-key page lookup)
 };
 
@@ -221,7 +235,7 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
   // live block.)
   const char* kc = (const char*)a.k;
   const char* vc = (const char*)a.v;
-  const uint32_t krow = (uint32_t)a.Dk * 2;           // bytes between tokens in k_cache
+  const uint32_t krow = (uint32_t)a.Dk * (S::F8 ? 1 : 2);   // bytes between tokens in k_cache
   const uint32_t vrow = (uint32_t)a.v_row_len * 2;    // ... in v_cache
   // per load i of this wave: region base and row stride (uniform), lane offset
   const char* lbase[S::kPerWave];
@@ -240,6 +254,11 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
     } else if (jb < S::kNBytes + S::kRBytes) {
       q2 = jb - S::kNBytes + lane * 16, lbase[i] = rope_base, lstride[i] = rope_row_bytes;
       r = q2 / S::kRRow, cs = (q2 - r * S::kRRow) >> 4, gc = cs ^ swz<S::kRRow>(r);
+    } else if (S::F8 && jb >= S::kScOff) {
+      // the tile's 32 K scales (4 bytes per token, tokens innermost): lanes 0-7 load them,
+      // the rest fall outside the buffer range
+      q2 = 0, lbase[i] = (const char*)a.k_scale, lstride[i] = 4u;
+      r = 4 * lane, cs = 0, gc = 0;
     } else {
       q2 = jb - S::kNBytes - S::kRBytes + lane * 16, lbase[i] = vc, lstride[i] = vrow;
       r = q2 / (S::DV * 2), cs = (q2 - r * (S::DV * 2)) >> 4, gc = cs ^ swz<S::DV * 2>(r);
@@ -354,6 +373,17 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
     for (int u = 0; u < 4; ++u) kn[u] = r * S::kNRow + 16 * (((4 * u + qd) ^ fn) & (kNW ? 15 : 7));
 #pragma unroll
     for (int u = 0; u < 2; ++u) kr[u] = S::kNBytes + r * S::kRRow + 16 * ((4 * u + qd) ^ fr);
+    // F8 nope operands: k-step j reads the 8 codes of depth 32 j + 8 qd .. +7, i.e. half
+    // qd & 1 of logical chunk 2 j + qd / 2 of row r (rows of 512 codes, the wide-row swizzle);
+    // the per-lane part repeats every 8 steps
+    int kn8[8];
+    if constexpr (S::F8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) kn8[u] = r * S::kNRow + 16 * ((2 * u + (qd >> 1)) ^ fn) + 8 * (qd & 1);
+    }
+    auto load_k8 = [&](const DA_LDS char* KL, int j) {
+      return *(const DA_LDS u32x2*)(KL + kn8[j & 7] + 256 * (j >> 3));
+    };
     auto load_k = [&](const DA_LDS char* KL, int j) {
       int off;
       if (j < S::NJN) off = kNW ? kn[j & 3] + 256 * (j >> 2) : kn[j & 1] + 128 * (j >> 1);
@@ -369,19 +399,50 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
     // block), then the softmax against m_ref and the P write.
     auto qk_step = [&](int s, bool first) {
       const DA_LDS char* KL = (const DA_LDS char*)sm.tile[s % R];
-      bf16x8 kf[S::NJ];
-#pragma unroll
-      for (int j = 0; j < kAhead; ++j) kf[j] = load_k(KL, j);
-      __builtin_amdgcn_sched_barrier(0);
       f32x4 acc[2][2];
 #pragma unroll
       for (int bi = 0; bi < 2; ++bi) acc[bi][0] = acc[bi][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 ks = f32x4{1.f, 1.f, 1.f, 1.f};   // F8: K scales of the lane's 4 keys
+      if constexpr (S::F8) {
+        // all nope codes (2 registers per step) and the rotary operands are requested first;
+        // a step's codes are widened to bf16 just before its products. The nope and rotary
+        // parts are summed apart: the K scale multiplies the nope part only.
+        u32x2 kc[S::NJN];
+        bf16x8 krp[S::NJ - S::NJN];
 #pragma unroll
-      for (int j = 0; j < S::NJ; ++j) {
-        acc[0][j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j], qf[0][j], acc[0][j & 1], 0, 0, 0);
-        acc[1][j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j], qf[1][j], acc[1][j & 1], 0, 0, 0);
-        if (j + kAhead < S::NJ) kf[j + kAhead] = load_k(KL, j + kAhead);
+        for (int j = 0; j < S::NJN; ++j) kc[j] = load_k8(KL, j);
+#pragma unroll
+        for (int j = S::NJN; j < S::NJ; ++j) krp[j - S::NJN] = load_k(KL, j);
+        ks = *(const DA_LDS f32x4*)(KL + S::kScOff + 4 * (16 * kh + 4 * qd));
         __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < S::NJN; ++j) {
+          const bf16x8 kf = fp8x8_to_bf16x8(kc[j][0], kc[j][1]);
+          acc[0][j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][j], acc[0][j & 1], 0, 0, 0);
+          acc[1][j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][j], acc[1][j & 1], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi) acc[bi][0] = (acc[bi][0] + acc[bi][1]) * ks;
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi) acc[bi][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = S::NJN; j < S::NJ; ++j) {
+          acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(krp[j - S::NJN], qf[0][j], acc[0][1], 0, 0, 0);
+          acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(krp[j - S::NJN], qf[1][j], acc[1][1], 0, 0, 0);
+        }
+      } else {
+        bf16x8 kf[S::NJ];
+#pragma unroll
+        for (int j = 0; j < kAhead; ++j) kf[j] = load_k(KL, j);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < S::NJ; ++j) {
+          acc[0][j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j], qf[0][j], acc[0][j & 1], 0, 0, 0);
+          acc[1][j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j], qf[1][j], acc[1][j & 1], 0, 0, 0);
+          if (j + kAhead < S::NJ) kf[j + kAhead] = load_k(KL, j + kAhead);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       const int t0 = start + s * kTile;
       float pr[2][4];
@@ -428,6 +489,9 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
         for (int i = 0; i < 4; ++i) {
           pr[bi][i] = exp2_fast(fmaf(pr[bi][i], c, -mc));
           l_lane[bi] += pr[bi][i];
+          // F8: V is code x the token's K scale; the scale goes into P.V's operand, l sums
+          // the unscaled p
+          if constexpr (S::F8) pr[bi][i] *= ks[i];
         }
         // hi and lo parts of P into the buffer (8 bytes each per lane)
         const uint32_t h0 = pack_bf16x2(pr[bi][0], pr[bi][1]), h1 = pack_bf16x2(pr[bi][2], pr[bi][3]);
@@ -494,7 +558,7 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
     const int ra = 4 * qd + (n >> 2);
     const int v_off = S::kVOff + ra * S::kVRow + (n & 1) * 8;
     auto load_v = [&](const DA_LDS char* KL, int db) {
-      const int ch = 2 * (v * S::kDB + db) + ((n & 3) >> 1);
+      const int ch = 2 * ((S::F8 ? 0 : v * S::kDB) + db) + ((n & 3) >> 1);
       const DA_LDS char* pa = KL + v_off + 16 * (ch ^ swz<S::kVRow>(ra));
       const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 DA_LDS*)pa);
       const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 DA_LDS*)(pa + 16 * S::kVRow));
@@ -507,8 +571,34 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
     // O^T += V^T P^T for the wave's depth blocks and all four column blocks: every operand is
     // requested first, then column block by column block the hi products of the depth blocks,
     // then their lo products, so that no product waits for the one just before it
+    // F8: the wave widens the codes of its V columns of tile s into its bf16 copy (lane:
+    // row lane / 2, four of the eight 16-code chunks of the row), which the transposing reads
+    // then see like a bf16 tile. Only this wave writes and reads the copy.
+    auto widen_v = [&](int s) {
+      if constexpr (S::F8) {
+        const char* src = sm.tile[s % R];
+        char* dst = sm.vpriv[v];
+        const int r = lane >> 1, h = lane & 1;
+        const int fs = swz<S::kNRow>(r), fd = swz<S::kVRow>(r);
+        u32x4 cw[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) cw[k] = *(const u32x4*)(src + r * S::kNRow + 16 * ((8 * v + 4 * h + k) ^ fs));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int bc = 2 * (4 * h + k);
+          *(bf16x8*)(dst + r * S::kVRow + 16 * (bc ^ fd)) = fp8x8_to_bf16x8(cw[k][0], cw[k][1]);
+          *(bf16x8*)(dst + r * S::kVRow + 16 * ((bc + 1) ^ fd)) = fp8x8_to_bf16x8(cw[k][2], cw[k][3]);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+    };
     auto pv_step = [&](int s) {
-      const DA_LDS char* KL = (const DA_LDS char*)sm.tile[s % R];
+      widen_v(s);
+      const DA_LDS char* KL;
+      if constexpr (S::F8) KL = (const DA_LDS char*)sm.vpriv[v];
+      else KL = (const DA_LDS char*)sm.tile[s % R];
       const char* pb = sm.pbuf[s & 1] + lane * 8;
       bf16x8 vf[S::kDB], ph[4], pl[4];
 #pragma unroll
@@ -589,7 +679,10 @@ hipError_t launch_shape(const PartArgs& a, int page_mode, hipStream_t s) {
       hipLaunchKernelGGL((partition_shared_kernel<S, kPagedAligned>), grid, block, 0, s, a, rope, rope_row);
       break;
     default:
-      hipLaunchKernelGGL((partition_shared_kernel<S, kPagedGeneral>), grid, block, 0, s, a, rope, rope_row);
+      // (fp8: not for the any-page-size form, which reads rows key by key while a tile's
+      // scales are loaded as consecutive rows)
+      if constexpr (S::F8) return hipErrorInvalidValue;
+      else hipLaunchKernelGGL((partition_shared_kernel<S, kPagedGeneral>), grid, block, 0, s, a, rope, rope_row);
       break;
   }
   return hipGetLastError();
@@ -601,8 +694,15 @@ hipError_t launch_shape(const PartArgs& a, int page_mode, hipStream_t s) {
 // first 512 nope columns) and one-kv-head GLM-style widths (q.K 256 = 192 nope + 64 rotary,
 // V 256 of its own). The rotary columns may be in the K rows or stored apart.
 hipError_t launch_partition_shared(const PartArgs& a, int page_mode, hipStream_t s) {
-  if (a.Hkv != 1 || a.kv_fp8) return hipErrorInvalidValue;
+  if (a.Hkv != 1) return hipErrorInvalidValue;
   const bool rope_apart = a.k_rope != nullptr;
+  if (a.kv_fp8) {
+    // latent over an fp8 cache: nope codes with per-token K scales, rotary columns bf16 apart
+    if (a.Dqk == 576 && a.Dv == 512 && a.v == a.k && a.Dk == 512 && rope_apart && a.k_scale && !a.v_scale &&
+        page_mode != kPagedGeneral)
+      return launch_shape<SShape<512, 64, 512, true, true>>(a, page_mode, s);
+    return hipErrorInvalidValue;
+  }
   if (a.Dqk == 576 && a.Dv == 512 && a.v == a.k && a.Dk == (rope_apart ? 512 : 576))
     return launch_shape<SShape<512, 64, 512, true>>(a, page_mode, s);
   if (a.Dqk == 256 && a.Dv == 256 && a.v != a.k && a.Dk == (rope_apart ? 192 : 256))

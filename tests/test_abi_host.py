@@ -220,8 +220,17 @@ def test_probe_argument_checks():
     (dict(kv_dtype=2, page_size=48, max_pages_per_seq=100), DA_EUNSUPPORTED),   # not a power of two
     (dict(kv_dtype=2, dtype=0), DA_EUNSUPPORTED),                # fp32 q
     (dict(kv_dtype=2, kernel=1), DA_EUNSUPPORTED),               # vector-ALU kernel
+    # latent over fp8: only with the rotary columns apart in bf16 and pages of a power of two
     (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1),
      DA_EUNSUPPORTED),
+    (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1,
+          nope_depth=512, rope_dtype=1), DA_OK),
+    (dict(kv_dtype=2, num_q_heads=16, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1,
+          nope_depth=512, rope_dtype=1, q_len=3, page_size=0, kv_capacity=4096), DA_OK),
+    (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1,
+          nope_depth=512, rope_dtype=1, page_size=48, max_pages_per_seq=100), DA_EUNSUPPORTED),
+    (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=256, ov_depth=256, nope_depth=192,
+          rope_dtype=1), DA_EUNSUPPORTED),                                   # one-kv-head GLM widths
     (dict(kv_dtype=7), DA_EINVAL),
 ])
 def test_fp8_cache_support(lib, kw, code):
@@ -343,6 +352,13 @@ def test_rotary_columns_apart_need_their_tensor(lib):
     assert r == DA_EINVAL
     assert lib.decode_attn_splitk_kv(ctypes.byref(p0), FAKE, None, FAKE, FAKE, 0.1, 0, 0, FAKE, None, None, FAKE,
                                      1 << 30, None) == DA_EINVAL
+    # a V read as the first K columns takes the K scales: a V scale of its own is refused
+    pl = prob(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1,
+              nope_depth=512, rope_dtype=1)
+    kv = DaKv(0x1000, None, 0x1000, 0x1000, 0x1000)
+    r = lib.decode_attn_partition_kv(ctypes.byref(pl), FAKE, ctypes.byref(kv), FAKE, FAKE, 0.1, 256, 16, FAKE, FAKE,
+                                     None)
+    assert r == DA_EINVAL and b"v_scale" in lib.da_last_error()
     # fp8 caches need their K scales here too
     p8 = prob(qk_depth=256, ov_depth=256, nope_depth=192, rope_dtype=1, kv_dtype=2)
     kv = DaKv(0x1000, 0x1000, 0x1000, None, None)

@@ -208,6 +208,19 @@ SHARED = [
                                                num_splits=0, seed=174, rope_apart=64, **GLM_MQA)),
     ("glm_mqa_apart_poisoned", dict(batch=3, num_q_heads=64, page_size=64, seq_lens=[100, 1, 1025], num_splits=2,
                                     seed=175, rope_apart=64, poison=True, spare_pages=3, **GLM_MQA)),
+    # latent over an fp8 cache (nope codes + per-token K scales, rotary bf16 apart)
+    ("latent_fp8_g64_paged64", dict(batch=2, num_q_heads=64, page_size=64, seq_lens=[700, 1313], num_splits=3,
+                                    seed=180, rope_apart=64, kv_fp8=True, **LATENT)),
+    ("latent_fp8_g128_contig_ragged", dict(batch=3, num_q_heads=128, seq_lens=[100, 33, 1], num_splits=2,
+                                           seed=181, rope_apart=64, kv_fp8=True, **LATENT)),
+    ("latent_fp8_g40_paged32_auto", dict(batch=3, num_q_heads=40, page_size=32, seq_lens=[517, 64, 2000],
+                                         num_splits=0, seed=182, rope_apart=64, kv_fp8=True, **LATENT)),
+    ("latent_fp8_q2_g64_paged64", dict(batch=3, num_q_heads=64, page_size=64, seq_lens=[1, 900, 2100],
+                                       num_splits=3, seed=183, q_len=2, rope_apart=64, kv_fp8=True, **LATENT)),
+    ("latent_fp8_one_split", dict(batch=2, num_q_heads=128, page_size=64, seq_lens=[90, 31], num_splits=1,
+                                  seed=184, rope_apart=64, kv_fp8=True, **LATENT)),
+    ("latent_fp8_poisoned", dict(batch=3, num_q_heads=64, page_size=64, seq_lens=[100, 1, 1025], num_splits=2,
+                                 seed=185, rope_apart=64, kv_fp8=True, poison=True, spare_pages=3, **LATENT)),
 ]
 
 
@@ -223,8 +236,9 @@ def test_shared_kv_head_parity(name, kw):
                     assert torch.all(out[b, i].float() == 0) and torch.all(torch.isneginf(lse[b, i]))
 
 
-@pytest.mark.parametrize("kw", [dict(rope_apart=64, **GLM_MQA), dict(rope_apart=64, **LATENT)],
-                         ids=["glm_mqa_apart", "latent_apart"])
+@pytest.mark.parametrize("kw", [dict(rope_apart=64, **GLM_MQA), dict(rope_apart=64, **LATENT),
+                                dict(rope_apart=64, kv_fp8=True, **LATENT)],
+                         ids=["glm_mqa_apart", "latent_apart", "latent_fp8"])
 def test_shared_kv_head_large_logits_take_the_second_pass(kw):
     case = make_case("big_shared", batch=2, num_q_heads=64, page_size=64, seq_lens=[1300, 700], num_splits=2,
                      seed=176, q_scale=64.0, **kw)
@@ -510,7 +524,7 @@ def test_combine_only_on_oracle_partials(Dv, P):
 # with the oracle: the method is an exact re-association of the definition, so no row may
 # differ beyond the stated tolerances (the oracle runs the largest of these in seconds).
 FULL_WORKLOADS = ["tiny", "gqa", "paged_gqa", "long", "latent", "paged_gqa_q2", "paged_gqa_fp8", "paged_glm",
-                  "paged_glm_fp8", "latent_rope_apart", "glm_mqa", "paged_mha"]
+                  "paged_glm_fp8", "latent_rope_apart", "glm_mqa", "paged_mha", "latent_fp8"]
 
 
 @pytest.mark.parametrize("name", FULL_WORKLOADS)
