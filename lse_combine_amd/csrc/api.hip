@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <mutex>
 
 #include "da_internal.h"
@@ -266,7 +267,10 @@ void ws_layout(const da_problem* p, int32_t chunk, int32_t max_splits, size_t* m
   const size_t meta = chunk == 0 ? (size_t)p->batch * 2 * sizeof(int32_t) : 0;
   const size_t ml = (rows * 2 * sizeof(float) + meta + 255) & ~(size_t)255;
   const size_t o = (rows * (size_t)p->ov_depth * sizeof(float) + 255) & ~(size_t)255;
-  const size_t cnt = ((size_t)p->batch * p->num_kv_heads * sizeof(int32_t) + 255) & ~(size_t)255;
+  // arrival counters of the fused combine: one per (sequence, kv head), or per (sequence,
+  // block of 64 columns) on the shared-kv-head kernel
+  const size_t per_seq = std::max<size_t>((size_t)p->num_kv_heads, (size_t)ceil_div(rows_per_seq(p), 64));
+  const size_t cnt = ((size_t)p->batch * per_seq * sizeof(int32_t) + 255) & ~(size_t)255;
   *ml_off = 0;
   *o_off = ml;
   *cnt_off = ml + o;
@@ -402,10 +406,8 @@ void set_kv_args(const da_problem* p, const da_kv& kv, da::PartArgs* a) {
   a->Dk = p->nope_depth > 0 ? p->nope_depth : p->qk_depth;
 }
 
-// The whole step. With `fused`, the GQA matrix-core kernel and the vector-ALU kernel
-// combine in their last-arriving workgroups (no second launch); the shared-kv-head kernel
-// runs the combine as a launch of its own.
-// The results are the same either way.
+// The whole step. With `fused`, the partition kernel's last-arriving workgroup of each
+// (sequence, head group) combines (no second launch). The results are the same either way.
 int run_splitk(const da_problem* p, const void* q, const da_kv& kv, const int32_t* page_table, const int32_t* seq_lens,
                float scale, int32_t num_splits, void* out, float* lse_out, float* o_f32_out, void* workspace,
                size_t workspace_bytes, void* stream, bool fused) {
@@ -437,7 +439,7 @@ int run_splitk(const da_problem* p, const void* q, const da_kv& kv, const int32_
   a.o32 = o_f32_out;
   a.direct_single = 1;
   set_kv_args(p, kv, &a);
-  const bool fuse = fused && var != kVarShared;
+  const bool fuse = fused;
   if (fuse) a.counters = (int32_t*)((char*)workspace + cnt_off);
   if ((r = launch_partition(p, var, a, s, cus))) return r;
   if (!fuse && (r = launch_combine(p, seq_lens, scale, C, P, po, pml, out, lse_out, o_f32_out, 1, s))) return r;

@@ -179,7 +179,18 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
   const int p = blockIdx.x, cblk = blockIdx.y, b = blockIdx.z;
   const int L = __builtin_amdgcn_readfirstlane(attended_len(a, b, PM == kContiguous));
   const int start = p * a.chunk;
-  if (start >= L) return;
+  if (start >= L) {
+    // fused combine: the rows of a sequence without keys (O = 0, LSE = -inf) come from its
+    // first workgroup of each column block
+    if (a.counters && p == 0 && L == 0) {
+      constexpr int kUnits = S::DV / 4;
+      const int nrow = min(kCols, a.Hq - cblk * kCols);
+      for (int u = threadIdx.x; u < nrow * kUnits; u += kThreads)
+        write_row_unit(a.out, a.o32, a.lse, (int64_t)b * a.Hq + cblk * kCols + u / kUnits, S::DV, (u % kUnits) * 4,
+                       -INFINITY, 0.f, f32x4{0.f, 0.f, 0.f, 0.f}, a.scale);
+    }
+    return;
+  }
   const int end = min(start + a.chunk, L);
   const int P_b = min((L + a.chunk - 1) / a.chunk, a.max_splits);
   const bool direct = a.direct_single && P_b == 1;
@@ -660,6 +671,72 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
                    v == 0 && db == 0 && qd == 0);
     }
   }
+
+  if (!a.counters || direct) return;
+  // Fused combine (fa4_splitk_combine_write, fourth paragraph): every wave's partial stores
+  // complete, one agent-scope release and a count on the (sequence, column block) counter;
+  // the workgroup that completes the count acquires the others' partials and folds the
+  // block's rows with every thread (S threads per (row, 4-wide slice) unit splitting the
+  // partitions, merged through LDS as in the combine launch).
+  wait_vm<0>();
+  __syncthreads();
+  int* cnt = a.counters + (int64_t)b * gridDim.y + cblk;
+  int* flag_s = (int*)sm.pbuf[0];
+  if (tid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const int last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == P_b - 1;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    *flag_s = last ? 1 : 0;
+  }
+  __syncthreads();
+  if (!__builtin_amdgcn_readfirstlane(*flag_s)) return;
+  {
+    constexpr int kUnits = S::DV / 4;
+    const int nrow = min(kCols, ncols - col0);
+    const int total = nrow * kUnits;
+    const int SUB = P_b <= 16 ? 1 : (P_b <= 64 ? 4 : 16);
+    const int UNITS = kThreads / SUB;
+    const int sub = tid / UNITS, ui = tid % UNITS;
+    // (the merge's LDS: the tile ring, free by now)
+    float* sM = (float*)&sm.tile[0][0];   // [SUB][UNITS]
+    float* sL = sM + SUB * UNITS;
+    f32x4* sO = (f32x4*)(sL + SUB * UNITS);
+    for (int u0 = 0; u0 < total; u0 += UNITS) {
+      const int u = u0 + ui;
+      const bool valid = u < total;
+      const int d0 = valid ? (u % kUnits) * 4 : 0;
+      const int64_t row = (int64_t)b * a.Hq + col0 + (valid ? u / kUnits : 0);
+      float M = -INFINITY, Ls = 0.f;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (valid)
+        fold_partials<S::DV>((const float2*)a.part_ml + row * a.max_splits, a.part_o + row * a.max_splits * S::DV + d0,
+                             1, P_b, sub, SUB, c, M, Ls, acc);
+      if (SUB > 1) {
+        sM[sub * UNITS + ui] = M;
+        sL[sub * UNITS + ui] = Ls;
+        sO[sub * UNITS + ui] = acc;
+        __syncthreads();
+        if (valid && sub == 0) {
+          float G = -INFINITY;
+          for (int t = 0; t < SUB; ++t)
+            if (sL[t * UNITS + ui] > 0.f) G = fmaxf(G, sM[t * UNITS + ui]);
+          Ls = 0.f;
+          acc = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int t = 0; t < SUB; ++t) {
+            if (sL[t * UNITS + ui] > 0.f) {
+              const float e = exp2_fast((sM[t * UNITS + ui] - G) * c);
+              Ls += sL[t * UNITS + ui] * e;
+              acc += e * sO[t * UNITS + ui];
+            }
+          }
+          M = G;
+        }
+        __syncthreads();   // (the LDS is reused by the next units)
+      }
+      if (valid && sub == 0) write_row_unit(a.out, a.o32, a.lse, row, S::DV, d0, M, Ls, acc, a.scale);
+    }
+  }
+  if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <class S>

@@ -141,9 +141,9 @@ def test_large_logits_overflow_safety():
     assert_parity(out, lse, o32, O, LSE, o32_row_rtol=1e-4, what="large logits")
 
 
-def test_latent_fused_entry_point_falls_back_to_two_launches():
-    # the fused entry point on a latent-shared problem runs the partition and combine
-    # launches; outputs (rows of an empty sequence included) match the oracle
+def test_latent_fused_entry_point_writes_every_row():
+    # the fused entry point on a latent-shared problem: the last workgroup of each column
+    # block combines; outputs (rows of an empty sequence included) match the oracle
     print("[parity] latent through the fused entry point", flush=True)
     case = make_case("latent_fused", batch=3, num_q_heads=64, num_kv_heads=1, qk_depth=576, ov_depth=512,
                      page_size=64, seq_lens=[900, 0, 65], num_splits=2, seed=38, v_is_k_prefix=True)
@@ -370,6 +370,19 @@ FUSED = [
     # one long sequence in a batch of short ones under equal shares: most workers meet it
     ("auto_one_long_many_short", dict(batch=40, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=64,
                                       seq_lens=[30000] + [64] * 39, num_splits=0, seed=74)),
+    # one kv head for all q heads (the shared-kv-head kernel): latent, latent over fp8 with
+    # an empty sequence, several queries, GLM widths with the rotary columns apart, and 20
+    # partitions (4 threads per unit in the fold)
+    ("latent_g64_paged64", dict(batch=2, num_q_heads=64, page_size=64, seq_lens=[700, 1313], num_splits=3,
+                                seed=90, **LATENT)),
+    ("latent_fp8_empty_seq", dict(batch=3, num_q_heads=128, page_size=64, seq_lens=[900, 0, 65], num_splits=2,
+                                  seed=91, rope_apart=64, kv_fp8=True, **LATENT)),
+    ("latent_q2_contig", dict(batch=2, num_q_heads=40, seq_lens=[1000, 3], num_splits=4, seed=92, q_len=2,
+                              **LATENT)),
+    ("glm_mqa_apart_paged32", dict(batch=2, num_q_heads=128, page_size=32, seq_lens=[1500, 333], num_splits=3,
+                                   seed=93, rope_apart=64, **GLM_MQA)),
+    ("glm_mqa_20_splits", dict(batch=1, num_q_heads=64, page_size=64, seq_lens=[5000], num_splits=20, seed=94,
+                               rope_apart=64, **GLM_MQA)),
     # the vector-ALU kernel: fp32 (its automatic choice) and bf16 on request
     ("fp32_tiny", dict(batch=1, num_q_heads=1, num_kv_heads=1, qk_depth=128, dtype=torch.float32,
                        seq_lens=[1024], num_splits=4, seed=75)),
@@ -393,7 +406,8 @@ def test_fused_combine_matches_oracle_on_repeated_calls(name, kw):
     kernel = kw.pop("kernel", "auto")
     case = make_case(name, **kw)
     dc = to_device(case)
-    prob = api.make_problem(dc.q, dc.k_cache, dc.v_cache, dc.page_table, page_size=case.page_size, kernel=kernel)
+    prob = api.make_problem(dc.q, dc.k_cache, dc.v_cache, dc.page_table, page_size=case.page_size, kernel=kernel,
+                            v_is_k_prefix=case.v_is_k_prefix, ov_depth=case.ov_depth, k_rope=dc.k_rope)
     ws = torch.zeros(api.workspace_bytes(prob, case.num_splits), dtype=torch.uint8, device="cuda")
     O, LSE = oracle_for(case)
     for rep in range(3):
@@ -414,6 +428,10 @@ FUSED_EMPTY = [
                        seq_lens=[0, 3000, 0, 5, 0, 0], num_splits=0, seed=68)),
     ("auto_all_empty", dict(batch=3, num_q_heads=8, num_kv_heads=1, qk_depth=128, page_size=64,
                             seq_lens=[0, 0, 0], num_splits=0, seed=69)),
+    ("latent_fixed2", dict(batch=4, num_q_heads=80, page_size=64, seq_lens=[0, 1, 700, 0], num_splits=2,
+                           seed=95, **LATENT)),
+    ("fp32_vector_alu", dict(batch=3, num_q_heads=4, num_kv_heads=2, qk_depth=128, dtype=torch.float32,
+                             seq_lens=[0, 300, 0], num_splits=2, seed=96)),
 ]
 
 
@@ -425,7 +443,7 @@ def test_fused_combine_writes_rows_of_empty_sequences(name, kw):
     case = make_case(name, **kw)
     dc = to_device(case)
     prob = api.make_problem(dc.q, dc.k_cache, dc.v_cache, dc.page_table, page_size=case.page_size,
-                            ov_depth=case.ov_depth, k_rope=dc.k_rope)
+                            v_is_k_prefix=case.v_is_k_prefix, ov_depth=case.ov_depth, k_rope=dc.k_rope)
     ws = torch.zeros(api.workspace_bytes(prob, case.num_splits), dtype=torch.uint8, device="cuda")
     rows = api.row_shape(prob)
     out = torch.empty(rows + (prob.ov_depth,), dtype=torch.bfloat16, device="cuda")
