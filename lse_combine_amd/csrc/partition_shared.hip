@@ -27,7 +27,8 @@
 // twice (two column pairs), V once, and P (8 KB) four times.
 //
 // Tiles pass through a ring of four LDS slots: in step s the q.K waves work on tile s, the
-// P.V waves on tile s - 1, and tiles s + 1 and s + 2 are in flight; one barrier per step. P
+// P.V waves on tile s - 1, and tiles s + 1 and s + 2 are in flight (their loads issued by
+// the q.K waves, so that the P.V waves keep to their products); one barrier per step. P
 // is double-buffered. (Four slots of the latent tile and the two P buffers fill the 160 KB
 // of LDS exactly: the page indices live in registers and the exchange arrays in a P buffer.
 // With one tile in flight a step waits for its whole tile, and a load-only copy streams at
@@ -84,7 +85,10 @@ struct SShape {
   static constexpr int kScOff = kNBytes + kRBytes + (SHARED ? 0 : kTile * DV * 2);   // F8: K scales
   static constexpr int kSlot = kScOff + (F8 ? 1024 : 0);
   static constexpr int kBlocks = kSlot / 1024;   // 1 KB direct-to-LDS loads per tile
-  static constexpr int kPerWave = (kBlocks + kWaves - 1) / kWaves;
+  // the tile's loads are issued by the four q.K waves (the P.V waves, with the most
+  // matrix-core work per tile, only consume): 61.0 against 63.5 us on the latent workload
+  static constexpr int kDmaWaves = 4;
+  static constexpr int kPerWave = (kBlocks + kDmaWaves - 1) / kDmaWaves;
   static_assert(NJ % 2 == 0 && DN % 64 == 0 && DR % 64 == 0 && DV % 64 == 0, "depths");
   static_assert(kNBytes % 1024 == 0 && kRBytes % 1024 == 0 && kSlot % 1024 == 0, "1 KB load blocks");
   static_assert(!SHARED || DV <= DN, "a shared V is a prefix of the nope columns");
@@ -234,7 +238,7 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
   __syncthreads();
 
   // The tile of keys t0 .. t0 + 31 lands in LDS by direct-to-LDS 16-byte loads: 1 KB block j
-  // of the slot is loaded by wave j % 8 (its load i = j / 8). Within a region of rows of RB
+  // of the slot is loaded by q.K wave j % 4 (its load i = j / 4). Within a region of rows of RB
   // bytes, lane l of a block writes slot byte pos = 1024 j + 16 l - (region offset), i.e. row
   // pos / RB and chunk slot (pos % RB) / 16, and loads the cache chunk slot ^ swz(row) of
   // that row there.
@@ -252,10 +256,12 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
   const char* lbase[S::kPerWave];
   uint32_t lstride[S::kPerWave], loff[S::kPerWave];
   bool lvalid[S::kPerWave];
+  const int dw = w;                 // index among the waves that load
+  const bool dma_wave = w < S::kDmaWaves;
 #pragma unroll
   for (int i = 0; i < S::kPerWave; ++i) {
-    const int j = w + kWaves * i;
-    lvalid[i] = j < S::kBlocks;
+    const int j = dw + S::kDmaWaves * i;
+    lvalid[i] = dma_wave && j < S::kBlocks;
     // (the region follows from the block alone: regions are whole 1 KB blocks)
     const int jb = (lvalid[i] ? j : 0) * 1024;
     int q2, r, cs, gc;
@@ -303,7 +309,7 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
       for (int i = 0; i < S::kPerWave; ++i) {
         if (!lvalid[i]) break;   // (uniform; only the last load of a wave can be surplus)
         const u32x4 rs = rsrc_words(lbase[i] + row0 * lstride[i], rows * lstride[i]);
-        lds_dma16(rs, loff[i], lb + (w + kWaves * i) * 1024);
+        lds_dma16(rs, loff[i], lb + (dw + S::kDmaWaves * i) * 1024);
       }
     } else {
       if (ti >= n_tiles) return;
@@ -313,7 +319,7 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
 #pragma unroll
       for (int i = 0; i < S::kPerWave; ++i) {
         if (!lvalid[i]) continue;
-        const int j = w + kWaves * i;
+        const int j = dw + S::kDmaWaves * i;
         const int r = (int)(loff[i] / lstride[i]);
         const int t = t0 + min(r, last);
         const int pi = t / a.page_size;
@@ -327,7 +333,8 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
   };
   // tile s has landed (this wave's loads): the loads of the A - 1 tiles after it may stay in
   // flight
-  // (blocks are dealt round-robin, so a wave has kPerWave or kPerWave - 1 of them)
+  // (blocks are dealt round-robin, so a loading wave has kPerWave or kPerWave - 1 of them;
+  // the P.V waves have none and wait for nothing here)
   const bool full_share = lvalid[S::kPerWave - 1];
   auto wait_tile = [&] {
     if constexpr (A == 2) {
