@@ -135,10 +135,12 @@ typedef struct da_problem {
  *    cache or pages of a power of two >= 32 keys) the depth pairs Dqk/Dv 128/128,
  *    192/128 and 256/256, with the K/V cache in bf16 or fp8 and optionally the 64 rotary
  *    columns stored apart in bf16 (nope_depth 128 or 192);
- *  - with one kv head, on the shared-kv-head kernel (bf16, any number of q heads and
+ *  - with one kv head, on the shared-kv-head kernel (bf16 q, any number of q heads and
  *    q_len): latent 576/512 with V = the first 512 K columns (v_is_k_prefix), and
  *    256/256 with V of its own when q_len x Hq > 16; the 64 rotary columns in the K rows
- *    or stored apart in bf16 (nope_depth 512 or 192). */
+ *    or stored apart in bf16 (nope_depth 512 or 192). Both also over an fp8 cache with the
+ *    rotary columns apart and a contiguous cache or pages of a power of two >= 32 keys
+ *    (a V that is the K prefix takes the K scales: v_scale NULL). */
 int da_supported(const da_problem* p);
 
 /* Split selection (FA4Config, with_splitk: partitions of the K/V sequence).

@@ -89,8 +89,8 @@ int check_problem(const da_problem* p, Variant* var) {
   // contractions over all q heads). MLA-style latent 576/512 with V = the first 512 nope
   // columns, and GLM-style 256/256 (nope 192, V of its own) once q_len x group exceeds the
   // 16 MFMA columns of the GQA kernel; the 64 rotary columns in the K rows or stored apart.
-  // The latent form also takes an fp8 cache: nope codes with per-token K scales, the rotary
-  // columns apart in bf16.
+  // Both take an fp8 cache: nope codes (and a V of its own) with per-token scales, the
+  // rotary columns apart in bf16.
   const bool latent = p->qk_depth == 576 && p->ov_depth == 512;
   const bool glm_mqa = p->qk_depth == 256 && p->ov_depth == 256 && !p->v_is_k_prefix && p->num_kv_heads == 1 &&
                        ql * g > 16;
@@ -106,13 +106,13 @@ int check_problem(const da_problem* p, Variant* var) {
     if (p->nope_depth > 0 && p->rope_dtype != DA_BF16)
       return fail(DA_EUNSUPPORTED, "rotary columns stored apart must be bf16 (rope_dtype %d)", p->rope_dtype);
     if (p->kv_dtype == DA_FP8_E4M3 &&
-        (!latent || p->nope_depth != 512 ||
+        (p->nope_depth != nope_apart ||
          (p->page_size != 0 && !(p->page_size >= kTileKeys && (p->page_size & (p->page_size - 1)) == 0))))
       return fail(DA_EUNSUPPORTED,
-                  "fp8 on the shared-kv-head kernel: the latent form (576/512) with the 64 rotary columns "
-                  "stored apart in bf16 (nope_depth 512) and a contiguous cache or pages of a power of two "
-                  ">= 32 keys (got depth %d/%d, nope_depth %d, page_size %d)",
-                  p->qk_depth, p->ov_depth, p->nope_depth, p->page_size);
+                  "fp8 on the shared-kv-head kernel: the 64 rotary columns stored apart in bf16 (nope_depth "
+                  "%d) and a contiguous cache or pages of a power of two >= 32 keys (got depth %d/%d, "
+                  "nope_depth %d, page_size %d)",
+                  nope_apart, p->qk_depth, p->ov_depth, p->nope_depth, p->page_size);
     *var = kVarShared;
     return DA_OK;
   }

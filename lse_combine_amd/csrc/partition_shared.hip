@@ -63,8 +63,9 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 
 // Depths of one instantiation: DN nope columns and DR rotary columns make the q.K depth; V
 // has DV columns and is either the first DV nope columns (SHARED) or a cache of its own.
-// F8: the nope columns are E4M3 codes with a per-token K scale (the rotary columns stay bf16,
-// stored apart); V, a prefix of them, is read as code x the token's K scale.
+// F8: the nope columns (and a V of its own) are E4M3 codes with per-token scales; the rotary
+// columns stay bf16, stored apart. A V that is a prefix of the nope columns is read as code x
+// the token's K scale, a V of its own as code x its V scale.
 template <int DN_, int DR_, int DV_, bool SHARED_, bool F8_ = false>
 struct SShape {
   static constexpr int DN = DN_, DR = DR_, DV = DV_;
@@ -72,8 +73,10 @@ struct SShape {
   static constexpr int DQK = DN + DR;
   static constexpr int NJ = DQK / 32;            // 32-deep k-steps of q.K
   static constexpr int NJN = DN / 32;            // ... over the nope columns
-  static constexpr int kNRow = F8 ? DN : DN * 2; // LDS bytes of one row, per region
+  static constexpr int kElt = F8 ? 1 : 2;        // bytes per cached nope / V element
+  static constexpr int kNRow = DN * kElt;        // LDS bytes of one row, per region
   static constexpr int kRRow = DR * 2;
+  static constexpr int kVSrcRow = DV * kElt;     // ... of the V region (a V of its own)
   static constexpr int kVCols = DV / 4;          // V columns of one P.V wave
   static constexpr int kDB = kVCols / 16;        // its 16-deep O blocks
   // rows of the tile that the transposing V reads see: the nope rows (bf16, SHARED), the V
@@ -82,8 +85,10 @@ struct SShape {
   static constexpr int kNBytes = kTile * kNRow;  // region offsets inside a slot
   static constexpr int kRBytes = kTile * kRRow;
   static constexpr int kVOff = SHARED ? 0 : kNBytes + kRBytes;
-  static constexpr int kScOff = kNBytes + kRBytes + (SHARED ? 0 : kTile * DV * 2);   // F8: K scales
-  static constexpr int kSlot = kScOff + (F8 ? 1024 : 0);
+  static constexpr int kVReadOff = F8 ? 0 : kVOff;   // the V rows the transposing reads see
+  static constexpr int kScOff = kNBytes + kRBytes + (SHARED ? 0 : kTile * kVSrcRow);   // F8: K scales
+  static constexpr int kVScOff = kScOff + 1024;                                         // F8, own V: V scales
+  static constexpr int kSlot = kScOff + (F8 ? (SHARED ? 1024 : 2048) : 0);
   static constexpr int kBlocks = kSlot / 1024;   // 1 KB direct-to-LDS loads per tile
   // the tile's loads are issued by the four q.K waves (the P.V waves, with the most
   // matrix-core work per tile, only consume): 61.0 against 63.5 us on the latent workload
@@ -92,7 +97,8 @@ struct SShape {
   static_assert(NJ % 2 == 0 && DN % 64 == 0 && DR % 64 == 0 && DV % 64 == 0, "depths");
   static_assert(kNBytes % 1024 == 0 && kRBytes % 1024 == 0 && kSlot % 1024 == 0, "1 KB load blocks");
   static_assert(!SHARED || DV <= DN, "a shared V is a prefix of the nope columns");
-  static_assert(!F8 || (SHARED && DN == 512), "fp8: the latent form (nope rows of 512 codes, V a prefix)");
+  static_assert(!F8 || (SHARED && DN == 512) || (!SHARED && DN == 192 && DV == 256),
+                "fp8: the latent form, or nope 192 with a V of 256 of its own");
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -130,9 +136,13 @@ static_assert(sizeof(XArrays) <= kPBytes, "exchange arrays fit a P buffer");
 //    distinct over 8 rows); the XOR spans 16-chunk groups.
 //  - rows of 128 bytes mod 256 (rotary 128, GLM nope 384): consecutive rows alternate bank
 //    halves, so swz(r) = (r >> 1) & 7; the XOR stays within 8-chunk groups.
+//  - rows of 192 bytes (GLM nope as fp8 codes): not swizzled. The stride is 48 banks, so
+//    16 rows fall on 4 bank phases: their 8-byte operand reads conflict four ways (six such
+//    reads per tile and wave, a few dozen clocks).
 template <int RB>
 __device__ __forceinline__ int swz(int r) {
-  static_assert(RB % 256 == 0 || RB % 256 == 128, "row strides of 128 + 256 k or 256 k bytes");
+  if constexpr (RB == 192) return 0;
+  static_assert(RB == 192 || RB % 256 == 0 || RB % 256 == 128, "row strides of 128 + 256 k, 256 k or 192 bytes");
   if constexpr (RB % 256 == 0) return ((r & 7) << 1) | ((r >> 3) & 1);
   else return (r >> 1) & 7;
 }
@@ -251,7 +261,7 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
   const char* kc = (const char*)a.k;
   const char* vc = (const char*)a.v;
   const uint32_t krow = (uint32_t)a.Dk * (S::F8 ? 1 : 2);   // bytes between tokens in k_cache
-  const uint32_t vrow = (uint32_t)a.v_row_len * 2;    // ... in v_cache
+  const uint32_t vrow = (uint32_t)a.v_row_len * S::kElt;   // ... in v_cache
   // per load i of this wave: region base and row stride (uniform), lane offset
   const char* lbase[S::kPerWave];
   uint32_t lstride[S::kPerWave], loff[S::kPerWave];
@@ -272,13 +282,15 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
       q2 = jb - S::kNBytes + lane * 16, lbase[i] = rope_base, lstride[i] = rope_row_bytes;
       r = q2 / S::kRRow, cs = (q2 - r * S::kRRow) >> 4, gc = cs ^ swz<S::kRRow>(r);
     } else if (S::F8 && jb >= S::kScOff) {
-      // the tile's 32 K scales (4 bytes per token, tokens innermost): lanes 0-7 load them,
-      // the rest fall outside the buffer range
-      q2 = 0, lbase[i] = (const char*)a.k_scale, lstride[i] = 4u;
+      // the tile's 32 K (then V) scales (4 bytes per token, tokens innermost): lanes 0-7 load
+      // them, the rest fall outside the buffer range. Without V scales the V block repeats the
+      // K scales and is not used.
+      const bool vsc = jb >= S::kVScOff && a.v_scale;
+      q2 = 0, lbase[i] = (const char*)(vsc ? a.v_scale : a.k_scale), lstride[i] = 4u;
       r = 4 * lane, cs = 0, gc = 0;
     } else {
       q2 = jb - S::kNBytes - S::kRBytes + lane * 16, lbase[i] = vc, lstride[i] = vrow;
-      r = q2 / (S::DV * 2), cs = (q2 - r * (S::DV * 2)) >> 4, gc = cs ^ swz<S::DV * 2>(r);
+      r = q2 / S::kVSrcRow, cs = (q2 - r * S::kVSrcRow) >> 4, gc = cs ^ swz<S::kVSrcRow>(r);
     }
     loff[i] = (uint32_t)r * lstride[i] + 16u * (uint32_t)gc;
   }
@@ -421,6 +433,7 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
 #pragma unroll
       for (int bi = 0; bi < 2; ++bi) acc[bi][0] = acc[bi][1] = f32x4{0.f, 0.f, 0.f, 0.f};
       f32x4 ks = f32x4{1.f, 1.f, 1.f, 1.f};   // F8: K scales of the lane's 4 keys
+      f32x4 vs = f32x4{1.f, 1.f, 1.f, 1.f};   // F8: their V scales (the K scales for a shared V)
       if constexpr (S::F8) {
         // all nope codes (2 registers per step) and the rotary operands are requested first;
         // a step's codes are widened to bf16 just before its products. The nope and rotary
@@ -432,6 +445,11 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
 #pragma unroll
         for (int j = S::NJN; j < S::NJ; ++j) krp[j - S::NJN] = load_k(KL, j);
         ks = *(const DA_LDS f32x4*)(KL + S::kScOff + 4 * (16 * kh + 4 * qd));
+        if constexpr (!S::SHARED) {
+          if (a.v_scale) vs = *(const DA_LDS f32x4*)(KL + S::kVScOff + 4 * (16 * kh + 4 * qd));
+        } else {
+          vs = ks;
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < S::NJN; ++j) {
@@ -507,9 +525,9 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
         for (int i = 0; i < 4; ++i) {
           pr[bi][i] = exp2_fast(fmaf(pr[bi][i], c, -mc));
           l_lane[bi] += pr[bi][i];
-          // F8: V is code x the token's K scale; the scale goes into P.V's operand, l sums
-          // the unscaled p
-          if constexpr (S::F8) pr[bi][i] *= ks[i];
+          // F8: V is code x the token's V scale (its K scale for a shared V); the scale goes
+          // into P.V's operand, l sums the unscaled p
+          if constexpr (S::F8) pr[bi][i] *= vs[i];
         }
         // hi and lo parts of P into the buffer (8 bytes each per lane)
         const uint32_t h0 = pack_bf16x2(pr[bi][0], pr[bi][1]), h1 = pack_bf16x2(pr[bi][2], pr[bi][3]);
@@ -574,7 +592,7 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
     // and 16 + 4 qd .. +3 (the k-slot order of the P buffer); that is chunk 2 D + ((n & 3) >> 1)
     // of rows ra and ra + 16, ra = 4 qd + (n >> 2), read transposed
     const int ra = 4 * qd + (n >> 2);
-    const int v_off = S::kVOff + ra * S::kVRow + (n & 1) * 8;
+    const int v_off = S::kVReadOff + ra * S::kVRow + (n & 1) * 8;
     auto load_v = [&](const DA_LDS char* KL, int db) {
       const int ch = 2 * ((S::F8 ? 0 : v * S::kDB) + db) + ((n & 3) >> 1);
       const DA_LDS char* pa = KL + v_off + 16 * (ch ^ swz<S::kVRow>(ra));
@@ -594,16 +612,22 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
     // then see like a bf16 tile. Only this wave writes and reads the copy.
     auto widen_v = [&](int s) {
       if constexpr (S::F8) {
-        const char* src = sm.tile[s % R];
+        // the wave's kVCols codes of each row: kWC 16-code chunks, half of them per lane
+        // (lane: row lane / 2, chunks (lane & 1) kWC / 2 ...); source rows are the nope rows
+        // (shared V) or the V region's rows, each with its region's swizzle
+        constexpr int kWC = S::kVCols / 16;
+        constexpr int kSrcRow = S::SHARED ? S::kNRow : S::kVSrcRow;
+        const char* src = sm.tile[s % R] + S::kVOff;
         char* dst = sm.vpriv[v];
         const int r = lane >> 1, h = lane & 1;
-        const int fs = swz<S::kNRow>(r), fd = swz<S::kVRow>(r);
-        u32x4 cw[4];
+        const int fs = swz<kSrcRow>(r), fd = swz<S::kVRow>(r);
+        u32x4 cw[kWC / 2];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) cw[k] = *(const u32x4*)(src + r * S::kNRow + 16 * ((8 * v + 4 * h + k) ^ fs));
+        for (int k = 0; k < kWC / 2; ++k)
+          cw[k] = *(const u32x4*)(src + r * kSrcRow + 16 * ((kWC * v + (kWC / 2) * h + k) ^ fs));
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int bc = 2 * (4 * h + k);
+        for (int k = 0; k < kWC / 2; ++k) {
+          const int bc = 2 * ((kWC / 2) * h + k);
           *(bf16x8*)(dst + r * S::kVRow + 16 * (bc ^ fd)) = fp8x8_to_bf16x8(cw[k][0], cw[k][1]);
           *(bf16x8*)(dst + r * S::kVRow + 16 * ((bc + 1) ^ fd)) = fp8x8_to_bf16x8(cw[k][2], cw[k][3]);
         }
@@ -785,6 +809,10 @@ hipError_t launch_partition_shared(const PartArgs& a, int page_mode, hipStream_t
     if (a.Dqk == 576 && a.Dv == 512 && a.v == a.k && a.Dk == 512 && rope_apart && a.k_scale && !a.v_scale &&
         page_mode != kPagedGeneral)
       return launch_shape<SShape<512, 64, 512, true, true>>(a, page_mode, s);
+    // one kv head with GLM widths: nope 192 and V 256 (its own, optional V scales) as codes
+    if (a.Dqk == 256 && a.Dv == 256 && a.v != a.k && a.Dk == 192 && rope_apart && a.k_scale &&
+        page_mode != kPagedGeneral)
+      return launch_shape<SShape<192, 64, 256, false, true>>(a, page_mode, s);
     return hipErrorInvalidValue;
   }
   if (a.Dqk == 576 && a.Dv == 512 && a.v == a.k && a.Dk == (rope_apart ? 512 : 576))

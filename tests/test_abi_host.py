@@ -230,7 +230,10 @@ def test_probe_argument_checks():
     (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1,
           nope_depth=512, rope_dtype=1, page_size=48, max_pages_per_seq=100), DA_EUNSUPPORTED),
     (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=256, ov_depth=256, nope_depth=192,
-          rope_dtype=1), DA_EUNSUPPORTED),                                   # one-kv-head GLM widths
+          rope_dtype=1), DA_OK),                                             # one-kv-head GLM widths
+    (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=256, ov_depth=256), DA_EUNSUPPORTED),   # rotary inline
+    (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=256, ov_depth=256, nope_depth=192,
+          rope_dtype=1, page_size=48, max_pages_per_seq=100), DA_EUNSUPPORTED),
     (dict(kv_dtype=7), DA_EINVAL),
 ])
 def test_fp8_cache_support(lib, kw, code):
