@@ -191,8 +191,10 @@ int decode_attn_splitk_noalloc(const da_problem* p, const void* q, const void* k
  * itself in on an arrival counter; the last one merges all partials of its heads and
  * writes out / lse_out / o_f32_out, then resets the counter. This saves the second
  * launch. Applied by every partition kernel (every depth pair, cache dtype and partition
- * count); the outputs are the same as decode_attn_splitk's. Rows of a sequence without
- * keys are written too (O = 0, LSE = -inf), by one workgroup that holds no keys. Same arguments and workspace size as decode_attn_splitk,
+ * count) while each partial array of the workspace stays below 2 GB (beyond that the step
+ * runs as decode_attn_splitk); the outputs are the same as decode_attn_splitk's. Rows of
+ * a sequence without keys are written too (O = 0, LSE = -inf), by one workgroup that holds
+ * no keys. Same arguments and workspace size as decode_attn_splitk,
  * with one more rule: the workspace must be zero-filled before its first use with this
  * function (the counters live in it and every call leaves them at zero), and calls that
  * share a workspace must not overlap. */

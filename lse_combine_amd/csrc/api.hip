@@ -439,7 +439,9 @@ int run_splitk(const da_problem* p, const void* q, const da_kv& kv, const int32_
   a.o32 = o_f32_out;
   a.direct_single = 1;
   set_kv_args(p, kv, &a);
-  const bool fuse = fused;
+  // (the fused combine addresses each partial array with 32-bit byte offsets below 2 GB;
+  // beyond that the step takes the combine launch, with the same results)
+  const bool fuse = fused && o_off < (size_t(1) << 31) && cnt_off - o_off < (size_t(1) << 31);
   if (fuse) a.counters = (int32_t*)((char*)workspace + cnt_off);
   if ((r = launch_partition(p, var, a, s, cus))) return r;
   if (!fuse && (r = launch_combine(p, seq_lens, scale, C, P, po, pml, out, lse_out, o_f32_out, 1, s))) return r;

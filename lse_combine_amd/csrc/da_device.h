@@ -168,14 +168,28 @@ __device__ __forceinline__ int64_t share_owner(int64_t t, int64_t U, int64_t W) 
   return ((t + 1) * W + U - 1) / U - 1;
 }
 
+// Device-coherent accesses for the fused combine's partials: 16- and 8-byte buffer accesses
+// with cache policy SC1 (the code this chip's agent-scope atomics use): a store is written
+// through the XCD's L2 and counts as complete once every XCD can see it; a load is served
+// coherently, never from a stale line of the reading XCD's L2. Offsets are bytes from the
+// start of the partial array (the fused path is used while the arrays stay below 4 GB).
+constexpr int kCpolSC1 = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t whole_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, kRsrcWord3);
+}
 // Folds partials j = j0, j0 + step, ... (< P) of one (row, 4-wide depth slice) unit into a
 // running (M, Ls, acc) with the combine's weights l_j exp2((m_j - M) c); when a batch
 // raises the running max, what was summed so far is rescaled (fa4_splitk_combine_write,
 // first paragraph). ml / po point at partial 0 of the row; partials are `stride` partial
 // rows apart; loads are issued kBatch at a time. Partials with l_j == 0 weigh nothing.
-template <int DV, int kBatch = 8>
+// DEV: the partials were published by device-coherent stores, and ml_base / po_base are the
+// starts of their arrays.
+template <int DV, int kBatch = 8, bool DEV = false>
 __device__ __forceinline__ void fold_partials(const float2* ml, const float* po, int64_t stride, int P, int j0,
-                                              int step, float c, float& M, float& Ls, f32x4& acc) {
+                                              int step, float c, float& M, float& Ls, f32x4& acc,
+                                              const float* ml_base = nullptr, const float* po_base = nullptr) {
+  __amdgpu_buffer_rsrc_t rml, ro;
+  if constexpr (DEV) rml = whole_rsrc(ml_base), ro = whole_rsrc(po_base);
   for (int p0 = j0; p0 < P; p0 += step * kBatch) {
     float2 v[kBatch];
     f32x4 o[kBatch];
@@ -183,8 +197,18 @@ __device__ __forceinline__ void fold_partials(const float2* ml, const float* po,
     for (int i = 0; i < kBatch; ++i) {
       const int p = p0 + i * step;
       const bool in = p < P;
-      v[i] = in ? ml[p * stride] : make_float2(-INFINITY, 0.f);
-      o[i] = in ? *(const f32x4*)(po + p * stride * DV) : f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (DEV) {
+        // (partials published by the fused combine's device-coherent stores)
+        const uint32_t mo = (uint32_t)((const char*)(ml + p * stride) - (const char*)ml_base);
+        const uint32_t oo = (uint32_t)((const char*)(po + p * stride * DV) - (const char*)po_base);
+        v[i] = in ? __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rml, mo, 0, kCpolSC1))
+                  : make_float2(-INFINITY, 0.f);
+        o[i] = in ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, oo, 0, kCpolSC1))
+                  : f32x4{0.f, 0.f, 0.f, 0.f};
+      } else {
+        v[i] = in ? ml[p * stride] : make_float2(-INFINITY, 0.f);
+        o[i] = in ? *(const f32x4*)(po + p * stride * DV) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
     float mb = M;
 #pragma unroll
@@ -241,6 +265,15 @@ __device__ __forceinline__ void store_unit(const PartArgs& a, int b, int hq, int
   } else {
     // fixed chunks: p is the partition of sequence b; equal shares: p is the slot
     const int64_t pr = a.workers ? (int64_t)p * a.Hq + hq : row * a.max_splits + p;
+    if (a.counters) {
+      // fused combine: the partial is read by whichever workgroup completes the count
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), whole_rsrc(a.part_o),
+                                             (uint32_t)((pr * a.Dv + d0) * 4), 0, kCpolSC1);
+      if (write_ml)
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, make_float2(M, Lsum)), whole_rsrc(a.part_ml),
+                                              (uint32_t)(pr * 8), 0, kCpolSC1);
+      return;
+    }
     *(f32x4*)(a.part_o + pr * a.Dv + d0) = o;
     if (write_ml) {
       float2 ml;

@@ -347,16 +347,15 @@ __global__ __launch_bounds__(kWaves * 64, (FmaLds<T, GMAX>::kMinWaves)) void par
   }
 
   if (!a.counters || direct) return;
-  // Fused combine: publish the partial (every wave's stores complete, then one device-scope
-  // release), count in on the (sequence, kv head) counter; the workgroup that completes the
-  // count acquires the others' partials and writes the g final rows.
+  // Fused combine, published as in the matrix-core kernel: the partial stores (device-
+  // coherent, cache policy SC1) of every wave complete before the barrier, then one count on
+  // the (sequence, kv head) counter; the workgroup that completes the count reads the
+  // others' partials with SC1 loads and writes the g final rows.
   wait_vm<0>();
   __syncthreads();
   int* cnt = a.counters + (int64_t)b * a.Hkv + kvh;
   if (tid == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const int last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == P_b - 1;
-    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     last_s = last ? 1 : 0;
   }
   __syncthreads();
@@ -366,8 +365,9 @@ __global__ __launch_bounds__(kWaves * 64, (FmaLds<T, GMAX>::kMinWaves)) void par
     const int64_t row = (int64_t)b * a.Hq + kvh * g + h;
     float M = -INFINITY, Ls = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    fold_partials<kD>((const float2*)a.part_ml + row * a.max_splits, a.part_o + row * a.max_splits * kD + d0, 1,
-                      P_b, 0, 1, a.c, M, Ls, acc);
+    fold_partials<kD, 8, true>((const float2*)a.part_ml + row * a.max_splits, a.part_o + row * a.max_splits * kD + d0, 1,
+                      P_b, 0, 1, a.c, M, Ls, acc,
+        a.part_ml, a.part_o);
     write_row_unit(a.out, a.o32, a.lse, row, kD, d0, M, Ls, acc, a.scale);
   }
   if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -209,13 +209,17 @@ __device__ __forceinline__ void merge_key_splits(const PartArgs& a, const WaveIn
 // final bf16 rows, LSE and fp32 O of the group's heads, then returns the counter to zero for
 // the next call. The counters (one int per (sequence, group)) must be zero before the first
 // call.
-// Publication: every wave waits until its own partial stores are complete (vmcnt(0)) before
-// the workgroup barrier, so that after the barrier all of them have reached the XCD's L2;
-// one thread then releases them at device scope (on this chip a write-back of that L2, done
-// once per workgroup rather than once per wave) and increments the counter. The workgroup
-// that completes the count saw every other workgroup's increment, each made after that
-// workgroup's release; its thread 0 acquires (an invalidation of its L2 and vector cache)
-// before the barrier after which its waves read the partials.
+// Publication without cache-wide fences: in fused mode every partial is stored with cache
+// policy SC1 (store_unit), i.e. written through the XCD's L2, and such a store counts as
+// complete only once it is visible to every XCD. Every wave waits until its own partial
+// stores are complete (vmcnt(0)) before the workgroup barrier, and only after that barrier
+// does one thread increment the counter (an agent-scope atomic). The workgroup that
+// completes the count therefore sees every partial of the set already visible device-wide;
+// its waves read them, after a second barrier, with SC1 loads, which never return a stale
+// line of their own XCD's L2 (that L2 may hold lines of these addresses from an earlier
+// call). The usual agent-scope release/acquire pair would instead write back and invalidate
+// the whole L2 of the XCD in every workgroup; the SC1 stores and loads cost the same
+// number of instructions as plain ones.
 // The fold uses every thread of the workgroup: NT / S (row, 4-wide slice) units at a time,
 // S threads per unit splitting the partitions (merged through LDS like the combine launch).
 template <class S>
@@ -226,9 +230,7 @@ __device__ __forceinline__ void fused_combine(const PartArgs& a, const WaveInfo&
   __syncthreads();
   int* cnt = a.counters + (int64_t)b * groups_of(a, HG) + kg;
   if (tid == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const int last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == count - 1;
-    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     *flag_s = last ? 1 : 0;
   }
   __syncthreads();
@@ -265,8 +267,9 @@ __device__ __forceinline__ void fused_combine(const PartArgs& a, const WaveInfo&
     float M = -INFINITY, Ls = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (valid)
-      fold_partials<DV>((const float2*)a.part_ml + first, a.part_o + first * DV + d0, stride, count, sub, SUB, a.c,
-                        M, Ls, acc);
+      fold_partials<DV, 8, true>((const float2*)a.part_ml + first, a.part_o + first * DV + d0, stride, count, sub, SUB, a.c,
+                        M, Ls, acc,
+        a.part_ml, a.part_o);
     if (SUB > 1) {
       if (sub < SUB) {
         sM[sub * UNITS + ui] = M;

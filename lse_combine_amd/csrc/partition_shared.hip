@@ -704,19 +704,18 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
   }
 
   if (!a.counters || direct) return;
-  // Fused combine (fa4_splitk_combine_write, fourth paragraph): every wave's partial stores
-  // complete, one agent-scope release and a count on the (sequence, column block) counter;
-  // the workgroup that completes the count acquires the others' partials and folds the
-  // block's rows with every thread (S threads per (row, 4-wide slice) unit splitting the
+  // Fused combine (fa4_splitk_combine_write, fourth paragraph), published as in the
+  // matrix-core kernel: every wave's partial stores (device-coherent, cache policy SC1)
+  // complete before the barrier, then one count on the (sequence, column block) counter; the
+  // workgroup that completes the count reads the others' partials with SC1 loads and folds
+  // the block's rows with every thread (S threads per (row, 4-wide slice) unit splitting the
   // partitions, merged through LDS as in the combine launch).
   wait_vm<0>();
   __syncthreads();
   int* cnt = a.counters + (int64_t)b * gridDim.y + cblk;
   int* flag_s = (int*)sm.pbuf[0];
   if (tid == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const int last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == P_b - 1;
-    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     *flag_s = last ? 1 : 0;
   }
   __syncthreads();
@@ -740,8 +739,9 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
       float M = -INFINITY, Ls = 0.f;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       if (valid)
-        fold_partials<S::DV>((const float2*)a.part_ml + row * a.max_splits, a.part_o + row * a.max_splits * S::DV + d0,
-                             1, P_b, sub, SUB, c, M, Ls, acc);
+        fold_partials<S::DV, 8, true>((const float2*)a.part_ml + row * a.max_splits, a.part_o + row * a.max_splits * S::DV + d0,
+                             1, P_b, sub, SUB, c, M, Ls, acc,
+        a.part_ml, a.part_o);
       if (SUB > 1) {
         sM[sub * UNITS + ui] = M;
         sL[sub * UNITS + ui] = Ls;
