@@ -265,7 +265,8 @@ def main():
             "qk_depth": prob.qk_depth, "ov_depth": Dv, "nope_depth": prob.nope_depth, "page_size": case.page_size,
             "keys": tokens, "max_seq_len": int(case.seq_lens.max()),
             "num_splits": case.num_splits, "chunk_tokens": chunk, "max_splits": max_splits, "kernel": args.kernel,
-            "combine": args.combine,
+            "combine": args.combine if args.combine == "separate" or api.fused_applies(prob, case.num_splits)
+                       else "fused entry point (runs the combine launch: fold beyond 1 MiB)",
             "kv_bytes": kv_bytes,
         },
         "roofline": {

@@ -159,6 +159,15 @@ int da_choose_splits(const da_problem* p, int32_t num_splits, int32_t num_cus,
  * (same num_splits / num_cus rule as da_choose_splits with num_cus queried). */
 int da_workspace_bytes(const da_problem* p, int32_t num_splits, size_t* bytes);
 
+/* 1 if decode_attn_splitk_fused merges the partials in pass 1 for this problem and
+ * num_splits, 0 if it runs the combine launch instead, or an error code as da_supported.
+ * It merges in pass 1 when the partial outputs one last-arriving workgroup must read stay
+ * within 1 MiB (max_splits, or every worker under equal shares, times the rows of its head
+ * group or 64-column block, times Dv x 4 bytes): one workgroup reads them alone, while the
+ * combine launch spreads them over the chip. Each partial array must also stay below 2 GB.
+ * (num_splits and the device's compute units as da_workspace_bytes.) */
+int da_fused_applies(const da_problem* p, int32_t num_splits);
+
 /* The whole decode step: partition kernel, then LSE combine.
  * q, k_cache, v_cache, page_table (NULL iff page_size == 0), seq_lens: device, read only.
  * scale: finite and > 0 (softmax scale, e.g. 1/sqrt(Dqk)).
@@ -191,10 +200,10 @@ int decode_attn_splitk_noalloc(const da_problem* p, const void* q, const void* k
  * itself in on an arrival counter; the last one merges all partials of its heads and
  * writes out / lse_out / o_f32_out, then resets the counter. This saves the second
  * launch. Applied by every partition kernel (every depth pair, cache dtype and partition
- * count) while each partial array of the workspace stays below 2 GB (beyond that the step
- * runs as decode_attn_splitk); the outputs are the same as decode_attn_splitk's. Rows of
- * a sequence without keys are written too (O = 0, LSE = -inf), by one workgroup that holds
- * no keys. Same arguments and workspace size as decode_attn_splitk,
+ * count) where da_fused_applies says so; otherwise the step runs as decode_attn_splitk.
+ * The outputs are the same either way. Rows of a sequence without keys are written too
+ * (O = 0, LSE = -inf), by one workgroup that holds no keys. Same arguments and workspace
+ * size as decode_attn_splitk,
  * with one more rule: the workspace must be zero-filled before its first use with this
  * function (the counters live in it and every call leaves them at zero), and calls that
  * share a workspace must not overlap. */

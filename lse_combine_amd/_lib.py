@@ -44,6 +44,7 @@ _SIGS = {
     "da_choose_splits": (ctypes.c_int, [ctypes.POINTER(DaProblem), _I32, _I32,
                                         ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
     "da_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(DaProblem), _I32, ctypes.POINTER(ctypes.c_size_t)]),
+    "da_fused_applies": (ctypes.c_int, [ctypes.POINTER(DaProblem), _I32]),
     "decode_attn_splitk": (ctypes.c_int, [ctypes.POINTER(DaProblem), _P, _P, _P, _P, _P, ctypes.c_float, _I32,
                                           _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "decode_attn_splitk_noalloc": (ctypes.c_int, [ctypes.POINTER(DaProblem), _P, _P, _P, _P, _P, ctypes.c_float,

@@ -143,6 +143,16 @@ def workspace_bytes(problem: DaProblem, num_splits=0):
     return n.value
 
 
+def fused_applies(problem: DaProblem, num_splits=0):
+    """True if the fused entry point merges the partials in pass 1 for this problem (else it
+    runs the combine launch, with the same results)."""
+    lib = _lib.load()
+    r = lib.da_fused_applies(ctypes.byref(problem), num_splits)
+    if r < 0:
+        check(r)
+    return r == 1
+
+
 def decode_attn(q, k_cache, v_cache, page_table, seq_lens, scale, num_splits=0, *, page_size=0,
                 max_seq_len=None, v_is_k_prefix=False, ov_depth=None, out=None, lse=None, o32=None,
                 return_lse=False, return_o32=False, workspace=None, kernel="auto", fused=False,

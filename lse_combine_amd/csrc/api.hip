@@ -406,6 +406,38 @@ void set_kv_args(const da_problem* p, const da_kv& kv, da::PartArgs* a) {
   a->Dk = p->nope_depth > 0 ? p->nope_depth : p->qk_depth;
 }
 
+// Fused combine: the last-arriving workgroup of a (sequence, head group) reads the partials
+// of every row of the group alone, so the fold is kept to sets of at most kFusedFoldBytes of
+// partial O (for the largest partition count the schedule allows a row: max_splits, or
+// every worker under equal shares). A larger set (e.g. one long sequence under equal shares,
+// 4 MB on one CU) takes the combine launch, which spreads the same fold over the chip.
+constexpr int64_t kFusedFoldBytes = 1 << 20;
+
+bool fused_fold_fits(const da_problem* p, Variant var, int32_t C, int32_t P, int cus) {
+  const int64_t ql = q_len_of(p), g = p->num_q_heads / p->num_kv_heads;
+  int64_t rows;
+  if (var == kVarFma) {
+    rows = ql * g;   // (sequence, kv head)
+  } else if (var == kVarMfma) {
+    int HG, KS, W;
+    if (C == 0) share_shape(p, cus, &HG, &KS, &W);
+    else mfma_shape(p, P, cus, &HG, &KS);
+    rows = ql * g * HG;   // (sequence, head group)
+  } else {
+    rows = std::min<int64_t>(64, rows_per_seq(p));   // (sequence, block of 64 columns)
+  }
+  return (int64_t)P * rows * p->ov_depth * 4 <= kFusedFoldBytes;
+}
+
+// Whether decode_attn_splitk_fused folds in pass 1 for this schedule and workspace layout:
+// the fold fits, and each partial array stays below 2 GB (the fused path addresses them with
+// 32-bit byte offsets).
+bool fused_applies(const da_problem* p, Variant var, int32_t C, int32_t P, int cus) {
+  size_t ml_off, o_off, cnt_off, total;
+  ws_layout(p, C, P, &ml_off, &o_off, &cnt_off, &total);
+  return o_off < (size_t(1) << 31) && cnt_off - o_off < (size_t(1) << 31) && fused_fold_fits(p, var, C, P, cus);
+}
+
 // The whole step. With `fused`, the partition kernel's last-arriving workgroup of each
 // (sequence, head group) combines (no second launch). The results are the same either way.
 int run_splitk(const da_problem* p, const void* q, const da_kv& kv, const int32_t* page_table, const int32_t* seq_lens,
@@ -439,9 +471,9 @@ int run_splitk(const da_problem* p, const void* q, const da_kv& kv, const int32_
   a.o32 = o_f32_out;
   a.direct_single = 1;
   set_kv_args(p, kv, &a);
-  // (the fused combine addresses each partial array with 32-bit byte offsets below 2 GB;
-  // beyond that the step takes the combine launch, with the same results)
-  const bool fuse = fused && o_off < (size_t(1) << 31) && cnt_off - o_off < (size_t(1) << 31);
+  // (where the fused fold does not apply the step takes the combine launch, with the same
+  // results)
+  const bool fuse = fused && fused_applies(p, var, C, P, cus);
   if (fuse) a.counters = (int32_t*)((char*)workspace + cnt_off);
   if ((r = launch_partition(p, var, a, s, cus))) return r;
   if (!fuse && (r = launch_combine(p, seq_lens, scale, C, P, po, pml, out, lse_out, o_f32_out, 1, s))) return r;
@@ -519,6 +551,18 @@ int da_workspace_bytes(const da_problem* p, int32_t num_splits, size_t* bytes) {
   size_t a, b, c;
   ws_layout(p, C, P, &a, &b, &c, bytes);
   return ok();
+}
+
+int da_fused_applies(const da_problem* p, int32_t num_splits) {
+  Variant v;
+  int r = check_problem(p, &v);
+  if (r) return r;
+  const int cus = device_num_cus();
+  int32_t C, P;
+  r = choose(p, v, num_splits, cus, &C, &P);
+  if (r) return r;
+  ok();
+  return fused_applies(p, v, C, P, cus) ? 1 : 0;
 }
 
 int decode_attn_splitk(const da_problem* p, const void* q, const void* k_cache, const void* v_cache,

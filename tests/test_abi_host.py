@@ -116,6 +116,26 @@ def test_fixed_splits_match_the_named_workloads(lib):
                             v_is_k_prefix=1, max_pages_per_seq=128, max_seq_len=8192), 8) == (1024, 8)
 
 
+def test_fused_fold_applies_where_one_workgroup_reads_at_most_1_mib(lib):
+    # (compute units: the device's, 256 on this host without one, as on an MI355X)
+    applies = lambda p, n: lib.da_fused_applies(ctypes.byref(p), n)
+    tiny = prob(batch=1, num_q_heads=1, num_kv_heads=1, dtype=0, page_size=0, kv_capacity=1024, max_seq_len=1024)
+    gqa = prob(batch=8, num_q_heads=32, num_kv_heads=8, page_size=0, kv_capacity=4096, max_seq_len=4096)
+    long_ = prob(batch=1, num_q_heads=32, num_kv_heads=4, max_pages_per_seq=2048, max_seq_len=131072)
+    latent = prob(batch=16, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1,
+                  max_pages_per_seq=128, max_seq_len=8192)
+    paged = prob(batch=32, num_q_heads=64, num_kv_heads=8, max_pages_per_seq=512, max_seq_len=32768)
+    assert applies(tiny, 4) == 1      # 4 partials x 1 row x 512 B
+    assert applies(gqa, 8) == 1       # 8 x 8 rows (2 kv heads per workgroup) x 512 B
+    assert applies(long_, 64) == 1    # 64 x 8 rows x 512 B = 256 KiB
+    assert applies(latent, 8) == 1    # 8 x 64 rows x 2 KiB = 1 MiB, the bound
+    assert applies(latent, 9) == 0
+    # equal shares: every one of the 256 workers may hold a piece of one sequence
+    assert applies(long_, 0) == 0     # 256 x 32 rows x 512 B = 4 MiB on one CU
+    assert applies(paged, 0) == 0
+    assert applies(prob(batch=0), 8) == DA_EINVAL
+
+
 @pytest.mark.parametrize("L,n,ps,dtype", [(1000, 3, 0, 1), (1000, 3, 64, 1), (77, 5, 0, 1), (5000, 7, 16, 1),
                                           (1, 1, 0, 1), (4096, 4096, 0, 1), (32768, 0, 64, 0), (131072, 0, 64, 0),
                                           (100, 0, 48, 0)])

@@ -357,7 +357,9 @@ def test_partition_partials_match_oracle():
 
 
 FUSED = [
-    ("paged64_auto", dict(batch=5, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=64,
+    # (equal shares: one kv head of 8 q heads keeps the bound on the last workgroup's fold,
+    # 256 workers x 8 rows x 512 B, within 1 MiB)
+    ("paged64_auto", dict(batch=5, num_q_heads=8, num_kv_heads=1, qk_depth=128, page_size=64,
                           len_range=(1, 5000), num_splits=0, seed=60)),
     ("contig_splits8", dict(batch=2, num_q_heads=8, num_kv_heads=2, qk_depth=128, seq_lens=[4096, 1000],
                             num_splits=8, seed=61)),
@@ -377,7 +379,7 @@ FUSED = [
     ("splits100", dict(batch=1, num_q_heads=8, num_kv_heads=1, qk_depth=128, page_size=32,
                        seq_lens=[6400], num_splits=100, seed=72)),
     # one long sequence in a batch of short ones under equal shares: most workers meet it
-    ("auto_one_long_many_short", dict(batch=40, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=64,
+    ("auto_one_long_many_short", dict(batch=40, num_q_heads=8, num_kv_heads=1, qk_depth=128, page_size=64,
                                       seq_lens=[30000] + [64] * 39, num_splits=0, seed=74)),
     # one kv head for all q heads (the shared-kv-head kernel): latent, latent over fp8 with
     # an empty sequence, several queries, GLM widths with the rotary columns apart, and 20
@@ -390,7 +392,7 @@ FUSED = [
                               **LATENT)),
     ("glm_mqa_apart_paged32", dict(batch=2, num_q_heads=128, page_size=32, seq_lens=[1500, 333], num_splits=3,
                                    seed=93, rope_apart=64, **GLM_MQA)),
-    ("glm_mqa_20_splits", dict(batch=1, num_q_heads=64, page_size=64, seq_lens=[5000], num_splits=20, seed=94,
+    ("glm_mqa_20_splits", dict(batch=1, num_q_heads=32, page_size=64, seq_lens=[5000], num_splits=20, seed=94,
                                rope_apart=64, **GLM_MQA)),
     # the vector-ALU kernel: fp32 (its automatic choice) and bf16 on request
     ("fp32_tiny", dict(batch=1, num_q_heads=1, num_kv_heads=1, qk_depth=128, dtype=torch.float32,
@@ -417,6 +419,7 @@ def test_fused_combine_matches_oracle_on_repeated_calls(name, kw):
     dc = to_device(case)
     prob = api.make_problem(dc.q, dc.k_cache, dc.v_cache, dc.page_table, page_size=case.page_size, kernel=kernel,
                             v_is_k_prefix=case.v_is_k_prefix, ov_depth=case.ov_depth, k_rope=dc.k_rope)
+    assert api.fused_applies(prob, case.num_splits), "the case must exercise the fold in pass 1"
     ws = torch.zeros(api.workspace_bytes(prob, case.num_splits), dtype=torch.uint8, device="cuda")
     O, LSE = oracle_for(case)
     for rep in range(3):
@@ -426,6 +429,24 @@ def test_fused_combine_matches_oracle_on_repeated_calls(name, kw):
         assert_parity(out, lse, o32, O, LSE, what=f"fused {name} call {rep}")
 
 
+def test_fused_entry_takes_the_combine_launch_for_a_fold_beyond_1_mib():
+    # equal shares over 256 workers: any one sequence may meet every share, so the last
+    # workgroup of a kv head could have to fold 256 partials of its 16 rows (2 MiB); the fused
+    # entry point runs the combine launch instead (same results), here on a workspace that
+    # was never zero-filled
+    print("[parity] fused entry point, fold beyond 1 MiB", flush=True)
+    case = make_case("fold_beyond_1mib", batch=2, num_q_heads=16, num_kv_heads=1, qk_depth=128, page_size=64,
+                     seq_lens=[9000, 100], num_splits=0, seed=73)
+    dc = to_device(case)
+    prob = api.make_problem(dc.q, dc.k_cache, dc.v_cache, dc.page_table, page_size=case.page_size)
+    assert not api.fused_applies(prob, 0)
+    ws = torch.full((api.workspace_bytes(prob, 0),), 255, dtype=torch.uint8, device="cuda")
+    O, LSE = oracle_for(case)
+    out, lse, o32 = api.case_call(dc, return_lse=True, return_o32=True, fused=True, workspace=ws)
+    torch.cuda.synchronize()
+    assert_parity(out, lse, o32, O, LSE, what="fused entry point, fold beyond 1 MiB")
+
+
 FUSED_EMPTY = [
     ("fixed8_bf16", dict(batch=5, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=64,
                          seq_lens=[0, 1, 33, 0, 2442], num_splits=8, seed=65)),
@@ -433,7 +454,7 @@ FUSED_EMPTY = [
                              seq_lens=[31, 0, 32, 0], num_splits=3, kv_fp8=True, seed=66)),
     ("fixed1_contig", dict(batch=3, num_q_heads=8, num_kv_heads=1, qk_depth=128, seq_lens=[0, 2, 700],
                            num_splits=1, seed=67)),
-    ("auto_bf16", dict(batch=6, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=64,
+    ("auto_bf16", dict(batch=6, num_q_heads=8, num_kv_heads=1, qk_depth=128, page_size=64,
                        seq_lens=[0, 3000, 0, 5, 0, 0], num_splits=0, seed=68)),
     ("auto_all_empty", dict(batch=3, num_q_heads=8, num_kv_heads=1, qk_depth=128, page_size=64,
                             seq_lens=[0, 0, 0], num_splits=0, seed=69)),
@@ -453,6 +474,7 @@ def test_fused_combine_writes_rows_of_empty_sequences(name, kw):
     dc = to_device(case)
     prob = api.make_problem(dc.q, dc.k_cache, dc.v_cache, dc.page_table, page_size=case.page_size,
                             v_is_k_prefix=case.v_is_k_prefix, ov_depth=case.ov_depth, k_rope=dc.k_rope)
+    assert api.fused_applies(prob, case.num_splits), "the case must exercise the fold in pass 1"
     ws = torch.zeros(api.workspace_bytes(prob, case.num_splits), dtype=torch.uint8, device="cuda")
     rows = api.row_shape(prob)
     out = torch.empty(rows + (prob.ov_depth,), dtype=torch.bfloat16, device="cuda")
