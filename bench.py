@@ -56,8 +56,9 @@ def parse():
     ap.add_argument("--workload", default="paged_gqa")
     ap.add_argument("--num-splits", type=int, default=None, help="override the workload's split count")
     ap.add_argument("--kernel", default="auto", choices=["auto", "fma", "mfma"])
-    ap.add_argument("--combine", default="separate", choices=["separate", "fused"],
-                    help="LSE combine as its own launch, or by each group's last-arriving workgroup")
+    ap.add_argument("--combine", default="separate", choices=["separate", "fused", "fused-force"],
+                    help="LSE combine as its own launch, or by each group's last-arriving workgroup (fused: "
+                         "where that pays, as the fused entry point decides; fused-force: always)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=30.0)
     ap.add_argument("--probe-gib", type=float, default=2.0, help="streaming-read probe size")
@@ -105,7 +106,8 @@ def main():
 
     plan = api.DecodePlan(dc.q, dc.k_cache, dc.v_cache, dc.page_table, dc.seq_lens, case.scale, case.num_splits,
                           page_size=case.page_size, v_is_k_prefix=case.v_is_k_prefix, ov_depth=case.ov_depth,
-                          kernel=args.kernel, out=out, fused=args.combine == "fused",
+                          kernel=args.kernel, out=out,
+                          fused={"separate": False, "fused": True, "fused-force": "force"}[args.combine],
                           k_scale=dc.k_scale, v_scale=dc.v_scale, k_rope=dc.k_rope)
     step = plan.run
 
@@ -265,8 +267,8 @@ def main():
             "qk_depth": prob.qk_depth, "ov_depth": Dv, "nope_depth": prob.nope_depth, "page_size": case.page_size,
             "keys": tokens, "max_seq_len": int(case.seq_lens.max()),
             "num_splits": case.num_splits, "chunk_tokens": chunk, "max_splits": max_splits, "kernel": args.kernel,
-            "combine": args.combine if args.combine == "separate" or api.fused_applies(prob, case.num_splits)
-                       else "fused entry point (runs the combine launch: fold beyond 1 MiB)",
+            "combine": args.combine if args.combine != "fused" or api.fused_applies(prob, case.num_splits)
+                       else "fused entry point, which runs the combine launch here (fold beyond 64 KiB)",
             "kv_bytes": kv_bytes,
         },
         "roofline": {

@@ -161,10 +161,12 @@ int da_workspace_bytes(const da_problem* p, int32_t num_splits, size_t* bytes);
 
 /* 1 if decode_attn_splitk_fused merges the partials in pass 1 for this problem and
  * num_splits, 0 if it runs the combine launch instead, or an error code as da_supported.
- * It merges in pass 1 when the partial outputs one last-arriving workgroup must read stay
- * within 1 MiB (max_splits, or every worker under equal shares, times the rows of its head
- * group or 64-column block, times Dv x 4 bytes): one workgroup reads them alone, while the
- * combine launch spreads them over the chip. Each partial array must also stay below 2 GB.
+ * The last-arriving workgroup of a group reads the group's partials alone, at the rate of
+ * one compute unit, while the combine launch spreads them over the chip; so the merge runs
+ * in pass 1 only while those partial outputs stay within 64 KiB: max_splits (or, under
+ * equal shares, every worker) times the rows of the head group or 64-column block times
+ * Dv x 4 bytes. (On an MI355X that is 1 us faster than the combine launch at 2-32 KiB and
+ * 5-19 us slower at 256 KiB-1 MiB.) Each partial array must also stay below 2 GB.
  * (num_splits and the device's compute units as da_workspace_bytes.) */
 int da_fused_applies(const da_problem* p, int32_t num_splits);
 
@@ -199,9 +201,10 @@ int decode_attn_splitk_noalloc(const da_problem* p, const void* q, const void* k
  * a (sequence, kv-head group) stores its partial, publishes it device-wide and counts
  * itself in on an arrival counter; the last one merges all partials of its heads and
  * writes out / lse_out / o_f32_out, then resets the counter. This saves the second
- * launch. Applied by every partition kernel (every depth pair, cache dtype and partition
- * count) where da_fused_applies says so; otherwise the step runs as decode_attn_splitk.
- * The outputs are the same either way. Rows of a sequence without keys are written too
+ * launch. Done by every partition kernel (every depth pair, cache dtype and partition
+ * count) where da_fused_applies says so; otherwise the step runs as decode_attn_splitk
+ * (decode_attn_splitk_kv with fused = 2 merges in pass 1 wherever the partial arrays stay
+ * below 2 GB). The outputs are the same either way. Rows of a sequence without keys are written too
  * (O = 0, LSE = -inf), by one workgroup that holds no keys. Same arguments and workspace
  * size as decode_attn_splitk,
  * with one more rule: the workspace must be zero-filled before its first use with this
@@ -249,8 +252,10 @@ typedef struct da_kv {
 
 /* The whole decode step with the caches described by `kv`: every problem the library
  * supports, including rotary columns stored apart (nope_depth > 0) and fp8 caches.
- * fused != 0 runs it as decode_attn_splitk_fused (same workspace rules), else as
- * decode_attn_splitk. Other arguments as decode_attn_splitk. */
+ * fused = 1 runs it as decode_attn_splitk_fused (same workspace rules); fused = 2 likewise
+ * but merges in pass 1 whatever the partials' size (for callers that must avoid the second
+ * launch; each partial array below 2 GB); fused = 0 as decode_attn_splitk; other values
+ * return DA_EINVAL. Other arguments as decode_attn_splitk. */
 int decode_attn_splitk_kv(const da_problem* p, const void* q, const da_kv* kv,
                           const int32_t* page_table, const int32_t* seq_lens, float scale,
                           int32_t num_splits, int32_t fused, void* out, float* lse_out,

@@ -143,6 +143,15 @@ def workspace_bytes(problem: DaProblem, num_splits=0):
     return n.value
 
 
+def _fused_mode(fused):
+    """fused=False: combine launch; True: fold in pass 1 where it pays; "force": always."""
+    if fused == "force":
+        return 2
+    if fused in (False, True, 0, 1):
+        return int(bool(fused))
+    raise ValueError(f"fused must be False, True or 'force' (got {fused!r})")
+
+
 def fused_applies(problem: DaProblem, num_splits=0):
     """True if the fused entry point merges the partials in pass 1 for this problem (else it
     runs the combine launch, with the same results)."""
@@ -160,11 +169,13 @@ def decode_attn(q, k_cache, v_cache, page_table, seq_lens, scale, num_splits=0, 
     """The whole split-K decode step. Returns out (bf16 [B, Hq, Dv]) or (out, lse, o32).
 
     fused=True runs decode_attn_splitk_fused (the combine done by each group's last
-    workgroup); a workspace passed in must then have been zero-filled before its first use.
+    workgroup where that pays, see ``fused_applies``), fused="force" always does it in pass 1;
+    a workspace passed in must then have been zero-filled before its first use.
     fp8 caches take k_scale / v_scale; rotary columns stored apart take k_rope (both run
     through the entry points that accept those tensors).
     """
     lib = _lib.load()
+    mode = _fused_mode(fused)
     prob = make_problem(q, k_cache, v_cache, page_table, page_size=page_size, max_seq_len=max_seq_len,
                         v_is_k_prefix=v_is_k_prefix, ov_depth=ov_depth, kernel=kernel, k_rope=k_rope)
     _check_tensors(q, k_cache, v_cache, page_table, seq_lens)
@@ -181,11 +192,11 @@ def decode_attn(q, k_cache, v_cache, page_table, seq_lens, scale, num_splits=0, 
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
     ws = (_ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
-    if k_rope is not None or (prob.kv_dtype and fused):
+    if k_rope is not None or (prob.kv_dtype and mode) or mode == 2:
         _check_tensors(k_rope, k_scale, v_scale)
         kv = _kv(k_cache, v_cache, k_rope, k_scale, v_scale)
         check(lib.decode_attn_splitk_kv(ctypes.byref(prob), _ptr(q), ctypes.byref(kv), _ptr(page_table),
-                                        _ptr(seq_lens), float(scale), int(num_splits), int(bool(fused)), _ptr(out),
+                                        _ptr(seq_lens), float(scale), int(num_splits), mode, _ptr(out),
                                         _ptr(lse), _ptr(o32), *ws))
     elif prob.kv_dtype:
         _check_tensors(k_scale, v_scale)
@@ -193,7 +204,7 @@ def decode_attn(q, k_cache, v_cache, page_table, seq_lens, scale, num_splits=0, 
                                          _ptr(v_scale), _ptr(page_table), _ptr(seq_lens), float(scale),
                                          int(num_splits), _ptr(out), _ptr(lse), _ptr(o32), *ws))
     else:
-        fn = lib.decode_attn_splitk_fused if fused else lib.decode_attn_splitk
+        fn = lib.decode_attn_splitk_fused if mode else lib.decode_attn_splitk
         check(fn(ctypes.byref(prob), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(seq_lens),
                  float(scale), int(num_splits), _ptr(out), _ptr(lse), _ptr(o32), *ws))
     if return_lse or return_o32:
@@ -305,14 +316,15 @@ class DecodePlan:
         need = workspace_bytes(self.prob, num_splits)
         # zero-filled once: the fused step keeps its arrival counters here
         self.workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
-        self.fn = self.lib.decode_attn_splitk_fused if fused else self.lib.decode_attn_splitk
+        mode = _fused_mode(fused)
+        self.fn = self.lib.decode_attn_splitk_fused if mode else self.lib.decode_attn_splitk
         self.chunk, self.max_splits = choose_splits(self.prob, num_splits)
         self._keep = (q, k_cache, v_cache, page_table, seq_lens, k_scale, v_scale, k_rope)
-        if k_rope is not None or (self.prob.kv_dtype and fused):
+        if k_rope is not None or (self.prob.kv_dtype and mode) or mode == 2:
             self.fn = self.lib.decode_attn_splitk_kv
             self.kv = _kv(k_cache, v_cache, k_rope, k_scale, v_scale)
             self._args = (ctypes.byref(self.prob), _ptr(q), ctypes.byref(self.kv), _ptr(page_table), _ptr(seq_lens),
-                          float(scale), int(num_splits), int(bool(fused)), _ptr(self.out), _ptr(lse), _ptr(o32),
+                          float(scale), int(num_splits), mode, _ptr(self.out), _ptr(lse), _ptr(o32),
                           _ptr(self.workspace), self.workspace.numel())
         elif self.prob.kv_dtype:
             self.fn = self.lib.decode_attn_splitk_fp8

@@ -407,13 +407,16 @@ void set_kv_args(const da_problem* p, const da_kv& kv, da::PartArgs* a) {
 }
 
 // Fused combine: the last-arriving workgroup of a (sequence, head group) reads the partials
-// of every row of the group alone, so the fold is kept to sets of at most kFusedFoldBytes of
-// partial O (for the largest partition count the schedule allows a row: max_splits, or
-// every worker under equal shares). A larger set (e.g. one long sequence under equal shares,
-// 4 MB on one CU) takes the combine launch, which spreads the same fold over the chip.
-constexpr int64_t kFusedFoldBytes = 1 << 20;
+// of every row of the group alone, at the rate of one CU (about 40 GB/s), while the combine
+// launch spreads the same fold over the chip for the cost of a launch (3-4 us). Measured
+// (flushed steps): 2 KB and 32 KB of partial O per group, the fold in pass 1 is 1 us faster;
+// 256 KB (64 partitions of 8 rows), 5 us slower; 1 MiB (8 partitions of 64 latent rows),
+// 19 us slower. The fused entry point therefore folds in pass 1 while a group's partial O
+// stays within kFusedFoldBytes, for the largest partition count the schedule allows a row
+// (max_splits, or every worker under equal shares); forced (mode 2) it always does.
+constexpr int64_t kFusedFoldBytes = 64 << 10;
 
-bool fused_fold_fits(const da_problem* p, Variant var, int32_t C, int32_t P, int cus) {
+int64_t fused_fold_bytes(const da_problem* p, Variant var, int32_t C, int32_t P, int cus) {
   const int64_t ql = q_len_of(p), g = p->num_q_heads / p->num_kv_heads;
   int64_t rows;
   if (var == kVarFma) {
@@ -426,23 +429,24 @@ bool fused_fold_fits(const da_problem* p, Variant var, int32_t C, int32_t P, int
   } else {
     rows = std::min<int64_t>(64, rows_per_seq(p));   // (sequence, block of 64 columns)
   }
-  return (int64_t)P * rows * p->ov_depth * 4 <= kFusedFoldBytes;
+  return (int64_t)P * rows * p->ov_depth * 4;
 }
 
-// Whether decode_attn_splitk_fused folds in pass 1 for this schedule and workspace layout:
-// the fold fits, and each partial array stays below 2 GB (the fused path addresses them with
-// 32-bit byte offsets).
-bool fused_applies(const da_problem* p, Variant var, int32_t C, int32_t P, int cus) {
+// Fused modes: 0 none (combine launch), 1 where the fold pays, 2 always. Either fused mode
+// needs each partial array below 2 GB (the fold addresses them with 32-bit byte offsets).
+bool fused_applies(const da_problem* p, Variant var, int32_t C, int32_t P, int cus, int mode) {
+  if (mode == 0) return false;
   size_t ml_off, o_off, cnt_off, total;
   ws_layout(p, C, P, &ml_off, &o_off, &cnt_off, &total);
-  return o_off < (size_t(1) << 31) && cnt_off - o_off < (size_t(1) << 31) && fused_fold_fits(p, var, C, P, cus);
+  if (o_off >= (size_t(1) << 31) || cnt_off - o_off >= (size_t(1) << 31)) return false;
+  return mode == 2 || fused_fold_bytes(p, var, C, P, cus) <= kFusedFoldBytes;
 }
 
 // The whole step. With `fused`, the partition kernel's last-arriving workgroup of each
 // (sequence, head group) combines (no second launch). The results are the same either way.
 int run_splitk(const da_problem* p, const void* q, const da_kv& kv, const int32_t* page_table, const int32_t* seq_lens,
                float scale, int32_t num_splits, void* out, float* lse_out, float* o_f32_out, void* workspace,
-               size_t workspace_bytes, void* stream, bool fused) {
+               size_t workspace_bytes, void* stream, int fused) {
   Variant var;
   int r = check_problem(p, &var);
   if (r) return r;
@@ -473,7 +477,7 @@ int run_splitk(const da_problem* p, const void* q, const da_kv& kv, const int32_
   set_kv_args(p, kv, &a);
   // (where the fused fold does not apply the step takes the combine launch, with the same
   // results)
-  const bool fuse = fused && fused_applies(p, var, C, P, cus);
+  const bool fuse = fused_applies(p, var, C, P, cus, fused);
   if (fuse) a.counters = (int32_t*)((char*)workspace + cnt_off);
   if ((r = launch_partition(p, var, a, s, cus))) return r;
   if (!fuse && (r = launch_combine(p, seq_lens, scale, C, P, po, pml, out, lse_out, o_f32_out, 1, s))) return r;
@@ -562,7 +566,7 @@ int da_fused_applies(const da_problem* p, int32_t num_splits) {
   r = choose(p, v, num_splits, cus, &C, &P);
   if (r) return r;
   ok();
-  return fused_applies(p, v, C, P, cus) ? 1 : 0;
+  return fused_applies(p, v, C, P, cus, 1) ? 1 : 0;
 }
 
 int decode_attn_splitk(const da_problem* p, const void* q, const void* k_cache, const void* v_cache,
@@ -570,7 +574,7 @@ int decode_attn_splitk(const da_problem* p, const void* q, const void* k_cache, 
                        void* out, float* lse_out, float* o_f32_out, void* workspace, size_t workspace_bytes,
                        void* stream) {
   return run_splitk(p, q, make_kv(k_cache, v_cache), page_table, seq_lens, scale, num_splits, out, lse_out,
-                    o_f32_out, workspace, workspace_bytes, stream, false);
+                    o_f32_out, workspace, workspace_bytes, stream, 0);
 }
 
 // Scratch memory of decode_attn_splitk_noalloc: the workspace of one step (fp32 partials,
@@ -613,7 +617,7 @@ int decode_attn_splitk_noalloc(const da_problem* p, const void* q, const void* k
   void* ws = nullptr;
   if ((r = scratch_ptr(&ws))) return r;
   return run_splitk(p, q, make_kv(k_cache, v_cache), page_table, seq_lens, scale, num_splits, out, lse_out,
-                    o_f32_out, ws, kScratchBytes, stream, false);
+                    o_f32_out, ws, kScratchBytes, stream, 0);
 }
 
 int decode_attn_splitk_fused(const da_problem* p, const void* q, const void* k_cache, const void* v_cache,
@@ -621,7 +625,7 @@ int decode_attn_splitk_fused(const da_problem* p, const void* q, const void* k_c
                              void* out, float* lse_out, float* o_f32_out, void* workspace, size_t workspace_bytes,
                              void* stream) {
   return run_splitk(p, q, make_kv(k_cache, v_cache), page_table, seq_lens, scale, num_splits, out, lse_out,
-                    o_f32_out, workspace, workspace_bytes, stream, true);
+                    o_f32_out, workspace, workspace_bytes, stream, 1);
 }
 
 int decode_attn_splitk_fp8(const da_problem* p, const void* q, const void* k_cache, const void* v_cache,
@@ -631,15 +635,16 @@ int decode_attn_splitk_fp8(const da_problem* p, const void* q, const void* k_cac
   if (!p) return fail(DA_EINVAL, "problem is NULL");
   if (p->kv_dtype != DA_FP8_E4M3) return fail(DA_EINVAL, "decode_attn_splitk_fp8 needs kv_dtype = DA_FP8_E4M3");
   return run_splitk(p, q, make_kv(k_cache, v_cache, k_scale, v_scale), page_table, seq_lens, scale, num_splits, out,
-                    lse_out, o_f32_out, workspace, workspace_bytes, stream, false);
+                    lse_out, o_f32_out, workspace, workspace_bytes, stream, 0);
 }
 
 int decode_attn_splitk_kv(const da_problem* p, const void* q, const da_kv* kv, const int32_t* page_table,
                           const int32_t* seq_lens, float scale, int32_t num_splits, int32_t fused, void* out,
                           float* lse_out, float* o_f32_out, void* workspace, size_t workspace_bytes, void* stream) {
   if (!kv) return fail(DA_EINVAL, "kv is NULL");
+  if (fused < 0 || fused > 2) return fail(DA_EINVAL, "fused must be 0, 1 or 2 (got %d)", fused);
   return run_splitk(p, q, *kv, page_table, seq_lens, scale, num_splits, out, lse_out, o_f32_out, workspace,
-                    workspace_bytes, stream, fused != 0);
+                    workspace_bytes, stream, fused);
 }
 
 static int partition_impl(const da_problem* p, const void* q, const da_kv& kv, const int32_t* page_table,

@@ -116,7 +116,7 @@ def test_fixed_splits_match_the_named_workloads(lib):
                             v_is_k_prefix=1, max_pages_per_seq=128, max_seq_len=8192), 8) == (1024, 8)
 
 
-def test_fused_fold_applies_where_one_workgroup_reads_at_most_1_mib(lib):
+def test_fused_fold_applies_where_one_workgroup_reads_at_most_64_kib(lib):
     # (compute units: the device's, 256 on this host without one, as on an MI355X)
     applies = lambda p, n: lib.da_fused_applies(ctypes.byref(p), n)
     tiny = prob(batch=1, num_q_heads=1, num_kv_heads=1, dtype=0, page_size=0, kv_capacity=1024, max_seq_len=1024)
@@ -126,14 +126,23 @@ def test_fused_fold_applies_where_one_workgroup_reads_at_most_1_mib(lib):
                   max_pages_per_seq=128, max_seq_len=8192)
     paged = prob(batch=32, num_q_heads=64, num_kv_heads=8, max_pages_per_seq=512, max_seq_len=32768)
     assert applies(tiny, 4) == 1      # 4 partials x 1 row x 512 B
-    assert applies(gqa, 8) == 1       # 8 x 8 rows (2 kv heads per workgroup) x 512 B
-    assert applies(long_, 64) == 1    # 64 x 8 rows x 512 B = 256 KiB
-    assert applies(latent, 8) == 1    # 8 x 64 rows x 2 KiB = 1 MiB, the bound
-    assert applies(latent, 9) == 0
+    assert applies(gqa, 8) == 1       # 8 x 8 rows (2 kv heads per workgroup) x 512 B = 32 KiB
+    assert applies(gqa, 16) == 0      # 4 kv heads per workgroup: 16 x 16 rows x 512 B = 128 KiB
+    assert applies(long_, 64) == 0    # 64 x 8 rows x 512 B = 256 KiB
+    assert applies(latent, 8) == 0    # 8 x 64 rows x 2 KiB = 1 MiB
     # equal shares: every one of the 256 workers may hold a piece of one sequence
-    assert applies(long_, 0) == 0     # 256 x 32 rows x 512 B = 4 MiB on one CU
+    assert applies(long_, 0) == 0
     assert applies(paged, 0) == 0
     assert applies(prob(batch=0), 8) == DA_EINVAL
+
+
+def test_fused_mode_argument(lib):
+    p = prob()
+    kv = _lib.DaKv(FAKE.value, FAKE.value, None, None, None)
+    for bad in (-1, 3):
+        r = lib.decode_attn_splitk_kv(ctypes.byref(p), FAKE, ctypes.byref(kv), FAKE, FAKE, 0.1, 0, bad, FAKE,
+                                      None, None, FAKE, 1 << 20, None)
+        assert r == DA_EINVAL and b"fused" in lib.da_last_error()
 
 
 @pytest.mark.parametrize("L,n,ps,dtype", [(1000, 3, 0, 1), (1000, 3, 64, 1), (77, 5, 0, 1), (5000, 7, 16, 1),

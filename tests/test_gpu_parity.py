@@ -142,7 +142,7 @@ def test_large_logits_overflow_safety():
 
 
 def test_latent_fused_entry_point_writes_every_row():
-    # the fused entry point on a latent-shared problem: the last workgroup of each column
+    # the fold in pass 1 forced on a latent-shared problem: the last workgroup of each column
     # block combines; outputs (rows of an empty sequence included) match the oracle
     print("[parity] latent through the fused entry point", flush=True)
     case = make_case("latent_fused", batch=3, num_q_heads=64, num_kv_heads=1, qk_depth=576, ov_depth=512,
@@ -155,7 +155,7 @@ def test_latent_fused_entry_point_writes_every_row():
     out = torch.full(rows + (prob.ov_depth,), float("nan"), dtype=torch.bfloat16, device="cuda")
     lse = torch.full(rows, float("nan"), dtype=torch.float32, device="cuda")
     o32 = torch.full(rows + (prob.ov_depth,), float("nan"), dtype=torch.float32, device="cuda")
-    api.case_call(dc, out=out, lse=lse, o32=o32, fused=True, workspace=ws)
+    api.case_call(dc, out=out, lse=lse, o32=o32, fused="force", workspace=ws)
     torch.cuda.synchronize()
     O, LSE = oracle_for(case)
     assert_parity(out, lse, o32, O, LSE, what="latent fused entry point")
@@ -296,7 +296,7 @@ DETERMINISM = [
     ("gqa_paged_auto", dict(batch=4, num_q_heads=32, num_kv_heads=4, qk_depth=128, page_size=64,
                             len_range=(500, 6000), num_splits=0, seed=43), {}),
     ("gqa_paged_auto_fused", dict(batch=4, num_q_heads=32, num_kv_heads=4, qk_depth=128, page_size=64,
-                                  len_range=(500, 6000), num_splits=0, seed=44), {"fused": True}),
+                                  len_range=(500, 6000), num_splits=0, seed=44), {"fused": "force"}),
     ("latent_splits4", dict(batch=3, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512,
                             v_is_k_prefix=True, page_size=64, seq_lens=[3000, 700, 64], num_splits=4,
                             seed=45), {}),
@@ -419,23 +419,23 @@ def test_fused_combine_matches_oracle_on_repeated_calls(name, kw):
     dc = to_device(case)
     prob = api.make_problem(dc.q, dc.k_cache, dc.v_cache, dc.page_table, page_size=case.page_size, kernel=kernel,
                             v_is_k_prefix=case.v_is_k_prefix, ov_depth=case.ov_depth, k_rope=dc.k_rope)
-    assert api.fused_applies(prob, case.num_splits), "the case must exercise the fold in pass 1"
+    # (forced: the fold runs in pass 1 whatever the size of the partials)
     ws = torch.zeros(api.workspace_bytes(prob, case.num_splits), dtype=torch.uint8, device="cuda")
     O, LSE = oracle_for(case)
     for rep in range(3):
-        out, lse, o32 = api.case_call(dc, return_lse=True, return_o32=True, fused=True, workspace=ws,
+        out, lse, o32 = api.case_call(dc, return_lse=True, return_o32=True, fused="force", workspace=ws,
                                       kernel=kernel)
         torch.cuda.synchronize()
         assert_parity(out, lse, o32, O, LSE, what=f"fused {name} call {rep}")
 
 
-def test_fused_entry_takes_the_combine_launch_for_a_fold_beyond_1_mib():
+def test_fused_entry_takes_the_combine_launch_for_a_fold_beyond_64_kib():
     # equal shares over 256 workers: any one sequence may meet every share, so the last
     # workgroup of a kv head could have to fold 256 partials of its 16 rows (2 MiB); the fused
     # entry point runs the combine launch instead (same results), here on a workspace that
     # was never zero-filled
-    print("[parity] fused entry point, fold beyond 1 MiB", flush=True)
-    case = make_case("fold_beyond_1mib", batch=2, num_q_heads=16, num_kv_heads=1, qk_depth=128, page_size=64,
+    print("[parity] fused entry point, fold beyond 64 KiB", flush=True)
+    case = make_case("fold_beyond_64kib", batch=2, num_q_heads=16, num_kv_heads=1, qk_depth=128, page_size=64,
                      seq_lens=[9000, 100], num_splits=0, seed=73)
     dc = to_device(case)
     prob = api.make_problem(dc.q, dc.k_cache, dc.v_cache, dc.page_table, page_size=case.page_size)
@@ -444,7 +444,36 @@ def test_fused_entry_takes_the_combine_launch_for_a_fold_beyond_1_mib():
     O, LSE = oracle_for(case)
     out, lse, o32 = api.case_call(dc, return_lse=True, return_o32=True, fused=True, workspace=ws)
     torch.cuda.synchronize()
-    assert_parity(out, lse, o32, O, LSE, what="fused entry point, fold beyond 1 MiB")
+    assert_parity(out, lse, o32, O, LSE, what="fused entry point, fold beyond 64 KiB")
+
+
+FUSED_WHERE_IT_PAYS = [
+    # 8 partitions x 4 rows (one kv head of 4 q heads per workgroup) x 512 B = 16 KiB
+    ("contig_splits8", dict(batch=2, num_q_heads=8, num_kv_heads=2, qk_depth=128, seq_lens=[4096, 1000],
+                            num_splits=8, seed=61)),
+    # the vector-ALU kernel: 4 partitions of one row
+    ("fp32_tiny", dict(batch=1, num_q_heads=1, num_kv_heads=1, qk_depth=128, dtype=torch.float32,
+                       seq_lens=[1024], num_splits=4, seed=75)),
+    # one kv head for all q heads: 2 partitions x 24 rows x 1 KiB (GLM widths) = 48 KiB
+    ("glm_mqa_24_heads", dict(batch=2, num_q_heads=24, page_size=64, seq_lens=[1500, 0], num_splits=2, seed=97,
+                              rope_apart=64, **GLM_MQA)),
+]
+
+
+@pytest.mark.parametrize("name,kw", FUSED_WHERE_IT_PAYS, ids=[c[0] for c in FUSED_WHERE_IT_PAYS])
+def test_fused_entry_point_folds_in_pass_1_where_it_pays(name, kw):
+    print(f"[parity] fused entry point folds in pass 1: {name}", flush=True)
+    case = make_case(name, **kw)
+    dc = to_device(case)
+    prob = api.make_problem(dc.q, dc.k_cache, dc.v_cache, dc.page_table, page_size=case.page_size,
+                            v_is_k_prefix=case.v_is_k_prefix, ov_depth=case.ov_depth, k_rope=dc.k_rope)
+    assert api.fused_applies(prob, case.num_splits)
+    ws = torch.zeros(api.workspace_bytes(prob, case.num_splits), dtype=torch.uint8, device="cuda")
+    O, LSE = oracle_for(case)
+    for rep in range(2):
+        out, lse, o32 = api.case_call(dc, return_lse=True, return_o32=True, fused=True, workspace=ws)
+        torch.cuda.synchronize()
+        assert_parity(out, lse, o32, O, LSE, what=f"fused where it pays {name} call {rep}")
 
 
 FUSED_EMPTY = [
@@ -474,7 +503,6 @@ def test_fused_combine_writes_rows_of_empty_sequences(name, kw):
     dc = to_device(case)
     prob = api.make_problem(dc.q, dc.k_cache, dc.v_cache, dc.page_table, page_size=case.page_size,
                             v_is_k_prefix=case.v_is_k_prefix, ov_depth=case.ov_depth, k_rope=dc.k_rope)
-    assert api.fused_applies(prob, case.num_splits), "the case must exercise the fold in pass 1"
     ws = torch.zeros(api.workspace_bytes(prob, case.num_splits), dtype=torch.uint8, device="cuda")
     rows = api.row_shape(prob)
     out = torch.empty(rows + (prob.ov_depth,), dtype=torch.bfloat16, device="cuda")
@@ -484,7 +512,7 @@ def test_fused_combine_writes_rows_of_empty_sequences(name, kw):
     for rep in range(2):
         for t in (out, lse, o32):
             t.fill_(float("nan"))
-        api.case_call(dc, out=out, lse=lse, o32=o32, fused=True, workspace=ws)
+        api.case_call(dc, out=out, lse=lse, o32=o32, fused="force", workspace=ws)
         torch.cuda.synchronize()
         assert_parity(out, lse, o32, O, LSE, what=f"fused empty rows {name} call {rep}")
 
@@ -663,7 +691,7 @@ def test_multiquery_fused_combine():
     prob = api.make_problem(dc.q, dc.k_cache, dc.v_cache, dc.page_table, page_size=case.page_size)
     ws = torch.zeros(api.workspace_bytes(prob, 0), dtype=torch.uint8, device="cuda")
     for rep in range(2):
-        out, lse, o32 = api.case_call(dc, return_lse=True, return_o32=True, fused=True, workspace=ws)
+        out, lse, o32 = api.case_call(dc, return_lse=True, return_o32=True, fused="force", workspace=ws)
         torch.cuda.synchronize()
         assert_parity(out, lse, o32, O, LSE, what=f"multi-query fused call {rep}")
 
@@ -720,7 +748,7 @@ def test_wide_depth_fused_combine():
                             k_rope=dc.k_rope)
     ws = torch.zeros(api.workspace_bytes(prob, 0), dtype=torch.uint8, device="cuda")
     for rep in range(2):
-        out, lse, o32 = api.case_call(dc, return_lse=True, return_o32=True, fused=True, workspace=ws)
+        out, lse, o32 = api.case_call(dc, return_lse=True, return_o32=True, fused="force", workspace=ws)
         torch.cuda.synchronize()
         assert_parity(out, lse, o32, O, LSE, what=f"wide depth fused call {rep}")
 
