@@ -184,10 +184,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t whole_rsrc(const void* base) {
 // rows apart; loads are issued kBatch at a time. Partials with l_j == 0 weigh nothing.
 // DEV: the partials were published by device-coherent stores, and ml_base / po_base are the
 // starts of their arrays.
+// The calling thread's own partial, when it is one of them, can stay in registers
+// (fa4_splitk_combine_write, second paragraph: the writer's own band is not read back):
+// partial `own` is then taken as (own_ml, own_o) instead of being loaded, in its place in the
+// order, so that the result does not depend on which workgroup folds.
+struct OwnPartial {
+  int idx = -1;   // index of the partial among the row's P, -1: none
+  float2 ml;
+  f32x4 o;
+};
 template <int DV, int kBatch = 8, bool DEV = false>
 __device__ __forceinline__ void fold_partials(const float2* ml, const float* po, int64_t stride, int P, int j0,
                                               int step, float c, float& M, float& Ls, f32x4& acc,
-                                              const float* ml_base = nullptr, const float* po_base = nullptr) {
+                                              const float* ml_base = nullptr, const float* po_base = nullptr,
+                                              const OwnPartial& own = OwnPartial()) {
   __amdgpu_buffer_rsrc_t rml, ro;
   if constexpr (DEV) rml = whole_rsrc(ml_base), ro = whole_rsrc(po_base);
   for (int p0 = j0; p0 < P; p0 += step * kBatch) {
@@ -197,7 +207,10 @@ __device__ __forceinline__ void fold_partials(const float2* ml, const float* po,
     for (int i = 0; i < kBatch; ++i) {
       const int p = p0 + i * step;
       const bool in = p < P;
-      if constexpr (DEV) {
+      if (p == own.idx) {
+        v[i] = own.ml;
+        o[i] = own.o;
+      } else if constexpr (DEV) {
         // (partials published by the fused combine's device-coherent stores)
         const uint32_t mo = (uint32_t)((const char*)(ml + p * stride) - (const char*)ml_base);
         const uint32_t oo = (uint32_t)((const char*)(po + p * stride * DV) - (const char*)po_base);

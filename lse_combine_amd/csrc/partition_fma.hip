@@ -327,8 +327,14 @@ __global__ __launch_bounds__(kWaves * 64, (FmaLds<T, GMAX>::kMinWaves)) void par
   }
   __syncthreads();
 
-  // merge the waves (same LSE weights as the split-K combine) and store
-  for (int u = tid; u < g * kUnits; u += kWaves * 64) {
+  // merge the waves (same LSE weights as the split-K combine) and store; the fused combine's
+  // fold below takes the same units in the same order, so each thread keeps what it stored
+  constexpr int kOwn = (GMAX * kUnits + kWaves * 64 - 1) / (kWaves * 64);
+  OwnPartial own[kOwn];
+#pragma unroll
+  for (int k = 0; k < kOwn; ++k) {
+    const int u = tid + k * kWaves * 64;
+    if (u >= g * kUnits) break;
     const int h = u / kUnits, d0 = (u % kUnits) * 4;
     float M = -INFINITY;
 #pragma unroll
@@ -343,7 +349,10 @@ __global__ __launch_bounds__(kWaves * 64, (FmaLds<T, GMAX>::kMinWaves)) void par
       acc += e * ov;
     }
     const float inv = 1.f / Ls;
-    store_unit(a, b, kvh * g + h, p, direct, d0, acc * inv, M, Ls, d0 == 0);
+    own[k].idx = p;
+    own[k].ml = make_float2(M, Ls);
+    own[k].o = acc * inv;
+    store_unit(a, b, kvh * g + h, p, direct, d0, own[k].o, M, Ls, d0 == 0);
   }
 
   if (!a.counters || direct) return;
@@ -360,14 +369,17 @@ __global__ __launch_bounds__(kWaves * 64, (FmaLds<T, GMAX>::kMinWaves)) void par
   }
   __syncthreads();
   if (!__builtin_amdgcn_readfirstlane(last_s)) return;
-  for (int u = tid; u < g * kUnits; u += kWaves * 64) {
+#pragma unroll
+  for (int k = 0; k < kOwn; ++k) {
+    const int u = tid + k * kWaves * 64;
+    if (u >= g * kUnits) break;
     const int h = u / kUnits, d0 = (u % kUnits) * 4;
     const int64_t row = (int64_t)b * a.Hq + kvh * g + h;
     float M = -INFINITY, Ls = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    fold_partials<kD, 8, true>((const float2*)a.part_ml + row * a.max_splits, a.part_o + row * a.max_splits * kD + d0, 1,
-                      P_b, 0, 1, a.c, M, Ls, acc,
-        a.part_ml, a.part_o);
+    fold_partials<kD, 8, true>((const float2*)a.part_ml + row * a.max_splits,
+                               a.part_o + row * a.max_splits * kD + d0, 1, P_b, 0, 1, a.c, M, Ls, acc, a.part_ml,
+                               a.part_o, own[k]);
     write_row_unit(a.out, a.o32, a.lse, row, kD, d0, M, Ls, acc, a.scale);
   }
   if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -150,8 +150,9 @@ struct WaveInfo {
 // region; waves that saw no tile hold m = -inf, l = 0, O = 0 and get weight 0), with the
 // log-sum-exp weights of the two-fragment combine (fa4_lse_combine_write).
 template <bool HL, class S>
-__device__ __forceinline__ void merge_key_splits(const PartArgs& a, const WaveInfo& wv, char* smem, int b, int p,
-                                                 bool direct, const f32x4* o, float m_run, float l_run) {
+__device__ __forceinline__ OwnPartial merge_key_splits(const PartArgs& a, const WaveInfo& wv, char* smem, int b,
+                                                       int p, bool direct, const f32x4* o, float m_run,
+                                                       float l_run) {
   const int tid = threadIdx.x, NW = wv.NW, HG = wv.HG, KS = wv.KS, kg = grp_of(a, HG);
   const int hc = wv.hc, qd = wv.qd, g = a.g;
   const bool col_valid = wv.col_valid, is_lo = wv.is_lo;
@@ -173,6 +174,7 @@ __device__ __forceinline__ void merge_key_splits(const PartArgs& a, const WaveIn
   constexpr int kUnits = DV / 4;
   const int cols = a.q_len * g;   // (query, head) columns per kv head
   const int units = HG * cols * kUnits;
+  OwnPartial own;
   for (int u = tid; u < units; u += NW * 64) {
     const int mem = u / (cols * kUnits);
     const int h = (u / kUnits) % cols, d0 = (u % kUnits) * 4;
@@ -196,10 +198,19 @@ __device__ __forceinline__ void merge_key_splits(const PartArgs& a, const WaveIn
       }
     }
     const int row = (h / g) * a.Hq1 + kv2 * g + h % g;
-    store_unit(a, b, row, p, direct, d0, acc * (Ls > 0.f ? 1.f / Ls : 0.f), M, Ls, d0 == 0);
+    const f32x4 on = acc * (Ls > 0.f ? 1.f / Ls : 0.f);
+    if (u == tid) {
+      // (the fused combine's fold takes the units in this order; with one unit per thread the
+      // thread keeps the partial it stores)
+      own.idx = p;
+      own.ml = make_float2(M, Ls);
+      own.o = on;
+    }
+    store_unit(a, b, row, p, direct, d0, on, M, Ls, d0 == 0);
   }
   // the merge read other waves' V tiles: the next piece may refill them only after this
   __syncthreads();
+  return units <= NW * 64 ? own : OwnPartial();
 }
 
 // Last-arriving-workgroup combine (fa4_splitk_combine_write, fourth paragraph: the writer
@@ -224,7 +235,7 @@ __device__ __forceinline__ void merge_key_splits(const PartArgs& a, const WaveIn
 // S threads per unit splitting the partitions (merged through LDS like the combine launch).
 template <class S>
 __device__ __forceinline__ void fused_combine(const PartArgs& a, const WaveInfo& wv, char* smem, int* flag_s, int b,
-                                              int count, int first_slot) {
+                                              int count, int first_slot, OwnPartial own) {
   const int tid = threadIdx.x, HG = wv.HG, kg = grp_of(a, HG), g = a.g;
   wait_vm<0>();   // this wave's partial stores are complete
   __syncthreads();
@@ -245,6 +256,13 @@ __device__ __forceinline__ void fused_combine(const PartArgs& a, const WaveInfo&
   const int SUB = count <= 16 ? 1 : (count <= 64 ? 4 : 16);
   const int UNITS = NT / SUB;
   const int sub = tid / UNITS, ui = tid % UNITS;
+  // the thread's own partial (stored by merge_key_splits for unit tid) stays in registers when
+  // the fold gives every unit to one thread in a single round: index among the row's partials
+  if (SUB == 1 && total <= UNITS && own.idx >= 0) {
+    if (first_slot >= 0) own.idx -= first_slot;
+  } else {
+    own.idx = -1;
+  }
   // (the merge's LDS: the waves' tile regions, free by now)
   float* sM = (float*)smem;                          // [SUB][UNITS]
   float* sL = sM + SUB * UNITS;
@@ -267,9 +285,8 @@ __device__ __forceinline__ void fused_combine(const PartArgs& a, const WaveInfo&
     float M = -INFINITY, Ls = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (valid)
-      fold_partials<DV, 8, true>((const float2*)a.part_ml + first, a.part_o + first * DV + d0, stride, count, sub, SUB, a.c,
-                        M, Ls, acc,
-        a.part_ml, a.part_o);
+      fold_partials<DV, 8, true>((const float2*)a.part_ml + first, a.part_o + first * DV + d0, stride, count, sub,
+                                 SUB, a.c, M, Ls, acc, a.part_ml, a.part_o, own);
     if (SUB > 1) {
       if (sub < SUB) {
         sM[sub * UNITS + ui] = M;
@@ -886,6 +903,7 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
       for (int i = 0; i < 4; ++i) o[db][i] += __shfl_xor(o[db][i], 8);
   }
 
+  OwnPartial own;   // (KS == 1 stores in the MFMA layout, not the fold's: nothing kept)
   if (KS == 1) {
     // one wave per kv head: store straight from registers
     if (wave_active && col_valid && !is_lo) {
@@ -896,9 +914,9 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
         store_unit(a, b, row, p, direct, 16 * db + 4 * qd, o[db] * inv, m_run, l_run, db == 0 && qd == 0);
     }
   } else {
-    merge_key_splits<HL, S>(a, wv, smem, b, p, direct, o, m_run, l_run);
+    own = merge_key_splits<HL, S>(a, wv, smem, b, p, direct, o, m_run, l_run);
   }
-  if (a.counters && !direct) fused_combine<S>(a, wv, smem, flag_s, b, count, first_slot);
+  if (a.counters && !direct) fused_combine<S>(a, wv, smem, flag_s, b, count, first_slot, own);
 }
 
 // A piece of work as wave 0 of a workgroup publishes it to the other waves.

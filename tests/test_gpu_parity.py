@@ -304,6 +304,9 @@ DETERMINISM = [
                             len_range=(500, 6000), num_splits=0, seed=46, kv_fp8=True), {}),
     ("d256_rotary_apart", dict(batch=3, num_q_heads=16, num_kv_heads=16, qk_depth=256, ov_depth=256,
                                page_size=64, len_range=(1, 3000), num_splits=0, seed=47, rope_apart=64), {}),
+    # the fold in pass 1 with the folding workgroup's own partial kept in registers
+    ("fused_own_partial", dict(batch=2, num_q_heads=8, num_kv_heads=2, qk_depth=128, seq_lens=[4096, 1000],
+                               num_splits=8, seed=48), {"fused": True}),
 ]
 
 
@@ -316,6 +319,30 @@ def test_determinism_bitwise(name, kw, call):
     print(f"[parity] determinism {name}", flush=True)
     a = api.case_call(dc, return_lse=True, return_o32=True, **call)
     b = api.case_call(dc, return_lse=True, return_o32=True, **call)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+FOLD_EQUALS_COMBINE = [
+    # one thread per unit and at most 8 partitions on both sides: the fold in pass 1 (own
+    # partial from registers: matrix-core kernel with key splits, vector-ALU kernel) and the
+    # combine launch take the same partials in the same order
+    ("mfma_key_splits", dict(batch=2, num_q_heads=8, num_kv_heads=2, qk_depth=128, seq_lens=[4096, 1000],
+                             num_splits=8, seed=49)),
+    ("vector_alu_fp32", dict(batch=2, num_q_heads=4, num_kv_heads=2, qk_depth=128, dtype=torch.float32,
+                             seq_lens=[2000, 700], num_splits=5, seed=50)),
+]
+
+
+@pytest.mark.parametrize("name,kw", FOLD_EQUALS_COMBINE, ids=[c[0] for c in FOLD_EQUALS_COMBINE])
+def test_fused_fold_equals_combine_launch_bitwise(name, kw):
+    case = make_case(name, **kw)
+    dc = to_device(case)
+    print(f"[parity] fused fold == combine launch {name}", flush=True)
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device="cuda")
+    a = api.case_call(dc, return_lse=True, return_o32=True, fused=True, workspace=ws)
+    b = api.case_call(dc, return_lse=True, return_o32=True)
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
