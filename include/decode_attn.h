@@ -163,9 +163,10 @@ int da_workspace_bytes(const da_problem* p, int32_t num_splits, size_t* bytes);
  * num_splits, 0 if it runs the combine launch instead, or an error code as da_supported.
  * The last-arriving workgroup of a group reads the group's partials alone, at the rate of
  * one compute unit, while the combine launch spreads them over the chip; so the merge runs
- * in pass 1 only while those partial outputs stay within 64 KiB: max_splits (or, under
- * equal shares, every worker) times the rows of the head group or 64-column block times
- * Dv x 4 bytes. (On an MI355X that is 1 us faster than the combine launch at 2-32 KiB and
+ * in pass 1 only while those partial outputs stay within 64 KiB: max_splits (under equal
+ * shares, the workers a sequence of max_seq_len keys can meet: at most
+ * ceil(ceil(max_seq_len / 32) / 8) + 1) times the rows of the head group or 64-column block
+ * times Dv x 4 bytes. (On an MI355X that is 1 us faster than the combine launch at 2-32 KiB and
  * 5-19 us slower at 256 KiB-1 MiB.) Each partial array must also stay below 2 GB.
  * (num_splits and the device's compute units as da_workspace_bytes.) */
 int da_fused_applies(const da_problem* p, int32_t num_splits);

@@ -413,7 +413,8 @@ void set_kv_args(const da_problem* p, const da_kv& kv, da::PartArgs* a) {
 // 256 KB (64 partitions of 8 rows), 5 us slower; 1 MiB (8 partitions of 64 latent rows),
 // 19 us slower. The fused entry point therefore folds in pass 1 while a group's partial O
 // stays within kFusedFoldBytes, for the largest partition count the schedule allows a row
-// (max_splits, or every worker under equal shares); forced (mode 2) it always does.
+// (max_splits; under equal shares the workers a sequence of max_seq_len keys can meet);
+// forced (mode 2) it always does.
 constexpr int64_t kFusedFoldBytes = 64 << 10;
 
 int64_t fused_fold_bytes(const da_problem* p, Variant var, int32_t C, int32_t P, int cus) {
@@ -429,7 +430,14 @@ int64_t fused_fold_bytes(const da_problem* p, Variant var, int32_t C, int32_t P,
   } else {
     rows = std::min<int64_t>(64, rows_per_seq(p));   // (sequence, block of 64 columns)
   }
-  return (int64_t)P * rows * p->ov_depth * 4;
+  // partials one row can have: max_splits; under equal shares (P = workers) also at most one
+  // per share its sequence's tiles meet, and every share holds >= kMinShareTiles tiles
+  int64_t parts = P;
+  if (C == 0) {
+    const int64_t tiles = ceil_div(p->max_seq_len > 0 ? p->max_seq_len : 1, kTileKeys);
+    parts = std::min<int64_t>(P, ceil_div(tiles, da::kMinShareTiles) + 1);
+  }
+  return parts * rows * p->ov_depth * 4;
 }
 
 // Fused modes: 0 none (combine launch), 1 where the fold pays, 2 always. Either fused mode

@@ -130,9 +130,13 @@ def test_fused_fold_applies_where_one_workgroup_reads_at_most_64_kib(lib):
     assert applies(gqa, 16) == 0      # 4 kv heads per workgroup: 16 x 16 rows x 512 B = 128 KiB
     assert applies(long_, 64) == 0    # 64 x 8 rows x 512 B = 256 KiB
     assert applies(latent, 8) == 0    # 8 x 64 rows x 2 KiB = 1 MiB
-    # equal shares: every one of the 256 workers may hold a piece of one sequence
-    assert applies(long_, 0) == 0
-    assert applies(paged, 0) == 0
+    # equal shares: a sequence of max_seq_len keys meets at most ceil(tiles / 8) + 1 of the
+    # 256 workers' shares
+    assert applies(long_, 0) == 0     # min(256, 513) x 32 rows x 512 B
+    assert applies(paged, 0) == 0     # 129 x 64 rows x 512 B
+    short = prob(batch=8, num_q_heads=8, num_kv_heads=1, max_pages_per_seq=8, max_seq_len=512)
+    assert applies(short, 0) == 1     # 3 x 8 rows x 512 B = 12 KiB
+    assert applies(prob(batch=8, num_q_heads=8, num_kv_heads=1, max_pages_per_seq=64, max_seq_len=4096), 0) == 0
     assert applies(prob(batch=0), 8) == DA_EINVAL
 
 

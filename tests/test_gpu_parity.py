@@ -481,6 +481,9 @@ FUSED_WHERE_IT_PAYS = [
     # the vector-ALU kernel: 4 partitions of one row
     ("fp32_tiny", dict(batch=1, num_q_heads=1, num_kv_heads=1, qk_depth=128, dtype=torch.float32,
                        seq_lens=[1024], num_splits=4, seed=75)),
+    # equal shares over short sequences: at most ceil(16 tiles / 8) + 1 = 3 pieces of 8 rows
+    ("auto_short_seqs", dict(batch=8, num_q_heads=8, num_kv_heads=1, qk_depth=128, page_size=64,
+                             len_range=(1, 512), num_splits=0, seed=98)),
     # one kv head for all q heads: 2 partitions x 24 rows x 1 KiB (GLM widths) = 48 KiB
     ("glm_mqa_24_heads", dict(batch=2, num_q_heads=24, page_size=64, seq_lens=[1500, 0], num_splits=2, seed=97,
                               rope_apart=64, **GLM_MQA)),
