@@ -5,8 +5,10 @@ Workload (the one the >= 70 %-of-HBM target is stated for): batch 32, 64 q heads
 KV length uniform in [512, 32768] (seed 3: 626 521 keys), page table a seeded
 random permutation of the page pool, splits chosen per sequence.
 
-A step is one call of decode_attn_splitk (partition kernel + LSE combine) on
-inputs already resident in HBM. The K timed steps run one at a time, each after the
+A step is one call of decode_attn_splitk_fused on inputs already resident in HBM: the
+partition kernel, then the LSE combine, either by each group's last-arriving workgroup
+(where that beats a second launch: small sets of partials) or by the combine launch
+(--combine separate forces the latter). The K timed steps run one at a time, each after the
 Infinity Cache has been flushed (1 GiB read and written outside the step's HIP events),
 so that no input is served from the memory-side cache of the step before. Output: one
 JSON line with
@@ -56,9 +58,10 @@ def parse():
     ap.add_argument("--workload", default="paged_gqa")
     ap.add_argument("--num-splits", type=int, default=None, help="override the workload's split count")
     ap.add_argument("--kernel", default="auto", choices=["auto", "fma", "mfma"])
-    ap.add_argument("--combine", default="separate", choices=["separate", "fused", "fused-force"],
-                    help="LSE combine as its own launch, or by each group's last-arriving workgroup (fused: "
-                         "where that pays, as the fused entry point decides; fused-force: always)")
+    ap.add_argument("--combine", default="auto", choices=["auto", "separate", "fused", "fused-force"],
+                    help="auto (= fused): the fused entry point, which folds the partials in each group's "
+                         "last-arriving workgroup where that beats a second launch and runs the combine launch "
+                         "otherwise; separate: always the combine launch; fused-force: always the fold in pass 1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=30.0)
     ap.add_argument("--probe-gib", type=float, default=2.0, help="streaming-read probe size")
@@ -107,7 +110,7 @@ def main():
     plan = api.DecodePlan(dc.q, dc.k_cache, dc.v_cache, dc.page_table, dc.seq_lens, case.scale, case.num_splits,
                           page_size=case.page_size, v_is_k_prefix=case.v_is_k_prefix, ov_depth=case.ov_depth,
                           kernel=args.kernel, out=out,
-                          fused={"separate": False, "fused": True, "fused-force": "force"}[args.combine],
+                          fused={"separate": False, "auto": True, "fused": True, "fused-force": "force"}[args.combine],
                           k_scale=dc.k_scale, v_scale=dc.v_scale, k_rope=dc.k_rope)
     step = plan.run
 
@@ -267,8 +270,9 @@ def main():
             "qk_depth": prob.qk_depth, "ov_depth": Dv, "nope_depth": prob.nope_depth, "page_size": case.page_size,
             "keys": tokens, "max_seq_len": int(case.seq_lens.max()),
             "num_splits": case.num_splits, "chunk_tokens": chunk, "max_splits": max_splits, "kernel": args.kernel,
-            "combine": args.combine if args.combine != "fused" or api.fused_applies(prob, case.num_splits)
-                       else "fused entry point, which runs the combine launch here (fold beyond 64 KiB)",
+            "combine": ("fold in pass 1 (last-arriving workgroup)" if args.combine == "fused-force" or
+                        (args.combine in ("auto", "fused") and api.fused_applies(prob, case.num_splits))
+                        else "combine launch"),
             "kv_bytes": kv_bytes,
         },
         "roofline": {
