@@ -348,6 +348,23 @@ def test_fused_fold_equals_combine_launch_bitwise(name, kw):
         assert torch.equal(x, y)
 
 
+def test_fused_fold_repeated_calls_equal_combine_launch_bitwise():
+    # publication under load: 256 workgroups in 32 groups of 8 per call, the fold in pass 1
+    # (forced) on one workspace for 30 calls in a row, every call bit-identical to the
+    # combine launch (one thread per unit and 8 partitions on both sides: the same fold)
+    case = make_case("fold_repeated", batch=8, num_q_heads=32, num_kv_heads=8, qk_depth=128,
+                     seq_lens=[4096] * 8, num_splits=8, seed=51)
+    dc = to_device(case)
+    print("[parity] fused fold, 30 calls against the combine launch", flush=True)
+    ref = api.case_call(dc, return_lse=True, return_o32=True)
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device="cuda")
+    outs = [api.case_call(dc, return_lse=True, return_o32=True, fused="force", workspace=ws) for _ in range(30)]
+    torch.cuda.synchronize()
+    for i, got in enumerate(outs):
+        for x, y in zip(got, ref):
+            assert torch.equal(x, y), f"call {i}"
+
+
 def test_seq_len_above_max_is_clamped():
     # seq_lens may not exceed max_seq_len; larger values are clamped to it
     case = make_case("clamp", batch=2, num_q_heads=8, num_kv_heads=1, qk_depth=128, page_size=64,
