@@ -643,17 +643,21 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
       else KL = (const DA_LDS char*)sm.tile[s % R];
       const char* pb = sm.pbuf[s & 1] + lane * 8;
       bf16x8 vf[S::kDB], ph[4], pl[4];
-#pragma unroll
-      for (int db = 0; db < S::kDB; ++db) vf[db] = load_v(KL, db);
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
+      auto load_p = [&](int cb) {
         const u32x2 h0 = *(const u32x2*)(pb + ((cb * 2 + 0) * 2 + 0) * 64 * 8);
         const u32x2 h1 = *(const u32x2*)(pb + ((cb * 2 + 0) * 2 + 1) * 64 * 8);
         const u32x2 l0 = *(const u32x2*)(pb + ((cb * 2 + 1) * 2 + 0) * 64 * 8);
         const u32x2 l1 = *(const u32x2*)(pb + ((cb * 2 + 1) * 2 + 1) * 64 * 8);
         ph[cb] = as_bf16x8(u32x4{h0[0], h0[1], h1[0], h1[1]});
         pl[cb] = as_bf16x8(u32x4{l0[0], l0[1], l1[0], l1[1]});
-      }
+      };
+      // P of column block 0, then V, then the other blocks' P: the first products wait for
+      // their own operands only (latent: 60.3 against 61.2 us with all of V first)
+      load_p(0);
+#pragma unroll
+      for (int db = 0; db < S::kDB; ++db) vf[db] = load_v(KL, db);
+#pragma unroll
+      for (int cb = 1; cb < 4; ++cb) load_p(cb);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
