@@ -43,7 +43,7 @@ extern "C" {
 typedef enum {
   DA_OK = 0,
   DA_EINVAL = -1,        /* bad argument: null pointer, bad size, inconsistent shape */
-  DA_EUNSUPPORTED = -2,  /* well-formed problem this build has no kernel for */
+  DA_EUNSUPPORTED = -2,  /* well-formed problem the library has no kernel for */
   DA_EWORKSPACE = -3,    /* workspace pointer null/misaligned or smaller than needed */
   DA_EHIP = -4           /* a HIP runtime call or kernel launch failed */
 } da_status;
