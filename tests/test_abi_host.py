@@ -401,3 +401,10 @@ def test_rotary_columns_apart_need_their_tensor(lib):
     r = lib.decode_attn_partition_kv(ctypes.byref(p8), FAKE, ctypes.byref(kv), FAKE, FAKE, 0.1, 256, 16, FAKE, FAKE,
                                      None)
     assert r == DA_EINVAL and b"k_scale" in lib.da_last_error()
+
+
+def test_binding_fused_modes():
+    from lse_combine_amd import api
+    assert api._fused_mode(False) == 0 and api._fused_mode(True) == 1 and api._fused_mode("force") == 2
+    with pytest.raises(ValueError):
+        api._fused_mode("always")
