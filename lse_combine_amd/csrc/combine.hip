@@ -20,12 +20,13 @@ namespace {
 
 constexpr int kCombineThreads = 256;
 constexpr int kBatch = 8;   // partitions whose loads are in flight together, per thread (fold_partials)
+constexpr int64_t kFewRows = 128;   // rows below which a many-partition row is split into depth bands
 // (the rows each block folds: combine_rows in da_device.h)
 
-template <int DV, int S, int NT = kCombineThreads>
+template <int DV, int S, int NT = kCombineThreads, int BANDS = 1>
 __global__ __launch_bounds__(NT) void combine_kernel(CombineArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[CombineLds<DV, S, NT>::kBytes];
-  combine_rows<DV, S, NT>(a, blockIdx.x, threadIdx.x, lds);
+  combine_rows<DV, S, NT, BANDS>(a, blockIdx.x, threadIdx.x, lds);
 }
 
 }  // namespace
@@ -37,7 +38,16 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   const int64_t pmax = a.meta ? (a.slots - a.B) / a.B + 1 : a.max_splits;
   int S = 1;
   while (S < 32 && (int64_t)S * kBatch < pmax) S *= 2;
-  if (a.Dv == 128) {
+  if (a.Dv == 128 && S >= 8 && rows < kFewRows) {
+    // few rows with many partitions each: every row's depth is cut into 4 bands, one block
+    // each, so that four compute units read a row's partials
+    auto go = [&](auto kern, int nt) { hipLaunchKernelGGL(kern, dim3((unsigned)(rows * 4)), dim3(nt), 0, s, a); };
+    switch (S) {
+      case 8: go(combine_kernel<128, 8, 64, 4>, 64); break;
+      case 16: go(combine_kernel<128, 16, 128, 4>, 128); break;
+      default: go(combine_kernel<128, 32, 256, 4>, 256); break;
+    }
+  } else if (a.Dv == 128) {
     auto go = [&](auto kern, int rpb, int nt = kCombineThreads) {
       hipLaunchKernelGGL(kern, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(nt), 0, s, a);
     };

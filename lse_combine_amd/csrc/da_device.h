@@ -312,19 +312,21 @@ struct CombineLds {
 // formula. With S = 1 this is the plain per-thread combine; S > 1 shortens the dependent
 // load chain of rows with many partitions by a factor S. Every thread of the block calls it
 // (it holds a barrier when S > 1).
-template <int DV, int S, int NT>
+// BANDS > 1 (rows with many partitions, few rows): block blk takes depth band blk % BANDS of
+// row blk / BANDS, so that the row's partials are read by BANDS compute units.
+template <int DV, int S, int NT, int BANDS = 1>
 __device__ __forceinline__ void combine_rows(const CombineArgs& a, int64_t blk, int tid, char* lds) {
-  constexpr int TPR = DV / 4;                       // threads (units) per row
+  constexpr int TPR = DV / 4 / BANDS;               // threads (units) per row in a block
   constexpr int UNITS = NT / S;                     // units per block
   constexpr int RPB = UNITS / TPR;                  // rows per block
-  static_assert(RPB >= 1 && UNITS % TPR == 0, "block shape");
+  static_assert(RPB >= 1 && UNITS % TPR == 0 && (BANDS == 1 || RPB == 1), "block shape");
   float* sM = (float*)lds;                          // [S][UNITS]
   float* sL = sM + S * UNITS;                       // [S][UNITS]
   f32x4* sO = (f32x4*)(sL + S * UNITS);             // [S][UNITS]
 
   const int sub = tid / UNITS, u = tid % UNITS;
-  const int r_in = u / TPR, ch = u % TPR;
-  const int64_t row = blk * RPB + r_in;
+  const int r_in = u / TPR, ch = (int)(blk % BANDS) * TPR + u % TPR;
+  const int64_t row = (blk / BANDS) * RPB + r_in;
   const bool row_ok = row < (int64_t)a.B * a.Hq;
   const int b = row_ok ? (int)(row / a.Hq) : 0;
   // partials of this row: P_b of them, `stride` partial rows apart, from partial row `first`
