@@ -25,7 +25,7 @@ struct PartArgs {
   float* part_o;            // fixed chunks: [B][Hq][max_splits][Dv]; equal shares: [slots][Hq][Dv]
   float* part_ml;           // fixed chunks: [B][Hq][max_splits][2];  equal shares: [slots][Hq][2]
   int32_t* meta;            // equal shares: [B][2] (first slot, partition count) per sequence
-  int32_t* counters;        // fused combine: [B][head groups] arrival counters (zero between
+  int32_t* counters;        // fused combine: [B][head groups or 64-column blocks] arrival counters (zero between
                             // calls); NULL: the combine is a separate launch
   const float* k_scale;     // fp8 caches: per-token scales, tokens innermost ([B][Hkv][Lcap]
   const float* v_scale;     //   or [pages][Hkv][page]); v_scale may be NULL (1)

@@ -216,7 +216,7 @@ __device__ __forceinline__ OwnPartial merge_key_splits(const PartArgs& a, const 
 // Last-arriving-workgroup combine (fa4_splitk_combine_write, fourth paragraph: the writer
 // that completes the set combines all). After storing its partial, every workgroup of a
 // (sequence, kv-head group) publishes it device-wide and counts itself in; the one that
-// brings the count to the number of partitions acquires the others' partials and writes the
+// brings the count to the number of partitions reads the others' partials and writes the
 // final bf16 rows, LSE and fp32 O of the group's heads, then returns the counter to zero for
 // the next call. The counters (one int per (sequence, group)) must be zero before the first
 // call.
