@@ -131,16 +131,19 @@ typedef struct da_problem {
  * message (FA4Config, supported). Supported:
  *  - Dqk == Dv == 128, g <= 16, one query per sequence: f32 (vector-ALU kernel) or bf16
  *    (matrix-core kernel; the vector-ALU one on request with DA_KERNEL_FMA);
- *  - on the matrix-core kernel (bf16 q, separate K and V, q_len x g <= 16, contiguous
- *    cache or pages of a power of two >= 32 keys) the depth pairs Dqk/Dv 128/128,
- *    192/128 and 256/256, with the K/V cache in bf16 or fp8 and optionally the 64 rotary
- *    columns stored apart in bf16 (nope_depth 128 or 192);
+ *  - on the matrix-core kernel (bf16 q, separate K and V, q_len x g <= 16) the depth
+ *    pairs Dqk/Dv 128/128, 192/128 and 256/256, with the K/V cache in bf16 or fp8 and
+ *    optionally the 64 rotary columns stored apart in bf16 (nope_depth 128 or 192);
  *  - with one kv head, on the shared-kv-head kernel (bf16 q, any number of q heads and
  *    q_len): latent 576/512 with V = the first 512 K columns (v_is_k_prefix), and
  *    256/256 with V of its own when q_len x Hq > 16; the 64 rotary columns in the K rows
  *    or stored apart in bf16 (nope_depth 512 or 192). Both also over an fp8 cache with the
- *    rotary columns apart and a contiguous cache or pages of a power of two >= 32 keys
- *    (a V that is the K prefix takes the K scales: v_scale NULL). */
+ *    rotary columns apart (a V that is the K prefix takes the K scales: v_scale NULL).
+ * Page sizes (FA4Config, v_row_major: multi-page tiles of a block-indirected cache): any
+ * page_size for bf16 caches whose K rows hold every q.K column; fp8 caches and rotary
+ * columns stored apart need a contiguous cache or pages of 16 keys or of a power of two
+ * >= 32 (with fp8 on the shared-kv-head kernel and pages of 16 keys, num_pages * 64 bytes
+ * of scales must stay below 2 GiB). */
 int da_supported(const da_problem* p);
 
 /* Split selection (FA4Config, with_splitk: partitions of the K/V sequence).
@@ -219,8 +222,8 @@ int decode_attn_splitk_fused(const da_problem* p, const void* q, const void* k_c
 
 /* The whole decode step over an fp8 cache (FA4Config: an fp8 qkv_dtype with a per-token
  * scale_dtype for K). kv_dtype must be DA_FP8_E4M3, dtype DA_BF16 (q), a matrix-core depth
- * pair (see da_supported), and the cache contiguous or paged with page_size a power of two
- * >= 32.
+ * pair (see da_supported), and the cache contiguous or paged with page_size 16 or a power
+ * of two >= 32.
  * k_cache / v_cache hold E4M3 codes (one byte each, same layouts as above); key t of kv
  * head k reads k_scale * code (fp32 scale of that token and kv head) and V likewise with
  * v_scale (NULL = 1). Scale layout, tokens innermost: contiguous [B][Hkv][kv_capacity],

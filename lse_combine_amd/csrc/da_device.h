@@ -70,6 +70,20 @@ __device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t voff, uint32_t ld
       : "memory");
 }
 
+// The same with 4 bytes per lane (the 64 lanes fill 256 bytes, lane l at 4 l).
+__device__ __forceinline__ void lds_dma4(u32x4 rsrc, uint32_t voff, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %1, %2, 0 offen nt lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"(lds_base)
+      : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const DA_LDS char*)p;
 }

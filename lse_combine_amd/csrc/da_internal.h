@@ -11,7 +11,8 @@ namespace da {
 enum PageMode : int {
   kContiguous = 0,   // row of key t in sequence b = b * kv_capacity + t
   kPagedAligned = 1, // paged, page_size a power of two >= 32: a 32-key tile never crosses a page
-  kPagedGeneral = 2  // paged, any page_size: per-key page lookup
+  kPagedGeneral = 2, // paged, any page_size: per-key page lookup
+  kPagedHalf = 3     // paged, page_size 16: each 16-key half of a 32-key tile is one page
 };
 
 // Everything the partition kernels need; passed by value as the kernel argument.

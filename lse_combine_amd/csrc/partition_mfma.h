@@ -34,7 +34,9 @@
 //
 // Addressing: tiles are 32 keys and partitions start on multiples of 32, so with a
 // contiguous cache or pages of a power of two >= 32 keys a tile is 32 consecutive cache
-// rows: the tile base is a scalar and every lane adds a fixed 32-bit offset. The page
+// rows, and with pages of 16 keys each 16-key half of it is: every load covers one half, its
+// base is a scalar and every lane adds a fixed 32-bit offset. Other page sizes take a
+// per-key page lookup (bf16 caches whose K rows hold every q.K column). The page
 // indices of the partition are staged in LDS once, so no dependent page-table load
 // sits between consecutive prefetches. Loads run one tile ahead: the next tile's K is
 // requested once the current tile's scores are done and its V once the current P.V is
@@ -374,12 +376,13 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
   for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int tid = threadIdx.x, NW = wv.NW;
   // first cache row of the tile starting at t0 (contiguous / aligned pages: the tile
-  // is 32 consecutive rows), and the row of key t in the general paged case
+  // is 32 consecutive rows; pages of 16 keys: the 16-key run starting at t0), and the row
+  // of key t in the general paged case
   auto tile_row0 = [&](int t0) -> int64_t {
     if constexpr (PM == kContiguous) {
       return (int64_t)b * a.kv_capacity + t0;
     } else {
-      const int pi = t0 >> a.page_shift;   // pages are a power of two >= 32 keys
+      const int pi = t0 >> a.page_shift;   // pages are a power of two >= 16 keys
       // an LDS value read at a uniform address: tell the compiler it is uniform; index and
       // value are clamped so that no cache address can leave the page pool
       const int slot = min(max(pi - first_page, 0), kMaxLdsPages - 1);
@@ -388,6 +391,12 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
       const int page = __builtin_amdgcn_readfirstlane(min(max(pages_s[slot], 0), a.num_pages - 1));
       return ((int64_t)page << a.page_shift) + (t0 & (a.page_size - 1));
     }
+  };
+  // first cache row of 16-key half h of the tile at t0, given row0 = tile_row0(t0): every
+  // half is 16 consecutive cache rows (with pages of 16 keys each half is a page of its own)
+  auto half_row0 = [&](int t0, int64_t row0, int h) -> int64_t {
+    if constexpr (PM == kPagedHalf) return h == 0 ? row0 : tile_row0(t0 + 16);
+    else return row0 + 16 * h;
   };
   auto general_row = [&](int t) -> int64_t {
     const int pi = t / a.page_size;
@@ -415,14 +424,15 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
       for (int h = 0; h < 2; ++h) {
         // (the clamp is selected as a vector op; readfirstlane keeps the descriptor scalar)
         const int rows = __builtin_amdgcn_readfirstlane(min(max(last + 1 - 16 * h, 0), 16));
+        const int64_t rowh = half_row0(t0, row0, h);
         const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(kc + (row0 + 16 * h) * krow_bytes + kslice), 0, rows * krow_bytes, kRsrcWord3);
+            (void*)(kc + rowh * krow_bytes + kslice), 0, rows * krow_bytes, kRsrcWord3);
         // bf16: 8 values per load, depth 32l + 8qd; fp8: 16 values, depth 64l + 16qd
 #pragma unroll
         for (int l = 0; l < KT::NL; ++l) T.k[h][l] = buf_load16(rk, koff + 64 * l, 0);
         if constexpr (S::NR > 0) {
           const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
-              (void*)(kr + (row0 + 16 * h) * rrow_bytes + rslice), 0, rows * rrow_bytes, kRsrcWord3);
+              (void*)(kr + rowh * rrow_bytes + rslice), 0, rows * rrow_bytes, kRsrcWord3);
 #pragma unroll
           for (int l = 0; l < S::NR; ++l) T.r[h][l] = buf_load16(rr, roff + 64 * l, 0);
         }
@@ -452,7 +462,7 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
       for (int h = 0; h < 2; ++h) {
         const int rows = __builtin_amdgcn_readfirstlane(min(max(last + 1 - 16 * h, 0), 16));
         const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(vc + (row0 + 16 * h) * vrow_bytes + vslice), 0, rows * vrow_bytes, kRsrcWord3);
+            (void*)(vc + half_row0(t0, row0, h) * vrow_bytes + vslice), 0, rows * vrow_bytes, kRsrcWord3);
 #pragma unroll
         for (int i = 0; i < kLoadsPerHalf; ++i) {
           const int r = kRpi * i + v_row;   // row within the half; the swizzle repeats per half
@@ -507,25 +517,42 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
   auto load_sc = [&](f32x4* ksc, f32x4* vsc, int t0, bool valid = true) {
     const int last = valid ? min(kTile - 1, end - 1 - t0) : -1;
     const int kv_safe = wave_active ? kvh : 0;
-    int64_t base;
-    if constexpr (PM == kContiguous) {
-      base = ((int64_t)b * a.Hkv + kv_safe) * a.kv_capacity + t0;
-    } else {
-      const int slot = min(max((t0 >> a.page_shift) - first_page, 0), kMaxLdsPages - 1);
-      const int page = __builtin_amdgcn_readfirstlane(min(max(pages_s[slot], 0), a.num_pages - 1));
-      base = ((int64_t)page * a.Hkv + kv_safe) * a.page_size + (t0 & (a.page_size - 1));
-    }
+    // scale index of the first key of the run of consecutive keys starting at t
+    auto sc_base = [&](int t) -> int64_t {
+      if constexpr (PM == kContiguous) {
+        return ((int64_t)b * a.Hkv + kv_safe) * a.kv_capacity + t;
+      } else {
+        const int slot = min(max((t >> a.page_shift) - first_page, 0), kMaxLdsPages - 1);
+        const int page = __builtin_amdgcn_readfirstlane(min(max(pages_s[slot], 0), a.num_pages - 1));
+        return ((int64_t)page * a.Hkv + kv_safe) * a.page_size + (t & (a.page_size - 1));
+      }
+    };
     const int nk = __builtin_amdgcn_readfirstlane(max(last + 1, 0));
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(a.k_scale + base), 0, nk * 4, kRsrcWord3);
-    ksc[0] = __builtin_bit_cast(f32x4, buf_load16(rk, 16 * qd, 0));
-    ksc[1] = __builtin_bit_cast(f32x4, buf_load16(rk, 64 + 16 * qd, 0));
-    // the V scales are loaded in every case (from the K scales when there are none, then
-    // replaced by 1 where they are used): the same loads on every path
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((a.v_scale ? a.v_scale : a.k_scale) + base), 0, nk * 4, kRsrcWord3);
-    vsc[0] = __builtin_bit_cast(f32x4, buf_load16(rv, 16 * qd, 0));
-    vsc[1] = __builtin_bit_cast(f32x4, buf_load16(rv, 64 + 16 * qd, 0));
+    const float* vs = a.v_scale ? a.v_scale : a.k_scale;
+    // (the V scales are loaded in every case, from the K scales when there are none, then
+    // replaced by 1 where they are used: the same loads on every path)
+    if constexpr (PM == kPagedHalf) {
+      // each 16-key half of the tile is a page of its own
+      const int64_t base0 = sc_base(t0), base1 = sc_base(t0 + 16);
+      const int n0 = min(nk, 16), n1 = max(nk - 16, 0);
+      const __amdgpu_buffer_rsrc_t rk0 = __builtin_amdgcn_make_buffer_rsrc((void*)(a.k_scale + base0), 0, n0 * 4, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rk1 = __builtin_amdgcn_make_buffer_rsrc((void*)(a.k_scale + base1), 0, n1 * 4, kRsrcWord3);
+      ksc[0] = __builtin_bit_cast(f32x4, buf_load16(rk0, 16 * qd, 0));
+      ksc[1] = __builtin_bit_cast(f32x4, buf_load16(rk1, 16 * qd, 0));
+      const __amdgpu_buffer_rsrc_t rv0 = __builtin_amdgcn_make_buffer_rsrc((void*)(vs + base0), 0, n0 * 4, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rv1 = __builtin_amdgcn_make_buffer_rsrc((void*)(vs + base1), 0, n1 * 4, kRsrcWord3);
+      vsc[0] = __builtin_bit_cast(f32x4, buf_load16(rv0, 16 * qd, 0));
+      vsc[1] = __builtin_bit_cast(f32x4, buf_load16(rv1, 16 * qd, 0));
+    } else {
+      const int64_t base = sc_base(t0);
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(a.k_scale + base), 0, nk * 4, kRsrcWord3);
+      ksc[0] = __builtin_bit_cast(f32x4, buf_load16(rk, 16 * qd, 0));
+      ksc[1] = __builtin_bit_cast(f32x4, buf_load16(rk, 64 + 16 * qd, 0));
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vs + base), 0, nk * 4, kRsrcWord3);
+      vsc[0] = __builtin_bit_cast(f32x4, buf_load16(rv, 16 * qd, 0));
+      vsc[1] = __builtin_bit_cast(f32x4, buf_load16(rv, 64 + 16 * qd, 0));
+    }
   };
   const bool has_vscale = a.v_scale != nullptr;
 
@@ -650,7 +677,7 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int rows = __builtin_amdgcn_readfirstlane(min(max(last + 1 - 16 * h, 0), 16));
-      const u32x4 rv = rsrc_words(vc + (row0 + 16 * h) * vrow_bytes + vslice, (uint32_t)rows * vrow_bytes);
+      const u32x4 rv = rsrc_words(vc + half_row0(t0, row0, h) * vrow_bytes + vslice, (uint32_t)rows * vrow_bytes);
 #pragma unroll
       for (int i = 0; i < kV8PerHalf; ++i) {
         const int r = kV8Rows * i + rr;
@@ -667,7 +694,7 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
     for (int h = 0; h < 2; ++h) {
       const int rows = __builtin_amdgcn_readfirstlane(min(max(last + 1 - 16 * h, 0), 16));
       const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(vc + (row0 + 16 * h) * vrow_bytes + vslice), 0, rows * vrow_bytes, kRsrcWord3);
+          (void*)(vc + half_row0(t0, row0, h) * vrow_bytes + vslice), 0, rows * vrow_bytes, kRsrcWord3);
 #pragma unroll
       for (int i = 0; i < kV8PerHalf; ++i) {
         const int r = kV8Rows * i + rr;
@@ -689,7 +716,7 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
   };
 
   // Segments: the page indices of up to kMaxLdsPages pages are staged in LDS at a time
-  // (one segment for every page size >= 32 with chunks up to 16K keys).
+  // (one segment for every page size >= 32 with chunks up to 16K keys, >= 16 up to 8K).
   int seg_len = end - start;
   if constexpr (PM != kContiguous) {
     const int cap = ((kMaxLdsPages - 1) * a.page_size) / kTile * kTile;
@@ -814,7 +841,7 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const int rows = __builtin_amdgcn_readfirstlane(min(max(last + 1 - 16 * h, 0), 16));
-            const u32x4 rs = rsrc_words(cache + (row0 + 16 * h) * row_bytes + slice, (uint32_t)rows * row_bytes);
+            const u32x4 rs = rsrc_words(cache + half_row0(t0, row0, h) * row_bytes + slice, (uint32_t)rows * row_bytes);
 #pragma unroll
             for (int i = 0; i < kLoadsPerHalf; ++i) {
               const int r = kRpi * i + v_row;
@@ -1115,15 +1142,17 @@ hipError_t launch_hl(const PartArgs& a, int pm, int HG, int KS, hipStream_t s) {
   const dim3 grid = a.workers > 0 ? dim3((unsigned)a.workers, groups) : dim3((unsigned)a.max_splits * groups, (unsigned)a.B);
   const dim3 block(HG * KS * 64);
   const size_t lds = (size_t)HG * KS * S::kWaveBytes;
-  constexpr bool kBase = S::DQK == 128 && S::DV == 128 && S::DR == 0;
   if (a.kv_fp8) {
-    // fp8 caches: contiguous or pages of a power of two >= 32 keys
+    // fp8 caches: contiguous or pages of a power of two >= 16 keys
     switch (pm) {
       case kContiguous:
         hipLaunchKernelGGL((partition_gqa_kernel<HL, kContiguous, true, S>), grid, block, lds, s, a, HG, KS);
         break;
       case kPagedAligned:
         hipLaunchKernelGGL((partition_gqa_kernel<HL, kPagedAligned, true, S>), grid, block, lds, s, a, HG, KS);
+        break;
+      case kPagedHalf:
+        hipLaunchKernelGGL((partition_gqa_kernel<HL, kPagedHalf, true, S>), grid, block, lds, s, a, HG, KS);
         break;
       default:
         return hipErrorInvalidValue;
@@ -1137,9 +1166,12 @@ hipError_t launch_hl(const PartArgs& a, int pm, int HG, int KS, hipStream_t s) {
     case kPagedAligned:
       hipLaunchKernelGGL((partition_gqa_kernel<HL, kPagedAligned, false, S>), grid, block, lds, s, a, HG, KS);
       break;
+    case kPagedHalf:
+      hipLaunchKernelGGL((partition_gqa_kernel<HL, kPagedHalf, false, S>), grid, block, lds, s, a, HG, KS);
+      break;
     default:
-      // per-key page lookup (any page size): the depth-128 shape with inline K rows only
-      if constexpr (kBase) {
+      // per-key page lookup (any page size): K rows that hold every q.K column
+      if constexpr (S::DR == 0) {
         hipLaunchKernelGGL((partition_gqa_kernel<HL, kPagedGeneral, false, S>), grid, block, lds, s, a, HG, KS);
         break;
       } else {

@@ -96,6 +96,8 @@ struct SShape {
   static constexpr int kPerWave = (kBlocks + kDmaWaves - 1) / kDmaWaves;
   static_assert(NJ % 2 == 0 && DN % 64 == 0 && DR % 64 == 0 && DV % 64 == 0, "depths");
   static_assert(kNBytes % 1024 == 0 && kRBytes % 1024 == 0 && kSlot % 1024 == 0, "1 KB load blocks");
+  static_assert((16 * kNRow) % 1024 == 0 && (16 * kRRow) % 1024 == 0 && (16 * kVSrcRow) % 1024 == 0,
+                "16 rows of a region are whole load blocks");
   static_assert(!SHARED || DV <= DN, "a shared V is a prefix of the nope columns");
   static_assert(!F8 || (SHARED && DN == 512) || (!SHARED && DN == 192 && DV == 256),
                 "fp8: the latent form, or nope 192 with a V of 256 of its own");
@@ -266,6 +268,9 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
   const char* lbase[S::kPerWave];
   uint32_t lstride[S::kPerWave], loff[S::kPerWave];
   bool lvalid[S::kPerWave];
+  // pages of 16 keys (each 16-key half of a tile is a page): the block's rows lie in the
+  // second half (row offsets then count from that half), or the block holds scales
+  bool lhalf[S::kPerWave], lsc[S::kPerWave];
   const int dw = w;                 // index among the waves that load
   const bool dma_wave = w < S::kDmaWaves;
 #pragma unroll
@@ -293,8 +298,14 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
       r = q2 / S::kVSrcRow, cs = (q2 - r * S::kVSrcRow) >> 4, gc = cs ^ swz<S::kVSrcRow>(r);
     }
     loff[i] = (uint32_t)r * lstride[i] + 16u * (uint32_t)gc;
+    // (16 rows of every region are whole 1 KB blocks, so all lanes of a block share lane
+    // 0's half)
+    lsc[i] = S::F8 && jb >= S::kScOff;
+    lhalf[i] = !lsc[i] && __builtin_amdgcn_readfirstlane(r) >= 16;
+    if (PM == kPagedHalf && lhalf[i]) loff[i] -= 16u * lstride[i];
   }
-  // cache row of the first key of the tile at t0 (the tile is 32 consecutive rows)
+  // cache row of the first key of the tile at t0 (the tile is 32 consecutive rows; pages of
+  // 16 keys: the 16-key run starting at t0)
   auto tile_row0 = [&](int t0) -> int64_t {
     if constexpr (PM == kContiguous) {
       return (int64_t)b * a.kv_capacity + t0;
@@ -309,7 +320,30 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
   auto issue = [&](int ti) {
     char* dst = sm.tile[ti % R];
     const int t0 = start + ti * kTile;
-    if constexpr (PM != kPagedGeneral) {
+    if constexpr (PM == kPagedHalf) {
+      // pages of 16 keys: a scalar base per region and half; the scales (4 bytes per token)
+      // come one token per lane from the whole scale tensor, lanes past the last valid key
+      // (and lanes 32-63) outside the buffer range, so they read nothing and write zeros
+      const bool live = ti < n_tiles;
+      const int64_t row0 = live ? tile_row0(t0) : 0, row1 = live ? tile_row0(t0 + 16) : 0;
+      const int rows = live ? __builtin_amdgcn_readfirstlane(min(kTile, end - t0)) : 0;
+      const uint32_t rows0 = (uint32_t)min(rows, 16), rows1 = (uint32_t)max(rows - 16, 0);
+      const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(dst));
+      const uint32_t sc_bytes = (uint32_t)a.num_pages * 16u * 4u;
+#pragma unroll
+      for (int i = 0; i < S::kPerWave; ++i) {
+        if (!lvalid[i]) break;
+        const uint32_t ldst = lb + (dw + S::kDmaWaves * i) * 1024;
+        if (S::F8 && lsc[i]) {
+          const uint32_t off = lane < rows ? (uint32_t)(((lane < 16 ? row0 : row1) + (lane & 15)) * 4) : sc_bytes;
+          lds_dma4(rsrc_words(lbase[i], sc_bytes), off, ldst);
+        } else {
+          const u32x4 rs = lhalf[i] ? rsrc_words(lbase[i] + row1 * lstride[i], rows1 * lstride[i])
+                                    : rsrc_words(lbase[i] + row0 * lstride[i], rows0 * lstride[i]);
+          lds_dma16(rs, loff[i], ldst);
+        }
+      }
+    } else if constexpr (PM != kPagedGeneral) {
       // 32 consecutive cache rows: one scalar base per region; the buffer range ends at the
       // last valid row, so a ragged tile's missing rows are not read (and past the last tile
       // nothing is)
@@ -790,9 +824,12 @@ hipError_t launch_shape(const PartArgs& a, int page_mode, hipStream_t s) {
     case kPagedAligned:
       hipLaunchKernelGGL((partition_shared_kernel<S, kPagedAligned>), grid, block, 0, s, a, rope, rope_row);
       break;
+    case kPagedHalf:
+      hipLaunchKernelGGL((partition_shared_kernel<S, kPagedHalf>), grid, block, 0, s, a, rope, rope_row);
+      break;
     default:
       // (fp8: not for the any-page-size form, which reads rows key by key while a tile's
-      // scales are loaded as consecutive rows)
+      // scales are loaded in runs of consecutive tokens)
       if constexpr (S::F8) return hipErrorInvalidValue;
       else hipLaunchKernelGGL((partition_shared_kernel<S, kPagedGeneral>), grid, block, 0, s, a, rope, rope_row);
       break;

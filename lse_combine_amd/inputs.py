@@ -174,6 +174,9 @@ def make_case(name="case", *, batch, num_q_heads, num_kv_heads, qk_depth, ov_dep
         _poison(k, v, pos_lens, pt, page_size)
         if k_rope is not None:
             _poison(k_rope, None, pos_lens, pt, page_size)
+        for sc in (k_scale, v_scale):
+            if sc is not None:   # [rows, Hkv, slots] -> slots second, like the caches
+                _poison(sc.transpose(1, 2), None, pos_lens, pt, page_size)
     sc = scale if scale is not None else 1.0 / math.sqrt(qk_depth)
     return Case(name=name, q=q, k_cache=k, v_cache=v, seq_lens=lens32, page_table=pt,
                 page_size=page_size, scale=sc, num_splits=num_splits,
@@ -194,6 +197,8 @@ def _to_fp8(x, scaled):
 
 
 def _poison(k, v, lens, pt, page_size):
+    """Fill the slots no sequence attends with NaN, in place (k and v are [rows, slots, ...],
+    views included)."""
     nan = float("nan") if k.dtype != torch.uint8 else 0x7F   # (0x7F: an E4M3 NaN code)
     if pt is None:
         for b, L in enumerate(lens.tolist()):

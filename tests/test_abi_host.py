@@ -249,11 +249,13 @@ def test_probe_argument_checks():
 @pytest.mark.parametrize("kw,code", [
     (dict(kv_dtype=2), DA_OK),                                   # paged 64, bf16 q
     (dict(kv_dtype=2, page_size=0, kv_capacity=4096), DA_OK),    # contiguous
-    (dict(kv_dtype=2, page_size=16, max_pages_per_seq=256), DA_EUNSUPPORTED),   # page below the tile
+    (dict(kv_dtype=2, page_size=16, max_pages_per_seq=256), DA_OK),             # a page per half tile
+    (dict(kv_dtype=2, page_size=8, max_pages_per_seq=512), DA_EUNSUPPORTED),    # below the half tile
     (dict(kv_dtype=2, page_size=48, max_pages_per_seq=100), DA_EUNSUPPORTED),   # not a power of two
     (dict(kv_dtype=2, dtype=0), DA_EUNSUPPORTED),                # fp32 q
     (dict(kv_dtype=2, kernel=1), DA_EUNSUPPORTED),               # vector-ALU kernel
-    # latent over fp8: only with the rotary columns apart in bf16 and pages of a power of two
+    # latent over fp8: only with the rotary columns apart in bf16 and pages of 16 keys or a power
+    # of two >= 32
     (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1),
      DA_EUNSUPPORTED),
     (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1,
@@ -262,6 +264,11 @@ def test_probe_argument_checks():
           nope_depth=512, rope_dtype=1, q_len=3, page_size=0, kv_capacity=4096), DA_OK),
     (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1,
           nope_depth=512, rope_dtype=1, page_size=48, max_pages_per_seq=100), DA_EUNSUPPORTED),
+    (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1,
+          nope_depth=512, rope_dtype=1, page_size=16, max_pages_per_seq=256), DA_OK),
+    (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1,
+          nope_depth=512, rope_dtype=1, page_size=16, max_pages_per_seq=256, num_pages=1 << 25),
+     DA_EUNSUPPORTED),                                                       # scales past 2 GiB
     (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=256, ov_depth=256, nope_depth=192,
           rope_dtype=1), DA_OK),                                             # one-kv-head GLM widths
     (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=256, ov_depth=256), DA_EUNSUPPORTED),   # rotary inline
@@ -292,7 +299,9 @@ def test_fp8_entry_points_need_their_scales(lib):
     (dict(q_len=2, page_size=0, kv_capacity=4096), DA_OK),
     (dict(q_len=3, num_q_heads=16, num_kv_heads=2), DA_EUNSUPPORTED),   # 24 columns
     (dict(q_len=2, dtype=0), DA_EUNSUPPORTED),                     # vector-ALU kernel
-    (dict(q_len=2, page_size=16, max_pages_per_seq=256), DA_EUNSUPPORTED),
+    (dict(q_len=2, page_size=16, max_pages_per_seq=256), DA_OK),
+    (dict(q_len=2, page_size=48, max_pages_per_seq=100), DA_OK),   # per-key page lookup
+    (dict(q_len=2, page_size=48, max_pages_per_seq=100, kv_dtype=2), DA_EUNSUPPORTED),
     (dict(q_len=2, kv_dtype=2), DA_OK),
     (dict(q_len=17), DA_EINVAL),
     (dict(q_len=2, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1), DA_OK),
@@ -350,7 +359,11 @@ def test_binding_refuses_output_buffers_without_every_row():
     (dict(qk_depth=256, ov_depth=256, nope_depth=-1), DA_EINVAL),
     (dict(qk_depth=256, ov_depth=128), DA_EUNSUPPORTED),
     (dict(qk_depth=256, ov_depth=256, dtype=0), DA_EUNSUPPORTED),
-    (dict(qk_depth=256, ov_depth=256, page_size=16, max_pages_per_seq=256), DA_EUNSUPPORTED),
+    (dict(qk_depth=256, ov_depth=256, page_size=16, max_pages_per_seq=256), DA_OK),
+    (dict(qk_depth=256, ov_depth=256, page_size=24, max_pages_per_seq=200), DA_OK),   # per-key page lookup
+    (dict(qk_depth=256, ov_depth=256, nope_depth=192, rope_dtype=1, page_size=24, max_pages_per_seq=200),
+     DA_EUNSUPPORTED),                                             # rotary apart: no per-key lookup
+    (dict(qk_depth=192, ov_depth=128, kv_dtype=2, page_size=16, max_pages_per_seq=256), DA_OK),
     (dict(qk_depth=256, ov_depth=256, kernel=1), DA_EUNSUPPORTED),
     (dict(qk_depth=256, ov_depth=256, num_q_heads=34, num_kv_heads=2), DA_EUNSUPPORTED),   # group 17
 ])

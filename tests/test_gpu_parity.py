@@ -62,8 +62,8 @@ CASES = [
                              seq_lens=[33, 1500, 64], num_splits=2, seed=27), "auto"),
     ("bf16_g16_paged32", dict(batch=2, num_q_heads=32, num_kv_heads=2, qk_depth=128, page_size=32,
                               seq_lens=[777, 2048], num_splits=3, seed=28), "auto"),
-    ("bf16_g8_paged16_general", dict(batch=3, num_q_heads=8, num_kv_heads=1, qk_depth=128, page_size=16,
-                                     seq_lens=[1000, 15, 257], num_splits=4, seed=29), "auto"),
+    ("bf16_g8_paged16", dict(batch=3, num_q_heads=8, num_kv_heads=1, qk_depth=128, page_size=16,
+                             seq_lens=[1000, 15, 257], num_splits=4, seed=29), "auto"),
     ("bf16_g2_paged48_general", dict(batch=2, num_q_heads=4, num_kv_heads=2, qk_depth=128, page_size=48,
                                      seq_lens=[1000, 97], num_splits=0, seed=30), "auto"),
     ("bf16_g8_one_split", dict(batch=3, num_q_heads=8, num_kv_heads=1, qk_depth=128, page_size=64,
@@ -79,7 +79,7 @@ CASES = [
                                            seed=34, v_is_k_prefix=True), "auto"),
     ("latent_g16_contig", dict(batch=3, num_q_heads=16, num_kv_heads=1, qk_depth=576, ov_depth=512,
                                seq_lens=[100, 33, 1], num_splits=2, seed=35, v_is_k_prefix=True), "auto"),
-    ("latent_g48_paged16_general", dict(batch=2, num_q_heads=48, num_kv_heads=1, qk_depth=576, ov_depth=512,
+    ("latent_g48_paged16", dict(batch=2, num_q_heads=48, num_kv_heads=1, qk_depth=576, ov_depth=512,
                                         page_size=16, seq_lens=[517, 64], num_splits=0, seed=36,
                                         v_is_k_prefix=True), "auto"),
     # 80 heads: one full block of 64 and a second block with one of its four head blocks
@@ -186,8 +186,8 @@ SHARED = [
                                       seed=160, rope_apart=64, **LATENT)),
     ("latent_apart_g128_contig", dict(batch=3, num_q_heads=128, seq_lens=[100, 33, 1], num_splits=2, seed=161,
                                       rope_apart=64, **LATENT)),
-    ("latent_apart_g40_paged16_general", dict(batch=2, num_q_heads=40, page_size=16, seq_lens=[517, 64],
-                                              num_splits=0, seed=162, rope_apart=64, **LATENT)),
+    ("latent_apart_g40_paged16", dict(batch=2, num_q_heads=40, page_size=16, seq_lens=[517, 64],
+                                      num_splits=0, seed=162, rope_apart=64, **LATENT)),
     ("latent_q2_g64_paged64", dict(batch=3, num_q_heads=64, page_size=64, seq_lens=[1, 900, 2100], num_splits=3,
                                    seed=163, q_len=2, **LATENT)),
     ("latent_q3_g20_apart_paged32", dict(batch=2, num_q_heads=20, page_size=32, seq_lens=[2, 1500], num_splits=2,
@@ -741,6 +741,89 @@ def test_multiquery_fused_combine():
         out, lse, o32 = api.case_call(dc, return_lse=True, return_o32=True, fused="force", workspace=ws)
         torch.cuda.synchronize()
         assert_parity(out, lse, o32, O, LSE, what=f"multi-query fused call {rep}")
+
+
+# ---------------------------------------------------------------------------
+# page sizes: pages of 16 keys (each half of a 32-key tile is a page) on every form, and
+# the per-key page lookup (any page size) on bf16 caches whose K rows hold every q.K
+# column; ragged last tiles end in either half, poisoned cases fill every slot no
+# sequence attends (codes, rotary columns and fp8 scales) with NaN
+# ---------------------------------------------------------------------------
+PAGE_FORMS = [
+    ("fp8_g8_paged16_auto", dict(batch=4, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=16,
+                                 seq_lens=[1201, 17, 0, 2500], num_splits=0, seed=130, kv_fp8=True)),
+    ("fp8_g4_paged16_splits3_poisoned", dict(batch=3, num_q_heads=8, num_kv_heads=2, qk_depth=128, page_size=16,
+                                             seq_lens=[100, 1, 1025], num_splits=3, seed=131, kv_fp8=True,
+                                             poison=True, spare_pages=3)),
+    ("fp8_g16_paged16_two_mfma", dict(batch=2, num_q_heads=32, num_kv_heads=2, qk_depth=128, page_size=16,
+                                      seq_lens=[777, 2048], num_splits=3, seed=132, kv_fp8=True)),
+    ("fp8_g8_paged16_no_v_scale", dict(batch=3, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=16,
+                                       seq_lens=[1000, 64, 2500], num_splits=0, seed=133, kv_fp8=True,
+                                       v_scaled=False)),
+    ("q2_g8_paged16_auto", dict(batch=4, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=16,
+                                seq_lens=[1, 517, 1201, 3000], num_splits=0, seed=134, q_len=2)),
+    ("q2_fp8_g8_paged16", dict(batch=3, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=16,
+                               seq_lens=[33, 1000, 2500], num_splits=0, seed=135, q_len=2, kv_fp8=True)),
+    ("d192_apart_g8_paged16", dict(batch=3, num_q_heads=16, num_kv_heads=2, qk_depth=192, ov_depth=128,
+                                   page_size=16, seq_lens=[1000, 33, 2100], num_splits=0, seed=136,
+                                   rope_apart=64)),
+    ("d256_apart_fp8_g4_paged16_poisoned", dict(batch=3, num_q_heads=8, num_kv_heads=2, qk_depth=256,
+                                                ov_depth=256, page_size=16, seq_lens=[100, 1, 1025],
+                                                num_splits=0, seed=137, rope_apart=64, kv_fp8=True, poison=True,
+                                                spare_pages=3)),
+    ("d256_inline_fp8_g8_paged16", dict(batch=2, num_q_heads=16, num_kv_heads=2, qk_depth=256, ov_depth=256,
+                                        page_size=16, seq_lens=[1200, 45], num_splits=2, seed=138, kv_fp8=True)),
+    ("d192_apart_fp8_q2_g1_paged16", dict(batch=3, num_q_heads=2, num_kv_heads=2, qk_depth=192, ov_depth=128,
+                                          page_size=16, seq_lens=[2, 900, 2048], num_splits=0, seed=139,
+                                          rope_apart=64, kv_fp8=True, q_len=2)),
+    # one kv head for all q heads, pages of 16 keys
+    ("latent_g64_inline_paged16", dict(batch=2, num_q_heads=64, page_size=16, seq_lens=[700, 1313], num_splits=3,
+                                       seed=140, **LATENT)),
+    ("latent_fp8_g64_paged16", dict(batch=3, num_q_heads=64, page_size=16, seq_lens=[700, 1313, 17],
+                                    num_splits=3, seed=141, rope_apart=64, kv_fp8=True, **LATENT)),
+    ("latent_fp8_g128_paged16_poisoned", dict(batch=3, num_q_heads=128, page_size=16, seq_lens=[100, 1, 1025],
+                                              num_splits=2, seed=142, rope_apart=64, kv_fp8=True, poison=True,
+                                              spare_pages=3, **LATENT)),
+    ("glm_mqa_fp8_q2_g32_paged16", dict(batch=3, num_q_heads=32, page_size=16, seq_lens=[1, 700, 1700],
+                                        num_splits=2, seed=143, q_len=2, rope_apart=64, kv_fp8=True, **GLM_MQA)),
+    ("glm_mqa_fp8_no_v_scale_paged16_poisoned", dict(batch=3, num_q_heads=64, page_size=16,
+                                                     seq_lens=[100, 1, 1025], num_splits=2, seed=144,
+                                                     rope_apart=64, kv_fp8=True, v_scaled=False, poison=True,
+                                                     spare_pages=3, **GLM_MQA)),
+    ("glm_mqa_apart_g64_paged16", dict(batch=2, num_q_heads=64, page_size=16, seq_lens=[1500, 333], num_splits=3,
+                                       seed=145, rope_apart=64, **GLM_MQA)),
+    # per-key page lookup
+    ("q2_g8_paged48_general", dict(batch=3, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=48,
+                                   seq_lens=[1, 1000, 2100], num_splits=0, seed=146, q_len=2)),
+    ("q3_g4_paged8_general_splits3", dict(batch=3, num_q_heads=8, num_kv_heads=2, qk_depth=128, page_size=8,
+                                          seq_lens=[2, 700, 1500], num_splits=3, seed=147, q_len=3)),
+    ("d192_inline_g8_paged48_general", dict(batch=3, num_q_heads=16, num_kv_heads=2, qk_depth=192, ov_depth=128,
+                                            page_size=48, seq_lens=[1000, 33, 2100], num_splits=0, seed=148)),
+    ("d256_inline_g4_paged24_general_poisoned", dict(batch=3, num_q_heads=8, num_kv_heads=2, qk_depth=256,
+                                                     ov_depth=256, page_size=24, seq_lens=[100, 1, 1025],
+                                                     num_splits=0, seed=149, poison=True, spare_pages=3)),
+    ("d256_inline_q2_g8_paged8_general", dict(batch=2, num_q_heads=16, num_kv_heads=2, qk_depth=256,
+                                              ov_depth=256, page_size=8, seq_lens=[900, 2], num_splits=2,
+                                              seed=150, q_len=2)),
+    ("latent_apart_g40_paged48_general", dict(batch=2, num_q_heads=40, page_size=48, seq_lens=[517, 64],
+                                              num_splits=0, seed=151, rope_apart=64, **LATENT)),
+    ("latent_g24_paged8_general", dict(batch=2, num_q_heads=24, page_size=8, seq_lens=[300, 45], num_splits=2,
+                                       seed=152, **LATENT)),
+]
+
+
+@pytest.mark.parametrize("name,kw", PAGE_FORMS, ids=[c[0] for c in PAGE_FORMS])
+def test_page_size_forms(name, kw):
+    # the combine launch, then the fold in pass 1 on the same inputs
+    case = make_case(name, **kw)
+    print(f"[parity] page sizes {name}", flush=True)
+    dc = to_device(case)
+    O, LSE = oracle_for(case)
+    for fused in (False, "force"):
+        out, lse, o32 = api.case_call(dc, return_lse=True, return_o32=True, fused=fused)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o32).all()
+        assert_parity(out, lse, o32, O, LSE, what=f"page sizes {name} fused={fused}")
 
 
 # ---------------------------------------------------------------------------
