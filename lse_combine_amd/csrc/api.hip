@@ -95,7 +95,7 @@ int check_problem(const da_problem* p, Variant* var) {
   // columns, and GLM-style 256/256 (nope 192, V of its own) once q_len x group exceeds the
   // 16 MFMA columns of the GQA kernel; the 64 rotary columns in the K rows or stored apart.
   // Both take an fp8 cache: nope codes (and a V of its own) with per-token scales, the
-  // rotary columns apart in bf16.
+  // rotary columns apart in bf16 or codes in the K rows (scaled with them).
   const bool latent = p->qk_depth == 576 && p->ov_depth == 512;
   const bool glm_mqa = p->qk_depth == 256 && p->ov_depth == 256 && !p->v_is_k_prefix && p->num_kv_heads == 1 &&
                        ql * g > 16;
@@ -110,12 +110,10 @@ int check_problem(const da_problem* p, Variant* var) {
                   p->qk_depth, p->ov_depth, nope_apart, p->nope_depth);
     if (p->nope_depth > 0 && p->rope_dtype != DA_BF16)
       return fail(DA_EUNSUPPORTED, "rotary columns stored apart must be bf16 (rope_dtype %d)", p->rope_dtype);
-    if (p->kv_dtype == DA_FP8_E4M3 && (p->nope_depth != nope_apart || (p->page_size != 0 && !run_pages(p->page_size))))
+    if (p->kv_dtype == DA_FP8_E4M3 && p->page_size != 0 && !run_pages(p->page_size))
       return fail(DA_EUNSUPPORTED,
-                  "fp8 on the shared-kv-head kernel: the 64 rotary columns stored apart in bf16 (nope_depth "
-                  "%d) and a contiguous cache or pages of 16 keys or a power of two >= 32 (got depth %d/%d, "
-                  "nope_depth %d, page_size %d)",
-                  nope_apart, p->qk_depth, p->ov_depth, p->nope_depth, p->page_size);
+                  "fp8 on the shared-kv-head kernel: a contiguous cache or pages of 16 keys or a power of two "
+                  ">= 32 (got page_size %d)", p->page_size);
     // (pages of 16 keys: the per-token scales are addressed from the start of their tensor)
     if (p->kv_dtype == DA_FP8_E4M3 && p->page_size == kTileKeys / 2 && (int64_t)p->num_pages * 16 * 4 >= INT32_MAX)
       return fail(DA_EUNSUPPORTED, "fp8 on the shared-kv-head kernel with pages of 16 keys: at most %d pages (got %d)",

@@ -64,18 +64,19 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 // Depths of one instantiation: DN nope columns and DR rotary columns make the q.K depth; V
 // has DV columns and is either the first DV nope columns (SHARED) or a cache of its own.
 // F8: the nope columns (and a V of its own) are E4M3 codes with per-token scales; the rotary
-// columns stay bf16, stored apart. A V that is a prefix of the nope columns is read as code x
-// the token's K scale, a V of its own as code x its V scale.
-template <int DN_, int DR_, int DV_, bool SHARED_, bool F8_ = false>
+// columns stay bf16, stored apart, or (RF8) are codes in the K rows, scaled with them. A V that
+// is a prefix of the nope columns is read as code x the token's K scale, a V of its own as
+// code x its V scale.
+template <int DN_, int DR_, int DV_, bool SHARED_, bool F8_ = false, bool RF8_ = false>
 struct SShape {
   static constexpr int DN = DN_, DR = DR_, DV = DV_;
-  static constexpr bool SHARED = SHARED_, F8 = F8_;
+  static constexpr bool SHARED = SHARED_, F8 = F8_, RF8 = RF8_;
   static constexpr int DQK = DN + DR;
   static constexpr int NJ = DQK / 32;            // 32-deep k-steps of q.K
   static constexpr int NJN = DN / 32;            // ... over the nope columns
   static constexpr int kElt = F8 ? 1 : 2;        // bytes per cached nope / V element
   static constexpr int kNRow = DN * kElt;        // LDS bytes of one row, per region
-  static constexpr int kRRow = DR * 2;
+  static constexpr int kRRow = DR * (RF8 ? 1 : 2);
   static constexpr int kVSrcRow = DV * kElt;     // ... of the V region (a V of its own)
   static constexpr int kVCols = DV / 4;          // V columns of one P.V wave
   static constexpr int kDB = kVCols / 16;        // its 16-deep O blocks
@@ -99,6 +100,7 @@ struct SShape {
   static_assert((16 * kNRow) % 1024 == 0 && (16 * kRRow) % 1024 == 0 && (16 * kVSrcRow) % 1024 == 0,
                 "16 rows of a region are whole load blocks");
   static_assert(!SHARED || DV <= DN, "a shared V is a prefix of the nope columns");
+  static_assert(!RF8 || F8, "rotary codes come with an fp8 cache");
   static_assert(!F8 || (SHARED && DN == 512) || (!SHARED && DN == 192 && DV == 256),
                 "fp8: the latent form, or nope 192 with a V of 256 of its own");
 };
@@ -140,11 +142,13 @@ static_assert(sizeof(XArrays) <= kPBytes, "exchange arrays fit a P buffer");
 //    halves, so swz(r) = (r >> 1) & 7; the XOR stays within 8-chunk groups.
 //  - rows of 192 bytes (GLM nope as fp8 codes): not swizzled. The stride is 48 banks, so
 //    16 rows fall on 4 bank phases: their 8-byte operand reads conflict four ways (six such
-//    reads per tile and wave, a few dozen clocks).
+//    reads per tile and wave, a few dozen clocks). Rows of 64 bytes (rotary columns as fp8
+//    codes in the K rows) likewise: a four-way conflict on two reads per tile and wave.
 template <int RB>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (RB == 192) return 0;
-  static_assert(RB == 192 || RB % 256 == 0 || RB % 256 == 128, "row strides of 128 + 256 k, 256 k or 192 bytes");
+  if constexpr (RB == 192 || RB == 64) return 0;
+  static_assert(RB == 192 || RB == 64 || RB % 256 == 0 || RB % 256 == 128,
+                "row strides of 128 + 256 k, 256 k, 192 or 64 bytes");
   if constexpr (RB % 256 == 0) return ((r & 7) << 1) | ((r >> 3) & 1);
   else return (r >> 1) & 7;
 }
@@ -470,14 +474,22 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
       f32x4 vs = f32x4{1.f, 1.f, 1.f, 1.f};   // F8: their V scales (the K scales for a shared V)
       if constexpr (S::F8) {
         // all nope codes (2 registers per step) and the rotary operands are requested first;
-        // a step's codes are widened to bf16 just before its products. The nope and rotary
-        // parts are summed apart: the K scale multiplies the nope part only.
+        // a step's codes are widened to bf16 just before its products. Rotary columns stored
+        // apart (bf16) are summed apart: the K scale multiplies the nope part only. Rotary
+        // codes in the K rows (RF8: step j reads the 8 codes of depth 32 (j - NJN) + 8 qd of
+        // the unswizzled 64-byte rotary row) join the nope sum and take the same scale.
         u32x2 kc[S::NJN];
         bf16x8 krp[S::NJ - S::NJN];
+        u32x2 kcr[S::NJ - S::NJN];
 #pragma unroll
         for (int j = 0; j < S::NJN; ++j) kc[j] = load_k8(KL, j);
 #pragma unroll
-        for (int j = S::NJN; j < S::NJ; ++j) krp[j - S::NJN] = load_k(KL, j);
+        for (int j = S::NJN; j < S::NJ; ++j) {
+          if constexpr (S::RF8)
+            kcr[j - S::NJN] = *(const DA_LDS u32x2*)(KL + S::kNBytes + r * S::kRRow + 32 * (j - S::NJN) + 8 * qd);
+          else
+            krp[j - S::NJN] = load_k(KL, j);
+        }
         ks = *(const DA_LDS f32x4*)(KL + S::kScOff + 4 * (16 * kh + 4 * qd));
         if constexpr (!S::SHARED) {
           if (a.v_scale) vs = *(const DA_LDS f32x4*)(KL + S::kVScOff + 4 * (16 * kh + 4 * qd));
@@ -492,14 +504,24 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
           acc[1][j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][j], acc[1][j & 1], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (S::RF8) {
+#pragma unroll
+          for (int j = S::NJN; j < S::NJ; ++j) {
+            const bf16x8 kf = fp8x8_to_bf16x8(kcr[j - S::NJN][0], kcr[j - S::NJN][1]);
+            acc[0][j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][j], acc[0][j & 1], 0, 0, 0);
+            acc[1][j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][j], acc[1][j & 1], 0, 0, 0);
+          }
+        }
 #pragma unroll
         for (int bi = 0; bi < 2; ++bi) acc[bi][0] = (acc[bi][0] + acc[bi][1]) * ks;
 #pragma unroll
         for (int bi = 0; bi < 2; ++bi) acc[bi][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (!S::RF8) {
 #pragma unroll
-        for (int j = S::NJN; j < S::NJ; ++j) {
-          acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(krp[j - S::NJN], qf[0][j], acc[0][1], 0, 0, 0);
-          acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(krp[j - S::NJN], qf[1][j], acc[1][1], 0, 0, 0);
+          for (int j = S::NJN; j < S::NJ; ++j) {
+            acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(krp[j - S::NJN], qf[0][j], acc[0][1], 0, 0, 0);
+            acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(krp[j - S::NJN], qf[1][j], acc[1][1], 0, 0, 0);
+          }
         }
       } else {
         bf16x8 kf[S::NJ];
@@ -811,8 +833,9 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
 template <class S>
 hipError_t launch_shape(const PartArgs& a, int page_mode, hipStream_t s) {
   // rotary columns: stored apart (k_rope rows of DR bf16), or the last DR of each K row
-  const char* rope = a.k_rope ? (const char*)a.k_rope : (const char*)a.k + S::DN * 2;
-  const uint32_t rope_row = a.k_rope ? (uint32_t)S::DR * 2 : (uint32_t)a.Dk * 2;
+  // (bf16, or codes with an fp8 cache)
+  const char* rope = a.k_rope ? (const char*)a.k_rope : (const char*)a.k + S::DN * S::kElt;
+  const uint32_t rope_row = a.k_rope ? (uint32_t)S::DR * 2 : (uint32_t)a.Dk * S::kElt;
   // x = partition, y = block of 64 columns, z = sequence: with 8 partitions the column blocks
   // of a (sequence, partition) are 8 workgroup ids apart (same XCD under round-robin
   // dispatch, so the second read of each tile is an L2 hit)
@@ -846,14 +869,18 @@ hipError_t launch_partition_shared(const PartArgs& a, int page_mode, hipStream_t
   if (a.Hkv != 1) return hipErrorInvalidValue;
   const bool rope_apart = a.k_rope != nullptr;
   if (a.kv_fp8) {
-    // latent over an fp8 cache: nope codes with per-token K scales, rotary columns bf16 apart
-    if (a.Dqk == 576 && a.Dv == 512 && a.v == a.k && a.Dk == 512 && rope_apart && a.k_scale && !a.v_scale &&
-        page_mode != kPagedGeneral)
-      return launch_shape<SShape<512, 64, 512, true, true>>(a, page_mode, s);
+    if (page_mode == kPagedGeneral || !a.k_scale) return hipErrorInvalidValue;
+    // latent over an fp8 cache: nope codes with per-token K scales, the rotary columns bf16
+    // apart or codes in the K rows
+    if (a.Dqk == 576 && a.Dv == 512 && a.v == a.k && !a.v_scale) {
+      if (rope_apart && a.Dk == 512) return launch_shape<SShape<512, 64, 512, true, true>>(a, page_mode, s);
+      if (!rope_apart && a.Dk == 576) return launch_shape<SShape<512, 64, 512, true, true, true>>(a, page_mode, s);
+    }
     // one kv head with GLM widths: nope 192 and V 256 (its own, optional V scales) as codes
-    if (a.Dqk == 256 && a.Dv == 256 && a.v != a.k && a.Dk == 192 && rope_apart && a.k_scale &&
-        page_mode != kPagedGeneral)
-      return launch_shape<SShape<192, 64, 256, false, true>>(a, page_mode, s);
+    if (a.Dqk == 256 && a.Dv == 256 && a.v != a.k) {
+      if (rope_apart && a.Dk == 192) return launch_shape<SShape<192, 64, 256, false, true>>(a, page_mode, s);
+      if (!rope_apart && a.Dk == 256) return launch_shape<SShape<192, 64, 256, false, true, true>>(a, page_mode, s);
+    }
     return hipErrorInvalidValue;
   }
   if (a.Dqk == 576 && a.Dv == 512 && a.v == a.k && a.Dk == (rope_apart ? 512 : 576))

@@ -274,6 +274,11 @@ WORKLOADS = {
     "glm_mqa_fp8": dict(seed=7, batch=16, num_q_heads=128, num_kv_heads=1, qk_depth=256, ov_depth=256,
                         dtype=torch.bfloat16, page_size=64, seq_lens=[8192] * 16, num_splits=8, rope_apart=64,
                         kv_fp8=True),
+    # the latent workload over an fp8 cache with the 64 rotary columns as codes in the K rows:
+    # one per-token scale for all 576 columns, V = the first 512 codes (same draws as "latent")
+    "latent_fp8_inline": dict(seed=5, batch=16, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512,
+                              dtype=torch.bfloat16, page_size=64, seq_lens=[8192] * 16, num_splits=8,
+                              v_is_k_prefix=True, kv_fp8=True),
     # one q head per kv head (multi-head attention, group 1): batch 32, 32 heads, head dim
     # 128, bf16, page 64, L_b ~ U[512, 8192], automatic splits
     "paged_mha": dict(seed=8, batch=32, num_q_heads=32, num_kv_heads=32, qk_depth=128,

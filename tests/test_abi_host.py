@@ -254,10 +254,10 @@ def test_probe_argument_checks():
     (dict(kv_dtype=2, page_size=48, max_pages_per_seq=100), DA_EUNSUPPORTED),   # not a power of two
     (dict(kv_dtype=2, dtype=0), DA_EUNSUPPORTED),                # fp32 q
     (dict(kv_dtype=2, kernel=1), DA_EUNSUPPORTED),               # vector-ALU kernel
-    # latent over fp8: only with the rotary columns apart in bf16 and pages of 16 keys or a power
-    # of two >= 32
+    # latent over fp8: the rotary columns apart in bf16 or as codes in the K rows, pages of 16
+    # keys or a power of two >= 32
     (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1),
-     DA_EUNSUPPORTED),
+     DA_OK),                                                                 # rotary codes in the K rows
     (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1,
           nope_depth=512, rope_dtype=1), DA_OK),
     (dict(kv_dtype=2, num_q_heads=16, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1,
@@ -271,7 +271,9 @@ def test_probe_argument_checks():
      DA_EUNSUPPORTED),                                                       # scales past 2 GiB
     (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=256, ov_depth=256, nope_depth=192,
           rope_dtype=1), DA_OK),                                             # one-kv-head GLM widths
-    (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=256, ov_depth=256), DA_EUNSUPPORTED),   # rotary inline
+    (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=256, ov_depth=256), DA_OK),   # rotary inline
+    (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=256, ov_depth=256, page_size=48,
+          max_pages_per_seq=100), DA_EUNSUPPORTED),
     (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=256, ov_depth=256, nope_depth=192,
           rope_dtype=1, page_size=48, max_pages_per_seq=100), DA_EUNSUPPORTED),
     (dict(kv_dtype=7), DA_EINVAL),

@@ -230,6 +230,19 @@ SHARED = [
                                         num_splits=2, seed=188, q_len=2, rope_apart=64, kv_fp8=True, **GLM_MQA)),
     ("glm_mqa_fp8_poisoned", dict(batch=3, num_q_heads=64, page_size=64, seq_lens=[100, 1, 1025], num_splits=2,
                                   seed=189, rope_apart=64, kv_fp8=True, poison=True, spare_pages=3, **GLM_MQA)),
+    # fp8 caches with the rotary columns as codes in the K rows (scaled with the nope columns)
+    ("latent_fp8_inline_g64_paged64", dict(batch=2, num_q_heads=64, page_size=64, seq_lens=[700, 1313],
+                                           num_splits=3, seed=190, kv_fp8=True, **LATENT)),
+    ("latent_fp8_inline_g128_contig_ragged", dict(batch=3, num_q_heads=128, seq_lens=[100, 33, 1], num_splits=2,
+                                                  seed=191, kv_fp8=True, **LATENT)),
+    ("latent_fp8_inline_q2_g40_paged16_poisoned", dict(batch=3, num_q_heads=40, page_size=16,
+                                                       seq_lens=[100, 1, 1025], num_splits=2, seed=192, q_len=2,
+                                                       kv_fp8=True, poison=True, spare_pages=3, **LATENT)),
+    ("glm_mqa_fp8_inline_g64_paged32", dict(batch=2, num_q_heads=64, page_size=32, seq_lens=[1500, 333],
+                                            num_splits=3, seed=193, kv_fp8=True, **GLM_MQA)),
+    ("glm_mqa_fp8_inline_no_v_scale_paged16", dict(batch=3, num_q_heads=32, page_size=16, seq_lens=[1, 700, 1700],
+                                                   num_splits=0, seed=194, kv_fp8=True, v_scaled=False,
+                                                   **GLM_MQA)),
 ]
 
 
@@ -246,8 +259,9 @@ def test_shared_kv_head_parity(name, kw):
 
 
 @pytest.mark.parametrize("kw", [dict(rope_apart=64, **GLM_MQA), dict(rope_apart=64, **LATENT),
-                                dict(rope_apart=64, kv_fp8=True, **LATENT), dict(rope_apart=64, kv_fp8=True, **GLM_MQA)],
-                         ids=["glm_mqa_apart", "latent_apart", "latent_fp8", "glm_mqa_fp8"])
+                                dict(rope_apart=64, kv_fp8=True, **LATENT), dict(rope_apart=64, kv_fp8=True, **GLM_MQA),
+                                dict(kv_fp8=True, **LATENT)],
+                         ids=["glm_mqa_apart", "latent_apart", "latent_fp8", "glm_mqa_fp8", "latent_fp8_inline"])
 def test_shared_kv_head_large_logits_take_the_second_pass(kw):
     case = make_case("big_shared", batch=2, num_q_heads=64, page_size=64, seq_lens=[1300, 700], num_splits=2,
                      seed=176, q_scale=64.0, **kw)
@@ -648,7 +662,8 @@ def test_combine_only_on_oracle_partials(Dv, P):
 # with the oracle: the method is an exact re-association of the definition, so no row may
 # differ beyond the stated tolerances (the oracle runs the largest of these in seconds).
 FULL_WORKLOADS = ["tiny", "gqa", "paged_gqa", "long", "latent", "paged_gqa_q2", "paged_gqa_fp8", "paged_glm",
-                  "paged_glm_fp8", "latent_rope_apart", "glm_mqa", "paged_mha", "latent_fp8", "glm_mqa_fp8"]
+                  "paged_glm_fp8", "latent_rope_apart", "glm_mqa", "paged_mha", "latent_fp8", "glm_mqa_fp8",
+                  "latent_fp8_inline"]
 
 
 @pytest.mark.parametrize("name", FULL_WORKLOADS)

@@ -59,12 +59,12 @@ def _draw(rng):
                   v_is_k_prefix=True)
         if rng.random() < 0.5:
             kw.update(rope_apart=64)
-            kv_fp8 = rng.random() < 0.4
+        kv_fp8 = rng.random() < 0.4
     else:
         kw.update(num_kv_heads=1, num_q_heads=rng.choice([24, 64, 128]), qk_depth=256, ov_depth=256)
         if rng.random() < 0.6:
             kw.update(rope_apart=64)
-            kv_fp8 = rng.random() < 0.4
+        kv_fp8 = rng.random() < 0.4
     lens = [rng.choice([0, rng.randint(1, 64), rng.randint(1, 2500)]) for _ in range(kw["batch"])]
     kw.update(page_size=page, seq_lens=lens, q_len=q_len, kv_fp8=kv_fp8,
               num_splits=rng.choice([0, 0, 1, 2, 3, 5, 8, 13]))
