@@ -139,11 +139,10 @@ typedef struct da_problem {
  *    256/256 with V of its own when q_len x Hq > 16; the 64 rotary columns in the K rows
  *    or stored apart in bf16 (nope_depth 512 or 192). Both also over an fp8 cache with the
  *    rotary columns apart (a V that is the K prefix takes the K scales: v_scale NULL).
- * Page sizes (FA4Config, v_row_major: multi-page tiles of a block-indirected cache): any
- * page_size for bf16 caches whose K rows hold every q.K column; fp8 caches and rotary
- * columns stored apart need a contiguous cache or pages of 16 keys or of a power of two
- * >= 32 (with fp8 on the shared-kv-head kernel and pages of 16 keys, num_pages * 64 bytes
- * of scales must stay below 2 GiB). */
+ *  - any page_size >= 1 on every form (FA4Config, v_row_major: multi-page tiles of a
+ *    block-indirected cache); pages of 16 keys or of a power of two >= 32 load a tile as
+ *    runs of consecutive rows, other sizes key by key (with fp8 on the shared-kv-head
+ *    kernel and pages of 16 keys, num_pages * 64 bytes of scales must stay below 2 GiB). */
 int da_supported(const da_problem* p);
 
 /* Split selection (FA4Config, with_splitk: partitions of the K/V sequence).
@@ -222,8 +221,7 @@ int decode_attn_splitk_fused(const da_problem* p, const void* q, const void* k_c
 
 /* The whole decode step over an fp8 cache (FA4Config: an fp8 qkv_dtype with a per-token
  * scale_dtype for K). kv_dtype must be DA_FP8_E4M3, dtype DA_BF16 (q), a matrix-core depth
- * pair (see da_supported), and the cache contiguous or paged with page_size 16 or a power
- * of two >= 32.
+ * pair (see da_supported); the cache contiguous or paged (any page_size).
  * k_cache / v_cache hold E4M3 codes (one byte each, same layouts as above); key t of kv
  * head k reads k_scale * code (fp32 scale of that token and kv head) and V likewise with
  * v_scale (NULL = 1). Scale layout, tokens innermost: contiguous [B][Hkv][kv_capacity],

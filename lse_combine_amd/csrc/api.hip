@@ -32,11 +32,6 @@ int ok() {
 enum Variant { kVarFma = 0, kVarMfma = 1, kVarShared = 2 };
 
 constexpr int kTileKeys = 32;  // key tile of every partition kernel; chunks are multiples of it
-// Pages whose tiles load as runs of consecutive cache rows: a power of two >= 32 keys (a
-// 32-key tile is one page) or 16 keys (each half of a tile is one page).
-bool run_pages(int page_size) {
-  return page_size == kTileKeys / 2 || (page_size >= kTileKeys && !(page_size & (page_size - 1)));
-}
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -110,10 +105,6 @@ int check_problem(const da_problem* p, Variant* var) {
                   p->qk_depth, p->ov_depth, nope_apart, p->nope_depth);
     if (p->nope_depth > 0 && p->rope_dtype != DA_BF16)
       return fail(DA_EUNSUPPORTED, "rotary columns stored apart must be bf16 (rope_dtype %d)", p->rope_dtype);
-    if (p->kv_dtype == DA_FP8_E4M3 && p->page_size != 0 && !run_pages(p->page_size))
-      return fail(DA_EUNSUPPORTED,
-                  "fp8 on the shared-kv-head kernel: a contiguous cache or pages of 16 keys or a power of two "
-                  ">= 32 (got page_size %d)", p->page_size);
     // (pages of 16 keys: the per-token scales are addressed from the start of their tensor)
     if (p->kv_dtype == DA_FP8_E4M3 && p->page_size == kTileKeys / 2 && (int64_t)p->num_pages * 16 * 4 >= INT32_MAX)
       return fail(DA_EUNSUPPORTED, "fp8 on the shared-kv-head kernel with pages of 16 keys: at most %d pages (got %d)",
@@ -126,7 +117,6 @@ int check_problem(const da_problem* p, Variant* var) {
   const bool d128 = p->qk_depth == 128 && p->ov_depth == 128;
   const bool wide = (p->qk_depth == 192 && p->ov_depth == 128) || (p->qk_depth == 256 && p->ov_depth == 256);
   if (ql > 1 || p->kv_dtype == DA_FP8_E4M3 || wide || p->nope_depth > 0) {
-    const bool aligned_pages = p->page_size == 0 || run_pages(p->page_size);
     if (!d128 && !wide)
       return fail(DA_EUNSUPPORTED,
                   "several queries per sequence, fp8 caches and rotary columns stored apart are supported at "
@@ -140,10 +130,6 @@ int check_problem(const da_problem* p, Variant* var) {
       return fail(DA_EUNSUPPORTED,
                   "this problem needs the matrix-core kernel: bf16 q, separate K and V caches, q_len x group <= 16 "
                   "(q_len %d, group %d)", ql, g);
-    if (!aligned_pages && (p->kv_dtype != 0 || p->nope_depth > 0))
-      return fail(DA_EUNSUPPORTED,
-                  "fp8 caches and rotary columns stored apart need a contiguous cache or pages of 16 keys or a "
-                  "power of two >= 32 (page_size %d)", p->page_size);
     *var = kVarMfma;
     return DA_OK;
   }

@@ -70,7 +70,22 @@ __device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t voff, uint32_t ld
       : "memory");
 }
 
-// The same with 4 bytes per lane (the 64 lanes fill 256 bytes, lane l at 4 l).
+// The same from a per-lane 64-bit address (global_load_lds_dwordx4: lane l fills 16 bytes
+// at lds_base + 16 l), for rows found key by key.
+__device__ __forceinline__ void lds_dma16_ptr(const void* src, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds_base)
+      : "memory");
+}
+
+// The buffer form with 4 bytes per lane (the 64 lanes fill 256 bytes, lane l at 4 l).
 __device__ __forceinline__ void lds_dma4(u32x4 rsrc, uint32_t voff, uint32_t lds_base) {
   uint32_t saved;
   asm volatile(

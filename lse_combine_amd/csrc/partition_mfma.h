@@ -36,7 +36,7 @@
 // contiguous cache or pages of a power of two >= 32 keys a tile is 32 consecutive cache
 // rows, and with pages of 16 keys each 16-key half of it is: every load covers one half, its
 // base is a scalar and every lane adds a fixed 32-bit offset. Other page sizes take a
-// per-key page lookup (bf16 caches whose K rows hold every q.K column). The page
+// per-key page lookup: every lane finds its own row. The page
 // indices of the partition are staged in LDS once, so no dependent page-table load
 // sits between consecutive prefetches. Loads run one tile ahead: the next tile's K is
 // requested once the current tile's scores are done and its V once the current P.V is
@@ -398,11 +398,18 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
     if constexpr (PM == kPagedHalf) return h == 0 ? row0 : tile_row0(t0 + 16);
     else return row0 + 16 * h;
   };
-  auto general_row = [&](int t) -> int64_t {
+  // (general case: the page of key t and its slot in that page)
+  auto general_page = [&](int t, int& off) -> int {
+    t = max(t, 0);
     const int pi = t / a.page_size;
     const int slot = min(max(pi - first_page, 0), kMaxLdsPages - 1);
-    const int page = min(max(pages_s[slot], 0), a.num_pages - 1);
-    return (int64_t)page * a.page_size + (t - pi * a.page_size);
+    off = t - pi * a.page_size;
+    return min(max(pages_s[slot], 0), a.num_pages - 1);
+  };
+  auto general_row = [&](int t) -> int64_t {
+    int off;
+    const int page = general_page(t, off);
+    return (int64_t)page * a.page_size + off;
   };
 
   // Per-lane byte offsets inside a 16-row half tile: key n, 16-byte depth chunk qd
@@ -438,12 +445,19 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
         }
       }
     } else {
-      static_assert(!F8 && S::NR == 0, "per-key page lookup: bf16 caches with inline rows only");
+      // per-key page lookup: each lane reads its own key's row (keys past the end of a ragged
+      // tile repeat the last one; their scores are masked)
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
-        const char* kp = kc + general_row(t0 + min(n + 16 * blk, last)) * krow_bytes + kslice + 16 * qd;
+        const int64_t row = general_row(t0 + min(n + 16 * blk, last));
+        const char* kp = kc + row * krow_bytes + kslice + 16 * qd;
 #pragma unroll
         for (int l = 0; l < KT::NL; ++l) T.k[blk][l] = __builtin_nontemporal_load((const u32x4*)(kp + 64 * l));
+        if constexpr (S::NR > 0) {
+          const char* rp = kr + row * rrow_bytes + rslice + 16 * qd;
+#pragma unroll
+          for (int l = 0; l < S::NR; ++l) T.r[blk][l] = __builtin_nontemporal_load((const u32x4*)(rp + 64 * l));
+        }
       }
     }
   };
@@ -513,7 +527,8 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
 
   // per-token scales of the tile's keys that this lane holds (fp8 caches): keys
   // 4qd .. 4qd+3 and 16+4qd .. 16+4qd+3, 16 contiguous bytes each in the tokens-innermost
-  // scale layout; missing keys of a ragged tile read 0 (their scores are masked anyway)
+  // scale layout (key by key with the per-key page lookup); missing keys of a ragged tile
+  // read 0 (their scores are masked anyway)
   auto load_sc = [&](f32x4* ksc, f32x4* vsc, int t0, bool valid = true) {
     const int last = valid ? min(kTile - 1, end - 1 - t0) : -1;
     const int kv_safe = wave_active ? kvh : 0;
@@ -531,7 +546,19 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
     const float* vs = a.v_scale ? a.v_scale : a.k_scale;
     // (the V scales are loaded in every case, from the K scales when there are none, then
     // replaced by 1 where they are used: the same loads on every path)
-    if constexpr (PM == kPagedHalf) {
+    if constexpr (PM == kPagedGeneral) {
+      // per-key page lookup: one 4-byte load per key (keys past the end repeat the last one)
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          int off;
+          const int page = general_page(t0 + min(16 * blk + 4 * qd + i, max(last, 0)), off);
+          const int64_t idx = ((int64_t)page * a.Hkv + kv_safe) * a.page_size + off;
+          ksc[blk][i] = __builtin_nontemporal_load(a.k_scale + idx);
+          vsc[blk][i] = __builtin_nontemporal_load(vs + idx);
+        }
+    } else if constexpr (PM == kPagedHalf) {
       // each 16-key half of the tile is a page of its own
       const int64_t base0 = sc_base(t0), base1 = sc_base(t0 + 16);
       const int n0 = min(nk, 16), n1 = max(nk - 16, 0);
@@ -670,10 +697,22 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
   // (the same loads through lds_dma16, for loops whose waits are all explicit)
   auto load_v8_lds_asm = [&](char* stage, int t0, bool valid) {
     const int last = valid ? min(kTile - 1, end - 1 - t0) : -1;
-    const int64_t row0 = tile_row0(t0);
     // (no LDS wait is needed here: the staging tile's reads fed the widening arithmetic,
     // so they have completed before this point)
     const int rr = lane / kV8Chunks, cc = lane % kV8Chunks;
+    if constexpr (PM == kPagedGeneral) {
+      // per-key page lookup: each lane loads from its own row (rows past the end of a ragged
+      // tile repeat the last key, finite codes that meet p = 0; past the last tile the data
+      // lands in a staging tile that is never read)
+#pragma unroll
+      for (int i = 0; i < 2 * kV8PerHalf; ++i) {
+        const int r = kV8Rows * (i % kV8PerHalf) + 16 * (i / kV8PerHalf) + rr;
+        lds_dma16_ptr(vc + general_row(t0 + min(r, last)) * vrow_bytes + vslice + 16 * cc,
+                      __builtin_amdgcn_readfirstlane(lds_addr(stage + i * 1024)));
+      }
+      return;
+    }
+    const int64_t row0 = tile_row0(t0);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int rows = __builtin_amdgcn_readfirstlane(min(max(last + 1 - 16 * h, 0), 16));
@@ -688,8 +727,19 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
   };
   auto load_v8_lds = [&](char* stage, int t0, bool valid = true) {
     const int last = valid ? min(kTile - 1, end - 1 - t0) : -1;
-    const int64_t row0 = tile_row0(t0);
     const int rr = lane / kV8Chunks, cc = lane % kV8Chunks;
+    if constexpr (PM == kPagedGeneral) {
+      // per-key page lookup, as above
+#pragma unroll
+      for (int i = 0; i < 2 * kV8PerHalf; ++i) {
+        const int r = kV8Rows * (i % kV8PerHalf) + 16 * (i / kV8PerHalf) + rr;
+        __builtin_amdgcn_global_load_lds((const void*)(vc + general_row(t0 + min(r, last)) * vrow_bytes + vslice +
+                                                       16 * cc),
+                                         (DA_LDS void*)(stage + i * 1024), 16, 0, 0);
+      }
+      return;
+    }
+    const int64_t row0 = tile_row0(t0);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int rows = __builtin_amdgcn_readfirstlane(min(max(last + 1 - 16 * h, 0), 16));
@@ -749,7 +799,8 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
         // the scores of tile j - 2, the scales after its softmax, V after its staged codes
         // were consumed. At the wait for tile j's V, the loads issued after it are those of
         // tile j + 1 and the K and scales of tile j + 2.
-        constexpr int kK = 2 * (KT::NL + S::NR), kSc = 4, kV = 2 * kV8PerHalf;
+        // (scales: four 16-byte loads per tile, or 16 single ones with the per-key page lookup)
+        constexpr int kK = 2 * (KT::NL + S::NR), kSc = PM == kPagedGeneral ? 16 : 4, kV = 2 * kV8PerHalf;
         KT T1;
         f32x4 ksc0[2], vsc0[2], ksc1[2], vsc1[2];
         // the wave's region: the half-depth bf16 tile, then the two staging tiles (their
@@ -1143,7 +1194,7 @@ hipError_t launch_hl(const PartArgs& a, int pm, int HG, int KS, hipStream_t s) {
   const dim3 block(HG * KS * 64);
   const size_t lds = (size_t)HG * KS * S::kWaveBytes;
   if (a.kv_fp8) {
-    // fp8 caches: contiguous or pages of a power of two >= 16 keys
+    // fp8 caches
     switch (pm) {
       case kContiguous:
         hipLaunchKernelGGL((partition_gqa_kernel<HL, kContiguous, true, S>), grid, block, lds, s, a, HG, KS);
@@ -1155,7 +1206,8 @@ hipError_t launch_hl(const PartArgs& a, int pm, int HG, int KS, hipStream_t s) {
         hipLaunchKernelGGL((partition_gqa_kernel<HL, kPagedHalf, true, S>), grid, block, lds, s, a, HG, KS);
         break;
       default:
-        return hipErrorInvalidValue;
+        hipLaunchKernelGGL((partition_gqa_kernel<HL, kPagedGeneral, true, S>), grid, block, lds, s, a, HG, KS);
+        break;
     }
     return hipGetLastError();
   }
@@ -1170,13 +1222,9 @@ hipError_t launch_hl(const PartArgs& a, int pm, int HG, int KS, hipStream_t s) {
       hipLaunchKernelGGL((partition_gqa_kernel<HL, kPagedHalf, false, S>), grid, block, lds, s, a, HG, KS);
       break;
     default:
-      // per-key page lookup (any page size): K rows that hold every q.K column
-      if constexpr (S::DR == 0) {
-        hipLaunchKernelGGL((partition_gqa_kernel<HL, kPagedGeneral, false, S>), grid, block, lds, s, a, HG, KS);
-        break;
-      } else {
-        return hipErrorInvalidValue;
-      }
+      // per-key page lookup (any page size)
+      hipLaunchKernelGGL((partition_gqa_kernel<HL, kPagedGeneral, false, S>), grid, block, lds, s, a, HG, KS);
+      break;
   }
   return hipGetLastError();
 }

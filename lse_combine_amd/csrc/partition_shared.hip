@@ -364,12 +364,21 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
     } else {
       if (ti >= n_tiles) return;
       // any page size: every lane looks up its own row (rows past the end repeat the last
-      // key; their scores are masked)
+      // key; their scores are masked); the fp8 scales come one token per lane (4 bytes)
       const int last = min(kTile - 1, end - 1 - t0);
 #pragma unroll
       for (int i = 0; i < S::kPerWave; ++i) {
         if (!lvalid[i]) continue;
         const int j = dw + S::kDmaWaves * i;
+        if (S::F8 && lsc[i]) {
+          const int t = t0 + min(lane, last);
+          const int pi = t / a.page_size;
+          const int slot = min(max(pi - first_page, 0), kMaxLdsPages - 1);
+          const int page = min(max(sm.pages[slot], 0), a.num_pages - 1);
+          const int64_t row = (int64_t)page * a.page_size + (t - pi * a.page_size);
+          __builtin_amdgcn_global_load_lds((const void*)(lbase[i] + row * 4), (DA_LDS void*)(dst + j * 1024), 4, 0, 0);
+          continue;
+        }
         const int r = (int)(loff[i] / lstride[i]);
         const int t = t0 + min(r, last);
         const int pi = t / a.page_size;
@@ -851,10 +860,7 @@ hipError_t launch_shape(const PartArgs& a, int page_mode, hipStream_t s) {
       hipLaunchKernelGGL((partition_shared_kernel<S, kPagedHalf>), grid, block, 0, s, a, rope, rope_row);
       break;
     default:
-      // (fp8: not for the any-page-size form, which reads rows key by key while a tile's
-      // scales are loaded in runs of consecutive tokens)
-      if constexpr (S::F8) return hipErrorInvalidValue;
-      else hipLaunchKernelGGL((partition_shared_kernel<S, kPagedGeneral>), grid, block, 0, s, a, rope, rope_row);
+      hipLaunchKernelGGL((partition_shared_kernel<S, kPagedGeneral>), grid, block, 0, s, a, rope, rope_row);
       break;
   }
   return hipGetLastError();
@@ -869,7 +875,7 @@ hipError_t launch_partition_shared(const PartArgs& a, int page_mode, hipStream_t
   if (a.Hkv != 1) return hipErrorInvalidValue;
   const bool rope_apart = a.k_rope != nullptr;
   if (a.kv_fp8) {
-    if (page_mode == kPagedGeneral || !a.k_scale) return hipErrorInvalidValue;
+    if (!a.k_scale) return hipErrorInvalidValue;
     // latent over an fp8 cache: nope codes with per-token K scales, the rotary columns bf16
     // apart or codes in the K rows
     if (a.Dqk == 576 && a.Dv == 512 && a.v == a.k && !a.v_scale) {

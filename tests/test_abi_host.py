@@ -250,12 +250,11 @@ def test_probe_argument_checks():
     (dict(kv_dtype=2), DA_OK),                                   # paged 64, bf16 q
     (dict(kv_dtype=2, page_size=0, kv_capacity=4096), DA_OK),    # contiguous
     (dict(kv_dtype=2, page_size=16, max_pages_per_seq=256), DA_OK),             # a page per half tile
-    (dict(kv_dtype=2, page_size=8, max_pages_per_seq=512), DA_EUNSUPPORTED),    # below the half tile
-    (dict(kv_dtype=2, page_size=48, max_pages_per_seq=100), DA_EUNSUPPORTED),   # not a power of two
+    (dict(kv_dtype=2, page_size=8, max_pages_per_seq=512), DA_OK),              # per-key page lookup
+    (dict(kv_dtype=2, page_size=48, max_pages_per_seq=100), DA_OK),             # not a power of two
     (dict(kv_dtype=2, dtype=0), DA_EUNSUPPORTED),                # fp32 q
     (dict(kv_dtype=2, kernel=1), DA_EUNSUPPORTED),               # vector-ALU kernel
-    # latent over fp8: the rotary columns apart in bf16 or as codes in the K rows, pages of 16
-    # keys or a power of two >= 32
+    # latent over fp8: the rotary columns apart in bf16 or as codes in the K rows, any page size
     (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1),
      DA_OK),                                                                 # rotary codes in the K rows
     (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1,
@@ -263,7 +262,7 @@ def test_probe_argument_checks():
     (dict(kv_dtype=2, num_q_heads=16, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1,
           nope_depth=512, rope_dtype=1, q_len=3, page_size=0, kv_capacity=4096), DA_OK),
     (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1,
-          nope_depth=512, rope_dtype=1, page_size=48, max_pages_per_seq=100), DA_EUNSUPPORTED),
+          nope_depth=512, rope_dtype=1, page_size=48, max_pages_per_seq=100), DA_OK),
     (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1,
           nope_depth=512, rope_dtype=1, page_size=16, max_pages_per_seq=256), DA_OK),
     (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1,
@@ -273,9 +272,9 @@ def test_probe_argument_checks():
           rope_dtype=1), DA_OK),                                             # one-kv-head GLM widths
     (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=256, ov_depth=256), DA_OK),   # rotary inline
     (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=256, ov_depth=256, page_size=48,
-          max_pages_per_seq=100), DA_EUNSUPPORTED),
+          max_pages_per_seq=100), DA_OK),
     (dict(kv_dtype=2, num_q_heads=128, num_kv_heads=1, qk_depth=256, ov_depth=256, nope_depth=192,
-          rope_dtype=1, page_size=48, max_pages_per_seq=100), DA_EUNSUPPORTED),
+          rope_dtype=1, page_size=48, max_pages_per_seq=100), DA_OK),
     (dict(kv_dtype=7), DA_EINVAL),
 ])
 def test_fp8_cache_support(lib, kw, code):
@@ -303,7 +302,7 @@ def test_fp8_entry_points_need_their_scales(lib):
     (dict(q_len=2, dtype=0), DA_EUNSUPPORTED),                     # vector-ALU kernel
     (dict(q_len=2, page_size=16, max_pages_per_seq=256), DA_OK),
     (dict(q_len=2, page_size=48, max_pages_per_seq=100), DA_OK),   # per-key page lookup
-    (dict(q_len=2, page_size=48, max_pages_per_seq=100, kv_dtype=2), DA_EUNSUPPORTED),
+    (dict(q_len=2, page_size=48, max_pages_per_seq=100, kv_dtype=2), DA_OK),
     (dict(q_len=2, kv_dtype=2), DA_OK),
     (dict(q_len=17), DA_EINVAL),
     (dict(q_len=2, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1), DA_OK),
@@ -364,7 +363,7 @@ def test_binding_refuses_output_buffers_without_every_row():
     (dict(qk_depth=256, ov_depth=256, page_size=16, max_pages_per_seq=256), DA_OK),
     (dict(qk_depth=256, ov_depth=256, page_size=24, max_pages_per_seq=200), DA_OK),   # per-key page lookup
     (dict(qk_depth=256, ov_depth=256, nope_depth=192, rope_dtype=1, page_size=24, max_pages_per_seq=200),
-     DA_EUNSUPPORTED),                                             # rotary apart: no per-key lookup
+     DA_OK),
     (dict(qk_depth=192, ov_depth=128, kv_dtype=2, page_size=16, max_pages_per_seq=256), DA_OK),
     (dict(qk_depth=256, ov_depth=256, kernel=1), DA_EUNSUPPORTED),
     (dict(qk_depth=256, ov_depth=256, num_q_heads=34, num_kv_heads=2), DA_EUNSUPPORTED),   # group 17

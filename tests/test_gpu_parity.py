@@ -759,10 +759,10 @@ def test_multiquery_fused_combine():
 
 
 # ---------------------------------------------------------------------------
-# page sizes: pages of 16 keys (each half of a 32-key tile is a page) on every form, and
-# the per-key page lookup (any page size) on bf16 caches whose K rows hold every q.K
-# column; ragged last tiles end in either half, poisoned cases fill every slot no
-# sequence attends (codes, rotary columns and fp8 scales) with NaN
+# page sizes: pages of 16 keys (each half of a 32-key tile is a page) and the per-key page
+# lookup (any other page size, down to one key per page) on every form; ragged last tiles
+# end in either half, poisoned cases fill every slot no sequence attends (codes, rotary
+# columns and fp8 scales) with NaN
 # ---------------------------------------------------------------------------
 PAGE_FORMS = [
     ("fp8_g8_paged16_auto", dict(batch=4, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=16,
@@ -824,6 +824,36 @@ PAGE_FORMS = [
                                               num_splits=0, seed=151, rope_apart=64, **LATENT)),
     ("latent_g24_paged8_general", dict(batch=2, num_q_heads=24, page_size=8, seq_lens=[300, 45], num_splits=2,
                                        seed=152, **LATENT)),
+    # per-key page lookup with fp8 caches (scales key by key) and rotary columns stored apart
+    ("fp8_g8_paged48_general_auto", dict(batch=4, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=48,
+                                         seq_lens=[1201, 17, 0, 2500], num_splits=0, seed=153, kv_fp8=True)),
+    ("fp8_g4_paged8_general_splits3_poisoned", dict(batch=3, num_q_heads=8, num_kv_heads=2, qk_depth=128,
+                                                    page_size=8, seq_lens=[100, 1, 1025], num_splits=3,
+                                                    seed=154, kv_fp8=True, poison=True, spare_pages=3)),
+    ("fp8_q2_g8_paged24_general_no_v_scale", dict(batch=3, num_q_heads=16, num_kv_heads=2, qk_depth=128,
+                                                  page_size=24, seq_lens=[2, 700, 1500], num_splits=0, seed=155,
+                                                  q_len=2, kv_fp8=True, v_scaled=False)),
+    ("d192_apart_fp8_g4_paged8_general", dict(batch=3, num_q_heads=8, num_kv_heads=2, qk_depth=192, ov_depth=128,
+                                              page_size=8, seq_lens=[1000, 33, 2100], num_splits=0, seed=156,
+                                              rope_apart=64, kv_fp8=True)),
+    ("d256_apart_g8_paged40_general_poisoned", dict(batch=3, num_q_heads=16, num_kv_heads=2, qk_depth=256,
+                                                    ov_depth=256, page_size=40, seq_lens=[100, 1, 1025],
+                                                    num_splits=0, seed=157, rope_apart=64, poison=True,
+                                                    spare_pages=3)),
+    ("d256_inline_fp8_g4_paged1_general", dict(batch=3, num_q_heads=8, num_kv_heads=2, qk_depth=256, ov_depth=256,
+                                               page_size=1, seq_lens=[300, 45, 2], num_splits=0, seed=158,
+                                               kv_fp8=True)),
+    ("latent_fp8_g64_paged48_general", dict(batch=2, num_q_heads=64, page_size=48, seq_lens=[700, 1313],
+                                            num_splits=3, seed=159, rope_apart=64, kv_fp8=True, **LATENT)),
+    ("latent_fp8_inline_q2_g40_paged8_general_poisoned", dict(batch=3, num_q_heads=40, page_size=8,
+                                                              seq_lens=[100, 1, 1025], num_splits=2, seed=195,
+                                                              q_len=2, kv_fp8=True, poison=True, spare_pages=3,
+                                                              **LATENT)),
+    ("glm_mqa_fp8_g64_paged24_general", dict(batch=2, num_q_heads=64, page_size=24, seq_lens=[1500, 333],
+                                             num_splits=3, seed=196, rope_apart=64, kv_fp8=True, **GLM_MQA)),
+    ("glm_mqa_fp8_inline_no_v_scale_paged1_general", dict(batch=3, num_q_heads=32, page_size=1,
+                                                          seq_lens=[300, 45, 2], num_splits=2, seed=197,
+                                                          kv_fp8=True, v_scaled=False, **GLM_MQA)),
 ]
 
 
