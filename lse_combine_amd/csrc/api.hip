@@ -126,10 +126,9 @@ int check_problem(const da_problem* p, Variant* var) {
                                    "(nope_depth 128 or 192; got %d of %d)", p->nope_depth, p->qk_depth);
     if (p->nope_depth > 0 && p->rope_dtype != DA_BF16)
       return fail(DA_EUNSUPPORTED, "rotary columns stored apart must be bf16 (rope_dtype %d)", p->rope_dtype);
-    if (p->dtype != DA_BF16 || p->v_is_k_prefix || ql * g > 16 || p->kernel == DA_KERNEL_FMA)
+    if (p->dtype != DA_BF16 || p->v_is_k_prefix || p->kernel == DA_KERNEL_FMA)
       return fail(DA_EUNSUPPORTED,
-                  "this problem needs the matrix-core kernel: bf16 q, separate K and V caches, q_len x group <= 16 "
-                  "(q_len %d, group %d)", ql, g);
+                  "this problem needs the matrix-core kernel: bf16 q and separate K and V caches");
     *var = kVarMfma;
     return DA_OK;
   }
@@ -138,7 +137,6 @@ int check_problem(const da_problem* p, Variant* var) {
     return fail(DA_EUNSUPPORTED,
                 "supported depths (q.K / V): 128/128; 192/128 and 256/256 with bf16 q on the matrix-core kernel; "
                 "576/512 latent-shared (got %d/%d)", p->qk_depth, p->ov_depth);
-  if (g > 16) return fail(DA_EUNSUPPORTED, "depth-128 kernels fuse at most 16 q heads per kv head (group %d)", g);
   if (p->dtype == DA_F32) {
     if (p->kernel == DA_KERNEL_MFMA) return fail(DA_EUNSUPPORTED, "the matrix-core kernel needs bf16 inputs");
     *var = kVarFma;
@@ -150,6 +148,8 @@ int check_problem(const da_problem* p, Variant* var) {
   } else {
     *var = kVarMfma;
   }
+  if (*var == kVarFma && g > 16)
+    return fail(DA_EUNSUPPORTED, "the vector-ALU kernel fuses at most 16 q heads per kv head (group %d)", g);
   return DA_OK;
 }
 
@@ -172,13 +172,28 @@ int page_mode(const da_problem* p) {
 }
 
 
+// Matrix-core GQA kernel: a wave serves at most 16 (query, head) MFMA columns. A larger
+// group is split into kv_div groups of g / kv_div heads (the largest divisor of g with
+// q_len x g / kv_div <= 16), each served as a kv head of its own: a virtual kv head, whose
+// waves read the rows of their cached kv head (a second read of the same rows, mostly from
+// L2). Shapes, schedules, counters and partial rows count virtual kv heads.
+int mfma_kv_div(const da_problem* p) {
+  const int ql = q_len_of(p), g = p->num_q_heads / p->num_kv_heads;
+  if (ql * g <= 16) return 1;
+  int d = 16 / ql;
+  while (d > 1 && g % d) --d;
+  return g / d;
+}
+int mfma_kv_heads(const da_problem* p) { return p->num_kv_heads * mfma_kv_div(p); }
+
 // Matrix-core kernel shape: HG kv heads per workgroup (their waves read whole token
 // rows of the cache together) times KS key splits per kv head, HG * KS = 8 waves.
 // HG is as large as possible while the grid still offers a workgroup per CU (one
 // 8-wave workgroup per CU fits at three waves per SIMD).
 void mfma_shape(const da_problem* p, int32_t max_splits, int cus, int* HG, int* KS) {
-  int hg = p->num_kv_heads < 8 ? p->num_kv_heads : 8;
-  auto wgs = [&](int h) { return (int64_t)max_splits * ((p->num_kv_heads + h - 1) / h) * p->batch; };
+  const int hkv = mfma_kv_heads(p);
+  int hg = hkv < 8 ? hkv : 8;
+  auto wgs = [&](int h) { return (int64_t)max_splits * ((hkv + h - 1) / h) * p->batch; };
   while (hg > 1 && wgs(hg) < (int64_t)cus) hg = (hg + 1) / 2;
   *HG = hg;
   *KS = 8 / hg > 0 ? 8 / hg : 1;
@@ -190,8 +205,9 @@ void mfma_shape(const da_problem* p, int32_t max_splits, int cus, int* HG, int* 
 // of kMinShareTiles tiles; W workers per head group so that W x groups ~ CUs.
 void share_shape(const da_problem* p, int cus, int* HG, int* KS, int* W) {
   const int64_t tiles_max = (int64_t)p->batch * ceil_div(p->max_seq_len > 0 ? p->max_seq_len : 1, kTileKeys);
-  int hg = p->num_kv_heads < 8 ? p->num_kv_heads : 8;
-  auto groups = [&](int h) { return (int64_t)((p->num_kv_heads + h - 1) / h); };
+  const int hkv = mfma_kv_heads(p);
+  int hg = hkv < 8 ? hkv : 8;
+  auto groups = [&](int h) { return (int64_t)((hkv + h - 1) / h); };
   while (hg > 1 && (tiles_max / da::kMinShareTiles) * groups(hg) < (int64_t)cus) hg = (hg + 1) / 2;
   *HG = hg;
   *KS = 8 / hg > 0 ? 8 / hg : 1;
@@ -263,9 +279,9 @@ void ws_layout(const da_problem* p, int32_t chunk, int32_t max_splits, size_t* m
   const size_t meta = chunk == 0 ? (size_t)p->batch * 2 * sizeof(int32_t) : 0;
   const size_t ml = (rows * 2 * sizeof(float) + meta + 255) & ~(size_t)255;
   const size_t o = (rows * (size_t)p->ov_depth * sizeof(float) + 255) & ~(size_t)255;
-  // arrival counters of the fused combine: one per (sequence, kv head), or per (sequence,
-  // block of 64 columns) on the shared-kv-head kernel
-  const size_t per_seq = std::max<size_t>((size_t)p->num_kv_heads, (size_t)ceil_div(rows_per_seq(p), 64));
+  // arrival counters of the fused combine: one per (sequence, kv head; virtual ones on the
+  // matrix-core GQA kernel), or per (sequence, block of 64 columns) on the shared-kv-head kernel
+  const size_t per_seq = std::max<size_t>((size_t)mfma_kv_heads(p), (size_t)ceil_div(rows_per_seq(p), 64));
   const size_t cnt = ((size_t)p->batch * per_seq * sizeof(int32_t) + 255) & ~(size_t)255;
   *ml_off = 0;
   *o_off = ml;
@@ -422,7 +438,7 @@ int64_t fused_fold_bytes(const da_problem* p, Variant var, int32_t C, int32_t P,
     int HG, KS, W;
     if (C == 0) share_shape(p, cus, &HG, &KS, &W);
     else mfma_shape(p, P, cus, &HG, &KS);
-    rows = ql * g * HG;   // (sequence, head group)
+    rows = ql * (g / mfma_kv_div(p)) * HG;   // (sequence, group of virtual kv heads)
   } else {
     rows = std::min<int64_t>(64, rows_per_seq(p));   // (sequence, block of 64 columns)
   }
@@ -470,7 +486,8 @@ int run_splitk(const da_problem* p, const void* q, const da_kv& kv, const int32_
   float* pml = (float*)((char*)workspace + ml_off);
   float* po = (float*)((char*)workspace + o_off);
   hipStream_t s = (hipStream_t)stream;
-  da::PartArgs a = da::build_part_args(p, q, kv.k_cache, kv.v_cache, page_table, seq_lens, scale, C, P);
+  da::PartArgs a = da::build_part_args(p, q, kv.k_cache, kv.v_cache, page_table, seq_lens, scale, C, P,
+                                       var == kVarMfma ? mfma_kv_div(p) : 1);
   a.part_o = po;
   a.part_ml = pml;
   if (C == 0) a.meta = meta_of(p, P, pml);
@@ -496,7 +513,7 @@ int page_shift_of(int page_size) { return log2_exact(page_size); }
 
 // Kernel arguments of a partition launch (shared with the tools that time kernels directly).
 PartArgs build_part_args(const da_problem* p, const void* q, const void* k, const void* v, const int32_t* pt,
-                       const int32_t* lens, float scale, int32_t chunk, int32_t max_splits) {
+                       const int32_t* lens, float scale, int32_t chunk, int32_t max_splits, int32_t kv_div) {
   PartArgs a;
   memset(&a, 0, sizeof(a));
   a.q = q;
@@ -508,8 +525,9 @@ PartArgs build_part_args(const da_problem* p, const void* q, const void* k, cons
   a.Hq = (int32_t)rows_per_seq(p);
   a.Hq1 = p->num_q_heads;
   a.q_len = q_len_of(p);
-  a.Hkv = p->num_kv_heads;
-  a.g = p->num_q_heads / p->num_kv_heads;
+  a.kv_div = kv_div < 1 ? 1 : kv_div;
+  a.Hkv = p->num_kv_heads * a.kv_div;
+  a.g = p->num_q_heads / a.Hkv;
   a.Dqk = p->qk_depth;
   a.Dk = p->nope_depth > 0 ? p->nope_depth : p->qk_depth;
   a.Dv = p->ov_depth;
@@ -690,8 +708,8 @@ static int partition_impl(const da_problem* p, const void* q, const da_kv& kv, c
   if ((r = check_scale(scale))) return r;
   if ((r = check_split_args(p, var, chunk_tokens, max_splits))) return r;
   if (!part_o || !part_ml) return fail(DA_EINVAL, "part_o and part_ml must be non-NULL");
-  da::PartArgs a =
-      da::build_part_args(p, q, kv.k_cache, kv.v_cache, page_table, seq_lens, scale, chunk_tokens, max_splits);
+  da::PartArgs a = da::build_part_args(p, q, kv.k_cache, kv.v_cache, page_table, seq_lens, scale, chunk_tokens,
+                                       max_splits, var == kVarMfma ? mfma_kv_div(p) : 1);
   a.part_o = part_o;
   a.part_ml = part_ml;
   if (chunk_tokens == 0) a.meta = meta_of(p, max_splits, part_ml);

@@ -35,6 +35,8 @@ struct PartArgs {
   float* lse;               // optional
   float* o32;               // optional
   int32_t B, Hq, Hkv, g, Dqk, Dv;   // Hq: rows per sequence (q_len x heads)
+  int32_t kv_div;                   // matrix-core GQA kernel: Hkv and g count virtual kv heads,
+                                    // kv_div per cached kv head (1: none); other kernels: 1
   int32_t Dk;                       // K cache columns (Dqk, or the nope part when k_rope)
   int32_t Hq1, q_len;               // heads; queries per sequence (>= 1)
   int32_t v_row_len;        // elements between consecutive (row, kv-head) V vectors / Hkv
@@ -70,7 +72,7 @@ constexpr int kMinShareTiles = 8;
 // Kernel arguments of a partition launch for a validated problem (api.hip).
 PartArgs build_part_args(const ::da_problem* p, const void* q, const void* k, const void* v,
                          const int32_t* page_table, const int32_t* seq_lens, float scale, int32_t chunk,
-                         int32_t max_splits);
+                         int32_t max_splits, int32_t kv_div = 1);
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_partition_fma(const PartArgs& a, int dtype, int page_mode, hipStream_t s);

@@ -362,12 +362,15 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
   const char* kr = (const char*)a.k_rope;
   const char* vc = (const char*)a.v;
   constexpr uint32_t es = F8 ? 1 : 2;                              // bytes per cache element
-  const uint32_t krow_bytes = (uint32_t)a.Hkv * DK * es;          // bytes between tokens (K)
-  const uint32_t rrow_bytes = (uint32_t)a.Hkv * DR * 2;           // ... (rotary columns, bf16)
-  const uint32_t vrow_bytes = (uint32_t)a.Hkv * a.v_row_len * es; // ... (V)
-  const uint32_t kslice = (uint32_t)(wave_active ? kvh : 0) * DK * es;
-  const uint32_t rslice = (uint32_t)(wave_active ? kvh : 0) * DR * 2;
-  const uint32_t vslice = (uint32_t)(wave_active ? kvh : 0) * a.v_row_len * es;
+  // (a.Hkv counts virtual kv heads, a.kv_div of them per cached kv head)
+  const int kv_heads = a.Hkv / a.kv_div;                          // kv heads in the cache rows
+  const int kvc = (wave_active ? kvh : 0) / a.kv_div;             // this wave's cached kv head
+  const uint32_t krow_bytes = (uint32_t)kv_heads * DK * es;       // bytes between tokens (K)
+  const uint32_t rrow_bytes = (uint32_t)kv_heads * DR * 2;        // ... (rotary columns, bf16)
+  const uint32_t vrow_bytes = (uint32_t)kv_heads * a.v_row_len * es; // ... (V)
+  const uint32_t kslice = (uint32_t)kvc * DK * es;
+  const uint32_t rslice = (uint32_t)kvc * DR * 2;
+  const uint32_t vslice = (uint32_t)kvc * a.v_row_len * es;
   const float c = a.c;
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -531,15 +534,14 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
   // read 0 (their scores are masked anyway)
   auto load_sc = [&](f32x4* ksc, f32x4* vsc, int t0, bool valid = true) {
     const int last = valid ? min(kTile - 1, end - 1 - t0) : -1;
-    const int kv_safe = wave_active ? kvh : 0;
     // scale index of the first key of the run of consecutive keys starting at t
     auto sc_base = [&](int t) -> int64_t {
       if constexpr (PM == kContiguous) {
-        return ((int64_t)b * a.Hkv + kv_safe) * a.kv_capacity + t;
+        return ((int64_t)b * kv_heads + kvc) * a.kv_capacity + t;
       } else {
         const int slot = min(max((t >> a.page_shift) - first_page, 0), kMaxLdsPages - 1);
         const int page = __builtin_amdgcn_readfirstlane(min(max(pages_s[slot], 0), a.num_pages - 1));
-        return ((int64_t)page * a.Hkv + kv_safe) * a.page_size + (t & (a.page_size - 1));
+        return ((int64_t)page * kv_heads + kvc) * a.page_size + (t & (a.page_size - 1));
       }
     };
     const int nk = __builtin_amdgcn_readfirstlane(max(last + 1, 0));
@@ -554,7 +556,7 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
         for (int i = 0; i < 4; ++i) {
           int off;
           const int page = general_page(t0 + min(16 * blk + 4 * qd + i, max(last, 0)), off);
-          const int64_t idx = ((int64_t)page * a.Hkv + kv_safe) * a.page_size + off;
+          const int64_t idx = ((int64_t)page * kv_heads + kvc) * a.page_size + off;
           ksc[blk][i] = __builtin_nontemporal_load(a.k_scale + idx);
           vsc[blk][i] = __builtin_nontemporal_load(vs + idx);
         }

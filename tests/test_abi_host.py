@@ -56,7 +56,8 @@ def test_probe_library_is_apart_from_the_product():
     (dict(dtype=0), DA_OK),
     (dict(num_q_heads=2, num_kv_heads=2), DA_OK),
     (dict(num_q_heads=32, num_kv_heads=2), DA_OK),             # group 16
-    (dict(num_q_heads=34, num_kv_heads=2), DA_EUNSUPPORTED),   # group 17
+    (dict(num_q_heads=34, num_kv_heads=2), DA_OK),             # group 17: 17 virtual kv heads of one
+    (dict(num_q_heads=34, num_kv_heads=2, dtype=0), DA_EUNSUPPORTED),   # ... not on the vector ALU
     (dict(num_q_heads=15, num_kv_heads=2), DA_EINVAL),         # not a multiple
     (dict(qk_depth=64, ov_depth=64), DA_EUNSUPPORTED),
     (dict(dtype=7), DA_EINVAL),
@@ -79,7 +80,7 @@ def test_probe_library_is_apart_from_the_product():
     (dict(num_q_heads=128, num_kv_heads=1, qk_depth=256, ov_depth=256, nope_depth=192, rope_dtype=1), DA_OK),
     (dict(num_q_heads=128, num_kv_heads=1, qk_depth=256, ov_depth=256, nope_depth=192, rope_dtype=0),
      DA_EUNSUPPORTED),
-    (dict(num_q_heads=128, num_kv_heads=2, qk_depth=256, ov_depth=256), DA_EUNSUPPORTED),   # group 64 > 16
+    (dict(num_q_heads=128, num_kv_heads=2, qk_depth=256, ov_depth=256), DA_OK),   # group 64: 4 virtual x 16
     (dict(num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=0), DA_EUNSUPPORTED),
     (dict(num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512, v_is_k_prefix=1, dtype=0), DA_EUNSUPPORTED),
 ])
@@ -298,7 +299,7 @@ def test_fp8_entry_points_need_their_scales(lib):
 @pytest.mark.parametrize("kw,code", [
     (dict(q_len=2), DA_OK),                                        # 2 x 8 columns
     (dict(q_len=2, page_size=0, kv_capacity=4096), DA_OK),
-    (dict(q_len=3, num_q_heads=16, num_kv_heads=2), DA_EUNSUPPORTED),   # 24 columns
+    (dict(q_len=3, num_q_heads=16, num_kv_heads=2), DA_OK),        # 24 columns: 2 virtual kv heads of 4
     (dict(q_len=2, dtype=0), DA_EUNSUPPORTED),                     # vector-ALU kernel
     (dict(q_len=2, page_size=16, max_pages_per_seq=256), DA_OK),
     (dict(q_len=2, page_size=48, max_pages_per_seq=100), DA_OK),   # per-key page lookup
@@ -366,7 +367,7 @@ def test_binding_refuses_output_buffers_without_every_row():
      DA_OK),
     (dict(qk_depth=192, ov_depth=128, kv_dtype=2, page_size=16, max_pages_per_seq=256), DA_OK),
     (dict(qk_depth=256, ov_depth=256, kernel=1), DA_EUNSUPPORTED),
-    (dict(qk_depth=256, ov_depth=256, num_q_heads=34, num_kv_heads=2), DA_EUNSUPPORTED),   # group 17
+    (dict(qk_depth=256, ov_depth=256, num_q_heads=34, num_kv_heads=2), DA_OK),   # group 17
 ])
 def test_wide_depth_support(lib, kw, code):
     assert lib.da_supported(ctypes.byref(prob(**kw))) == code, lib.da_last_error()

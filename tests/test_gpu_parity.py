@@ -872,6 +872,46 @@ def test_page_size_forms(name, kw):
 
 
 # ---------------------------------------------------------------------------
+# more than 16 (query, head) columns per kv head on the matrix-core GQA kernel: the group
+# is split into virtual kv heads of at most 16 columns that read the same cached kv head
+# ---------------------------------------------------------------------------
+LARGE_GROUPS = [
+    ("mqa_g32_paged64_auto", dict(batch=3, num_q_heads=32, num_kv_heads=1, qk_depth=128, page_size=64,
+                                  seq_lens=[1500, 33, 2600], num_splits=0, seed=200)),
+    ("g24_hkv2_contig_splits5", dict(batch=2, num_q_heads=48, num_kv_heads=2, qk_depth=128, seq_lens=[2000, 77],
+                                     num_splits=5, seed=201)),
+    ("g17_prime_paged16", dict(batch=2, num_q_heads=34, num_kv_heads=2, qk_depth=128, page_size=16,
+                               seq_lens=[700, 1313], num_splits=0, seed=202)),
+    ("q3_g8_paged32", dict(batch=3, num_q_heads=16, num_kv_heads=2, qk_depth=128, page_size=32,
+                           seq_lens=[2, 700, 1500], num_splits=0, seed=203, q_len=3)),
+    ("q2_g16_fp8_paged64", dict(batch=3, num_q_heads=32, num_kv_heads=2, qk_depth=128, page_size=64,
+                                seq_lens=[33, 1000, 2500], num_splits=0, seed=204, q_len=2, kv_fp8=True)),
+    ("d256_apart_g32_hkv2_paged48_general", dict(batch=2, num_q_heads=64, num_kv_heads=2, qk_depth=256,
+                                                 ov_depth=256, page_size=48, seq_lens=[1000, 97], num_splits=0,
+                                                 seed=205, rope_apart=64)),
+    ("d192_fp8_q4_g8_contig_splits3", dict(batch=2, num_q_heads=16, num_kv_heads=2, qk_depth=192, ov_depth=128,
+                                           seq_lens=[900, 3], num_splits=3, seed=206, q_len=4, kv_fp8=True)),
+    ("mqa_g48_fp8_paged16_poisoned", dict(batch=3, num_q_heads=48, num_kv_heads=1, qk_depth=128, page_size=16,
+                                          seq_lens=[100, 1, 1025], num_splits=0, seed=207, kv_fp8=True, poison=True,
+                                          spare_pages=3)),
+]
+
+
+@pytest.mark.parametrize("name,kw", LARGE_GROUPS, ids=[c[0] for c in LARGE_GROUPS])
+def test_large_group_virtual_kv_heads(name, kw):
+    # the combine launch, then the fold in pass 1 on the same inputs
+    case = make_case(name, **kw)
+    print(f"[parity] large group {name}", flush=True)
+    dc = to_device(case)
+    O, LSE = oracle_for(case)
+    for fused in (False, "force"):
+        out, lse, o32 = api.case_call(dc, return_lse=True, return_o32=True, fused=fused)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o32).all()
+        assert_parity(out, lse, o32, O, LSE, what=f"large group {name} fused={fused}")
+
+
+# ---------------------------------------------------------------------------
 # wider depth pairs: q.K 192 / V 128 and q.K 256 / V 256 (nope 192 != V 256), with the
 # 64 rotary columns in the K rows or stored apart in bf16, bf16 or fp8 caches
 # ---------------------------------------------------------------------------
