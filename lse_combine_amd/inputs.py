@@ -279,6 +279,12 @@ WORKLOADS = {
     "latent_fp8_inline": dict(seed=5, batch=16, num_q_heads=128, num_kv_heads=1, qk_depth=576, ov_depth=512,
                               dtype=torch.bfloat16, page_size=64, seq_lens=[8192] * 16, num_splits=8,
                               v_is_k_prefix=True, kv_fp8=True),
+    # one kv head for 48 q heads at head dim 128 (multi-query attention): the group runs as
+    # three virtual kv heads of 16 columns on the matrix-core kernel; batch 32, bf16, page 64,
+    # L_b ~ U[512, 8192], automatic splits
+    "paged_mqa": dict(seed=9, batch=32, num_q_heads=48, num_kv_heads=1, qk_depth=128,
+                      dtype=torch.bfloat16, page_size=64, len_range=(512, 8192), num_splits=0,
+                      page_table_width=128),
     # one q head per kv head (multi-head attention, group 1): batch 32, 32 heads, head dim
     # 128, bf16, page 64, L_b ~ U[512, 8192], automatic splits
     "paged_mha": dict(seed=8, batch=32, num_q_heads=32, num_kv_heads=32, qk_depth=128,
