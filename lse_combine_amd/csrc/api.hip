@@ -94,6 +94,16 @@ int check_problem(const da_problem* p, Variant* var) {
   const bool latent = p->qk_depth == 576 && p->ov_depth == 512;
   const bool glm_mqa = p->qk_depth == 256 && p->ov_depth == 256 && !p->v_is_k_prefix && p->num_kv_heads == 1 &&
                        ql * g > 16;
+  // multi-query attention at depth 128 with more than 16 columns: bf16 caches on the
+  // shared-kv-head kernel (K read once per 64 columns); fp8 ones run as virtual kv heads on
+  // the GQA kernel
+  const bool mqa128 = p->qk_depth == 128 && p->ov_depth == 128 && !p->v_is_k_prefix && p->num_kv_heads == 1 &&
+                      ql * g > 16 && p->dtype == DA_BF16 && p->kv_dtype == 0 && p->nope_depth == 0 &&
+                      p->kernel != DA_KERNEL_FMA;
+  if (mqa128) {
+    *var = kVarShared;
+    return DA_OK;
+  }
   if (latent || glm_mqa) {
     const int nope_apart = latent ? 512 : 192;
     if (p->dtype != DA_BF16 || p->num_kv_heads != 1 || (latent && !p->v_is_k_prefix) || p->kernel == DA_KERNEL_FMA)
@@ -245,7 +255,11 @@ int choose(const da_problem* p, Variant var, int32_t num_splits, int cus, int32_
     const int64_t per_part = var == kVarShared ? ceil_div(rows_per_seq(p), 64) : p->num_kv_heads;
     const int64_t est_units = (int64_t)p->batch * per_part * ((maxlen + 1) / 2);
     C = ceil_div(est_units, 4LL * slots);
-    if (C < 256) C = 256;
+    // (multi-query attention at depth 128 on the shared-kv-head kernel: partitions of 256 keys
+    // are dominated by each workgroup's first tiles; measured on the paged MQA workload,
+    // 512-key chunks 33.0 us, 256: 40.7, 704: 37.0, 1024: 36.6)
+    const int64_t min_chunk = var == kVarShared && p->qk_depth == 128 ? 512 : 256;
+    if (C < min_chunk) C = min_chunk;
     if (C > 8192) C = 8192;
   }
   C = ceil_div(C, unit) * unit;

@@ -288,8 +288,9 @@ void partition_shared_kernel(PartArgs a, const char* rope_base, uint32_t rope_ro
       q2 = jb + lane * 16, lbase[i] = kc, lstride[i] = krow;
       r = q2 / S::kNRow, cs = (q2 - r * S::kNRow) >> 4, gc = cs ^ swz<S::kNRow>(r);
     } else if (jb < S::kNBytes + S::kRBytes) {
+      constexpr int kRR = S::kRRow > 0 ? S::kRRow : 1;   // (no rotary region without rotary columns)
       q2 = jb - S::kNBytes + lane * 16, lbase[i] = rope_base, lstride[i] = rope_row_bytes;
-      r = q2 / S::kRRow, cs = (q2 - r * S::kRRow) >> 4, gc = cs ^ swz<S::kRRow>(r);
+      r = q2 / kRR, cs = (q2 - r * kRR) >> 4, gc = cs ^ swz<S::kRRow>(r);
     } else if (S::F8 && jb >= S::kScOff) {
       // the tile's 32 K (then V) scales (4 bytes per token, tokens innermost): lanes 0-7 load
       // them, the rest fall outside the buffer range. Without V scales the V block repeats the
@@ -869,8 +870,9 @@ hipError_t launch_shape(const PartArgs& a, int page_mode, hipStream_t s) {
 }  // namespace
 
 // One kv head for all q heads: MLA-style latent (q.K 576 = 512 nope + 64 rotary, V = the
-// first 512 nope columns) and one-kv-head GLM-style widths (q.K 256 = 192 nope + 64 rotary,
-// V 256 of its own). The rotary columns may be in the K rows or stored apart.
+// first 512 nope columns), one-kv-head GLM-style widths (q.K 256 = 192 nope + 64 rotary,
+// V 256 of its own) and multi-query attention at depth 128 (bf16). The rotary columns may be
+// in the K rows or stored apart.
 hipError_t launch_partition_shared(const PartArgs& a, int page_mode, hipStream_t s) {
   if (a.Hkv != 1) return hipErrorInvalidValue;
   const bool rope_apart = a.k_rope != nullptr;
@@ -891,6 +893,9 @@ hipError_t launch_partition_shared(const PartArgs& a, int page_mode, hipStream_t
   }
   if (a.Dqk == 576 && a.Dv == 512 && a.v == a.k && a.Dk == (rope_apart ? 512 : 576))
     return launch_shape<SShape<512, 64, 512, true>>(a, page_mode, s);
+  // multi-query attention at depth 128: no rotary columns of their own, V its own cache
+  if (a.Dqk == 128 && a.Dv == 128 && a.v != a.k && a.Dk == 128 && !rope_apart)
+    return launch_shape<SShape<128, 0, 128, false>>(a, page_mode, s);
   if (a.Dqk == 256 && a.Dv == 256 && a.v != a.k && a.Dk == (rope_apart ? 192 : 256))
     return launch_shape<SShape<192, 64, 256, false>>(a, page_mode, s);
   return hipErrorInvalidValue;

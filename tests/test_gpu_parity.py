@@ -874,6 +874,7 @@ def test_page_size_forms(name, kw):
 # ---------------------------------------------------------------------------
 # more than 16 (query, head) columns per kv head on the matrix-core GQA kernel: the group
 # is split into virtual kv heads of at most 16 columns that read the same cached kv head
+# (multi-query bf16 at depth 128 runs on the shared-kv-head kernel instead: the first case)
 # ---------------------------------------------------------------------------
 LARGE_GROUPS = [
     ("mqa_g32_paged64_auto", dict(batch=3, num_q_heads=32, num_kv_heads=1, qk_depth=128, page_size=64,
@@ -898,7 +899,7 @@ LARGE_GROUPS = [
 
 
 @pytest.mark.parametrize("name,kw", LARGE_GROUPS, ids=[c[0] for c in LARGE_GROUPS])
-def test_large_group_virtual_kv_heads(name, kw):
+def test_large_group_parity(name, kw):
     # the combine launch, then the fold in pass 1 on the same inputs
     case = make_case(name, **kw)
     print(f"[parity] large group {name}", flush=True)
