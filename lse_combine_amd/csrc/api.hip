@@ -158,8 +158,6 @@ int check_problem(const da_problem* p, Variant* var) {
   } else {
     *var = kVarMfma;
   }
-  if (*var == kVarFma && g > 16)
-    return fail(DA_EUNSUPPORTED, "the vector-ALU kernel fuses at most 16 q heads per kv head (group %d)", g);
   return DA_OK;
 }
 
@@ -182,26 +180,26 @@ int page_mode(const da_problem* p) {
 }
 
 
-// Matrix-core GQA kernel: a wave serves at most 16 (query, head) MFMA columns. A larger
-// group is split into kv_div groups of g / kv_div heads (the largest divisor of g with
-// q_len x g / kv_div <= 16), each served as a kv head of its own: a virtual kv head, whose
-// waves read the rows of their cached kv head (a second read of the same rows, mostly from
-// L2). Shapes, schedules, counters and partial rows count virtual kv heads.
-int mfma_kv_div(const da_problem* p) {
+// GQA kernels (matrix-core and vector-ALU): a wave serves at most 16 (query, head) columns.
+// A larger group is split into kv_div groups of g / kv_div heads (the largest divisor of g
+// with q_len x g / kv_div <= 16), each served as a kv head of its own: a virtual kv head,
+// whose waves read the rows of their cached kv head (a second read of the same rows, mostly
+// from L2). Shapes, schedules, counters and partial rows count virtual kv heads.
+int kv_div_of(const da_problem* p) {
   const int ql = q_len_of(p), g = p->num_q_heads / p->num_kv_heads;
   if (ql * g <= 16) return 1;
   int d = 16 / ql;
   while (d > 1 && g % d) --d;
   return g / d;
 }
-int mfma_kv_heads(const da_problem* p) { return p->num_kv_heads * mfma_kv_div(p); }
+int virtual_kv_heads(const da_problem* p) { return p->num_kv_heads * kv_div_of(p); }
 
 // Matrix-core kernel shape: HG kv heads per workgroup (their waves read whole token
 // rows of the cache together) times KS key splits per kv head, HG * KS = 8 waves.
 // HG is as large as possible while the grid still offers a workgroup per CU (one
 // 8-wave workgroup per CU fits at three waves per SIMD).
 void mfma_shape(const da_problem* p, int32_t max_splits, int cus, int* HG, int* KS) {
-  const int hkv = mfma_kv_heads(p);
+  const int hkv = virtual_kv_heads(p);
   int hg = hkv < 8 ? hkv : 8;
   auto wgs = [&](int h) { return (int64_t)max_splits * ((hkv + h - 1) / h) * p->batch; };
   while (hg > 1 && wgs(hg) < (int64_t)cus) hg = (hg + 1) / 2;
@@ -215,7 +213,7 @@ void mfma_shape(const da_problem* p, int32_t max_splits, int cus, int* HG, int* 
 // of kMinShareTiles tiles; W workers per head group so that W x groups ~ CUs.
 void share_shape(const da_problem* p, int cus, int* HG, int* KS, int* W) {
   const int64_t tiles_max = (int64_t)p->batch * ceil_div(p->max_seq_len > 0 ? p->max_seq_len : 1, kTileKeys);
-  const int hkv = mfma_kv_heads(p);
+  const int hkv = virtual_kv_heads(p);
   int hg = hkv < 8 ? hkv : 8;
   auto groups = [&](int h) { return (int64_t)((hkv + h - 1) / h); };
   while (hg > 1 && (tiles_max / da::kMinShareTiles) * groups(hg) < (int64_t)cus) hg = (hg + 1) / 2;
@@ -252,7 +250,7 @@ int choose(const da_problem* p, Variant var, int32_t num_splits, int cus, int32_
     const int slots = cus * wgs_per_cu(p, var);
     // workgroups per (sequence, partition): kv heads, or 64-column blocks on the
     // shared-kv-head kernel
-    const int64_t per_part = var == kVarShared ? ceil_div(rows_per_seq(p), 64) : p->num_kv_heads;
+    const int64_t per_part = var == kVarShared ? ceil_div(rows_per_seq(p), 64) : virtual_kv_heads(p);
     const int64_t est_units = (int64_t)p->batch * per_part * ((maxlen + 1) / 2);
     C = ceil_div(est_units, 4LL * slots);
     // (multi-query attention at depth 128 on the shared-kv-head kernel: partitions of 256 keys
@@ -295,7 +293,7 @@ void ws_layout(const da_problem* p, int32_t chunk, int32_t max_splits, size_t* m
   const size_t o = (rows * (size_t)p->ov_depth * sizeof(float) + 255) & ~(size_t)255;
   // arrival counters of the fused combine: one per (sequence, kv head; virtual ones on the
   // matrix-core GQA kernel), or per (sequence, block of 64 columns) on the shared-kv-head kernel
-  const size_t per_seq = std::max<size_t>((size_t)mfma_kv_heads(p), (size_t)ceil_div(rows_per_seq(p), 64));
+  const size_t per_seq = std::max<size_t>((size_t)virtual_kv_heads(p), (size_t)ceil_div(rows_per_seq(p), 64));
   const size_t cnt = ((size_t)p->batch * per_seq * sizeof(int32_t) + 255) & ~(size_t)255;
   *ml_off = 0;
   *o_off = ml;
@@ -447,12 +445,12 @@ int64_t fused_fold_bytes(const da_problem* p, Variant var, int32_t C, int32_t P,
   const int64_t ql = q_len_of(p), g = p->num_q_heads / p->num_kv_heads;
   int64_t rows;
   if (var == kVarFma) {
-    rows = ql * g;   // (sequence, kv head)
+    rows = ql * (g / kv_div_of(p));   // (sequence, virtual kv head)
   } else if (var == kVarMfma) {
     int HG, KS, W;
     if (C == 0) share_shape(p, cus, &HG, &KS, &W);
     else mfma_shape(p, P, cus, &HG, &KS);
-    rows = ql * (g / mfma_kv_div(p)) * HG;   // (sequence, group of virtual kv heads)
+    rows = ql * (g / kv_div_of(p)) * HG;   // (sequence, group of virtual kv heads)
   } else {
     rows = std::min<int64_t>(64, rows_per_seq(p));   // (sequence, block of 64 columns)
   }
@@ -501,7 +499,7 @@ int run_splitk(const da_problem* p, const void* q, const da_kv& kv, const int32_
   float* po = (float*)((char*)workspace + o_off);
   hipStream_t s = (hipStream_t)stream;
   da::PartArgs a = da::build_part_args(p, q, kv.k_cache, kv.v_cache, page_table, seq_lens, scale, C, P,
-                                       var == kVarMfma ? mfma_kv_div(p) : 1);
+                                       var == kVarShared ? 1 : kv_div_of(p));
   a.part_o = po;
   a.part_ml = pml;
   if (C == 0) a.meta = meta_of(p, P, pml);
@@ -723,7 +721,7 @@ static int partition_impl(const da_problem* p, const void* q, const da_kv& kv, c
   if ((r = check_split_args(p, var, chunk_tokens, max_splits))) return r;
   if (!part_o || !part_ml) return fail(DA_EINVAL, "part_o and part_ml must be non-NULL");
   da::PartArgs a = da::build_part_args(p, q, kv.k_cache, kv.v_cache, page_table, seq_lens, scale, chunk_tokens,
-                                       max_splits, var == kVarMfma ? mfma_kv_div(p) : 1);
+                                       max_splits, var == kVarShared ? 1 : kv_div_of(p));
   a.part_o = part_o;
   a.part_ml = part_ml;
   if (chunk_tokens == 0) a.meta = meta_of(p, max_splits, part_ml);

@@ -35,8 +35,8 @@ struct PartArgs {
   float* lse;               // optional
   float* o32;               // optional
   int32_t B, Hq, Hkv, g, Dqk, Dv;   // Hq: rows per sequence (q_len x heads)
-  int32_t kv_div;                   // matrix-core GQA kernel: Hkv and g count virtual kv heads,
-                                    // kv_div per cached kv head (1: none); other kernels: 1
+  int32_t kv_div;                   // GQA kernels: Hkv and g count virtual kv heads, kv_div per
+                                    // cached kv head (1: none); shared-kv-head kernel: 1
   int32_t Dk;                       // K cache columns (Dqk, or the nope part when k_rope)
   int32_t Hq1, q_len;               // heads; queries per sequence (>= 1)
   int32_t v_row_len;        // elements between consecutive (row, kv-head) V vectors / Hkv

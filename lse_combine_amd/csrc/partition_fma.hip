@@ -125,10 +125,12 @@ __global__ __launch_bounds__(kWaves * 64, (FmaLds<T, GMAX>::kMinWaves)) void par
     }
   }
 
-  const char* kc = (const char*)a.k + (int64_t)kvh * RB;
-  const char* vc = (const char*)a.v + (int64_t)kvh * a.v_row_len * (int64_t)sizeof(T);
-  const int64_t kstride = (int64_t)a.Hkv * RB;                                  // bytes between K rows
-  const int64_t vstride = (int64_t)a.Hkv * a.v_row_len * (int64_t)sizeof(T);   // bytes between V rows
+  // (kvh and a.Hkv count virtual kv heads, a.kv_div of them per cached kv head)
+  const int kvc = kvh / a.kv_div, kv_heads = a.Hkv / a.kv_div;
+  const char* kc = (const char*)a.k + (int64_t)kvc * RB;
+  const char* vc = (const char*)a.v + (int64_t)kvc * a.v_row_len * (int64_t)sizeof(T);
+  const int64_t kstride = (int64_t)kv_heads * RB;                                  // bytes between K rows
+  const int64_t vstride = (int64_t)kv_heads * a.v_row_len * (int64_t)sizeof(T);   // bytes between V rows
 
   float m[GMAX], lsum[GMAX], o[GMAX][VEC];
 #pragma unroll

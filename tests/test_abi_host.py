@@ -57,7 +57,7 @@ def test_probe_library_is_apart_from_the_product():
     (dict(num_q_heads=2, num_kv_heads=2), DA_OK),
     (dict(num_q_heads=32, num_kv_heads=2), DA_OK),             # group 16
     (dict(num_q_heads=34, num_kv_heads=2), DA_OK),             # group 17: 17 virtual kv heads of one
-    (dict(num_q_heads=34, num_kv_heads=2, dtype=0), DA_EUNSUPPORTED),   # ... not on the vector ALU
+    (dict(num_q_heads=34, num_kv_heads=2, dtype=0), DA_OK),          # ... also on the vector ALU
     (dict(num_q_heads=15, num_kv_heads=2), DA_EINVAL),         # not a multiple
     (dict(qk_depth=64, ov_depth=64), DA_EUNSUPPORTED),
     (dict(dtype=7), DA_EINVAL),

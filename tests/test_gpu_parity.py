@@ -872,9 +872,9 @@ def test_page_size_forms(name, kw):
 
 
 # ---------------------------------------------------------------------------
-# more than 16 (query, head) columns per kv head on the matrix-core GQA kernel: the group
-# is split into virtual kv heads of at most 16 columns that read the same cached kv head
-# (multi-query bf16 at depth 128 runs on the shared-kv-head kernel instead: the first case)
+# more than 16 (query, head) columns per kv head on the GQA kernels: the group is split into
+# virtual kv heads of at most 16 columns that read the same cached kv head (multi-query bf16
+# at depth 128 runs on the shared-kv-head kernel instead: the first case)
 # ---------------------------------------------------------------------------
 LARGE_GROUPS = [
     ("mqa_g32_paged64_auto", dict(batch=3, num_q_heads=32, num_kv_heads=1, qk_depth=128, page_size=64,
@@ -895,6 +895,11 @@ LARGE_GROUPS = [
     ("mqa_g48_fp8_paged16_poisoned", dict(batch=3, num_q_heads=48, num_kv_heads=1, qk_depth=128, page_size=16,
                                           seq_lens=[100, 1, 1025], num_splits=0, seed=207, kv_fp8=True, poison=True,
                                           spare_pages=3)),
+    # fp32 on the vector-ALU kernel, same split into virtual kv heads
+    ("fp32_mqa_g32_paged64", dict(batch=2, num_q_heads=32, num_kv_heads=1, qk_depth=128, dtype=torch.float32,
+                                  page_size=64, seq_lens=[1000, 77], num_splits=0, seed=208)),
+    ("fp32_g24_hkv2_contig_splits3", dict(batch=2, num_q_heads=48, num_kv_heads=2, qk_depth=128,
+                                          dtype=torch.float32, seq_lens=[600, 1300], num_splits=3, seed=209)),
 ]
 
 
