@@ -134,9 +134,9 @@ typedef struct da_problem {
  *    the shared-kv-head kernel below);
  *  - Dqk == Dv == 128, one query per sequence: f32 (vector-ALU kernel) or bf16
  *    (matrix-core kernel; the vector-ALU one on request with DA_KERNEL_FMA);
- *  - on the matrix-core kernel (bf16 q, separate K and V) the depth pairs Dqk/Dv 128/128,
- *    192/128 and 256/256, with the K/V cache in bf16 or fp8 and optionally the 64 rotary
- *    columns stored apart in bf16 (nope_depth 128 or 192);
+ *  - on the matrix-core kernel (bf16 q, separate K and V) the depth pairs Dqk/Dv 64/64,
+ *    128/128, 192/128 and 256/256, with the K/V cache in bf16 or fp8 and, at 192/128 and
+ *    256/256, optionally the 64 rotary columns stored apart in bf16 (nope_depth 128 or 192);
  *  - with one kv head, on the shared-kv-head kernel (bf16 q, any number of q heads and
  *    q_len): latent 576/512 with V = the first 512 K columns (v_is_k_prefix), and
  *    256/256 with V of its own when q_len x Hq > 16; the 64 rotary columns in the K rows

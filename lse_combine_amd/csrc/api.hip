@@ -125,13 +125,14 @@ int check_problem(const da_problem* p, Variant* var) {
   // Features only the matrix-core kernel has: several queries per sequence, fp8 caches,
   // the wider depth pairs and rotary columns stored apart.
   const bool d128 = p->qk_depth == 128 && p->ov_depth == 128;
+  const bool d64 = p->qk_depth == 64 && p->ov_depth == 64;
   const bool wide = (p->qk_depth == 192 && p->ov_depth == 128) || (p->qk_depth == 256 && p->ov_depth == 256);
-  if (ql > 1 || p->kv_dtype == DA_FP8_E4M3 || wide || p->nope_depth > 0) {
-    if (!d128 && !wide)
+  if (ql > 1 || p->kv_dtype == DA_FP8_E4M3 || wide || d64 || p->nope_depth > 0) {
+    if (!d128 && !d64 && !wide)
       return fail(DA_EUNSUPPORTED,
                   "several queries per sequence, fp8 caches and rotary columns stored apart are supported at "
-                  "depths (q.K / V) 128/128, 192/128 and 256/256 (got %d/%d)", p->qk_depth, p->ov_depth);
-    if (p->nope_depth > 0 && (d128 || p->qk_depth - p->nope_depth != 64))
+                  "depths (q.K / V) 64/64, 128/128, 192/128 and 256/256 (got %d/%d)", p->qk_depth, p->ov_depth);
+    if (p->nope_depth > 0 && (d128 || d64 || p->qk_depth - p->nope_depth != 64))
       return fail(DA_EUNSUPPORTED, "rotary columns stored apart: 64 of them at depth 192/128 or 256/256 "
                                    "(nope_depth 128 or 192; got %d of %d)", p->nope_depth, p->qk_depth);
     if (p->nope_depth > 0 && p->rope_dtype != DA_BF16)
@@ -145,7 +146,7 @@ int check_problem(const da_problem* p, Variant* var) {
 
   if (p->qk_depth != 128 || p->ov_depth != 128)
     return fail(DA_EUNSUPPORTED,
-                "supported depths (q.K / V): 128/128; 192/128 and 256/256 with bf16 q on the matrix-core kernel; "
+                "supported depths (q.K / V): 128/128; 64/64, 192/128 and 256/256 with bf16 q on the matrix-core kernel; "
                 "576/512 latent-shared (got %d/%d)", p->qk_depth, p->ov_depth);
   if (p->dtype == DA_F32) {
     if (p->kernel == DA_KERNEL_MFMA) return fail(DA_EUNSUPPORTED, "the matrix-core kernel needs bf16 inputs");
@@ -737,8 +738,8 @@ int decode_attn_combine(const da_problem* p, const int32_t* seq_lens, float scal
   Variant var = kVarFma;
   int r = check_problem(p, &var);
   if (r && r != DA_EUNSUPPORTED) return r;
-  if (p->ov_depth != 128 && p->ov_depth != 256 && p->ov_depth != 512)
-    return fail(DA_EUNSUPPORTED, "combine supports ov_depth 128, 256 or 512 (got %d)", p->ov_depth);
+  if (p->ov_depth != 64 && p->ov_depth != 128 && p->ov_depth != 256 && p->ov_depth != 512)
+    return fail(DA_EUNSUPPORTED, "combine supports ov_depth 64, 128, 256 or 512 (got %d)", p->ov_depth);
   if (!seq_lens || !part_o || !part_ml || !out) return fail(DA_EINVAL, "seq_lens, part_o, part_ml and out must be non-NULL");
   if ((r = check_scale(scale))) return r;
   if ((r = check_split_args(p, var, chunk_tokens, max_splits))) return r;

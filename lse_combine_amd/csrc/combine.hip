@@ -60,6 +60,18 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
       case 16: go(combine_kernel<128, 16, 512>, 1, 512); break;
       default: go(combine_kernel<128, 32, 1024>, 1, 1024); break;
     }
+  } else if (a.Dv == 64) {
+    auto go = [&](auto kern, int rpb, int nt = kCombineThreads) {
+      hipLaunchKernelGGL(kern, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(nt), 0, s, a);
+    };
+    switch (S) {
+      case 1: go(combine_kernel<64, 1>, 16); break;
+      case 2: go(combine_kernel<64, 2>, 8); break;
+      case 4: go(combine_kernel<64, 4>, 4); break;
+      case 8: go(combine_kernel<64, 8>, 2); break;
+      case 16: go(combine_kernel<64, 16>, 1); break;
+      default: go(combine_kernel<64, 32, 512>, 1, 512); break;
+    }
   } else if (a.Dv == 256) {
     auto go = [&](auto kern, int rpb) {
       hipLaunchKernelGGL(kern, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(kCombineThreads), 0, s, a);

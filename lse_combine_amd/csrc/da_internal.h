@@ -80,6 +80,8 @@ hipError_t launch_partition_fma(const PartArgs& a, int dtype, int page_mode, hip
 // wider shapes' own translation units
 hipError_t launch_partition_mfma(const PartArgs& a, int page_mode, int kv_heads_per_wg, int key_splits,
                                  hipStream_t s);
+hipError_t launch_partition_mfma_d64(const PartArgs& a, int page_mode, int kv_heads_per_wg, int key_splits,
+                                     hipStream_t s);
 hipError_t launch_partition_mfma_d192(const PartArgs& a, int page_mode, int kv_heads_per_wg, int key_splits,
                                       hipStream_t s);
 hipError_t launch_partition_mfma_d256(const PartArgs& a, int page_mode, int kv_heads_per_wg, int key_splits,

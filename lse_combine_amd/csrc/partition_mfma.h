@@ -72,6 +72,7 @@ struct MShape {
   static constexpr int NR = DR / 32;           //   ... over the rotary columns
   static constexpr int DB = DV / 16;           // 16-deep blocks of O
   static constexpr int kVRow = DV * 2;         // bytes of one bf16 V row in LDS
+  static constexpr int kVXm = DV >= 128 ? 15 : DV / 8 - 1;   // chunk swizzle mask of a V row
   static constexpr int kVBytes = kTile * kVRow;       // one wave's V tile in LDS
   // fp8 caches stage V codes (32 x DV bytes per tile) beside a half-depth bf16 tile; at
   // V depth 128 the region has room for two staged tiles (two tiles in flight)
@@ -82,7 +83,7 @@ struct MShape {
   static_assert(!kKLds || 3 * kTile * DV <= 2 * kVBytes, "the fp8 staging fits the region");
   static_assert(kRegionBytes >= kVBytes, "the region holds a bf16 V tile");
   static constexpr int kWaveBytes = kRegionBytes + 256;   // + merge (m, l) for up to 16 columns
-  static_assert(DK % 64 == 0 && DR % 32 == 0 && (DV == 128 || DV == 256), "unsupported depths");
+  static_assert(DK % 64 == 0 && DR % 32 == 0 && (DV == 64 || DV == 128 || DV == 256), "unsupported depths");
 };
 
 typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -467,7 +468,7 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
 
   // V of the tile at t0 straight into this wave's LDS tile with direct-to-LDS 16-byte loads
   // of 1 KB each: a load fills kRpi consecutive rows of kCpr 16-byte chunks, lane l writing
-  // row l / kCpr, chunk slot l % kCpr with the swizzled source chunk slot ^ (row & 15). Rows
+  // row l / kCpr, chunk slot l % kCpr with the swizzled source chunk slot ^ (row & kVXm). Rows
   // past the end of a ragged tile are outside the buffer range and deliver zeros.
   constexpr int kCpr = S::DV / 8, kRpi = 64 / kCpr, kLoadsPerHalf = 16 / kRpi;
   const int v_row = lane / kCpr, v_slot = lane % kCpr;
@@ -483,7 +484,7 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
 #pragma unroll
         for (int i = 0; i < kLoadsPerHalf; ++i) {
           const int r = kRpi * i + v_row;   // row within the half; the swizzle repeats per half
-          const uint32_t voff = (uint32_t)r * vrow_bytes + 16 * (v_slot ^ (r & 15));
+          const uint32_t voff = (uint32_t)r * vrow_bytes + 16 * (v_slot ^ (r & S::kVXm));
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (DA_LDS void*)(vt + (kLoadsPerHalf * h + i) * 1024), 16,
                                                    voff, 0, 0, kLoadNT);
         }
@@ -492,7 +493,7 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
 #pragma unroll
       for (int i = 0; i < 2 * kLoadsPerHalf; ++i) {
         const int r = kRpi * i + v_row;
-        const char* vp = vc + general_row(t0 + min(r, last)) * vrow_bytes + vslice + 16 * (v_slot ^ (r & 15));
+        const char* vp = vc + general_row(t0 + min(r, last)) * vrow_bytes + vslice + 16 * (v_slot ^ (r & S::kVXm));
         __builtin_amdgcn_global_load_lds((const void*)vp, (DA_LDS void*)(vt + i * 1024), 16, 0, 0);
       }
     }
@@ -683,7 +684,7 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
     }
   };
   auto pv = [&](const bf16x8& pb_hi, const bf16x8& pb_lo) {
-    pv_tile(IntC<0>{}, IntC<DB>{}, IntC<S::kVRow>{}, IntC<15>{}, vt, pb_hi, pb_lo);
+    pv_tile(IntC<0>{}, IntC<DB>{}, IntC<S::kVRow>{}, IntC<S::kVXm>{}, vt, pb_hi, pb_lo);
   };
 
   // fp8 V through LDS: the tile's 32 rows of DV codes land, direct-to-LDS and
@@ -1239,6 +1240,7 @@ hipError_t launch_shape(const PartArgs& a, int page_mode, int HG, int KS, hipStr
   return a.q_len * a.g <= 8 ? launch_hl<true, S>(a, page_mode, HG, KS, s) : launch_hl<false, S>(a, page_mode, HG, KS, s);
 }
 
+typedef MShape<64, 64, 0> Shape64;
 typedef MShape<128, 128, 0> Shape128;
 typedef MShape<192, 128, 0> Shape192;        // nope 128 + 64 rotary, V 128 (nope == V)
 typedef MShape<192, 128, 64> Shape192R;      //   ... rotary columns stored apart

@@ -59,7 +59,7 @@ def test_probe_library_is_apart_from_the_product():
     (dict(num_q_heads=34, num_kv_heads=2), DA_OK),             # group 17: 17 virtual kv heads of one
     (dict(num_q_heads=34, num_kv_heads=2, dtype=0), DA_OK),          # ... also on the vector ALU
     (dict(num_q_heads=15, num_kv_heads=2), DA_EINVAL),         # not a multiple
-    (dict(qk_depth=64, ov_depth=64), DA_EUNSUPPORTED),
+    (dict(qk_depth=96, ov_depth=96), DA_EUNSUPPORTED),
     (dict(dtype=7), DA_EINVAL),
     (dict(batch=0), DA_EINVAL),
     (dict(page_size=-1), DA_EINVAL),
@@ -361,6 +361,11 @@ def test_binding_refuses_output_buffers_without_every_row():
     (dict(qk_depth=256, ov_depth=256, nope_depth=-1), DA_EINVAL),
     (dict(qk_depth=256, ov_depth=128), DA_EUNSUPPORTED),
     (dict(qk_depth=256, ov_depth=256, dtype=0), DA_EUNSUPPORTED),
+    (dict(qk_depth=64, ov_depth=64), DA_OK),                        # heads of 64
+    (dict(qk_depth=64, ov_depth=64, kv_dtype=2, q_len=2, page_size=24, max_pages_per_seq=200), DA_OK),
+    (dict(qk_depth=64, ov_depth=64, dtype=0), DA_EUNSUPPORTED),     # fp32: the vector-ALU kernel is depth 128
+    (dict(qk_depth=64, ov_depth=64, nope_depth=32, rope_dtype=1), DA_EUNSUPPORTED),
+    (dict(qk_depth=64, ov_depth=128), DA_EUNSUPPORTED),
     (dict(qk_depth=256, ov_depth=256, page_size=16, max_pages_per_seq=256), DA_OK),
     (dict(qk_depth=256, ov_depth=256, page_size=24, max_pages_per_seq=200), DA_OK),   # per-key page lookup
     (dict(qk_depth=256, ov_depth=256, nope_depth=192, rope_dtype=1, page_size=24, max_pages_per_seq=200),

@@ -624,8 +624,8 @@ def test_equal_share_partials_match_oracle(name, kw, workers):
     assert_parity(out, lse, o32, Oref, Lref, what=f"equal shares {name} combine")
 
 
-@pytest.mark.parametrize("Dv,P", [(128, 4), (128, 16), (128, 24), (128, 64), (256, 8), (256, 40), (512, 8),
-                                  (512, 20)])
+@pytest.mark.parametrize("Dv,P", [(64, 4), (64, 40), (64, 300), (128, 4), (128, 16), (128, 24), (128, 64),
+                                  (256, 8), (256, 40), (512, 8), (512, 20)])
 def test_combine_only_on_oracle_partials(Dv, P):
     # oracle partials (with empty partitions) fed to the HIP combine
     r = np.random.default_rng(Dv + P)
@@ -643,7 +643,7 @@ def test_combine_only_on_oracle_partials(Dv, P):
     Oref, Lref = combine_fp64(m32, l32, O32, 0.125)
     prob = api._lib.DaProblem()
     prob.batch, prob.num_q_heads, prob.num_kv_heads = B, Hq, 1
-    prob.qk_depth = {128: 128, 256: 256, 512: 576}[Dv]
+    prob.qk_depth = {64: 64, 128: 128, 256: 256, 512: 576}[Dv]
     prob.ov_depth, prob.dtype, prob.page_size, prob.kv_capacity = Dv, 1, 0, P * chunk
     prob.max_seq_len = P * chunk
     prob.v_is_k_prefix = 1 if Dv == 512 else 0
@@ -915,6 +915,40 @@ def test_large_group_parity(name, kw):
         torch.cuda.synchronize()
         assert torch.isfinite(o32).all()
         assert_parity(out, lse, o32, O, LSE, what=f"large group {name} fused={fused}")
+
+
+# ---------------------------------------------------------------------------
+# heads of 64 dimensions (q.K 64 / V 64) on the matrix-core kernel
+# ---------------------------------------------------------------------------
+D64 = [
+    ("d64_g4_contig_splits3", dict(batch=2, num_q_heads=16, num_kv_heads=4, qk_depth=64, seq_lens=[1000, 77],
+                                   num_splits=3, seed=210)),
+    ("d64_g8_paged64_auto", dict(batch=4, num_q_heads=16, num_kv_heads=2, qk_depth=64, page_size=64,
+                                 len_range=(1, 4000), num_splits=0, seed=211)),
+    ("d64_fp8_g8_paged16_poisoned", dict(batch=3, num_q_heads=16, num_kv_heads=2, qk_depth=64, page_size=16,
+                                         seq_lens=[100, 1, 1025], num_splits=0, seed=212, kv_fp8=True, poison=True,
+                                         spare_pages=3)),
+    ("d64_q2_g16_paged48_general", dict(batch=3, num_q_heads=32, num_kv_heads=2, qk_depth=64, page_size=48,
+                                        seq_lens=[2, 700, 1500], num_splits=0, seed=213, q_len=2)),
+    ("d64_fp8_g1_contig_key_splits", dict(batch=2, num_q_heads=4, num_kv_heads=4, qk_depth=64,
+                                          seq_lens=[3000, 1], num_splits=2, seed=214, kv_fp8=True)),
+    ("d64_mqa_g32_paged32", dict(batch=2, num_q_heads=32, num_kv_heads=1, qk_depth=64, page_size=32,
+                                 seq_lens=[1500, 333], num_splits=0, seed=215)),
+]
+
+
+@pytest.mark.parametrize("name,kw", D64, ids=[c[0] for c in D64])
+def test_depth64_parity(name, kw):
+    # the combine launch, then the fold in pass 1 on the same inputs
+    case = make_case(name, **kw)
+    print(f"[parity] depth 64 {name}", flush=True)
+    dc = to_device(case)
+    O, LSE = oracle_for(case)
+    for fused in (False, "force"):
+        out, lse, o32 = api.case_call(dc, return_lse=True, return_o32=True, fused=fused)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o32).all()
+        assert_parity(out, lse, o32, O, LSE, what=f"depth 64 {name} fused={fused}")
 
 
 # ---------------------------------------------------------------------------

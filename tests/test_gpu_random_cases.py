@@ -1,6 +1,6 @@
 """Seeded random problems across every kernel family, each checked against the oracle.
 
-Each case draws a family (GQA matrix-core depths 128/128, 192/128, 256/256 with rotary
+Each case draws a family (GQA matrix-core depths 64/64, 128/128, 192/128, 256/256 with rotary
 columns inline or apart; fp32 and bf16 on the vector-ALU kernel; one kv head for all q
 heads in the latent and GLM widths), a cache dtype (bf16, or fp8 where the family has it),
 a page size (contiguous, powers of two, or 48 keys), 1-5 sequences with random lengths
@@ -26,7 +26,7 @@ N_CASES = 120
 
 
 def _draw(rng):
-    fam = rng.choice(["gqa128", "gqa128", "wide", "fp32", "fma_bf16", "latent", "glm_mqa"])
+    fam = rng.choice(["gqa128", "gqa128", "wide", "fp32", "fma_bf16", "latent", "glm_mqa", "d64"])
     kw = dict(batch=rng.randint(1, 5), seed=rng.randint(0, 1 << 30))
     kernel = "auto"
     page = rng.choice([0, 16, 32, 64, 128, 48])
@@ -35,6 +35,10 @@ def _draw(rng):
     if fam == "gqa128":
         hkv = rng.choice([1, 2, 4, 8])
         kw.update(num_kv_heads=hkv, num_q_heads=hkv * rng.choice([1, 2, 4, 8, 16]), qk_depth=128)
+        kv_fp8 = rng.random() < 0.3
+    elif fam == "d64":
+        hkv = rng.choice([1, 2, 4])
+        kw.update(num_kv_heads=hkv, num_q_heads=hkv * rng.choice([1, 4, 8, 16, 24]), qk_depth=64)
         kv_fp8 = rng.random() < 0.3
     elif fam == "wide":
         hkv = rng.choice([1, 2, 4])
