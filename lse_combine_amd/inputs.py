@@ -285,6 +285,11 @@ WORKLOADS = {
     "paged_mqa": dict(seed=9, batch=32, num_q_heads=48, num_kv_heads=1, qk_depth=128,
                       dtype=torch.bfloat16, page_size=64, len_range=(512, 8192), num_splits=0,
                       page_table_width=128),
+    # heads of 64 dimensions: batch 32, 32 q heads / 8 kv heads (group 4), bf16, page 64,
+    # L_b ~ U[512, 8192], automatic splits
+    "paged_gqa_d64": dict(seed=10, batch=32, num_q_heads=32, num_kv_heads=8, qk_depth=64,
+                          dtype=torch.bfloat16, page_size=64, len_range=(512, 8192), num_splits=0,
+                          page_table_width=128),
     # one q head per kv head (multi-head attention, group 1): batch 32, 32 heads, head dim
     # 128, bf16, page 64, L_b ~ U[512, 8192], automatic splits
     "paged_mha": dict(seed=8, batch=32, num_q_heads=32, num_kv_heads=32, qk_depth=128,

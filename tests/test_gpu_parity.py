@@ -663,7 +663,7 @@ def test_combine_only_on_oracle_partials(Dv, P):
 # differ beyond the stated tolerances (the oracle runs the largest of these in seconds).
 FULL_WORKLOADS = ["tiny", "gqa", "paged_gqa", "long", "latent", "paged_gqa_q2", "paged_gqa_fp8", "paged_glm",
                   "paged_glm_fp8", "latent_rope_apart", "glm_mqa", "paged_mha", "latent_fp8", "glm_mqa_fp8",
-                  "latent_fp8_inline", "paged_mqa"]
+                  "latent_fp8_inline", "paged_mqa", "paged_gqa_d64"]
 
 
 @pytest.mark.parametrize("name", FULL_WORKLOADS)
