@@ -3,7 +3,7 @@
 Each case draws a family (GQA matrix-core depths 64/64, 128/128, 192/128, 256/256 with rotary
 columns inline or apart; fp32 and bf16 on the vector-ALU kernel; one kv head for all q
 heads in the latent and GLM widths), a cache dtype (bf16, or fp8 where the family has it),
-a page size (contiguous, powers of two, or 48 keys), 1-5 sequences with random lengths
+a page size (contiguous, powers of two from 1 to 128 keys, 24 or 48), 1-5 sequences with random lengths
 (empty ones included), one to three queries per sequence, a split count (automatic or
 fixed) and a combine (separate launch, fused where it pays, fold forced in pass 1). Draws
 the library does not support (da_supported) are drawn again. Every case prints its draw
@@ -29,12 +29,12 @@ def _draw(rng):
     fam = rng.choice(["gqa128", "gqa128", "wide", "fp32", "fma_bf16", "latent", "glm_mqa", "d64"])
     kw = dict(batch=rng.randint(1, 5), seed=rng.randint(0, 1 << 30))
     kernel = "auto"
-    page = rng.choice([0, 16, 32, 64, 128, 48])
+    page = rng.choice([0, 16, 32, 64, 128, 48, 8, 24, 1])
     q_len = rng.choice([1, 1, 1, 2, 3])
     kv_fp8 = False
     if fam == "gqa128":
         hkv = rng.choice([1, 2, 4, 8])
-        kw.update(num_kv_heads=hkv, num_q_heads=hkv * rng.choice([1, 2, 4, 8, 16]), qk_depth=128)
+        kw.update(num_kv_heads=hkv, num_q_heads=hkv * rng.choice([1, 2, 4, 8, 16, 24, 32]), qk_depth=128)
         kv_fp8 = rng.random() < 0.3
     elif fam == "d64":
         hkv = rng.choice([1, 2, 4])
@@ -52,7 +52,7 @@ def _draw(rng):
         kv_fp8 = rng.random() < 0.3
     elif fam == "fp32":
         hkv = rng.choice([1, 2])
-        kw.update(num_kv_heads=hkv, num_q_heads=hkv * rng.choice([1, 2, 4, 8]), qk_depth=128, dtype=torch.float32)
+        kw.update(num_kv_heads=hkv, num_q_heads=hkv * rng.choice([1, 2, 4, 8, 20]), qk_depth=128, dtype=torch.float32)
     elif fam == "fma_bf16":
         hkv = rng.choice([1, 2])
         kw.update(num_kv_heads=hkv, num_q_heads=hkv * rng.choice([1, 4, 8, 16]), qk_depth=128)
