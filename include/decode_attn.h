@@ -56,7 +56,7 @@ typedef enum {
 
 typedef enum {
   DA_KERNEL_AUTO = 0,    /* library's choice */
-  DA_KERNEL_FMA = 1,     /* vector-ALU partition kernel (fp32 or bf16, group <= 16, depth 128);
+  DA_KERNEL_FMA = 1,     /* vector-ALU partition kernel (fp32 or bf16, depth 128, one query);
                             the automatic choice for fp32 only */
   DA_KERNEL_MFMA = 2     /* matrix-core partition kernel (bf16 q; bf16 or fp8 caches) */
 } da_kernel;
@@ -276,7 +276,7 @@ int decode_attn_partition_kv(const da_problem* p, const void* q, const da_kv* kv
  * normalised O and its (max, sum)). Writes part_ml / part_o (device, layouts above) for
  * p < P_b; entries for p >= P_b are not written. chunk_tokens must be a positive multiple
  * of 32 with max_splits >= ceil(max_seq_len / chunk_tokens), or 0 (equal shares, 1 <=
- * max_splits <= 65535; DA_EUNSUPPORTED unless the matrix-core depth-128 kernel runs). */
+ * max_splits <= 65535; DA_EUNSUPPORTED unless the matrix-core GQA kernel runs). */
 int decode_attn_partition(const da_problem* p, const void* q, const void* k_cache,
                           const void* v_cache, const int32_t* page_table,
                           const int32_t* seq_lens, float scale, int32_t chunk_tokens,
