@@ -77,8 +77,9 @@ struct MShape {
   // fp8 caches stage V codes (32 x DV bytes per tile) beside a half-depth bf16 tile; at
   // V depth 128 the region has room for two staged tiles (two tiles in flight)
   static constexpr int kV8Tiles = DV == 128 ? 2 : 1;
-  // bf16 caches at depth 128/128 also stage the K tile (32 x 256 bytes) in the region
-  static constexpr bool kKLds = DQK == 128 && DV == 128 && DR == 0;
+  // bf16 caches at depth 128/128 and 64/64 also stage the K tile (32 rows like V's) in the
+  // region
+  static constexpr bool kKLds = DQK == DV && (DV == 128 || DV == 64) && DR == 0;
   static constexpr int kRegionBytes = kKLds ? 2 * kVBytes : (kV8Tiles == 2 ? 3 * kTile * DV : kVBytes);
   static_assert(!kKLds || 3 * kTile * DV <= 2 * kVBytes, "the fp8 staging fits the region");
   static_assert(kRegionBytes >= kVBytes, "the region holds a bf16 V tile");
@@ -899,7 +900,7 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
 #pragma unroll
             for (int i = 0; i < kLoadsPerHalf; ++i) {
               const int r = kRpi * i + v_row;
-              lds_dma16(rs, (uint32_t)r * row_bytes + 16 * (v_slot ^ (r & 15)),
+              lds_dma16(rs, (uint32_t)r * row_bytes + 16 * (v_slot ^ (r & S::kVXm)),
                         __builtin_amdgcn_readfirstlane(lds_addr(dst + (kLoadsPerHalf * h + i) * 1024)));
             }
           }
@@ -912,7 +913,8 @@ __device__ __forceinline__ void run_piece(const PartArgs& a, const WaveInfo& wv,
             const int r = n + 16 * blk;
 #pragma unroll
             for (int j = 0; j < NJK; ++j) {
-              const bf16x8 kf = as_bf16x8(*(const u32x4*)(kt + r * S::kVRow + (((4 * j + qd) ^ (r & 15)) << 4)));
+              const bf16x8 kf =
+                  as_bf16x8(*(const u32x4*)(kt + r * S::kVRow + (((4 * j + qd) ^ (r & S::kVXm)) << 4)));
               s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[j], s[blk], 0, 0, 0);
             }
           }

@@ -1,6 +1,6 @@
 // Matrix-core partition kernel, q.K and V depth 64 (heads of 64 dimensions): the same
-// per-tile scheme as depth 128 with 8-chunk V rows, K straight into the A-operand
-// registers (FA4Config: any qk_depth / ov_depth pair the tiles divide).
+// per-tile scheme as depth 128 with 8-chunk rows, bf16 K staged through LDS like V
+// (FA4Config: any qk_depth / ov_depth pair the tiles divide).
 #include "partition_mfma.h"
 
 namespace da {
