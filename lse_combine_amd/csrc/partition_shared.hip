@@ -1,14 +1,16 @@
 // Split-K pass 1 when one kv head serves every q head of a sequence (FA4Config,
 // use_shared_kv / shared_kv_cols: MLA-style latent attention, where V is the first ov_depth
 // columns of each K row, and one-kv-head attention with a V of its own whose depth need not
-// equal the nope depth, as FA4Config's with_splitk keeps for GLM-style configs). Every q
-// head reads the same K and V rows, so q.K and P.V are dense contractions (about 200 flop
-// per byte of KV) and run on v_mfma_f32_16x16x32_bf16.
+// equal the nope depth, as FA4Config's with_splitk keeps for GLM-style configs, or, at
+// depth 128, multi-query attention). Every q head reads the same K and V rows, so q.K and
+// P.V are dense contractions (about 200 flop per byte of KV for the latent form) and run on
+// v_mfma_f32_16x16x32_bf16.
 //
 // A K row is [nope columns | rotary columns] (FA4Config, rope_depth = q.K depth minus the
 // nope depth); the rotary columns sit in the K rows or in a tensor of their own (bf16,
 // FA4Config rope_dtype). The kernel only sees two column ranges with their own base and row
-// stride, so both forms run the same code.
+// stride, so both forms run the same code (a shape without rotary columns has an empty
+// second range).
 //
 // Workgroup = (partition p, block of 64 (query, head) columns, sequence b): eight waves,
 // two per SIMD, with one role each:
